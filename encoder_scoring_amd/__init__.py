@@ -1,0 +1,23 @@
+"""MI355X-native variable-length transformer scoring (gfx950 HIP behind a C ABI).
+
+Public API (all compute runs in libencscore's HIP kernels; PyTorch only
+provides device memory and the current stream):
+
+    Scorer(blob, max_tokens, max_seqs)       load a weight blob (bytes or path)
+    Scorer.score(d_ids, offsets)             one packed batch -> rewards (device)
+    Scorer.score_requests(d_ids, lengths)    plan + pack + score + scatter a stream
+    plan_batches(lengths, max_tokens, c)     host DP batch planner
+    pack_offsets(lengths, order, b, e)       packed offsets of one planned batch
+"""
+from .api import (  # noqa: F401
+    Scorer,
+    plan_batches,
+    pack_offsets,
+    layernorm,
+    RaggedScores,
+    softmax_ragged,
+    gemm_bf16,
+    version,
+)
+from ._lib import EncScoreError, EXPORTS  # noqa: F401
+from . import blob  # noqa: F401

@@ -1,0 +1,219 @@
+"""User-facing wrappers over the C ABI (marshalling only, no compute).
+
+Device tensors are torch tensors on the current ROCm device; the HIP stream is
+torch's current stream.  Host arrays are numpy.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import _lib
+from ._lib import as_i32, check, i32p
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream():
+    return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
+
+
+def _dptr(t, dtype, name):
+    torch = _torch()
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def version():
+    return _lib.load().es_version().decode()
+
+
+# ------------------------------------------------------------------ planner
+
+def plan_batches(lengths, max_tokens, batch_overhead, lib=None):
+    """Host DP planner -> (order int32[n], batch_starts int32[B+1], total_cost)."""
+    lib = lib or _lib.load()
+    lengths = as_i32(lengths)
+    n = lengths.size
+    order = np.zeros(n, dtype=np.int32)
+    starts = np.zeros(n + 1, dtype=np.int32)
+    nb = ctypes.c_int32()
+    cost = ctypes.c_int64()
+    check(lib, lib.es_plan_batches(i32p(lengths), n, int(max_tokens), int(batch_overhead),
+                                   i32p(order), i32p(starts), ctypes.byref(nb), ctypes.byref(cost)))
+    return order, starts[: nb.value + 1].copy(), cost.value
+
+
+def pack_offsets(lengths, order, begin, end, lib=None):
+    lib = lib or _lib.load()
+    lengths, order = as_i32(lengths), as_i32(order)
+    out = np.zeros(max(end - begin, 0) + 1, dtype=np.int32)
+    check(lib, lib.es_pack_offsets(i32p(lengths), i32p(order), int(begin), int(end), i32p(out)))
+    return out
+
+
+# ------------------------------------------------------------------ model
+
+class Scorer:
+    """A loaded scoring model on the current device.
+
+    ``blob`` is the weight blob as bytes or a file path.  ``max_tokens`` and
+    ``max_seqs`` size the workspace (tokens / sequences per packed batch).
+    """
+
+    def __init__(self, blob, max_tokens, max_seqs):
+        self.lib = _lib.load()
+        h = ctypes.c_void_p()
+        if isinstance(blob, (bytes, bytearray, memoryview, np.ndarray)):
+            arr = np.frombuffer(blob, dtype=np.uint8)     # no copy
+            st = self.lib.es_load_weights_mem(ctypes.c_void_p(arr.ctypes.data), arr.size,
+                                              int(max_tokens), int(max_seqs), ctypes.byref(h))
+        else:
+            st = self.lib.es_load_weights(os.fsencode(blob), int(max_tokens), int(max_seqs),
+                                          ctypes.byref(h))
+        check(self.lib, st)
+        self.handle = h
+        self.info = _lib.ModelInfo()
+        check(self.lib, self.lib.es_model_info(self.handle, ctypes.byref(self.info)))
+
+    def close(self):
+        if getattr(self, "handle", None):
+            self.lib.es_free(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def reward_offset(self):
+        v = ctypes.c_float()
+        check(self.lib, self.lib.es_get_reward_offset(self.handle, ctypes.byref(v)))
+        return v.value
+
+    @reward_offset.setter
+    def reward_offset(self, value):
+        check(self.lib, self.lib.es_set_reward_offset(self.handle, float(value)))
+
+    def score(self, d_ids, offsets, out=None):
+        """Rewards float32[n] (device) of one packed batch; offsets on the host."""
+        torch = _torch()
+        offsets = as_i32(offsets)
+        n = offsets.size - 1
+        if out is None:
+            out = torch.empty(max(n, 0), dtype=torch.float32, device=d_ids.device)
+        check(self.lib, self.lib.es_score_batch(self.handle, _dptr(d_ids, torch.int32, "ids"),
+                                                i32p(offsets), n,
+                                                _dptr(out, torch.float32, "out"), _stream()))
+        return out
+
+    def score_requests(self, d_ids, lengths, batch_overhead=1024, out=None):
+        """Plan, pack, score and scatter a request stream; returns (rewards, stats)."""
+        torch = _torch()
+        lengths = as_i32(lengths)
+        n = lengths.size
+        if out is None:
+            out = torch.empty(n, dtype=torch.float32, device=d_ids.device)
+        stats = _lib.StreamStats()
+        check(self.lib, self.lib.es_score_requests(
+            self.handle, _dptr(d_ids, torch.int32, "ids"), i32p(lengths), n, int(batch_overhead),
+            _dptr(out, torch.float32, "out"), _stream(), ctypes.byref(stats)))
+        return out, {"n_batches": stats.n_batches, "total_cost": stats.total_cost,
+                     "padded_tokens": stats.padded_tokens, "packed_tokens": stats.packed_tokens}
+
+    def hidden(self, d_ids, offsets, n_layers=None):
+        """fp32 residual stream [tokens, hidden] after ``n_layers`` layers (diagnostic)."""
+        torch = _torch()
+        offsets = as_i32(offsets)
+        L = self.info.n_layers if n_layers is None else n_layers
+        out = torch.empty((int(offsets[-1]), self.info.hidden), dtype=torch.float32,
+                          device=d_ids.device)
+        check(self.lib, self.lib.es_forward_hidden(self.handle, _dptr(d_ids, torch.int32, "ids"),
+                                                   i32p(offsets), offsets.size - 1, int(L),
+                                                   _dptr(out, torch.float32, "out"), _stream()))
+        return out
+
+    def calibrate_offset(self, d_ids, offsets):
+        """offset = -mean raw reward of the reference set (does not set it)."""
+        torch = _torch()
+        offsets = as_i32(offsets)
+        v = ctypes.c_float()
+        check(self.lib, self.lib.es_calibrate_offset(self.handle, _dptr(d_ids, torch.int32, "ids"),
+                                                     i32p(offsets), offsets.size - 1, _stream(),
+                                                     ctypes.byref(v)))
+        return v.value
+
+    def check_device_errors(self):
+        check(self.lib, self.lib.es_check_device_errors(self.handle, _stream()))
+
+
+# ------------------------------------------------------------------ single ops
+
+def layernorm(x, gamma, beta, eps, y=None, ybf16=None):
+    """Row LayerNorm of fp32 x [rows, cols] into y (fp32) and/or ybf16 (int16 bits)."""
+    torch = _torch()
+    lib = _lib.load()
+    rows, cols = x.shape
+    ld = ybf16.shape[1] if ybf16 is not None else 0
+    check(lib, lib.es_op_layernorm(
+        _dptr(x, torch.float32, "x"), _dptr(gamma, torch.float32, "gamma"),
+        _dptr(beta, torch.float32, "beta"), rows, cols, float(eps),
+        _dptr(y, torch.float32, "y") if y is not None else None,
+        _dptr(ybf16, torch.int16, "ybf16") if ybf16 is not None else None, ld, _stream()))
+
+
+class RaggedScores:
+    """Ragged score layout of one batch (see es_ragged_create)."""
+
+    def __init__(self, lengths, n_heads, causal):
+        self.lib = _lib.load()
+        self.lengths = as_i32(lengths)
+        self.n_heads, self.causal = int(n_heads), int(bool(causal))
+        h = ctypes.c_void_p()
+        n_el = ctypes.c_int64()
+        check(self.lib, self.lib.es_ragged_create(i32p(self.lengths), self.lengths.size,
+                                                  self.n_heads, self.causal, ctypes.byref(h),
+                                                  ctypes.byref(n_el)))
+        self.handle, self.n_elems = h, n_el.value
+
+    def close(self):
+        if getattr(self, "handle", None):
+            self.lib.es_ragged_free(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def softmax_ragged(rag, scores, probs):
+    """Row softmax over the ragged layout; probs fp32 or int16 (bf16 bits)."""
+    torch = _torch()
+    lib = _lib.load()
+    p_bf16 = probs.dtype == torch.int16
+    check(lib, lib.es_op_softmax(rag.handle, _dptr(scores, torch.float32, "scores"),
+                                 _dptr(probs, probs.dtype, "probs"), int(p_bf16), _stream()))
+
+
+def gemm_bf16(a, w, bias, out, M, N, K, epilogue, res=None):
+    """out = epilogue(A W^T + bias) on the bf16 MFMA kernel (a, w as int16 bits)."""
+    torch = _torch()
+    lib = _lib.load()
+    check(lib, lib.es_op_gemm_bf16(
+        _dptr(a, torch.int16, "a"), a.shape[1], _dptr(w, torch.int16, "w"),
+        _dptr(bias, torch.float32, "bias"),
+        _dptr(res, torch.float32, "res") if res is not None else None,
+        ctypes.c_void_p(out.data_ptr()), out.shape[1], int(M), int(N), int(K), int(epilogue),
+        _stream()))

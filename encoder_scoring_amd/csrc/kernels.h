@@ -1,0 +1,60 @@
+// Launch wrappers for the gfx950 kernels of libencscore (host-callable).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace es {
+
+// Query rows per attention work item; also the row tile of the softmax.
+constexpr int kQTile = 32;
+
+// Device metadata of one packed batch (built on the host per call).
+struct Ragged {
+  const int32_t *off;    // [n_seqs + 1] token offsets, off[0] = 0
+  const int64_t *sbase;  // [n_seqs] first element of sequence i's score blocks
+  const int32_t *items;  // [2 * n_items] (sequence, first query row), kQTile rows each
+  const int32_t *src = nullptr;   // [n_seqs] first id of sequence i in the id buffer (NULL: off)
+  const int32_t *dest = nullptr;  // [n_seqs] reward slot of sequence i (NULL: i)
+  int32_t n_seqs = 0, n_items = 0, max_len = 0, n_tokens = 0;
+};
+
+// Score-block row stride of a sequence of length n (elements).
+__host__ __device__ inline int score_ld(int n) { return (n + 7) & ~7; }
+
+// ---- row kernels (rowops.hip)
+// Embedding gather + position add (+ LayerNorm when `ln`): x fp32 [T, H];
+// xb (bf16 bits or fp32, chosen by `act_bf16`) [T, ldb] when ln.
+hipError_t launch_embed(bool w_bf16, bool act_bf16, bool ln, const int32_t *ids, const Ragged &r,
+                        const void *tok, const void *pos, int vocab, int H, const float *g,
+                        const float *b, float eps, float *x, void *xb, int ldb, int *flag,
+                        hipStream_t st);
+// Row LayerNorm: y fp32 [rows, cols] (nullable), yb [rows, ldb] (nullable).
+hipError_t launch_layernorm(bool act_bf16, const float *x, const float *g, const float *b,
+                            int64_t rows, int cols, float eps, float *y, void *yb, int ldb,
+                            hipStream_t st);
+// Ragged softmax over score blocks: S fp32 -> P (bf16 bits or fp32).
+hipError_t launch_softmax(bool p_bf16, const float *S, void *P, const Ragged &r, int n_heads,
+                          bool causal, hipStream_t st);
+// Reward head on the last token of each sequence (pre_ln: final LN first).
+hipError_t launch_head(bool pre_ln, const float *x, int H, const Ragged &r, const float *g,
+                       const float *b, float eps, const float *w, const float *hb, float offset,
+                       float *rewards, hipStream_t st);
+
+// ---- GEMMs (gemm.hip): out[m, n] = epi(sum_k A[m, k] W[n, k] + bias[n])
+enum Epilogue { kEpiBias = 0, kEpiGelu = 1, kEpiResidual = 2, kEpiF32 = 3 };
+hipError_t launch_gemm_bf16(const uint16_t *A, int lda, const uint16_t *W, const float *bias,
+                            const float *res, void *out, int ldc, int M, int N, int K, int epi,
+                            hipStream_t st);
+hipError_t launch_gemm_f32(const float *A, int lda, const float *W, const float *bias,
+                           const float *res, float *out, int ldc, int M, int N, int K, int epi,
+                           hipStream_t st);
+
+// ---- attention (attn.hip).  qkv [T, ldq]: Q heads at columns h*dp, K at
+// n_heads*dp + h*dp, V at 2*n_heads*dp + h*dp (dp = padded head dim).
+hipError_t launch_scores(bool act_bf16, const void *qkv, int ldq, int n_heads, int dp, float scale,
+                         bool causal, const Ragged &r, float *S, hipStream_t st);
+hipError_t launch_pv(bool act_bf16, const void *P, const void *qkv, int ldq, int n_heads, int dp,
+                     bool causal, const Ragged &r, void *ctx, int ldc, hipStream_t st);
+
+}  // namespace es

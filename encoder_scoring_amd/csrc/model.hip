@@ -1,0 +1,617 @@
+// Model handle, weight upload, per-batch metadata and the forward pass.
+//
+// Data layout in HBM (T = packed tokens of one batch, no padding between
+// sequences; every buffer is sized once for max_tokens rounded up to 256 rows):
+//   x     fp32 [T, H]        residual stream (post-LN: LayerNorm outputs)
+//   y     fp32 [T, H]        GEMM + residual output before a post-LN LayerNorm
+//   xb    act  [T, Hp]       GEMM input copy of the normalised rows
+//   qkv   act  [T, 3*A*dp]   Q | K | V, head h at columns h*dp of each part
+//   ctx   act  [T, Kc]       attention context, head h at columns h*dp
+//   hmid  act  [T, Fp]       GELU(FFN1)
+//   S     fp32 ragged        per (sequence, head) n x ld score blocks
+//   P     act  ragged        softmax output, same indexing as S
+// act = bf16 for bf16 models (fp32 accumulation everywhere), fp32 otherwise.
+// Hp, Kc, Fp round widths up to 64 (zero columns); dp rounds the head dim up
+// to a power of two >= 16 by inserting zero rows into W_qkv and zero columns
+// into W_o, which leaves every result unchanged.
+#include <algorithm>
+#include <cinttypes>
+#include <cmath>
+#include <cstring>
+#include <fstream>
+#include <vector>
+
+#include "blob.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+using es::fail;
+using es::round_up;
+
+#define HIP_TRY(expr)                                                                     \
+  do {                                                                                    \
+    hipError_t _e = (expr);                                                               \
+    if (_e != hipSuccess)                                                                 \
+      return fail(ES_ERR_HIP, "%s failed: %s (%s:%d)", #expr, hipGetErrorString(_e),      \
+                  __FILE__, __LINE__);                                                    \
+  } while (0)
+
+struct DevLayer {
+  void *w_qkv = nullptr, *w_o = nullptr, *w_1 = nullptr, *w_2 = nullptr;
+  float *b_qkv = nullptr, *b_o = nullptr, *ln1_g = nullptr, *ln1_b = nullptr;
+  float *b_1 = nullptr, *b_2 = nullptr, *ln2_g = nullptr, *ln2_b = nullptr;
+};
+
+int pow2_at_least(int v) {
+  int p = 16;
+  while (p < v) p <<= 1;
+  return p;
+}
+
+}  // namespace
+
+struct es_model {
+  // shape
+  int L = 0, H = 0, A = 0, d = 0, dp = 0, F = 0, V = 0, P = 0;
+  bool pre_ln = false, causal = false, bf16 = false;
+  float eps = 0.f, offset = 0.f;
+  int Hp = 0, Nqkv = 0, Kc = 0, Fp = 0;
+  // capacity
+  int64_t max_tokens = 0, Tcap = 0, score_cap = 0;
+  int max_seqs = 0, max_items = 0;
+  int device = 0;
+  // weights
+  void *tok_emb = nullptr, *pos_emb = nullptr;
+  float *norm_g = nullptr, *norm_b = nullptr, *head_w = nullptr, *head_b = nullptr;
+  std::vector<DevLayer> layers;
+  // workspace
+  float *x = nullptr, *y = nullptr, *S = nullptr, *rew = nullptr;
+  void *xb = nullptr, *qkv = nullptr, *ctx = nullptr, *hmid = nullptr, *Pb = nullptr;
+  int *flag = nullptr;
+  // per-call metadata: host assembly -> pinned staging -> one upload
+  std::vector<uint8_t> meta_asm;
+  char *meta_host = nullptr, *meta_dev = nullptr;
+  size_t meta_cap = 0;
+  hipEvent_t meta_ev = nullptr;
+  bool meta_pending = false;
+  std::vector<void *> allocs;
+  int64_t device_bytes = 0;
+  std::vector<int32_t> order_scratch;
+};
+
+namespace {
+
+es_status dalloc(es_model *m, void **p, size_t bytes) {
+  bytes = std::max<size_t>(bytes, 256);
+  hipError_t e = hipMalloc(p, bytes);
+  if (e != hipSuccess)
+    return fail(ES_ERR_HIP, "hipMalloc(%zu) failed: %s", bytes, hipGetErrorString(e));
+  m->allocs.push_back(*p);
+  m->device_bytes += (int64_t)bytes;
+  e = hipMemset(*p, 0, bytes);
+  if (e != hipSuccess) return fail(ES_ERR_HIP, "hipMemset failed: %s", hipGetErrorString(e));
+  return ES_OK;
+}
+
+void release(es_model *m) {
+  if (!m) return;
+  (void)hipDeviceSynchronize();
+  for (void *p : m->allocs) (void)hipFree(p);
+  m->allocs.clear();
+  if (m->meta_host) (void)hipHostFree(m->meta_host);
+  if (m->meta_dev) (void)hipFree(m->meta_dev);
+  if (m->meta_ev) (void)hipEventDestroy(m->meta_ev);
+  delete m;
+}
+
+// Upload a [rows, cols] tensor into a zero-filled [rows_alloc, ld] device matrix
+// of element size `elem`, mapping source row r to destination row rmap(r) and
+// source column c to destination column cmap(c).
+template <typename RM, typename CM>
+es_status upload_matrix(es_model *m, void **dst, const es::TensorView &t, int64_t rows_alloc,
+                        int64_t ld, RM rmap, CM cmap) {
+  const int elem = t.elem;
+  // runs of source columns that stay contiguous after the column map
+  struct Run { int64_t src, dst, len; };
+  std::vector<Run> runs;
+  for (int64_t c = 0; c < t.cols; ++c) {
+    const int64_t dc = cmap(c);
+    if (!runs.empty() && runs.back().src + runs.back().len == c &&
+        runs.back().dst + runs.back().len == dc)
+      ++runs.back().len;
+    else
+      runs.push_back({c, dc, 1});
+  }
+  std::vector<uint8_t> host((size_t)(rows_alloc * ld * elem), 0);
+  const uint8_t *src = static_cast<const uint8_t *>(t.data);
+  for (int64_t r = 0; r < t.rows; ++r) {
+    const int64_t dr = rmap(r);
+    for (const Run &u : runs)
+      std::memcpy(&host[(size_t)((dr * ld + u.dst) * elem)], src + (r * t.cols + u.src) * elem,
+                  (size_t)(u.len * elem));
+  }
+  es_status s = dalloc(m, dst, host.size());
+  if (s != ES_OK) return s;
+  HIP_TRY(hipMemcpy(*dst, host.data(), host.size(), hipMemcpyHostToDevice));
+  return ES_OK;
+}
+
+es_status upload_vec(es_model *m, float **dst, const es::TensorView &t, int64_t n_alloc,
+                     int64_t (*map)(int64_t, const es_model *) = nullptr) {
+  std::vector<float> host((size_t)n_alloc, 0.f);
+  const float *src = static_cast<const float *>(t.data);
+  for (int64_t i = 0; i < t.cols; ++i) host[(size_t)(map ? map(i, m) : i)] = src[i];
+  es_status s = dalloc(m, (void **)dst, host.size() * sizeof(float));
+  if (s != ES_OK) return s;
+  HIP_TRY(hipMemcpy(*dst, host.data(), host.size() * sizeof(float), hipMemcpyHostToDevice));
+  return ES_OK;
+}
+
+// Row r of W_qkv (part p = r / H, head h, dim e) -> head-padded row.
+int64_t qkv_row(int64_t r, const es_model *m) {
+  const int64_t part = r / m->H, rem = r % m->H, h = rem / m->d, e = rem % m->d;
+  return part * m->A * m->dp + h * m->dp + e;
+}
+int64_t ctx_col(int64_t c, const es_model *m) { return (c / m->d) * m->dp + c % m->d; }
+
+es_status build(const es::ParsedBlob &pb, int64_t max_tokens, int32_t max_seqs, es_model *m) {
+  const es::BlobHeader &h = pb.h;
+  m->L = (int)h.n_layers;
+  m->H = (int)h.hidden;
+  m->A = (int)h.n_heads;
+  m->d = m->H / m->A;
+  m->dp = pow2_at_least(m->d);
+  m->F = (int)h.ffn;
+  m->V = (int)h.vocab;
+  m->P = (int)h.max_pos;
+  m->pre_ln = h.pre_ln != 0;
+  m->causal = h.causal != 0;
+  m->bf16 = h.wdtype == 1;
+  m->eps = h.eps;
+  m->offset = h.reward_offset;
+  m->Hp = (int)round_up(m->H, 64);
+  m->Nqkv = 3 * m->A * m->dp;
+  m->Kc = (int)round_up((int64_t)m->A * m->dp, 64);
+  m->Fp = (int)round_up(m->F, 64);
+  m->max_tokens = max_tokens;
+  m->max_seqs = max_seqs;
+  m->Tcap = round_up(max_tokens, 256);
+  const int64_t lmax = std::min<int64_t>(m->P, max_tokens);
+  m->score_cap = (int64_t)m->A * max_tokens * es::score_ld((int)lmax);
+  m->max_items = (int)(max_tokens / es::kQTile + max_seqs + 1);
+  HIP_TRY(hipGetDevice(&m->device));
+
+  const int act = m->bf16 ? 2 : 4;
+  es_status s;
+  auto id = [](int64_t r) { return r; };
+  // embeddings keep their natural [rows, H] layout
+  if ((s = upload_matrix(m, &m->tok_emb, pb.tok_emb, m->V, m->H, id, id)) != ES_OK) return s;
+  if ((s = upload_matrix(m, &m->pos_emb, pb.pos_emb, m->P, m->H, id, id)) != ES_OK) return s;
+  if ((s = upload_vec(m, &m->norm_g, pb.norm_g, m->H)) != ES_OK) return s;
+  if ((s = upload_vec(m, &m->norm_b, pb.norm_b, m->H)) != ES_OK) return s;
+  if ((s = upload_vec(m, &m->head_w, pb.head_w, m->H)) != ES_OK) return s;
+  if ((s = upload_vec(m, &m->head_b, pb.head_b, 1)) != ES_OK) return s;
+  m->layers.assign(m->L, DevLayer{});
+  const es_model *cm = m;
+  for (int l = 0; l < m->L; ++l) {
+    const es::LayerViews &L = pb.layers[l];
+    DevLayer &D = m->layers[l];
+    auto qrow = [cm](int64_t r) { return qkv_row(r, cm); };
+    auto ccol = [cm](int64_t c) { return ctx_col(c, cm); };
+    if ((s = upload_matrix(m, &D.w_qkv, L.w_qkv, round_up(m->Nqkv, 256), m->Hp, qrow, id)) != ES_OK) return s;
+    if ((s = upload_vec(m, &D.b_qkv, L.b_qkv, m->Nqkv, qkv_row)) != ES_OK) return s;
+    if ((s = upload_matrix(m, &D.w_o, L.w_o, round_up(m->H, 256), m->Kc, id, ccol)) != ES_OK) return s;
+    if ((s = upload_vec(m, &D.b_o, L.b_o, m->H)) != ES_OK) return s;
+    if ((s = upload_vec(m, &D.ln1_g, L.ln1_g, m->H)) != ES_OK) return s;
+    if ((s = upload_vec(m, &D.ln1_b, L.ln1_b, m->H)) != ES_OK) return s;
+    if ((s = upload_matrix(m, &D.w_1, L.w_1, round_up(m->F, 256), m->Hp, id, id)) != ES_OK) return s;
+    if ((s = upload_vec(m, &D.b_1, L.b_1, m->F)) != ES_OK) return s;
+    if ((s = upload_matrix(m, &D.w_2, L.w_2, round_up(m->H, 256), m->Fp, id, id)) != ES_OK) return s;
+    if ((s = upload_vec(m, &D.b_2, L.b_2, m->H)) != ES_OK) return s;
+    if ((s = upload_vec(m, &D.ln2_g, L.ln2_g, m->H)) != ES_OK) return s;
+    if ((s = upload_vec(m, &D.ln2_b, L.ln2_b, m->H)) != ES_OK) return s;
+  }
+  // workspace (zero-filled once: padding columns stay zero forever)
+  const int64_t T = m->Tcap;
+  if ((s = dalloc(m, (void **)&m->x, T * m->H * 4)) != ES_OK) return s;
+  if ((s = dalloc(m, (void **)&m->y, T * m->H * 4)) != ES_OK) return s;
+  if ((s = dalloc(m, &m->xb, T * m->Hp * act)) != ES_OK) return s;
+  if ((s = dalloc(m, &m->qkv, T * m->Nqkv * act)) != ES_OK) return s;
+  if ((s = dalloc(m, &m->ctx, T * m->Kc * act)) != ES_OK) return s;
+  if ((s = dalloc(m, &m->hmid, T * m->Fp * act)) != ES_OK) return s;
+  if ((s = dalloc(m, (void **)&m->S, m->score_cap * 4)) != ES_OK) return s;
+  if ((s = dalloc(m, &m->Pb, m->score_cap * act)) != ES_OK) return s;
+  if ((s = dalloc(m, (void **)&m->rew, (size_t)m->max_seqs * 4)) != ES_OK) return s;
+  if ((s = dalloc(m, (void **)&m->flag, 4)) != ES_OK) return s;
+  HIP_TRY(hipEventCreateWithFlags(&m->meta_ev, hipEventDisableTiming));
+  HIP_TRY(hipDeviceSynchronize());
+  return ES_OK;
+}
+
+// ---- per-call metadata.  Every batch of a call gets offsets, score-block
+// bases, attention work items and (optionally) id-source / reward-slot maps,
+// assembled on the host, staged in pinned memory and uploaded in ONE copy.
+struct BatchLayout {
+  size_t off = 0, sbase = 0, items = 0, src = 0, dest = 0;
+  bool has_src = false, has_dest = false;
+  int n = 0, n_items = 0, max_len = 0, n_tokens = 0;
+};
+
+size_t push_bytes(std::vector<uint8_t> &buf, const void *p, size_t bytes) {
+  const size_t at = (size_t)round_up((int64_t)buf.size(), 16);
+  buf.resize(at + bytes);
+  if (bytes) std::memcpy(buf.data() + at, p, bytes);
+  return at;
+}
+
+// Validate one batch's host offsets and append its metadata to m->meta_asm.
+es_status add_batch(es_model *m, const int32_t *h_off, int32_t n, const int32_t *src,
+                    const int32_t *dest, BatchLayout *L) {
+  if (!h_off) return fail(ES_ERR_ARG, "offsets pointer is NULL");
+  if (n < 1) return fail(ES_ERR_ARG, "n_seqs=%d < 1", n);
+  if (n > m->max_seqs) return fail(ES_ERR_CAPACITY, "n_seqs=%d above max_seqs=%d", n, m->max_seqs);
+  if (h_off[0] != 0) return fail(ES_ERR_ARG, "offsets[0]=%d, must be 0", h_off[0]);
+  int max_len = 0;
+  int64_t score = 0;
+  std::vector<int64_t> sbase((size_t)n);
+  for (int32_t i = 0; i < n; ++i) {
+    const int64_t len = (int64_t)h_off[i + 1] - h_off[i];
+    if (len < 1) return fail(ES_ERR_ARG, "offsets not strictly increasing at %d", i);
+    if (len > m->P)
+      return fail(ES_ERR_RANGE, "sequence %d has length %" PRId64 " > max_pos=%d", i, len, m->P);
+    if (h_off[i + 1] > m->max_tokens)
+      return fail(ES_ERR_CAPACITY, "batch has more than max_tokens=%" PRId64 " tokens", m->max_tokens);
+    max_len = std::max<int>(max_len, (int)len);
+    sbase[i] = score;
+    score += (int64_t)m->A * len * es::score_ld((int)len);
+  }
+  if (score > m->score_cap)
+    return fail(ES_ERR_CAPACITY, "batch needs %" PRId64 " score elements (capacity %" PRId64 ")",
+                score, m->score_cap);
+  // attention work items, longest sequences first
+  auto &ord = m->order_scratch;
+  ord.resize(n);
+  for (int32_t i = 0; i < n; ++i) ord[i] = i;
+  std::stable_sort(ord.begin(), ord.end(), [&](int32_t a, int32_t b) {
+    return h_off[a + 1] - h_off[a] > h_off[b + 1] - h_off[b];
+  });
+  std::vector<int32_t> items;
+  for (int32_t sq : ord) {
+    const int len = h_off[sq + 1] - h_off[sq];
+    for (int q0 = 0; q0 < len; q0 += es::kQTile) {
+      items.push_back(sq);
+      items.push_back(q0);
+    }
+  }
+  auto &buf = m->meta_asm;
+  L->off = push_bytes(buf, h_off, sizeof(int32_t) * (n + 1));
+  L->sbase = push_bytes(buf, sbase.data(), sizeof(int64_t) * n);
+  L->items = push_bytes(buf, items.data(), sizeof(int32_t) * items.size());
+  L->has_src = src != nullptr;
+  L->has_dest = dest != nullptr;
+  if (src) L->src = push_bytes(buf, src, sizeof(int32_t) * n);
+  if (dest) L->dest = push_bytes(buf, dest, sizeof(int32_t) * n);
+  L->n = n;
+  L->n_items = (int)(items.size() / 2);
+  L->max_len = max_len;
+  L->n_tokens = h_off[n];
+  return ES_OK;
+}
+
+// Stage m->meta_asm in pinned memory and enqueue its upload on `st`.
+es_status upload_meta(es_model *m, hipStream_t st) {
+  const size_t bytes = std::max<size_t>(m->meta_asm.size(), 16);
+  // the previous call's upload must have left the staging buffer
+  if (m->meta_pending) HIP_TRY(hipEventSynchronize(m->meta_ev));
+  m->meta_pending = false;
+  if (bytes > m->meta_cap) {
+    const size_t cap = (size_t)round_up((int64_t)(bytes + bytes / 2), 4096);
+    if (m->meta_dev) {
+      HIP_TRY(hipStreamSynchronize(st));  // device copy may still be read by queued kernels
+      HIP_TRY(hipDeviceSynchronize());
+      HIP_TRY(hipFree(m->meta_dev));
+      m->meta_dev = nullptr;
+    }
+    if (m->meta_host) {
+      HIP_TRY(hipHostFree(m->meta_host));
+      m->meta_host = nullptr;
+    }
+    m->meta_cap = 0;
+    HIP_TRY(hipMalloc((void **)&m->meta_dev, cap));
+    HIP_TRY(hipHostMalloc((void **)&m->meta_host, cap, hipHostMallocDefault));
+    m->meta_cap = cap;
+  }
+  std::memcpy(m->meta_host, m->meta_asm.data(), m->meta_asm.size());
+  HIP_TRY(hipMemcpyAsync(m->meta_dev, m->meta_host, bytes, hipMemcpyHostToDevice, st));
+  HIP_TRY(hipEventRecord(m->meta_ev, st));
+  m->meta_pending = true;
+  return ES_OK;
+}
+
+es::Ragged ragged_of(const es_model *m, const BatchLayout &L) {
+  es::Ragged r;
+  r.off = reinterpret_cast<const int32_t *>(m->meta_dev + L.off);
+  r.sbase = reinterpret_cast<const int64_t *>(m->meta_dev + L.sbase);
+  r.items = reinterpret_cast<const int32_t *>(m->meta_dev + L.items);
+  r.src = L.has_src ? reinterpret_cast<const int32_t *>(m->meta_dev + L.src) : nullptr;
+  r.dest = L.has_dest ? reinterpret_cast<const int32_t *>(m->meta_dev + L.dest) : nullptr;
+  r.n_seqs = L.n;
+  r.n_items = L.n_items;
+  r.max_len = L.max_len;
+  r.n_tokens = L.n_tokens;
+  return r;
+}
+
+// One batch given by host offsets: validate, stage, upload.
+es_status prepare(es_model *m, const int32_t *h_off, int32_t n, hipStream_t st, es::Ragged *r) {
+  m->meta_asm.clear();
+  BatchLayout L;
+  es_status s = add_batch(m, h_off, n, nullptr, nullptr, &L);
+  if (s != ES_OK) return s;
+  if ((s = upload_meta(m, st)) != ES_OK) return s;
+  *r = ragged_of(m, L);
+  return ES_OK;
+}
+
+es_status gemm(es_model *m, const void *A, int lda, const void *W, const float *bias,
+               const float *res, void *out, int ldc, int M, int N, int K, int epi, hipStream_t st) {
+  if (m->bf16)
+    HIP_TRY(es::launch_gemm_bf16((const uint16_t *)A, lda, (const uint16_t *)W, bias, res, out, ldc,
+                                 M, N, K, epi, st));
+  else
+    HIP_TRY(es::launch_gemm_f32((const float *)A, lda, (const float *)W, bias, res, (float *)out, ldc,
+                                M, N, K, epi, st));
+  return ES_OK;
+}
+
+es_status attention(es_model *m, const es::Ragged &r, hipStream_t st) {
+  const float scale = 1.0f / std::sqrt((float)m->d);
+  HIP_TRY(es::launch_scores(m->bf16, m->qkv, m->Nqkv, m->A, m->dp, scale, m->causal, r, m->S, st));
+  HIP_TRY(es::launch_softmax(m->bf16, m->S, m->Pb, r, m->A, m->causal, st));
+  HIP_TRY(es::launch_pv(m->bf16, m->Pb, m->qkv, m->Nqkv, m->A, m->dp, m->causal, r, m->ctx, m->Kc, st));
+  return ES_OK;
+}
+
+es_status forward(es_model *m, const int32_t *d_ids, const es::Ragged &r, int n_layers,
+                  hipStream_t st) {
+  const int T = r.n_tokens, H = m->H;
+  es_status s;
+  HIP_TRY(es::launch_embed(m->bf16, m->bf16, !m->pre_ln, d_ids, r, m->tok_emb, m->pos_emb, m->V, H,
+                           m->norm_g, m->norm_b, m->eps, m->x, m->xb, m->Hp, m->flag, st));
+  for (int l = 0; l < n_layers; ++l) {
+    const DevLayer &D = m->layers[l];
+    if (!m->pre_ln) {
+      if ((s = gemm(m, m->xb, m->Hp, D.w_qkv, D.b_qkv, nullptr, m->qkv, m->Nqkv, T, m->Nqkv, m->Hp,
+                    es::kEpiBias, st)) != ES_OK) return s;
+      if ((s = attention(m, r, st)) != ES_OK) return s;
+      if ((s = gemm(m, m->ctx, m->Kc, D.w_o, D.b_o, m->x, m->y, H, T, H, m->Kc, es::kEpiResidual,
+                    st)) != ES_OK) return s;
+      HIP_TRY(es::launch_layernorm(m->bf16, m->y, D.ln1_g, D.ln1_b, T, H, m->eps, m->x, m->xb, m->Hp, st));
+      if ((s = gemm(m, m->xb, m->Hp, D.w_1, D.b_1, nullptr, m->hmid, m->Fp, T, m->F, m->Hp,
+                    es::kEpiGelu, st)) != ES_OK) return s;
+      if ((s = gemm(m, m->hmid, m->Fp, D.w_2, D.b_2, m->x, m->y, H, T, H, m->Fp, es::kEpiResidual,
+                    st)) != ES_OK) return s;
+      HIP_TRY(es::launch_layernorm(m->bf16, m->y, D.ln2_g, D.ln2_b, T, H, m->eps, m->x, m->xb, m->Hp, st));
+    } else {
+      HIP_TRY(es::launch_layernorm(m->bf16, m->x, D.ln1_g, D.ln1_b, T, H, m->eps, nullptr, m->xb, m->Hp, st));
+      if ((s = gemm(m, m->xb, m->Hp, D.w_qkv, D.b_qkv, nullptr, m->qkv, m->Nqkv, T, m->Nqkv, m->Hp,
+                    es::kEpiBias, st)) != ES_OK) return s;
+      if ((s = attention(m, r, st)) != ES_OK) return s;
+      if ((s = gemm(m, m->ctx, m->Kc, D.w_o, D.b_o, m->x, m->x, H, T, H, m->Kc, es::kEpiResidual,
+                    st)) != ES_OK) return s;
+      HIP_TRY(es::launch_layernorm(m->bf16, m->x, D.ln2_g, D.ln2_b, T, H, m->eps, nullptr, m->xb, m->Hp, st));
+      if ((s = gemm(m, m->xb, m->Hp, D.w_1, D.b_1, nullptr, m->hmid, m->Fp, T, m->F, m->Hp,
+                    es::kEpiGelu, st)) != ES_OK) return s;
+      if ((s = gemm(m, m->hmid, m->Fp, D.w_2, D.b_2, m->x, m->x, H, T, H, m->Fp, es::kEpiResidual,
+                    st)) != ES_OK) return s;
+    }
+  }
+  return ES_OK;
+}
+
+es_status check_model(const es_model *m) {
+  if (!m) return fail(ES_ERR_ARG, "model handle is NULL");
+  return ES_OK;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ C ABI
+
+extern "C" es_status es_load_weights_mem(const void *h_blob, int64_t nbytes, int64_t max_tokens,
+                                         int32_t max_seqs, es_model **out) {
+  if (!out) return fail(ES_ERR_ARG, "out is NULL");
+  *out = nullptr;
+  if (max_tokens < 1 || max_tokens > (int64_t)1 << 28)
+    return fail(ES_ERR_ARG, "max_tokens=%" PRId64 " outside [1, 2^28]", max_tokens);
+  if (max_seqs < 1 || max_seqs > (1 << 24)) return fail(ES_ERR_ARG, "max_seqs=%d outside [1, 2^24]", max_seqs);
+  es::ParsedBlob pb;
+  es_status s = es::parse_blob(h_blob, nbytes, &pb);
+  if (s != ES_OK) return s;
+  es_model *m = new es_model();
+  s = build(pb, max_tokens, max_seqs, m);
+  if (s != ES_OK) {
+    release(m);
+    return s;
+  }
+  *out = m;
+  es::clear_error();
+  return ES_OK;
+}
+
+extern "C" es_status es_load_weights(const char *blob_path, int64_t max_tokens, int32_t max_seqs,
+                                     es_model **out) {
+  if (!blob_path || !out) return fail(ES_ERR_ARG, "NULL path or out");
+  std::ifstream f(blob_path, std::ios::binary | std::ios::ate);
+  if (!f) return fail(ES_ERR_IO, "cannot open %s", blob_path);
+  const std::streamsize size = f.tellg();
+  f.seekg(0);
+  std::vector<char> buf((size_t)size);
+  if (!f.read(buf.data(), size)) return fail(ES_ERR_IO, "cannot read %s", blob_path);
+  return es_load_weights_mem(buf.data(), (int64_t)size, max_tokens, max_seqs, out);
+}
+
+extern "C" void es_free(es_model *m) { release(m); }
+
+extern "C" es_status es_model_info(const es_model *m, es_model_info_t *info) {
+  if (!m || !info) return fail(ES_ERR_ARG, "NULL argument");
+  info->n_layers = m->L;
+  info->hidden = m->H;
+  info->n_heads = m->A;
+  info->head_dim = m->d;
+  info->ffn = m->F;
+  info->vocab = m->V;
+  info->max_pos = m->P;
+  info->pre_ln = m->pre_ln;
+  info->causal = m->causal;
+  info->bf16 = m->bf16;
+  info->eps = m->eps;
+  info->reward_offset = m->offset;
+  info->max_tokens = m->max_tokens;
+  info->max_seqs = m->max_seqs;
+  info->device_bytes = m->device_bytes;
+  return ES_OK;
+}
+
+extern "C" es_status es_score_batch(es_model *m, const int32_t *d_token_ids, const int32_t *h_offsets,
+                                    int32_t n_seqs, float *d_rewards, void *stream) {
+  es_status s = check_model(m);
+  if (s != ES_OK) return s;
+  if (!d_token_ids || !d_rewards) return fail(ES_ERR_ARG, "NULL device pointer");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  es::Ragged r;
+  if ((s = prepare(m, h_offsets, n_seqs, st, &r)) != ES_OK) return s;
+  if ((s = forward(m, d_token_ids, r, m->L, st)) != ES_OK) return s;
+  HIP_TRY(es::launch_head(m->pre_ln, m->x, m->H, r, m->norm_g, m->norm_b, m->eps, m->head_w,
+                          m->head_b, m->offset, d_rewards, st));
+  es::clear_error();
+  return ES_OK;
+}
+
+extern "C" es_status es_score_requests(es_model *m, const int32_t *d_token_ids,
+                                       const int32_t *h_lengths, int32_t n, int64_t batch_overhead,
+                                       float *d_rewards, void *stream, es_stream_stats_t *stats) {
+  es_status s = check_model(m);
+  if (s != ES_OK) return s;
+  if (!d_token_ids || !d_rewards || !h_lengths) return fail(ES_ERR_ARG, "NULL argument");
+  if (n < 1) return fail(ES_ERR_ARG, "n=%d < 1", n);
+  for (int32_t i = 0; i < n; ++i)
+    if (h_lengths[i] < 1 || h_lengths[i] > m->P)
+      return fail(ES_ERR_RANGE, "lengths[%d]=%d outside [1, max_pos=%d]", i, h_lengths[i], m->P);
+  // a1: plan over the whole stream (host DP), budget = the workspace size
+  std::vector<int32_t> order((size_t)n), starts((size_t)n + 1);
+  int32_t nb = 0;
+  int64_t cost = 0;
+  if ((s = es_plan_batches(h_lengths, n, m->max_tokens, batch_overhead, order.data(),
+                           starts.data(), &nb, &cost)) != ES_OK)
+    return s;
+  // request-order start of every sequence's ids in d_token_ids
+  std::vector<int32_t> first((size_t)n);
+  int64_t acc = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    first[i] = (int32_t)acc;
+    acc += h_lengths[i];
+    if (acc > INT32_MAX) return fail(ES_ERR_RANGE, "more than INT32_MAX tokens in one call");
+  }
+  // a2: pack -- per batch, offsets over the plan order plus id-source and reward-slot maps
+  m->meta_asm.clear();
+  std::vector<BatchLayout> layouts((size_t)nb);
+  std::vector<int32_t> off, src, dest;
+  int64_t padded = 0;
+  for (int32_t b = 0; b < nb; ++b) {
+    const int32_t lo = starts[b], hi = starts[b + 1], k = hi - lo;
+    off.assign((size_t)k + 1, 0);
+    src.resize((size_t)k);
+    dest.resize((size_t)k);
+    if ((s = es_pack_offsets(h_lengths, order.data(), lo, hi, off.data())) != ES_OK) return s;
+    for (int32_t j = 0; j < k; ++j) {
+      src[j] = first[order[lo + j]];
+      dest[j] = order[lo + j];
+    }
+    padded += (int64_t)k * h_lengths[order[hi - 1]];
+    if ((s = add_batch(m, off.data(), k, src.data(), dest.data(), &layouts[b])) != ES_OK) return s;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if ((s = upload_meta(m, st)) != ES_OK) return s;
+  // a3..a13: every batch through the layers; the head scatters to request order
+  for (int32_t b = 0; b < nb; ++b) {
+    const es::Ragged r = ragged_of(m, layouts[b]);
+    if ((s = forward(m, d_token_ids, r, m->L, st)) != ES_OK) return s;
+    HIP_TRY(es::launch_head(m->pre_ln, m->x, m->H, r, m->norm_g, m->norm_b, m->eps, m->head_w,
+                            m->head_b, m->offset, d_rewards, st));
+  }
+  if (stats) {
+    stats->n_batches = nb;
+    stats->total_cost = cost;
+    stats->padded_tokens = padded;
+    stats->packed_tokens = acc;
+  }
+  es::clear_error();
+  return ES_OK;
+}
+
+extern "C" es_status es_forward_hidden(es_model *m, const int32_t *d_token_ids,
+                                       const int32_t *h_offsets, int32_t n_seqs, int32_t n_layers,
+                                       float *d_hidden, void *stream) {
+  es_status s = check_model(m);
+  if (s != ES_OK) return s;
+  if (!d_token_ids || !d_hidden) return fail(ES_ERR_ARG, "NULL device pointer");
+  if (n_layers < 0 || n_layers > m->L) return fail(ES_ERR_ARG, "n_layers=%d outside [0, %d]", n_layers, m->L);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  es::Ragged r;
+  if ((s = prepare(m, h_offsets, n_seqs, st, &r)) != ES_OK) return s;
+  if ((s = forward(m, d_token_ids, r, n_layers, st)) != ES_OK) return s;
+  HIP_TRY(hipMemcpyAsync(d_hidden, m->x, (size_t)r.n_tokens * m->H * 4, hipMemcpyDeviceToDevice, st));
+  return ES_OK;
+}
+
+extern "C" es_status es_set_reward_offset(es_model *m, float offset) {
+  if (!m) return fail(ES_ERR_ARG, "model handle is NULL");
+  if (!std::isfinite(offset)) return fail(ES_ERR_ARG, "offset is not finite");
+  m->offset = offset;
+  return ES_OK;
+}
+
+extern "C" es_status es_get_reward_offset(const es_model *m, float *offset) {
+  if (!m || !offset) return fail(ES_ERR_ARG, "NULL argument");
+  *offset = m->offset;
+  return ES_OK;
+}
+
+extern "C" es_status es_calibrate_offset(es_model *m, const int32_t *d_token_ids,
+                                         const int32_t *h_offsets, int32_t n_ref, void *stream,
+                                         float *offset_out) {
+  es_status s = check_model(m);
+  if (s != ES_OK) return s;
+  if (!offset_out || !d_token_ids) return fail(ES_ERR_ARG, "NULL argument");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  es::Ragged r;
+  if ((s = prepare(m, h_offsets, n_ref, st, &r)) != ES_OK) return s;
+  if ((s = forward(m, d_token_ids, r, m->L, st)) != ES_OK) return s;
+  HIP_TRY(es::launch_head(m->pre_ln, m->x, m->H, r, m->norm_g, m->norm_b, m->eps, m->head_w,
+                          m->head_b, 0.0f, m->rew, st));
+  std::vector<float> raw((size_t)n_ref);
+  HIP_TRY(hipMemcpyAsync(raw.data(), m->rew, raw.size() * 4, hipMemcpyDeviceToHost, st));
+  HIP_TRY(hipStreamSynchronize(st));
+  double acc = 0.0;
+  for (float v : raw) acc += v;
+  *offset_out = (float)(-(acc / n_ref));
+  return ES_OK;
+}
+
+extern "C" es_status es_check_device_errors(es_model *m, void *stream) {
+  es_status s = check_model(m);
+  if (s != ES_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int flag = 0;
+  HIP_TRY(hipMemcpyAsync(&flag, m->flag, 4, hipMemcpyDeviceToHost, st));
+  HIP_TRY(hipStreamSynchronize(st));
+  if (flag) {
+    HIP_TRY(hipMemsetAsync(m->flag, 0, 4, st));
+    HIP_TRY(hipStreamSynchronize(st));
+    return fail(ES_ERR_DEVICE_FLAG, "a token id outside [0, %d) was seen (row 0 used instead)", m->V);
+  }
+  return ES_OK;
+}

@@ -1,0 +1,116 @@
+// Single-kernel entry points: the LayerNorm, Softmax and GEMM kernels of the
+// hot path on caller buffers, for per-kernel parity tests and measurement.
+#include <cinttypes>
+#include <vector>
+
+#include "common.h"
+#include "kernels.h"
+
+using es::fail;
+
+#define HIP_TRY(expr)                                                                     \
+  do {                                                                                    \
+    hipError_t _e = (expr);                                                               \
+    if (_e != hipSuccess)                                                                 \
+      return fail(ES_ERR_HIP, "%s failed: %s", #expr, hipGetErrorString(_e));             \
+  } while (0)
+
+struct es_ragged {
+  void *dev = nullptr;  // off | sbase | items
+  es::Ragged r;
+  int n_heads = 0, causal = 0;
+};
+
+extern "C" es_status es_op_layernorm(const float *d_x, const float *d_gamma, const float *d_beta,
+                                     int64_t rows, int32_t cols, float eps, float *d_y,
+                                     uint16_t *d_ybf16, int32_t ld_bf16, void *stream) {
+  if (!d_x || !d_gamma || !d_beta || (!d_y && !d_ybf16))
+    return fail(ES_ERR_ARG, "es_op_layernorm: NULL pointer");
+  if (rows < 0 || cols < 4 || cols % 4 || cols > 8192 || (d_ybf16 && (ld_bf16 < cols || ld_bf16 % 4)))
+    return fail(ES_ERR_ARG, "es_op_layernorm: rows=%" PRId64 " cols=%d ld_bf16=%d", rows, cols, ld_bf16);
+  HIP_TRY(es::launch_layernorm(true, d_x, d_gamma, d_beta, rows, cols, eps, d_y, d_ybf16, ld_bf16,
+                               static_cast<hipStream_t>(stream)));
+  return ES_OK;
+}
+
+extern "C" es_status es_ragged_create(const int32_t *h_lengths, int32_t n_seqs, int32_t n_heads,
+                                      int32_t causal, es_ragged **out, int64_t *n_elems) {
+  if (!h_lengths || !out || n_seqs < 1 || n_heads < 1 || (causal != 0 && causal != 1))
+    return fail(ES_ERR_ARG, "es_ragged_create: bad arguments");
+  *out = nullptr;
+  std::vector<int32_t> off(n_seqs + 1, 0);
+  std::vector<int64_t> sbase(n_seqs);
+  std::vector<int32_t> items;
+  int64_t acc = 0;
+  int max_len = 0;
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    const int n = h_lengths[i];
+    if (n < 1 || n > 4096) return fail(ES_ERR_RANGE, "es_ragged_create: length %d outside [1, 4096]", n);
+    if ((int64_t)off[i] + n > INT32_MAX) return fail(ES_ERR_RANGE, "es_ragged_create: too many tokens");
+    off[i + 1] = off[i] + n;
+    sbase[i] = acc;
+    acc += (int64_t)n_heads * n * es::score_ld(n);
+    max_len = max_len > n ? max_len : n;
+    for (int q0 = 0; q0 < n; q0 += es::kQTile) {
+      items.push_back(i);
+      items.push_back(q0);
+    }
+  }
+  const size_t b_off = es::round_up((int64_t)off.size() * 4, 16);
+  const size_t b_sb = es::round_up((int64_t)sbase.size() * 8, 16);
+  const size_t bytes = b_off + b_sb + items.size() * 4;
+  es_ragged *g = new es_ragged();
+  hipError_t e = hipMalloc(&g->dev, bytes);
+  if (e == hipSuccess) e = hipMemcpy(g->dev, off.data(), off.size() * 4, hipMemcpyHostToDevice);
+  if (e == hipSuccess)
+    e = hipMemcpy((char *)g->dev + b_off, sbase.data(), sbase.size() * 8, hipMemcpyHostToDevice);
+  if (e == hipSuccess)
+    e = hipMemcpy((char *)g->dev + b_off + b_sb, items.data(), items.size() * 4, hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    if (g->dev) (void)hipFree(g->dev);
+    delete g;
+    return fail(ES_ERR_HIP, "es_ragged_create: %s", hipGetErrorString(e));
+  }
+  g->r.off = (const int32_t *)g->dev;
+  g->r.sbase = (const int64_t *)((char *)g->dev + b_off);
+  g->r.items = (const int32_t *)((char *)g->dev + b_off + b_sb);
+  g->r.n_seqs = n_seqs;
+  g->r.n_items = (int32_t)(items.size() / 2);
+  g->r.max_len = max_len;
+  g->r.n_tokens = off[n_seqs];
+  g->n_heads = n_heads;
+  g->causal = causal;
+  if (n_elems) *n_elems = acc;
+  *out = g;
+  return ES_OK;
+}
+
+extern "C" void es_ragged_free(es_ragged *r) {
+  if (!r) return;
+  (void)hipDeviceSynchronize();
+  (void)hipFree(r->dev);
+  delete r;
+}
+
+extern "C" es_status es_op_softmax(const es_ragged *r, const float *d_scores, void *d_p,
+                                   int32_t p_bf16, void *stream) {
+  if (!r || !d_scores || !d_p) return fail(ES_ERR_ARG, "es_op_softmax: NULL pointer");
+  HIP_TRY(es::launch_softmax(p_bf16 != 0, d_scores, d_p, r->r, r->n_heads, r->causal != 0,
+                             static_cast<hipStream_t>(stream)));
+  return ES_OK;
+}
+
+extern "C" es_status es_op_gemm_bf16(const uint16_t *d_a, int32_t lda, const uint16_t *d_w,
+                                     const float *d_bias, const float *d_res, void *d_out,
+                                     int32_t ldc, int32_t M, int32_t N, int32_t K, int32_t epilogue,
+                                     void *stream) {
+  if (!d_a || !d_w || !d_bias || !d_out || (epilogue == es::kEpiResidual && !d_res))
+    return fail(ES_ERR_ARG, "es_op_gemm_bf16: NULL pointer");
+  if (M < 0 || N < 0 || K <= 0 || K % 64 || lda < K || lda % 8 || ldc < N || epilogue < 0 ||
+      epilogue > 3)
+    return fail(ES_ERR_ARG, "es_op_gemm_bf16: M=%d N=%d K=%d lda=%d ldc=%d epilogue=%d", M, N, K,
+                lda, ldc, epilogue);
+  HIP_TRY(es::launch_gemm_bf16(d_a, lda, d_w, d_bias, d_res, d_out, ldc, M, N, K, epilogue,
+                               static_cast<hipStream_t>(stream)));
+  return ES_OK;
+}

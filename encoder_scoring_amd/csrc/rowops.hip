@@ -1,0 +1,323 @@
+// Row kernels: embedding (+LN), LayerNorm, ragged Softmax, reward head.
+//
+// TurboTransformers review (Proposed method): Softmax and LayerNorm are the
+// hot spots besides the GEMMs and are computed as parallel per-row ("batch")
+// reductions.  On gfx950 each row (or group of short rows) is owned by one
+// 64-lane wavefront: coalesced 16-byte loads straight into registers, one
+// pass over HBM in and out, reductions by butterfly shuffles inside the
+// wavefront, no barriers.
+#include "device.h"
+#include "kernels.h"
+
+namespace es {
+
+namespace {
+
+constexpr int kRowsPerBlock = 4;  // one row per wavefront, 4 wavefronts per block
+
+__device__ __forceinline__ float4 load4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
+__device__ __forceinline__ float4 load4(const uint16_t *p) {
+  const uint2 u = *reinterpret_cast<const uint2 *>(p);
+  return make_float4(bf2f(u.x & 0xffff), bf2f(u.x >> 16), bf2f(u.y & 0xffff), bf2f(u.y >> 16));
+}
+__device__ __forceinline__ void store4(float *p, float4 v) { *reinterpret_cast<float4 *>(p) = v; }
+__device__ __forceinline__ void store4(uint16_t *p, float4 v) {
+  uint2 u;
+  u.x = (uint32_t)f2bf(v.x) | ((uint32_t)f2bf(v.y) << 16);
+  u.y = (uint32_t)f2bf(v.z) | ((uint32_t)f2bf(v.w) << 16);
+  *reinterpret_cast<uint2 *>(p) = u;
+}
+
+// LayerNorm of one row held as NC float4 chunks per lane (chunk c4 = lane + 64 j).
+// Two passes over registers: mean, then the biased variance of (x - mean).
+template <int NC>
+__device__ __forceinline__ void ln_row(float4 (&v)[NC], int lane, int c4n, int cols,
+                                       const float *__restrict__ g, const float *__restrict__ b,
+                                       float eps) {
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < NC; ++j)
+    if (lane + kWave * j < c4n) s += (v[j].x + v[j].y) + (v[j].z + v[j].w);
+  const float mean = wave_sum(s) / (float)cols;
+  float s2 = 0.f;
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    if (lane + kWave * j < c4n) {
+      const float a = v[j].x - mean, bb = v[j].y - mean, c = v[j].z - mean, d = v[j].w - mean;
+      s2 += (a * a + bb * bb) + (c * c + d * d);
+    }
+  }
+  const float var = wave_sum(s2) / (float)cols;
+  const float rstd = 1.0f / sqrtf(var + eps);
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    const int c4 = lane + kWave * j;
+    if (c4 < c4n) {
+      const float4 gg = load4(g + 4 * c4), bb = load4(b + 4 * c4);
+      v[j].x = (v[j].x - mean) * rstd * gg.x + bb.x;
+      v[j].y = (v[j].y - mean) * rstd * gg.y + bb.y;
+      v[j].z = (v[j].z - mean) * rstd * gg.z + bb.z;
+      v[j].w = (v[j].w - mean) * rstd * gg.w + bb.w;
+    }
+  }
+}
+
+template <int NC, typename OutB>
+__global__ __launch_bounds__(256) void layernorm_kernel(const float *x, const float *__restrict__ g,
+                                                        const float *__restrict__ b, int64_t rows,
+                                                        int cols, float eps, float *y, OutB *yb,
+                                                        int ldb) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int c4n = cols >> 2;
+  const float *xr = x + row * cols;
+  float4 v[NC];
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    const int c4 = lane + kWave * j;
+    v[j] = c4 < c4n ? load4(xr + 4 * c4) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  ln_row<NC>(v, lane, c4n, cols, g, b, eps);
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    const int c4 = lane + kWave * j;
+    if (c4 < c4n) {
+      if (y) store4(y + row * cols + 4 * c4, v[j]);
+      if (yb) store4(yb + row * ldb + 4 * c4, v[j]);
+    }
+  }
+}
+
+// Token t of the packed batch belongs to sequence s; its id is read at
+// src[s] + position, so a batch can be gathered straight out of a request
+// stream kept in arrival order (the packing step costs no extra copy).
+template <int NC, typename W, bool LN, typename OutB>
+__global__ __launch_bounds__(256) void embed_kernel(const int32_t *__restrict__ ids,
+                                                    const int32_t *__restrict__ off,
+                                                    const int32_t *__restrict__ src, int n_seqs,
+                                                    int T, const W *__restrict__ tok,
+                                                    const W *__restrict__ pos, int vocab, int H,
+                                                    const float *__restrict__ g,
+                                                    const float *__restrict__ b, float eps,
+                                                    float *__restrict__ x, OutB *__restrict__ xb,
+                                                    int ldb, int *flag) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int t = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int s = seq_of_token(off, n_seqs, t);
+  const int p = t - off[s];  // positions restart at 0 in every sequence
+  int id = ids[(src ? src[s] : off[s]) + p];
+  if (id < 0 || id >= vocab) {
+    if (lane == 0) atomicOr(flag, 1);
+    id = 0;
+  }
+  const int c4n = H >> 2;
+  const W *tr = tok + (int64_t)id * H;
+  const W *pr = pos + (int64_t)p * H;
+  float4 v[NC];
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    const int c4 = lane + kWave * j;
+    if (c4 < c4n) {
+      const float4 a = load4(tr + 4 * c4), c = load4(pr + 4 * c4);
+      v[j] = make_float4(a.x + c.x, a.y + c.y, a.z + c.z, a.w + c.w);
+    } else {
+      v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+  if (LN) ln_row<NC>(v, lane, c4n, H, g, b, eps);
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    const int c4 = lane + kWave * j;
+    if (c4 < c4n) {
+      store4(x + (int64_t)t * H + 4 * c4, v[j]);
+      if (LN) store4(xb + (int64_t)t * ldb + 4 * c4, v[j]);
+    }
+  }
+}
+
+// Softmax over the rows of one (sequence, head) score block, kQTile rows per
+// block of 256 threads.  Rows shorter than 64 are packed G = 8/16/32 lanes
+// per row so short sequences still use whole wavefronts; longer rows hold up
+// to NJ elements per lane in registers (single read, single write).
+template <int NJ, typename PT>
+__global__ __launch_bounds__(256) void softmax_kernel(const float *__restrict__ S, PT *__restrict__ P,
+                                                      const int32_t *__restrict__ off,
+                                                      const int64_t *__restrict__ sbase,
+                                                      const int32_t *__restrict__ items, int n_heads,
+                                                      int causal) {
+  const int item = blockIdx.x, h = blockIdx.y;
+  const int seq = items[2 * item], q0 = items[2 * item + 1];
+  const int n = off[seq + 1] - off[seq];
+  const int ld = score_ld(n);
+  const int64_t base = sbase[seq] + (int64_t)h * n * ld;
+  int G = 64;
+  if (n <= 8) G = 8;
+  else if (n <= 16) G = 16;
+  else if (n <= 32) G = 32;
+  const int rpw = kWave / G;  // rows per wavefront pass
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  const int sub = lane / G, c0 = lane % G;
+  const int q_end = min(q0 + kQTile, n);
+  for (int qa = q0 + wave * rpw; qa < q_end; qa += 4 * rpw) {
+    const int q = qa + sub;
+    const int m = q < q_end ? (causal ? q + 1 : n) : 0;  // valid scores in this row
+    const float *sr = S + base + (int64_t)q * ld;
+    float v[NJ];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int c = c0 + G * j;
+      v[j] = c < m ? sr[c] : -INFINITY;
+      mx = fmaxf(mx, v[j]);
+    }
+    mx = group_max(mx, G);
+    float sum = 0.f;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int c = c0 + G * j;
+      v[j] = c < m ? expf(v[j] - mx) : 0.f;
+      sum += v[j];
+    }
+    sum = group_sum(sum, G);
+    PT *pr = P + base + (int64_t)q * ld;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int c = c0 + G * j;
+      if (c < m) pr[c] = from_f<PT>(v[j] / sum);
+    }
+  }
+}
+
+template <int NC, bool PRE_LN>
+__global__ __launch_bounds__(256) void head_kernel(const float *__restrict__ x, int H,
+                                                   const int32_t *__restrict__ off, int n_seqs,
+                                                   const float *__restrict__ g,
+                                                   const float *__restrict__ b, float eps,
+                                                   const float *__restrict__ w,
+                                                   const float *__restrict__ hb, float offset,
+                                                   const int32_t *__restrict__ dest,
+                                                   float *__restrict__ rewards) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int i = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (i >= n_seqs) return;
+  const int64_t t = off[i + 1] - 1;  // reward read at the end of the sequence
+  const int c4n = H >> 2;
+  float4 v[NC];
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    const int c4 = lane + kWave * j;
+    v[j] = c4 < c4n ? load4(x + t * H + 4 * c4) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  if (PRE_LN) ln_row<NC>(v, lane, c4n, H, g, b, eps);
+  float d = 0.f;
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    const int c4 = lane + kWave * j;
+    if (c4 < c4n) {
+      const float4 ww = load4(w + 4 * c4);
+      d += (v[j].x * ww.x + v[j].y * ww.y) + (v[j].z * ww.z + v[j].w * ww.w);
+    }
+  }
+  d = wave_sum(d);
+  if (lane == 0) rewards[dest ? dest[i] : i] = (d + hb[0]) + offset;
+}
+
+// Smallest register-chunk count NC (float4 per lane) covering `cols`.
+template <typename F>
+hipError_t dispatch_nc(int cols, F &&f) {
+  const int c4 = (cols + 3) / 4;
+  if (c4 <= 64) return f(std::integral_constant<int, 1>{});
+  if (c4 <= 128) return f(std::integral_constant<int, 2>{});
+  if (c4 <= 256) return f(std::integral_constant<int, 4>{});
+  if (c4 <= 512) return f(std::integral_constant<int, 8>{});
+  if (c4 <= 1024) return f(std::integral_constant<int, 16>{});
+  if (c4 <= 2048) return f(std::integral_constant<int, 32>{});
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_layernorm(bool act_bf16, const float *x, const float *g, const float *b,
+                            int64_t rows, int cols, float eps, float *y, void *yb, int ldb,
+                            hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)), block(256);
+  return dispatch_nc(cols, [&](auto nc) {
+    constexpr int NC = decltype(nc)::value;
+    if (act_bf16)
+      layernorm_kernel<NC, uint16_t><<<grid, block, 0, st>>>(x, g, b, rows, cols, eps, y,
+                                                              (uint16_t *)yb, ldb);
+    else
+      layernorm_kernel<NC, float><<<grid, block, 0, st>>>(x, g, b, rows, cols, eps, y, (float *)yb,
+                                                           ldb);
+    return hipGetLastError();
+  });
+}
+
+hipError_t launch_embed(bool w_bf16, bool act_bf16, bool ln, const int32_t *ids, const Ragged &r,
+                        const void *tok, const void *pos, int vocab, int H, const float *g,
+                        const float *b, float eps, float *x, void *xb, int ldb, int *flag,
+                        hipStream_t st) {
+  if (r.n_tokens <= 0) return hipSuccess;
+  const dim3 grid((r.n_tokens + kRowsPerBlock - 1) / kRowsPerBlock), block(256);
+  return dispatch_nc(H, [&](auto nc) {
+    constexpr int NC = decltype(nc)::value;
+    if (w_bf16 != act_bf16) return hipErrorInvalidValue;
+    if (w_bf16) {
+      auto k = ln ? embed_kernel<NC, uint16_t, true, uint16_t> : embed_kernel<NC, uint16_t, false, uint16_t>;
+      k<<<grid, block, 0, st>>>(ids, r.off, r.src, r.n_seqs, r.n_tokens, (const uint16_t *)tok,
+                                (const uint16_t *)pos, vocab, H, g, b, eps, x, (uint16_t *)xb, ldb,
+                                flag);
+    } else {
+      auto k = ln ? embed_kernel<NC, float, true, float> : embed_kernel<NC, float, false, float>;
+      k<<<grid, block, 0, st>>>(ids, r.off, r.src, r.n_seqs, r.n_tokens, (const float *)tok,
+                                (const float *)pos, vocab, H, g, b, eps, x, (float *)xb, ldb, flag);
+    }
+    return hipGetLastError();
+  });
+}
+
+hipError_t launch_softmax(bool p_bf16, const float *S, void *P, const Ragged &r, int n_heads,
+                          bool causal, hipStream_t st) {
+  if (r.n_items <= 0) return hipSuccess;
+  const dim3 grid(r.n_items, n_heads), block(256);
+  const int nj = (r.max_len + kWave - 1) / kWave;
+  auto go = [&](auto njc) {
+    constexpr int NJ = decltype(njc)::value;
+    if (p_bf16)
+      softmax_kernel<NJ, uint16_t><<<grid, block, 0, st>>>(S, (uint16_t *)P, r.off, r.sbase,
+                                                            r.items, n_heads, causal ? 1 : 0);
+    else
+      softmax_kernel<NJ, float><<<grid, block, 0, st>>>(S, (float *)P, r.off, r.sbase, r.items,
+                                                         n_heads, causal ? 1 : 0);
+    return hipGetLastError();
+  };
+  if (nj <= 1) return go(std::integral_constant<int, 1>{});
+  if (nj <= 2) return go(std::integral_constant<int, 2>{});
+  if (nj <= 4) return go(std::integral_constant<int, 4>{});
+  if (nj <= 8) return go(std::integral_constant<int, 8>{});
+  if (nj <= 16) return go(std::integral_constant<int, 16>{});
+  if (nj <= 64) return go(std::integral_constant<int, 64>{});
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_head(bool pre_ln, const float *x, int H, const Ragged &r, const float *g,
+                       const float *b, float eps, const float *w, const float *hb, float offset,
+                       float *rewards, hipStream_t st) {
+  if (r.n_seqs <= 0) return hipSuccess;
+  const dim3 grid((r.n_seqs + kRowsPerBlock - 1) / kRowsPerBlock), block(256);
+  return dispatch_nc(H, [&](auto nc) {
+    constexpr int NC = decltype(nc)::value;
+    if (pre_ln)
+      head_kernel<NC, true><<<grid, block, 0, st>>>(x, H, r.off, r.n_seqs, g, b, eps, w, hb, offset,
+                                                    r.dest, rewards);
+    else
+      head_kernel<NC, false><<<grid, block, 0, st>>>(x, H, r.off, r.n_seqs, g, b, eps, w, hb,
+                                                     offset, r.dest, rewards);
+    return hipGetLastError();
+  });
+}
+
+}  // namespace es

@@ -1,0 +1,301 @@
+/*
+ * encscore.h -- C ABI of the variable-length transformer scorer for MI355X
+ * (gfx950).
+ *
+ * The library gives every sequence of a packed, variable-length batch one
+ * scalar score (reward-model scoring, compact-BERT inference) and plans how to
+ * group a stream of requests into batches.  The method follows:
+ *   - "TurboTransformers: An Efficient GPU Serving System For Transformer
+ *     Models" (review; Abstract and Proposed method): GEMMs plus per-row
+ *     ("batch reduction") Softmax and LayerNorm kernels, no fixed-length
+ *     padding, requests sorted by length and grouped by a dynamic-programming
+ *     batch scheduler;
+ *   - "Learning to summarize from human feedback" (summary; Method): a scalar
+ *     head read at the end of the complete sequence, with rewards normalised
+ *     so that reference sequences average zero.
+ *
+ * Conventions for every function:
+ *   - The return value is an es_status; ES_OK is 0, errors are negative.  No
+ *     C++ exception crosses this boundary.  es_last_error() gives a message
+ *     for the last failure on the calling thread.
+ *   - Pointers prefixed d_ are device pointers (HIP device memory of the
+ *     current device), h_ are host pointers.  The caller owns every buffer it
+ *     passes; the library neither frees nor keeps them after the call.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Device work is
+ *     enqueued on it and the call returns without waiting, unless stated.
+ *   - One es_model handle runs one call at a time: its workspace is shared,
+ *     so overlapping calls on one handle (from several threads, or on two
+ *     streams without synchronising between them) race.  Separate handles are
+ *     independent.
+ */
+#ifndef ENCSCORE_H
+#define ENCSCORE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t es_status;
+enum {
+  ES_OK = 0,
+  ES_ERR_ARG = -1,         /* null pointer, bad count, malformed offsets       */
+  ES_ERR_RANGE = -2,       /* a length outside [1, limit]                       */
+  ES_ERR_CAPACITY = -3,    /* batch exceeds the workspace sized at load time    */
+  ES_ERR_FORMAT = -4,      /* weight blob header or size invalid                */
+  ES_ERR_IO = -5,          /* blob file unreadable                              */
+  ES_ERR_HIP = -6,         /* a HIP runtime call failed (message has details)   */
+  ES_ERR_DEVICE_FLAG = -7  /* a kernel saw an out-of-range token id             */
+};
+
+typedef struct es_model es_model; /* opaque: device weights + workspace */
+
+/* Model description returned by es_model_info. */
+typedef struct {
+  int32_t n_layers, hidden, n_heads, head_dim, ffn, vocab, max_pos;
+  int32_t pre_ln;      /* 0: post-LN encoder (embedding LN), 1: pre-LN + final LN */
+  int32_t causal;      /* 0: bidirectional within a sequence, 1: causal          */
+  int32_t bf16;        /* 0: fp32 weights and activations; 1: bf16 GEMM operands,
+                          fp32 accumulation, fp32 residual stream and LN        */
+  float eps;           /* LayerNorm epsilon                                     */
+  float reward_offset; /* added to every raw reward                             */
+  int64_t max_tokens;  /* capacity: tokens per es_score_batch call              */
+  int32_t max_seqs;    /* capacity: sequences per call                          */
+  int64_t device_bytes;/* device memory held by the handle                      */
+} es_model_info_t;
+
+/* ------------------------------------------------------------------ models */
+
+/*
+ * es_load_weights / es_load_weights_mem -- parse a weight blob, upload it to
+ * the current HIP device and size the workspace for batches of up to
+ * `max_tokens` packed tokens and `max_seqs` sequences.
+ *
+ * Blob ("ESW1", little-endian): a 64-byte header
+ *   char magic[4]="ESW1"; u32 version=1; u32 n_layers, hidden, n_heads, ffn,
+ *   vocab, max_pos, pre_ln, causal, act(0 = exact-erf GELU), wdtype(0 fp32,
+ *   1 bf16); f32 eps, reward_offset; u32 reserved[2]
+ * followed by the tensors in this order (matrices/embeddings in wdtype,
+ * vectors always fp32): tok_emb[V,H], pos_emb[P,H], norm_g[H], norm_b[H]
+ * (embedding LN for post-LN, final LN for pre-LN); per layer w_qkv[3H,H]
+ * (rows Q|K|V, head h = rows h*d..h*d+d-1 of each part), b_qkv[3H],
+ * w_o[H,H], b_o[H], ln1_g[H], ln1_b[H], w_1[F,H], b_1[F], w_2[H,F], b_2[H],
+ * ln2_g[H], ln2_b[H]; then head_w[H], head_b[1].  Weight matrices are
+ * [out, in] (y = x W^T + b).
+ *
+ * Errors: ES_ERR_IO (file), ES_ERR_FORMAT (magic/version/sizes/trailing
+ * bytes), ES_ERR_ARG (max_tokens < 1, max_seqs < 1, out NULL), ES_ERR_HIP.
+ * On success *out owns device memory until es_free.
+ */
+es_status es_load_weights(const char *blob_path, int64_t max_tokens, int32_t max_seqs,
+                          es_model **out);
+es_status es_load_weights_mem(const void *h_blob, int64_t nbytes, int64_t max_tokens,
+                              int32_t max_seqs, es_model **out);
+
+/* Release the handle and its device memory (synchronises the device first). */
+void es_free(es_model *m);
+
+es_status es_model_info(const es_model *m, es_model_info_t *info);
+
+/* ----------------------------------------------------------------- scoring */
+
+/*
+ * es_score_batch -- the hot path: one forward pass over a packed batch.
+ *
+ *   d_token_ids  int32[h_offsets[n_seqs]] on the device, sequences back to
+ *                back with no padding (TurboTransformers review, Proposed
+ *                method: batches formed without fixed-length padding).
+ *   h_offsets    int32[n_seqs+1] on the host, offsets[0] = 0, strictly
+ *                increasing; sequence i is tokens offsets[i] .. offsets[i+1]-1
+ *                and its positions restart at 0.
+ *   d_rewards    float32[n_seqs] on the device; rewards[i] = w . h + b +
+ *                offset, h the final hidden state of the LAST token of
+ *                sequence i (after the final LayerNorm for pre-LN models)
+ *                ("Learning to summarize from human feedback", Method: scalar
+ *                head, reward at the end of the complete sequence).
+ *
+ * Host-side validation (synchronous, before any device work): n_seqs in
+ * [1, max_seqs] (ES_ERR_ARG / ES_ERR_CAPACITY), offsets malformed (ES_ERR_ARG),
+ * a length above max_pos (ES_ERR_RANGE), total tokens above max_tokens
+ * (ES_ERR_CAPACITY).  Token ids are checked on the device: an id outside
+ * [0, vocab) reads row 0 and sets a sticky flag reported by
+ * es_check_device_errors.  Results are bitwise reproducible for identical
+ * inputs.  The call copies its small per-batch metadata from pinned host
+ * memory and may wait for the previous call's copy before reusing it.
+ */
+es_status es_score_batch(es_model *m, const int32_t *d_token_ids, const int32_t *h_offsets,
+                         int32_t n_seqs, float *d_rewards, void *stream);
+
+/* Plan / work summary of one es_score_requests call. */
+typedef struct {
+  int32_t n_batches;     /* batches the planner formed                           */
+  int64_t total_cost;    /* planner objective: sum of overhead + |B| * max_len   */
+  int64_t padded_tokens; /* sum over batches of |B| * max_len(B)                 */
+  int64_t packed_tokens; /* tokens actually computed (no padding)                */
+} es_stream_stats_t;
+
+/*
+ * es_score_requests -- score a whole request stream: plan, pack, forward
+ * every batch, scatter the rewards back to request order.
+ *
+ *   d_token_ids  int32[sum h_lengths] on the device, the requests back to back
+ *                in arrival order.
+ *   h_lengths    int32[n] on the host, each in [1, max_pos].
+ *   d_rewards    float32[n] on the device; d_rewards[i] is request i's reward.
+ *
+ * The planner is es_plan_batches with max_tokens = the handle's max_tokens
+ * and the given batch_overhead (TurboTransformers review, Proposed method:
+ * requests sorted by length and grouped by dynamic programming with minimal
+ * padding).  Each batch is packed without padding: its sequences' ids are read
+ * in place from d_token_ids by the embedding kernel, and the head kernel
+ * writes each reward to its request slot.  Per-call metadata for all batches
+ * is uploaded in one copy.  `stats` may be NULL.  Errors: as es_plan_batches
+ * and es_score_batch; ES_ERR_CAPACITY if a planned batch has more sequences
+ * than max_seqs.
+ */
+es_status es_score_requests(es_model *m, const int32_t *d_token_ids, const int32_t *h_lengths,
+                            int32_t n, int64_t batch_overhead, float *d_rewards, void *stream,
+                            es_stream_stats_t *stats);
+
+/*
+ * es_forward_hidden -- diagnostic form of es_score_batch: runs the embedding
+ * and the first `n_layers` layers (0 <= n_layers <= model layers) and copies
+ * the fp32 residual stream into d_hidden float32[offsets[n_seqs], hidden]
+ * (row t = token t of the packed batch).  Same validation as es_score_batch.
+ */
+es_status es_forward_hidden(es_model *m, const int32_t *d_token_ids, const int32_t *h_offsets,
+                            int32_t n_seqs, int32_t n_layers, float *d_hidden, void *stream);
+
+/* Set / read the scalar added to every reward. */
+es_status es_set_reward_offset(es_model *m, float offset);
+es_status es_get_reward_offset(const es_model *m, float *offset);
+
+/*
+ * es_calibrate_offset -- score a reference set (same layout as
+ * es_score_batch, at most max_seqs sequences and max_tokens tokens) with the
+ * offset at zero, and return offset = -mean(raw rewards) (mean over the set in
+ * double precision, stored as float) so that the reference set averages zero
+ * ("Learning to summarize from human feedback", Method).  Synchronises
+ * `stream`.  The model's offset is NOT changed; pass the result to
+ * es_set_reward_offset.
+ */
+es_status es_calibrate_offset(es_model *m, const int32_t *d_token_ids, const int32_t *h_offsets,
+                              int32_t n_ref, void *stream, float *offset_out);
+
+/*
+ * es_check_device_errors -- synchronise `stream`, then report and clear the
+ * sticky device flag: ES_ERR_DEVICE_FLAG if any kernel since the last check
+ * saw an out-of-range token id, else ES_OK.
+ */
+es_status es_check_device_errors(es_model *m, void *stream);
+
+/* ---------------------------------------------------------------- planner */
+
+/*
+ * es_plan_batches -- host-only batch planner (never touches HIP).
+ *
+ * TurboTransformers review (Abstract; Proposed method): requests sorted by
+ * length and grouped by dynamic programming with minimal padding.  Reading
+ * used: minimise  sum_B ( batch_overhead + |B| * max_len(B) )  subject to
+ * |B| * max_len(B) <= max_tokens, over partitions of the requests.
+ *   order[n]          request indices sorted by (length, index)
+ *   batch_starts[B+1] batch b is order[batch_starts[b] .. batch_starts[b+1]-1]
+ *   *n_batches = B, *total_cost = the optimal cost.
+ * The DP over sorted prefixes keeps the first minimising split point, so ties
+ * resolve to the plan whose start list, read backwards, is smallest.
+ * batch_starts must hold n+1 entries.  n = 0 gives B = 0, starts = {0}.
+ * Errors: ES_ERR_ARG (n < 0, NULL pointers, max_tokens < 1,
+ * batch_overhead < 0), ES_ERR_RANGE (a length < 1 or > max_tokens).
+ */
+es_status es_plan_batches(const int32_t *lengths, int32_t n, int64_t max_tokens,
+                          int64_t batch_overhead, int32_t *order, int32_t *batch_starts,
+                          int32_t *n_batches, int64_t *total_cost);
+
+/*
+ * es_pack_offsets -- host-only: offsets[0] = 0, offsets[k+1] = offsets[k] +
+ * lengths[order[begin+k]] for k < end-begin (the packed layout of one batch).
+ * offsets holds end-begin+1 entries.  Errors: ES_ERR_ARG (NULL, begin > end,
+ * begin < 0), ES_ERR_RANGE (a length < 1 or a sum above INT32_MAX).
+ */
+es_status es_pack_offsets(const int32_t *lengths, const int32_t *order, int32_t begin,
+                          int32_t end, int32_t *offsets);
+
+/* ------------------------------------------------------- single-kernel ops */
+/*
+ * The kernels of the hot path on caller buffers, for per-kernel parity tests
+ * and bandwidth / MFMA measurement.  All enqueue on `stream`.
+ */
+
+/*
+ * es_op_layernorm -- per-row LayerNorm (TurboTransformers review, Proposed
+ * method: LayerNorm as a row "batch reduction"): for each of `rows` rows of
+ * `cols` floats (row stride `cols`),
+ *   y = (x - mean) / sqrt(var + eps) * gamma + beta,  var biased.
+ * d_y float32[rows, cols] (may be NULL), d_ybf16 bf16[rows, ld_bf16] (may be
+ * NULL; columns >= cols untouched).  cols must be a multiple of 4 and at most
+ * 8192; d_x and d_y may alias.  Errors: ES_ERR_ARG.
+ */
+es_status es_op_layernorm(const float *d_x, const float *d_gamma, const float *d_beta,
+                          int64_t rows, int32_t cols, float eps, float *d_y, uint16_t *d_ybf16,
+                          int32_t ld_bf16, void *stream);
+
+/*
+ * es_ragged_create / es_ragged_free -- ragged attention-score layout of one
+ * packed batch, uploaded to the current device once (synchronous; allocates)
+ * so that es_op_softmax can be launched repeatedly without host work.
+ *
+ * For sequence i of length n_i (h_lengths[i], 1..4096) and head h < n_heads,
+ * rows q < n_i of the score block start at element
+ *     base_i + (h * n_i + q) * ld_i,  ld_i = round_up(n_i, 8),
+ *     base_0 = 0, base_{i+1} = base_i + n_heads * n_i * ld_i,
+ * and hold n_i scores (causal = 1: q + 1 scores).  *n_elems (may be NULL)
+ * receives base_{n_seqs}, the element count the score buffers need.
+ * Errors: ES_ERR_ARG (NULL, n_seqs < 1, n_heads < 1), ES_ERR_RANGE (a length
+ * outside [1, 4096]), ES_ERR_HIP.
+ */
+typedef struct es_ragged es_ragged;
+es_status es_ragged_create(const int32_t *h_lengths, int32_t n_seqs, int32_t n_heads,
+                           int32_t causal, es_ragged **out, int64_t *n_elems);
+void es_ragged_free(es_ragged *r);
+
+/*
+ * es_op_softmax -- per-row softmax over the ragged score layout of `r`
+ * (TurboTransformers review, Proposed method: Softmax as a row "batch
+ * reduction"):  p = exp(s - max) / sum exp(s - max)  over the valid scores
+ * of every row, written to the same positions of d_p (bf16 bits if
+ * p_bf16 = 1, else float32); other positions are not written.  Asynchronous;
+ * allocates nothing.  Errors: ES_ERR_ARG.
+ */
+es_status es_op_softmax(const es_ragged *r, const float *d_scores, void *d_p, int32_t p_bf16,
+                        void *stream);
+
+/*
+ * es_op_gemm_bf16 -- C = epilogue(A W^T + bias) on bf16 MFMA, fp32 accumulate.
+ *   d_a  bf16[rows >= round_up(M,256), lda]  (K columns used)
+ *   d_w  bf16[rows >= round_up(N,256), K]    (row n = output feature n)
+ *   d_bias float32[N]
+ *   epilogue 0: out bf16 = acc + bias
+ *            1: out bf16 = GELU(acc + bias)            (exact erf form)
+ *            2: out fp32 = acc + bias + d_res[m, n]     (d_res fp32, ld ldc)
+ *            3: out fp32 = acc + bias
+ *   d_out [M, ldc] (bf16 for 0/1, fp32 for 2/3); only n < N, m < M written.
+ * K must be a positive multiple of 64, lda >= K and a multiple of 8, ldc >= N.
+ * Rows beyond M (A) and N (W) up to the rounded sizes are read, never used.
+ * Errors: ES_ERR_ARG.
+ */
+es_status es_op_gemm_bf16(const uint16_t *d_a, int32_t lda, const uint16_t *d_w,
+                          const float *d_bias, const float *d_res, void *d_out, int32_t ldc,
+                          int32_t M, int32_t N, int32_t K, int32_t epilogue, void *stream);
+
+/* Thread-local message describing the last error on this thread ("" if none). */
+const char *es_last_error(void);
+
+/* Library version string. */
+const char *es_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ENCSCORE_H */

@@ -1,0 +1,189 @@
+"""End-to-end parity of the HIP scoring path against the oracle (small inputs).
+
+Bars: rewards max-abs <= 1e-5 for fp32 models and <= 1e-2 for bf16 models
+(bf16 GEMM operands, fp32 accumulation); plans and offsets bit-exact; the GPU
+result for a sequence does not depend on the rest of its batch (bitwise).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from encoder_scoring_amd import EncScoreError, Scorer, blob
+from helpers import mini, need_gpu, offsets_of, say
+from synth import get_config, make_fixed_batch, make_reference_set, make_requests, make_weights
+from synth.generate import random_stream, split
+
+pytestmark = pytest.mark.gpu
+
+FP32_TOL = 1e-5
+BF16_TOL = 1e-2
+
+
+def scorer_for(cfg, w, offset=0.0, max_tokens=4096, max_seqs=512):
+    return Scorer(blob.to_bytes(cfg, w, offset), max_tokens, max_seqs)
+
+
+def gpu_score(torch, sc, ids, lengths):
+    d = torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).cuda()
+    r = sc.score(d, offsets_of(lengths))
+    torch.cuda.synchronize()
+    return r.cpu().numpy().astype(np.float64)
+
+
+CASES = [
+    ("tiny_fp32", get_config("tiny_fp32"), FP32_TOL),
+    ("dec_fp32", mini("dec_fp32", True, True, False, H=128, A=2, F=256, P=128), FP32_TOL),
+    ("enc_fp32_d26", mini("enc_fp32_d26", False, False, False, H=52, A=2, F=96, P=80), FP32_TOL),
+    ("dec_bf16_d128", mini("dec_bf16_d128", True, True, True, H=256, A=2, F=512, V=1000, P=300), BF16_TOL),
+    ("enc_bf16", mini("enc_bf16", False, False, True, H=192, A=3, F=384, V=500, P=200), BF16_TOL),
+]
+
+
+@pytest.mark.parametrize("name,cfg,tol", CASES, ids=[c[0] for c in CASES])
+def test_rewards_match_oracle(name, cfg, tol):
+    torch = need_gpu()
+    say("rewards", name)
+    w = make_weights(cfg)
+    ids, lengths = random_stream(5, 11, 1, min(cfg.max_pos, 150), cfg.vocab)
+    sc = scorer_for(cfg, w, offset=0.125)
+    got = gpu_score(torch, sc, ids, lengths)
+    want = oracle.OracleModel(cfg, w).score_many(split(ids, lengths), 0.125)
+    say(name, "max |d reward| =", float(np.max(np.abs(got - want))))
+    assert np.max(np.abs(got - want)) <= tol
+
+
+@pytest.mark.parametrize("name,cfg,tol", CASES[:3], ids=[c[0] for c in CASES[:3]])
+def test_hidden_states_match_oracle_fp32(name, cfg, tol):
+    torch = need_gpu()
+    w = make_weights(cfg)
+    ids, lengths = random_stream(6, 5, 1, min(cfg.max_pos, 90), cfg.vocab)
+    sc = scorer_for(cfg, w)
+    m = oracle.OracleModel(cfg, w)
+    d = torch.from_numpy(ids).cuda()
+    for L in range(cfg.n_layers + 1):
+        got = sc.hidden(d, offsets_of(lengths), L).cpu().numpy()
+        want = np.concatenate([m.hidden(s, L) for s in split(ids, lengths)])
+        err = np.max(np.abs(got - want))
+        say(name, "layer", L, "max |d hidden| =", float(err))
+        assert err < 2e-5 * max(1.0, float(np.max(np.abs(want))))
+
+
+def test_tiny_workload_and_calibration():
+    torch = need_gpu()
+    cfg = get_config("tiny_fp32")
+    w = make_weights(cfg)
+    m = oracle.OracleModel(cfg, w)
+    rid, rlen = make_reference_set(cfg)
+    off_oracle = m.calibrate_offset(split(rid, rlen))
+    sc = scorer_for(cfg, w, 0.0, max_tokens=1024, max_seqs=64)
+    off_gpu = sc.calibrate_offset(torch.from_numpy(rid).cuda(), offsets_of(rlen))
+    assert abs(off_gpu - off_oracle) <= FP32_TOL
+    sc.reward_offset = off_gpu
+    ref = gpu_score(torch, sc, rid, rlen)
+    assert abs(ref.mean()) < 1e-6
+    ids, lengths, _ = make_requests(cfg)
+    got = gpu_score(torch, sc, ids, lengths)
+    want = m.score_many(split(ids, lengths), off_gpu)
+    assert np.max(np.abs(got - want)) <= FP32_TOL
+
+
+def test_tinybert_fixed_lengths():
+    torch = need_gpu()
+    cfg = get_config("tinybert")
+    w = make_weights(cfg)
+    m = oracle.OracleModel(cfg, w)
+    sc = scorer_for(cfg, w, 0.0, max_tokens=16384, max_seqs=64)
+    for n, B in [(64, 1), (128, 1), (256, 1), (64, 8), (256, 3)]:
+        ids, lengths = make_fixed_batch(cfg, n, B)
+        got = gpu_score(torch, sc, ids, lengths)
+        want = m.score_many(split(ids, lengths))
+        say("tinybert", n, B, float(np.max(np.abs(got - want))))
+        assert np.max(np.abs(got - want)) <= BF16_TOL
+
+
+def test_bert_base_short_sample():
+    torch = need_gpu()
+    cfg = get_config("bert_base_short")
+    w = make_weights(cfg)
+    ids, lengths, _ = make_requests(cfg)
+    seqs = split(ids, lengths)[:6]
+    sc = scorer_for(cfg, w, 0.0, max_tokens=4096, max_seqs=2048)
+    got = gpu_score(torch, sc, np.concatenate(seqs), [len(s) for s in seqs])
+    want = oracle.OracleModel(cfg, w).score_many(seqs)
+    say("bert_base sample", float(np.max(np.abs(got - want))))
+    assert np.max(np.abs(got - want)) <= BF16_TOL
+
+
+@pytest.mark.parametrize("cfg", [CASES[0][1], CASES[3][1]], ids=["fp32", "bf16_causal"])
+def test_batch_invariance_and_determinism(cfg):
+    torch = need_gpu()
+    w = make_weights(cfg)
+    ids, lengths = random_stream(8, 9, 1, min(cfg.max_pos, 120), cfg.vocab)
+    sc = scorer_for(cfg, w)
+    packed = gpu_score(torch, sc, ids, lengths)
+    again = gpu_score(torch, sc, ids, lengths)
+    assert np.array_equal(packed, again)                       # run to run, bitwise
+    alone = np.array([gpu_score(torch, sc, s, [len(s)])[0] for s in split(ids, lengths)])
+    assert np.array_equal(packed, alone)                       # batch composition, bitwise
+    perm = np.random.default_rng(0).permutation(len(lengths))
+    seqs = split(ids, lengths)
+    pids = np.concatenate([seqs[i] for i in perm])
+    assert np.array_equal(gpu_score(torch, sc, pids, lengths[perm]), packed[perm])
+
+
+def test_score_requests_matches_batches_and_oracle():
+    torch = need_gpu()
+    cfg = CASES[4][1]
+    w = make_weights(cfg)
+    ids, lengths = random_stream(9, 40, 1, 120, cfg.vocab)
+    T = 512
+    sc = scorer_for(cfg, w, 0.5, max_tokens=T, max_seqs=512)
+    d = torch.from_numpy(ids).cuda()
+    rew, stats = sc.score_requests(d, lengths, batch_overhead=64)
+    torch.cuda.synchronize()
+    rew = rew.cpu().numpy().astype(np.float64)
+    order, starts, cost = oracle.plan_batches(lengths, T, 64)
+    assert stats["n_batches"] == len(starts) - 1 and stats["total_cost"] == cost
+    assert stats["packed_tokens"] == int(lengths.sum())
+    seqs = split(ids, lengths)
+    for b in range(len(starts) - 1):
+        idx = order[starts[b]:starts[b + 1]]
+        sub = gpu_score(torch, sc, np.concatenate([seqs[i] for i in idx]), lengths[idx])
+        assert np.array_equal(sub, rew[idx])
+    want = oracle.OracleModel(cfg, w).score_many(seqs, 0.5)
+    assert np.max(np.abs(rew - want)) <= BF16_TOL
+
+
+def test_host_validation_errors():
+    torch = need_gpu()
+    cfg = CASES[0][1]
+    sc = scorer_for(cfg, make_weights(cfg), max_tokens=100, max_seqs=4)
+    d = torch.zeros(200, dtype=torch.int32, device="cuda")
+    bad = [
+        (np.array([1, 3]), -1),          # offsets[0] != 0
+        (np.array([0, 3, 3]), -1),       # empty sequence
+        (np.array([0, 65]), -2),         # longer than max_pos (64)
+        (np.array([0, 60, 120]), -3),    # above max_tokens
+        (np.array([0, 1, 2, 3, 4, 5]), -3),  # above max_seqs
+    ]
+    for off, code in bad:
+        with pytest.raises(EncScoreError) as e:
+            sc.score(d, off)
+        assert e.value.status == code, (off, str(e.value))
+    ok = sc.score(d[:10], np.array([0, 4, 10]))
+    torch.cuda.synchronize()
+    assert np.all(np.isfinite(ok.cpu().numpy()))
+
+
+def test_out_of_range_token_sets_device_flag():
+    torch = need_gpu()
+    cfg = CASES[0][1]
+    sc = scorer_for(cfg, make_weights(cfg), max_tokens=100, max_seqs=4)
+    sc.check_device_errors()
+    d = torch.tensor([1, 2, cfg.vocab + 5, 3], dtype=torch.int32, device="cuda")
+    r = sc.score(d, np.array([0, 4]))
+    with pytest.raises(EncScoreError) as e:
+        sc.check_device_errors()
+    assert e.value.status == -7
+    sc.check_device_errors()                     # flag was cleared
+    assert np.isfinite(r.cpu().numpy()).all()
