@@ -1,0 +1,231 @@
+#!/usr/bin/env python3
+"""Throughput of variable-length transformer scoring on one MI355X.
+
+One step = one pass of the whole hot path over the workload's request
+stream: DP batch planning, packing, embedding, every layer (QKV GEMM, masked
+scores, row softmax, P.V, output GEMM + residual, LayerNorm, FFN GEMMs with
+fused GELU / residual, LayerNorm), the last-token reward head and the scatter
+of rewards back to request order -- a single es_score_requests call on token
+ids already resident in HBM.
+
+Prints ONE JSON line (sequences/s for the whole job).  The dominant kernel
+class is timed live with HIP events on the stream it runs on (the library's
+profiling hook) and reported against the MI355X peak; the CPU oracle is timed
+on a bounded sample of the same stream on the host cores.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload bert_base_short]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAKS = {  # MI355X published peaks
+    "hbm": (8000.0, "GB/s"),
+    "mfma_bf16": (2500.0, "TFLOP/s"),
+    "alu_fp32": (157.3, "TFLOP/s"),
+}
+GEMM_CLASSES = ("qkv_gemm", "oproj_gemm", "ffn1_gemm", "ffn2_gemm")
+HBM_CLASSES = ("softmax", "layernorm", "embed", "head")
+WORKLOAD_DESC = {
+    "tiny_fp32": "2-layer fp32 encoder (hidden 128, 2 heads, FFN 512, vocab 1000); 8 requests U{2..32}",
+    "tinybert": "TinyBERT-shaped bf16 encoder (4x312, 12 heads of 26, FFN 1200, vocab 30522); 64 requests of 128 tokens",
+    "bert_base_short": "BERT-base-shaped bf16 encoder (12x768, 12 heads, FFN 3072, vocab 30522); 2000 requests U{2..100}; DP planner T=4096 c=1024",
+    "bert_base_longtail": "BERT-base-shaped bf16 encoder; 2000 requests: 1800 U{5..500} + 200 U{400..500}; DP planner T=16384 c=1024",
+    "decoder_rm": "decoder reward model bf16 (24x2048, 16 heads, FFN 8192, vocab 50257, causal, pre-LN); best-of-16 for 64 prompts of 512 + summaries U{8..48}; DP planner T=16384 c=1024",
+}
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def traffic_from_profiles(workload, kernel_class, launches_per_step):
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel_class}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    src = os.path.join(ROOT, "encoder_scoring_amd", "csrc", kv.get("source_file", ""))
+    if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != kv.get("source_sha256"):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        info = threadpool_info()
+        return max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1]), \
+            ",".join(sorted({i.get("internal_api", "?") for i in info if i.get("user_api") == "blas"}))
+    except Exception:
+        return os.cpu_count() or 1, "unknown"
+
+
+def cpu_baseline(cfg, weights, ids, lengths, budget_s):
+    """The oracle (plain fp32 numpy forward, one sequence at a time) on the host
+    cores, over the first requests of the same stream until ~budget_s."""
+    import numpy as np
+    import oracle
+    from synth.generate import split
+    seqs = split(ids, lengths)
+    m = oracle.OracleModel(cfg, weights, dtype=np.float32, cache=cfg.name != "decoder_rm")
+    m.score(seqs[0][:4])  # widen weights outside the timed sample
+    t0 = time.perf_counter()
+    done = tokens = 0
+    while done < len(seqs) and time.perf_counter() - t0 < budget_s:
+        m.score(seqs[done])
+        tokens += len(seqs[done])
+        done += 1
+    dt = time.perf_counter() - t0
+    threads, api = blas_threads()
+    return {"value": round(done / dt, 4), "unit": "sequences/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"first {done} of {len(seqs)} requests ({tokens} tokens) in request order, "
+                      f"numpy float32 forward one sequence at a time, {dt:.1f} s, BLAS={api}, "
+                      f"host cpu_count={os.cpu_count()}",
+            "tokens_per_s": round(tokens / dt, 1)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="bert_base_short", choices=sorted(WORKLOAD_DESC))
+    ap.add_argument("--batch-overhead", type=int, default=None)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the scoring path is "
+              "data-parallel over batches and runs one process per GPU -- run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from encoder_scoring_amd import Scorer, blob
+    from synth import get_config, make_reference_set, make_requests, make_weights, make_fixed_batch
+
+    assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
+    torch.cuda.set_device(0)
+    cfg = get_config(args.workload)
+    c = cfg.batch_overhead if args.batch_overhead is None else args.batch_overhead
+    t = time.perf_counter()
+    weights = make_weights(cfg)
+    if cfg.name == "tinybert":
+        ids, lengths = make_fixed_batch(cfg, 128, 64)
+    else:
+        ids, lengths, _ = make_requests(cfg)
+    n, n_tokens = int(lengths.size), int(lengths.sum())
+    log(f"{cfg.name}: {n} requests, {n_tokens} tokens; weights drawn in {time.perf_counter() - t:.1f} s")
+    sc = Scorer(blob.to_bytes(cfg, weights, 0.0), cfg.max_tokens, max(1, min(cfg.max_tokens, 65536)))
+    rid, rlen = make_reference_set(cfg)
+    d_ref = torch.from_numpy(rid).cuda()
+    roff = np.concatenate([[0], np.cumsum(rlen)]).astype(np.int32)
+    if int(rlen.sum()) <= cfg.max_tokens:
+        sc.reward_offset = sc.calibrate_offset(d_ref, roff)   # reference set averages zero
+    d_ids = torch.from_numpy(ids).cuda()
+    out = torch.empty(n, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    # warm-up steps with every kernel class timed, to find the dominant one
+    sc.profile_enable(None)
+    for _ in range(max(1, args.warmup)):
+        _, stats = sc.score_requests(d_ids, lengths, c, out)
+    stream.synchronize()
+    per_class = sc.profile_collect()
+    dominant = max(per_class, key=lambda k: per_class[k]["total_ms"])
+    log("warm-up per-class ms/step:", {k: round(v["total_ms"] / max(1, args.warmup), 3)
+                                       for k, v in per_class.items()})
+
+    # timed region: only the dominant class carries event pairs
+    sc.profile_enable([dominant])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        sc.score_requests(d_ids, lengths, c, out)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    dom = sc.profile_collect()[dominant]
+    sc.profile_enable([])
+    ms = (t1 - t0) * 1e3 / args.steps
+    value = n / (ms / 1e3)
+    assert torch.isfinite(out).all().item(), "non-finite rewards"
+
+    launches = dom["launches"] / args.steps
+    avg_ms = dom["total_ms"] / max(1, dom["launches"])
+    if dominant in GEMM_CLASSES:
+        key = "mfma_bf16" if cfg.bf16 else "alu_fp32"
+        bound = "mfma" if cfg.bf16 else "alu"
+        achieved = dom["flops"] / (dom["total_ms"] / 1e3) / 1e12
+    else:
+        key, bound = "hbm", "hbm"
+        achieved = dom["bytes"] / (dom["total_ms"] / 1e3) / 1e9
+    peak, unit = PEAKS[key]
+    traffic = traffic_from_profiles(cfg.name, dominant, launches)
+
+    kernels = {}
+    for k, v in per_class.items():
+        if v["launches"] == 0:
+            continue
+        sec = v["total_ms"] / 1e3
+        if k in GEMM_CLASSES:
+            kpeak, kunit = PEAKS["mfma_bf16" if cfg.bf16 else "alu_fp32"]
+            ach = v["flops"] / sec / 1e12
+        elif k in HBM_CLASSES:
+            kpeak, kunit = PEAKS["hbm"]
+            ach = v["bytes"] / sec / 1e9
+        else:   # attention contractions: report flops against the MFMA peak
+            kpeak, kunit = PEAKS["mfma_bf16" if cfg.bf16 else "alu_fp32"]
+            ach = v["flops"] / sec / 1e12
+        kernels[k] = {"ms_per_step": round(v["total_ms"] / max(1, args.warmup), 3),
+                      "achieved": round(ach, 2), "unit": kunit, "frac": round(ach / kpeak, 4),
+                      "launches_per_step": v["launches"] // max(1, args.warmup)}
+
+    line = {
+        "metric": "sequences scored/sec on var-len batches",
+        "value": round(value, 2),
+        "unit": "sequences/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.bf16 else "f32",
+        "data": "synthetic (seeded ids and N(0,0.02) weights of the stated shapes)",
+        "config": {"workload": cfg.name, "description": WORKLOAD_DESC[cfg.name],
+                   "requests": n, "tokens": n_tokens, "batches": stats["n_batches"],
+                   "padded_tokens": stats["padded_tokens"], "max_tokens": cfg.max_tokens,
+                   "batch_overhead": c},
+        "tokens_per_s": round(n_tokens / (ms / 1e3), 1),
+        "roofline": {"bound": bound, "kernel": dominant, "achieved": round(achieved, 2),
+                     "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
+                     "traffic": traffic, "avg_launch_ms": round(avg_ms, 5),
+                     "launches_per_step": launches},
+        "kernels": kernels,
+        "device": torch.cuda.get_device_name(0),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg, weights, ids, lengths, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -25,8 +25,11 @@ EXPORTS = [
     "es_forward_hidden", "es_set_reward_offset", "es_get_reward_offset", "es_calibrate_offset",
     "es_check_device_errors", "es_plan_batches", "es_pack_offsets", "es_op_layernorm",
     "es_ragged_create", "es_ragged_free", "es_op_softmax", "es_op_gemm_bf16", "es_last_error",
-    "es_version",
+    "es_version", "es_profile_enable", "es_profile_collect", "es_kernel_class_name",
 ]
+
+KERNEL_CLASSES = ["embed", "qkv_gemm", "scores", "softmax", "pv", "oproj_gemm", "layernorm",
+                  "ffn1_gemm", "ffn2_gemm", "head"]
 
 
 class EncScoreError(RuntimeError):
@@ -48,6 +51,12 @@ class ModelInfo(ctypes.Structure):
 class StreamStats(ctypes.Structure):
     _fields_ = [("n_batches", ctypes.c_int32), ("total_cost", ctypes.c_int64),
                 ("padded_tokens", ctypes.c_int64), ("packed_tokens", ctypes.c_int64)]
+
+
+class KernelStat(ctypes.Structure):
+    _fields_ = [("kernel_class", ctypes.c_int32), ("launches", ctypes.c_int32),
+                ("total_ms", ctypes.c_double), ("flops", ctypes.c_double),
+                ("bytes", ctypes.c_double)]
 
 
 _P = ctypes.c_void_p
@@ -72,6 +81,9 @@ _SIGS = {
     "es_ragged_free": (None, [_P]),
     "es_op_softmax": (ctypes.c_int32, [_P, _P, _P, ctypes.c_int32, _P]),
     "es_op_gemm_bf16": (ctypes.c_int32, [_P, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P]),
+    "es_profile_enable": (ctypes.c_int32, [_P, ctypes.c_uint32]),
+    "es_profile_collect": (ctypes.c_int32, [_P, ctypes.POINTER(KernelStat)]),
+    "es_kernel_class_name": (ctypes.c_char_p, [ctypes.c_int32]),
     "es_last_error": (ctypes.c_char_p, []),
     "es_version": (ctypes.c_char_p, []),
 }

@@ -153,6 +153,21 @@ class Scorer:
                                                      ctypes.byref(v)))
         return v.value
 
+    def profile_enable(self, classes=None):
+        """Record HIP events around the given kernel classes (names; None = all)."""
+        names = _lib.KERNEL_CLASSES
+        mask = (1 << len(names)) - 1 if classes is None else \
+            sum(1 << names.index(c) for c in classes)
+        check(self.lib, self.lib.es_profile_enable(self.handle, mask))
+
+    def profile_collect(self):
+        """Per-class {launches, total_ms, flops, bytes} since profile_enable."""
+        arr = (_lib.KernelStat * len(_lib.KERNEL_CLASSES))()
+        check(self.lib, self.lib.es_profile_collect(self.handle, arr))
+        return {_lib.KERNEL_CLASSES[k.kernel_class]: {"launches": k.launches, "total_ms": k.total_ms,
+                                                      "flops": k.flops, "bytes": k.bytes}
+                for k in arr}
+
     def check_device_errors(self):
         check(self.lib, self.lib.es_check_device_errors(self.handle, _stream()))
 

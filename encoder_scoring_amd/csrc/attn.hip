@@ -108,10 +108,161 @@ __global__ __launch_bounds__(256) void pv_kernel(const PT *__restrict__ P, const
   }
 }
 
+// ---------------------------------------------------------------- bf16 MFMA
+// One wavefront per (32-query tile, head).  Scores: S^T = K Q^T with
+// v_mfma_f32_32x32x16_bf16, Q and K fragments read straight from the packed
+// qkv rows (16 contiguous bytes per lane); with K as the first operand a lane
+// ends up holding four consecutive keys of one query row, stored as one
+// float4.  Context: ctx^T = V^T P^T; the V tile is transposed through LDS
+// (keys contiguous per head dimension) and P rows are read directly.
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ bf16x8 ld_frag(const uint16_t *p) {
+  return *reinterpret_cast<const bf16x8 *>(p);
+}
+__device__ __forceinline__ bf16x8 zero_frag() {
+  bf16x8 z;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) z[i] = (__bf16)0.0f;
+  return z;
+}
+
+template <int DP>
+__global__ __launch_bounds__(64) void scores_mfma_kernel(const uint16_t *__restrict__ qkv, int ldq,
+                                                         int n_heads, float scale, int causal,
+                                                         const int32_t *__restrict__ off,
+                                                         const int64_t *__restrict__ sbase,
+                                                         const int32_t *__restrict__ items,
+                                                         float *__restrict__ S) {
+  constexpr int KS = DP / 16;
+  const int item = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+  const int seq = items[2 * item], q0 = items[2 * item + 1];
+  const int64_t t0 = off[seq];
+  const int n = off[seq + 1] - (int)t0;
+  const int ld = score_ld(n);
+  const int64_t base = sbase[seq] + (int64_t)h * n * ld;
+  const int fr = lane & 31, fh = lane >> 5;
+  const int q = q0 + fr;
+  bf16x8 qf[KS];
+  const uint16_t *Qr = qkv + (t0 + q) * ldq + h * DP + fh * 8;
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) qf[kk] = q < n ? ld_frag(Qr + kk * 16) : zero_frag();
+  const int kend = causal ? min(n, q0 + kQTile) : n;
+  float *Sr = S + base + (int64_t)q * ld;
+  const int qlim = causal ? min(q + 1, n) : n;  // keys visible to this query row
+  for (int k0 = 0; k0 < kend; k0 += 32) {
+    const int k = k0 + fr;
+    const uint16_t *Kr = qkv + (t0 + k) * ldq + (n_heads + h) * DP + fh * 8;
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const bf16x8 kf = k < n ? ld_frag(Kr + kk * 16) : zero_frag();
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], acc, 0, 0, 0);
+    }
+    if (q >= n) continue;
+    // lane holds keys k0 + 8 g + 4 fh + (0..3) of query q
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int kb = k0 + 8 * g + 4 * fh;
+      const float4 v = make_float4(acc[4 * g] * scale, acc[4 * g + 1] * scale,
+                                   acc[4 * g + 2] * scale, acc[4 * g + 3] * scale);
+      if (kb + 3 < qlim) {
+        *reinterpret_cast<float4 *>(Sr + kb) = v;
+      } else {
+        if (kb < qlim) Sr[kb] = v.x;
+        if (kb + 1 < qlim) Sr[kb + 1] = v.y;
+        if (kb + 2 < qlim) Sr[kb + 2] = v.z;
+      }
+    }
+  }
+}
+
+template <int DP>
+__global__ __launch_bounds__(64) void pv_mfma_kernel(const uint16_t *__restrict__ P,
+                                                     const uint16_t *__restrict__ qkv, int ldq,
+                                                     int n_heads, int causal,
+                                                     const int32_t *__restrict__ off,
+                                                     const int64_t *__restrict__ sbase,
+                                                     const int32_t *__restrict__ items,
+                                                     uint16_t *__restrict__ ctx, int ldc) {
+  constexpr int NT = DP / 32, VP = 32 + 8;  // output column tiles; LDS pitch of V^T
+  __shared__ __attribute__((aligned(16))) uint16_t sV[DP * VP];
+  const int item = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+  const int seq = items[2 * item], q0 = items[2 * item + 1];
+  const int64_t t0 = off[seq];
+  const int n = off[seq + 1] - (int)t0;
+  const int ld = score_ld(n);
+  const int64_t base = sbase[seq] + (int64_t)h * n * ld;
+  const int fr = lane & 31, fh = lane >> 5;
+  const int q = q0 + fr;
+  const int qlim = q < n ? (causal ? q + 1 : n) : 0;  // valid P entries of this row
+  const uint16_t *Pr = P + base + (int64_t)q * ld;
+  const uint16_t *V = qkv + t0 * ldq + (2 * n_heads + h) * DP;
+  f32x16 acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
+  const int kend = causal ? min(n, q0 + kQTile) : n;
+  for (int k0 = 0; k0 < kend; k0 += 32) {
+    __syncthreads();
+    // V tile (32 keys x DP) -> LDS transposed: sV[e][key]
+#pragma unroll
+    for (int c = lane; c < 32 * DP / 8; c += 64) {
+      const int key = c / (DP / 8), e0 = (c % (DP / 8)) * 8;
+      uint4 u = make_uint4(0, 0, 0, 0);
+      if (k0 + key < n) u = *reinterpret_cast<const uint4 *>(V + (int64_t)(k0 + key) * ldq + e0);
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sV[(e0 + 2 * j) * VP + key] = (uint16_t)(w[j] & 0xffff);
+        sV[(e0 + 2 * j + 1) * VP + key] = (uint16_t)(w[j] >> 16);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int kb = k0 + kk * 16 + fh * 8;  // first key of this lane's P chunk
+      bf16x8 pf;
+      if (kb + 7 < qlim) {
+        pf = ld_frag(Pr + kb);
+      } else {
+        pf = zero_frag();
+        if (kb < qlim) {
+          const bf16x8 raw = ld_frag(Pr + kb);
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (kb + j < qlim) pf[j] = raw[j];
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const bf16x8 vf = ld_frag(sV + (t * 32 + fr) * VP + kk * 16 + fh * 8);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, acc[t], 0, 0, 0);
+      }
+    }
+  }
+  if (q >= n) return;
+  uint16_t *Cr = ctx + (t0 + q) * ldc + h * DP;
+  // lane holds head dims t*32 + 8 g + 4 fh + (0..3) of query q
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      uint2 u;
+      u.x = (uint32_t)f2bf(acc[t][4 * g]) | ((uint32_t)f2bf(acc[t][4 * g + 1]) << 16);
+      u.y = (uint32_t)f2bf(acc[t][4 * g + 2]) | ((uint32_t)f2bf(acc[t][4 * g + 3]) << 16);
+      *reinterpret_cast<uint2 *>(Cr + t * 32 + 8 * g + 4 * fh) = u;
+    }
+}
+
 template <typename F>
 hipError_t dispatch_dp(int dp, F &&f) {
   switch (dp) {
-    case 16: return f(std::integral_constant<int, 16>{});
     case 32: return f(std::integral_constant<int, 32>{});
     case 64: return f(std::integral_constant<int, 64>{});
     case 128: return f(std::integral_constant<int, 128>{});
@@ -128,8 +279,8 @@ hipError_t launch_scores(bool act_bf16, const void *qkv, int ldq, int n_heads, i
   return dispatch_dp(dp, [&](auto dpc) {
     constexpr int DP = decltype(dpc)::value;
     if (act_bf16)
-      scores_kernel<uint16_t, DP><<<grid, block, 0, st>>>((const uint16_t *)qkv, ldq, n_heads, scale,
-                                                          causal ? 1 : 0, r.off, r.sbase, r.items, S);
+      scores_mfma_kernel<DP><<<grid, dim3(64), 0, st>>>((const uint16_t *)qkv, ldq, n_heads, scale,
+                                                        causal ? 1 : 0, r.off, r.sbase, r.items, S);
     else
       scores_kernel<float, DP><<<grid, block, 0, st>>>((const float *)qkv, ldq, n_heads, scale,
                                                        causal ? 1 : 0, r.off, r.sbase, r.items, S);
@@ -144,9 +295,9 @@ hipError_t launch_pv(bool act_bf16, const void *P, const void *qkv, int ldq, int
   return dispatch_dp(dp, [&](auto dpc) {
     constexpr int DP = decltype(dpc)::value;
     if (act_bf16)
-      pv_kernel<uint16_t, uint16_t, DP><<<grid, block, 0, st>>>(
-          (const uint16_t *)P, (const uint16_t *)qkv, ldq, n_heads, causal ? 1 : 0, r.off, r.sbase,
-          r.items, (uint16_t *)ctx, ldc);
+      pv_mfma_kernel<DP><<<grid, dim3(64), 0, st>>>((const uint16_t *)P, (const uint16_t *)qkv, ldq,
+                                                    n_heads, causal ? 1 : 0, r.off, r.sbase,
+                                                    r.items, (uint16_t *)ctx, ldc);
     else
       pv_kernel<float, float, DP><<<grid, block, 0, st>>>((const float *)P, (const float *)qkv, ldq,
                                                           n_heads, causal ? 1 : 0, r.off, r.sbase,

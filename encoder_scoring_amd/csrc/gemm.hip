@@ -11,6 +11,9 @@
 //
 // Epilogues fuse what follows each GEMM: bias (QKV), bias + exact GELU (FFN1),
 // bias + fp32 residual (attention output, FFN2).
+#include <cmath>
+#include <cstdlib>
+
 #include "device.h"
 #include "kernels.h"
 
@@ -21,70 +24,128 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
+constexpr int kBK = 64;       // K step per pipeline stage (128 bytes of bf16 per row)
+constexpr int kThreads = 256; // 4 wavefronts in a 2 x 2 grid
+
+// LDS tile layout: rows of 64 bf16 (128 B, no padding); the eight 16-byte
+// k-chunks of row r are stored XOR-swizzled (slot = chunk ^ (r & 7)), so the
+// MFMA fragment reads of 8 consecutive rows at one k-chunk hit 8 different
+// bank groups and the row-wise 16-byte writes stay contiguous.
+__device__ __forceinline__ int swz(int row, int chunk) { return row * kBK + ((chunk ^ (row & 7)) << 3); }
+
+// Staging registers of one pipeline stage: ROWS x 64 bf16 spread over the
+// block, 16 bytes per thread per chunk, held in ONE vector value so it lives
+// in VGPRs (an array here would be demoted to scratch or LDS).
+template <int ROWS>
+struct Stage {
+  static constexpr int C = ROWS * kBK / 8 / kThreads;
+  typedef uint32_t vec_t __attribute__((ext_vector_type(4 * C)));
+  vec_t v;
+};
+
+template <int ROWS>
+__device__ __forceinline__ void load_stage(Stage<ROWS> &r, const uint16_t *__restrict__ g,
+                                           int64_t ld, int k0, int tid) {
+#pragma unroll
+  for (int i = 0; i < Stage<ROWS>::C; ++i) {
+    const int c = tid + kThreads * i, row = c >> 3, kc = c & 7;
+    const uint4 u = *reinterpret_cast<const uint4 *>(g + row * ld + k0 + kc * 8);
+    r.v[4 * i + 0] = u.x;
+    r.v[4 * i + 1] = u.y;
+    r.v[4 * i + 2] = u.z;
+    r.v[4 * i + 3] = u.w;
+  }
+}
+
+template <int ROWS>
+__device__ __forceinline__ void store_stage(const Stage<ROWS> &r, uint16_t *s, int tid) {
+#pragma unroll
+  for (int i = 0; i < Stage<ROWS>::C; ++i) {
+    const int c = tid + kThreads * i, row = c >> 3, kc = c & 7;
+    *reinterpret_cast<uint4 *>(s + swz(row, kc)) =
+        make_uint4(r.v[4 * i + 0], r.v[4 * i + 1], r.v[4 * i + 2], r.v[4 * i + 3]);
+  }
+}
+
+// Four consecutive outputs (m, n..n+3) of one lane.
 template <int EPI>
-__device__ __forceinline__ void epi_store(void *out, const float *__restrict__ res, int ldc,
-                                          int64_t m, int n, float v) {
-  if (EPI == kEpiBias) {
-    static_cast<uint16_t *>(out)[m * ldc + n] = f2bf(v);
-  } else if (EPI == kEpiGelu) {
-    static_cast<uint16_t *>(out)[m * ldc + n] = f2bf(gelu_erf(v));
-  } else if (EPI == kEpiResidual) {
-    static_cast<float *>(out)[m * ldc + n] = v + res[m * ldc + n];
-  } else {
-    static_cast<float *>(out)[m * ldc + n] = v;
+__device__ __forceinline__ void epi_store4(void *out, const float *res, int ldc, int64_t m, int n,
+                                           int N, float4 v, const float *__restrict__ bias) {
+  const int64_t o = m * ldc + n;
+  if (n + 3 < N) {
+    const float4 b = *reinterpret_cast<const float4 *>(bias + n);
+    v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w;
+    if (EPI == kEpiBias || EPI == kEpiGelu) {
+      if (EPI == kEpiGelu) {
+        v.x = gelu_erf(v.x); v.y = gelu_erf(v.y); v.z = gelu_erf(v.z); v.w = gelu_erf(v.w);
+      }
+      uint2 u;
+      u.x = (uint32_t)f2bf(v.x) | ((uint32_t)f2bf(v.y) << 16);
+      u.y = (uint32_t)f2bf(v.z) | ((uint32_t)f2bf(v.w) << 16);
+      *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(out) + o) = u;
+    } else {
+      if (EPI == kEpiResidual) {
+        const float4 r = *reinterpret_cast<const float4 *>(res + o);
+        v.x += r.x; v.y += r.y; v.z += r.z; v.w += r.w;
+      }
+      *reinterpret_cast<float4 *>(static_cast<float *>(out) + o) = v;
+    }
+    return;
+  }
+  const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if (n + e >= N) break;
+    float x = vv[e] + bias[n + e];
+    if (EPI == kEpiBias) static_cast<uint16_t *>(out)[o + e] = f2bf(x);
+    else if (EPI == kEpiGelu) static_cast<uint16_t *>(out)[o + e] = f2bf(gelu_erf(x));
+    else if (EPI == kEpiResidual) static_cast<float *>(out)[o + e] = x + res[o + e];
+    else static_cast<float *>(out)[o + e] = x;
   }
 }
 
 // ---------------------------------------------------------------- bf16 MFMA
 //
-// Block tile BM x BN, K step 64, 4 wavefronts in a 2 x 2 grid, each owning a
-// (BM/2) x (BN/2) sub-tile of 32 x 32 MFMA tiles.  Tiles of A and W are
-// staged through LDS, double-buffered: the global loads of step k+1 are in
-// flight while the matrix cores work on step k, and one barrier per step
-// separates the buffers.  LDS rows are padded to 72 bf16 (144 B) so the
-// 16-byte fragment reads of a wavefront hit distinct banks.
+// Block tile BM x BN, K step 64, four wavefronts in a 2 x 2 grid each owning a
+// (BM/2) x (BN/2) sub-tile of 32 x 32 MFMA tiles.  A and W tiles are staged
+// through LDS, double-buffered: the global loads of step k+1 are issued into
+// registers before the matrix cores start on step k and land in the other LDS
+// buffer afterwards, one barrier per step.  The MFMA is issued as W x A so a
+// lane's accumulators hold four consecutive output columns of one row, which
+// the epilogue writes as one vector.
 template <int BM, int BN, int EPI>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t *__restrict__ A, int lda,
-                                                        const uint16_t *__restrict__ W,
-                                                        const float *__restrict__ bias,
-                                                        const float *res, void *out, int ldc,
-                                                        int M, int N, int K) {
-  constexpr int BK = 64, PITCH = BK + 8;
+__global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
+    const uint16_t *__restrict__ A, int lda, const uint16_t *__restrict__ W,
+    const float *__restrict__ bias, const float *res, void *out, int ldc, int M, int N, int K,
+    int tiles_m, int tiles_n) {
   constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
-  constexpr int CA = BM * BK / 8 / 256, CB = BN * BK / 8 / 256;  // 16-byte chunks per thread
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * PITCH];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * PITCH];
+  static_assert(Stage<BM>::C >= 1 && Stage<BN>::C >= 1 && TM >= 1 && TN >= 1, "tile too small");
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * kBK];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * kBK];
+
+  // XCD-aware order: consecutive block ids go to different XCDs (8 of them),
+  // so remap them so each XCD works on a contiguous run of tiles, and walk
+  // the tiles in groups of 8 M-tiles so neighbours share A rows and W rows
+  // inside one XCD's L2.
+  const int nblk = tiles_m * tiles_n;
+  int bid = blockIdx.x;
+  {
+    const int per = (nblk + 7) / 8, xcd = bid & 7, loc = bid >> 3;
+    const int full = nblk - (per - 1) * 8;  // XCDs that receive `per` blocks
+    bid = xcd < full ? xcd * per + loc : full * per + (xcd - full) * (per - 1) + loc;
+  }
+  constexpr int G = 8;
+  const int group = bid / (G * tiles_n), first_m = group * G;
+  const int gm = min(G, tiles_m - first_m);
+  const int tm = first_m + (bid % (G * tiles_n)) % gm;
+  const int tn = (bid % (G * tiles_n)) / gm;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int64_t m0 = (int64_t)blockIdx.y * BM;
-  const int n0 = blockIdx.x * BN;
-
-  uint4 ra[CA], rb[CB];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < CA; ++i) {
-      const int c = tid + 256 * i, row = c >> 3, kc = c & 7;
-      ra[i] = *reinterpret_cast<const uint4 *>(A + (m0 + row) * lda + k0 + kc * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < CB; ++i) {
-      const int c = tid + 256 * i, row = c >> 3, kc = c & 7;
-      rb[i] = *reinterpret_cast<const uint4 *>(W + (int64_t)(n0 + row) * K + k0 + kc * 8);
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < CA; ++i) {
-      const int c = tid + 256 * i, row = c >> 3, kc = c & 7;
-      *reinterpret_cast<uint4 *>(&sA[buf][row * PITCH + kc * 8]) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < CB; ++i) {
-      const int c = tid + 256 * i, row = c >> 3, kc = c & 7;
-      *reinterpret_cast<uint4 *>(&sB[buf][row * PITCH + kc * 8]) = rb[i];
-    }
-  };
+  const int64_t m0 = (int64_t)tm * BM;
+  const int n0 = tn * BN;
+  const uint16_t *Ag = A + m0 * lda;
+  const uint16_t *Wg = W + (int64_t)n0 * K;
 
   f32x16 acc[TM][TN];
 #pragma unroll
@@ -94,48 +155,64 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t *__restri
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int nk = K / BK;
-  gload(0);
-  lstore(0);
+  Stage<BM> ra;
+  Stage<BN> rb;
+  load_stage<BM>(ra, Ag, lda, 0, tid);
+  load_stage<BN>(rb, Wg, K, 0, tid);
+  store_stage<BM>(ra, sA[0], tid);
+  store_stage<BN>(rb, sB[0], tid);
   __syncthreads();
-  const int fr = lane & 31, fk = (lane >> 5) * 8;  // fragment row and k offset of this lane
+
+  const int fr = lane & 31, fh = lane >> 5;  // fragment row, k-half of this lane
+  const int nk = K / kBK;
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
-    const uint16_t *a_s = sA[cur] + (wm * WM + fr) * PITCH + fk;
-    const uint16_t *b_s = sB[cur] + (wn * WN + fr) * PITCH + fk;
+    const bool more = kt + 1 < nk;
+    if (more) {
+      load_stage<BM>(ra, Ag, lda, (kt + 1) * kBK, tid);
+      load_stage<BN>(rb, Wg, K, (kt + 1) * kBK, tid);
+    }
+    const uint16_t *a_s = sA[cur] + (wm * WM + fr) * kBK;
+    const uint16_t *b_s = sB[cur] + (wn * WN + fr) * kBK;
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+      const int slot = ((kk * 2 + fh) ^ (fr & 7)) << 3;
       bf16x8 a[TM], b[TN];
 #pragma unroll
       for (int i = 0; i < TM; ++i)
-        a[i] = *reinterpret_cast<const bf16x8 *>(a_s + i * 32 * PITCH + kk * 16);
+        a[i] = *reinterpret_cast<const bf16x8 *>(a_s + i * 32 * kBK + slot);
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        b[j] = *reinterpret_cast<const bf16x8 *>(b_s + j * 32 * PITCH + kk * 16);
+        b[j] = *reinterpret_cast<const bf16x8 *>(b_s + j * 32 * kBK + slot);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) lstore(cur ^ 1);
+    if (more) {
+      store_stage<BM>(ra, sA[cur ^ 1], tid);
+      store_stage<BN>(rb, sB[cur ^ 1], tid);
+    }
     __syncthreads();
   }
 
-  // 32x32 accumulator layout: lane holds column (lane & 31); register r holds
-  // row 8 * (r / 4) + 4 * (lane / 32) + (r % 4).
+  // acc[i][j] = D[n][m] of the W x A product: lane holds row m = lane & 31
+  // and register r holds column 8 * (r / 4) + 4 * (lane / 32) + (r % 4).
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
+    const int64_t m = m0 + wm * WM + i * 32 + fr;
+    if (m >= M) continue;
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const int n = n0 + wn * WN + j * 32 + (lane & 31);
-      if (n >= N) continue;
-      const float bn = bias[n];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t m = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (m < M) epi_store<EPI>(out, res, ldc, m, n, acc[i][j][r] + bn);
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + wn * WN + j * 32 + 8 * g + 4 * fh;
+        if (n < N)
+          epi_store4<EPI>(out, res, ldc, m, n, N,
+                          make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1],
+                                      acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]),
+                          bias);
       }
     }
   }
@@ -197,19 +274,20 @@ template <int BM, int BN>
 hipError_t go_bf16(const uint16_t *A, int lda, const uint16_t *W, const float *bias,
                    const float *res, void *out, int ldc, int M, int N, int K, int epi,
                    hipStream_t st) {
-  const dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM), block(256);
+  const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
+  const dim3 grid(tm * tn), block(kThreads);
   switch (epi) {
     case kEpiBias:
-      gemm_bf16_kernel<BM, BN, kEpiBias><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K);
+      gemm_bf16_kernel<BM, BN, kEpiBias><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K, tm, tn);
       break;
     case kEpiGelu:
-      gemm_bf16_kernel<BM, BN, kEpiGelu><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K);
+      gemm_bf16_kernel<BM, BN, kEpiGelu><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K, tm, tn);
       break;
     case kEpiResidual:
-      gemm_bf16_kernel<BM, BN, kEpiResidual><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K);
+      gemm_bf16_kernel<BM, BN, kEpiResidual><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K, tm, tn);
       break;
     case kEpiF32:
-      gemm_bf16_kernel<BM, BN, kEpiF32><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K);
+      gemm_bf16_kernel<BM, BN, kEpiF32><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K, tm, tn);
       break;
     default:
       return hipErrorInvalidValue;
@@ -217,19 +295,49 @@ hipError_t go_bf16(const uint16_t *A, int lda, const uint16_t *W, const float *b
   return hipGetLastError();
 }
 
+constexpr int kCUs = 256;
+
 }  // namespace
 
-// Both tile shapes issue the same MFMA over K in the same order and K is never
-// split, so each output's accumulation order does not depend on the tile
-// chosen or on the other sequences in the batch.
+// Tile shape for an M x N x K problem.  Measured on MI355X (bf16, this
+// kernel): 128 x 128 tiles (two blocks per CU) win once there are enough of
+// them to fill the chip twice, or K is long; below that 128 x 64 tiles (three
+// blocks per CU) keep more CUs busy.  Every tile shape issues the same MFMA
+// over K in the same order and K is never split, so each output's
+// accumulation order does not depend on the tile chosen or on the other
+// sequences in the batch.
+int gemm_tile_index(int M, int N, int K) {
+  const int64_t b128 = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
+  if (b128 >= 4 * kCUs || (K >= 2048 && b128 >= 2 * kCUs)) return 3;
+  return 4;
+}
+
+hipError_t launch_gemm_bf16_tile(int tile, const uint16_t *A, int lda, const uint16_t *W,
+                                 const float *bias, const float *res, void *out, int ldc, int M,
+                                 int N, int K, int epi, hipStream_t st) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (K <= 0 || K % kBK) return hipErrorInvalidValue;
+  switch (tile) {
+    case 0: return go_bf16<256, 256>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
+    case 1: return go_bf16<256, 128>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
+    case 2: return go_bf16<128, 256>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
+    case 3: return go_bf16<128, 128>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
+    case 4: return go_bf16<128, 64>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
+    case 5: return go_bf16<64, 128>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// ES_GEMM_TILE=<0..5> forces one tile shape (for tuning sweeps); unset = model.
 hipError_t launch_gemm_bf16(const uint16_t *A, int lda, const uint16_t *W, const float *bias,
                             const float *res, void *out, int ldc, int M, int N, int K, int epi,
                             hipStream_t st) {
-  if (M <= 0 || N <= 0) return hipSuccess;
-  if (K <= 0 || K % 64) return hipErrorInvalidValue;
-  const int64_t tiles_big = (int64_t)((M + 255) / 256) * ((N + 127) / 128);
-  if (tiles_big >= 512) return go_bf16<256, 128>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
-  return go_bf16<128, 128>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
+  static const int forced = [] {
+    const char *e = std::getenv("ES_GEMM_TILE");
+    return e ? std::atoi(e) : -1;
+  }();
+  const int tile = forced >= 0 ? forced : gemm_tile_index(M, N, K);
+  return launch_gemm_bf16_tile(tile, A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
 }
 
 hipError_t launch_gemm_f32(const float *A, int lda, const float *W, const float *bias,

@@ -12,7 +12,7 @@
 //   P     act  ragged        softmax output, same indexing as S
 // act = bf16 for bf16 models (fp32 accumulation everywhere), fp32 otherwise.
 // Hp, Kc, Fp round widths up to 64 (zero columns); dp rounds the head dim up
-// to a power of two >= 16 by inserting zero rows into W_qkv and zero columns
+// to a power of two >= 32 by inserting zero rows into W_qkv and zero columns
 // into W_o, which leaves every result unchanged.
 #include <algorithm>
 #include <cinttypes>
@@ -45,7 +45,7 @@ struct DevLayer {
 };
 
 int pow2_at_least(int v) {
-  int p = 16;
+  int p = 32;
   while (p < v) p <<= 1;
   return p;
 }
@@ -79,6 +79,16 @@ struct es_model {
   std::vector<void *> allocs;
   int64_t device_bytes = 0;
   std::vector<int32_t> order_scratch;
+  // profiling (es_profile_enable / es_profile_collect)
+  struct Rec {
+    int cls;
+    hipEvent_t a, b;
+    double flops, bytes;
+  };
+  uint32_t prof_mask = 0;
+  std::vector<hipEvent_t> ev_pool;
+  size_t ev_used = 0;
+  std::vector<Rec> prof_recs;
 };
 
 namespace {
@@ -103,6 +113,7 @@ void release(es_model *m) {
   if (m->meta_host) (void)hipHostFree(m->meta_host);
   if (m->meta_dev) (void)hipFree(m->meta_dev);
   if (m->meta_ev) (void)hipEventDestroy(m->meta_ev);
+  for (hipEvent_t e : m->ev_pool) (void)hipEventDestroy(e);
   delete m;
 }
 
@@ -237,6 +248,7 @@ struct BatchLayout {
   size_t off = 0, sbase = 0, items = 0, src = 0, dest = 0;
   bool has_src = false, has_dest = false;
   int n = 0, n_items = 0, max_len = 0, n_tokens = 0;
+  int64_t pairs = 0;  // visible (query, key) pairs summed over heads
 };
 
 size_t push_bytes(std::vector<uint8_t> &buf, const void *p, size_t bytes) {
@@ -264,6 +276,7 @@ es_status add_batch(es_model *m, const int32_t *h_off, int32_t n, const int32_t 
     if (h_off[i + 1] > m->max_tokens)
       return fail(ES_ERR_CAPACITY, "batch has more than max_tokens=%" PRId64 " tokens", m->max_tokens);
     max_len = std::max<int>(max_len, (int)len);
+    L->pairs += (int64_t)m->A * (m->causal ? len * (len + 1) / 2 : len * len);
     sbase[i] = score;
     score += (int64_t)m->A * len * es::score_ld((int)len);
   }
@@ -345,69 +358,140 @@ es::Ragged ragged_of(const es_model *m, const BatchLayout &L) {
 }
 
 // One batch given by host offsets: validate, stage, upload.
-es_status prepare(es_model *m, const int32_t *h_off, int32_t n, hipStream_t st, es::Ragged *r) {
+es_status prepare(es_model *m, const int32_t *h_off, int32_t n, hipStream_t st, es::Ragged *r,
+                  int64_t *pairs) {
   m->meta_asm.clear();
   BatchLayout L;
   es_status s = add_batch(m, h_off, n, nullptr, nullptr, &L);
   if (s != ES_OK) return s;
   if ((s = upload_meta(m, st)) != ES_OK) return s;
   *r = ragged_of(m, L);
+  *pairs = L.pairs;
   return ES_OK;
 }
 
-es_status gemm(es_model *m, const void *A, int lda, const void *W, const float *bias,
-               const float *res, void *out, int ldc, int M, int N, int K, int epi, hipStream_t st) {
+// ---- profiling: an event pair around each launch of a kernel class, with
+// the algorithmic flops and HBM bytes of that launch (what the method must
+// compute and move, no padding), aggregated by es_profile_collect.
+struct Prof {
+  es_model *m;
+  hipStream_t st;
+  int cls;
+  hipEvent_t a = nullptr;
+  Prof(es_model *m_, hipStream_t st_, int cls_) : m(m_), st(st_), cls(cls_) {
+    if (m->prof_mask & (1u << cls)) a = next_event(m), (void)hipEventRecord(a, st);
+  }
+  void done(double flops, double bytes) {
+    if (!a) return;
+    hipEvent_t b = next_event(m);
+    (void)hipEventRecord(b, st);
+    m->prof_recs.push_back({cls, a, b, flops, bytes});
+  }
+  static hipEvent_t next_event(es_model *m) {
+    if (m->ev_used == m->ev_pool.size()) {
+      hipEvent_t e = nullptr;
+      (void)hipEventCreate(&e);
+      m->ev_pool.push_back(e);
+    }
+    return m->ev_pool[m->ev_used++];
+  }
+};
+
+es_status gemm(es_model *m, int cls, const void *A, int lda, const void *W, const float *bias,
+               const float *res, void *out, int ldc, int M, int N, int K, int Kreal, int epi,
+               hipStream_t st) {
+  Prof p(m, st, cls);
   if (m->bf16)
     HIP_TRY(es::launch_gemm_bf16((const uint16_t *)A, lda, (const uint16_t *)W, bias, res, out, ldc,
                                  M, N, K, epi, st));
   else
     HIP_TRY(es::launch_gemm_f32((const float *)A, lda, (const float *)W, bias, res, (float *)out, ldc,
                                 M, N, K, epi, st));
+  const double a = m->bf16 ? 2.0 : 4.0, out_b = (epi == es::kEpiBias || epi == es::kEpiGelu) ? a : 4.0;
+  p.done(2.0 * M * N * Kreal,
+         (double)M * Kreal * a + (double)N * Kreal * a + (double)M * N * out_b +
+             (epi == es::kEpiResidual ? 4.0 * M * N : 0.0) + 4.0 * N);
   return ES_OK;
 }
 
-es_status attention(es_model *m, const es::Ragged &r, hipStream_t st) {
+es_status attention(es_model *m, const es::Ragged &r, int64_t pairs, hipStream_t st) {
   const float scale = 1.0f / std::sqrt((float)m->d);
-  HIP_TRY(es::launch_scores(m->bf16, m->qkv, m->Nqkv, m->A, m->dp, scale, m->causal, r, m->S, st));
-  HIP_TRY(es::launch_softmax(m->bf16, m->S, m->Pb, r, m->A, m->causal, st));
-  HIP_TRY(es::launch_pv(m->bf16, m->Pb, m->qkv, m->Nqkv, m->A, m->dp, m->causal, r, m->ctx, m->Kc, st));
+  const double a = m->bf16 ? 2.0 : 4.0, T = r.n_tokens, Hd = (double)m->H;
+  {
+    Prof p(m, st, ES_KC_SCORES);
+    HIP_TRY(es::launch_scores(m->bf16, m->qkv, m->Nqkv, m->A, m->dp, scale, m->causal, r, m->S, st));
+    p.done(2.0 * m->d * pairs, 2.0 * T * Hd * a + 4.0 * pairs);
+  }
+  {
+    Prof p(m, st, ES_KC_SOFTMAX);
+    HIP_TRY(es::launch_softmax(m->bf16, m->S, m->Pb, r, m->A, m->causal, st));
+    p.done(4.0 * pairs, (4.0 + a) * pairs);
+  }
+  {
+    Prof p(m, st, ES_KC_PV);
+    HIP_TRY(es::launch_pv(m->bf16, m->Pb, m->qkv, m->Nqkv, m->A, m->dp, m->causal, r, m->ctx, m->Kc, st));
+    p.done(2.0 * m->d * pairs, a * pairs + 2.0 * T * Hd * a);
+  }
   return ES_OK;
 }
 
-es_status forward(es_model *m, const int32_t *d_ids, const es::Ragged &r, int n_layers,
-                  hipStream_t st) {
-  const int T = r.n_tokens, H = m->H;
+es_status layernorm(es_model *m, const float *x, const float *g, const float *b, int T, float *y,
+                    hipStream_t st) {
+  Prof p(m, st, ES_KC_LAYERNORM);
+  HIP_TRY(es::launch_layernorm(m->bf16, x, g, b, T, m->H, m->eps, y, m->xb, m->Hp, st));
+  const double a = m->bf16 ? 2.0 : 4.0;
+  p.done(8.0 * T * m->H, (double)T * m->H * (4.0 + a + (y ? 4.0 : 0.0)));
+  return ES_OK;
+}
+
+es_status forward(es_model *m, const int32_t *d_ids, const es::Ragged &r, int64_t pairs,
+                  int n_layers, hipStream_t st) {
+  const int T = r.n_tokens, H = m->H, F = m->F, Hd = m->A * m->d;
+  const double a = m->bf16 ? 2.0 : 4.0;
   es_status s;
-  HIP_TRY(es::launch_embed(m->bf16, m->bf16, !m->pre_ln, d_ids, r, m->tok_emb, m->pos_emb, m->V, H,
-                           m->norm_g, m->norm_b, m->eps, m->x, m->xb, m->Hp, m->flag, st));
+  {
+    Prof p(m, st, ES_KC_EMBED);
+    HIP_TRY(es::launch_embed(m->bf16, m->bf16, !m->pre_ln, d_ids, r, m->tok_emb, m->pos_emb, m->V, H,
+                             m->norm_g, m->norm_b, m->eps, m->x, m->xb, m->Hp, m->flag, st));
+    p.done(10.0 * T * H, (double)T * H * (2.0 * a + 4.0 + (m->pre_ln ? 0.0 : a)) + 4.0 * T);
+  }
   for (int l = 0; l < n_layers; ++l) {
     const DevLayer &D = m->layers[l];
     if (!m->pre_ln) {
-      if ((s = gemm(m, m->xb, m->Hp, D.w_qkv, D.b_qkv, nullptr, m->qkv, m->Nqkv, T, m->Nqkv, m->Hp,
-                    es::kEpiBias, st)) != ES_OK) return s;
-      if ((s = attention(m, r, st)) != ES_OK) return s;
-      if ((s = gemm(m, m->ctx, m->Kc, D.w_o, D.b_o, m->x, m->y, H, T, H, m->Kc, es::kEpiResidual,
-                    st)) != ES_OK) return s;
-      HIP_TRY(es::launch_layernorm(m->bf16, m->y, D.ln1_g, D.ln1_b, T, H, m->eps, m->x, m->xb, m->Hp, st));
-      if ((s = gemm(m, m->xb, m->Hp, D.w_1, D.b_1, nullptr, m->hmid, m->Fp, T, m->F, m->Hp,
-                    es::kEpiGelu, st)) != ES_OK) return s;
-      if ((s = gemm(m, m->hmid, m->Fp, D.w_2, D.b_2, m->x, m->y, H, T, H, m->Fp, es::kEpiResidual,
-                    st)) != ES_OK) return s;
-      HIP_TRY(es::launch_layernorm(m->bf16, m->y, D.ln2_g, D.ln2_b, T, H, m->eps, m->x, m->xb, m->Hp, st));
+      if ((s = gemm(m, ES_KC_QKV, m->xb, m->Hp, D.w_qkv, D.b_qkv, nullptr, m->qkv, m->Nqkv, T,
+                    m->Nqkv, m->Hp, H, es::kEpiBias, st)) != ES_OK) return s;
+      if ((s = attention(m, r, pairs, st)) != ES_OK) return s;
+      if ((s = gemm(m, ES_KC_OPROJ, m->ctx, m->Kc, D.w_o, D.b_o, m->x, m->y, H, T, H, m->Kc, Hd,
+                    es::kEpiResidual, st)) != ES_OK) return s;
+      if ((s = layernorm(m, m->y, D.ln1_g, D.ln1_b, T, m->x, st)) != ES_OK) return s;
+      if ((s = gemm(m, ES_KC_FFN1, m->xb, m->Hp, D.w_1, D.b_1, nullptr, m->hmid, m->Fp, T, F, m->Hp,
+                    H, es::kEpiGelu, st)) != ES_OK) return s;
+      if ((s = gemm(m, ES_KC_FFN2, m->hmid, m->Fp, D.w_2, D.b_2, m->x, m->y, H, T, H, m->Fp, F,
+                    es::kEpiResidual, st)) != ES_OK) return s;
+      if ((s = layernorm(m, m->y, D.ln2_g, D.ln2_b, T, m->x, st)) != ES_OK) return s;
     } else {
-      HIP_TRY(es::launch_layernorm(m->bf16, m->x, D.ln1_g, D.ln1_b, T, H, m->eps, nullptr, m->xb, m->Hp, st));
-      if ((s = gemm(m, m->xb, m->Hp, D.w_qkv, D.b_qkv, nullptr, m->qkv, m->Nqkv, T, m->Nqkv, m->Hp,
-                    es::kEpiBias, st)) != ES_OK) return s;
-      if ((s = attention(m, r, st)) != ES_OK) return s;
-      if ((s = gemm(m, m->ctx, m->Kc, D.w_o, D.b_o, m->x, m->x, H, T, H, m->Kc, es::kEpiResidual,
-                    st)) != ES_OK) return s;
-      HIP_TRY(es::launch_layernorm(m->bf16, m->x, D.ln2_g, D.ln2_b, T, H, m->eps, nullptr, m->xb, m->Hp, st));
-      if ((s = gemm(m, m->xb, m->Hp, D.w_1, D.b_1, nullptr, m->hmid, m->Fp, T, m->F, m->Hp,
-                    es::kEpiGelu, st)) != ES_OK) return s;
-      if ((s = gemm(m, m->hmid, m->Fp, D.w_2, D.b_2, m->x, m->x, H, T, H, m->Fp, es::kEpiResidual,
-                    st)) != ES_OK) return s;
+      if ((s = layernorm(m, m->x, D.ln1_g, D.ln1_b, T, nullptr, st)) != ES_OK) return s;
+      if ((s = gemm(m, ES_KC_QKV, m->xb, m->Hp, D.w_qkv, D.b_qkv, nullptr, m->qkv, m->Nqkv, T,
+                    m->Nqkv, m->Hp, H, es::kEpiBias, st)) != ES_OK) return s;
+      if ((s = attention(m, r, pairs, st)) != ES_OK) return s;
+      if ((s = gemm(m, ES_KC_OPROJ, m->ctx, m->Kc, D.w_o, D.b_o, m->x, m->x, H, T, H, m->Kc, Hd,
+                    es::kEpiResidual, st)) != ES_OK) return s;
+      if ((s = layernorm(m, m->x, D.ln2_g, D.ln2_b, T, nullptr, st)) != ES_OK) return s;
+      if ((s = gemm(m, ES_KC_FFN1, m->xb, m->Hp, D.w_1, D.b_1, nullptr, m->hmid, m->Fp, T, F, m->Hp,
+                    H, es::kEpiGelu, st)) != ES_OK) return s;
+      if ((s = gemm(m, ES_KC_FFN2, m->hmid, m->Fp, D.w_2, D.b_2, m->x, m->x, H, T, H, m->Fp, F,
+                    es::kEpiResidual, st)) != ES_OK) return s;
     }
   }
+  (void)a;
+  return ES_OK;
+}
+
+es_status head(es_model *m, const es::Ragged &r, float offset, float *rewards, hipStream_t st) {
+  Prof p(m, st, ES_KC_HEAD);
+  HIP_TRY(es::launch_head(m->pre_ln, m->x, m->H, r, m->norm_g, m->norm_b, m->eps, m->head_w,
+                          m->head_b, offset, rewards, st));
+  p.done(2.0 * r.n_seqs * m->H, 8.0 * r.n_seqs * m->H);
   return ES_OK;
 }
 
@@ -482,10 +566,10 @@ extern "C" es_status es_score_batch(es_model *m, const int32_t *d_token_ids, con
   if (!d_token_ids || !d_rewards) return fail(ES_ERR_ARG, "NULL device pointer");
   hipStream_t st = static_cast<hipStream_t>(stream);
   es::Ragged r;
-  if ((s = prepare(m, h_offsets, n_seqs, st, &r)) != ES_OK) return s;
-  if ((s = forward(m, d_token_ids, r, m->L, st)) != ES_OK) return s;
-  HIP_TRY(es::launch_head(m->pre_ln, m->x, m->H, r, m->norm_g, m->norm_b, m->eps, m->head_w,
-                          m->head_b, m->offset, d_rewards, st));
+  int64_t pairs = 0;
+  if ((s = prepare(m, h_offsets, n_seqs, st, &r, &pairs)) != ES_OK) return s;
+  if ((s = forward(m, d_token_ids, r, pairs, m->L, st)) != ES_OK) return s;
+  if ((s = head(m, r, m->offset, d_rewards, st)) != ES_OK) return s;
   es::clear_error();
   return ES_OK;
 }
@@ -538,9 +622,8 @@ extern "C" es_status es_score_requests(es_model *m, const int32_t *d_token_ids,
   // a3..a13: every batch through the layers; the head scatters to request order
   for (int32_t b = 0; b < nb; ++b) {
     const es::Ragged r = ragged_of(m, layouts[b]);
-    if ((s = forward(m, d_token_ids, r, m->L, st)) != ES_OK) return s;
-    HIP_TRY(es::launch_head(m->pre_ln, m->x, m->H, r, m->norm_g, m->norm_b, m->eps, m->head_w,
-                            m->head_b, m->offset, d_rewards, st));
+    if ((s = forward(m, d_token_ids, r, layouts[b].pairs, m->L, st)) != ES_OK) return s;
+    if ((s = head(m, r, m->offset, d_rewards, st)) != ES_OK) return s;
   }
   if (stats) {
     stats->n_batches = nb;
@@ -561,8 +644,9 @@ extern "C" es_status es_forward_hidden(es_model *m, const int32_t *d_token_ids,
   if (n_layers < 0 || n_layers > m->L) return fail(ES_ERR_ARG, "n_layers=%d outside [0, %d]", n_layers, m->L);
   hipStream_t st = static_cast<hipStream_t>(stream);
   es::Ragged r;
-  if ((s = prepare(m, h_offsets, n_seqs, st, &r)) != ES_OK) return s;
-  if ((s = forward(m, d_token_ids, r, n_layers, st)) != ES_OK) return s;
+  int64_t pairs = 0;
+  if ((s = prepare(m, h_offsets, n_seqs, st, &r, &pairs)) != ES_OK) return s;
+  if ((s = forward(m, d_token_ids, r, pairs, n_layers, st)) != ES_OK) return s;
   HIP_TRY(hipMemcpyAsync(d_hidden, m->x, (size_t)r.n_tokens * m->H * 4, hipMemcpyDeviceToDevice, st));
   return ES_OK;
 }
@@ -588,10 +672,10 @@ extern "C" es_status es_calibrate_offset(es_model *m, const int32_t *d_token_ids
   if (!offset_out || !d_token_ids) return fail(ES_ERR_ARG, "NULL argument");
   hipStream_t st = static_cast<hipStream_t>(stream);
   es::Ragged r;
-  if ((s = prepare(m, h_offsets, n_ref, st, &r)) != ES_OK) return s;
-  if ((s = forward(m, d_token_ids, r, m->L, st)) != ES_OK) return s;
-  HIP_TRY(es::launch_head(m->pre_ln, m->x, m->H, r, m->norm_g, m->norm_b, m->eps, m->head_w,
-                          m->head_b, 0.0f, m->rew, st));
+  int64_t pairs = 0;
+  if ((s = prepare(m, h_offsets, n_ref, st, &r, &pairs)) != ES_OK) return s;
+  if ((s = forward(m, d_token_ids, r, pairs, m->L, st)) != ES_OK) return s;
+  if ((s = head(m, r, 0.0f, m->rew, st)) != ES_OK) return s;
   std::vector<float> raw((size_t)n_ref);
   HIP_TRY(hipMemcpyAsync(raw.data(), m->rew, raw.size() * 4, hipMemcpyDeviceToHost, st));
   HIP_TRY(hipStreamSynchronize(st));
@@ -614,4 +698,39 @@ extern "C" es_status es_check_device_errors(es_model *m, void *stream) {
     return fail(ES_ERR_DEVICE_FLAG, "a token id outside [0, %d) was seen (row 0 used instead)", m->V);
   }
   return ES_OK;
+}
+
+// ------------------------------------------------------------------ profiling
+
+extern "C" es_status es_profile_enable(es_model *m, uint32_t class_mask) {
+  if (!m) return fail(ES_ERR_ARG, "model handle is NULL");
+  m->prof_mask = class_mask & ((1u << ES_KC_COUNT) - 1);
+  m->prof_recs.clear();
+  m->ev_used = 0;
+  return ES_OK;
+}
+
+extern "C" es_status es_profile_collect(es_model *m, es_kernel_stat_t *out) {
+  if (!m || !out) return fail(ES_ERR_ARG, "NULL argument");
+  for (int c = 0; c < ES_KC_COUNT; ++c) out[c] = es_kernel_stat_t{c, 0, 0.0, 0.0, 0.0};
+  if (!m->prof_recs.empty()) HIP_TRY(hipEventSynchronize(m->prof_recs.back().b));
+  for (const auto &rec : m->prof_recs) {
+    float ms = 0.f;
+    HIP_TRY(hipEventElapsedTime(&ms, rec.a, rec.b));
+    es_kernel_stat_t &o = out[rec.cls];
+    o.launches += 1;
+    o.total_ms += ms;
+    o.flops += rec.flops;
+    o.bytes += rec.bytes;
+  }
+  m->prof_recs.clear();
+  m->ev_used = 0;
+  return ES_OK;
+}
+
+extern "C" const char *es_kernel_class_name(int32_t cls) {
+  static const char *names[ES_KC_COUNT] = {"embed", "qkv_gemm", "scores", "softmax", "pv",
+                                           "oproj_gemm", "layernorm", "ffn1_gemm", "ffn2_gemm",
+                                           "head"};
+  return (cls >= 0 && cls < ES_KC_COUNT) ? names[cls] : "";
 }

@@ -289,6 +289,40 @@ es_status es_op_gemm_bf16(const uint16_t *d_a, int32_t lda, const uint16_t *d_w,
                           const float *d_bias, const float *d_res, void *d_out, int32_t ldc,
                           int32_t M, int32_t N, int32_t K, int32_t epilogue, void *stream);
 
+/* ------------------------------------------------------------- profiling */
+
+/* Kernel classes of the hot path, in launch order within a layer. */
+enum {
+  ES_KC_EMBED = 0, ES_KC_QKV = 1, ES_KC_SCORES = 2, ES_KC_SOFTMAX = 3, ES_KC_PV = 4,
+  ES_KC_OPROJ = 5, ES_KC_LAYERNORM = 6, ES_KC_FFN1 = 7, ES_KC_FFN2 = 8, ES_KC_HEAD = 9,
+  ES_KC_COUNT = 10
+};
+
+typedef struct {
+  int32_t kernel_class; /* ES_KC_*                                                */
+  int32_t launches;     /* launches recorded since the last collect               */
+  double total_ms;      /* sum of HIP-event durations around those launches       */
+  double flops;         /* algorithmic flops of those launches (no padding)       */
+  double bytes;         /* algorithmic HBM bytes (each operand read / written once) */
+} es_kernel_stat_t;
+
+/*
+ * es_profile_enable -- from the next call on, record a HIP event pair on the
+ * call's stream around every launch of the classes in `class_mask`
+ * (bit ES_KC_x), together with that launch's algorithmic flops and bytes.
+ * 0 disables.  Clears earlier records.
+ */
+es_status es_profile_enable(es_model *m, uint32_t class_mask);
+
+/*
+ * es_profile_collect -- wait for the last recorded event, then fill
+ * out[ES_KC_COUNT] with per-class totals and clear the records.
+ */
+es_status es_profile_collect(es_model *m, es_kernel_stat_t *out);
+
+/* Name of a kernel class ("ffn1_gemm", ...), "" if out of range. */
+const char *es_kernel_class_name(int32_t kernel_class);
+
 /* Thread-local message describing the last error on this thread ("" if none). */
 const char *es_last_error(void);
 
