@@ -28,10 +28,14 @@ constexpr int kBK = 64;       // K step per pipeline stage (128 bytes of bf16 pe
 constexpr int kThreads = 256; // 4 wavefronts in a 2 x 2 grid
 
 // LDS tile layout: rows of 64 bf16 (128 B, no padding); the eight 16-byte
-// k-chunks of row r are stored XOR-swizzled (slot = chunk ^ (r & 7)), so the
-// MFMA fragment reads of 8 consecutive rows at one k-chunk hit 8 different
-// bank groups and the row-wise 16-byte writes stay contiguous.
-__device__ __forceinline__ int swz(int row, int chunk) { return row * kBK + ((chunk ^ (row & 7)) << 3); }
+// k-chunks of row r are stored XOR-swizzled, slot = chunk ^ ((r >> 1) & 7).
+// gfx950 LDS serves a 16-byte read for 16 lanes per cycle from 64 four-byte
+// banks (256-byte lines): two consecutive 128-byte rows share a line, so the
+// swizzle must separate rows of equal parity -- then the 16 rows read by 16
+// lanes at one k-chunk land in 16 distinct bank groups (measured with
+// SQ_LDS_BANK_CONFLICT), and row-wise 16-byte writes stay contiguous.
+__device__ __forceinline__ int swz_slot(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
+__device__ __forceinline__ int swz(int row, int chunk) { return row * kBK + (swz_slot(row, chunk) << 3); }
 
 // Staging registers of one pipeline stage: ROWS x 64 bf16 spread over the
 // block, 16 bytes per thread per chunk, held in ONE vector value so it lives
@@ -108,13 +112,21 @@ __device__ __forceinline__ void epi_store4(void *out, const float *res, int ldc,
 //
 // Block tile BM x BN, K step 64, four wavefronts in a 2 x 2 grid each owning a
 // (BM/2) x (BN/2) sub-tile of 32 x 32 MFMA tiles.  A and W tiles are staged
-// through LDS, double-buffered: the global loads of step k+1 are issued into
-// registers before the matrix cores start on step k and land in the other LDS
-// buffer afterwards, one barrier per step.  The MFMA is issued as W x A so a
+// through two LDS buffers fed from two register staging sets, so the global
+// loads of step k+2 are in flight while the matrix cores work on step k; one
+// barrier per step.  The MFMA is issued as W x A so a
 // lane's accumulators hold four consecutive output columns of one row, which
 // the epilogue writes as one vector.
+// Resident blocks per CU the kernel is register-budgeted for (LDS allows
+// 160 KB / (2 * (BM + BN) * 128 B) of them).
+template <int BM, int BN>
+constexpr int gemm_occupancy() {
+  constexpr int lds = 2 * (BM + BN) * kBK * 2;  // two stages of A and W tiles, bytes
+  return 160 * 1024 / lds >= 3 ? 3 : 160 * 1024 / lds;
+}
+
 template <int BM, int BN, int EPI>
-__global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
+__global__ __launch_bounds__(kThreads, (gemm_occupancy<BM, BN>())) void gemm_bf16_kernel(
     const uint16_t *__restrict__ A, int lda, const uint16_t *__restrict__ W,
     const float *__restrict__ bias, const float *res, void *out, int ldc, int M, int N, int K,
     int tiles_m, int tiles_n) {
@@ -155,28 +167,33 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  Stage<BM> ra;
-  Stage<BN> rb;
-  load_stage<BM>(ra, Ag, lda, 0, tid);
-  load_stage<BN>(rb, Wg, K, 0, tid);
-  store_stage<BM>(ra, sA[0], tid);
-  store_stage<BN>(rb, sB[0], tid);
+  // Three tiles in flight: LDS buffer kt & 1 holds tile kt, register set
+  // (kt + 1) & 1 holds tile kt + 1 (loaded one iteration earlier), and the
+  // loads of tile kt + 2 go into the free register set before the matrix
+  // cores start on tile kt.  The loop is unrolled by two so both register sets
+  // are fixed names.
+  Stage<BM> ra0, ra1;
+  Stage<BN> rb0, rb1;
+  const int nk = K / kBK;
+  load_stage<BM>(ra0, Ag, lda, 0, tid);
+  load_stage<BN>(rb0, Wg, K, 0, tid);
+  if (nk > 1) {
+    load_stage<BM>(ra1, Ag, lda, kBK, tid);
+    load_stage<BN>(rb1, Wg, K, kBK, tid);
+  }
+  store_stage<BM>(ra0, sA[0], tid);
+  store_stage<BN>(rb0, sB[0], tid);
   __syncthreads();
 
   const int fr = lane & 31, fh = lane >> 5;  // fragment row, k-half of this lane
-  const int nk = K / kBK;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      load_stage<BM>(ra, Ag, lda, (kt + 1) * kBK, tid);
-      load_stage<BN>(rb, Wg, K, (kt + 1) * kBK, tid);
-    }
-    const uint16_t *a_s = sA[cur] + (wm * WM + fr) * kBK;
-    const uint16_t *b_s = sB[cur] + (wn * WN + fr) * kBK;
+  const uint16_t *a_base = sA[0] + (wm * WM + fr) * kBK;
+  const uint16_t *b_base = sB[0] + (wn * WN + fr) * kBK;
+  auto mma_tile = [&](int buf) {
+    const uint16_t *a_s = a_base + buf * BM * kBK;
+    const uint16_t *b_s = b_base + buf * BN * kBK;
 #pragma unroll
     for (int kk = 0; kk < kBK / 16; ++kk) {
-      const int slot = ((kk * 2 + fh) ^ (fr & 7)) << 3;
+      const int slot = swz_slot(fr, kk * 2 + fh) << 3;
       bf16x8 a[TM], b[TN];
 #pragma unroll
       for (int i = 0; i < TM; ++i)
@@ -190,9 +207,27 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
         for (int j = 0; j < TN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
     }
-    if (more) {
-      store_stage<BM>(ra, sA[cur ^ 1], tid);
-      store_stage<BN>(rb, sB[cur ^ 1], tid);
+  };
+  for (int kt = 0; kt < nk; kt += 2) {
+    if (kt + 2 < nk) {
+      load_stage<BM>(ra0, Ag, lda, (kt + 2) * kBK, tid);
+      load_stage<BN>(rb0, Wg, K, (kt + 2) * kBK, tid);
+    }
+    mma_tile(0);
+    if (kt + 1 < nk) {
+      store_stage<BM>(ra1, sA[1], tid);
+      store_stage<BN>(rb1, sB[1], tid);
+    }
+    __syncthreads();
+    if (kt + 1 >= nk) break;
+    if (kt + 3 < nk) {
+      load_stage<BM>(ra1, Ag, lda, (kt + 3) * kBK, tid);
+      load_stage<BN>(rb1, Wg, K, (kt + 3) * kBK, tid);
+    }
+    mma_tile(1);
+    if (kt + 2 < nk) {
+      store_stage<BM>(ra0, sA[0], tid);
+      store_stage<BN>(rb0, sB[0], tid);
     }
     __syncthreads();
   }

@@ -14,10 +14,26 @@ struct Ragged {
   const int32_t *off;    // [n_seqs + 1] token offsets, off[0] = 0
   const int64_t *sbase;  // [n_seqs] first element of sequence i's score blocks
   const int32_t *items;  // [2 * n_items] (sequence, first query row), kQTile rows each
+  const int32_t *sm_items = nullptr;  // [2 * n_sm_items] (sequence, first row) softmax work
   const int32_t *src = nullptr;   // [n_seqs] first id of sequence i in the id buffer (NULL: off)
   const int32_t *dest = nullptr;  // [n_seqs] reward slot of sequence i (NULL: i)
-  int32_t n_seqs = 0, n_items = 0, max_len = 0, n_tokens = 0;
+  int32_t n_seqs = 0, n_items = 0, max_len = 0, n_tokens = 0, n_sm_items = 0;
 };
+
+// Softmax work geometry (shared by the host item builder and the kernel): the
+// A * n rows of a sequence's score block ([head][query] major, stride ld) are
+// handled G lanes per row, G = the power of two covering n/4 float4 chunks
+// (at most 64), in items of 4 wavefronts x (64 / G) rows x kSoftmaxPasses.
+constexpr int kSoftmaxPasses = 2;
+__host__ __device__ inline int softmax_lanes(int n) {
+  const int nc = (n + 3) >> 2;
+  int g = 1;
+  while (g < nc && g < 64) g <<= 1;
+  return g;
+}
+__host__ __device__ inline int softmax_rows_per_item(int n) {
+  return 4 * (64 / softmax_lanes(n)) * kSoftmaxPasses;
+}
 
 // Score-block row stride of a sequence of length n (elements).
 __host__ __device__ inline int score_ld(int n) { return (n + 7) & ~7; }

@@ -245,9 +245,9 @@ es_status build(const es::ParsedBlob &pb, int64_t max_tokens, int32_t max_seqs, 
 // bases, attention work items and (optionally) id-source / reward-slot maps,
 // assembled on the host, staged in pinned memory and uploaded in ONE copy.
 struct BatchLayout {
-  size_t off = 0, sbase = 0, items = 0, src = 0, dest = 0;
+  size_t off = 0, sbase = 0, items = 0, sm_items = 0, src = 0, dest = 0;
   bool has_src = false, has_dest = false;
-  int n = 0, n_items = 0, max_len = 0, n_tokens = 0;
+  int n = 0, n_items = 0, n_sm_items = 0, max_len = 0, n_tokens = 0;
   int64_t pairs = 0;  // visible (query, key) pairs summed over heads
 };
 
@@ -290,18 +290,25 @@ es_status add_batch(es_model *m, const int32_t *h_off, int32_t n, const int32_t 
   std::stable_sort(ord.begin(), ord.end(), [&](int32_t a, int32_t b) {
     return h_off[a + 1] - h_off[a] > h_off[b + 1] - h_off[b];
   });
-  std::vector<int32_t> items;
+  std::vector<int32_t> items, sm_items;
   for (int32_t sq : ord) {
     const int len = h_off[sq + 1] - h_off[sq];
     for (int q0 = 0; q0 < len; q0 += es::kQTile) {
       items.push_back(sq);
       items.push_back(q0);
     }
+    const int rpi = es::softmax_rows_per_item(len);
+    for (int r0 = 0; r0 < m->A * len; r0 += rpi) {
+      sm_items.push_back(sq);
+      sm_items.push_back(r0);
+    }
   }
   auto &buf = m->meta_asm;
   L->off = push_bytes(buf, h_off, sizeof(int32_t) * (n + 1));
   L->sbase = push_bytes(buf, sbase.data(), sizeof(int64_t) * n);
   L->items = push_bytes(buf, items.data(), sizeof(int32_t) * items.size());
+  L->sm_items = push_bytes(buf, sm_items.data(), sizeof(int32_t) * sm_items.size());
+  L->n_sm_items = (int)(sm_items.size() / 2);
   L->has_src = src != nullptr;
   L->has_dest = dest != nullptr;
   if (src) L->src = push_bytes(buf, src, sizeof(int32_t) * n);
@@ -348,6 +355,8 @@ es::Ragged ragged_of(const es_model *m, const BatchLayout &L) {
   r.off = reinterpret_cast<const int32_t *>(m->meta_dev + L.off);
   r.sbase = reinterpret_cast<const int64_t *>(m->meta_dev + L.sbase);
   r.items = reinterpret_cast<const int32_t *>(m->meta_dev + L.items);
+  r.sm_items = reinterpret_cast<const int32_t *>(m->meta_dev + L.sm_items);
+  r.n_sm_items = L.n_sm_items;
   r.src = L.has_src ? reinterpret_cast<const int32_t *>(m->meta_dev + L.src) : nullptr;
   r.dest = L.has_dest ? reinterpret_cast<const int32_t *>(m->meta_dev + L.dest) : nullptr;
   r.n_seqs = L.n;

@@ -40,7 +40,7 @@ extern "C" es_status es_ragged_create(const int32_t *h_lengths, int32_t n_seqs, 
   *out = nullptr;
   std::vector<int32_t> off(n_seqs + 1, 0);
   std::vector<int64_t> sbase(n_seqs);
-  std::vector<int32_t> items;
+  std::vector<int32_t> items, sm_items;
   int64_t acc = 0;
   int max_len = 0;
   for (int32_t i = 0; i < n_seqs; ++i) {
@@ -55,10 +55,15 @@ extern "C" es_status es_ragged_create(const int32_t *h_lengths, int32_t n_seqs, 
       items.push_back(i);
       items.push_back(q0);
     }
+    for (int r0 = 0; r0 < n_heads * n; r0 += es::softmax_rows_per_item(n)) {
+      sm_items.push_back(i);
+      sm_items.push_back(r0);
+    }
   }
   const size_t b_off = es::round_up((int64_t)off.size() * 4, 16);
   const size_t b_sb = es::round_up((int64_t)sbase.size() * 8, 16);
-  const size_t bytes = b_off + b_sb + items.size() * 4;
+  const size_t b_it = es::round_up((int64_t)items.size() * 4, 16);
+  const size_t bytes = b_off + b_sb + b_it + sm_items.size() * 4;
   es_ragged *g = new es_ragged();
   hipError_t e = hipMalloc(&g->dev, bytes);
   if (e == hipSuccess) e = hipMemcpy(g->dev, off.data(), off.size() * 4, hipMemcpyHostToDevice);
@@ -66,6 +71,9 @@ extern "C" es_status es_ragged_create(const int32_t *h_lengths, int32_t n_seqs, 
     e = hipMemcpy((char *)g->dev + b_off, sbase.data(), sbase.size() * 8, hipMemcpyHostToDevice);
   if (e == hipSuccess)
     e = hipMemcpy((char *)g->dev + b_off + b_sb, items.data(), items.size() * 4, hipMemcpyHostToDevice);
+  if (e == hipSuccess)
+    e = hipMemcpy((char *)g->dev + b_off + b_sb + b_it, sm_items.data(), sm_items.size() * 4,
+                  hipMemcpyHostToDevice);
   if (e != hipSuccess) {
     if (g->dev) (void)hipFree(g->dev);
     delete g;
@@ -76,6 +84,8 @@ extern "C" es_status es_ragged_create(const int32_t *h_lengths, int32_t n_seqs, 
   g->r.items = (const int32_t *)((char *)g->dev + b_off + b_sb);
   g->r.n_seqs = n_seqs;
   g->r.n_items = (int32_t)(items.size() / 2);
+  g->r.sm_items = (const int32_t *)((char *)g->dev + b_off + b_sb + b_it);
+  g->r.n_sm_items = (int32_t)(sm_items.size() / 2);
   g->r.max_len = max_len;
   g->r.n_tokens = off[n_seqs];
   g->n_heads = n_heads;
@@ -106,7 +116,7 @@ extern "C" es_status es_op_gemm_bf16(const uint16_t *d_a, int32_t lda, const uin
                                      void *stream) {
   if (!d_a || !d_w || !d_bias || !d_out || (epilogue == es::kEpiResidual && !d_res))
     return fail(ES_ERR_ARG, "es_op_gemm_bf16: NULL pointer");
-  if (M < 0 || N < 0 || K <= 0 || K % 64 || lda < K || lda % 8 || ldc < N || epilogue < 0 ||
+  if (M < 0 || N < 0 || K <= 0 || K % 64 || lda < K || lda % 8 || ldc < N || ldc % 4 || epilogue < 0 ||
       epilogue > 3)
     return fail(ES_ERR_ARG, "es_op_gemm_bf16: M=%d N=%d K=%d lda=%d ldc=%d epilogue=%d", M, N, K,
                 lda, ldc, epilogue);

@@ -30,10 +30,20 @@ __device__ __forceinline__ void store4(uint16_t *p, float4 v) {
 
 // LayerNorm of one row held as NC float4 chunks per lane (chunk c4 = lane + 64 j).
 // Two passes over registers: mean, then the biased variance of (x - mean).
+// Gains and shifts are loaded before the reductions so their latency overlaps.
 template <int NC>
 __device__ __forceinline__ void ln_row(float4 (&v)[NC], int lane, int c4n, int cols,
                                        const float *__restrict__ g, const float *__restrict__ b,
                                        float eps) {
+  float4 gg[NC], bb[NC];
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    const int c4 = lane + kWave * j;
+    if (c4 < c4n) {
+      gg[j] = load4(g + 4 * c4);
+      bb[j] = load4(b + 4 * c4);
+    }
+  }
   float s = 0.f;
 #pragma unroll
   for (int j = 0; j < NC; ++j)
@@ -43,8 +53,8 @@ __device__ __forceinline__ void ln_row(float4 (&v)[NC], int lane, int c4n, int c
 #pragma unroll
   for (int j = 0; j < NC; ++j) {
     if (lane + kWave * j < c4n) {
-      const float a = v[j].x - mean, bb = v[j].y - mean, c = v[j].z - mean, d = v[j].w - mean;
-      s2 += (a * a + bb * bb) + (c * c + d * d);
+      const float a = v[j].x - mean, b2 = v[j].y - mean, c = v[j].z - mean, d = v[j].w - mean;
+      s2 += (a * a + b2 * b2) + (c * c + d * d);
     }
   }
   const float var = wave_sum(s2) / (float)cols;
@@ -53,11 +63,10 @@ __device__ __forceinline__ void ln_row(float4 (&v)[NC], int lane, int c4n, int c
   for (int j = 0; j < NC; ++j) {
     const int c4 = lane + kWave * j;
     if (c4 < c4n) {
-      const float4 gg = load4(g + 4 * c4), bb = load4(b + 4 * c4);
-      v[j].x = (v[j].x - mean) * rstd * gg.x + bb.x;
-      v[j].y = (v[j].y - mean) * rstd * gg.y + bb.y;
-      v[j].z = (v[j].z - mean) * rstd * gg.z + bb.z;
-      v[j].w = (v[j].w - mean) * rstd * gg.w + bb.w;
+      v[j].x = (v[j].x - mean) * rstd * gg[j].x + bb[j].x;
+      v[j].y = (v[j].y - mean) * rstd * gg[j].y + bb[j].y;
+      v[j].z = (v[j].z - mean) * rstd * gg[j].z + bb[j].z;
+      v[j].w = (v[j].w - mean) * rstd * gg[j].w + bb[j].w;
     }
   }
 }
@@ -137,55 +146,77 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t *__restrict__ 
   }
 }
 
-// Softmax over the rows of one (sequence, head) score block, kQTile rows per
-// block of 256 threads.  Rows shorter than 64 are packed G = 8/16/32 lanes
-// per row so short sequences still use whole wavefronts; longer rows hold up
-// to NJ elements per lane in registers (single read, single write).
+// Softmax over the ragged score rows.  One item covers a run of rows of one
+// sequence's [A * n, ld] score block (all heads; rows of equal length n, or
+// q + 1 when causal).  Each row is owned by G lanes (G from its length) that
+// read it as float4 chunks straight into registers; both passes of rows are
+// loaded before any reduction so two rows per lane group are in flight.
+// Max and sum reduce by butterfly shuffles within the G-lane group.
 template <int NJ, typename PT>
 __global__ __launch_bounds__(256) void softmax_kernel(const float *__restrict__ S, PT *__restrict__ P,
                                                       const int32_t *__restrict__ off,
                                                       const int64_t *__restrict__ sbase,
                                                       const int32_t *__restrict__ items, int n_heads,
                                                       int causal) {
-  const int item = blockIdx.x, h = blockIdx.y;
-  const int seq = items[2 * item], q0 = items[2 * item + 1];
+  const int seq = items[2 * blockIdx.x], row0 = items[2 * blockIdx.x + 1];
   const int n = off[seq + 1] - off[seq];
   const int ld = score_ld(n);
-  const int64_t base = sbase[seq] + (int64_t)h * n * ld;
-  int G = 64;
-  if (n <= 8) G = 8;
-  else if (n <= 16) G = 16;
-  else if (n <= 32) G = 32;
-  const int rpw = kWave / G;  // rows per wavefront pass
+  const int64_t base = sbase[seq];
+  const int G = softmax_lanes(n), rpw = kWave / G;
+  const int row_end = min(row0 + softmax_rows_per_item(n), n_heads * n);
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
   const int sub = lane / G, c0 = lane % G;
-  const int q_end = min(q0 + kQTile, n);
-  for (int qa = q0 + wave * rpw; qa < q_end; qa += 4 * rpw) {
-    const int q = qa + sub;
-    const int m = q < q_end ? (causal ? q + 1 : n) : 0;  // valid scores in this row
-    const float *sr = S + base + (int64_t)q * ld;
-    float v[NJ];
+  float4 v[kSoftmaxPasses][NJ];
+  int m[kSoftmaxPasses];
+  int64_t ro[kSoftmaxPasses];
+#pragma unroll
+  for (int p = 0; p < kSoftmaxPasses; ++p) {
+    const int r = row0 + (p * 4 + wave) * rpw + sub;
+    m[p] = r < row_end ? (causal ? r % n + 1 : n) : 0;  // valid scores of row r
+    ro[p] = base + (int64_t)r * ld;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int c = (c0 + G * j) * 4;
+      v[p][j] = c < m[p] ? *reinterpret_cast<const float4 *>(S + ro[p] + c)
+                         : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < kSoftmaxPasses; ++p) {
     float mx = -INFINITY;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      const int c = c0 + G * j;
-      v[j] = c < m ? sr[c] : -INFINITY;
-      mx = fmaxf(mx, v[j]);
+      const int c = (c0 + G * j) * 4;
+      if (c < m[p]) mx = fmaxf(mx, v[p][j].x);
+      if (c + 1 < m[p]) mx = fmaxf(mx, v[p][j].y);
+      if (c + 2 < m[p]) mx = fmaxf(mx, v[p][j].z);
+      if (c + 3 < m[p]) mx = fmaxf(mx, v[p][j].w);
     }
     mx = group_max(mx, G);
     float sum = 0.f;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      const int c = c0 + G * j;
-      v[j] = c < m ? expf(v[j] - mx) : 0.f;
-      sum += v[j];
+      const int c = (c0 + G * j) * 4;
+      v[p][j].x = c < m[p] ? expf(v[p][j].x - mx) : 0.f;
+      v[p][j].y = c + 1 < m[p] ? expf(v[p][j].y - mx) : 0.f;
+      v[p][j].z = c + 2 < m[p] ? expf(v[p][j].z - mx) : 0.f;
+      v[p][j].w = c + 3 < m[p] ? expf(v[p][j].w - mx) : 0.f;
+      sum += (v[p][j].x + v[p][j].y) + (v[p][j].z + v[p][j].w);
     }
     sum = group_sum(sum, G);
-    PT *pr = P + base + (int64_t)q * ld;
+    PT *pr = P + ro[p];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      const int c = c0 + G * j;
-      if (c < m) pr[c] = from_f<PT>(v[j] / sum);
+      const int c = (c0 + G * j) * 4;
+      if (c >= m[p]) continue;
+      const float4 o = make_float4(v[p][j].x / sum, v[p][j].y / sum, v[p][j].z / sum, v[p][j].w / sum);
+      if (c + 3 < m[p]) {
+        store4(pr + c, o);
+      } else {
+        pr[c] = from_f<PT>(o.x);
+        if (c + 1 < m[p]) pr[c + 1] = from_f<PT>(o.y);
+        if (c + 2 < m[p]) pr[c + 2] = from_f<PT>(o.z);
+      }
     }
   }
 }
@@ -281,16 +312,17 @@ hipError_t launch_embed(bool w_bf16, bool act_bf16, bool ln, const int32_t *ids,
 
 hipError_t launch_softmax(bool p_bf16, const float *S, void *P, const Ragged &r, int n_heads,
                           bool causal, hipStream_t st) {
-  if (r.n_items <= 0) return hipSuccess;
-  const dim3 grid(r.n_items, n_heads), block(256);
-  const int nj = (r.max_len + kWave - 1) / kWave;
+  if (r.n_sm_items <= 0) return hipSuccess;
+  const dim3 grid(r.n_sm_items), block(256);
+  const int nc = (r.max_len + 3) / 4;
+  const int nj = nc <= 64 ? 1 : (nc + 63) / 64;
   auto go = [&](auto njc) {
     constexpr int NJ = decltype(njc)::value;
     if (p_bf16)
       softmax_kernel<NJ, uint16_t><<<grid, block, 0, st>>>(S, (uint16_t *)P, r.off, r.sbase,
-                                                            r.items, n_heads, causal ? 1 : 0);
+                                                            r.sm_items, n_heads, causal ? 1 : 0);
     else
-      softmax_kernel<NJ, float><<<grid, block, 0, st>>>(S, (float *)P, r.off, r.sbase, r.items,
+      softmax_kernel<NJ, float><<<grid, block, 0, st>>>(S, (float *)P, r.off, r.sbase, r.sm_items,
                                                          n_heads, causal ? 1 : 0);
     return hipGetLastError();
   };
@@ -299,7 +331,6 @@ hipError_t launch_softmax(bool p_bf16, const float *S, void *P, const Ragged &r,
   if (nj <= 4) return go(std::integral_constant<int, 4>{});
   if (nj <= 8) return go(std::integral_constant<int, 8>{});
   if (nj <= 16) return go(std::integral_constant<int, 16>{});
-  if (nj <= 64) return go(std::integral_constant<int, 64>{});
   return hipErrorInvalidValue;
 }
 

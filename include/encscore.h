@@ -281,7 +281,8 @@ es_status es_op_softmax(const es_ragged *r, const float *d_scores, void *d_p, in
  *            2: out fp32 = acc + bias + d_res[m, n]     (d_res fp32, ld ldc)
  *            3: out fp32 = acc + bias
  *   d_out [M, ldc] (bf16 for 0/1, fp32 for 2/3); only n < N, m < M written.
- * K must be a positive multiple of 64, lda >= K and a multiple of 8, ldc >= N.
+ * K must be a positive multiple of 64, lda >= K and a multiple of 8, ldc >= N and a
+ * multiple of 4; d_bias, d_res and d_out 16-byte aligned.
  * Rows beyond M (A) and N (W) up to the rounded sizes are read, never used.
  * Errors: ES_ERR_ARG.
  */
