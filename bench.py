@@ -109,6 +109,10 @@ def main():
     ap.add_argument("--batch-overhead", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--single-step", action="store_true",
+                    help="one warm-up call and one step, then exit (for counter collection)")
+    ap.add_argument("--in-flight", type=int, default=3,
+                    help="planned batches overlapped on internal streams (es_set_concurrency)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the scoring path is "
@@ -139,35 +143,50 @@ def main():
     roff = np.concatenate([[0], np.cumsum(rlen)]).astype(np.int32)
     if int(rlen.sum()) <= cfg.max_tokens:
         sc.reward_offset = sc.calibrate_offset(d_ref, roff)   # reference set averages zero
+    sc.set_concurrency(args.in_flight)
     d_ids = torch.from_numpy(ids).cuda()
     out = torch.empty(n, dtype=torch.float32, device="cuda")
-    stream = torch.cuda.current_stream()
 
-    # warm-up steps with every kernel class timed, to find the dominant one
-    sc.profile_enable(None)
+    if args.single_step:
+        for _ in range(2):
+            sc.score_requests(d_ids, lengths, c, out)
+        torch.cuda.synchronize()
+        print(json.dumps({"single_step": cfg.name, "finite": bool(torch.isfinite(out).all().item())}))
+        return
+    # warm-up (also sizes the metadata buffers), then the timed region: K steps
+    # of the production configuration with no profiling events
     for _ in range(max(1, args.warmup)):
         _, stats = sc.score_requests(d_ids, lengths, c, out)
-    stream.synchronize()
-    per_class = sc.profile_collect()
-    dominant = max(per_class, key=lambda k: per_class[k]["total_ms"])
-    log("warm-up per-class ms/step:", {k: round(v["total_ms"] / max(1, args.warmup), 3)
-                                       for k, v in per_class.items()})
-
-    # timed region: only the dominant class carries event pairs
-    sc.profile_enable([dominant])
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         sc.score_requests(d_ids, lengths, c, out)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    dom = sc.profile_collect()[dominant]
-    sc.profile_enable([])
     ms = (t1 - t0) * 1e3 / args.steps
     value = n / (ms / 1e3)
     assert torch.isfinite(out).all().item(), "non-finite rewards"
 
-    launches = dom["launches"] / args.steps
+    # roofline pass: one batch in flight so each kernel runs alone, every
+    # kernel class bracketed by HIP events on the stream it is launched on
+    prof_steps = max(2, min(args.steps, 5))
+    sc.set_concurrency(1)
+    sc.score_requests(d_ids, lengths, c, out)
+    sc.profile_enable(None)
+    torch.cuda.synchronize()
+    tp0 = time.perf_counter()
+    for _ in range(prof_steps):
+        sc.score_requests(d_ids, lengths, c, out)
+    torch.cuda.synchronize()
+    ms_isolated = (time.perf_counter() - tp0) * 1e3 / prof_steps
+    per_class = sc.profile_collect()
+    sc.profile_enable([])
+    dominant = max(per_class, key=lambda k: per_class[k]["total_ms"])
+    dom = per_class[dominant]
+    log("isolated per-class ms/step:", {k: round(v["total_ms"] / prof_steps, 3)
+                                        for k, v in per_class.items()})
+
+    launches = dom["launches"] / prof_steps
     avg_ms = dom["total_ms"] / max(1, dom["launches"])
     if dominant in GEMM_CLASSES:
         key = "mfma_bf16" if cfg.bf16 else "alu_fp32"
@@ -193,9 +212,9 @@ def main():
         else:   # attention contractions: report flops against the MFMA peak
             kpeak, kunit = PEAKS["mfma_bf16" if cfg.bf16 else "alu_fp32"]
             ach = v["flops"] / sec / 1e12
-        kernels[k] = {"ms_per_step": round(v["total_ms"] / max(1, args.warmup), 3),
+        kernels[k] = {"ms_per_step": round(v["total_ms"] / prof_steps, 3),
                       "achieved": round(ach, 2), "unit": kunit, "frac": round(ach / kpeak, 4),
-                      "launches_per_step": v["launches"] // max(1, args.warmup)}
+                      "launches_per_step": v["launches"] // prof_steps}
 
     line = {
         "metric": "sequences scored/sec on var-len batches",
@@ -213,12 +232,14 @@ def main():
         "config": {"workload": cfg.name, "description": WORKLOAD_DESC[cfg.name],
                    "requests": n, "tokens": n_tokens, "batches": stats["n_batches"],
                    "padded_tokens": stats["padded_tokens"], "max_tokens": cfg.max_tokens,
-                   "batch_overhead": c},
+                   "batch_overhead": c, "batches_in_flight": args.in_flight},
         "tokens_per_s": round(n_tokens / (ms / 1e3), 1),
         "roofline": {"bound": bound, "kernel": dominant, "achieved": round(achieved, 2),
                      "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
                      "traffic": traffic, "avg_launch_ms": round(avg_ms, 5),
-                     "launches_per_step": launches},
+                     "launches_per_step": launches,
+                     "measured": f"HIP events around every launch over {prof_steps} steps with one "
+                                 f"batch in flight ({ms_isolated:.2f} ms/step)"},
         "kernels": kernels,
         "device": torch.cuda.get_device_name(0),
     }

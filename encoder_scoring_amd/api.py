@@ -153,6 +153,10 @@ class Scorer:
                                                      ctypes.byref(v)))
         return v.value
 
+    def set_concurrency(self, batches_in_flight):
+        """Planned batches es_score_requests overlaps on internal streams (1..4)."""
+        check(self.lib, self.lib.es_set_concurrency(self.handle, int(batches_in_flight)))
+
     def profile_enable(self, classes=None):
         """Record HIP events around the given kernel classes (names; None = all)."""
         names = _lib.KERNEL_CLASSES

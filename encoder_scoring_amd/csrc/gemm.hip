@@ -88,7 +88,7 @@ __device__ __forceinline__ void epi_store4(void *out, const float *res, int ldc,
       u.y = (uint32_t)f2bf(v.z) | ((uint32_t)f2bf(v.w) << 16);
       *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(out) + o) = u;
     } else {
-      if (EPI == kEpiResidual) {
+      if (EPI == kEpiResidual || EPI == kEpiResidualFfn) {
         const float4 r = *reinterpret_cast<const float4 *>(res + o);
         v.x += r.x; v.y += r.y; v.z += r.z; v.w += r.w;
       }
@@ -103,7 +103,7 @@ __device__ __forceinline__ void epi_store4(void *out, const float *res, int ldc,
     float x = vv[e] + bias[n + e];
     if (EPI == kEpiBias) static_cast<uint16_t *>(out)[o + e] = f2bf(x);
     else if (EPI == kEpiGelu) static_cast<uint16_t *>(out)[o + e] = f2bf(gelu_erf(x));
-    else if (EPI == kEpiResidual) static_cast<float *>(out)[o + e] = x + res[o + e];
+    else if (EPI == kEpiResidual || EPI == kEpiResidualFfn) static_cast<float *>(out)[o + e] = x + res[o + e];
     else static_cast<float *>(out)[o + e] = x;
   }
 }
@@ -299,7 +299,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float *__restrict__
       if (n >= N) continue;
       const float v = acc[i][j] + bias[n];
       if (EPI == kEpiBias || EPI == kEpiF32) out[m * ldc + n] = v;
-      else if (EPI == kEpiGelu) out[m * ldc + n] = gelu_erf(v);
+        else if (EPI == kEpiGelu) out[m * ldc + n] = gelu_erf(v);
       else out[m * ldc + n] = v + res[m * ldc + n];
     }
   }
@@ -323,6 +323,9 @@ hipError_t go_bf16(const uint16_t *A, int lda, const uint16_t *W, const float *b
       break;
     case kEpiF32:
       gemm_bf16_kernel<BM, BN, kEpiF32><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K, tm, tn);
+      break;
+    case kEpiResidualFfn:
+      gemm_bf16_kernel<BM, BN, kEpiResidualFfn><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K, tm, tn);
       break;
     default:
       return hipErrorInvalidValue;

@@ -58,7 +58,10 @@ hipError_t launch_head(bool pre_ln, const float *x, int H, const Ragged &r, cons
                        float *rewards, hipStream_t st);
 
 // ---- GEMMs (gemm.hip): out[m, n] = epi(sum_k A[m, k] W[n, k] + bias[n])
-enum Epilogue { kEpiBias = 0, kEpiGelu = 1, kEpiResidual = 2, kEpiF32 = 3 };
+// kEpiResidualFfn behaves exactly like kEpiResidual; it is a separate kernel
+// instance only so that profilers can tell the FFN2 GEMM from the
+// attention-output GEMM.
+enum Epilogue { kEpiBias = 0, kEpiGelu = 1, kEpiResidual = 2, kEpiF32 = 3, kEpiResidualFfn = 4 };
 hipError_t launch_gemm_bf16(const uint16_t *A, int lda, const uint16_t *W, const float *bias,
                             const float *res, void *out, int ldc, int M, int N, int K, int epi,
                             hipStream_t st);

@@ -66,9 +66,18 @@ struct es_model {
   void *tok_emb = nullptr, *pos_emb = nullptr;
   float *norm_g = nullptr, *norm_b = nullptr, *head_w = nullptr, *head_b = nullptr;
   std::vector<DevLayer> layers;
-  // workspace
-  float *x = nullptr, *y = nullptr, *S = nullptr, *rew = nullptr;
-  void *xb = nullptr, *qkv = nullptr, *ctx = nullptr, *hmid = nullptr, *Pb = nullptr;
+  // workspaces: one per batch in flight (es_set_concurrency)
+  struct Workspace {
+    float *x = nullptr, *y = nullptr, *S = nullptr;
+    void *xb = nullptr, *qkv = nullptr, *ctx = nullptr, *hmid = nullptr, *Pb = nullptr;
+    hipStream_t stream = nullptr;  // internal stream used when several batches are in flight
+    hipEvent_t done = nullptr;
+  };
+  std::vector<Workspace> ws;  // allocated workspaces; the first `lanes` are used
+  int lanes = 1;
+  hipEvent_t fork_ev = nullptr;
+  float *rew = nullptr;  // raw rewards of a reference set (es_calibrate_offset)
+  size_t rew_cap = 0;
   int *flag = nullptr;
   // per-call metadata: host assembly -> pinned staging -> one upload
   std::vector<uint8_t> meta_asm;
@@ -112,7 +121,13 @@ void release(es_model *m) {
   m->allocs.clear();
   if (m->meta_host) (void)hipHostFree(m->meta_host);
   if (m->meta_dev) (void)hipFree(m->meta_dev);
+  if (m->rew) (void)hipFree(m->rew);
   if (m->meta_ev) (void)hipEventDestroy(m->meta_ev);
+  if (m->fork_ev) (void)hipEventDestroy(m->fork_ev);
+  for (auto &w : m->ws) {
+    if (w.stream) (void)hipStreamDestroy(w.stream);
+    if (w.done) (void)hipEventDestroy(w.done);
+  }
   for (hipEvent_t e : m->ev_pool) (void)hipEventDestroy(e);
   delete m;
 }
@@ -167,6 +182,23 @@ int64_t qkv_row(int64_t r, const es_model *m) {
 }
 int64_t ctx_col(int64_t c, const es_model *m) { return (c / m->d) * m->dp + c % m->d; }
 
+// Activations and score buffers for one batch in flight (zero-filled once:
+// padding columns stay zero forever).
+es_status alloc_workspace(es_model *m, es_model::Workspace &w) {
+  const int act = m->bf16 ? 2 : 4;
+  const int64_t T = m->Tcap;
+  es_status s;
+  if ((s = dalloc(m, (void **)&w.x, T * m->H * 4)) != ES_OK) return s;
+  if ((s = dalloc(m, (void **)&w.y, T * m->H * 4)) != ES_OK) return s;
+  if ((s = dalloc(m, &w.xb, T * m->Hp * act)) != ES_OK) return s;
+  if ((s = dalloc(m, &w.qkv, T * m->Nqkv * act)) != ES_OK) return s;
+  if ((s = dalloc(m, &w.ctx, T * m->Kc * act)) != ES_OK) return s;
+  if ((s = dalloc(m, &w.hmid, T * m->Fp * act)) != ES_OK) return s;
+  if ((s = dalloc(m, (void **)&w.S, m->score_cap * 4)) != ES_OK) return s;
+  if ((s = dalloc(m, &w.Pb, m->score_cap * act)) != ES_OK) return s;
+  return ES_OK;
+}
+
 es_status build(const es::ParsedBlob &pb, int64_t max_tokens, int32_t max_seqs, es_model *m) {
   const es::BlobHeader &h = pb.h;
   m->L = (int)h.n_layers;
@@ -194,7 +226,6 @@ es_status build(const es::ParsedBlob &pb, int64_t max_tokens, int32_t max_seqs, 
   m->max_items = (int)(max_tokens / es::kQTile + max_seqs + 1);
   HIP_TRY(hipGetDevice(&m->device));
 
-  const int act = m->bf16 ? 2 : 4;
   es_status s;
   auto id = [](int64_t r) { return r; };
   // embeddings keep their natural [rows, H] layout
@@ -224,17 +255,8 @@ es_status build(const es::ParsedBlob &pb, int64_t max_tokens, int32_t max_seqs, 
     if ((s = upload_vec(m, &D.ln2_g, L.ln2_g, m->H)) != ES_OK) return s;
     if ((s = upload_vec(m, &D.ln2_b, L.ln2_b, m->H)) != ES_OK) return s;
   }
-  // workspace (zero-filled once: padding columns stay zero forever)
-  const int64_t T = m->Tcap;
-  if ((s = dalloc(m, (void **)&m->x, T * m->H * 4)) != ES_OK) return s;
-  if ((s = dalloc(m, (void **)&m->y, T * m->H * 4)) != ES_OK) return s;
-  if ((s = dalloc(m, &m->xb, T * m->Hp * act)) != ES_OK) return s;
-  if ((s = dalloc(m, &m->qkv, T * m->Nqkv * act)) != ES_OK) return s;
-  if ((s = dalloc(m, &m->ctx, T * m->Kc * act)) != ES_OK) return s;
-  if ((s = dalloc(m, &m->hmid, T * m->Fp * act)) != ES_OK) return s;
-  if ((s = dalloc(m, (void **)&m->S, m->score_cap * 4)) != ES_OK) return s;
-  if ((s = dalloc(m, &m->Pb, m->score_cap * act)) != ES_OK) return s;
-  if ((s = dalloc(m, (void **)&m->rew, (size_t)m->max_seqs * 4)) != ES_OK) return s;
+  m->ws.resize(1);
+  if ((s = alloc_workspace(m, m->ws[0])) != ES_OK) return s;
   if ((s = dalloc(m, (void **)&m->flag, 4)) != ES_OK) return s;
   HIP_TRY(hipEventCreateWithFlags(&m->meta_ev, hipEventDisableTiming));
   HIP_TRY(hipDeviceSynchronize());
@@ -412,7 +434,7 @@ es_status gemm(es_model *m, int cls, const void *A, int lda, const void *W, cons
   Prof p(m, st, cls);
   if (m->bf16)
     HIP_TRY(es::launch_gemm_bf16((const uint16_t *)A, lda, (const uint16_t *)W, bias, res, out, ldc,
-                                 M, N, K, epi, st));
+                                 M, N, K, cls == ES_KC_FFN2 ? es::kEpiResidualFfn : epi, st));
   else
     HIP_TRY(es::launch_gemm_f32((const float *)A, lda, (const float *)W, bias, res, (float *)out, ldc,
                                 M, N, K, epi, st));
@@ -423,72 +445,74 @@ es_status gemm(es_model *m, int cls, const void *A, int lda, const void *W, cons
   return ES_OK;
 }
 
-es_status attention(es_model *m, const es::Ragged &r, int64_t pairs, hipStream_t st) {
+using Workspace = es_model::Workspace;
+
+es_status attention(es_model *m, Workspace &w, const es::Ragged &r, int64_t pairs, hipStream_t st) {
   const float scale = 1.0f / std::sqrt((float)m->d);
   const double a = m->bf16 ? 2.0 : 4.0, T = r.n_tokens, Hd = (double)m->H;
   {
     Prof p(m, st, ES_KC_SCORES);
-    HIP_TRY(es::launch_scores(m->bf16, m->qkv, m->Nqkv, m->A, m->dp, scale, m->causal, r, m->S, st));
+    HIP_TRY(es::launch_scores(m->bf16, w.qkv, m->Nqkv, m->A, m->dp, scale, m->causal, r, w.S, st));
     p.done(2.0 * m->d * pairs, 2.0 * T * Hd * a + 4.0 * pairs);
   }
   {
     Prof p(m, st, ES_KC_SOFTMAX);
-    HIP_TRY(es::launch_softmax(m->bf16, m->S, m->Pb, r, m->A, m->causal, st));
+    HIP_TRY(es::launch_softmax(m->bf16, w.S, w.Pb, r, m->A, m->causal, st));
     p.done(4.0 * pairs, (4.0 + a) * pairs);
   }
   {
     Prof p(m, st, ES_KC_PV);
-    HIP_TRY(es::launch_pv(m->bf16, m->Pb, m->qkv, m->Nqkv, m->A, m->dp, m->causal, r, m->ctx, m->Kc, st));
+    HIP_TRY(es::launch_pv(m->bf16, w.Pb, w.qkv, m->Nqkv, m->A, m->dp, m->causal, r, w.ctx, m->Kc, st));
     p.done(2.0 * m->d * pairs, a * pairs + 2.0 * T * Hd * a);
   }
   return ES_OK;
 }
 
-es_status layernorm(es_model *m, const float *x, const float *g, const float *b, int T, float *y,
-                    hipStream_t st) {
+es_status layernorm(es_model *m, Workspace &w, const float *x, const float *g, const float *b, int T,
+                    float *y, hipStream_t st) {
   Prof p(m, st, ES_KC_LAYERNORM);
-  HIP_TRY(es::launch_layernorm(m->bf16, x, g, b, T, m->H, m->eps, y, m->xb, m->Hp, st));
+  HIP_TRY(es::launch_layernorm(m->bf16, x, g, b, T, m->H, m->eps, y, w.xb, m->Hp, st));
   const double a = m->bf16 ? 2.0 : 4.0;
   p.done(8.0 * T * m->H, (double)T * m->H * (4.0 + a + (y ? 4.0 : 0.0)));
   return ES_OK;
 }
 
-es_status forward(es_model *m, const int32_t *d_ids, const es::Ragged &r, int64_t pairs,
-                  int n_layers, hipStream_t st) {
+es_status forward(es_model *m, Workspace &w, const int32_t *d_ids, const es::Ragged &r,
+                  int64_t pairs, int n_layers, hipStream_t st) {
   const int T = r.n_tokens, H = m->H, F = m->F, Hd = m->A * m->d;
   const double a = m->bf16 ? 2.0 : 4.0;
   es_status s;
   {
     Prof p(m, st, ES_KC_EMBED);
     HIP_TRY(es::launch_embed(m->bf16, m->bf16, !m->pre_ln, d_ids, r, m->tok_emb, m->pos_emb, m->V, H,
-                             m->norm_g, m->norm_b, m->eps, m->x, m->xb, m->Hp, m->flag, st));
+                             m->norm_g, m->norm_b, m->eps, w.x, w.xb, m->Hp, m->flag, st));
     p.done(10.0 * T * H, (double)T * H * (2.0 * a + 4.0 + (m->pre_ln ? 0.0 : a)) + 4.0 * T);
   }
   for (int l = 0; l < n_layers; ++l) {
     const DevLayer &D = m->layers[l];
     if (!m->pre_ln) {
-      if ((s = gemm(m, ES_KC_QKV, m->xb, m->Hp, D.w_qkv, D.b_qkv, nullptr, m->qkv, m->Nqkv, T,
+      if ((s = gemm(m, ES_KC_QKV, w.xb, m->Hp, D.w_qkv, D.b_qkv, nullptr, w.qkv, m->Nqkv, T,
                     m->Nqkv, m->Hp, H, es::kEpiBias, st)) != ES_OK) return s;
-      if ((s = attention(m, r, pairs, st)) != ES_OK) return s;
-      if ((s = gemm(m, ES_KC_OPROJ, m->ctx, m->Kc, D.w_o, D.b_o, m->x, m->y, H, T, H, m->Kc, Hd,
+      if ((s = attention(m, w, r, pairs, st)) != ES_OK) return s;
+      if ((s = gemm(m, ES_KC_OPROJ, w.ctx, m->Kc, D.w_o, D.b_o, w.x, w.y, H, T, H, m->Kc, Hd,
                     es::kEpiResidual, st)) != ES_OK) return s;
-      if ((s = layernorm(m, m->y, D.ln1_g, D.ln1_b, T, m->x, st)) != ES_OK) return s;
-      if ((s = gemm(m, ES_KC_FFN1, m->xb, m->Hp, D.w_1, D.b_1, nullptr, m->hmid, m->Fp, T, F, m->Hp,
+      if ((s = layernorm(m, w, w.y, D.ln1_g, D.ln1_b, T, w.x, st)) != ES_OK) return s;
+      if ((s = gemm(m, ES_KC_FFN1, w.xb, m->Hp, D.w_1, D.b_1, nullptr, w.hmid, m->Fp, T, F, m->Hp,
                     H, es::kEpiGelu, st)) != ES_OK) return s;
-      if ((s = gemm(m, ES_KC_FFN2, m->hmid, m->Fp, D.w_2, D.b_2, m->x, m->y, H, T, H, m->Fp, F,
+      if ((s = gemm(m, ES_KC_FFN2, w.hmid, m->Fp, D.w_2, D.b_2, w.x, w.y, H, T, H, m->Fp, F,
                     es::kEpiResidual, st)) != ES_OK) return s;
-      if ((s = layernorm(m, m->y, D.ln2_g, D.ln2_b, T, m->x, st)) != ES_OK) return s;
+      if ((s = layernorm(m, w, w.y, D.ln2_g, D.ln2_b, T, w.x, st)) != ES_OK) return s;
     } else {
-      if ((s = layernorm(m, m->x, D.ln1_g, D.ln1_b, T, nullptr, st)) != ES_OK) return s;
-      if ((s = gemm(m, ES_KC_QKV, m->xb, m->Hp, D.w_qkv, D.b_qkv, nullptr, m->qkv, m->Nqkv, T,
+      if ((s = layernorm(m, w, w.x, D.ln1_g, D.ln1_b, T, nullptr, st)) != ES_OK) return s;
+      if ((s = gemm(m, ES_KC_QKV, w.xb, m->Hp, D.w_qkv, D.b_qkv, nullptr, w.qkv, m->Nqkv, T,
                     m->Nqkv, m->Hp, H, es::kEpiBias, st)) != ES_OK) return s;
-      if ((s = attention(m, r, pairs, st)) != ES_OK) return s;
-      if ((s = gemm(m, ES_KC_OPROJ, m->ctx, m->Kc, D.w_o, D.b_o, m->x, m->x, H, T, H, m->Kc, Hd,
+      if ((s = attention(m, w, r, pairs, st)) != ES_OK) return s;
+      if ((s = gemm(m, ES_KC_OPROJ, w.ctx, m->Kc, D.w_o, D.b_o, w.x, w.x, H, T, H, m->Kc, Hd,
                     es::kEpiResidual, st)) != ES_OK) return s;
-      if ((s = layernorm(m, m->x, D.ln2_g, D.ln2_b, T, nullptr, st)) != ES_OK) return s;
-      if ((s = gemm(m, ES_KC_FFN1, m->xb, m->Hp, D.w_1, D.b_1, nullptr, m->hmid, m->Fp, T, F, m->Hp,
+      if ((s = layernorm(m, w, w.x, D.ln2_g, D.ln2_b, T, nullptr, st)) != ES_OK) return s;
+      if ((s = gemm(m, ES_KC_FFN1, w.xb, m->Hp, D.w_1, D.b_1, nullptr, w.hmid, m->Fp, T, F, m->Hp,
                     H, es::kEpiGelu, st)) != ES_OK) return s;
-      if ((s = gemm(m, ES_KC_FFN2, m->hmid, m->Fp, D.w_2, D.b_2, m->x, m->x, H, T, H, m->Fp, F,
+      if ((s = gemm(m, ES_KC_FFN2, w.hmid, m->Fp, D.w_2, D.b_2, w.x, w.x, H, T, H, m->Fp, F,
                     es::kEpiResidual, st)) != ES_OK) return s;
     }
   }
@@ -496,9 +520,10 @@ es_status forward(es_model *m, const int32_t *d_ids, const es::Ragged &r, int64_
   return ES_OK;
 }
 
-es_status head(es_model *m, const es::Ragged &r, float offset, float *rewards, hipStream_t st) {
+es_status head(es_model *m, Workspace &w, const es::Ragged &r, float offset, float *rewards,
+               hipStream_t st) {
   Prof p(m, st, ES_KC_HEAD);
-  HIP_TRY(es::launch_head(m->pre_ln, m->x, m->H, r, m->norm_g, m->norm_b, m->eps, m->head_w,
+  HIP_TRY(es::launch_head(m->pre_ln, w.x, m->H, r, m->norm_g, m->norm_b, m->eps, m->head_w,
                           m->head_b, offset, rewards, st));
   p.done(2.0 * r.n_seqs * m->H, 8.0 * r.n_seqs * m->H);
   return ES_OK;
@@ -577,8 +602,8 @@ extern "C" es_status es_score_batch(es_model *m, const int32_t *d_token_ids, con
   es::Ragged r;
   int64_t pairs = 0;
   if ((s = prepare(m, h_offsets, n_seqs, st, &r, &pairs)) != ES_OK) return s;
-  if ((s = forward(m, d_token_ids, r, pairs, m->L, st)) != ES_OK) return s;
-  if ((s = head(m, r, m->offset, d_rewards, st)) != ES_OK) return s;
+  if ((s = forward(m, m->ws[0], d_token_ids, r, pairs, m->L, st)) != ES_OK) return s;
+  if ((s = head(m, m->ws[0], r, m->offset, d_rewards, st)) != ES_OK) return s;
   es::clear_error();
   return ES_OK;
 }
@@ -628,11 +653,26 @@ extern "C" es_status es_score_requests(es_model *m, const int32_t *d_token_ids,
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
   if ((s = upload_meta(m, st)) != ES_OK) return s;
-  // a3..a13: every batch through the layers; the head scatters to request order
+  // a3..a13: every batch through the layers; the head scatters to request
+  // order.  With k workspaces, batch b runs on internal stream b % k, forked
+  // from and joined back to the caller's stream.
+  const int k = m->lanes;
+  if (k > 1) {
+    HIP_TRY(hipEventRecord(m->fork_ev, st));
+    for (int i = 0; i < k; ++i) HIP_TRY(hipStreamWaitEvent(m->ws[i].stream, m->fork_ev, 0));
+  }
   for (int32_t b = 0; b < nb; ++b) {
+    Workspace &w = m->ws[b % k];
+    hipStream_t ls = k > 1 ? w.stream : st;
     const es::Ragged r = ragged_of(m, layouts[b]);
-    if ((s = forward(m, d_token_ids, r, layouts[b].pairs, m->L, st)) != ES_OK) return s;
-    if ((s = head(m, r, m->offset, d_rewards, st)) != ES_OK) return s;
+    if ((s = forward(m, w, d_token_ids, r, layouts[b].pairs, m->L, ls)) != ES_OK) return s;
+    if ((s = head(m, w, r, m->offset, d_rewards, ls)) != ES_OK) return s;
+  }
+  if (k > 1) {
+    for (int i = 0; i < k; ++i) {
+      HIP_TRY(hipEventRecord(m->ws[i].done, m->ws[i].stream));
+      HIP_TRY(hipStreamWaitEvent(st, m->ws[i].done, 0));
+    }
   }
   if (stats) {
     stats->n_batches = nb;
@@ -655,8 +695,27 @@ extern "C" es_status es_forward_hidden(es_model *m, const int32_t *d_token_ids,
   es::Ragged r;
   int64_t pairs = 0;
   if ((s = prepare(m, h_offsets, n_seqs, st, &r, &pairs)) != ES_OK) return s;
-  if ((s = forward(m, d_token_ids, r, pairs, n_layers, st)) != ES_OK) return s;
-  HIP_TRY(hipMemcpyAsync(d_hidden, m->x, (size_t)r.n_tokens * m->H * 4, hipMemcpyDeviceToDevice, st));
+  if ((s = forward(m, m->ws[0], d_token_ids, r, pairs, n_layers, st)) != ES_OK) return s;
+  HIP_TRY(hipMemcpyAsync(d_hidden, m->ws[0].x, (size_t)r.n_tokens * m->H * 4, hipMemcpyDeviceToDevice, st));
+  return ES_OK;
+}
+
+extern "C" es_status es_set_concurrency(es_model *m, int32_t batches_in_flight) {
+  if (!m) return fail(ES_ERR_ARG, "model handle is NULL");
+  if (batches_in_flight < 1 || batches_in_flight > 4)
+    return fail(ES_ERR_ARG, "batches_in_flight=%d outside [1, 4]", batches_in_flight);
+  HIP_TRY(hipDeviceSynchronize());
+  if (!m->fork_ev) HIP_TRY(hipEventCreateWithFlags(&m->fork_ev, hipEventDisableTiming));
+  while ((int)m->ws.size() < batches_in_flight) {
+    m->ws.emplace_back();
+    es_status s = alloc_workspace(m, m->ws.back());
+    if (s != ES_OK) return s;
+  }
+  for (auto &w : m->ws) {
+    if (!w.stream) HIP_TRY(hipStreamCreateWithFlags(&w.stream, hipStreamNonBlocking));
+    if (!w.done) HIP_TRY(hipEventCreateWithFlags(&w.done, hipEventDisableTiming));
+  }
+  m->lanes = batches_in_flight;  // extra workspaces stay allocated until es_free
   return ES_OK;
 }
 
@@ -678,13 +737,30 @@ extern "C" es_status es_calibrate_offset(es_model *m, const int32_t *d_token_ids
                                          float *offset_out) {
   es_status s = check_model(m);
   if (s != ES_OK) return s;
-  if (!offset_out || !d_token_ids) return fail(ES_ERR_ARG, "NULL argument");
+  if (!offset_out || !d_token_ids || !h_offsets) return fail(ES_ERR_ARG, "NULL argument");
+  if (n_ref < 1) return fail(ES_ERR_ARG, "n_ref=%d < 1", n_ref);
+  if (h_offsets[0] != 0) return fail(ES_ERR_ARG, "offsets[0]=%d, must be 0", h_offsets[0]);
+  std::vector<int32_t> lens((size_t)n_ref);
+  for (int32_t i = 0; i < n_ref; ++i) {
+    lens[i] = h_offsets[i + 1] - h_offsets[i];
+    if (lens[i] < 1) return fail(ES_ERR_ARG, "offsets not strictly increasing at %d", i);
+  }
+  // raw rewards of the whole reference set through the planned-stream path
+  // (any size; batch composition does not change a sequence's reward)
+  if ((size_t)n_ref > m->rew_cap) {
+    HIP_TRY(hipDeviceSynchronize());
+    if (m->rew) HIP_TRY(hipFree(m->rew));
+    m->rew = nullptr;
+    m->rew_cap = 0;
+    HIP_TRY(hipMalloc((void **)&m->rew, (size_t)n_ref * 4));
+    m->rew_cap = (size_t)n_ref;
+  }
+  const float saved = m->offset;
+  m->offset = 0.0f;
+  s = es_score_requests(m, d_token_ids, lens.data(), n_ref, 0, m->rew, stream, nullptr);
+  m->offset = saved;
+  if (s != ES_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  es::Ragged r;
-  int64_t pairs = 0;
-  if ((s = prepare(m, h_offsets, n_ref, st, &r, &pairs)) != ES_OK) return s;
-  if ((s = forward(m, d_token_ids, r, pairs, m->L, st)) != ES_OK) return s;
-  if ((s = head(m, r, 0.0f, m->rew, st)) != ES_OK) return s;
   std::vector<float> raw((size_t)n_ref);
   HIP_TRY(hipMemcpyAsync(raw.data(), m->rew, raw.size() * 4, hipMemcpyDeviceToHost, st));
   HIP_TRY(hipStreamSynchronize(st));

@@ -168,18 +168,30 @@ es_status es_score_requests(es_model *m, const int32_t *d_token_ids, const int32
 es_status es_forward_hidden(es_model *m, const int32_t *d_token_ids, const int32_t *h_offsets,
                             int32_t n_seqs, int32_t n_layers, float *d_hidden, void *stream);
 
+/*
+ * es_set_concurrency -- number of planned batches es_score_requests keeps in
+ * flight at once (1..4, default 1).  Each needs its own activation and score
+ * workspace (allocated here, synchronously, sized like the first) and runs on
+ * an internal stream forked from and joined back to the caller's stream, so
+ * the call stays ordered on that stream.  Batches are still formed by the
+ * planner; this only overlaps their kernels to fill the GPU.  Other entry
+ * points use one workspace on the caller's stream.  Errors: ES_ERR_ARG,
+ * ES_ERR_HIP.
+ */
+es_status es_set_concurrency(es_model *m, int32_t batches_in_flight);
+
 /* Set / read the scalar added to every reward. */
 es_status es_set_reward_offset(es_model *m, float offset);
 es_status es_get_reward_offset(const es_model *m, float *offset);
 
 /*
- * es_calibrate_offset -- score a reference set (same layout as
- * es_score_batch, at most max_seqs sequences and max_tokens tokens) with the
- * offset at zero, and return offset = -mean(raw rewards) (mean over the set in
- * double precision, stored as float) so that the reference set averages zero
- * ("Learning to summarize from human feedback", Method).  Synchronises
- * `stream`.  The model's offset is NOT changed; pass the result to
- * es_set_reward_offset.
+ * es_calibrate_offset -- score a reference set (packed like es_score_batch,
+ * any number of sequences; it is planned into batches internally as in
+ * es_score_requests) with the offset at zero, and return
+ * offset = -mean(raw rewards) (mean in double precision, stored as float) so
+ * that the reference set averages zero ("Learning to summarize from human
+ * feedback", Method).  Synchronises `stream`.  The model's offset is NOT
+ * changed; pass the result to es_set_reward_offset.
  */
 es_status es_calibrate_offset(es_model *m, const int32_t *d_token_ids, const int32_t *h_offsets,
                               int32_t n_ref, void *stream, float *offset_out);

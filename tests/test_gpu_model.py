@@ -187,3 +187,25 @@ def test_out_of_range_token_sets_device_flag():
     assert e.value.status == -7
     sc.check_device_errors()                     # flag was cleared
     assert np.isfinite(r.cpu().numpy()).all()
+
+
+@pytest.mark.parametrize("lanes", [2, 3])
+def test_batches_in_flight_match_serial(lanes):
+    """Overlapping planned batches on internal streams changes nothing (bitwise)."""
+    torch = need_gpu()
+    cfg = CASES[3][1]
+    w = make_weights(cfg)
+    ids, lengths = random_stream(10, 60, 1, 200, cfg.vocab)
+    sc = scorer_for(cfg, w, 0.25, max_tokens=600, max_seqs=512)
+    d = torch.from_numpy(ids).cuda()
+    serial, st1 = sc.score_requests(d, lengths, batch_overhead=64)
+    serial = serial.clone()
+    sc.set_concurrency(lanes)
+    for _ in range(2):
+        par, st2 = sc.score_requests(d, lengths, batch_overhead=64)
+        torch.cuda.synchronize()
+        assert st2 == st1 and st1["n_batches"] > lanes
+        assert torch.equal(par, serial)
+    sc.set_concurrency(1)
+    again, _ = sc.score_requests(d, lengths, batch_overhead=64)
+    assert torch.equal(again, serial)
