@@ -141,7 +141,7 @@ def main():
     rid, rlen = make_reference_set(cfg)
     d_ref = torch.from_numpy(rid).cuda()
     roff = np.concatenate([[0], np.cumsum(rlen)]).astype(np.int32)
-    if int(rlen.sum()) <= cfg.max_tokens:
+    if not args.single_step:
         sc.reward_offset = sc.calibrate_offset(d_ref, roff)   # reference set averages zero
     sc.set_concurrency(args.in_flight)
     d_ids = torch.from_numpy(ids).cuda()

@@ -757,7 +757,7 @@ extern "C" es_status es_calibrate_offset(es_model *m, const int32_t *d_token_ids
   }
   const float saved = m->offset;
   m->offset = 0.0f;
-  s = es_score_requests(m, d_token_ids, lens.data(), n_ref, 0, m->rew, stream, nullptr);
+  s = es_score_requests(m, d_token_ids, lens.data(), n_ref, 1024, m->rew, stream, nullptr);
   m->offset = saved;
   if (s != ES_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);

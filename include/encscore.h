@@ -10,7 +10,7 @@
  *     ("batch reduction") Softmax and LayerNorm kernels, no fixed-length
  *     padding, requests sorted by length and grouped by a dynamic-programming
  *     batch scheduler;
- *   - "Learning to summarize from human feedback" (summary; Method): a scalar
+ *   - "Learning to summarize from human feedback" (summary; Method adaptation): a scalar
  *     head read at the end of the complete sequence, with rewards normalised
  *     so that reference sequences average zero.
  *
@@ -113,7 +113,7 @@ es_status es_model_info(const es_model *m, es_model_info_t *info);
  *   d_rewards    float32[n_seqs] on the device; rewards[i] = w . h + b +
  *                offset, h the final hidden state of the LAST token of
  *                sequence i (after the final LayerNorm for pre-LN models)
- *                ("Learning to summarize from human feedback", Method: scalar
+ *                ("Learning to summarize from human feedback", Method adaptation: scalar
  *                head, reward at the end of the complete sequence).
  *
  * Host-side validation (synchronous, before any device work): n_seqs in

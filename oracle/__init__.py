@@ -12,7 +12,7 @@ Sources (the pages, by title and section):
     as row ("batch") reductions next to the BLAS GEMMs; requests sorted by
     length and grouped by a dynamic-programming batch scheduler with minimal
     padding.
-  * "Learning to summarize from human feedback" (summary), Method: the reward
+  * "Learning to summarize from human feedback" (summary), Method adaptation: the reward
     model is a transformer with a scalar head, the reward is read at the end
     of the complete sequence, and rewards are normalised so that reference
     summaries average zero; best-of-N scores N candidates per prompt.

@@ -4,7 +4,7 @@ Model, read from the pages (see the package docstring for titles):
   * Encoder workloads (compact BERT / BERT-base shapes): post-LN layers with an
     embedding LayerNorm, bidirectional attention inside each sequence.
   * Decoder reward model ("Learning to summarize from human feedback",
-    Method): pre-LN layers, causal attention, a final LayerNorm, and a scalar
+    Compute setup and Method adaptation): pre-LN layers, causal attention, a final LayerNorm, and a scalar
     head read at the last token of the complete sequence.
   * Every workload: token + learned absolute position embeddings (positions
     restart at 0 in each sequence), GELU in its exact erf form, LayerNorm with
@@ -194,7 +194,7 @@ class OracleModel:
     def calibrate_offset(self, ref_seqs):
         """offset = -mean of the raw reference rewards (mean taken in float64).
 
-        "Learning to summarize from human feedback", Method: reward outputs are
+        "Learning to summarize from human feedback", Method adaptation: reward outputs are
         normalised so that reference summaries score zero on average.
         """
         raw = self.score_many(ref_seqs, 0.0)

@@ -6,7 +6,8 @@ model deployment": TinyBERT for batch-1 online inference), BERT-base-sized
 encoders serving variable-length request streams (TurboTransformers review,
 "Main results": lengths 2-100 and 5-500), and a GPT-style decoder reward model
 with a scalar head on the final token ("Learning to summarize from human
-feedback", Method: 1.3B decoder, summaries under 48 tokens, best-of-N).
+feedback", Compute setup / Method adaptation / Limitations: 1.3B decoder,
+summaries under 48 tokens, best-of-N).
 """
 from dataclasses import dataclass, field
 
