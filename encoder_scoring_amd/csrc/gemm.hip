@@ -24,35 +24,49 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kBK = 64;       // K step per pipeline stage (128 bytes of bf16 per row)
-constexpr int kThreads = 256; // 4 wavefronts in a 2 x 2 grid
+// One GEMM kernel instance: block tile BM x BN, K depth BK per pipeline
+// stage, WGM x WGN wavefronts (each owning a (BM/WGM) x (BN/WGN) sub-tile of
+// 32 x 32 MFMA tiles), PF register staging sets (global prefetch distance),
+// MINW wavefronts per SIMD the register budget is set for.
+template <int BM_, int BN_, int BK_, int WGM_, int WGN_, int PF_, int MINW_>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, WGM = WGM_, WGN = WGN_, PF = PF_;
+  static constexpr int MINW = MINW_;
+  static constexpr int NT = 64 * WGM * WGN;
+  static constexpr int WM = BM / WGM, WN = BN / WGN, TM = WM / 32, TN = WN / 32;
+  static constexpr int CPR = BK / 8;            // 16-byte chunks per LDS row
+  static constexpr int RPL = 256 / (BK * 2);    // rows sharing one 256-byte bank line
+  static_assert(TM >= 1 && TN >= 1 && RPL >= 1, "bad tile");
+  static_assert((BM * CPR) % NT == 0 && (BN * CPR) % NT == 0, "tile not divisible by threads");
+};
 
-// LDS tile layout: rows of 64 bf16 (128 B, no padding); the eight 16-byte
-// k-chunks of row r are stored XOR-swizzled, slot = chunk ^ ((r >> 1) & 7).
-// gfx950 LDS serves a 16-byte read for 16 lanes per cycle from 64 four-byte
-// banks (256-byte lines): two consecutive 128-byte rows share a line, so the
-// swizzle must separate rows of equal parity -- then the 16 rows read by 16
-// lanes at one k-chunk land in 16 distinct bank groups (measured with
-// SQ_LDS_BANK_CONFLICT), and row-wise 16-byte writes stay contiguous.
-__device__ __forceinline__ int swz_slot(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
-__device__ __forceinline__ int swz(int row, int chunk) { return row * kBK + (swz_slot(row, chunk) << 3); }
+// LDS tile layout: rows of BK bf16, no padding; the 16-byte k-chunks of row r
+// are XOR-swizzled by (r / rows-per-line) mod chunks-per-row.  gfx950 LDS
+// serves a 16-byte read for 16 lanes per cycle from 64 four-byte banks
+// (256-byte lines), so the 16 rows read by 16 lanes at one k-chunk must land
+// on 16 distinct (line offset, chunk slot) pairs -- they do (checked with
+// SQ_LDS_BANK_CONFLICT = 0) -- while row-wise 16-byte writes stay contiguous.
+template <class C>
+__device__ __forceinline__ int swz_slot(int row, int chunk) {
+  return chunk ^ ((row / C::RPL) % C::CPR);
+}
 
-// Staging registers of one pipeline stage: ROWS x 64 bf16 spread over the
-// block, 16 bytes per thread per chunk, held in ONE vector value so it lives
-// in VGPRs (an array here would be demoted to scratch or LDS).
-template <int ROWS>
+// Staging registers of one stage: ROWS x BK bf16 spread over the block, 16
+// bytes per thread per chunk, held in ONE vector value so it stays in VGPRs
+// (an array here is demoted to scratch or LDS by the compiler).
+template <class C, int ROWS>
 struct Stage {
-  static constexpr int C = ROWS * kBK / 8 / kThreads;
-  typedef uint32_t vec_t __attribute__((ext_vector_type(4 * C)));
+  static constexpr int N = ROWS * C::CPR / C::NT;
+  typedef uint32_t vec_t __attribute__((ext_vector_type(4 * N)));
   vec_t v;
 };
 
-template <int ROWS>
-__device__ __forceinline__ void load_stage(Stage<ROWS> &r, const uint16_t *__restrict__ g,
+template <class C, int ROWS>
+__device__ __forceinline__ void load_stage(Stage<C, ROWS> &r, const uint16_t *__restrict__ g,
                                            int64_t ld, int k0, int tid) {
 #pragma unroll
-  for (int i = 0; i < Stage<ROWS>::C; ++i) {
-    const int c = tid + kThreads * i, row = c >> 3, kc = c & 7;
+  for (int i = 0; i < Stage<C, ROWS>::N; ++i) {
+    const int c = tid + C::NT * i, row = c / C::CPR, kc = c % C::CPR;
     const uint4 u = *reinterpret_cast<const uint4 *>(g + row * ld + k0 + kc * 8);
     r.v[4 * i + 0] = u.x;
     r.v[4 * i + 1] = u.y;
@@ -61,12 +75,12 @@ __device__ __forceinline__ void load_stage(Stage<ROWS> &r, const uint16_t *__res
   }
 }
 
-template <int ROWS>
-__device__ __forceinline__ void store_stage(const Stage<ROWS> &r, uint16_t *s, int tid) {
+template <class C, int ROWS>
+__device__ __forceinline__ void store_stage(const Stage<C, ROWS> &r, uint16_t *s, int tid) {
 #pragma unroll
-  for (int i = 0; i < Stage<ROWS>::C; ++i) {
-    const int c = tid + kThreads * i, row = c >> 3, kc = c & 7;
-    *reinterpret_cast<uint4 *>(s + swz(row, kc)) =
+  for (int i = 0; i < Stage<C, ROWS>::N; ++i) {
+    const int c = tid + C::NT * i, row = c / C::CPR, kc = c % C::CPR;
+    *reinterpret_cast<uint4 *>(s + row * C::BK + (swz_slot<C>(row, kc) << 3)) =
         make_uint4(r.v[4 * i + 0], r.v[4 * i + 1], r.v[4 * i + 2], r.v[4 * i + 3]);
   }
 }
@@ -76,6 +90,7 @@ template <int EPI>
 __device__ __forceinline__ void epi_store4(void *out, const float *res, int ldc, int64_t m, int n,
                                            int N, float4 v, const float *__restrict__ bias) {
   const int64_t o = m * ldc + n;
+  constexpr bool RES = EPI == kEpiResidual || EPI == kEpiResidualFfn;
   if (n + 3 < N) {
     const float4 b = *reinterpret_cast<const float4 *>(bias + n);
     v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w;
@@ -88,7 +103,7 @@ __device__ __forceinline__ void epi_store4(void *out, const float *res, int ldc,
       u.y = (uint32_t)f2bf(v.z) | ((uint32_t)f2bf(v.w) << 16);
       *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(out) + o) = u;
     } else {
-      if (EPI == kEpiResidual || EPI == kEpiResidualFfn) {
+      if (RES) {
         const float4 r = *reinterpret_cast<const float4 *>(res + o);
         v.x += r.x; v.y += r.y; v.z += r.z; v.w += r.w;
       }
@@ -103,37 +118,27 @@ __device__ __forceinline__ void epi_store4(void *out, const float *res, int ldc,
     float x = vv[e] + bias[n + e];
     if (EPI == kEpiBias) static_cast<uint16_t *>(out)[o + e] = f2bf(x);
     else if (EPI == kEpiGelu) static_cast<uint16_t *>(out)[o + e] = f2bf(gelu_erf(x));
-    else if (EPI == kEpiResidual || EPI == kEpiResidualFfn) static_cast<float *>(out)[o + e] = x + res[o + e];
+    else if (RES) static_cast<float *>(out)[o + e] = x + res[o + e];
     else static_cast<float *>(out)[o + e] = x;
   }
 }
 
 // ---------------------------------------------------------------- bf16 MFMA
 //
-// Block tile BM x BN, K step 64, four wavefronts in a 2 x 2 grid each owning a
-// (BM/2) x (BN/2) sub-tile of 32 x 32 MFMA tiles.  A and W tiles are staged
-// through two LDS buffers fed from two register staging sets, so the global
-// loads of step k+2 are in flight while the matrix cores work on step k; one
-// barrier per step.  The MFMA is issued as W x A so a
-// lane's accumulators hold four consecutive output columns of one row, which
-// the epilogue writes as one vector.
-// Resident blocks per CU the kernel is register-budgeted for (LDS allows
-// 160 KB / (2 * (BM + BN) * 128 B) of them).
-template <int BM, int BN>
-constexpr int gemm_occupancy() {
-  constexpr int lds = 2 * (BM + BN) * kBK * 2;  // two stages of A and W tiles, bytes
-  return 160 * 1024 / lds >= 3 ? 3 : 160 * 1024 / lds;
-}
-
-template <int BM, int BN, int EPI>
-__global__ __launch_bounds__(kThreads, (gemm_occupancy<BM, BN>())) void gemm_bf16_kernel(
+// A and W tiles stage through two LDS buffers; with PF = 2 they are fed from
+// two register staging sets so the global loads of step k+2 are in flight
+// while the matrix cores work on step k (PF = 1: loads of step k+1).  One
+// barrier per step.  The MFMA is issued as W x A so a lane's accumulators hold
+// four consecutive output columns of one row, which the epilogue writes as
+// one vector.
+template <class C, int EPI>
+__global__ __launch_bounds__(C::NT, C::MINW) void gemm_bf16_kernel(
     const uint16_t *__restrict__ A, int lda, const uint16_t *__restrict__ W,
     const float *__restrict__ bias, const float *res, void *out, int ldc, int M, int N, int K,
     int tiles_m, int tiles_n) {
-  constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
-  static_assert(Stage<BM>::C >= 1 && Stage<BN>::C >= 1 && TM >= 1 && TN >= 1, "tile too small");
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * kBK];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * kBK];
+  constexpr int BM = C::BM, BN = C::BN, BK = C::BK, TM = C::TM, TN = C::TN;
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * BK];
 
   // XCD-aware order: consecutive block ids go to different XCDs (8 of them),
   // so remap them so each XCD works on a contiguous run of tiles, and walk
@@ -153,7 +158,7 @@ __global__ __launch_bounds__(kThreads, (gemm_occupancy<BM, BN>())) void gemm_bf1
   const int tn = (bid % (G * tiles_n)) / gm;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / C::WGN, wn = wave % C::WGN;
   const int64_t m0 = (int64_t)tm * BM;
   const int n0 = tn * BN;
   const uint16_t *Ag = A + m0 * lda;
@@ -167,40 +172,22 @@ __global__ __launch_bounds__(kThreads, (gemm_occupancy<BM, BN>())) void gemm_bf1
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // Three tiles in flight: LDS buffer kt & 1 holds tile kt, register set
-  // (kt + 1) & 1 holds tile kt + 1 (loaded one iteration earlier), and the
-  // loads of tile kt + 2 go into the free register set before the matrix
-  // cores start on tile kt.  The loop is unrolled by two so both register sets
-  // are fixed names.
-  Stage<BM> ra0, ra1;
-  Stage<BN> rb0, rb1;
-  const int nk = K / kBK;
-  load_stage<BM>(ra0, Ag, lda, 0, tid);
-  load_stage<BN>(rb0, Wg, K, 0, tid);
-  if (nk > 1) {
-    load_stage<BM>(ra1, Ag, lda, kBK, tid);
-    load_stage<BN>(rb1, Wg, K, kBK, tid);
-  }
-  store_stage<BM>(ra0, sA[0], tid);
-  store_stage<BN>(rb0, sB[0], tid);
-  __syncthreads();
-
   const int fr = lane & 31, fh = lane >> 5;  // fragment row, k-half of this lane
-  const uint16_t *a_base = sA[0] + (wm * WM + fr) * kBK;
-  const uint16_t *b_base = sB[0] + (wn * WN + fr) * kBK;
+  const uint16_t *a_base = sA[0] + (C::WM * wm + fr) * BK;
+  const uint16_t *b_base = sB[0] + (C::WN * wn + fr) * BK;
   auto mma_tile = [&](int buf) {
-    const uint16_t *a_s = a_base + buf * BM * kBK;
-    const uint16_t *b_s = b_base + buf * BN * kBK;
+    const uint16_t *a_s = a_base + buf * BM * BK;
+    const uint16_t *b_s = b_base + buf * BN * BK;
 #pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      const int slot = swz_slot(fr, kk * 2 + fh) << 3;
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      const int slot = swz_slot<C>(fr, kk * 2 + fh) << 3;
       bf16x8 a[TM], b[TN];
 #pragma unroll
       for (int i = 0; i < TM; ++i)
-        a[i] = *reinterpret_cast<const bf16x8 *>(a_s + i * 32 * kBK + slot);
+        a[i] = *reinterpret_cast<const bf16x8 *>(a_s + i * 32 * BK + slot);
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        b[j] = *reinterpret_cast<const bf16x8 *>(b_s + j * 32 * kBK + slot);
+        b[j] = *reinterpret_cast<const bf16x8 *>(b_s + j * 32 * BK + slot);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -208,41 +195,75 @@ __global__ __launch_bounds__(kThreads, (gemm_occupancy<BM, BN>())) void gemm_bf1
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
     }
   };
-  for (int kt = 0; kt < nk; kt += 2) {
-    if (kt + 2 < nk) {
-      load_stage<BM>(ra0, Ag, lda, (kt + 2) * kBK, tid);
-      load_stage<BN>(rb0, Wg, K, (kt + 2) * kBK, tid);
+
+  const int nk = K / BK;
+  Stage<C, BM> ra0, ra1;
+  Stage<C, BN> rb0, rb1;
+  load_stage<C, BM>(ra0, Ag, lda, 0, tid);
+  load_stage<C, BN>(rb0, Wg, K, 0, tid);
+  if (C::PF == 2 && nk > 1) {
+    load_stage<C, BM>(ra1, Ag, lda, BK, tid);
+    load_stage<C, BN>(rb1, Wg, K, BK, tid);
+  }
+  store_stage<C, BM>(ra0, sA[0], tid);
+  store_stage<C, BN>(rb0, sB[0], tid);
+  __syncthreads();
+
+  if (C::PF == 2) {
+    // LDS buffer kt & 1 holds tile kt, register set (kt + 1) & 1 holds tile
+    // kt + 1, loads of tile kt + 2 go into the free set.  Unrolled by two so
+    // both register sets are fixed names.
+    for (int kt = 0; kt < nk; kt += 2) {
+      if (kt + 2 < nk) {
+        load_stage<C, BM>(ra0, Ag, lda, (kt + 2) * BK, tid);
+        load_stage<C, BN>(rb0, Wg, K, (kt + 2) * BK, tid);
+      }
+      mma_tile(0);
+      if (kt + 1 < nk) {
+        store_stage<C, BM>(ra1, sA[1], tid);
+        store_stage<C, BN>(rb1, sB[1], tid);
+      }
+      __syncthreads();
+      if (kt + 1 >= nk) break;
+      if (kt + 3 < nk) {
+        load_stage<C, BM>(ra1, Ag, lda, (kt + 3) * BK, tid);
+        load_stage<C, BN>(rb1, Wg, K, (kt + 3) * BK, tid);
+      }
+      mma_tile(1);
+      if (kt + 2 < nk) {
+        store_stage<C, BM>(ra0, sA[0], tid);
+        store_stage<C, BN>(rb0, sB[0], tid);
+      }
+      __syncthreads();
     }
-    mma_tile(0);
-    if (kt + 1 < nk) {
-      store_stage<BM>(ra1, sA[1], tid);
-      store_stage<BN>(rb1, sB[1], tid);
+  } else {
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      const bool more = kt + 1 < nk;
+      if (more) {
+        load_stage<C, BM>(ra0, Ag, lda, (kt + 1) * BK, tid);
+        load_stage<C, BN>(rb0, Wg, K, (kt + 1) * BK, tid);
+      }
+      mma_tile(cur);
+      if (more) {
+        store_stage<C, BM>(ra0, sA[cur ^ 1], tid);
+        store_stage<C, BN>(rb0, sB[cur ^ 1], tid);
+      }
+      __syncthreads();
     }
-    __syncthreads();
-    if (kt + 1 >= nk) break;
-    if (kt + 3 < nk) {
-      load_stage<BM>(ra1, Ag, lda, (kt + 3) * kBK, tid);
-      load_stage<BN>(rb1, Wg, K, (kt + 3) * kBK, tid);
-    }
-    mma_tile(1);
-    if (kt + 2 < nk) {
-      store_stage<BM>(ra0, sA[0], tid);
-      store_stage<BN>(rb0, sB[0], tid);
-    }
-    __syncthreads();
   }
 
   // acc[i][j] = D[n][m] of the W x A product: lane holds row m = lane & 31
   // and register r holds column 8 * (r / 4) + 4 * (lane / 32) + (r % 4).
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
-    const int64_t m = m0 + wm * WM + i * 32 + fr;
+    const int64_t m = m0 + C::WM * wm + i * 32 + fr;
     if (m >= M) continue;
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * WN + j * 32 + 8 * g + 4 * fh;
+        const int n = n0 + C::WN * wn + j * 32 + 8 * g + 4 * fh;
         if (n < N)
           epi_store4<EPI>(out, res, ldc, m, n, N,
                           make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1],
@@ -305,27 +326,28 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float *__restrict__
   }
 }
 
-template <int BM, int BN>
+template <class C>
 hipError_t go_bf16(const uint16_t *A, int lda, const uint16_t *W, const float *bias,
                    const float *res, void *out, int ldc, int M, int N, int K, int epi,
                    hipStream_t st) {
-  const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
-  const dim3 grid(tm * tn), block(kThreads);
+  if (K % C::BK) return hipErrorInvalidValue;
+  const int tm = (M + C::BM - 1) / C::BM, tn = (N + C::BN - 1) / C::BN;
+  const dim3 grid(tm * tn), block(C::NT);
   switch (epi) {
     case kEpiBias:
-      gemm_bf16_kernel<BM, BN, kEpiBias><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K, tm, tn);
+      gemm_bf16_kernel<C, kEpiBias><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K, tm, tn);
       break;
     case kEpiGelu:
-      gemm_bf16_kernel<BM, BN, kEpiGelu><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K, tm, tn);
+      gemm_bf16_kernel<C, kEpiGelu><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K, tm, tn);
       break;
     case kEpiResidual:
-      gemm_bf16_kernel<BM, BN, kEpiResidual><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K, tm, tn);
+      gemm_bf16_kernel<C, kEpiResidual><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K, tm, tn);
       break;
     case kEpiF32:
-      gemm_bf16_kernel<BM, BN, kEpiF32><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K, tm, tn);
+      gemm_bf16_kernel<C, kEpiF32><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K, tm, tn);
       break;
     case kEpiResidualFfn:
-      gemm_bf16_kernel<BM, BN, kEpiResidualFfn><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K, tm, tn);
+      gemm_bf16_kernel<C, kEpiResidualFfn><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K, tm, tn);
       break;
     default:
       return hipErrorInvalidValue;
@@ -333,40 +355,51 @@ hipError_t go_bf16(const uint16_t *A, int lda, const uint16_t *W, const float *b
   return hipGetLastError();
 }
 
+// Configurations kept after a sweep on MI355X (TFLOP/s, bf16, this kernel):
+//                            4096x768x3072  4096x3072x768  16384x3072x768  16384x2048x8192
+//   T0 128x128, 4 waves           429            486             566              843
+//   T1 128x64,  4 waves           445            498             559              697
+//   T2 256x256, 8 waves           188            468             632              968
+// Larger per-wave tiles at one wavefront per SIMD (256x128, 128x256,
+// 256x256 with 4 waves, K depth 128) were slower on every shape: a second
+// wavefront per SIMD hides more latency than the saved LDS traffic buys.
+//                  BM   BN   BK WGM WGN PF MINW
+using T0 = Cfg<128, 128, 64, 2, 2, 2, 2>;   // 64 x 64 per wave, 2 waves / SIMD
+using T1 = Cfg<128, 64, 64, 2, 2, 2, 3>;    // 64 x 32 per wave, 3 waves / SIMD
+using T2 = Cfg<256, 256, 64, 2, 4, 1, 2>;   // 8 waves of 128 x 64, 2 waves / SIMD
+constexpr int kNumTiles = 3;
+
 constexpr int kCUs = 256;
 
 }  // namespace
 
-// Tile shape for an M x N x K problem.  Measured on MI355X (bf16, this
-// kernel): 128 x 128 tiles (two blocks per CU) win once there are enough of
-// them to fill the chip twice, or K is long; below that 128 x 64 tiles (three
-// blocks per CU) keep more CUs busy.  Every tile shape issues the same MFMA
-// over K in the same order and K is never split, so each output's
-// accumulation order does not depend on the tile chosen or on the other
-// sequences in the batch.
+// Configuration for an M x N x K problem, from the sweep above: 256 x 256
+// blocks once they fill every CU, else 128 x 128 blocks (two per CU) when
+// there are enough of them or K is long, else 128 x 64 blocks (three per CU).  Every configuration issues the same MFMA over K in the same
+// order and K is never split, so each output's accumulation order does not
+// depend on the configuration chosen or on the other sequences in the batch.
 int gemm_tile_index(int M, int N, int K) {
+  const int64_t b256 = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
   const int64_t b128 = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
-  if (b128 >= 4 * kCUs || (K >= 2048 && b128 >= 2 * kCUs)) return 3;
-  return 4;
+  if (b256 >= kCUs) return 2;
+  if (b128 >= 4 * kCUs || (K >= 2048 && b128 >= 2 * kCUs)) return 0;
+  return 1;
 }
 
 hipError_t launch_gemm_bf16_tile(int tile, const uint16_t *A, int lda, const uint16_t *W,
                                  const float *bias, const float *res, void *out, int ldc, int M,
                                  int N, int K, int epi, hipStream_t st) {
   if (M <= 0 || N <= 0) return hipSuccess;
-  if (K <= 0 || K % kBK) return hipErrorInvalidValue;
+  if (K <= 0 || K % 64) return hipErrorInvalidValue;
   switch (tile) {
-    case 0: return go_bf16<256, 256>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
-    case 1: return go_bf16<256, 128>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
-    case 2: return go_bf16<128, 256>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
-    case 3: return go_bf16<128, 128>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
-    case 4: return go_bf16<128, 64>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
-    case 5: return go_bf16<64, 128>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
+    case 0: return go_bf16<T0>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
+    case 1: return go_bf16<T1>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
+    case 2: return go_bf16<T2>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
     default: return hipErrorInvalidValue;
   }
 }
 
-// ES_GEMM_TILE=<0..5> forces one tile shape (for tuning sweeps); unset = model.
+// ES_GEMM_TILE=<0..2> forces one configuration (for tuning sweeps); unset = model.
 hipError_t launch_gemm_bf16(const uint16_t *A, int lda, const uint16_t *W, const float *bias,
                             const float *res, void *out, int ldc, int M, int N, int K, int epi,
                             hipStream_t st) {
@@ -374,7 +407,7 @@ hipError_t launch_gemm_bf16(const uint16_t *A, int lda, const uint16_t *W, const
     const char *e = std::getenv("ES_GEMM_TILE");
     return e ? std::atoi(e) : -1;
   }();
-  const int tile = forced >= 0 ? forced : gemm_tile_index(M, N, K);
+  const int tile = forced >= 0 && forced < kNumTiles ? forced : gemm_tile_index(M, N, K);
   return launch_gemm_bf16_tile(tile, A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
 }
 
