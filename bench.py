@@ -30,7 +30,7 @@ PEAKS = {  # MI355X published peaks
     "mfma_bf16": (2500.0, "TFLOP/s"),
     "alu_fp32": (157.3, "TFLOP/s"),
 }
-GEMM_CLASSES = ("qkv_gemm", "oproj_gemm", "ffn1_gemm", "ffn2_gemm")
+GEMM_CLASSES = ("qkv_gemm", "oproj_gemm", "ffn1_gemm", "ffn2_gemm", "attn_fused")
 HBM_CLASSES = ("softmax", "layernorm", "embed", "head")
 WORKLOAD_DESC = {
     "tiny_fp32": "2-layer fp32 encoder (hidden 128, 2 heads, FFN 512, vocab 1000); 8 requests U{2..32}",
@@ -111,6 +111,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--single-step", action="store_true",
                     help="one warm-up call and one step, then exit (for counter collection)")
+    ap.add_argument("--attention", default="unfused", choices=["unfused", "fused"],
+                    help="attention as scores + softmax row reduction + P.V, or one fused kernel")
     ap.add_argument("--in-flight", type=int, default=3,
                     help="planned batches overlapped on internal streams (es_set_concurrency)")
     args = ap.parse_args()
@@ -144,6 +146,8 @@ def main():
     if not args.single_step:
         sc.reward_offset = sc.calibrate_offset(d_ref, roff)   # reference set averages zero
     sc.set_concurrency(args.in_flight)
+    if cfg.bf16:
+        sc.set_attention(args.attention)
     d_ids = torch.from_numpy(ids).cuda()
     out = torch.empty(n, dtype=torch.float32, device="cuda")
 
@@ -232,7 +236,8 @@ def main():
         "config": {"workload": cfg.name, "description": WORKLOAD_DESC[cfg.name],
                    "requests": n, "tokens": n_tokens, "batches": stats["n_batches"],
                    "padded_tokens": stats["padded_tokens"], "max_tokens": cfg.max_tokens,
-                   "batch_overhead": c, "batches_in_flight": args.in_flight},
+                   "batch_overhead": c, "batches_in_flight": args.in_flight,
+                   "attention": args.attention if cfg.bf16 else "unfused"},
         "tokens_per_s": round(n_tokens / (ms / 1e3), 1),
         "roofline": {"bound": bound, "kernel": dominant, "achieved": round(achieved, 2),
                      "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),

@@ -157,6 +157,11 @@ class Scorer:
         """Planned batches es_score_requests overlaps on internal streams (1..4)."""
         check(self.lib, self.lib.es_set_concurrency(self.handle, int(batches_in_flight)))
 
+    def set_attention(self, mode):
+        """"unfused" (scores, softmax row reduction, P.V) or "fused" (one kernel)."""
+        code = {"unfused": 0, "fused": 1}[mode]
+        check(self.lib, self.lib.es_set_attention(self.handle, code))
+
     def profile_enable(self, classes=None):
         """Record HIP events around the given kernel classes (names; None = all)."""
         names = _lib.KERNEL_CLASSES

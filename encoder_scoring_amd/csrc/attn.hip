@@ -181,6 +181,41 @@ __global__ __launch_bounds__(64) void scores_mfma_kernel(const uint16_t *__restr
   }
 }
 
+// V tile of keys [k0, k0 + 32) of one head, staged into LDS transposed:
+// sV[e * kVP + key].  A lane loads 4 keys x 8 dims (four coalesced 16-byte
+// reads along the key rows) and writes them as eight 8-byte rows of 4 keys,
+// so the MFMA fragments below read keys contiguously.  Keys >= n become 0.
+constexpr int kVP = 40;  // LDS pitch of a transposed row (32 keys + 8, keeps 16-byte reads aligned)
+
+template <int DP>
+__device__ __forceinline__ void stage_vt(uint16_t *__restrict__ sV, const uint16_t *__restrict__ V,
+                                         int ldq, int k0, int n, int lane) {
+  constexpr int OCT = DP / 8;
+#pragma unroll
+  for (int u = lane; u < 8 * OCT; u += 64) {
+    const int quad = u / OCT, oct = u % OCT;
+    uint4 r[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int key = k0 + 4 * quad + j;
+      r[j] = key < n ? *reinterpret_cast<const uint4 *>(V + (int64_t)key * ldq + oct * 8)
+                     : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      const int c = d >> 1, sh = (d & 1) * 16;
+      auto pick = [&](const uint4 &x) {
+        const uint32_t w = c == 0 ? x.x : c == 1 ? x.y : c == 2 ? x.z : x.w;
+        return (w >> sh) & 0xffffu;
+      };
+      const uint2 w = make_uint2(pick(r[0]) | (pick(r[1]) << 16), pick(r[2]) | (pick(r[3]) << 16));
+      *reinterpret_cast<uint2 *>(sV + (oct * 8 + d) * kVP + 4 * quad) = w;
+    }
+  }
+}
+
+// P.V: ctx^T = V^T P^T on MFMA.  P rows are read straight from global
+// memory, 8 consecutive keys per lane; the V tile comes transposed from LDS.
 template <int DP>
 __global__ __launch_bounds__(64) void pv_mfma_kernel(const uint16_t *__restrict__ P,
                                                      const uint16_t *__restrict__ qkv, int ldq,
@@ -189,8 +224,8 @@ __global__ __launch_bounds__(64) void pv_mfma_kernel(const uint16_t *__restrict_
                                                      const int64_t *__restrict__ sbase,
                                                      const int32_t *__restrict__ items,
                                                      uint16_t *__restrict__ ctx, int ldc) {
-  constexpr int NT = DP / 32, VP = 32 + 8;  // output column tiles; LDS pitch of V^T
-  __shared__ __attribute__((aligned(16))) uint16_t sV[DP * VP];
+  constexpr int NT = DP / 32;  // output column tiles
+  __shared__ __attribute__((aligned(16))) uint16_t sV[DP * kVP];
   const int item = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
   const int seq = items[2 * item], q0 = items[2 * item + 1];
   const int64_t t0 = off[seq];
@@ -210,23 +245,11 @@ __global__ __launch_bounds__(64) void pv_mfma_kernel(const uint16_t *__restrict_
   const int kend = causal ? min(n, q0 + kQTile) : n;
   for (int k0 = 0; k0 < kend; k0 += 32) {
     __syncthreads();
-    // V tile (32 keys x DP) -> LDS transposed: sV[e][key]
-#pragma unroll
-    for (int c = lane; c < 32 * DP / 8; c += 64) {
-      const int key = c / (DP / 8), e0 = (c % (DP / 8)) * 8;
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (k0 + key < n) u = *reinterpret_cast<const uint4 *>(V + (int64_t)(k0 + key) * ldq + e0);
-      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        sV[(e0 + 2 * j) * VP + key] = (uint16_t)(w[j] & 0xffff);
-        sV[(e0 + 2 * j + 1) * VP + key] = (uint16_t)(w[j] >> 16);
-      }
-    }
+    stage_vt<DP>(sV, V, ldq, k0, n, lane);
     __syncthreads();
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const int kb = k0 + kk * 16 + fh * 8;  // first key of this lane's P chunk
+      const int kb = k0 + kk * 16 + fh * 8;  // first key of this lane's chunk
       bf16x8 pf;
       if (kb + 7 < qlim) {
         pf = ld_frag(Pr + kb);
@@ -241,7 +264,7 @@ __global__ __launch_bounds__(64) void pv_mfma_kernel(const uint16_t *__restrict_
       }
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const bf16x8 vf = ld_frag(sV + (t * 32 + fr) * VP + kk * 16 + fh * 8);
+        const bf16x8 vf = ld_frag(sV + (t * 32 + fr) * kVP + kk * 16 + fh * 8);
         acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, acc[t], 0, 0, 0);
       }
     }
@@ -256,6 +279,110 @@ __global__ __launch_bounds__(64) void pv_mfma_kernel(const uint16_t *__restrict_
       uint2 u;
       u.x = (uint32_t)f2bf(acc[t][4 * g]) | ((uint32_t)f2bf(acc[t][4 * g + 1]) << 16);
       u.y = (uint32_t)f2bf(acc[t][4 * g + 2]) | ((uint32_t)f2bf(acc[t][4 * g + 3]) << 16);
+      *reinterpret_cast<uint2 *>(Cr + t * 32 + 8 * g + 4 * fh) = u;
+    }
+}
+
+// Fused attention for one (32-query tile, head): per 32-key tile, the scores
+// S^T = K Q^T (MFMA), an online softmax (running max and sum per query,
+// rescaling the context accumulator), and ctx^T += V^T P^T (MFMA) -- the
+// score rows never leave registers.  With K as the first operand a lane
+// holds keys k0 + 8 g + 4 fh + (0..3) of its query; the P.V MFMA is fed those
+// registers directly by giving its 16 k-slots the key order
+//   slots 0..3 -> keys 16 kk + 4 fh + (0..3),  slots 4..7 -> 16 kk + 8 + 4 fh + (0..3)
+// and reading the transposed V tile in the same order (two 8-byte LDS reads).
+// The contraction is order-free, so the result equals softmax(S) V up to
+// rounding.
+template <int DP>
+__global__ __launch_bounds__(64) void attn_fused_kernel(const uint16_t *__restrict__ qkv, int ldq,
+                                                        int n_heads, float scale, int causal,
+                                                        const int32_t *__restrict__ off,
+                                                        const int32_t *__restrict__ items,
+                                                        uint16_t *__restrict__ ctx, int ldc) {
+  constexpr int KS = DP / 16, NT = DP / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t sV[DP * kVP];
+  const int item = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+  const int seq = items[2 * item], q0 = items[2 * item + 1];
+  const int64_t t0 = off[seq];
+  const int n = off[seq + 1] - (int)t0;
+  const int fr = lane & 31, fh = lane >> 5;
+  const int q = q0 + fr;
+  bf16x8 qf[KS];
+  const uint16_t *Qr = qkv + (t0 + q) * ldq + h * DP + fh * 8;
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) qf[kk] = q < n ? ld_frag(Qr + kk * 16) : zero_frag();
+  const uint16_t *Kb = qkv + t0 * ldq + (n_heads + h) * DP + fh * 8;
+  const uint16_t *V = qkv + t0 * ldq + (2 * n_heads + h) * DP;
+  f32x16 acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  const int kend = causal ? min(n, q0 + kQTile) : n;
+  for (int k0 = 0; k0 < kend; k0 += 32) {
+    __syncthreads();
+    stage_vt<DP>(sV, V, ldq, k0, n, lane);
+    const int k = k0 + fr;
+    f32x16 s;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const bf16x8 kf = k < n ? ld_frag(Kb + (int64_t)k * ldq + kk * 16) : zero_frag();
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s, 0, 0, 0);
+    }
+    // every query sees at least key k0 in this tile, so the tile max is finite
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = k0 + 8 * (r >> 2) + 4 * fh + (r & 3);
+      const bool ok = key < n && (!causal || key <= q);
+      s[r] = ok ? s[r] * scale : -INFINITY;
+      mx = fmaxf(mx, s[r]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));  // the other 16 keys of this query
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = expf(m_run - m_new);
+    float psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s[r] = expf(s[r] - m_new);
+      psum += s[r];
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[t][r] *= alpha;
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      bf16x8 pf;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pf[j] = __builtin_bit_cast(__bf16, f2bf(s[8 * kk + j]));
+      const int c0 = 16 * kk + 4 * fh;  // tile keys of slots 0..3; slots 4..7 are c0 + 8
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const uint16_t *vr = sV + (t * 32 + fr) * kVP + c0;
+        const uint2 lo = *reinterpret_cast<const uint2 *>(vr);
+        const uint2 hi = *reinterpret_cast<const uint2 *>(vr + 8);
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, acc[t], 0, 0, 0);
+      }
+    }
+  }
+  if (q >= n) return;
+  const float inv = 1.0f / (l_run + __shfl_xor(l_run, 32, kWave));
+  uint16_t *Cr = ctx + (t0 + q) * ldc + h * DP;
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      uint2 u;
+      u.x = (uint32_t)f2bf(acc[t][4 * g] * inv) | ((uint32_t)f2bf(acc[t][4 * g + 1] * inv) << 16);
+      u.y = (uint32_t)f2bf(acc[t][4 * g + 2] * inv) | ((uint32_t)f2bf(acc[t][4 * g + 3] * inv) << 16);
       *reinterpret_cast<uint2 *>(Cr + t * 32 + 8 * g + 4 * fh) = u;
     }
 }
@@ -302,6 +429,18 @@ hipError_t launch_pv(bool act_bf16, const void *P, const void *qkv, int ldq, int
       pv_kernel<float, float, DP><<<grid, block, 0, st>>>((const float *)P, (const float *)qkv, ldq,
                                                           n_heads, causal ? 1 : 0, r.off, r.sbase,
                                                           r.items, (float *)ctx, ldc);
+    return hipGetLastError();
+  });
+}
+
+hipError_t launch_attn_fused(const uint16_t *qkv, int ldq, int n_heads, int dp, float scale,
+                             bool causal, const Ragged &r, uint16_t *ctx, int ldc, hipStream_t st) {
+  if (r.n_items <= 0) return hipSuccess;
+  const dim3 grid(r.n_items, n_heads);
+  return dispatch_dp(dp, [&](auto dpc) {
+    constexpr int DP = decltype(dpc)::value;
+    attn_fused_kernel<DP><<<grid, dim3(64), 0, st>>>(qkv, ldq, n_heads, scale, causal ? 1 : 0,
+                                                     r.off, r.items, ctx, ldc);
     return hipGetLastError();
   });
 }

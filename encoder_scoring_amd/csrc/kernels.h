@@ -75,5 +75,9 @@ hipError_t launch_scores(bool act_bf16, const void *qkv, int ldq, int n_heads, i
                          bool causal, const Ragged &r, float *S, hipStream_t st);
 hipError_t launch_pv(bool act_bf16, const void *P, const void *qkv, int ldq, int n_heads, int dp,
                      bool causal, const Ragged &r, void *ctx, int ldc, hipStream_t st);
+// Fused attention (bf16): scores, online softmax and P.V in one kernel; the
+// score rows never leave registers.
+hipError_t launch_attn_fused(const uint16_t *qkv, int ldq, int n_heads, int dp, float scale,
+                             bool causal, const Ragged &r, uint16_t *ctx, int ldc, hipStream_t st);
 
 }  // namespace es

@@ -60,6 +60,7 @@ struct es_model {
   int Hp = 0, Nqkv = 0, Kc = 0, Fp = 0;
   // capacity
   int64_t max_tokens = 0, Tcap = 0, score_cap = 0;
+  int attn_mode = 0;  // 0: scores -> softmax -> P.V, 1: fused
   int max_seqs = 0, max_items = 0;
   int device = 0;
   // weights
@@ -450,6 +451,13 @@ using Workspace = es_model::Workspace;
 es_status attention(es_model *m, Workspace &w, const es::Ragged &r, int64_t pairs, hipStream_t st) {
   const float scale = 1.0f / std::sqrt((float)m->d);
   const double a = m->bf16 ? 2.0 : 4.0, T = r.n_tokens, Hd = (double)m->H;
+  if (m->bf16 && m->attn_mode == 1) {
+    Prof p(m, st, ES_KC_ATTN_FUSED);
+    HIP_TRY(es::launch_attn_fused((const uint16_t *)w.qkv, m->Nqkv, m->A, m->dp, scale, m->causal, r,
+                                  (uint16_t *)w.ctx, m->Kc, st));
+    p.done(4.0 * m->d * pairs, 4.0 * T * Hd * a);  // Q, K, V read, ctx written
+    return ES_OK;
+  }
   {
     Prof p(m, st, ES_KC_SCORES);
     HIP_TRY(es::launch_scores(m->bf16, w.qkv, m->Nqkv, m->A, m->dp, scale, m->causal, r, w.S, st));
@@ -719,6 +727,14 @@ extern "C" es_status es_set_concurrency(es_model *m, int32_t batches_in_flight) 
   return ES_OK;
 }
 
+extern "C" es_status es_set_attention(es_model *m, int32_t mode) {
+  if (!m) return fail(ES_ERR_ARG, "model handle is NULL");
+  if (mode != 0 && mode != 1) return fail(ES_ERR_ARG, "attention mode %d (0 unfused, 1 fused)", mode);
+  if (mode == 1 && !m->bf16) return fail(ES_ERR_ARG, "fused attention needs a bf16 model");
+  m->attn_mode = mode;
+  return ES_OK;
+}
+
 extern "C" es_status es_set_reward_offset(es_model *m, float offset) {
   if (!m) return fail(ES_ERR_ARG, "model handle is NULL");
   if (!std::isfinite(offset)) return fail(ES_ERR_ARG, "offset is not finite");
@@ -816,6 +832,6 @@ extern "C" es_status es_profile_collect(es_model *m, es_kernel_stat_t *out) {
 extern "C" const char *es_kernel_class_name(int32_t cls) {
   static const char *names[ES_KC_COUNT] = {"embed", "qkv_gemm", "scores", "softmax", "pv",
                                            "oproj_gemm", "layernorm", "ffn1_gemm", "ffn2_gemm",
-                                           "head"};
+                                           "head", "attn_fused"};
   return (cls >= 0 && cls < ES_KC_COUNT) ? names[cls] : "";
 }

@@ -180,6 +180,16 @@ es_status es_forward_hidden(es_model *m, const int32_t *d_token_ids, const int32
  */
 es_status es_set_concurrency(es_model *m, int32_t batches_in_flight);
 
+/*
+ * es_set_attention -- how the masked attention of each layer runs (bf16
+ * models): 0 (default) = three kernels, scores to HBM, the Softmax row
+ * reduction (TurboTransformers review, Proposed method), then P.V; 1 = one
+ * fused kernel per (query tile, head) that keeps each score row in registers
+ * with an online softmax (same result up to rounding, no score traffic).
+ * fp32 models support 0 only.  Errors: ES_ERR_ARG.
+ */
+es_status es_set_attention(es_model *m, int32_t mode);
+
 /* Set / read the scalar added to every reward. */
 es_status es_set_reward_offset(es_model *m, float offset);
 es_status es_get_reward_offset(const es_model *m, float *offset);
@@ -308,7 +318,7 @@ es_status es_op_gemm_bf16(const uint16_t *d_a, int32_t lda, const uint16_t *d_w,
 enum {
   ES_KC_EMBED = 0, ES_KC_QKV = 1, ES_KC_SCORES = 2, ES_KC_SOFTMAX = 3, ES_KC_PV = 4,
   ES_KC_OPROJ = 5, ES_KC_LAYERNORM = 6, ES_KC_FFN1 = 7, ES_KC_FFN2 = 8, ES_KC_HEAD = 9,
-  ES_KC_COUNT = 10
+  ES_KC_ATTN_FUSED = 10, ES_KC_COUNT = 11
 };
 
 typedef struct {

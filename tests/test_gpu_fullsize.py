@@ -23,9 +23,10 @@ BF16_TOL = 1e-2
 IN_FLIGHT = 3
 
 
-def _stream(torch, cfg, w, ids, lengths, offset=0.0):
+def _stream(torch, cfg, w, ids, lengths, offset=0.0, attention="unfused"):
     sc = Scorer(blob.to_bytes(cfg, w, offset), cfg.max_tokens, min(cfg.max_tokens, 65536))
     sc.set_concurrency(IN_FLIGHT)
+    sc.set_attention(attention)
     d = torch.from_numpy(ids).cuda()
     rew, stats = sc.score_requests(d, lengths, cfg.batch_overhead)
     again, _ = sc.score_requests(d, lengths, cfg.batch_overhead)
@@ -66,12 +67,13 @@ def test_bert_base_short_full_stream():
     _check_sample(torch, sc, cfg, w, ids, lengths, rew, idx)
 
 
-def test_bert_base_longtail_full_stream():
+@pytest.mark.parametrize("attention", ["unfused", "fused"])
+def test_bert_base_longtail_full_stream(attention):
     torch = need_gpu()
     cfg = get_config("bert_base_longtail")
     w = make_weights(cfg)
     ids, lengths, _ = make_requests(cfg)
-    sc, rew = _stream(torch, cfg, w, ids, lengths)
+    sc, rew = _stream(torch, cfg, w, ids, lengths, attention=attention)
     idx = np.random.default_rng(2).choice(lengths.size, 3, replace=False)
     idx = np.concatenate([idx, [int(np.argmax(lengths)), int(np.argmin(lengths))]])
     _check_sample(torch, sc, cfg, w, ids, lengths, rew, idx)
@@ -87,13 +89,14 @@ def test_tinybert_fixed_length_batch64(n):
     _check_sample(torch, sc, cfg, w, ids, lengths, rew, np.array([0, 31, 63]))
 
 
-def test_decoder_rm_best_of_16_full_stream():
+@pytest.mark.parametrize("attention", ["unfused", "fused"])
+def test_decoder_rm_best_of_16_full_stream(attention):
     torch = need_gpu()
     cfg = get_config("decoder_rm")
     say("decoder_rm: drawing 1.4B weights")
     w = make_weights(cfg)
     ids, lengths, group = make_requests(cfg)
-    sc, rew = _stream(torch, cfg, w, ids, lengths)
+    sc, rew = _stream(torch, cfg, w, ids, lengths, attention=attention)
     # calibration on the reference set (64 x ~540 tokens, several batches)
     rid, rlen = make_reference_set(cfg)
     d_ref = torch.from_numpy(rid).cuda()

@@ -209,3 +209,38 @@ def test_batches_in_flight_match_serial(lanes):
     sc.set_concurrency(1)
     again, _ = sc.score_requests(d, lengths, batch_overhead=64)
     assert torch.equal(again, serial)
+
+
+@pytest.mark.parametrize("name,cfg", [(c[0], c[1]) for c in CASES if c[1].bf16],
+                         ids=[c[0] for c in CASES if c[1].bf16])
+def test_fused_attention_matches_oracle_and_unfused(name, cfg):
+    """The fused attention kernel: same rewards as the oracle (1e-2) and close
+    to the three-kernel path (both round P to bf16, in different places)."""
+    torch = need_gpu()
+    w = make_weights(cfg)
+    ids, lengths = random_stream(15, 13, 1, min(cfg.max_pos, 200), cfg.vocab)
+    sc = scorer_for(cfg, w, offset=0.125)
+    unfused = gpu_score(torch, sc, ids, lengths)
+    sc.set_attention("fused")
+    fused = gpu_score(torch, sc, ids, lengths)
+    assert np.array_equal(fused, gpu_score(torch, sc, ids, lengths))
+    want = oracle.OracleModel(cfg, w).score_many(split(ids, lengths), 0.125)
+    say(name, "fused max |d| =", float(np.max(np.abs(fused - want))),
+        "vs unfused", float(np.max(np.abs(fused - unfused))))
+    assert np.max(np.abs(fused - want)) <= BF16_TOL
+    assert np.max(np.abs(fused - unfused)) <= 5e-3
+    sc.set_attention("unfused")
+    assert np.array_equal(gpu_score(torch, sc, ids, lengths), unfused)
+
+
+def test_fused_attention_hidden_states():
+    torch = need_gpu()
+    cfg = CASES[3][1]          # causal pre-LN, head dim 128
+    w = make_weights(cfg)
+    ids, lengths = random_stream(16, 7, 1, 150, cfg.vocab)
+    sc = scorer_for(cfg, w)
+    sc.set_attention("fused")
+    m = oracle.OracleModel(cfg, w)
+    got = sc.hidden(torch.from_numpy(ids).cuda(), offsets_of(lengths), 1).cpu().numpy()
+    want = np.concatenate([m.hidden(s, 1) for s in split(ids, lengths)])
+    assert np.max(np.abs(got - want)) < 0.05 * max(1.0, float(np.max(np.abs(want))))
