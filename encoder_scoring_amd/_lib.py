@@ -24,7 +24,7 @@ EXPORTS = [
     "es_score_requests",
     "es_forward_hidden", "es_set_reward_offset", "es_get_reward_offset", "es_calibrate_offset",
     "es_check_device_errors", "es_plan_batches", "es_pack_offsets", "es_op_layernorm",
-    "es_ragged_create", "es_ragged_free", "es_op_softmax", "es_op_gemm_bf16", "es_last_error",
+    "es_ragged_create", "es_ragged_free", "es_op_softmax", "es_op_gemm_bf16", "es_op_gemm_bf16_tile", "es_last_error",
     "es_version", "es_set_concurrency", "es_set_attention", "es_profile_enable", "es_profile_collect", "es_kernel_class_name",
 ]
 
@@ -83,6 +83,7 @@ _SIGS = {
     "es_ragged_free": (None, [_P]),
     "es_op_softmax": (ctypes.c_int32, [_P, _P, _P, ctypes.c_int32, _P]),
     "es_op_gemm_bf16": (ctypes.c_int32, [_P, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P]),
+    "es_op_gemm_bf16_tile": (ctypes.c_int32, [_P, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P]),
     "es_profile_enable": (ctypes.c_int32, [_P, ctypes.c_uint32]),
     "es_profile_collect": (ctypes.c_int32, [_P, ctypes.POINTER(KernelStat)]),
     "es_kernel_class_name": (ctypes.c_char_p, [ctypes.c_int32]),

@@ -231,13 +231,16 @@ def softmax_ragged(rag, scores, probs):
                                  _dptr(probs, probs.dtype, "probs"), int(p_bf16), _stream()))
 
 
-def gemm_bf16(a, w, bias, out, M, N, K, epilogue, res=None):
-    """out = epilogue(A W^T + bias) on the bf16 MFMA kernel (a, w as int16 bits)."""
+def gemm_bf16(a, w, bias, out, M, N, K, epilogue, res=None, tile=None):
+    """out = epilogue(A W^T + bias) on the bf16 MFMA kernel (a, w as int16 bits);
+    tile forces a block-tile configuration (0, 1, 2), None chooses from the shape."""
     torch = _torch()
     lib = _lib.load()
-    check(lib, lib.es_op_gemm_bf16(
-        _dptr(a, torch.int16, "a"), a.shape[1], _dptr(w, torch.int16, "w"),
-        _dptr(bias, torch.float32, "bias"),
-        _dptr(res, torch.float32, "res") if res is not None else None,
-        ctypes.c_void_p(out.data_ptr()), out.shape[1], int(M), int(N), int(K), int(epilogue),
-        _stream()))
+    args = (_dptr(a, torch.int16, "a"), a.shape[1], _dptr(w, torch.int16, "w"),
+            _dptr(bias, torch.float32, "bias"),
+            _dptr(res, torch.float32, "res") if res is not None else None,
+            ctypes.c_void_p(out.data_ptr()), out.shape[1], int(M), int(N), int(K), int(epilogue))
+    if tile is None:
+        check(lib, lib.es_op_gemm_bf16(*args, _stream()))
+    else:
+        check(lib, lib.es_op_gemm_bf16_tile(*args, int(tile), _stream()))

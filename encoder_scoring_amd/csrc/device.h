@@ -58,6 +58,31 @@ __device__ __forceinline__ float gelu_erf(float z) {
   return 0.5f * z * (1.0f + erff(z * 0.70710678118654752440f));
 }
 
+// The same GELU for outputs stored as bf16, with erfc from the Chebyshev fit
+// of Numerical Recipes (Press et al., 2nd ed., section 6.2, "erfcc":
+// fractional error below 1.2e-7 for every argument):
+//   erfc(x) = t exp(-x^2 + P(t)),  t = 1 / (1 + x/2),  x >= 0,
+// and 1 + erf(x) = 2 - erfc(x) for x >= 0, erfc(-x) for x < 0, so the
+// negative tail keeps its relative accuracy (no cancellation).  Measured in
+// float32 over z in [-12, 12]: relative error below 3e-6 wherever
+// |GELU(z)| > 1e-6, i.e. far below one bf16 step (2^-8).
+__device__ __forceinline__ float gelu_erf_bf16out(float z) {
+  const float x = fabsf(z) * 0.70710678118654752440f;
+  const float t = __builtin_amdgcn_rcpf(1.0f + 0.5f * x);
+  float p = 0.17087277f;
+  p = fmaf(p, t, -0.82215223f);
+  p = fmaf(p, t, 1.48851587f);
+  p = fmaf(p, t, -1.13520398f);
+  p = fmaf(p, t, 0.27886807f);
+  p = fmaf(p, t, -0.18628806f);
+  p = fmaf(p, t, 0.09678418f);
+  p = fmaf(p, t, 0.37409196f);
+  p = fmaf(p, t, 1.00002368f);
+  p = fmaf(p, t, -1.26551223f);
+  const float q = t * __builtin_amdgcn_exp2f((p - x * x) * 1.44269504088896340736f);  // erfc(|x|)
+  return 0.5f * z * (z >= 0.0f ? 2.0f - q : q);
+}
+
 // Sequence that owns packed token t: the last i with off[i] <= t.
 __device__ __forceinline__ int seq_of_token(const int32_t *off, int n_seqs, int t) {
   int lo = 0, hi = n_seqs - 1;

@@ -96,7 +96,8 @@ __device__ __forceinline__ void epi_store4(void *out, const float *res, int ldc,
     v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w;
     if (EPI == kEpiBias || EPI == kEpiGelu) {
       if (EPI == kEpiGelu) {
-        v.x = gelu_erf(v.x); v.y = gelu_erf(v.y); v.z = gelu_erf(v.z); v.w = gelu_erf(v.w);
+        v.x = gelu_erf_bf16out(v.x); v.y = gelu_erf_bf16out(v.y);
+        v.z = gelu_erf_bf16out(v.z); v.w = gelu_erf_bf16out(v.w);
       }
       uint2 u;
       u.x = (uint32_t)f2bf(v.x) | ((uint32_t)f2bf(v.y) << 16);
@@ -117,10 +118,29 @@ __device__ __forceinline__ void epi_store4(void *out, const float *res, int ldc,
     if (n + e >= N) break;
     float x = vv[e] + bias[n + e];
     if (EPI == kEpiBias) static_cast<uint16_t *>(out)[o + e] = f2bf(x);
-    else if (EPI == kEpiGelu) static_cast<uint16_t *>(out)[o + e] = f2bf(gelu_erf(x));
+    else if (EPI == kEpiGelu) static_cast<uint16_t *>(out)[o + e] = f2bf(gelu_erf_bf16out(x));
     else if (RES) static_cast<float *>(out)[o + e] = x + res[o + e];
     else static_cast<float *>(out)[o + e] = x;
   }
+}
+
+// XCD-aware tile order: consecutive block ids go to different XCDs (8 of
+// them), so remap them so each XCD works on a contiguous run of tiles, and
+// walk the tiles in groups of 8 M-tiles so neighbours share A rows and W rows
+// inside one XCD's L2.
+__device__ __forceinline__ void tile_of_block(int tiles_m, int tiles_n, int &tm, int &tn) {
+  const int nblk = tiles_m * tiles_n;
+  int bid = blockIdx.x;
+  {
+    const int per = (nblk + 7) / 8, xcd = bid & 7, loc = bid >> 3;
+    const int full = nblk - (per - 1) * 8;  // XCDs that receive `per` blocks
+    bid = xcd < full ? xcd * per + loc : full * per + (xcd - full) * (per - 1) + loc;
+  }
+  constexpr int G = 8;
+  const int group = bid / (G * tiles_n), first_m = group * G;
+  const int gm = min(G, tiles_m - first_m);
+  tm = first_m + (bid % (G * tiles_n)) % gm;
+  tn = (bid % (G * tiles_n)) / gm;
 }
 
 // ---------------------------------------------------------------- bf16 MFMA
@@ -140,22 +160,8 @@ __global__ __launch_bounds__(C::NT, C::MINW) void gemm_bf16_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * BK];
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * BK];
 
-  // XCD-aware order: consecutive block ids go to different XCDs (8 of them),
-  // so remap them so each XCD works on a contiguous run of tiles, and walk
-  // the tiles in groups of 8 M-tiles so neighbours share A rows and W rows
-  // inside one XCD's L2.
-  const int nblk = tiles_m * tiles_n;
-  int bid = blockIdx.x;
-  {
-    const int per = (nblk + 7) / 8, xcd = bid & 7, loc = bid >> 3;
-    const int full = nblk - (per - 1) * 8;  // XCDs that receive `per` blocks
-    bid = xcd < full ? xcd * per + loc : full * per + (xcd - full) * (per - 1) + loc;
-  }
-  constexpr int G = 8;
-  const int group = bid / (G * tiles_n), first_m = group * G;
-  const int gm = min(G, tiles_m - first_m);
-  const int tm = first_m + (bid % (G * tiles_n)) % gm;
-  const int tn = (bid % (G * tiles_n)) / gm;
+  int tm, tn;
+  tile_of_block(tiles_m, tiles_n, tm, tn);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C::WGN, wn = wave % C::WGN;
@@ -274,6 +280,210 @@ __global__ __launch_bounds__(C::NT, C::MINW) void gemm_bf16_kernel(
   }
 }
 
+// ---------------------------------------------------------------- bf16 MFMA, ping-pong
+//
+// Block BM x BN x 64, eight wavefronts in two groups of four (wave w runs on
+// SIMD w % 4, so each SIMD holds one wave of each group).  Group g owns the
+// output rows [g BM/2, (g+1) BM/2); wave q of a group owns the columns
+// [q BN/4, (q+1) BN/4).  The groups alternate between two phases that a
+// barrier separates: in one a wave reads a whole K stage of fragments from
+// LDS into registers, in the other it runs that stage's MFMAs back to back.
+// Group 1 runs one phase behind group 0, so on every SIMD one wave keeps the
+// matrix core busy while the other reads LDS, and no barrier leaves a SIMD
+// without MFMA work.
+//
+// Stages reach LDS by direct loads (buffer_load ... lds: L2 to LDS without
+// VGPRs) issued by group 0 one stage ahead into the buffer group 1 has just
+// finished reading; two 64-deep stage buffers.  A stage's rows are written
+// in the swizzled layout above by permuting, per lane, which 16-byte chunk of
+// the row it fetches.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// 16 bytes per lane from a buffer resource into LDS at lds + 16 * lane.  The
+// load is inline asm because the compiler's wait-count pass, when it sees
+// direct-to-LDS loads in a loop, waits for all of them before every LDS read;
+// the kernels order these loads with explicit vmcnt waits and barriers.  M0
+// (the LDS base of the load) is saved and restored within the statement, and
+// one wait state separates the M0 write from the load that reads it.
+__device__ __forceinline__ void dma16(i32x4 rsrc, int voff, int soff, uint32_t lds) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %4\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, %3 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds)
+      : "memory");
+}
+
+// Raw buffer resource over [p, p + 2 GB): base, stride 0, num_records,
+// 32-bit dword format.
+__device__ __forceinline__ i32x4 make_rsrc(const void *p) {
+  const uint64_t a = (uint64_t)p;
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffff));
+  r[2] = 0x7ffffff0;
+  r[3] = 0x00020000;
+  return r;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// vmcnt(n) and lgkmcnt(0) in one s_waitcnt; lgkmcnt(0) alone.
+__device__ __forceinline__ constexpr int wait_vm_lgkm0(int n) {
+  return (n & 15) | ((n >> 4) << 14) | (7 << 4);
+}
+constexpr int kWaitLgkm0 = 0xc07f;
+
+template <int BM_, int BN_>
+struct PPCfg {
+  static constexpr int BM = BM_, BN = BN_, BK = 64;
+  static constexpr int WM = BM / 2, WN = BN / 4, TM = WM / 32, TN = WN / 32;
+  static constexpr int CPR = BK / 8, RPL = 256 / (BK * 2), KS = BK / 16;
+  static constexpr int NL = 4;  // wavefronts issuing the direct loads (group 0)
+  static constexpr int NIA = BM * CPR / (64 * NL), NIB = BN * CPR / (64 * NL);
+  static constexpr int SZ = (BM + BN) * BK;  // bf16 elements per stage
+  // rows between consecutive loads of one wave; the swizzle repeats every
+  // such step, so one per-lane offset serves all of a wave's loads
+  static constexpr int DR = NL * 64 / CPR;
+  static_assert(TM >= 1 && TN >= 1, "bad tile");
+  static_assert(NIA * 64 * NL == BM * CPR && NIB * 64 * NL == BN * CPR, "stage not divisible");
+  static_assert(DR % RPL == 0 && (DR / RPL) % CPR == 0, "swizzle must repeat between loads");
+};
+
+template <class C, int EPI>
+__global__ __launch_bounds__(512, 2) void gemm_pp_kernel(
+    const uint16_t *__restrict__ A, int lda, const uint16_t *__restrict__ W,
+    const float *__restrict__ bias, const float *res, void *out, int ldc, int M, int N, int K,
+    int tiles_m, int tiles_n) {
+  constexpr int BM = C::BM, BK = C::BK, TM = C::TM, TN = C::TN, KS = C::KS, DR = C::DR;
+  // two named buffers (not one array) so the compiler can tell their
+  // accesses apart
+  __shared__ __attribute__((aligned(1024))) uint16_t L0[C::SZ];
+  __shared__ __attribute__((aligned(1024))) uint16_t L1[C::SZ];
+
+  int tm, tn;
+  tile_of_block(tiles_m, tiles_n, tm, tn);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, q = wave & 3;
+  const int64_t m0 = (int64_t)tm * BM;
+  const int n0 = tn * C::BN;
+  const uint16_t *Ag = A + m0 * lda;
+  const uint16_t *Wg = W + (int64_t)n0 * K;
+
+  const i32x4 ra = make_rsrc(Ag), rb = make_rsrc(Wg);
+  int voA, voB;  // byte offsets of this lane's chunk in the wave's first load
+  {
+    const int e = q * 64 + lane, row = e / C::CPR, slot = e % C::CPR;
+    voA = (row * lda + swz_slot<C>(row, slot) * 8) * 2;
+    voB = (row * K + swz_slot<C>(row, slot) * 8) * 2;
+  }
+  auto issue = [&](uint16_t *buf, int k0) {
+    const uint32_t l0 = lds_addr(buf) + q * 1024;
+#pragma unroll
+    for (int i = 0; i < C::NIA; ++i) dma16(ra, voA, (k0 + i * DR * lda) * 2, l0 + i * C::NL * 1024);
+#pragma unroll
+    for (int i = 0; i < C::NIB; ++i)
+      dma16(rb, voB, (k0 + i * DR * K) * 2, l0 + BM * BK * 2 + i * C::NL * 1024);
+  };
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int fr = lane & 31, fh = lane >> 5;
+  bf16x8 fa[KS][TM], fb[KS][TN];
+  auto read_stage = [&](const uint16_t *buf) {
+    const uint16_t *a_s = buf + (C::WM * grp + fr) * BK;
+    const uint16_t *b_s = buf + BM * BK + (C::WN * q + fr) * BK;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const int slot = swz_slot<C>(fr, kk * 2 + fh) << 3;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) fa[kk][i] = *reinterpret_cast<const bf16x8 *>(a_s + i * 32 * BK + slot);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) fb[kk][j] = *reinterpret_cast<const bf16x8 *>(b_s + j * 32 * BK + slot);
+    }
+  };
+  auto mma_stage = [&]() {
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kk][j], fa[kk][i], acc[i][j], 0, 0, 0);
+  };
+  // Nothing is scheduled across a phase boundary: the compiler would
+  // otherwise move MFMAs over the barrier and merge the two phases.
+  auto end_phase = [&](bool wait_loads) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (wait_loads) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
+    else __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // Phase p lies between barriers p and p+1.  Group 0 reads stage k in phase
+  // 2k and computes it in phase 2k+1; group 1 one phase later.  Group 0
+  // issues stage k+1 at the start of phase 2k into the buffer that group 1
+  // finished reading in phase 2k-1, and waits for it at the end of phase
+  // 2k+1, before it reads it.  Both groups pass 2 nk + 2 barriers.
+  const int nk = K / BK;
+  if (grp == 0) {
+    issue(L0, 0);
+    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
+  }
+  __builtin_amdgcn_s_barrier();
+  if (grp == 1) __builtin_amdgcn_s_barrier();
+  for (int k0 = 0; k0 < nk; k0 += 2) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int k = k0 + s;
+      if (k < nk) {
+        uint16_t *cur = s == 0 ? L0 : L1;
+        uint16_t *nxt = s == 0 ? L1 : L0;
+        if (grp == 0 && k + 1 < nk) issue(nxt, (k + 1) * BK);
+        read_stage(cur);
+        end_phase(false);
+        mma_stage();
+        end_phase(grp == 0);
+      }
+    }
+  }
+  if (grp == 0) __builtin_amdgcn_s_barrier();
+
+  // acc[i][j] = D[n][m] of the W x A product: lane holds row m = lane & 31
+  // and register r holds column 8 * (r / 4) + 4 * (lane / 32) + (r % 4).
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int64_t m = m0 + C::WM * grp + i * 32 + fr;
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + C::WN * q + j * 32 + 8 * g + 4 * fh;
+        if (n < N)
+          epi_store4<EPI>(out, res, ldc, m, n, N,
+                          make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1],
+                                      acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]),
+                          bias);
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- fp32 SIMT
 // 64 x 64 tile, K step 16, 4 x 4 outputs per thread; for the fp32 model.
 template <int EPI>
@@ -355,35 +565,73 @@ hipError_t go_bf16(const uint16_t *A, int lda, const uint16_t *W, const float *b
   return hipGetLastError();
 }
 
-// Configurations kept after a sweep on MI355X (TFLOP/s, bf16, this kernel):
-//                            4096x768x3072  4096x3072x768  16384x3072x768  16384x2048x8192
-//   T0 128x128, 4 waves           429            486             566              843
-//   T1 128x64,  4 waves           445            498             559              697
-//   T2 256x256, 8 waves           188            468             632              968
-// Larger per-wave tiles at one wavefront per SIMD (256x128, 128x256,
-// 256x256 with 4 waves, K depth 128) were slower on every shape: a second
-// wavefront per SIMD hides more latency than the saved LDS traffic buys.
-//                  BM   BN   BK WGM WGN PF MINW
-using T0 = Cfg<128, 128, 64, 2, 2, 2, 2>;   // 64 x 64 per wave, 2 waves / SIMD
-using T1 = Cfg<128, 64, 64, 2, 2, 2, 3>;    // 64 x 32 per wave, 3 waves / SIMD
-using T2 = Cfg<256, 256, 64, 2, 4, 1, 2>;   // 8 waves of 128 x 64, 2 waves / SIMD
-constexpr int kNumTiles = 3;
+template <class C>
+hipError_t go_pp(const uint16_t *A, int lda, const uint16_t *W, const float *bias,
+                 const float *res, void *out, int ldc, int M, int N, int K, int epi,
+                 hipStream_t st) {
+  if (K % C::BK) return hipErrorInvalidValue;
+  const int tm = (M + C::BM - 1) / C::BM, tn = (N + C::BN - 1) / C::BN;
+  const dim3 grid(tm * tn), block(512);
+  switch (epi) {
+    case kEpiBias:
+      gemm_pp_kernel<C, kEpiBias><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K, tm, tn);
+      break;
+    case kEpiGelu:
+      gemm_pp_kernel<C, kEpiGelu><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K, tm, tn);
+      break;
+    case kEpiResidual:
+      gemm_pp_kernel<C, kEpiResidual><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K, tm, tn);
+      break;
+    case kEpiF32:
+      gemm_pp_kernel<C, kEpiF32><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K, tm, tn);
+      break;
+    case kEpiResidualFfn:
+      gemm_pp_kernel<C, kEpiResidualFfn><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K, tm, tn);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// Tile configurations:
+//   0  T1  128 x 64, register-staged, 4 waves (64 x 32 each), three blocks per CU
+//   1  P1  128 x 128 ping-pong, 8 waves (64 x 32 each), two blocks per CU
+//   2  P2  256 x 256 ping-pong, 8 waves (128 x 64 each), one block per CU
+//                  BM  BN  BK WGM WGN PF MINW
+using T1 = Cfg<128, 64, 64, 2, 2, 2, 3>;
+using P1 = PPCfg<128, 128>;
+using P2 = PPCfg<256, 256>;
+static_assert(kGemmTiles == 3, "tile menu and launcher disagree");
 
 constexpr int kCUs = 256;
 
 }  // namespace
 
-// Configuration for an M x N x K problem, from the sweep above: 256 x 256
-// blocks once they fill every CU, else 128 x 128 blocks (two per CU) when
-// there are enough of them or K is long, else 128 x 64 blocks (three per CU).  Every configuration issues the same MFMA over K in the same
-// order and K is never split, so each output's accumulation order does not
-// depend on the configuration chosen or on the other sequences in the batch.
+// Configuration for an M x N x K problem, from a sweep of the model's GEMM
+// shapes on MI355X (TFLOP/s; tile 0 / 1 / 2):
+//   M      N     K    epilogue     0     1     2
+//   4096   2304  768  bias        436   462   404
+//   4096   768   768  residual    288   299   131
+//   4096   3072  768  GELU        462   551   423
+//   8192   768   3072 residual    635   728   470
+//   16384  2304  768  bias        597   658   556
+//   16384  768   3072 residual    631   734   828
+//   16384  6144  2048 bias        673   947  1043
+//   16384  2048  8192 residual    655   929  1093
+//   2048   768   768  residual    201   168    70
+// 256 x 256 blocks pay off only with a long K and enough blocks for half the
+// CUs; 128 x 128 blocks while they cover half the CUs; else 128 x 64 blocks
+// (more of them).  Every configuration issues the same MFMA over K in the
+// same order and K is never split, so each output's accumulation order does
+// not depend on the configuration chosen or on the other sequences in the
+// batch.
 int gemm_tile_index(int M, int N, int K) {
   const int64_t b256 = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
   const int64_t b128 = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
-  if (b256 >= kCUs) return 2;
-  if (b128 >= 4 * kCUs || (K >= 2048 && b128 >= 2 * kCUs)) return 0;
-  return 1;
+  if (K >= 2048 && b256 >= kCUs / 2) return 2;
+  if (b128 >= kCUs / 2) return 1;
+  return 0;
 }
 
 hipError_t launch_gemm_bf16_tile(int tile, const uint16_t *A, int lda, const uint16_t *W,
@@ -392,9 +640,9 @@ hipError_t launch_gemm_bf16_tile(int tile, const uint16_t *A, int lda, const uin
   if (M <= 0 || N <= 0) return hipSuccess;
   if (K <= 0 || K % 64) return hipErrorInvalidValue;
   switch (tile) {
-    case 0: return go_bf16<T0>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
-    case 1: return go_bf16<T1>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
-    case 2: return go_bf16<T2>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
+    case 0: return go_bf16<T1>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
+    case 1: return go_pp<P1>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
+    case 2: return go_pp<P2>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -407,7 +655,7 @@ hipError_t launch_gemm_bf16(const uint16_t *A, int lda, const uint16_t *W, const
     const char *e = std::getenv("ES_GEMM_TILE");
     return e ? std::atoi(e) : -1;
   }();
-  const int tile = forced >= 0 && forced < kNumTiles ? forced : gemm_tile_index(M, N, K);
+  const int tile = forced >= 0 && forced < kGemmTiles ? forced : gemm_tile_index(M, N, K);
   return launch_gemm_bf16_tile(tile, A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
 }
 

@@ -65,6 +65,12 @@ enum Epilogue { kEpiBias = 0, kEpiGelu = 1, kEpiResidual = 2, kEpiF32 = 3, kEpiR
 hipError_t launch_gemm_bf16(const uint16_t *A, int lda, const uint16_t *W, const float *bias,
                             const float *res, void *out, int ldc, int M, int N, int K, int epi,
                             hipStream_t st);
+// The same with one tile configuration forced: 0 = 128 x 64 register-staged,
+// 1 = 128 x 128 ping-pong, 2 = 256 x 256 ping-pong.
+constexpr int kGemmTiles = 3;
+hipError_t launch_gemm_bf16_tile(int tile, const uint16_t *A, int lda, const uint16_t *W,
+                                 const float *bias, const float *res, void *out, int ldc, int M,
+                                 int N, int K, int epi, hipStream_t st);
 hipError_t launch_gemm_f32(const float *A, int lda, const float *W, const float *bias,
                            const float *res, float *out, int ldc, int M, int N, int K, int epi,
                            hipStream_t st);

@@ -110,17 +110,39 @@ extern "C" es_status es_op_softmax(const es_ragged *r, const float *d_scores, vo
   return ES_OK;
 }
 
+static es_status gemm_bf16_checked(const char *who, const uint16_t *d_a, int32_t lda,
+                                   const uint16_t *d_w, const float *d_bias, const float *d_res,
+                                   void *d_out, int32_t ldc, int32_t M, int32_t N, int32_t K,
+                                   int32_t epilogue, int32_t tile, void *stream) {
+  if (!d_a || !d_w || !d_bias || !d_out || (epilogue == es::kEpiResidual && !d_res))
+    return fail(ES_ERR_ARG, "%s: NULL pointer", who);
+  if (M < 0 || N < 0 || K <= 0 || K % 64 || lda < K || lda % 8 || ldc < N || ldc % 4 || epilogue < 0 ||
+      epilogue > 3)
+    return fail(ES_ERR_ARG, "%s: M=%d N=%d K=%d lda=%d ldc=%d epilogue=%d", who, M, N, K, lda, ldc,
+                epilogue);
+  if (tile < -1 || tile >= es::kGemmTiles) return fail(ES_ERR_ARG, "%s: tile %d", who, tile);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (tile < 0) {
+    HIP_TRY(es::launch_gemm_bf16(d_a, lda, d_w, d_bias, d_res, d_out, ldc, M, N, K, epilogue, st));
+  } else {
+    HIP_TRY(es::launch_gemm_bf16_tile(tile, d_a, lda, d_w, d_bias, d_res, d_out, ldc, M, N, K,
+                                      epilogue, st));
+  }
+  return ES_OK;
+}
+
 extern "C" es_status es_op_gemm_bf16(const uint16_t *d_a, int32_t lda, const uint16_t *d_w,
                                      const float *d_bias, const float *d_res, void *d_out,
                                      int32_t ldc, int32_t M, int32_t N, int32_t K, int32_t epilogue,
                                      void *stream) {
-  if (!d_a || !d_w || !d_bias || !d_out || (epilogue == es::kEpiResidual && !d_res))
-    return fail(ES_ERR_ARG, "es_op_gemm_bf16: NULL pointer");
-  if (M < 0 || N < 0 || K <= 0 || K % 64 || lda < K || lda % 8 || ldc < N || ldc % 4 || epilogue < 0 ||
-      epilogue > 3)
-    return fail(ES_ERR_ARG, "es_op_gemm_bf16: M=%d N=%d K=%d lda=%d ldc=%d epilogue=%d", M, N, K,
-                lda, ldc, epilogue);
-  HIP_TRY(es::launch_gemm_bf16(d_a, lda, d_w, d_bias, d_res, d_out, ldc, M, N, K, epilogue,
-                               static_cast<hipStream_t>(stream)));
-  return ES_OK;
+  return gemm_bf16_checked("es_op_gemm_bf16", d_a, lda, d_w, d_bias, d_res, d_out, ldc, M, N, K,
+                           epilogue, -1, stream);
+}
+
+extern "C" es_status es_op_gemm_bf16_tile(const uint16_t *d_a, int32_t lda, const uint16_t *d_w,
+                                          const float *d_bias, const float *d_res, void *d_out,
+                                          int32_t ldc, int32_t M, int32_t N, int32_t K,
+                                          int32_t epilogue, int32_t tile, void *stream) {
+  return gemm_bf16_checked("es_op_gemm_bf16_tile", d_a, lda, d_w, d_bias, d_res, d_out, ldc, M, N,
+                           K, epilogue, tile, stream);
 }

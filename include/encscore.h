@@ -299,7 +299,8 @@ es_status es_op_softmax(const es_ragged *r, const float *d_scores, void *d_p, in
  *   d_w  bf16[rows >= round_up(N,256), K]    (row n = output feature n)
  *   d_bias float32[N]
  *   epilogue 0: out bf16 = acc + bias
- *            1: out bf16 = GELU(acc + bias)            (exact erf form)
+ *            1: out bf16 = GELU(acc + bias)            (erf form; erfc by a Chebyshev
+ *                                                       fit, fractional error < 1.2e-7)
  *            2: out fp32 = acc + bias + d_res[m, n]     (d_res fp32, ld ldc)
  *            3: out fp32 = acc + bias
  *   d_out [M, ldc] (bf16 for 0/1, fp32 for 2/3); only n < N, m < M written.
@@ -311,6 +312,19 @@ es_status es_op_softmax(const es_ragged *r, const float *d_scores, void *d_p, in
 es_status es_op_gemm_bf16(const uint16_t *d_a, int32_t lda, const uint16_t *d_w,
                           const float *d_bias, const float *d_res, void *d_out, int32_t ldc,
                           int32_t M, int32_t N, int32_t K, int32_t epilogue, void *stream);
+
+/*
+ * es_op_gemm_bf16_tile -- es_op_gemm_bf16 with the block-tile configuration
+ * forced instead of chosen from the shape (for tests and tuning): tile -1 =
+ * automatic, 0 = 128x64 register-staged, 1 = 128x128 ping-pong, 2 = 256x256
+ * ping-pong.  Every configuration accumulates each output over K in the same
+ * order, so all give bitwise the same result.  Errors: as es_op_gemm_bf16,
+ * and ES_ERR_ARG for a tile outside [-1, 2].
+ */
+es_status es_op_gemm_bf16_tile(const uint16_t *d_a, int32_t lda, const uint16_t *d_w,
+                               const float *d_bias, const float *d_res, void *d_out, int32_t ldc,
+                               int32_t M, int32_t N, int32_t K, int32_t epilogue, int32_t tile,
+                               void *stream);
 
 /* ------------------------------------------------------------- profiling */
 

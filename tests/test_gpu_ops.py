@@ -97,9 +97,10 @@ GEMM_SHAPES = [(1, 64, 64), (37, 936, 320), (300, 768, 768), (1000, 3072, 768),
 
 @pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
 @pytest.mark.parametrize("epi", [0, 1, 2, 3])
-def test_gemm_bf16_op(M, N, K, epi):
+@pytest.mark.parametrize("tile", [None, 0, 1, 2])
+def test_gemm_bf16_op(M, N, K, epi, tile):
     torch = need_gpu()
-    say("gemm", M, N, K, epi)
+    say("gemm", M, N, K, "epilogue", epi, "tile", tile)
     rng = np.random.default_rng(M * 7 + N * 3 + K + epi)
     Mr, Nr = -(-M // 256) * 256, -(-N // 256) * 256
     a = f32_to_bf16_bits(rng.standard_normal((Mr, K)).astype(np.float32))
@@ -116,7 +117,7 @@ def test_gemm_bf16_op(M, N, K, epi):
     db = torch.from_numpy(bias).cuda()
     if epi in (0, 1):
         out = torch.full((M, ldc), 0x5555, dtype=torch.int16, device="cuda")
-        gemm_bf16(da, dw, db, out, M, N, K, epi)
+        gemm_bf16(da, dw, db, out, M, N, K, epi, tile=tile)
         torch.cuda.synchronize()
         got = bf16_bits_to_f32(out)[:, :N].astype(np.float64)
         want = z if epi == 0 else oracle.gelu(z)
@@ -126,12 +127,33 @@ def test_gemm_bf16_op(M, N, K, epi):
     else:
         dres = torch.from_numpy(res).cuda()
         out = torch.full((M, ldc), float("nan"), dtype=torch.float32, device="cuda")
-        gemm_bf16(da, dw, db, out, M, N, K, epi, res=dres if epi == 2 else None)
+        gemm_bf16(da, dw, db, out, M, N, K, epi, res=dres if epi == 2 else None, tile=tile)
         torch.cuda.synchronize()
         got = out.cpu().numpy()[:, :N].astype(np.float64)
         want = z + res[:, :N] if epi == 2 else z
         assert np.all(np.abs(got - want) <= bound + 1e-6 * np.abs(want))
         assert np.all(np.isnan(out.cpu().numpy()[:, N:]))
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 768, 768), (4100, 2304, 768), (2100, 3072, 2048)])
+def test_gemm_tiles_bitwise_identical(M, N, K):
+    """Every tile configuration accumulates each output over K in the same
+    order, so all of them give bitwise the same fp32 result (this is what
+    makes a sequence's reward independent of the batch it is scored in)."""
+    torch = need_gpu()
+    say("gemm tiles", M, N, K)
+    rng = np.random.default_rng(M + N + K)
+    Mr, Nr = -(-M // 256) * 256, -(-N // 256) * 256
+    da = torch.from_numpy(f32_to_bf16_bits(rng.standard_normal((Mr, K)).astype(np.float32)).view(np.int16)).cuda()
+    dw = torch.from_numpy(f32_to_bf16_bits((rng.standard_normal((Nr, K)) / np.sqrt(K)).astype(np.float32)).view(np.int16)).cuda()
+    db = torch.from_numpy((0.1 * rng.standard_normal(N)).astype(np.float32)).cuda()
+    outs = []
+    for tile in (0, 1, 2):
+        out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        gemm_bf16(da, dw, db, out, M, N, K, 3, tile=tile)
+        outs.append(out)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
 
 
 def test_gemm_rejects_bad_shapes():
@@ -143,3 +165,7 @@ def test_gemm_rejects_bad_shapes():
     out = torch.zeros((4, 64), dtype=torch.int16, device="cuda")
     with pytest.raises(EncScoreError):
         gemm_bf16(a, w, bias, out, 4, 64, 96, 0)      # K not a multiple of 64
+    a64 = torch.zeros((256, 64), dtype=torch.int16, device="cuda")
+    w64 = torch.zeros((256, 64), dtype=torch.int16, device="cuda")
+    with pytest.raises(EncScoreError):
+        gemm_bf16(a64, w64, bias, out, 4, 64, 64, 0, tile=3)  # no such tile
