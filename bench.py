@@ -3,10 +3,12 @@
 
 One step = one pass of the whole hot path over the workload's request
 stream: DP batch planning, packing, embedding, every layer (QKV GEMM, masked
-scores, row softmax, P.V, output GEMM + residual, LayerNorm, FFN GEMMs with
-fused GELU / residual, LayerNorm), the last-token reward head and the scatter
-of rewards back to request order -- a single es_score_requests call on token
-ids already resident in HBM.
+attention -- fused by default, or scores + row softmax + P.V --, output GEMM +
+residual, LayerNorm, FFN GEMMs with fused GELU / residual, LayerNorm), the
+last-token reward head and the scatter of rewards back to request order -- a
+single es_score_requests call on token ids already resident in HBM.  The
+other attention form is timed on the same stream and reported under
+"variants".
 
 Prints ONE JSON line (sequences/s for the whole job).  The dominant kernel
 class is timed live with HIP events on the stream it runs on (the library's
@@ -111,10 +113,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--single-step", action="store_true",
                     help="one warm-up call and one step, then exit (for counter collection)")
-    ap.add_argument("--attention", default="unfused", choices=["unfused", "fused"],
+    ap.add_argument("--attention", default="fused", choices=["unfused", "fused"],
                     help="attention as scores + softmax row reduction + P.V, or one fused kernel")
-    ap.add_argument("--in-flight", type=int, default=3,
-                    help="planned batches overlapped on internal streams (es_set_concurrency)")
+    ap.add_argument("--in-flight", type=int, default=2,
+                    help="passes overlapped on internal streams (es_set_concurrency)")
+    ap.add_argument("--group", type=int, default=4,
+                    help="planned batches packed into one pass through the layers "
+                         "(es_set_batch_grouping)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the scoring path is "
@@ -145,6 +150,7 @@ def main():
     roff = np.concatenate([[0], np.cumsum(rlen)]).astype(np.int32)
     if not args.single_step:
         sc.reward_offset = sc.calibrate_offset(d_ref, roff)   # reference set averages zero
+    sc.set_grouping(args.group)
     sc.set_concurrency(args.in_flight)
     if cfg.bf16:
         sc.set_attention(args.attention)
@@ -171,20 +177,49 @@ def main():
     value = n / (ms / 1e3)
     assert torch.isfinite(out).all().item(), "non-finite rewards"
 
-    # roofline pass: one batch in flight so each kernel runs alone, every
+    def timed(steps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            sc.score_requests(d_ids, lengths, c, out)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / steps
+
+    # roofline pass: one pass in flight so each kernel runs alone, every
     # kernel class bracketed by HIP events on the stream it is launched on
     prof_steps = max(2, min(args.steps, 5))
-    sc.set_concurrency(1)
-    sc.score_requests(d_ids, lengths, c, out)
-    sc.profile_enable(None)
-    torch.cuda.synchronize()
-    tp0 = time.perf_counter()
-    for _ in range(prof_steps):
+
+    def profile_pass():
+        sc.set_concurrency(1)
         sc.score_requests(d_ids, lengths, c, out)
-    torch.cuda.synchronize()
-    ms_isolated = (time.perf_counter() - tp0) * 1e3 / prof_steps
-    per_class = sc.profile_collect()
-    sc.profile_enable([])
+        sc.profile_enable(None)
+        ms_iso = timed(prof_steps)
+        pc = sc.profile_collect()
+        sc.profile_enable([])
+        sc.set_concurrency(args.in_flight)
+        return pc, ms_iso
+
+    def class_table(pc):
+        table = {}
+        for k, v in pc.items():
+            if v["launches"] == 0:
+                continue
+            sec = v["total_ms"] / 1e3
+            if k in GEMM_CLASSES:
+                kpeak, kunit = PEAKS["mfma_bf16" if cfg.bf16 else "alu_fp32"]
+                ach = v["flops"] / sec / 1e12
+            elif k in HBM_CLASSES:
+                kpeak, kunit = PEAKS["hbm"]
+                ach = v["bytes"] / sec / 1e9
+            else:   # attention contractions: report flops against the MFMA peak
+                kpeak, kunit = PEAKS["mfma_bf16" if cfg.bf16 else "alu_fp32"]
+                ach = v["flops"] / sec / 1e12
+            table[k] = {"ms_per_step": round(v["total_ms"] / prof_steps, 3),
+                        "achieved": round(ach, 2), "unit": kunit, "frac": round(ach / kpeak, 4),
+                        "launches_per_step": v["launches"] // prof_steps}
+        return table
+
+    per_class, ms_isolated = profile_pass()
     dominant = max(per_class, key=lambda k: per_class[k]["total_ms"])
     dom = per_class[dominant]
     log("isolated per-class ms/step:", {k: round(v["total_ms"] / prof_steps, 3)
@@ -201,24 +236,22 @@ def main():
         achieved = dom["bytes"] / (dom["total_ms"] / 1e3) / 1e9
     peak, unit = PEAKS[key]
     traffic = traffic_from_profiles(cfg.name, dominant, launches)
+    kernels = class_table(per_class)
 
-    kernels = {}
-    for k, v in per_class.items():
-        if v["launches"] == 0:
-            continue
-        sec = v["total_ms"] / 1e3
-        if k in GEMM_CLASSES:
-            kpeak, kunit = PEAKS["mfma_bf16" if cfg.bf16 else "alu_fp32"]
-            ach = v["flops"] / sec / 1e12
-        elif k in HBM_CLASSES:
-            kpeak, kunit = PEAKS["hbm"]
-            ach = v["bytes"] / sec / 1e9
-        else:   # attention contractions: report flops against the MFMA peak
-            kpeak, kunit = PEAKS["mfma_bf16" if cfg.bf16 else "alu_fp32"]
-            ach = v["flops"] / sec / 1e12
-        kernels[k] = {"ms_per_step": round(v["total_ms"] / prof_steps, 3),
-                      "achieved": round(ach, 2), "unit": kunit, "frac": round(ach / kpeak, 4),
-                      "launches_per_step": v["launches"] // prof_steps}
+    # the other attention form, same stream and settings: its own timed steps
+    # and kernel table (the row-softmax kernel runs only in the unfused form)
+    variants = {}
+    if cfg.bf16:
+        other = "unfused" if args.attention == "fused" else "fused"
+        sc.set_attention(other)
+        sc.score_requests(d_ids, lengths, c, out)
+        ms_other = timed(args.steps)
+        assert torch.isfinite(out).all().item(), "non-finite rewards"
+        pc_other, _ = profile_pass()
+        variants["attention_" + other] = {"value": round(n / (ms_other / 1e3), 2),
+                                          "ms_per_step": round(ms_other, 3),
+                                          "kernels": class_table(pc_other)}
+        sc.set_attention(args.attention)
 
     line = {
         "metric": "sequences scored/sec on var-len batches",
@@ -236,7 +269,8 @@ def main():
         "config": {"workload": cfg.name, "description": WORKLOAD_DESC[cfg.name],
                    "requests": n, "tokens": n_tokens, "batches": stats["n_batches"],
                    "padded_tokens": stats["padded_tokens"], "max_tokens": cfg.max_tokens,
-                   "batch_overhead": c, "batches_in_flight": args.in_flight,
+                   "batch_overhead": c, "batches_per_pass": args.group,
+                   "passes_in_flight": args.in_flight,
                    "attention": args.attention if cfg.bf16 else "unfused"},
         "tokens_per_s": round(n_tokens / (ms / 1e3), 1),
         "roofline": {"bound": bound, "kernel": dominant, "achieved": round(achieved, 2),
@@ -244,8 +278,9 @@ def main():
                      "traffic": traffic, "avg_launch_ms": round(avg_ms, 5),
                      "launches_per_step": launches,
                      "measured": f"HIP events around every launch over {prof_steps} steps with one "
-                                 f"batch in flight ({ms_isolated:.2f} ms/step)"},
+                                 f"pass in flight ({ms_isolated:.2f} ms/step)"},
         "kernels": kernels,
+        "variants": variants,
         "device": torch.cuda.get_device_name(0),
     }
     if not args.no_cpu_baseline:

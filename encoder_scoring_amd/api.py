@@ -157,6 +157,10 @@ class Scorer:
         """Planned batches es_score_requests overlaps on internal streams (1..4)."""
         check(self.lib, self.lib.es_set_concurrency(self.handle, int(batches_in_flight)))
 
+    def set_grouping(self, batches_per_pass):
+        """Planned batches score_requests packs into one pass (es_set_batch_grouping)."""
+        check(self.lib, self.lib.es_set_batch_grouping(self.handle, int(batches_per_pass)))
+
     def set_attention(self, mode):
         """"unfused" (scores, softmax row reduction, P.V) or "fused" (one kernel)."""
         code = {"unfused": 0, "fused": 1}[mode]

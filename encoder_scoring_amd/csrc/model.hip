@@ -61,7 +61,7 @@ struct es_model {
   // capacity
   int64_t max_tokens = 0, Tcap = 0, score_cap = 0;
   int attn_mode = 0;  // 0: scores -> softmax -> P.V, 1: fused
-  int max_seqs = 0, max_items = 0;
+  int max_seqs = 0;
   int device = 0;
   // weights
   void *tok_emb = nullptr, *pos_emb = nullptr;
@@ -69,6 +69,7 @@ struct es_model {
   std::vector<DevLayer> layers;
   // workspaces: one per batch in flight (es_set_concurrency)
   struct Workspace {
+    int scale = 0;  // capacity in planned batches (tokens, sequences, score elements)
     float *x = nullptr, *y = nullptr, *S = nullptr;
     void *xb = nullptr, *qkv = nullptr, *ctx = nullptr, *hmid = nullptr, *Pb = nullptr;
     hipStream_t stream = nullptr;  // internal stream used when several batches are in flight
@@ -76,6 +77,7 @@ struct es_model {
   };
   std::vector<Workspace> ws;  // allocated workspaces; the first `lanes` are used
   int lanes = 1;
+  int group = 1;  // planned batches scored by one pass through the layers
   hipEvent_t fork_ev = nullptr;
   float *rew = nullptr;  // raw rewards of a reference set (es_calibrate_offset)
   size_t rew_cap = 0;
@@ -86,7 +88,7 @@ struct es_model {
   size_t meta_cap = 0;
   hipEvent_t meta_ev = nullptr;
   bool meta_pending = false;
-  std::vector<void *> allocs;
+  std::vector<std::pair<void *, size_t>> allocs;
   int64_t device_bytes = 0;
   std::vector<int32_t> order_scratch;
   // profiling (es_profile_enable / es_profile_collect)
@@ -108,17 +110,30 @@ es_status dalloc(es_model *m, void **p, size_t bytes) {
   hipError_t e = hipMalloc(p, bytes);
   if (e != hipSuccess)
     return fail(ES_ERR_HIP, "hipMalloc(%zu) failed: %s", bytes, hipGetErrorString(e));
-  m->allocs.push_back(*p);
+  m->allocs.emplace_back(*p, bytes);
   m->device_bytes += (int64_t)bytes;
   e = hipMemset(*p, 0, bytes);
   if (e != hipSuccess) return fail(ES_ERR_HIP, "hipMemset failed: %s", hipGetErrorString(e));
   return ES_OK;
 }
 
+// Free one dalloc'ed buffer (the device must be idle on it).
+void dfree(es_model *m, void *p) {
+  if (!p) return;
+  for (size_t i = 0; i < m->allocs.size(); ++i) {
+    if (m->allocs[i].first == p) {
+      m->device_bytes -= (int64_t)m->allocs[i].second;
+      m->allocs.erase(m->allocs.begin() + (std::ptrdiff_t)i);
+      (void)hipFree(p);
+      return;
+    }
+  }
+}
+
 void release(es_model *m) {
   if (!m) return;
   (void)hipDeviceSynchronize();
-  for (void *p : m->allocs) (void)hipFree(p);
+  for (auto &a : m->allocs) (void)hipFree(a.first);
   m->allocs.clear();
   if (m->meta_host) (void)hipHostFree(m->meta_host);
   if (m->meta_dev) (void)hipFree(m->meta_dev);
@@ -185,9 +200,16 @@ int64_t ctx_col(int64_t c, const es_model *m) { return (c / m->d) * m->dp + c % 
 
 // Activations and score buffers for one batch in flight (zero-filled once:
 // padding columns stay zero forever).
-es_status alloc_workspace(es_model *m, es_model::Workspace &w) {
+// Activation and score buffers for `scale` planned batches of up to
+// max_tokens tokens each; a workspace that already holds buffers is resized.
+es_status alloc_workspace(es_model *m, es_model::Workspace &w, int scale) {
+  for (void *p : {(void *)w.x, (void *)w.y, (void *)w.S, w.xb, w.qkv, w.ctx, w.hmid, w.Pb}) dfree(m, p);
+  w.x = w.y = w.S = nullptr;
+  w.xb = w.qkv = w.ctx = w.hmid = w.Pb = nullptr;
+  w.scale = 0;
   const int act = m->bf16 ? 2 : 4;
-  const int64_t T = m->Tcap;
+  const int64_t T = round_up(scale * m->max_tokens, 256);
+  const int64_t S = scale * m->score_cap;
   es_status s;
   if ((s = dalloc(m, (void **)&w.x, T * m->H * 4)) != ES_OK) return s;
   if ((s = dalloc(m, (void **)&w.y, T * m->H * 4)) != ES_OK) return s;
@@ -195,8 +217,9 @@ es_status alloc_workspace(es_model *m, es_model::Workspace &w) {
   if ((s = dalloc(m, &w.qkv, T * m->Nqkv * act)) != ES_OK) return s;
   if ((s = dalloc(m, &w.ctx, T * m->Kc * act)) != ES_OK) return s;
   if ((s = dalloc(m, &w.hmid, T * m->Fp * act)) != ES_OK) return s;
-  if ((s = dalloc(m, (void **)&w.S, m->score_cap * 4)) != ES_OK) return s;
-  if ((s = dalloc(m, &w.Pb, m->score_cap * act)) != ES_OK) return s;
+  if ((s = dalloc(m, (void **)&w.S, S * 4)) != ES_OK) return s;
+  if ((s = dalloc(m, &w.Pb, S * act)) != ES_OK) return s;
+  w.scale = scale;
   return ES_OK;
 }
 
@@ -224,7 +247,6 @@ es_status build(const es::ParsedBlob &pb, int64_t max_tokens, int32_t max_seqs, 
   m->Tcap = round_up(max_tokens, 256);
   const int64_t lmax = std::min<int64_t>(m->P, max_tokens);
   m->score_cap = (int64_t)m->A * max_tokens * es::score_ld((int)lmax);
-  m->max_items = (int)(max_tokens / es::kQTile + max_seqs + 1);
   HIP_TRY(hipGetDevice(&m->device));
 
   es_status s;
@@ -257,7 +279,7 @@ es_status build(const es::ParsedBlob &pb, int64_t max_tokens, int32_t max_seqs, 
     if ((s = upload_vec(m, &D.ln2_b, L.ln2_b, m->H)) != ES_OK) return s;
   }
   m->ws.resize(1);
-  if ((s = alloc_workspace(m, m->ws[0])) != ES_OK) return s;
+  if ((s = alloc_workspace(m, m->ws[0], 1)) != ES_OK) return s;
   if ((s = dalloc(m, (void **)&m->flag, 4)) != ES_OK) return s;
   HIP_TRY(hipEventCreateWithFlags(&m->meta_ev, hipEventDisableTiming));
   HIP_TRY(hipDeviceSynchronize());
@@ -283,10 +305,11 @@ size_t push_bytes(std::vector<uint8_t> &buf, const void *p, size_t bytes) {
 
 // Validate one batch's host offsets and append its metadata to m->meta_asm.
 es_status add_batch(es_model *m, const int32_t *h_off, int32_t n, const int32_t *src,
-                    const int32_t *dest, BatchLayout *L) {
+                    const int32_t *dest, BatchLayout *L, int scale = 1) {
   if (!h_off) return fail(ES_ERR_ARG, "offsets pointer is NULL");
   if (n < 1) return fail(ES_ERR_ARG, "n_seqs=%d < 1", n);
-  if (n > m->max_seqs) return fail(ES_ERR_CAPACITY, "n_seqs=%d above max_seqs=%d", n, m->max_seqs);
+  if (n > (int64_t)scale * m->max_seqs)
+    return fail(ES_ERR_CAPACITY, "n_seqs=%d above max_seqs=%d", n, m->max_seqs);
   if (h_off[0] != 0) return fail(ES_ERR_ARG, "offsets[0]=%d, must be 0", h_off[0]);
   int max_len = 0;
   int64_t score = 0;
@@ -296,14 +319,14 @@ es_status add_batch(es_model *m, const int32_t *h_off, int32_t n, const int32_t 
     if (len < 1) return fail(ES_ERR_ARG, "offsets not strictly increasing at %d", i);
     if (len > m->P)
       return fail(ES_ERR_RANGE, "sequence %d has length %" PRId64 " > max_pos=%d", i, len, m->P);
-    if (h_off[i + 1] > m->max_tokens)
+    if (h_off[i + 1] > scale * m->max_tokens)
       return fail(ES_ERR_CAPACITY, "batch has more than max_tokens=%" PRId64 " tokens", m->max_tokens);
     max_len = std::max<int>(max_len, (int)len);
     L->pairs += (int64_t)m->A * (m->causal ? len * (len + 1) / 2 : len * len);
     sbase[i] = score;
     score += (int64_t)m->A * len * es::score_ld((int)len);
   }
-  if (score > m->score_cap)
+  if (score > scale * m->score_cap)
     return fail(ES_ERR_CAPACITY, "batch needs %" PRId64 " score elements (capacity %" PRId64 ")",
                 score, m->score_cap);
   // attention work items, longest sequences first
@@ -641,39 +664,53 @@ extern "C" es_status es_score_requests(es_model *m, const int32_t *d_token_ids,
     acc += h_lengths[i];
     if (acc > INT32_MAX) return fail(ES_ERR_RANGE, "more than INT32_MAX tokens in one call");
   }
-  // a2: pack -- per batch, offsets over the plan order plus id-source and reward-slot maps
+  // a2: pack -- per batch, offsets over the plan order plus id-source and
+  // reward-slot maps.  G consecutive planned batches (similar lengths, the
+  // plan is sorted) are packed back to back into one layout and scored by one
+  // pass through the layers: every kernel works per token or per sequence, so
+  // a sequence's reward does not depend on which batches share the pass.
+  const int G = m->group;
+  const int32_t ng = (nb + G - 1) / G;
   m->meta_asm.clear();
-  std::vector<BatchLayout> layouts((size_t)nb);
-  std::vector<int32_t> off, src, dest;
+  std::vector<BatchLayout> layouts((size_t)ng);
+  std::vector<int32_t> off, goff, src, dest;
   int64_t padded = 0;
-  for (int32_t b = 0; b < nb; ++b) {
-    const int32_t lo = starts[b], hi = starts[b + 1], k = hi - lo;
-    off.assign((size_t)k + 1, 0);
-    src.resize((size_t)k);
-    dest.resize((size_t)k);
-    if ((s = es_pack_offsets(h_lengths, order.data(), lo, hi, off.data())) != ES_OK) return s;
-    for (int32_t j = 0; j < k; ++j) {
-      src[j] = first[order[lo + j]];
-      dest[j] = order[lo + j];
+  for (int32_t g = 0; g < ng; ++g) {
+    const int32_t b0 = g * G, b1 = std::min<int32_t>(nb, b0 + G);
+    goff.assign(1, 0);
+    src.clear();
+    dest.clear();
+    for (int32_t b = b0; b < b1; ++b) {
+      const int32_t lo = starts[b], hi = starts[b + 1], k = hi - lo;
+      off.assign((size_t)k + 1, 0);
+      if ((s = es_pack_offsets(h_lengths, order.data(), lo, hi, off.data())) != ES_OK) return s;
+      const int32_t base = goff.back();
+      for (int32_t j = 0; j < k; ++j) {
+        goff.push_back(base + off[j + 1]);
+        src.push_back(first[order[lo + j]]);
+        dest.push_back(order[lo + j]);
+      }
+      padded += (int64_t)k * h_lengths[order[hi - 1]];
     }
-    padded += (int64_t)k * h_lengths[order[hi - 1]];
-    if ((s = add_batch(m, off.data(), k, src.data(), dest.data(), &layouts[b])) != ES_OK) return s;
+    if ((s = add_batch(m, goff.data(), (int32_t)dest.size(), src.data(), dest.data(), &layouts[g],
+                       b1 - b0)) != ES_OK)
+      return s;
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
   if ((s = upload_meta(m, st)) != ES_OK) return s;
-  // a3..a13: every batch through the layers; the head scatters to request
-  // order.  With k workspaces, batch b runs on internal stream b % k, forked
+  // a3..a13: every group through the layers; the head scatters to request
+  // order.  With k workspaces, group g runs on internal stream g % k, forked
   // from and joined back to the caller's stream.
   const int k = m->lanes;
   if (k > 1) {
     HIP_TRY(hipEventRecord(m->fork_ev, st));
     for (int i = 0; i < k; ++i) HIP_TRY(hipStreamWaitEvent(m->ws[i].stream, m->fork_ev, 0));
   }
-  for (int32_t b = 0; b < nb; ++b) {
-    Workspace &w = m->ws[b % k];
+  for (int32_t g = 0; g < ng; ++g) {
+    Workspace &w = m->ws[g % k];
     hipStream_t ls = k > 1 ? w.stream : st;
-    const es::Ragged r = ragged_of(m, layouts[b]);
-    if ((s = forward(m, w, d_token_ids, r, layouts[b].pairs, m->L, ls)) != ES_OK) return s;
+    const es::Ragged r = ragged_of(m, layouts[g]);
+    if ((s = forward(m, w, d_token_ids, r, layouts[g].pairs, m->L, ls)) != ES_OK) return s;
     if ((s = head(m, w, r, m->offset, d_rewards, ls)) != ES_OK) return s;
   }
   if (k > 1) {
@@ -714,16 +751,33 @@ extern "C" es_status es_set_concurrency(es_model *m, int32_t batches_in_flight) 
     return fail(ES_ERR_ARG, "batches_in_flight=%d outside [1, 4]", batches_in_flight);
   HIP_TRY(hipDeviceSynchronize());
   if (!m->fork_ev) HIP_TRY(hipEventCreateWithFlags(&m->fork_ev, hipEventDisableTiming));
-  while ((int)m->ws.size() < batches_in_flight) {
-    m->ws.emplace_back();
-    es_status s = alloc_workspace(m, m->ws.back());
-    if (s != ES_OK) return s;
-  }
-  for (auto &w : m->ws) {
+  while ((int)m->ws.size() < batches_in_flight) m->ws.emplace_back();
+  for (int i = 0; i < batches_in_flight; ++i) {
+    es_model::Workspace &w = m->ws[i];
+    if (w.scale < m->group) {
+      es_status s = alloc_workspace(m, w, m->group);
+      if (s != ES_OK) return s;
+    }
     if (!w.stream) HIP_TRY(hipStreamCreateWithFlags(&w.stream, hipStreamNonBlocking));
     if (!w.done) HIP_TRY(hipEventCreateWithFlags(&w.done, hipEventDisableTiming));
   }
   m->lanes = batches_in_flight;  // extra workspaces stay allocated until es_free
+  return ES_OK;
+}
+
+extern "C" es_status es_set_batch_grouping(es_model *m, int32_t batches_per_pass) {
+  if (!m) return fail(ES_ERR_ARG, "model handle is NULL");
+  if (batches_per_pass < 1 || batches_per_pass > 8)
+    return fail(ES_ERR_ARG, "batches_per_pass=%d outside [1, 8]", batches_per_pass);
+  HIP_TRY(hipDeviceSynchronize());
+  m->group = batches_per_pass;
+  for (int i = 0; i < m->lanes; ++i) {
+    es_model::Workspace &w = m->ws[i];
+    if (w.scale < m->group) {
+      es_status s = alloc_workspace(m, w, m->group);
+      if (s != ES_OK) return s;
+    }
+  }
   return ES_OK;
 }
 

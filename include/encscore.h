@@ -181,6 +181,20 @@ es_status es_forward_hidden(es_model *m, const int32_t *d_token_ids, const int32
 es_status es_set_concurrency(es_model *m, int32_t batches_in_flight);
 
 /*
+ * es_set_batch_grouping -- number of consecutive planned batches (1..8,
+ * default 1) that es_score_requests packs back to back and scores in one
+ * pass through the layers.  The planner's batches stay as planned
+ * (TurboTransformers review, Proposed method: the DP scheduler over sorted
+ * requests); grouping only makes each GEMM see the tokens of several of them
+ * at once, so the matrix cores get larger problems.  Every kernel works per
+ * token or per sequence, so rewards are bitwise the same for any grouping.
+ * The workspaces of the batches in flight grow to hold that many planned
+ * batches (allocated here, synchronously).  Combines with es_set_concurrency:
+ * groups are what is kept in flight.  Errors: ES_ERR_ARG, ES_ERR_HIP.
+ */
+es_status es_set_batch_grouping(es_model *m, int32_t batches_per_pass);
+
+/*
  * es_set_attention -- how the masked attention of each layer runs (bf16
  * models): 0 (default) = three kernels, scores to HBM, the Softmax row
  * reduction (TurboTransformers review, Proposed method), then P.V; 1 = one

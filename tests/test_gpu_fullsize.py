@@ -1,8 +1,8 @@
 """Parity at the workloads' full sizes, in the launch configuration bench.py times.
 
 Each test scores a workload's whole request stream through es_score_requests
-(DP planner at the workload's token budget and batch overhead, three planned
-batches in flight, the bench default), then
+(DP planner at the workload's token budget and batch overhead; four planned
+batches packed per pass and two passes in flight, the bench default), then
   * compares a seeded sample of requests, computed one by one by the float64
     oracle, within 1e-2 (bf16 operands, fp32 accumulation);
   * checks properties that hold at any size: every reward finite, the sampled
@@ -20,11 +20,13 @@ from synth.generate import split
 
 pytestmark = pytest.mark.gpu
 BF16_TOL = 1e-2
-IN_FLIGHT = 3
+IN_FLIGHT = 2
+GROUP = 4
 
 
-def _stream(torch, cfg, w, ids, lengths, offset=0.0, attention="unfused"):
+def _stream(torch, cfg, w, ids, lengths, offset=0.0, attention="fused"):
     sc = Scorer(blob.to_bytes(cfg, w, offset), cfg.max_tokens, min(cfg.max_tokens, 65536))
+    sc.set_grouping(GROUP)
     sc.set_concurrency(IN_FLIGHT)
     sc.set_attention(attention)
     d = torch.from_numpy(ids).cuda()
@@ -56,12 +58,13 @@ def _check_sample(torch, sc, cfg, w, ids, lengths, rew, idx, cache=True):
     assert worst <= BF16_TOL
 
 
-def test_bert_base_short_full_stream():
+@pytest.mark.parametrize("attention", ["unfused", "fused"])
+def test_bert_base_short_full_stream(attention):
     torch = need_gpu()
     cfg = get_config("bert_base_short")
     w = make_weights(cfg)
     ids, lengths, _ = make_requests(cfg)
-    sc, rew = _stream(torch, cfg, w, ids, lengths)
+    sc, rew = _stream(torch, cfg, w, ids, lengths, attention=attention)
     idx = np.random.default_rng(1).choice(lengths.size, 8, replace=False)
     idx = np.concatenate([idx, [int(np.argmax(lengths)), int(np.argmin(lengths))]])
     _check_sample(torch, sc, cfg, w, ids, lengths, rew, idx)

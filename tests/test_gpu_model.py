@@ -211,6 +211,48 @@ def test_batches_in_flight_match_serial(lanes):
     assert torch.equal(again, serial)
 
 
+@pytest.mark.parametrize("group,lanes", [(2, 1), (3, 1), (4, 2), (8, 1)])
+@pytest.mark.parametrize("attention", ["unfused", "fused"])
+def test_batch_grouping_matches_ungrouped(group, lanes, attention):
+    """Packing G planned batches into one pass changes nothing (bitwise), with
+    and without passes in flight, for both attention forms."""
+    torch = need_gpu()
+    cfg = CASES[3][1]
+    w = make_weights(cfg)
+    ids, lengths = random_stream(11, 70, 1, 200, cfg.vocab)
+    sc = scorer_for(cfg, w, 0.25, max_tokens=600, max_seqs=512)
+    sc.set_attention(attention)
+    d = torch.from_numpy(ids).cuda()
+    ref, st1 = sc.score_requests(d, lengths, batch_overhead=64)
+    ref = ref.clone()
+    say("grouping", group, "lanes", lanes, attention, st1["n_batches"], "planned batches")
+    assert st1["n_batches"] > group
+    sc.set_grouping(group)
+    sc.set_concurrency(lanes)
+    for _ in range(2):
+        got, st2 = sc.score_requests(d, lengths, batch_overhead=64)
+        torch.cuda.synchronize()
+        assert st2 == st1
+        assert torch.equal(got, ref)
+    sc.set_grouping(1)
+    sc.set_concurrency(1)
+    again, _ = sc.score_requests(d, lengths, batch_overhead=64)
+    assert torch.equal(again, ref)
+
+
+def test_grouping_and_concurrency_validation():
+    torch = need_gpu()
+    from encoder_scoring_amd import EncScoreError
+    cfg = CASES[0][1]
+    sc = scorer_for(cfg, make_weights(cfg), 0.0)
+    for bad in (0, 9, -1):
+        with pytest.raises(EncScoreError):
+            sc.set_grouping(bad)
+    for bad in (0, 5):
+        with pytest.raises(EncScoreError):
+            sc.set_concurrency(bad)
+
+
 @pytest.mark.parametrize("name,cfg", [(c[0], c[1]) for c in CASES if c[1].bf16],
                          ids=[c[0] for c in CASES if c[1].bf16])
 def test_fused_attention_matches_oracle_and_unfused(name, cfg):
