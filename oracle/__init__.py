@@ -18,6 +18,8 @@ Sources (the pages, by title and section):
     summaries average zero; best-of-N scores N candidates per prompt.
   * SambaNova, "Breakthrough efficiency in NLP model deployment": compact
     BERT (TinyBERT) for online inference.
+  * "Learning to summarize from human feedback" (summary), Method adaptation:
+    best-of-N selection over the reward model's scores (selection.py).
 
 Precision: float64 by default (``dtype`` argument; float32 is the plain fp32
 forward used as the CPU baseline).  GELU's erf is evaluated in float64 by
@@ -36,6 +38,7 @@ from .model import (  # noqa: F401
     linear,
     attention,
 )
+from .selection import best_of_n  # noqa: F401
 from .scheduler import (  # noqa: F401
     plan_batches,
     pack_offsets,

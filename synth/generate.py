@@ -168,3 +168,34 @@ def random_stream(seed: int, n: int, lo: int, hi: int, vocab: int):
     """Generic seeded stream: n sequences with lengths U{lo..hi}; (ids, lengths)."""
     rng = np.random.default_rng(seed)
     return _draw(rng, rng.integers(lo, hi + 1, size=n), vocab)
+
+
+def best_of_n_form(ids, lengths, group, prompt_len):
+    """Split a best-of-N request stream into its prompt / candidate form.
+
+    Every request is prompt + candidate, requests of one prompt are adjacent
+    and share their first ``prompt_len`` ids (the decoder workload's law).
+    Pure slicing.  Returns (prompt_ids, prompt_lengths, cand_ids, cand_lengths,
+    cand_counts), all int32; candidates keep request order.
+    """
+    ids = np.asarray(ids)
+    lengths = np.asarray(lengths)
+    group = np.asarray(group)
+    starts = np.concatenate([[0], np.cumsum(lengths)])
+    p_ids, p_len, c_ids, c_len, counts = [], [], [], [], []
+    i = 0
+    while i < lengths.size:
+        j = i
+        while j < lengths.size and group[j] == group[i]:
+            j += 1
+        p_ids.append(ids[starts[i]:starts[i] + prompt_len])
+        p_len.append(prompt_len)
+        for k in range(i, j):
+            assert np.array_equal(ids[starts[k]:starts[k] + prompt_len], p_ids[-1])
+            c_ids.append(ids[starts[k] + prompt_len:starts[k + 1]])
+            c_len.append(int(lengths[k]) - prompt_len)
+        counts.append(j - i)
+        i = j
+    as32 = lambda a: np.asarray(a, dtype=np.int32)
+    return (as32(np.concatenate(p_ids)), as32(p_len), as32(np.concatenate(c_ids)), as32(c_len),
+            as32(counts))

@@ -92,3 +92,26 @@ def test_phi_table_pin_detects_tanh_gelu():
     assert worst > 1e-5
     worst_exact = max(abs(float(om.gelu(np.array(x))) - x * phi) for x, phi in _phi_table())
     assert worst_exact < 1e-10
+
+
+def test_selection_pins_detect_ties_to_the_last_index(monkeypatch):
+    """A best-of-N that lets an equal later reward win (>= instead of >) must
+    fail the hand-worked tie cases."""
+    import json
+    import os
+    import oracle.selection as sel
+
+    def last_wins(rewards, counts):
+        out, start = [], 0
+        for c in counts:
+            k = 0
+            for j in range(1, c):
+                if rewards[start + j] >= rewards[start + k]:
+                    k = j
+            out.append(k)
+            start += c
+        return out
+
+    golden = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_examples.json")))
+    monkeypatch.setattr(sel, "best_of_n", last_wins)
+    assert any(sel.best_of_n(c["rewards"], c["counts"]) != c["best"] for c in golden["best_of_n"])
