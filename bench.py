@@ -6,7 +6,9 @@ stream: DP batch planning, packing, embedding, every layer (QKV GEMM, masked
 attention -- fused by default, or scores + row softmax + P.V --, output GEMM +
 residual, LayerNorm, FFN GEMMs with fused GELU / residual, LayerNorm), the
 last-token reward head and the scatter of rewards back to request order -- a
-single es_score_requests call on token ids already resident in HBM.  The
+single es_score_requests call on token ids already resident in HBM (with
+--best-of-n on the decoder workload: one es_score_best_of_n call, each
+prompt run once for its candidates, plus the per-prompt selection).  The
 other attention form is timed on the same stream and reported under
 "variants".
 
@@ -117,6 +119,9 @@ def main():
                     help="attention as scores + softmax row reduction + P.V, or one fused kernel")
     ap.add_argument("--in-flight", type=int, default=2,
                     help="passes overlapped on internal streams (es_set_concurrency)")
+    ap.add_argument("--best-of-n", action="store_true",
+                    help="decoder_rm only: score through es_score_best_of_n (each prompt run once "
+                         "for its candidates) instead of prompt + candidate sequences")
     ap.add_argument("--group", type=int, default=4,
                     help="planned batches packed into one pass through the layers "
                          "(es_set_batch_grouping)")
@@ -138,10 +143,13 @@ def main():
     c = cfg.batch_overhead if args.batch_overhead is None else args.batch_overhead
     t = time.perf_counter()
     weights = make_weights(cfg)
+    group = None
     if cfg.name == "tinybert":
         ids, lengths = make_fixed_batch(cfg, 128, 64)
     else:
-        ids, lengths, _ = make_requests(cfg)
+        ids, lengths, group = make_requests(cfg)
+    if args.best_of_n and cfg.name != "decoder_rm":
+        sys.exit("--best-of-n applies to the decoder_rm workload (prompts shared by 16 candidates)")
     n, n_tokens = int(lengths.size), int(lengths.sum())
     log(f"{cfg.name}: {n} requests, {n_tokens} tokens; weights drawn in {time.perf_counter() - t:.1f} s")
     sc = Scorer(blob.to_bytes(cfg, weights, 0.0), cfg.max_tokens, max(1, min(cfg.max_tokens, 65536)))
@@ -156,21 +164,36 @@ def main():
         sc.set_attention(args.attention)
     d_ids = torch.from_numpy(ids).cuda()
     out = torch.empty(n, dtype=torch.float32, device="cuda")
+    stats = None
+    if args.best_of_n:
+        # same requests in prompt / candidate form: prompts once, then candidates
+        from synth.generate import best_of_n_form
+        p_ids, pl, c_ids, cl, cn = best_of_n_form(ids, lengths, group, 512)
+        d_bon = torch.from_numpy(np.concatenate([p_ids, c_ids])).cuda()
+        best = torch.empty(pl.size, dtype=torch.int32, device="cuda")
+
+        def step():
+            nonlocal stats
+            _, _, stats = sc.score_best_of_n(d_bon, pl, cl, cn, c, out, best)
+    else:
+        def step():
+            nonlocal stats
+            _, stats = sc.score_requests(d_ids, lengths, c, out)
 
     if args.single_step:
         for _ in range(2):
-            sc.score_requests(d_ids, lengths, c, out)
+            step()
         torch.cuda.synchronize()
         print(json.dumps({"single_step": cfg.name, "finite": bool(torch.isfinite(out).all().item())}))
         return
     # warm-up (also sizes the metadata buffers), then the timed region: K steps
     # of the production configuration with no profiling events
     for _ in range(max(1, args.warmup)):
-        _, stats = sc.score_requests(d_ids, lengths, c, out)
+        step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        sc.score_requests(d_ids, lengths, c, out)
+        step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / args.steps
@@ -181,7 +204,7 @@ def main():
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for _ in range(steps):
-            sc.score_requests(d_ids, lengths, c, out)
+            step()
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) * 1e3 / steps
 
@@ -191,7 +214,7 @@ def main():
 
     def profile_pass():
         sc.set_concurrency(1)
-        sc.score_requests(d_ids, lengths, c, out)
+        step()
         sc.profile_enable(None)
         ms_iso = timed(prof_steps)
         pc = sc.profile_collect()
@@ -241,10 +264,10 @@ def main():
     # the other attention form, same stream and settings: its own timed steps
     # and kernel table (the row-softmax kernel runs only in the unfused form)
     variants = {}
-    if cfg.bf16:
+    if cfg.bf16 and not args.best_of_n:  # shared prompts always use the fused attention
         other = "unfused" if args.attention == "fused" else "fused"
         sc.set_attention(other)
-        sc.score_requests(d_ids, lengths, c, out)
+        step()
         ms_other = timed(args.steps)
         assert torch.isfinite(out).all().item(), "non-finite rewards"
         pc_other, _ = profile_pass()
@@ -271,7 +294,9 @@ def main():
                    "padded_tokens": stats["padded_tokens"], "max_tokens": cfg.max_tokens,
                    "batch_overhead": c, "batches_per_pass": args.group,
                    "passes_in_flight": args.in_flight,
-                   "attention": args.attention if cfg.bf16 else "unfused"},
+                   "attention": ("fused" if args.best_of_n else args.attention) if cfg.bf16 else "unfused",
+                   "shared_prompts": bool(args.best_of_n),
+                   "computed_tokens": stats["packed_tokens"]},
         "tokens_per_s": round(n_tokens / (ms / 1e3), 1),
         "roofline": {"bound": bound, "kernel": dominant, "achieved": round(achieved, 2),
                      "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),

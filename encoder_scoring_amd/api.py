@@ -131,6 +131,26 @@ class Scorer:
         return out, {"n_batches": stats.n_batches, "total_cost": stats.total_cost,
                      "padded_tokens": stats.padded_tokens, "packed_tokens": stats.packed_tokens}
 
+    def score_best_of_n(self, d_ids, prompt_lengths, cand_lengths, cand_counts,
+                        batch_overhead=1024, rewards=None, best=None):
+        """Best-of-N with shared prompts: d_ids holds the prompts back to back,
+        then the candidates; returns (rewards per candidate, best index per
+        prompt, stats)."""
+        torch = _torch()
+        pl, cl, cc = as_i32(prompt_lengths), as_i32(cand_lengths), as_i32(cand_counts)
+        if rewards is None:
+            rewards = torch.empty(cl.size, dtype=torch.float32, device=d_ids.device)
+        if best is None:
+            best = torch.empty(pl.size, dtype=torch.int32, device=d_ids.device)
+        stats = _lib.StreamStats()
+        check(self.lib, self.lib.es_score_best_of_n(
+            self.handle, _dptr(d_ids, torch.int32, "ids"), i32p(pl), pl.size, i32p(cl), i32p(cc),
+            int(batch_overhead), _dptr(rewards, torch.float32, "rewards"),
+            _dptr(best, torch.int32, "best"), _stream(), ctypes.byref(stats)))
+        return rewards, best, {"n_batches": stats.n_batches, "total_cost": stats.total_cost,
+                               "padded_tokens": stats.padded_tokens,
+                               "packed_tokens": stats.packed_tokens}
+
     def hidden(self, d_ids, offsets, n_layers=None):
         """fp32 residual stream [tokens, hidden] after ``n_layers`` layers (diagnostic)."""
         torch = _torch()

@@ -187,9 +187,12 @@ __global__ __launch_bounds__(64) void scores_mfma_kernel(const uint16_t *__restr
 // so the MFMA fragments below read keys contiguously.  Keys >= n become 0.
 constexpr int kVP = 40;  // LDS pitch of a transposed row (32 keys + 8, keeps 16-byte reads aligned)
 
+// Keys at positions [0, np) come from rows Vp[0 .. np) (a shared prompt) and
+// keys at positions >= np from Vs[key - np]; np = 0 for a plain sequence.
 template <int DP>
-__device__ __forceinline__ void stage_vt(uint16_t *__restrict__ sV, const uint16_t *__restrict__ V,
-                                         int ldq, int k0, int n, int lane) {
+__device__ __forceinline__ void stage_vt(uint16_t *__restrict__ sV, const uint16_t *__restrict__ Vp,
+                                         const uint16_t *__restrict__ Vs, int np, int ldq, int k0,
+                                         int n, int lane) {
   constexpr int OCT = DP / 8;
 #pragma unroll
   for (int u = lane; u < 8 * OCT; u += 64) {
@@ -198,8 +201,8 @@ __device__ __forceinline__ void stage_vt(uint16_t *__restrict__ sV, const uint16
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int key = k0 + 4 * quad + j;
-      r[j] = key < n ? *reinterpret_cast<const uint4 *>(V + (int64_t)key * ldq + oct * 8)
-                     : make_uint4(0, 0, 0, 0);
+      const uint16_t *row = key < np ? Vp + (int64_t)key * ldq : Vs + (int64_t)(key - np) * ldq;
+      r[j] = key < n ? *reinterpret_cast<const uint4 *>(row + oct * 8) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
@@ -245,7 +248,7 @@ __global__ __launch_bounds__(64) void pv_mfma_kernel(const uint16_t *__restrict_
   const int kend = causal ? min(n, q0 + kQTile) : n;
   for (int k0 = 0; k0 < kend; k0 += 32) {
     __syncthreads();
-    stage_vt<DP>(sV, V, ldq, k0, n, lane);
+    stage_vt<DP>(sV, V, V, 0, ldq, k0, n, lane);
     __syncthreads();
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
@@ -293,11 +296,13 @@ __global__ __launch_bounds__(64) void pv_mfma_kernel(const uint16_t *__restrict_
 // and reading the transposed V tile in the same order (two 8-byte LDS reads).
 // The contraction is order-free, so the result equals softmax(S) V up to
 // rounding.
-template <int DP>
+template <int DP, bool PFX>
 __global__ __launch_bounds__(64) void attn_fused_kernel(const uint16_t *__restrict__ qkv, int ldq,
                                                         int n_heads, float scale, int causal,
                                                         const int32_t *__restrict__ off,
                                                         const int32_t *__restrict__ items,
+                                                        const int32_t *__restrict__ pref,
+                                                        const int32_t *__restrict__ plen,
                                                         uint16_t *__restrict__ ctx, int ldc) {
   constexpr int KS = DP / 16, NT = DP / 32;
   __shared__ __attribute__((aligned(16))) uint16_t sV[DP * kVP];
@@ -305,6 +310,14 @@ __global__ __launch_bounds__(64) void attn_fused_kernel(const uint16_t *__restri
   const int seq = items[2 * item], q0 = items[2 * item + 1];
   const int64_t t0 = off[seq];
   const int n = off[seq + 1] - (int)t0;
+  // With a shared prompt of np tokens at rows p0.., key position j < np is
+  // row p0 + j and position j >= np is the sequence's own row t0 + j - np;
+  // query q (own token q) sits at position np + q.  Key tiles stay aligned to
+  // position 0, so every query sees the same tiles, in the same order, as in
+  // the prompt + continuation laid out as one sequence.
+  const int np = PFX ? plen[seq] : 0;
+  const int64_t p0 = PFX ? pref[seq] : 0;
+  const int ntot = np + n;
   const int fr = lane & 31, fh = lane >> 5;
   const int q = q0 + fr;
   bf16x8 qf[KS];
@@ -312,32 +325,38 @@ __global__ __launch_bounds__(64) void attn_fused_kernel(const uint16_t *__restri
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk) qf[kk] = q < n ? ld_frag(Qr + kk * 16) : zero_frag();
   const uint16_t *Kb = qkv + t0 * ldq + (n_heads + h) * DP + fh * 8;
+  const uint16_t *Kp = qkv + p0 * ldq + (n_heads + h) * DP + fh * 8;
   const uint16_t *V = qkv + t0 * ldq + (2 * n_heads + h) * DP;
+  const uint16_t *Vp = qkv + p0 * ldq + (2 * n_heads + h) * DP;
   f32x16 acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
-  const int kend = causal ? min(n, q0 + kQTile) : n;
+  const int qpos = np + q;
+  const int kend = causal ? min(ntot, np + q0 + kQTile) : ntot;
   for (int k0 = 0; k0 < kend; k0 += 32) {
     __syncthreads();
-    stage_vt<DP>(sV, V, ldq, k0, n, lane);
+    stage_vt<DP>(sV, Vp, V, np, ldq, k0, ntot, lane);
     const int k = k0 + fr;
+    const uint16_t *Kr = PFX && k < np ? Kp + (int64_t)k * ldq : Kb + (int64_t)(k - np) * ldq;
     f32x16 s;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-      const bf16x8 kf = k < n ? ld_frag(Kb + (int64_t)k * ldq + kk * 16) : zero_frag();
+      const bf16x8 kf = k < ntot ? ld_frag(Kr + kk * 16) : zero_frag();
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s, 0, 0, 0);
     }
-    // every query sees at least key k0 in this tile, so the tile max is finite
+    // the first tile shows every query key 0, so m_run is finite after it; a
+    // later tile whose keys are all masked for a query leaves that query's
+    // running max, sum and accumulator exactly unchanged (alpha = 1, p = 0)
     float mx = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = k0 + 8 * (r >> 2) + 4 * fh + (r & 3);
-      const bool ok = key < n && (!causal || key <= q);
+      const bool ok = key < ntot && (!causal || key <= qpos);
       s[r] = ok ? s[r] * scale : -INFINITY;
       mx = fmaxf(mx, s[r]);
     }
@@ -401,6 +420,7 @@ hipError_t dispatch_dp(int dp, F &&f) {
 
 hipError_t launch_scores(bool act_bf16, const void *qkv, int ldq, int n_heads, int dp, float scale,
                          bool causal, const Ragged &r, float *S, hipStream_t st) {
+  if (r.plen) return hipErrorInvalidValue;  // shared prompts: fused attention only
   if (r.n_items <= 0) return hipSuccess;
   const dim3 grid(r.n_items, n_heads), block(256);
   return dispatch_dp(dp, [&](auto dpc) {
@@ -417,6 +437,7 @@ hipError_t launch_scores(bool act_bf16, const void *qkv, int ldq, int n_heads, i
 
 hipError_t launch_pv(bool act_bf16, const void *P, const void *qkv, int ldq, int n_heads, int dp,
                      bool causal, const Ragged &r, void *ctx, int ldc, hipStream_t st) {
+  if (r.plen) return hipErrorInvalidValue;  // shared prompts: fused attention only
   if (r.n_items <= 0) return hipSuccess;
   const dim3 grid(r.n_items, n_heads), block(256);
   return dispatch_dp(dp, [&](auto dpc) {
@@ -436,11 +457,16 @@ hipError_t launch_pv(bool act_bf16, const void *P, const void *qkv, int ldq, int
 hipError_t launch_attn_fused(const uint16_t *qkv, int ldq, int n_heads, int dp, float scale,
                              bool causal, const Ragged &r, uint16_t *ctx, int ldc, hipStream_t st) {
   if (r.n_items <= 0) return hipSuccess;
+  if ((r.plen != nullptr) != (r.pref != nullptr)) return hipErrorInvalidValue;
   const dim3 grid(r.n_items, n_heads);
   return dispatch_dp(dp, [&](auto dpc) {
     constexpr int DP = decltype(dpc)::value;
-    attn_fused_kernel<DP><<<grid, dim3(64), 0, st>>>(qkv, ldq, n_heads, scale, causal ? 1 : 0,
-                                                     r.off, r.items, ctx, ldc);
+    if (r.plen)
+      attn_fused_kernel<DP, true><<<grid, dim3(64), 0, st>>>(qkv, ldq, n_heads, scale, causal ? 1 : 0,
+                                                             r.off, r.items, r.pref, r.plen, ctx, ldc);
+    else
+      attn_fused_kernel<DP, false><<<grid, dim3(64), 0, st>>>(qkv, ldq, n_heads, scale, causal ? 1 : 0,
+                                                              r.off, r.items, nullptr, nullptr, ctx, ldc);
     return hipGetLastError();
   });
 }

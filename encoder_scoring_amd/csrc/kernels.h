@@ -16,7 +16,11 @@ struct Ragged {
   const int32_t *items;  // [2 * n_items] (sequence, first query row), kQTile rows each
   const int32_t *sm_items = nullptr;  // [2 * n_sm_items] (sequence, first row) softmax work
   const int32_t *src = nullptr;   // [n_seqs] first id of sequence i in the id buffer (NULL: off)
-  const int32_t *dest = nullptr;  // [n_seqs] reward slot of sequence i (NULL: i)
+  const int32_t *dest = nullptr;  // [n_seqs] reward slot of sequence i (NULL: i; < 0: none)
+  // Shared prompts (causal models, fused attention only): sequence i continues
+  // the plen[i] tokens at packed rows pref[i].. -- its positions start at
+  // plen[i] and its queries also see those rows' keys and values.  NULL: none.
+  const int32_t *pref = nullptr, *plen = nullptr;
   int32_t n_seqs = 0, n_items = 0, max_len = 0, n_tokens = 0, n_sm_items = 0;
 };
 
@@ -52,6 +56,10 @@ hipError_t launch_layernorm(bool act_bf16, const float *x, const float *g, const
 // Ragged softmax over score blocks: S fp32 -> P (bf16 bits or fp32).
 hipError_t launch_softmax(bool p_bf16, const float *S, void *P, const Ragged &r, int n_heads,
                           bool causal, hipStream_t st);
+// Best-of-N selection: best[p] = index (within prompt p's candidates
+// cstart[p] .. cstart[p+1]-1) of the largest reward, the lowest among equals.
+hipError_t launch_best_of_n(const float *rewards, const int32_t *cstart, int n_prompts,
+                            int32_t *best, hipStream_t st);
 // Reward head on the last token of each sequence (pre_ln: final LN first).
 hipError_t launch_head(bool pre_ln, const float *x, int H, const Ragged &r, const float *g,
                        const float *b, float eps, const float *w, const float *hb, float offset,

@@ -290,8 +290,8 @@ es_status build(const es::ParsedBlob &pb, int64_t max_tokens, int32_t max_seqs, 
 // bases, attention work items and (optionally) id-source / reward-slot maps,
 // assembled on the host, staged in pinned memory and uploaded in ONE copy.
 struct BatchLayout {
-  size_t off = 0, sbase = 0, items = 0, sm_items = 0, src = 0, dest = 0;
-  bool has_src = false, has_dest = false;
+  size_t off = 0, sbase = 0, items = 0, sm_items = 0, src = 0, dest = 0, pref = 0, plen = 0;
+  bool has_src = false, has_dest = false, has_prefix = false;
   int n = 0, n_items = 0, n_sm_items = 0, max_len = 0, n_tokens = 0;
   int64_t pairs = 0;  // visible (query, key) pairs summed over heads
 };
@@ -304,8 +304,13 @@ size_t push_bytes(std::vector<uint8_t> &buf, const void *p, size_t bytes) {
 }
 
 // Validate one batch's host offsets and append its metadata to m->meta_asm.
+// pref/plen (optional, both or neither): sequence i continues the plen[i]
+// tokens at packed rows pref[i].. (a shared prompt); then score capacity is
+// not checked (only the fused attention, which keeps no score buffer, takes
+// such layouts) and lengths are checked with the prompt included.
 es_status add_batch(es_model *m, const int32_t *h_off, int32_t n, const int32_t *src,
-                    const int32_t *dest, BatchLayout *L, int scale = 1) {
+                    const int32_t *dest, BatchLayout *L, int scale = 1,
+                    const int32_t *pref = nullptr, const int32_t *plen = nullptr) {
   if (!h_off) return fail(ES_ERR_ARG, "offsets pointer is NULL");
   if (n < 1) return fail(ES_ERR_ARG, "n_seqs=%d < 1", n);
   if (n > (int64_t)scale * m->max_seqs)
@@ -316,26 +321,27 @@ es_status add_batch(es_model *m, const int32_t *h_off, int32_t n, const int32_t 
   std::vector<int64_t> sbase((size_t)n);
   for (int32_t i = 0; i < n; ++i) {
     const int64_t len = (int64_t)h_off[i + 1] - h_off[i];
+    const int64_t np = plen ? plen[i] : 0;
     if (len < 1) return fail(ES_ERR_ARG, "offsets not strictly increasing at %d", i);
-    if (len > m->P)
-      return fail(ES_ERR_RANGE, "sequence %d has length %" PRId64 " > max_pos=%d", i, len, m->P);
+    if (np + len > m->P)
+      return fail(ES_ERR_RANGE, "sequence %d has length %" PRId64 " > max_pos=%d", i, np + len, m->P);
     if (h_off[i + 1] > scale * m->max_tokens)
       return fail(ES_ERR_CAPACITY, "batch has more than max_tokens=%" PRId64 " tokens", m->max_tokens);
     max_len = std::max<int>(max_len, (int)len);
-    L->pairs += (int64_t)m->A * (m->causal ? len * (len + 1) / 2 : len * len);
+    // visible (query, key) pairs over the sequence's own queries
+    L->pairs += (int64_t)m->A * (m->causal ? len * np + len * (len + 1) / 2 : len * len);
     sbase[i] = score;
     score += (int64_t)m->A * len * es::score_ld((int)len);
   }
-  if (score > scale * m->score_cap)
+  if (!plen && score > scale * m->score_cap)
     return fail(ES_ERR_CAPACITY, "batch needs %" PRId64 " score elements (capacity %" PRId64 ")",
                 score, m->score_cap);
   // attention work items, longest sequences first
   auto &ord = m->order_scratch;
   ord.resize(n);
   for (int32_t i = 0; i < n; ++i) ord[i] = i;
-  std::stable_sort(ord.begin(), ord.end(), [&](int32_t a, int32_t b) {
-    return h_off[a + 1] - h_off[a] > h_off[b + 1] - h_off[b];
-  });
+  auto keys_of = [&](int32_t i) { return h_off[i + 1] - h_off[i] + (plen ? plen[i] : 0); };
+  std::stable_sort(ord.begin(), ord.end(), [&](int32_t a, int32_t b) { return keys_of(a) > keys_of(b); });
   std::vector<int32_t> items, sm_items;
   for (int32_t sq : ord) {
     const int len = h_off[sq + 1] - h_off[sq];
@@ -359,6 +365,11 @@ es_status add_batch(es_model *m, const int32_t *h_off, int32_t n, const int32_t 
   L->has_dest = dest != nullptr;
   if (src) L->src = push_bytes(buf, src, sizeof(int32_t) * n);
   if (dest) L->dest = push_bytes(buf, dest, sizeof(int32_t) * n);
+  L->has_prefix = plen != nullptr;
+  if (plen) {
+    L->pref = push_bytes(buf, pref, sizeof(int32_t) * n);
+    L->plen = push_bytes(buf, plen, sizeof(int32_t) * n);
+  }
   L->n = n;
   L->n_items = (int)(items.size() / 2);
   L->max_len = max_len;
@@ -405,6 +416,8 @@ es::Ragged ragged_of(const es_model *m, const BatchLayout &L) {
   r.n_sm_items = L.n_sm_items;
   r.src = L.has_src ? reinterpret_cast<const int32_t *>(m->meta_dev + L.src) : nullptr;
   r.dest = L.has_dest ? reinterpret_cast<const int32_t *>(m->meta_dev + L.dest) : nullptr;
+  r.pref = L.has_prefix ? reinterpret_cast<const int32_t *>(m->meta_dev + L.pref) : nullptr;
+  r.plen = L.has_prefix ? reinterpret_cast<const int32_t *>(m->meta_dev + L.plen) : nullptr;
   r.n_seqs = L.n;
   r.n_items = L.n_items;
   r.max_len = L.max_len;
@@ -474,7 +487,7 @@ using Workspace = es_model::Workspace;
 es_status attention(es_model *m, Workspace &w, const es::Ragged &r, int64_t pairs, hipStream_t st) {
   const float scale = 1.0f / std::sqrt((float)m->d);
   const double a = m->bf16 ? 2.0 : 4.0, T = r.n_tokens, Hd = (double)m->H;
-  if (m->bf16 && m->attn_mode == 1) {
+  if (m->bf16 && (m->attn_mode == 1 || r.plen)) {  // shared prompts: fused only
     Prof p(m, st, ES_KC_ATTN_FUSED);
     HIP_TRY(es::launch_attn_fused((const uint16_t *)w.qkv, m->Nqkv, m->A, m->dp, scale, m->causal, r,
                                   (uint16_t *)w.ctx, m->Kc, st));
@@ -724,6 +737,134 @@ extern "C" es_status es_score_requests(es_model *m, const int32_t *d_token_ids,
     stats->total_cost = cost;
     stats->padded_tokens = padded;
     stats->packed_tokens = acc;
+  }
+  es::clear_error();
+  return ES_OK;
+}
+
+extern "C" es_status es_score_best_of_n(es_model *m, const int32_t *d_token_ids,
+                                        const int32_t *h_prompt_lengths, int32_t n_prompts,
+                                        const int32_t *h_cand_lengths, const int32_t *h_cand_counts,
+                                        int64_t batch_overhead, float *d_rewards, int32_t *d_best,
+                                        void *stream, es_stream_stats_t *stats) {
+  es_status s = check_model(m);
+  if (s != ES_OK) return s;
+  if (!d_token_ids || !d_rewards || !d_best || !h_prompt_lengths || !h_cand_lengths || !h_cand_counts)
+    return fail(ES_ERR_ARG, "NULL argument");
+  if (!m->causal || !m->bf16)
+    return fail(ES_ERR_ARG, "shared-prompt scoring needs a causal bf16 model (a bidirectional "
+                            "prompt's states depend on its continuation)");
+  if (n_prompts < 1) return fail(ES_ERR_ARG, "n_prompts=%d < 1", n_prompts);
+  // per prompt: first candidate, token totals, group size (prompt + its candidates)
+  std::vector<int32_t> cstart((size_t)n_prompts + 1, 0), group((size_t)n_prompts);
+  std::vector<int64_t> pfirst((size_t)n_prompts), cfirst;
+  int64_t ptok = 0;
+  for (int32_t p = 0; p < n_prompts; ++p) {
+    if (h_cand_counts[p] < 1) return fail(ES_ERR_ARG, "prompt %d has %d candidates", p, h_cand_counts[p]);
+    if (h_prompt_lengths[p] < 1) return fail(ES_ERR_RANGE, "prompt %d has length %d", p, h_prompt_lengths[p]);
+    cstart[p + 1] = cstart[p] + h_cand_counts[p];
+    pfirst[p] = ptok;
+    ptok += h_prompt_lengths[p];
+  }
+  const int32_t n_cand = cstart[n_prompts];
+  cfirst.resize((size_t)n_cand);
+  int64_t ctok = 0;
+  for (int32_t p = 0; p < n_prompts; ++p) {
+    int64_t g = h_prompt_lengths[p];
+    for (int32_t c = cstart[p]; c < cstart[p + 1]; ++c) {
+      const int32_t len = h_cand_lengths[c];
+      if (len < 1 || (int64_t)h_prompt_lengths[p] + len > m->P)
+        return fail(ES_ERR_RANGE, "candidate %d: prompt %d + %d tokens outside [2, max_pos=%d]", c,
+                    h_prompt_lengths[p], len, m->P);
+      cfirst[c] = ptok + ctok;
+      ctok += len;
+      g += len;
+    }
+    if (g > m->max_tokens)
+      return fail(ES_ERR_CAPACITY, "prompt %d with its candidates has %" PRId64 " tokens > max_tokens=%" PRId64,
+                  p, g, m->max_tokens);
+    if (1 + h_cand_counts[p] > m->max_seqs)
+      return fail(ES_ERR_CAPACITY, "prompt %d has %d candidates (max_seqs=%d)", p, h_cand_counts[p], m->max_seqs);
+    group[p] = (int32_t)g;
+  }
+  if (ptok + ctok > INT32_MAX) return fail(ES_ERR_RANGE, "more than INT32_MAX tokens in one call");
+  // a1: the planner over prompt groups, each an item as long as its tokens
+  std::vector<int32_t> order((size_t)n_prompts), starts((size_t)n_prompts + 1);
+  int32_t nb = 0;
+  int64_t cost = 0;
+  if ((s = es_plan_batches(group.data(), n_prompts, m->max_tokens, batch_overhead, order.data(),
+                           starts.data(), &nb, &cost)) != ES_OK)
+    return s;
+  // a2: per pass (G planned batches), every group as its prompt followed by
+  // its candidates; a candidate continues its prompt's rows
+  const int G = m->group;
+  const int32_t ng = (nb + G - 1) / G;
+  m->meta_asm.clear();
+  std::vector<BatchLayout> layouts((size_t)ng);
+  std::vector<int32_t> off, src, dest, pref, plen;
+  int64_t padded = 0;
+  for (int32_t gi = 0; gi < ng; ++gi) {
+    const int32_t b0 = gi * G, b1 = std::min<int32_t>(nb, b0 + G);
+    off.assign(1, 0);
+    src.clear();
+    dest.clear();
+    pref.clear();
+    plen.clear();
+    for (int32_t b = b0; b < b1; ++b) {
+      int32_t gmax = 0;
+      for (int32_t k = starts[b]; k < starts[b + 1]; ++k) {
+        const int32_t p = order[k];
+        gmax = std::max(gmax, group[p]);
+        const int32_t prow = off.back();
+        off.push_back(prow + h_prompt_lengths[p]);
+        src.push_back((int32_t)pfirst[p]);
+        dest.push_back(-1);
+        pref.push_back(0);
+        plen.push_back(0);
+        for (int32_t c = cstart[p]; c < cstart[p + 1]; ++c) {
+          off.push_back(off.back() + h_cand_lengths[c]);
+          src.push_back((int32_t)cfirst[c]);
+          dest.push_back(c);
+          pref.push_back(prow);
+          plen.push_back(h_prompt_lengths[p]);
+        }
+      }
+      padded += (int64_t)(starts[b + 1] - starts[b]) * gmax;
+    }
+    if ((s = add_batch(m, off.data(), (int32_t)dest.size(), src.data(), dest.data(), &layouts[gi],
+                       b1 - b0, pref.data(), plen.data())) != ES_OK)
+      return s;
+  }
+  const size_t cs_at = push_bytes(m->meta_asm, cstart.data(), sizeof(int32_t) * cstart.size());
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if ((s = upload_meta(m, st)) != ES_OK) return s;
+  // a3..a13 per pass, passes in flight as in es_score_requests
+  const int k = m->lanes;
+  if (k > 1) {
+    HIP_TRY(hipEventRecord(m->fork_ev, st));
+    for (int i = 0; i < k; ++i) HIP_TRY(hipStreamWaitEvent(m->ws[i].stream, m->fork_ev, 0));
+  }
+  for (int32_t gi = 0; gi < ng; ++gi) {
+    Workspace &w = m->ws[gi % k];
+    hipStream_t ls = k > 1 ? w.stream : st;
+    const es::Ragged r = ragged_of(m, layouts[gi]);
+    if ((s = forward(m, w, d_token_ids, r, layouts[gi].pairs, m->L, ls)) != ES_OK) return s;
+    if ((s = head(m, w, r, m->offset, d_rewards, ls)) != ES_OK) return s;
+  }
+  if (k > 1) {
+    for (int i = 0; i < k; ++i) {
+      HIP_TRY(hipEventRecord(m->ws[i].done, m->ws[i].stream));
+      HIP_TRY(hipStreamWaitEvent(st, m->ws[i].done, 0));
+    }
+  }
+  // selection: per prompt the best candidate, lowest index among equals
+  HIP_TRY(es::launch_best_of_n(d_rewards, reinterpret_cast<const int32_t *>(m->meta_dev + cs_at),
+                               n_prompts, d_best, st));
+  if (stats) {
+    stats->n_batches = nb;
+    stats->total_cost = cost;
+    stats->padded_tokens = padded;
+    stats->packed_tokens = ptok + ctok;
   }
   es::clear_error();
   return ES_OK;

@@ -104,7 +104,8 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float *x, const fl
 template <int NC, typename W, bool LN, typename OutB>
 __global__ __launch_bounds__(256) void embed_kernel(const int32_t *__restrict__ ids,
                                                     const int32_t *__restrict__ off,
-                                                    const int32_t *__restrict__ src, int n_seqs,
+                                                    const int32_t *__restrict__ src,
+                                                    const int32_t *__restrict__ plen, int n_seqs,
                                                     int T, const W *__restrict__ tok,
                                                     const W *__restrict__ pos, int vocab, int H,
                                                     const float *__restrict__ g,
@@ -115,8 +116,9 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t *__restrict__ 
   const int t = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
   if (t >= T) return;
   const int s = seq_of_token(off, n_seqs, t);
-  const int p = t - off[s];  // positions restart at 0 in every sequence
-  int id = ids[(src ? src[s] : off[s]) + p];
+  const int j = t - off[s];                  // index within the sequence's own tokens
+  const int p = j + (plen ? plen[s] : 0);    // position: restarts at 0, after a shared prompt
+  int id = ids[(src ? src[s] : off[s]) + j];
   if (id < 0 || id >= vocab) {
     if (lane == 0) atomicOr(flag, 1);
     id = 0;
@@ -233,6 +235,8 @@ __global__ __launch_bounds__(256) void head_kernel(const float *__restrict__ x, 
   const int lane = threadIdx.x & (kWave - 1);
   const int i = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
   if (i >= n_seqs) return;
+  const int slot = dest ? dest[i] : i;
+  if (slot < 0) return;  // a shared prompt: its continuations carry the rewards
   const int64_t t = off[i + 1] - 1;  // reward read at the end of the sequence
   const int c4n = H >> 2;
   float4 v[NC];
@@ -252,7 +256,28 @@ __global__ __launch_bounds__(256) void head_kernel(const float *__restrict__ x, 
     }
   }
   d = wave_sum(d);
-  if (lane == 0) rewards[dest ? dest[i] : i] = (d + hb[0]) + offset;
+  if (lane == 0) rewards[slot] = (d + hb[0]) + offset;
+}
+
+// Best-of-N selection, one thread per prompt ("Learning to summarize from
+// human feedback", Method adaptation: keep the candidate the reward model
+// scores highest); a strict comparison keeps the lowest index among equals.
+__global__ __launch_bounds__(256) void best_of_n_kernel(const float *__restrict__ rewards,
+                                                        const int32_t *__restrict__ cstart,
+                                                        int n_prompts, int32_t *__restrict__ best) {
+  const int p = blockIdx.x * blockDim.x + threadIdx.x;
+  if (p >= n_prompts) return;
+  const int c0 = cstart[p], c1 = cstart[p + 1];
+  int k = 0;
+  float v = rewards[c0];
+  for (int c = c0 + 1; c < c1; ++c) {
+    const float r = rewards[c];
+    if (r > v) {
+      v = r;
+      k = c - c0;
+    }
+  }
+  best[p] = k;
 }
 
 // Smallest register-chunk count NC (float4 per lane) covering `cols`.
@@ -298,12 +323,12 @@ hipError_t launch_embed(bool w_bf16, bool act_bf16, bool ln, const int32_t *ids,
     if (w_bf16 != act_bf16) return hipErrorInvalidValue;
     if (w_bf16) {
       auto k = ln ? embed_kernel<NC, uint16_t, true, uint16_t> : embed_kernel<NC, uint16_t, false, uint16_t>;
-      k<<<grid, block, 0, st>>>(ids, r.off, r.src, r.n_seqs, r.n_tokens, (const uint16_t *)tok,
+      k<<<grid, block, 0, st>>>(ids, r.off, r.src, r.plen, r.n_seqs, r.n_tokens, (const uint16_t *)tok,
                                 (const uint16_t *)pos, vocab, H, g, b, eps, x, (uint16_t *)xb, ldb,
                                 flag);
     } else {
       auto k = ln ? embed_kernel<NC, float, true, float> : embed_kernel<NC, float, false, float>;
-      k<<<grid, block, 0, st>>>(ids, r.off, r.src, r.n_seqs, r.n_tokens, (const float *)tok,
+      k<<<grid, block, 0, st>>>(ids, r.off, r.src, r.plen, r.n_seqs, r.n_tokens, (const float *)tok,
                                 (const float *)pos, vocab, H, g, b, eps, x, (float *)xb, ldb, flag);
     }
     return hipGetLastError();
@@ -349,6 +374,13 @@ hipError_t launch_head(bool pre_ln, const float *x, int H, const Ragged &r, cons
                                                      offset, r.dest, rewards);
     return hipGetLastError();
   });
+}
+
+hipError_t launch_best_of_n(const float *rewards, const int32_t *cstart, int n_prompts,
+                            int32_t *best, hipStream_t st) {
+  if (n_prompts <= 0) return hipSuccess;
+  best_of_n_kernel<<<(n_prompts + 255) / 256, 256, 0, st>>>(rewards, cstart, n_prompts, best);
+  return hipGetLastError();
 }
 
 }  // namespace es

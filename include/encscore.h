@@ -160,6 +160,45 @@ es_status es_score_requests(es_model *m, const int32_t *d_token_ids, const int32
                             es_stream_stats_t *stats);
 
 /*
+ * es_score_best_of_n -- best-of-N scoring with shared prompts ("Learning to
+ * summarize from human feedback", Method adaptation: the reward model scores
+ * N candidate summaries of a post and the highest-scoring one is kept).
+ *
+ *   d_token_ids     int32 on the device: the n_prompts prompts back to back,
+ *                   then every candidate continuation back to back (the
+ *                   candidates of prompt 0 first, then those of prompt 1, ...).
+ *   h_prompt_lengths int32[n_prompts] (host), each >= 1.
+ *   h_cand_lengths  int32[sum h_cand_counts] (host), each >= 1, and prompt +
+ *                   candidate <= max_pos.
+ *   h_cand_counts   int32[n_prompts] (host), candidates per prompt, each >= 1.
+ *   d_rewards       float32[sum h_cand_counts] (device): the reward of prompt
+ *                   p followed by candidate c, in candidate order.
+ *   d_best          int32[n_prompts] (device): per prompt, the index within
+ *                   its candidates of the largest reward; the lowest index
+ *                   among equal rewards.
+ *
+ * The model must be causal (a token's state depends only on earlier tokens)
+ * and bf16.  Each prompt is embedded and run through the layers once; its
+ * candidates' tokens take positions after it and attend to its keys and
+ * values, so the work is that of the prompt plus the candidates rather than
+ * N copies of the prompt.  Rewards are bitwise those es_score_requests gives
+ * for the concatenated prompt + candidate sequences under fused attention.
+ * Prompt groups (a prompt with all its candidates) are the planner's items,
+ * each as long as its tokens (es_plan_batches, budget max_tokens); grouping
+ * and passes in flight apply as in es_score_requests; attention is always
+ * the fused kernel here.  Asynchronous on `stream`; `stats` may be NULL
+ * (packed_tokens counts each prompt once).  Errors: ES_ERR_ARG (NULL,
+ * counts < 1, model not causal bf16), ES_ERR_RANGE (a length outside its
+ * bounds), ES_ERR_CAPACITY (a prompt group above max_tokens tokens or
+ * max_seqs - 1 candidates), ES_ERR_HIP.
+ */
+es_status es_score_best_of_n(es_model *m, const int32_t *d_token_ids,
+                             const int32_t *h_prompt_lengths, int32_t n_prompts,
+                             const int32_t *h_cand_lengths, const int32_t *h_cand_counts,
+                             int64_t batch_overhead, float *d_rewards, int32_t *d_best,
+                             void *stream, es_stream_stats_t *stats);
+
+/*
  * es_forward_hidden -- diagnostic form of es_score_batch: runs the embedding
  * and the first `n_layers` layers (0 <= n_layers <= model layers) and copies
  * the fp32 residual stream into d_hidden float32[offsets[n_seqs], hidden]

@@ -115,3 +115,26 @@ def test_decoder_rm_best_of_16_full_stream(attention):
     sc.reward_offset = 0.0
     idx = np.array([int(np.argmin(lengths)), int(np.argmax(lengths))])
     _check_sample(torch, sc, cfg, w, ids, lengths, rew, idx, cache=False)
+
+
+def test_decoder_rm_best_of_16_shared_prompts():
+    """The decoder workload through es_score_best_of_n (each 512-token prompt
+    run once for its 16 candidates): rewards bitwise equal to scoring the
+    prompt + candidate sequences (fused attention, same launch settings; those
+    are oracle-checked in the stream test above), and the per-prompt choice
+    equals the oracle's selection on them."""
+    torch = need_gpu()
+    from synth.generate import best_of_n_form
+    cfg = get_config("decoder_rm")
+    say("decoder_rm: drawing 1.4B weights")
+    w = make_weights(cfg)
+    ids, lengths, group = make_requests(cfg)
+    sc, rew = _stream(torch, cfg, w, ids, lengths, attention="fused")
+    p_ids, pl, c_ids, cl, cn = best_of_n_form(ids, lengths, group, 512)
+    d = torch.from_numpy(np.concatenate([p_ids, c_ids])).cuda()
+    got, best, stats = sc.score_best_of_n(d, pl, cl, cn, cfg.batch_overhead)
+    torch.cuda.synchronize()
+    say("shared prompts:", stats)
+    assert np.array_equal(got.cpu().numpy().astype(np.float64), rew)
+    assert best.cpu().numpy().tolist() == oracle.best_of_n(rew.tolist(), cn.tolist())
+    assert stats["packed_tokens"] == int(pl.sum() + cl.sum())
