@@ -280,8 +280,8 @@ __global__ __launch_bounds__(64) void pv_mfma_kernel(const uint16_t *__restrict_
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       uint2 u;
-      u.x = (uint32_t)f2bf(acc[t][4 * g]) | ((uint32_t)f2bf(acc[t][4 * g + 1]) << 16);
-      u.y = (uint32_t)f2bf(acc[t][4 * g + 2]) | ((uint32_t)f2bf(acc[t][4 * g + 3]) << 16);
+      u.x = f2bf2(acc[t][4 * g], acc[t][4 * g + 1]);
+      u.y = f2bf2(acc[t][4 * g + 2], acc[t][4 * g + 3]);
       *reinterpret_cast<uint2 *>(Cr + t * 32 + 8 * g + 4 * fh) = u;
     }
 }
@@ -380,7 +380,7 @@ __global__ __launch_bounds__(64) void attn_fused_kernel(const uint16_t *__restri
     for (int kk = 0; kk < 2; ++kk) {
       bf16x8 pf;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) pf[j] = __builtin_bit_cast(__bf16, f2bf(s[8 * kk + j]));
+      for (int j = 0; j < 8; ++j) pf[j] = (__bf16)s[8 * kk + j];
       const int c0 = 16 * kk + 4 * fh;  // tile keys of slots 0..3; slots 4..7 are c0 + 8
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
@@ -400,8 +400,8 @@ __global__ __launch_bounds__(64) void attn_fused_kernel(const uint16_t *__restri
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       uint2 u;
-      u.x = (uint32_t)f2bf(acc[t][4 * g] * inv) | ((uint32_t)f2bf(acc[t][4 * g + 1] * inv) << 16);
-      u.y = (uint32_t)f2bf(acc[t][4 * g + 2] * inv) | ((uint32_t)f2bf(acc[t][4 * g + 3] * inv) << 16);
+      u.x = f2bf2(acc[t][4 * g] * inv, acc[t][4 * g + 1] * inv);
+      u.y = f2bf2(acc[t][4 * g + 2] * inv, acc[t][4 * g + 3] * inv);
       *reinterpret_cast<uint2 *>(Cr + t * 32 + 8 * g + 4 * fh) = u;
     }
 }

@@ -11,11 +11,15 @@ constexpr int kWave = 64;  // CDNA wavefront width
 // bf16 is stored as raw 16-bit patterns; conversion rounds to nearest even.
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
-__device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// float -> bf16 bits, round to nearest even (gfx950's v_cvt_pk_bf16_f32; a
+// NaN stays a quiet NaN).
+__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
+// Two floats -> packed bf16 bits (lo in bits 0..15), one conversion instruction.
+__device__ __forceinline__ uint32_t f2bf2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ float to_f(float v) { return v; }

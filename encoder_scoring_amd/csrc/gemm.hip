@@ -85,6 +85,43 @@ __device__ __forceinline__ void store_stage(const Stage<C, ROWS> &r, uint16_t *s
   }
 }
 
+// Four consecutive outputs (m, n..n+3) of one lane, with bias[n..n+3]
+// already loaded in bv when n + 3 < N.
+template <int EPI>
+__device__ __forceinline__ void epi_store4_bias(void *out, const float *res, int ldc, int64_t m,
+                                                int n, int N, float4 v, float4 bv,
+                                                const float *__restrict__ bias) {
+  const int64_t o = m * ldc + n;
+  constexpr bool RES = EPI == kEpiResidual || EPI == kEpiResidualFfn;
+  if (n + 3 < N) {
+    v.x += bv.x; v.y += bv.y; v.z += bv.z; v.w += bv.w;
+    if (EPI == kEpiBias || EPI == kEpiGelu) {
+      if (EPI == kEpiGelu) {
+        v.x = gelu_erf_bf16out(v.x); v.y = gelu_erf_bf16out(v.y);
+        v.z = gelu_erf_bf16out(v.z); v.w = gelu_erf_bf16out(v.w);
+      }
+      *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(out) + o) = make_uint2(f2bf2(v.x, v.y), f2bf2(v.z, v.w));
+    } else {
+      if (RES) {
+        const float4 r = *reinterpret_cast<const float4 *>(res + o);
+        v.x += r.x; v.y += r.y; v.z += r.z; v.w += r.w;
+      }
+      *reinterpret_cast<float4 *>(static_cast<float *>(out) + o) = v;
+    }
+    return;
+  }
+  const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if (n + e >= N) break;
+    float x = vv[e] + bias[n + e];
+    if (EPI == kEpiBias) static_cast<uint16_t *>(out)[o + e] = f2bf(x);
+    else if (EPI == kEpiGelu) static_cast<uint16_t *>(out)[o + e] = f2bf(gelu_erf_bf16out(x));
+    else if (RES) static_cast<float *>(out)[o + e] = x + res[o + e];
+    else static_cast<float *>(out)[o + e] = x;
+  }
+}
+
 // Four consecutive outputs (m, n..n+3) of one lane.
 template <int EPI>
 __device__ __forceinline__ void epi_store4(void *out, const float *res, int ldc, int64_t m, int n,
@@ -100,8 +137,8 @@ __device__ __forceinline__ void epi_store4(void *out, const float *res, int ldc,
         v.z = gelu_erf_bf16out(v.z); v.w = gelu_erf_bf16out(v.w);
       }
       uint2 u;
-      u.x = (uint32_t)f2bf(v.x) | ((uint32_t)f2bf(v.y) << 16);
-      u.y = (uint32_t)f2bf(v.z) | ((uint32_t)f2bf(v.w) << 16);
+      u.x = f2bf2(v.x, v.y);
+      u.y = f2bf2(v.z, v.w);
       *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(out) + o) = u;
     } else {
       if (RES) {
@@ -463,23 +500,39 @@ __global__ __launch_bounds__(512, 2) void gemm_pp_kernel(
   }
   if (grp == 0) __builtin_amdgcn_s_barrier();
 
-  // acc[i][j] = D[n][m] of the W x A product: lane holds row m = lane & 31
-  // and register r holds column 8 * (r / 4) + 4 * (lane / 32) + (r % 4).
+  // Epilogue.  acc[i][j] = D[n][m] of the W x A product: lane holds row
+  // m = lane & 31 and register r column 8 (r / 4) + 4 (lane / 32) + (r % 4),
+  // so stored straight from registers one instruction writes 16-32 bytes in
+  // each of 32 rows.  Instead each wave stages 32 rows of its accumulators at
+  // a time in its own LDS region (the stage buffers are free after the last
+  // barrier) and reads them back along rows: a lane then owns one 4-column
+  // chunk, bias (and residual) loads and output stores cover whole row
+  // segments.  Rows are padded by 4 floats so both the staging writes and
+  // the row reads spread over the LDS banks.  Every access is by the wave
+  // that wrote it, in program order, so no barrier is needed.
+  constexpr int PITCH = C::WN + 4;              // floats per staged row
+  constexpr int CH = C::WN / 4;                 // 4-column chunks per row
+  constexpr int RPI = 64 / CH;                  // rows per read instruction
+  static_assert(4 * 32 * PITCH * 4 <= C::SZ * 2, "epilogue staging exceeds a stage buffer");
+  float *stage = reinterpret_cast<float *>(grp == 0 ? L0 : L1) + q * 32 * PITCH;  // group g in buffer g
+  const int cc = lane % CH, rr = lane / CH;
+  const int n = n0 + C::WN * q + 4 * cc;
+  float4 bv = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (n + 3 < N) bv = *reinterpret_cast<const float4 *>(bias + n);
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
-    const int64_t m = m0 + C::WM * grp + i * 32 + fr;
-    if (m >= M) continue;
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = n0 + C::WN * q + j * 32 + 8 * g + 4 * fh;
-        if (n < N)
-          epi_store4<EPI>(out, res, ldc, m, n, N,
-                          make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1],
-                                      acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]),
-                          bias);
-      }
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<float4 *>(stage + fr * PITCH + j * 32 + 8 * g + 4 * fh) =
+            make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+#pragma unroll
+    for (int r0 = 0; r0 < 32; r0 += RPI) {
+      const int row = r0 + rr;
+      const int64_t m = m0 + C::WM * grp + i * 32 + row;
+      const float4 v = *reinterpret_cast<const float4 *>(stage + row * PITCH + 4 * cc);
+      if (m < M && n < N) epi_store4_bias<EPI>(out, res, ldc, m, n, N, v, bv, bias);
     }
   }
 }

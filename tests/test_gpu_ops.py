@@ -169,3 +169,34 @@ def test_gemm_rejects_bad_shapes():
     w64 = torch.zeros((256, 64), dtype=torch.int16, device="cuda")
     with pytest.raises(EncScoreError):
         gemm_bf16(a64, w64, bias, out, 4, 64, 64, 0, tile=3)  # no such tile
+
+
+def test_bf16_conversion_ties_and_specials():
+    """The bf16 epilogue's float -> bf16 conversion rounds to nearest, ties to
+    even: with zero operands every output is exactly bf16(bias[n]), and the
+    biases are exact midpoints between neighbouring bf16 values (even and odd
+    lower neighbour), infinities, subnormals, and the largest finite values."""
+    torch = need_gpu()
+    rng = np.random.default_rng(11)
+    hi = rng.integers(0x0080, 0x7F00, size=96).astype(np.uint32)       # bf16 patterns
+    mids = ((hi << 16) | 0x8000).view(np.float32)                       # exact ties
+    mids = np.concatenate([mids, -mids[:32]])
+    specials = np.array([np.inf, -np.inf, 0.0, -0.0, 1e-40, -3e-39, 3.3895314e38, -3.3895314e38,
+                         1.0 + 2 ** -9, 1.0 + 3 * 2 ** -9, 2 ** -126, 0.1], dtype=np.float32)
+    bias = np.concatenate([mids, specials]).astype(np.float32)
+    N = bias.size
+    M, K = 33, 64
+    a = torch.zeros((256, K), dtype=torch.int16, device="cuda")
+    w = torch.zeros((-(-N // 256) * 256, K), dtype=torch.int16, device="cuda")
+    out = torch.zeros((M, N + (-N) % 4), dtype=torch.int16, device="cuda")
+    gemm_bf16(a, w, torch.from_numpy(bias).cuda(), out, M, N, K, 0)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint16)[:, :N]
+    want = f32_to_bf16_bits((np.float32(0.0) + bias).astype(np.float32))   # acc (+0) + bias
+    assert np.array_equal(got, np.broadcast_to(want, got.shape))
+    # NaN stays NaN
+    nan_bias = torch.full((4,), float("nan"), device="cuda")
+    out4 = torch.zeros((M, 4), dtype=torch.int16, device="cuda")
+    gemm_bf16(a, torch.zeros((256, K), dtype=torch.int16, device="cuda"), nan_bias, out4, M, 4, K, 0)
+    torch.cuda.synchronize()
+    assert np.all(np.isnan(bf16_bits_to_f32(out4)))
