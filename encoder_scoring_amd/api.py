@@ -257,7 +257,7 @@ def softmax_ragged(rag, scores, probs):
 
 def gemm_bf16(a, w, bias, out, M, N, K, epilogue, res=None, tile=None):
     """out = epilogue(A W^T + bias) on the bf16 MFMA kernel (a, w as int16 bits);
-    tile forces a block-tile configuration (0, 1, 2), None chooses from the shape."""
+    tile forces a block-tile configuration (0..3), None chooses from the shape."""
     torch = _torch()
     lib = _lib.load()
     args = (_dptr(a, torch.int16, "a"), a.shape[1], _dptr(w, torch.int16, "w"),

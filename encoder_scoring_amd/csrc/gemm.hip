@@ -512,7 +512,8 @@ __global__ __launch_bounds__(512, 2) void gemm_pp_kernel(
   // that wrote it, in program order, so no barrier is needed.
   constexpr int PITCH = C::WN + 4;              // floats per staged row
   constexpr int CH = C::WN / 4;                 // 4-column chunks per row
-  constexpr int RPI = 64 / CH;                  // rows per read instruction
+  constexpr int RPI = 64 / CH;                  // rows per read instruction (lanes beyond
+                                                // RPI * CH idle when CH does not divide 64)
   static_assert(4 * 32 * PITCH * 4 <= C::SZ * 2, "epilogue staging exceeds a stage buffer");
   float *stage = reinterpret_cast<float *>(grp == 0 ? L0 : L1) + q * 32 * PITCH;  // group g in buffer g
   const int cc = lane % CH, rr = lane / CH;
@@ -530,9 +531,11 @@ __global__ __launch_bounds__(512, 2) void gemm_pp_kernel(
 #pragma unroll
     for (int r0 = 0; r0 < 32; r0 += RPI) {
       const int row = r0 + rr;
-      const int64_t m = m0 + C::WM * grp + i * 32 + row;
-      const float4 v = *reinterpret_cast<const float4 *>(stage + row * PITCH + 4 * cc);
-      if (m < M && n < N) epi_store4_bias<EPI>(out, res, ldc, m, n, N, v, bv, bias);
+      if (rr < RPI && row < 32) {
+        const int64_t m = m0 + C::WM * grp + i * 32 + row;
+        const float4 v = *reinterpret_cast<const float4 *>(stage + row * PITCH + 4 * cc);
+        if (m < M && n < N) epi_store4_bias<EPI>(out, res, ldc, m, n, N, v, bv, bias);
+      }
     }
   }
 }
@@ -651,38 +654,46 @@ hipError_t go_pp(const uint16_t *A, int lda, const uint16_t *W, const float *bia
 //   0  T1  128 x 64, register-staged, 4 waves (64 x 32 each), three blocks per CU
 //   1  P1  128 x 128 ping-pong, 8 waves (64 x 32 each), two blocks per CU
 //   2  P2  256 x 256 ping-pong, 8 waves (128 x 64 each), one block per CU
+//   3  P3  128 x 384 ping-pong, 8 waves (64 x 96 each), one block per CU
 //                  BM  BN  BK WGM WGN PF MINW
 using T1 = Cfg<128, 64, 64, 2, 2, 2, 3>;
 using P1 = PPCfg<128, 128>;
 using P2 = PPCfg<256, 256>;
-static_assert(kGemmTiles == 3, "tile menu and launcher disagree");
+using P3 = PPCfg<128, 384>;
+static_assert(kGemmTiles == 4, "tile menu and launcher disagree");
 
 constexpr int kCUs = 256;
 
 }  // namespace
 
 // Configuration for an M x N x K problem, from a sweep of the model's GEMM
-// shapes on MI355X (TFLOP/s; tile 0 / 1 / 2):
-//   M      N     K    epilogue     0     1     2
-//   4096   2304  768  bias        436   462   404
-//   4096   768   768  residual    288   299   131
-//   4096   3072  768  GELU        462   551   423
-//   8192   768   3072 residual    635   728   470
-//   16384  2304  768  bias        597   658   556
-//   16384  768   3072 residual    631   734   828
-//   16384  6144  2048 bias        673   947  1043
-//   16384  2048  8192 residual    655   929  1093
-//   2048   768   768  residual    201   168    70
-// 256 x 256 blocks pay off only with a long K and enough blocks for half the
-// CUs; 128 x 128 blocks while they cover half the CUs; else 128 x 64 blocks
-// (more of them).  Every configuration issues the same MFMA over K in the
-// same order and K is never split, so each output's accumulation order does
-// not depend on the configuration chosen or on the other sequences in the
-// batch.
+// shapes on MI355X (TFLOP/s; tile 0 / 1 / 2 / 3):
+//   M      N     K    epilogue     0     1     2     3
+//   2048   768   768  residual    203   194    90   105
+//   4096   2304  768  bias        471   555   515   561
+//   4096   3072  768  GELU        481   577   478   497
+//   8192   768   3072 residual    577   794   469   522
+//   16384  2304  768  bias        566   791   712   772
+//   16384  3072  768  GELU        509   655   634   554
+//   16384  768   3072 residual    608   795   833   915
+//   16384  6144  2048 bias        645   973  1163  1052
+//   16384  2048  8192 residual    644   973  1091   975
+// Wide blocks (2, 3) pay off only with a long K, and only while their count
+// fills the chip: 128 x 384 for narrow outputs (N <= 1024) once its blocks
+// cover 90 % of the CUs, 256 x 256 once they cover half; 128 x 128 while its
+// blocks cover half the CUs; else 128 x 64 (more blocks).  Every
+// configuration issues the same MFMA over K in the same order and K is never
+// split, so each output's accumulation order does not depend on the
+// configuration chosen or on the other sequences in the batch.
 int gemm_tile_index(int M, int N, int K) {
-  const int64_t b256 = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
   const int64_t b128 = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
-  if (K >= 2048 && b256 >= kCUs / 2) return 2;
+  const int64_t b256 = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
+  const int64_t b384 = (int64_t)((M + 127) / 128) * ((N + 383) / 384);
+  const bool p3_fits = (N + 383) / 384 * 384 <= (N + 255) / 256 * 256;
+  if (K >= 2048) {
+    if (N <= 1024 && p3_fits && 10 * b384 >= 9 * kCUs) return 3;
+    if (b256 >= kCUs / 2) return 2;
+  }
   if (b128 >= kCUs / 2) return 1;
   return 0;
 }
@@ -696,11 +707,17 @@ hipError_t launch_gemm_bf16_tile(int tile, const uint16_t *A, int lda, const uin
     case 0: return go_bf16<T1>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
     case 1: return go_pp<P1>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
     case 2: return go_pp<P2>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
+    case 3:
+      // W is padded to 256 rows; a 384-wide last column block must stay inside
+      // that padding, else the 128 x 128 tile does the work (same result)
+      if ((N + 383) / 384 * 384 > (N + 255) / 256 * 256)
+        return go_pp<P1>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
+      return go_pp<P3>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
     default: return hipErrorInvalidValue;
   }
 }
 
-// ES_GEMM_TILE=<0..2> forces one configuration (for tuning sweeps); unset = model.
+// ES_GEMM_TILE=<0..3> forces one configuration (for tuning sweeps); unset = model.
 hipError_t launch_gemm_bf16(const uint16_t *A, int lda, const uint16_t *W, const float *bias,
                             const float *res, void *out, int ldc, int M, int N, int K, int epi,
                             hipStream_t st) {
