@@ -35,7 +35,7 @@ PEAKS = {  # MI355X published peaks
     "alu_fp32": (157.3, "TFLOP/s"),
 }
 GEMM_CLASSES = ("qkv_gemm", "oproj_gemm", "ffn1_gemm", "ffn2_gemm", "attn_fused")
-HBM_CLASSES = ("softmax", "layernorm", "embed", "head")
+HBM_CLASSES = ("softmax", "layernorm", "embed", "head", "gather")
 WORKLOAD_DESC = {
     "tiny_fp32": "2-layer fp32 encoder (hidden 128, 2 heads, FFN 512, vocab 1000); 8 requests U{2..32}",
     "tinybert": "TinyBERT-shaped bf16 encoder (4x312, 12 heads of 26, FFN 1200, vocab 30522); 64 requests of 128 tokens",

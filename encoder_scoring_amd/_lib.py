@@ -25,11 +25,11 @@ EXPORTS = [
     "es_forward_hidden", "es_set_reward_offset", "es_get_reward_offset", "es_calibrate_offset",
     "es_check_device_errors", "es_plan_batches", "es_pack_offsets", "es_op_layernorm",
     "es_ragged_create", "es_ragged_free", "es_op_softmax", "es_op_gemm_bf16", "es_op_gemm_bf16_tile", "es_last_error",
-    "es_version", "es_set_concurrency", "es_set_batch_grouping", "es_score_best_of_n", "es_set_attention", "es_profile_enable", "es_profile_collect", "es_kernel_class_name",
+    "es_version", "es_set_concurrency", "es_set_batch_grouping", "es_score_best_of_n", "es_set_pruning", "es_set_attention", "es_profile_enable", "es_profile_collect", "es_kernel_class_name",
 ]
 
 KERNEL_CLASSES = ["embed", "qkv_gemm", "scores", "softmax", "pv", "oproj_gemm", "layernorm",
-                  "ffn1_gemm", "ffn2_gemm", "head", "attn_fused"]
+                  "ffn1_gemm", "ffn2_gemm", "head", "attn_fused", "gather"]
 
 
 class EncScoreError(RuntimeError):
@@ -74,6 +74,7 @@ _SIGS = {
     "es_set_reward_offset": (ctypes.c_int32, [_P, ctypes.c_float]),
     "es_set_concurrency": (ctypes.c_int32, [_P, ctypes.c_int32]),
     "es_set_batch_grouping": (ctypes.c_int32, [_P, ctypes.c_int32]),
+    "es_set_pruning": (ctypes.c_int32, [_P, ctypes.c_int32]),
     "es_set_attention": (ctypes.c_int32, [_P, ctypes.c_int32]),
     "es_get_reward_offset": (ctypes.c_int32, [_P, ctypes.POINTER(ctypes.c_float)]),
     "es_calibrate_offset": (ctypes.c_int32, [_P, _P, _I32P, ctypes.c_int32, _P, ctypes.POINTER(ctypes.c_float)]),

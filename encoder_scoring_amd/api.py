@@ -181,6 +181,10 @@ class Scorer:
         """Planned batches score_requests packs into one pass (es_set_batch_grouping)."""
         check(self.lib, self.lib.es_set_batch_grouping(self.handle, int(batches_per_pass)))
 
+    def set_pruning(self, enabled):
+        """Last layer on the last tokens only (default on; es_set_pruning)."""
+        check(self.lib, self.lib.es_set_pruning(self.handle, 1 if enabled else 0))
+
     def set_attention(self, mode):
         """"unfused" (scores, softmax row reduction, P.V) or "fused" (one kernel)."""
         code = {"unfused": 0, "fused": 1}[mode]

@@ -56,6 +56,12 @@ hipError_t launch_layernorm(bool act_bf16, const float *x, const float *g, const
 // Ragged softmax over score blocks: S fp32 -> P (bf16 bits or fp32).
 hipError_t launch_softmax(bool p_bf16, const float *S, void *P, const Ragged &r, int n_heads,
                           bool causal, hipStream_t st);
+// Row gather for the pruned last layer: a_dst row i = a_src row rows[i]
+// (a_bytes per row, pitches in bytes), and the same for c; all sizes and
+// pitches multiples of 4 bytes.
+hipError_t launch_gather_rows(const void *a_src, int a_pitch, void *a_dst, int a_dpitch, int a_bytes,
+                              const void *c_src, int c_pitch, void *c_dst, int c_dpitch, int c_bytes,
+                              const int32_t *rows, int n, hipStream_t st);
 // Best-of-N selection: best[p] = index (within prompt p's candidates
 // cstart[p] .. cstart[p+1]-1) of the largest reward, the lowest among equals.
 hipError_t launch_best_of_n(const float *rewards, const int32_t *cstart, int n_prompts,

@@ -78,6 +78,7 @@ struct es_model {
   std::vector<Workspace> ws;  // allocated workspaces; the first `lanes` are used
   int lanes = 1;
   int group = 1;  // planned batches scored by one pass through the layers
+  bool prune = true;  // last layer on the last token of each sequence only (es_set_pruning)
   hipEvent_t fork_ev = nullptr;
   float *rew = nullptr;  // raw rewards of a reference set (es_calibrate_offset)
   size_t rew_cap = 0;
@@ -291,6 +292,8 @@ es_status build(const es::ParsedBlob &pb, int64_t max_tokens, int32_t max_seqs, 
 // assembled on the host, staged in pinned memory and uploaded in ONE copy.
 struct BatchLayout {
   size_t off = 0, sbase = 0, items = 0, sm_items = 0, src = 0, dest = 0, pref = 0, plen = 0;
+  size_t last_items = 0, last_rows = 0, iota = 0;  // last-token work of the pruned last layer
+  int64_t last_pairs = 0;  // visible (query, key) pairs of the last queries, over heads
   bool has_src = false, has_dest = false, has_prefix = false;
   int n = 0, n_items = 0, n_sm_items = 0, max_len = 0, n_tokens = 0;
   int64_t pairs = 0;  // visible (query, key) pairs summed over heads
@@ -365,6 +368,21 @@ es_status add_batch(es_model *m, const int32_t *h_off, int32_t n, const int32_t 
   L->has_dest = dest != nullptr;
   if (src) L->src = push_bytes(buf, src, sizeof(int32_t) * n);
   if (dest) L->dest = push_bytes(buf, dest, sizeof(int32_t) * n);
+  {
+    std::vector<int32_t> li((size_t)2 * n), lr((size_t)n), io((size_t)n + 1);
+    for (int32_t i = 0; i < n; ++i) {
+      const int32_t len = h_off[i + 1] - h_off[i];
+      li[2 * i] = i;
+      li[2 * i + 1] = len - 1;
+      lr[i] = h_off[i + 1] - 1;
+      io[i] = i;
+      L->last_pairs += (int64_t)m->A * (m->causal ? len + (plen ? plen[i] : 0) : len);
+    }
+    io[n] = n;
+    L->last_items = push_bytes(buf, li.data(), sizeof(int32_t) * li.size());
+    L->last_rows = push_bytes(buf, lr.data(), sizeof(int32_t) * lr.size());
+    L->iota = push_bytes(buf, io.data(), sizeof(int32_t) * io.size());
+  }
   L->has_prefix = plen != nullptr;
   if (plen) {
     L->pref = push_bytes(buf, pref, sizeof(int32_t) * n);
@@ -407,6 +425,33 @@ es_status upload_meta(es_model *m, hipStream_t st) {
   return ES_OK;
 }
 
+// The last-token view of a layout, for the pruned last layer: `attn` keeps
+// the packed offsets (and shared prompts) with one work item per sequence
+// (its last query); `rows` lists the packed row of every last token; `tail`
+// indexes the compacted rows 0..n-1 (offsets 0, 1, .., n) with the same
+// reward slots.
+struct LastView {
+  es::Ragged attn, tail;
+  const int32_t *rows = nullptr;
+  int64_t pairs = 0;
+};
+
+es::Ragged ragged_of(const es_model *m, const BatchLayout &L);
+
+LastView last_view_of(const es_model *m, const BatchLayout &L) {
+  LastView v;
+  v.attn = ragged_of(m, L);
+  v.attn.items = reinterpret_cast<const int32_t *>(m->meta_dev + L.last_items);
+  v.attn.n_items = L.n;
+  v.rows = reinterpret_cast<const int32_t *>(m->meta_dev + L.last_rows);
+  v.tail = v.attn;
+  v.tail.off = reinterpret_cast<const int32_t *>(m->meta_dev + L.iota);
+  v.tail.n_tokens = L.n;
+  v.tail.pref = v.tail.plen = nullptr;
+  v.pairs = L.last_pairs;
+  return v;
+}
+
 es::Ragged ragged_of(const es_model *m, const BatchLayout &L) {
   es::Ragged r;
   r.off = reinterpret_cast<const int32_t *>(m->meta_dev + L.off);
@@ -427,7 +472,7 @@ es::Ragged ragged_of(const es_model *m, const BatchLayout &L) {
 
 // One batch given by host offsets: validate, stage, upload.
 es_status prepare(es_model *m, const int32_t *h_off, int32_t n, hipStream_t st, es::Ragged *r,
-                  int64_t *pairs) {
+                  int64_t *pairs, BatchLayout *layout = nullptr) {
   m->meta_asm.clear();
   BatchLayout L;
   es_status s = add_batch(m, h_off, n, nullptr, nullptr, &L);
@@ -435,6 +480,7 @@ es_status prepare(es_model *m, const int32_t *h_off, int32_t n, hipStream_t st, 
   if ((s = upload_meta(m, st)) != ES_OK) return s;
   *r = ragged_of(m, L);
   *pairs = L.pairs;
+  if (layout) *layout = L;
   return ES_OK;
 }
 
@@ -521,10 +567,30 @@ es_status layernorm(es_model *m, Workspace &w, const float *x, const float *g, c
   return ES_OK;
 }
 
+// Copy each last-token row of the residual stream (x -> y rows 0..n-1) and
+// of the attention context (ctx -> qkv rows 0..n-1, pitch Nqkv) for the
+// pruned last layer; the full-size contents of both sources are dead after.
+es_status gather_last(es_model *m, Workspace &w, const LastView &lv, hipStream_t st) {
+  Prof p(m, st, ES_KC_GATHER);
+  const int act = m->bf16 ? 2 : 4, n = lv.tail.n_seqs;
+  HIP_TRY(es::launch_gather_rows(w.x, m->H * 4, w.y, m->H * 4, m->H * 4, w.ctx, m->Kc * act, w.qkv,
+                                 m->Nqkv * act, m->Kc * act, lv.rows, n, st));
+  p.done(0.0, 2.0 * n * (m->H * 4.0 + m->Kc * act));
+  return ES_OK;
+}
+
+// Embedding and n_layers layers.  With `last` (scoring), the last layer runs
+// its QKV GEMM on every token (all keys and values are needed) and everything
+// after it on the last token of each sequence only -- the reward reads nothing
+// else -- leaving the final states in x rows 0..n_seqs-1 (head: last->tail).
+// Each row's arithmetic is unchanged (GEMMs, LayerNorm are per row; the last
+// query sees the same key tiles in the same order), so rewards are bitwise
+// those of the full last layer.
 es_status forward(es_model *m, Workspace &w, const int32_t *d_ids, const es::Ragged &r,
-                  int64_t pairs, int n_layers, hipStream_t st) {
+                  int64_t pairs, int n_layers, hipStream_t st, const LastView *last = nullptr) {
   const int T = r.n_tokens, H = m->H, F = m->F, Hd = m->A * m->d;
   const double a = m->bf16 ? 2.0 : 4.0;
+  const bool fused = m->bf16 && (m->attn_mode == 1 || r.plen);
   es_status s;
   {
     Prof p(m, st, ES_KC_EMBED);
@@ -534,30 +600,58 @@ es_status forward(es_model *m, Workspace &w, const int32_t *d_ids, const es::Rag
   }
   for (int l = 0; l < n_layers; ++l) {
     const DevLayer &D = m->layers[l];
+    const bool tail = last && l == n_layers - 1;
     if (!m->pre_ln) {
       if ((s = gemm(m, ES_KC_QKV, w.xb, m->Hp, D.w_qkv, D.b_qkv, nullptr, w.qkv, m->Nqkv, T,
                     m->Nqkv, m->Hp, H, es::kEpiBias, st)) != ES_OK) return s;
-      if ((s = attention(m, w, r, pairs, st)) != ES_OK) return s;
-      if ((s = gemm(m, ES_KC_OPROJ, w.ctx, m->Kc, D.w_o, D.b_o, w.x, w.y, H, T, H, m->Kc, Hd,
-                    es::kEpiResidual, st)) != ES_OK) return s;
-      if ((s = layernorm(m, w, w.y, D.ln1_g, D.ln1_b, T, w.x, st)) != ES_OK) return s;
-      if ((s = gemm(m, ES_KC_FFN1, w.xb, m->Hp, D.w_1, D.b_1, nullptr, w.hmid, m->Fp, T, F, m->Hp,
-                    H, es::kEpiGelu, st)) != ES_OK) return s;
-      if ((s = gemm(m, ES_KC_FFN2, w.hmid, m->Fp, D.w_2, D.b_2, w.x, w.y, H, T, H, m->Fp, F,
-                    es::kEpiResidual, st)) != ES_OK) return s;
-      if ((s = layernorm(m, w, w.y, D.ln2_g, D.ln2_b, T, w.x, st)) != ES_OK) return s;
+      if (!tail) {
+        if ((s = attention(m, w, r, pairs, st)) != ES_OK) return s;
+        if ((s = gemm(m, ES_KC_OPROJ, w.ctx, m->Kc, D.w_o, D.b_o, w.x, w.y, H, T, H, m->Kc, Hd,
+                      es::kEpiResidual, st)) != ES_OK) return s;
+        if ((s = layernorm(m, w, w.y, D.ln1_g, D.ln1_b, T, w.x, st)) != ES_OK) return s;
+        if ((s = gemm(m, ES_KC_FFN1, w.xb, m->Hp, D.w_1, D.b_1, nullptr, w.hmid, m->Fp, T, F, m->Hp,
+                      H, es::kEpiGelu, st)) != ES_OK) return s;
+        if ((s = gemm(m, ES_KC_FFN2, w.hmid, m->Fp, D.w_2, D.b_2, w.x, w.y, H, T, H, m->Fp, F,
+                      es::kEpiResidual, st)) != ES_OK) return s;
+        if ((s = layernorm(m, w, w.y, D.ln2_g, D.ln2_b, T, w.x, st)) != ES_OK) return s;
+      } else {
+        const int n = last->tail.n_seqs;
+        if ((s = attention(m, w, fused ? last->attn : r, fused ? last->pairs : pairs, st)) != ES_OK) return s;
+        if ((s = gather_last(m, w, *last, st)) != ES_OK) return s;  // x -> y, ctx -> qkv
+        if ((s = gemm(m, ES_KC_OPROJ, w.qkv, m->Nqkv, D.w_o, D.b_o, w.y, w.x, H, n, H, m->Kc, Hd,
+                      es::kEpiResidual, st)) != ES_OK) return s;
+        if ((s = layernorm(m, w, w.x, D.ln1_g, D.ln1_b, n, w.y, st)) != ES_OK) return s;
+        if ((s = gemm(m, ES_KC_FFN1, w.xb, m->Hp, D.w_1, D.b_1, nullptr, w.hmid, m->Fp, n, F, m->Hp,
+                      H, es::kEpiGelu, st)) != ES_OK) return s;
+        if ((s = gemm(m, ES_KC_FFN2, w.hmid, m->Fp, D.w_2, D.b_2, w.y, w.x, H, n, H, m->Fp, F,
+                      es::kEpiResidual, st)) != ES_OK) return s;
+        if ((s = layernorm(m, w, w.x, D.ln2_g, D.ln2_b, n, w.x, st)) != ES_OK) return s;
+      }
     } else {
       if ((s = layernorm(m, w, w.x, D.ln1_g, D.ln1_b, T, nullptr, st)) != ES_OK) return s;
       if ((s = gemm(m, ES_KC_QKV, w.xb, m->Hp, D.w_qkv, D.b_qkv, nullptr, w.qkv, m->Nqkv, T,
                     m->Nqkv, m->Hp, H, es::kEpiBias, st)) != ES_OK) return s;
-      if ((s = attention(m, w, r, pairs, st)) != ES_OK) return s;
-      if ((s = gemm(m, ES_KC_OPROJ, w.ctx, m->Kc, D.w_o, D.b_o, w.x, w.x, H, T, H, m->Kc, Hd,
-                    es::kEpiResidual, st)) != ES_OK) return s;
-      if ((s = layernorm(m, w, w.x, D.ln2_g, D.ln2_b, T, nullptr, st)) != ES_OK) return s;
-      if ((s = gemm(m, ES_KC_FFN1, w.xb, m->Hp, D.w_1, D.b_1, nullptr, w.hmid, m->Fp, T, F, m->Hp,
-                    H, es::kEpiGelu, st)) != ES_OK) return s;
-      if ((s = gemm(m, ES_KC_FFN2, w.hmid, m->Fp, D.w_2, D.b_2, w.x, w.x, H, T, H, m->Fp, F,
-                    es::kEpiResidual, st)) != ES_OK) return s;
+      if (!tail) {
+        if ((s = attention(m, w, r, pairs, st)) != ES_OK) return s;
+        if ((s = gemm(m, ES_KC_OPROJ, w.ctx, m->Kc, D.w_o, D.b_o, w.x, w.x, H, T, H, m->Kc, Hd,
+                      es::kEpiResidual, st)) != ES_OK) return s;
+        if ((s = layernorm(m, w, w.x, D.ln2_g, D.ln2_b, T, nullptr, st)) != ES_OK) return s;
+        if ((s = gemm(m, ES_KC_FFN1, w.xb, m->Hp, D.w_1, D.b_1, nullptr, w.hmid, m->Fp, T, F, m->Hp,
+                      H, es::kEpiGelu, st)) != ES_OK) return s;
+        if ((s = gemm(m, ES_KC_FFN2, w.hmid, m->Fp, D.w_2, D.b_2, w.x, w.x, H, T, H, m->Fp, F,
+                      es::kEpiResidual, st)) != ES_OK) return s;
+      } else {
+        const int n = last->tail.n_seqs;
+        if ((s = attention(m, w, fused ? last->attn : r, fused ? last->pairs : pairs, st)) != ES_OK) return s;
+        if ((s = gather_last(m, w, *last, st)) != ES_OK) return s;  // x -> y, ctx -> qkv
+        if ((s = gemm(m, ES_KC_OPROJ, w.qkv, m->Nqkv, D.w_o, D.b_o, w.y, w.y, H, n, H, m->Kc, Hd,
+                      es::kEpiResidual, st)) != ES_OK) return s;
+        if ((s = layernorm(m, w, w.y, D.ln2_g, D.ln2_b, n, nullptr, st)) != ES_OK) return s;
+        if ((s = gemm(m, ES_KC_FFN1, w.xb, m->Hp, D.w_1, D.b_1, nullptr, w.hmid, m->Fp, n, F, m->Hp,
+                      H, es::kEpiGelu, st)) != ES_OK) return s;
+        if ((s = gemm(m, ES_KC_FFN2, w.hmid, m->Fp, D.w_2, D.b_2, w.y, w.x, H, n, H, m->Fp, F,
+                      es::kEpiResidual, st)) != ES_OK) return s;
+      }
     }
   }
   (void)a;
@@ -637,6 +731,20 @@ extern "C" es_status es_model_info(const es_model *m, es_model_info_t *info) {
   return ES_OK;
 }
 
+// One pass of a laid-out batch: every layer, then the head.
+es_status score_pass(es_model *m, Workspace &w, const int32_t *d_ids, const BatchLayout &L,
+                     float *d_rewards, hipStream_t st) {
+  const es::Ragged r = ragged_of(m, L);
+  es_status s;
+  if (m->prune && m->L > 0) {
+    const LastView lv = last_view_of(m, L);
+    if ((s = forward(m, w, d_ids, r, L.pairs, m->L, st, &lv)) != ES_OK) return s;
+    return head(m, w, lv.tail, m->offset, d_rewards, st);
+  }
+  if ((s = forward(m, w, d_ids, r, L.pairs, m->L, st)) != ES_OK) return s;
+  return head(m, w, r, m->offset, d_rewards, st);
+}
+
 extern "C" es_status es_score_batch(es_model *m, const int32_t *d_token_ids, const int32_t *h_offsets,
                                     int32_t n_seqs, float *d_rewards, void *stream) {
   es_status s = check_model(m);
@@ -645,9 +753,9 @@ extern "C" es_status es_score_batch(es_model *m, const int32_t *d_token_ids, con
   hipStream_t st = static_cast<hipStream_t>(stream);
   es::Ragged r;
   int64_t pairs = 0;
-  if ((s = prepare(m, h_offsets, n_seqs, st, &r, &pairs)) != ES_OK) return s;
-  if ((s = forward(m, m->ws[0], d_token_ids, r, pairs, m->L, st)) != ES_OK) return s;
-  if ((s = head(m, m->ws[0], r, m->offset, d_rewards, st)) != ES_OK) return s;
+  BatchLayout L;
+  if ((s = prepare(m, h_offsets, n_seqs, st, &r, &pairs, &L)) != ES_OK) return s;
+  if ((s = score_pass(m, m->ws[0], d_token_ids, L, d_rewards, st)) != ES_OK) return s;
   es::clear_error();
   return ES_OK;
 }
@@ -722,9 +830,7 @@ extern "C" es_status es_score_requests(es_model *m, const int32_t *d_token_ids,
   for (int32_t g = 0; g < ng; ++g) {
     Workspace &w = m->ws[g % k];
     hipStream_t ls = k > 1 ? w.stream : st;
-    const es::Ragged r = ragged_of(m, layouts[g]);
-    if ((s = forward(m, w, d_token_ids, r, layouts[g].pairs, m->L, ls)) != ES_OK) return s;
-    if ((s = head(m, w, r, m->offset, d_rewards, ls)) != ES_OK) return s;
+    if ((s = score_pass(m, w, d_token_ids, layouts[g], d_rewards, ls)) != ES_OK) return s;
   }
   if (k > 1) {
     for (int i = 0; i < k; ++i) {
@@ -847,9 +953,7 @@ extern "C" es_status es_score_best_of_n(es_model *m, const int32_t *d_token_ids,
   for (int32_t gi = 0; gi < ng; ++gi) {
     Workspace &w = m->ws[gi % k];
     hipStream_t ls = k > 1 ? w.stream : st;
-    const es::Ragged r = ragged_of(m, layouts[gi]);
-    if ((s = forward(m, w, d_token_ids, r, layouts[gi].pairs, m->L, ls)) != ES_OK) return s;
-    if ((s = head(m, w, r, m->offset, d_rewards, ls)) != ES_OK) return s;
+    if ((s = score_pass(m, w, d_token_ids, layouts[gi], d_rewards, ls)) != ES_OK) return s;
   }
   if (k > 1) {
     for (int i = 0; i < k; ++i) {
@@ -919,6 +1023,13 @@ extern "C" es_status es_set_batch_grouping(es_model *m, int32_t batches_per_pass
       if (s != ES_OK) return s;
     }
   }
+  return ES_OK;
+}
+
+extern "C" es_status es_set_pruning(es_model *m, int32_t enabled) {
+  if (!m) return fail(ES_ERR_ARG, "model handle is NULL");
+  if (enabled != 0 && enabled != 1) return fail(ES_ERR_ARG, "enabled=%d (0 or 1)", enabled);
+  m->prune = enabled != 0;
   return ES_OK;
 }
 
@@ -1027,6 +1138,6 @@ extern "C" es_status es_profile_collect(es_model *m, es_kernel_stat_t *out) {
 extern "C" const char *es_kernel_class_name(int32_t cls) {
   static const char *names[ES_KC_COUNT] = {"embed", "qkv_gemm", "scores", "softmax", "pv",
                                            "oproj_gemm", "layernorm", "ffn1_gemm", "ffn2_gemm",
-                                           "head", "attn_fused"};
+                                           "head", "attn_fused", "gather"};
   return (cls >= 0 && cls < ES_KC_COUNT) ? names[cls] : "";
 }

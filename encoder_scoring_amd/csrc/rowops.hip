@@ -383,4 +383,28 @@ hipError_t launch_best_of_n(const float *rewards, const int32_t *cstart, int n_p
   return hipGetLastError();
 }
 
+namespace {
+// One block per gathered row: 4-byte words of the two row pieces.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint32_t *__restrict__ a, int ap, uint32_t *__restrict__ ad,
+                                                          int adp, int aw, const uint32_t *__restrict__ c, int cp,
+                                                          uint32_t *__restrict__ cd, int cdp, int cw,
+                                                          const int32_t *__restrict__ rows) {
+  const int i = blockIdx.x;
+  const int64_t r = rows[i];
+  for (int k = threadIdx.x; k < aw; k += blockDim.x) ad[(int64_t)i * adp + k] = a[r * ap + k];
+  for (int k = threadIdx.x; k < cw; k += blockDim.x) cd[(int64_t)i * cdp + k] = c[r * cp + k];
+}
+}  // namespace
+
+hipError_t launch_gather_rows(const void *a_src, int a_pitch, void *a_dst, int a_dpitch, int a_bytes,
+                              const void *c_src, int c_pitch, void *c_dst, int c_dpitch, int c_bytes,
+                              const int32_t *rows, int n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  if ((a_pitch | a_dpitch | a_bytes | c_pitch | c_dpitch | c_bytes) & 3) return hipErrorInvalidValue;
+  gather_rows_kernel<<<n, 256, 0, st>>>((const uint32_t *)a_src, a_pitch / 4, (uint32_t *)a_dst, a_dpitch / 4,
+                                        a_bytes / 4, (const uint32_t *)c_src, c_pitch / 4, (uint32_t *)c_dst,
+                                        c_dpitch / 4, c_bytes / 4, rows);
+  return hipGetLastError();
+}
+
 }  // namespace es

@@ -220,6 +220,18 @@ es_status es_forward_hidden(es_model *m, const int32_t *d_token_ids, const int32
 es_status es_set_concurrency(es_model *m, int32_t batches_in_flight);
 
 /*
+ * es_set_pruning -- last-layer pruning for the scoring entry points (default
+ * on).  The reward reads only the final state of each sequence's last token
+ * ("Learning to summarize from human feedback", Method adaptation: the
+ * reward is read at the end of the complete sequence), so the last layer runs
+ * its QKV GEMM on every token (all keys and values) and the rest -- the last
+ * query's attention, the output projection, the LayerNorms and the FFN -- on
+ * the last token of each sequence only.  Rewards are bitwise the same either
+ * way; es_forward_hidden never prunes.  enabled: 0 or 1.  Errors: ES_ERR_ARG.
+ */
+es_status es_set_pruning(es_model *m, int32_t enabled);
+
+/*
  * es_set_batch_grouping -- number of consecutive planned batches (1..8,
  * default 1) that es_score_requests packs back to back and scores in one
  * pass through the layers.  The planner's batches stay as planned
@@ -385,7 +397,7 @@ es_status es_op_gemm_bf16_tile(const uint16_t *d_a, int32_t lda, const uint16_t 
 enum {
   ES_KC_EMBED = 0, ES_KC_QKV = 1, ES_KC_SCORES = 2, ES_KC_SOFTMAX = 3, ES_KC_PV = 4,
   ES_KC_OPROJ = 5, ES_KC_LAYERNORM = 6, ES_KC_FFN1 = 7, ES_KC_FFN2 = 8, ES_KC_HEAD = 9,
-  ES_KC_ATTN_FUSED = 10, ES_KC_COUNT = 11
+  ES_KC_ATTN_FUSED = 10, ES_KC_GATHER = 11, ES_KC_COUNT = 12
 };
 
 typedef struct {

@@ -72,6 +72,10 @@ def test_shared_prompts_bitwise_equal_concatenated(cfg, group, lanes):
     assert stats["packed_tokens"] == int(plens.sum() + clens.sum())
     r = rew.cpu().numpy().astype(np.float64)
     assert best.cpu().numpy().tolist() == oracle.best_of_n(r.tolist(), counts.tolist())
+    sc.set_pruning(False)                        # the full last layer: same bits
+    full, _, _ = sc.score_best_of_n(d, plens, clens, counts, batch_overhead=64)
+    torch.cuda.synchronize()
+    assert torch.equal(full, rew)
 
 
 def test_shared_prompts_match_oracle():

@@ -211,6 +211,33 @@ def test_batches_in_flight_match_serial(lanes):
     assert torch.equal(again, serial)
 
 
+@pytest.mark.parametrize("name,cfg,tol", CASES, ids=[c[0] for c in CASES])
+@pytest.mark.parametrize("attention", ["unfused", "fused"])
+def test_last_layer_pruning_is_bitwise_exact(name, cfg, tol, attention):
+    """The last layer on the last tokens only gives bitwise the rewards of the
+    full last layer (es_score_batch and es_score_requests), for every model
+    form and both attention forms."""
+    torch = need_gpu()
+    if attention == "fused" and not cfg.bf16:
+        pytest.skip("fused attention needs a bf16 model")
+    w = make_weights(cfg)
+    ids, lengths = random_stream(17, 23, 1, min(cfg.max_pos, 120), cfg.vocab)
+    sc = scorer_for(cfg, w, offset=0.5, max_tokens=3000)
+    if cfg.bf16:
+        sc.set_attention(attention)
+    d = torch.from_numpy(ids).cuda()
+    sc.set_pruning(False)
+    full_b = gpu_score(torch, sc, ids, lengths)
+    full_s, st = sc.score_requests(d, lengths, batch_overhead=32)
+    full_s = full_s.clone()
+    sc.set_pruning(True)
+    assert np.array_equal(gpu_score(torch, sc, ids, lengths), full_b)
+    pr_s, _ = sc.score_requests(d, lengths, batch_overhead=32)
+    torch.cuda.synchronize()
+    say(name, attention, "pruned vs full:", st["n_batches"], "batches")
+    assert torch.equal(pr_s, full_s)
+
+
 @pytest.mark.parametrize("group,lanes", [(2, 1), (3, 1), (4, 2), (8, 1)])
 @pytest.mark.parametrize("attention", ["unfused", "fused"])
 def test_batch_grouping_matches_ungrouped(group, lanes, attention):
@@ -251,6 +278,9 @@ def test_grouping_and_concurrency_validation():
     for bad in (0, 5):
         with pytest.raises(EncScoreError):
             sc.set_concurrency(bad)
+    from encoder_scoring_amd._lib import check
+    with pytest.raises(EncScoreError):
+        check(sc.lib, sc.lib.es_set_pruning(sc.handle, 2))
 
 
 @pytest.mark.parametrize("name,cfg", [(c[0], c[1]) for c in CASES if c[1].bf16],
