@@ -35,8 +35,14 @@ def _hipcc():
     raise RuntimeError("hipcc not found (ROCm toolchain required to build libencscore)")
 
 
+# Per-source extras: the attention kernels keep their MFMA accumulators in
+# VGPRs (the default AGPR form costs a copy of every accumulator at each
+# online-softmax rescale).
+EXTRA_FLAGS = {"attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src, obj):
-    cmd = [_hipcc(), *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *HIP_FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd.insert(1, "-xhip")
     r = subprocess.run(cmd, capture_output=True, text=True)

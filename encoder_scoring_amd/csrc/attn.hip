@@ -333,6 +333,9 @@ __global__ __launch_bounds__(64) void attn_fused_kernel(const uint16_t *__restri
   for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
+  // scores are kept in base 2: s log2(e) / sqrt(d), so every probability is
+  // one v_exp_f32 (2^x) -- exp(x) = 2^(x log2 e), the same softmax
+  const float sl2 = scale * 1.44269504088896340736f;
   float m_run = -INFINITY, l_run = 0.f;
   const int qpos = np + q;
   const int kend = causal ? min(ntot, np + q0 + kQTile) : ntot;
@@ -357,16 +360,16 @@ __global__ __launch_bounds__(64) void attn_fused_kernel(const uint16_t *__restri
     for (int r = 0; r < 16; ++r) {
       const int key = k0 + 8 * (r >> 2) + 4 * fh + (r & 3);
       const bool ok = key < ntot && (!causal || key <= qpos);
-      s[r] = ok ? s[r] * scale : -INFINITY;
+      s[r] = ok ? s[r] * sl2 : -INFINITY;
       mx = fmaxf(mx, s[r]);
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));  // the other 16 keys of this query
     const float m_new = fmaxf(m_run, mx);
-    const float alpha = expf(m_run - m_new);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     float psum = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      s[r] = expf(s[r] - m_new);
+      s[r] = __builtin_amdgcn_exp2f(s[r] - m_new);
       psum += s[r];
     }
     l_run = l_run * alpha + psum;

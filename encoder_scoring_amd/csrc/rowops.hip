@@ -148,6 +148,8 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t *__restrict__ 
   }
 }
 
+constexpr float kLog2e = 1.44269504088896340736f;
+
 // Softmax over the ragged score rows.  One item covers a run of rows of one
 // sequence's [A * n, ld] score block (all heads; rows of equal length n, or
 // q + 1 when causal).  Each row is owned by G lanes (G from its length) that
@@ -199,10 +201,11 @@ __global__ __launch_bounds__(256) void softmax_kernel(const float *__restrict__ 
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int c = (c0 + G * j) * 4;
-      v[p][j].x = c < m[p] ? expf(v[p][j].x - mx) : 0.f;
-      v[p][j].y = c + 1 < m[p] ? expf(v[p][j].y - mx) : 0.f;
-      v[p][j].z = c + 2 < m[p] ? expf(v[p][j].z - mx) : 0.f;
-      v[p][j].w = c + 3 < m[p] ? expf(v[p][j].w - mx) : 0.f;
+      // exp(v - max) as 2^((v - max) log2 e): one v_exp_f32 each
+      v[p][j].x = c < m[p] ? __builtin_amdgcn_exp2f((v[p][j].x - mx) * kLog2e) : 0.f;
+      v[p][j].y = c + 1 < m[p] ? __builtin_amdgcn_exp2f((v[p][j].y - mx) * kLog2e) : 0.f;
+      v[p][j].z = c + 2 < m[p] ? __builtin_amdgcn_exp2f((v[p][j].z - mx) * kLog2e) : 0.f;
+      v[p][j].w = c + 3 < m[p] ? __builtin_amdgcn_exp2f((v[p][j].w - mx) * kLog2e) : 0.f;
       sum += (v[p][j].x + v[p][j].y) + (v[p][j].z + v[p][j].w);
     }
     sum = group_sum(sum, G);
