@@ -23,7 +23,7 @@ EXPORTS = [
     "es_load_weights", "es_load_weights_mem", "es_free", "es_model_info", "es_score_batch",
     "es_score_requests",
     "es_forward_hidden", "es_set_reward_offset", "es_get_reward_offset", "es_calibrate_offset",
-    "es_check_device_errors", "es_plan_batches", "es_pack_offsets", "es_op_layernorm",
+    "es_check_device_errors", "es_plan_batches", "es_pack_offsets", "es_op_layernorm", "es_op_add_layernorm",
     "es_ragged_create", "es_ragged_free", "es_op_softmax", "es_op_gemm_bf16", "es_op_gemm_bf16_tile", "es_last_error",
     "es_version", "es_set_concurrency", "es_set_batch_grouping", "es_score_best_of_n", "es_set_pruning", "es_set_attention", "es_profile_enable", "es_profile_collect", "es_kernel_class_name",
 ]
@@ -82,6 +82,7 @@ _SIGS = {
     "es_plan_batches": (ctypes.c_int32, [_I32P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, _I32P, _I32P, _I32P, _I64P]),
     "es_pack_offsets": (ctypes.c_int32, [_I32P, _I32P, ctypes.c_int32, ctypes.c_int32, _I32P]),
     "es_op_layernorm": (ctypes.c_int32, [_P, _P, _P, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, _P, _P, ctypes.c_int32, _P]),
+    "es_op_add_layernorm": (ctypes.c_int32, [_P, _P, _P, _P, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, _P, _P, ctypes.c_int32, _P]),
     "es_ragged_create": (ctypes.c_int32, [_I32P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(_P), _I64P]),
     "es_ragged_free": (None, [_P]),
     "es_op_softmax": (ctypes.c_int32, [_P, _P, _P, ctypes.c_int32, _P]),

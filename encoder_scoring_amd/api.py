@@ -211,17 +211,23 @@ class Scorer:
 
 # ------------------------------------------------------------------ single ops
 
-def layernorm(x, gamma, beta, eps, y=None, ybf16=None):
-    """Row LayerNorm of fp32 x [rows, cols] into y (fp32) and/or ybf16 (int16 bits)."""
+def layernorm(x, gamma, beta, eps, y=None, ybf16=None, sub=None):
+    """Row LayerNorm of fp32 x [rows, cols] (of x + sub with `sub`, through
+    es_op_add_layernorm) into y (fp32) and/or ybf16 (int16 bits)."""
     torch = _torch()
     lib = _lib.load()
     rows, cols = x.shape
     ld = ybf16.shape[1] if ybf16 is not None else 0
-    check(lib, lib.es_op_layernorm(
-        _dptr(x, torch.float32, "x"), _dptr(gamma, torch.float32, "gamma"),
-        _dptr(beta, torch.float32, "beta"), rows, cols, float(eps),
-        _dptr(y, torch.float32, "y") if y is not None else None,
-        _dptr(ybf16, torch.int16, "ybf16") if ybf16 is not None else None, ld, _stream()))
+    outs = (_dptr(y, torch.float32, "y") if y is not None else None,
+            _dptr(ybf16, torch.int16, "ybf16") if ybf16 is not None else None, ld, _stream())
+    g, b = _dptr(gamma, torch.float32, "gamma"), _dptr(beta, torch.float32, "beta")
+    if sub is None:
+        check(lib, lib.es_op_layernorm(_dptr(x, torch.float32, "x"), g, b, rows, cols, float(eps), *outs))
+    else:
+        if tuple(sub.shape) != (rows, cols):
+            raise ValueError(f"sub shape {tuple(sub.shape)} != x shape {(rows, cols)}")
+        check(lib, lib.es_op_add_layernorm(_dptr(x, torch.float32, "x"), _dptr(sub, torch.float32, "sub"),
+                                           g, b, rows, cols, float(eps), *outs))
 
 
 class RaggedScores:

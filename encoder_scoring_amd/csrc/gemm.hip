@@ -355,6 +355,21 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, int voff, int soff, uint32_t l
       : "memory");
 }
 
+// 4 bytes per lane into LDS at lds + 4 * lane: used only to pull lines of a
+// later stage into L2 ahead of its real load (the LDS words are never read).
+__device__ __forceinline__ void dma4(i32x4 rsrc, int voff, int soff, uint32_t lds) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %4\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %1, %2, %3 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds)
+      : "memory");
+}
+
 // Raw buffer resource over [p, p + 2 GB): base, stride 0, num_records,
 // 32-bit dword format.
 __device__ __forceinline__ i32x4 make_rsrc(const void *p) {
@@ -393,7 +408,7 @@ struct PPCfg {
   static_assert(DR % RPL == 0 && (DR / RPL) % CPR == 0, "swizzle must repeat between loads");
 };
 
-template <class C, int EPI>
+template <class C, int EPI, int PFD>
 __global__ __launch_bounds__(512, 2) void gemm_pp_kernel(
     const uint16_t *__restrict__ A, int lda, const uint16_t *__restrict__ W,
     const float *__restrict__ bias, const float *res, void *out, int ldc, int M, int N, int K,
@@ -403,6 +418,7 @@ __global__ __launch_bounds__(512, 2) void gemm_pp_kernel(
   // accesses apart
   __shared__ __attribute__((aligned(1024))) uint16_t L0[C::SZ];
   __shared__ __attribute__((aligned(1024))) uint16_t L1[C::SZ];
+  __shared__ uint32_t Lpf[64];  // landing words of the L2 prefetches (never read)
 
   int tm, tn;
   tile_of_block(tiles_m, tiles_n, tm, tn);
@@ -428,6 +444,18 @@ __global__ __launch_bounds__(512, 2) void gemm_pp_kernel(
 #pragma unroll
     for (int i = 0; i < C::NIB; ++i)
       dma16(rb, voB, (k0 + i * DR * K) * 2, l0 + BM * BK * 2 + i * C::NL * 1024);
+  };
+  // With PFD > 0, group 0 also touches every 32-byte sector of the A panel of
+  // stage k + 1 + PFD right after issuing stage k + 1, so that stage's real
+  // loads find it in L2 instead of waiting on HBM: A is the operand streamed
+  // from memory (W is shared by every block and stays in L2).  One 4-byte
+  // load per sector; lane e of the group covers row e / 4, sector e % 4.
+  constexpr int NPA = BM * 4 / (64 * C::NL);
+  const int voP = ((q * 64 + lane) / 4 * lda + (lane % 4) * 16) * 2;
+  auto prefetch = [&](int k0) {
+    const uint32_t lp = lds_addr(Lpf);
+#pragma unroll
+    for (int i = 0; i < NPA; ++i) dma4(ra, voP, (k0 + i * 64 * lda) * 2, lp);
   };
 
   f32x16 acc[TM][TN];
@@ -463,9 +491,11 @@ __global__ __launch_bounds__(512, 2) void gemm_pp_kernel(
   };
   // Nothing is scheduled across a phase boundary: the compiler would
   // otherwise move MFMAs over the barrier and merge the two phases.
-  auto end_phase = [&](bool wait_loads) {
+  // wait_loads: 0 none, 1 all loads, 2 all but the prefetches issued last.
+  auto end_phase = [&](int wait_loads) {
     __builtin_amdgcn_sched_barrier(0);
-    if (wait_loads) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
+    if (wait_loads == 2) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(NPA));
+    else if (wait_loads == 1) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
     else __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
@@ -476,9 +506,15 @@ __global__ __launch_bounds__(512, 2) void gemm_pp_kernel(
   // issues stage k+1 at the start of phase 2k into the buffer that group 1
   // finished reading in phase 2k-1, and waits for it at the end of phase
   // 2k+1, before it reads it.  Both groups pass 2 nk + 2 barriers.
+  //
+  // Prefetches: stages 1 .. PFD before the loop, stage k + 1 + PFD after
+  // stage k + 1's loads.  Loads complete in order, so the wait at the end of
+  // phase 2k+1 may leave that last batch of prefetches in flight.
   const int nk = K / BK;
   if (grp == 0) {
     issue(L0, 0);
+    if (PFD > 0)
+      for (int p = 1; p <= PFD && p < nk; ++p) prefetch(p * BK);
     __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
   }
   __builtin_amdgcn_s_barrier();
@@ -490,11 +526,15 @@ __global__ __launch_bounds__(512, 2) void gemm_pp_kernel(
       if (k < nk) {
         uint16_t *cur = s == 0 ? L0 : L1;
         uint16_t *nxt = s == 0 ? L1 : L0;
-        if (grp == 0 && k + 1 < nk) issue(nxt, (k + 1) * BK);
+        const bool pf = PFD > 0 && k + 1 + PFD < nk;
+        if (grp == 0 && k + 1 < nk) {
+          issue(nxt, (k + 1) * BK);
+          if (pf) prefetch((k + 1 + PFD) * BK);
+        }
         read_stage(cur);
-        end_phase(false);
+        end_phase(0);
         mma_stage();
-        end_phase(grp == 0);
+        end_phase(grp == 0 ? (pf ? 2 : 1) : 0);
       }
     }
   }
@@ -621,7 +661,7 @@ hipError_t go_bf16(const uint16_t *A, int lda, const uint16_t *W, const float *b
   return hipGetLastError();
 }
 
-template <class C>
+template <class C, int PFD>
 hipError_t go_pp(const uint16_t *A, int lda, const uint16_t *W, const float *bias,
                  const float *res, void *out, int ldc, int M, int N, int K, int epi,
                  hipStream_t st) {
@@ -630,19 +670,19 @@ hipError_t go_pp(const uint16_t *A, int lda, const uint16_t *W, const float *bia
   const dim3 grid(tm * tn), block(512);
   switch (epi) {
     case kEpiBias:
-      gemm_pp_kernel<C, kEpiBias><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K, tm, tn);
+      gemm_pp_kernel<C, kEpiBias, PFD><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K, tm, tn);
       break;
     case kEpiGelu:
-      gemm_pp_kernel<C, kEpiGelu><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K, tm, tn);
+      gemm_pp_kernel<C, kEpiGelu, PFD><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K, tm, tn);
       break;
     case kEpiResidual:
-      gemm_pp_kernel<C, kEpiResidual><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K, tm, tn);
+      gemm_pp_kernel<C, kEpiResidual, PFD><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K, tm, tn);
       break;
     case kEpiF32:
-      gemm_pp_kernel<C, kEpiF32><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K, tm, tn);
+      gemm_pp_kernel<C, kEpiF32, PFD><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K, tm, tn);
       break;
     case kEpiResidualFfn:
-      gemm_pp_kernel<C, kEpiResidualFfn><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K, tm, tn);
+      gemm_pp_kernel<C, kEpiResidualFfn, PFD><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K, tm, tn);
       break;
     default:
       return hipErrorInvalidValue;
@@ -654,7 +694,12 @@ hipError_t go_pp(const uint16_t *A, int lda, const uint16_t *W, const float *bia
 //   0  T1  128 x 64, register-staged, 4 waves (64 x 32 each), three blocks per CU
 //   1  P1  128 x 128 ping-pong, 8 waves (64 x 32 each), two blocks per CU
 //   2  P2  256 x 256 ping-pong, 8 waves (128 x 64 each), one block per CU
-//   3  P3  128 x 384 ping-pong, 8 waves (64 x 96 each), one block per CU
+//   3  P3  128 x 384 ping-pong, 8 waves (64 x 96 each), one block per CU, A
+//          prefetched to L2 one stage beyond the direct loads (P3 serves the
+//          long-K, narrow-N products whose A rows stream from HBM; measured in
+//          a layer sequence at 15880 x 768 x 3072: 125 -> 117 us.  For the
+//          K = 768 products, whose A panels are shared by many column tiles
+//          and already hit in L2, the same prefetch costs 5-10 %)
 //                  BM  BN  BK WGM WGN PF MINW
 using T1 = Cfg<128, 64, 64, 2, 2, 2, 3>;
 using P1 = PPCfg<128, 128>;
@@ -705,14 +750,14 @@ hipError_t launch_gemm_bf16_tile(int tile, const uint16_t *A, int lda, const uin
   if (K <= 0 || K % 64) return hipErrorInvalidValue;
   switch (tile) {
     case 0: return go_bf16<T1>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
-    case 1: return go_pp<P1>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
-    case 2: return go_pp<P2>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
+    case 1: return go_pp<P1, 0>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
+    case 2: return go_pp<P2, 0>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
     case 3:
       // W is padded to 256 rows; a 384-wide last column block must stay inside
       // that padding, else the 128 x 128 tile does the work (same result)
       if ((N + 383) / 384 * 384 > (N + 255) / 256 * 256)
-        return go_pp<P1>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
-      return go_pp<P3>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
+        return go_pp<P1, 0>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
+      return go_pp<P3, 1>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -49,10 +49,11 @@ hipError_t launch_embed(bool w_bf16, bool act_bf16, bool ln, const int32_t *ids,
                         const void *tok, const void *pos, int vocab, int H, const float *g,
                         const float *b, float eps, float *x, void *xb, int ldb, int *flag,
                         hipStream_t st);
-// Row LayerNorm: y fp32 [rows, cols] (nullable), yb [rows, ldb] (nullable).
-hipError_t launch_layernorm(bool act_bf16, const float *x, const float *g, const float *b,
-                            int64_t rows, int cols, float eps, float *y, void *yb, int ldb,
-                            hipStream_t st);
+// Row LayerNorm of x (of x + sub when sub is non-NULL, both [rows, cols]):
+// y fp32 [rows, cols] (nullable, may alias x or sub), yb [rows, ldb] (nullable).
+hipError_t launch_layernorm(bool act_bf16, const float *x, const float *sub, const float *g,
+                            const float *b, int64_t rows, int cols, float eps, float *y, void *yb,
+                            int ldb, hipStream_t st);
 // Ragged softmax over score blocks: S fp32 -> P (bf16 bits or fp32).
 hipError_t launch_softmax(bool p_bf16, const float *S, void *P, const Ragged &r, int n_heads,
                           bool causal, hipStream_t st);

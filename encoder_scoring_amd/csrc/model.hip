@@ -517,7 +517,9 @@ es_status gemm(es_model *m, int cls, const void *A, int lda, const void *W, cons
   Prof p(m, st, cls);
   if (m->bf16)
     HIP_TRY(es::launch_gemm_bf16((const uint16_t *)A, lda, (const uint16_t *)W, bias, res, out, ldc,
-                                 M, N, K, cls == ES_KC_FFN2 ? es::kEpiResidualFfn : epi, st));
+                                 M, N, K,
+                                 cls == ES_KC_FFN2 && epi == es::kEpiResidual ? es::kEpiResidualFfn : epi,
+                                 st));
   else
     HIP_TRY(es::launch_gemm_f32((const float *)A, lda, (const float *)W, bias, res, (float *)out, ldc,
                                 M, N, K, epi, st));
@@ -558,12 +560,14 @@ es_status attention(es_model *m, Workspace &w, const es::Ragged &r, int64_t pair
   return ES_OK;
 }
 
+// LayerNorm of x (of x + sub, a residual connection, when sub is non-NULL)
+// into y (fp32, nullable) and the bf16 / fp32 GEMM input w.xb.
 es_status layernorm(es_model *m, Workspace &w, const float *x, const float *g, const float *b, int T,
-                    float *y, hipStream_t st) {
+                    float *y, hipStream_t st, const float *sub = nullptr) {
   Prof p(m, st, ES_KC_LAYERNORM);
-  HIP_TRY(es::launch_layernorm(m->bf16, x, g, b, T, m->H, m->eps, y, w.xb, m->Hp, st));
+  HIP_TRY(es::launch_layernorm(m->bf16, x, sub, g, b, T, m->H, m->eps, y, w.xb, m->Hp, st));
   const double a = m->bf16 ? 2.0 : 4.0;
-  p.done(8.0 * T * m->H, (double)T * m->H * (4.0 + a + (y ? 4.0 : 0.0)));
+  p.done((sub ? 9.0 : 8.0) * T * m->H, (double)T * m->H * (4.0 + a + (y ? 4.0 : 0.0) + (sub ? 4.0 : 0.0)));
   return ES_OK;
 }
 
@@ -611,9 +615,12 @@ es_status forward(es_model *m, Workspace &w, const int32_t *d_ids, const es::Rag
         if ((s = layernorm(m, w, w.y, D.ln1_g, D.ln1_b, T, w.x, st)) != ES_OK) return s;
         if ((s = gemm(m, ES_KC_FFN1, w.xb, m->Hp, D.w_1, D.b_1, nullptr, w.hmid, m->Fp, T, F, m->Hp,
                       H, es::kEpiGelu, st)) != ES_OK) return s;
-        if ((s = gemm(m, ES_KC_FFN2, w.hmid, m->Fp, D.w_2, D.b_2, w.x, w.y, H, T, H, m->Fp, F,
-                      es::kEpiResidual, st)) != ES_OK) return s;
-        if ((s = layernorm(m, w, w.y, D.ln2_g, D.ln2_b, T, w.x, st)) != ES_OK) return s;
+        // the residual joins in the LayerNorm: the GEMM's output tiles then
+        // end without a read (its grid is often a single wave of tiles, whose
+        // epilogues all hit HBM at once), and LayerNorm streams it instead
+        if ((s = gemm(m, ES_KC_FFN2, w.hmid, m->Fp, D.w_2, D.b_2, nullptr, w.y, H, T, H, m->Fp, F,
+                      es::kEpiF32, st)) != ES_OK) return s;
+        if ((s = layernorm(m, w, w.x, D.ln2_g, D.ln2_b, T, w.x, st, w.y)) != ES_OK) return s;
       } else {
         const int n = last->tail.n_seqs;
         if ((s = attention(m, w, fused ? last->attn : r, fused ? last->pairs : pairs, st)) != ES_OK) return s;

@@ -71,8 +71,12 @@ __device__ __forceinline__ void ln_row(float4 (&v)[NC], int lane, int c4n, int c
   }
 }
 
-template <int NC, typename OutB>
-__global__ __launch_bounds__(256) void layernorm_kernel(const float *x, const float *__restrict__ g,
+// With ADD, the row is x + sub (a residual connection followed by its
+// LayerNorm); y may alias x or sub: a wavefront reads its whole row before
+// it writes any of it.
+template <int NC, typename OutB, bool ADD>
+__global__ __launch_bounds__(256) void layernorm_kernel(const float *x, const float *sub,
+                                                        const float *__restrict__ g,
                                                         const float *__restrict__ b, int64_t rows,
                                                         int cols, float eps, float *y, OutB *yb,
                                                         int ldb) {
@@ -86,6 +90,10 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float *x, const fl
   for (int j = 0; j < NC; ++j) {
     const int c4 = lane + kWave * j;
     v[j] = c4 < c4n ? load4(xr + 4 * c4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    if (ADD && c4 < c4n) {
+      const float4 u = load4(sub + row * cols + 4 * c4);
+      v[j].x += u.x; v[j].y += u.y; v[j].z += u.z; v[j].w += u.w;
+    }
   }
   ln_row<NC>(v, lane, c4n, cols, g, b, eps);
 #pragma unroll
@@ -298,19 +306,20 @@ hipError_t dispatch_nc(int cols, F &&f) {
 
 }  // namespace
 
-hipError_t launch_layernorm(bool act_bf16, const float *x, const float *g, const float *b,
-                            int64_t rows, int cols, float eps, float *y, void *yb, int ldb,
-                            hipStream_t st) {
+hipError_t launch_layernorm(bool act_bf16, const float *x, const float *sub, const float *g,
+                            const float *b, int64_t rows, int cols, float eps, float *y, void *yb,
+                            int ldb, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
   const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)), block(256);
   return dispatch_nc(cols, [&](auto nc) {
     constexpr int NC = decltype(nc)::value;
-    if (act_bf16)
-      layernorm_kernel<NC, uint16_t><<<grid, block, 0, st>>>(x, g, b, rows, cols, eps, y,
-                                                              (uint16_t *)yb, ldb);
-    else
-      layernorm_kernel<NC, float><<<grid, block, 0, st>>>(x, g, b, rows, cols, eps, y, (float *)yb,
-                                                           ldb);
+    if (act_bf16) {
+      auto k = sub ? layernorm_kernel<NC, uint16_t, true> : layernorm_kernel<NC, uint16_t, false>;
+      k<<<grid, block, 0, st>>>(x, sub, g, b, rows, cols, eps, y, (uint16_t *)yb, ldb);
+    } else {
+      auto k = sub ? layernorm_kernel<NC, float, true> : layernorm_kernel<NC, float, false>;
+      k<<<grid, block, 0, st>>>(x, sub, g, b, rows, cols, eps, y, (float *)yb, ldb);
+    }
     return hipGetLastError();
   });
 }

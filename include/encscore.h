@@ -329,6 +329,22 @@ es_status es_op_layernorm(const float *d_x, const float *d_gamma, const float *d
                           int32_t ld_bf16, void *stream);
 
 /*
+ * es_op_add_layernorm -- residual connection and its LayerNorm in one pass
+ * (the post-LN encoder layer: LayerNorm(x + sublayer(x)); TurboTransformers
+ * review, Proposed method, for the row reduction): per row,
+ *   s = x + sub,  y = (s - mean) / sqrt(var + eps) * gamma + beta,
+ * with the sum rounded to float32 before the statistics, so the result is
+ * bitwise es_op_layernorm of the float32 sum.  d_x and d_sub float32[rows,
+ * cols]; d_y (may be NULL) may alias d_x or d_sub; d_ybf16 as in
+ * es_op_layernorm.  The encoder's FFN output GEMM writes the sublayer term
+ * and this op adds the residual (the GEMM then reads no residual).
+ * Errors: ES_ERR_ARG.
+ */
+es_status es_op_add_layernorm(const float *d_x, const float *d_sub, const float *d_gamma,
+                              const float *d_beta, int64_t rows, int32_t cols, float eps,
+                              float *d_y, uint16_t *d_ybf16, int32_t ld_bf16, void *stream);
+
+/*
  * es_ragged_create / es_ragged_free -- ragged attention-score layout of one
  * packed batch, uploaded to the current device once (synchronous; allocates)
  * so that es_op_softmax can be launched repeatedly without host work.

@@ -43,6 +43,40 @@ def test_layernorm_op(rows, cols):
     assert np.array_equal(dx.cpu().numpy(), got)
 
 
+@pytest.mark.parametrize("rows,cols", [(1, 128), (37, 312), (1000, 768), (5, 8192)])
+def test_add_layernorm_op(rows, cols):
+    """es_op_add_layernorm = LayerNorm of the float32 sum x + sub: bitwise the
+    plain op on that sum (computed by torch in float32), within 2e-5 of the
+    float64 oracle on it, and unchanged when y aliases x or sub."""
+    torch = need_gpu()
+    say("add_layernorm", rows, cols)
+    rng = np.random.default_rng(rows * 7 + cols)
+    x = (rng.standard_normal((rows, cols)) * 0.7 + 0.2).astype(np.float32)
+    u = (rng.standard_normal((rows, cols)) * 1.3 - 0.1).astype(np.float32)
+    g = (1 + 0.1 * rng.standard_normal(cols)).astype(np.float32)
+    b = (0.1 * rng.standard_normal(cols)).astype(np.float32)
+    eps = 1e-5
+    dx, du, dg, db = (torch.from_numpy(a).cuda() for a in (x, u, g, b))
+    ld = cols + 4
+    y, yb = torch.empty_like(dx), torch.full((rows, ld), 0x1234, dtype=torch.int16, device="cuda")
+    layernorm(dx, dg, db, eps, y=y, ybf16=yb, sub=du)
+    s = dx + du
+    y0, yb0 = torch.empty_like(dx), torch.full((rows, ld), 0x1234, dtype=torch.int16, device="cuda")
+    layernorm(s, dg, db, eps, y=y0, ybf16=yb0)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y0) and torch.equal(yb, yb0)
+    s64 = x.astype(np.float32) + u.astype(np.float32)        # the float32 sum, as the kernel forms it
+    want = oracle.layer_norm(s64.astype(np.float64), g.astype(np.float64), b.astype(np.float64), eps)
+    assert np.max(np.abs(y.cpu().numpy() - want)) < 2e-5
+    for alias in ("x", "sub"):
+        ax, au = dx.clone(), du.clone()
+        layernorm(ax, dg, db, eps, y=ax if alias == "x" else au, sub=au)
+        torch.cuda.synchronize()
+        assert torch.equal(ax if alias == "x" else au, y0), alias
+    with pytest.raises(ValueError):
+        layernorm(dx, dg, db, eps, y=y, sub=du[:, :-4].contiguous())
+
+
 def _ragged_rows(lengths, n_heads, causal):
     """(element index of row start, n valid) for every (seq, head, row)."""
     out = []
