@@ -145,24 +145,29 @@ __global__ __launch_bounds__(64) void scores_mfma_kernel(const uint16_t *__restr
   const int64_t base = sbase[seq] + (int64_t)h * n * ld;
   const int fr = lane & 31, fh = lane >> 5;
   const int q = q0 + fr;
+  // rows are clamped to the sequence and the out-of-range fragments zeroed
+  // after the load, so no load sits behind a branch and they overlap
   bf16x8 qf[KS];
-  const uint16_t *Qr = qkv + (t0 + q) * ldq + h * DP + fh * 8;
+  const uint16_t *Qr = qkv + (t0 + min(q, n - 1)) * ldq + h * DP + fh * 8;
 #pragma unroll
-  for (int kk = 0; kk < KS; ++kk) qf[kk] = q < n ? ld_frag(Qr + kk * 16) : zero_frag();
+  for (int kk = 0; kk < KS; ++kk) qf[kk] = ld_frag(Qr + kk * 16);
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) qf[kk] = q < n ? qf[kk] : zero_frag();
   const int kend = causal ? min(n, q0 + kQTile) : n;
   float *Sr = S + base + (int64_t)q * ld;
   const int qlim = causal ? min(q + 1, n) : n;  // keys visible to this query row
   for (int k0 = 0; k0 < kend; k0 += 32) {
     const int k = k0 + fr;
-    const uint16_t *Kr = qkv + (t0 + k) * ldq + (n_heads + h) * DP + fh * 8;
+    const uint16_t *Kr = qkv + (t0 + min(k, n - 1)) * ldq + (n_heads + h) * DP + fh * 8;
+    bf16x8 kf[KS];
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) kf[kk] = ld_frag(Kr + kk * 16);
     f32x16 acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      const bf16x8 kf = k < n ? ld_frag(Kr + kk * 16) : zero_frag();
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], acc, 0, 0, 0);
-    }
+    for (int kk = 0; kk < KS; ++kk)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k < n ? kf[kk] : zero_frag(), qf[kk], acc, 0, 0, 0);
     if (q >= n) continue;
     // lane holds keys k0 + 8 g + 4 fh + (0..3) of query q
 #pragma unroll
@@ -185,34 +190,59 @@ __global__ __launch_bounds__(64) void scores_mfma_kernel(const uint16_t *__restr
 // sV[e * kVP + key].  A lane loads 4 keys x 8 dims (four coalesced 16-byte
 // reads along the key rows) and writes them as eight 8-byte rows of 4 keys,
 // so the MFMA fragments below read keys contiguously.  Keys >= n become 0.
+// Loading and storing are separate steps so that a kernel can put the loads
+// of a tile in flight together with its other loads before it waits.
 constexpr int kVP = 40;  // LDS pitch of a transposed row (32 keys + 8, keeps 16-byte reads aligned)
+
+template <int DP>
+struct VtTile {
+  static constexpr int OCT = DP / 8, UNITS = 8 * OCT, NU = (UNITS + 63) / 64;
+  uint4 r[NU][4];
+};
 
 // Keys at positions [0, np) come from rows Vp[0 .. np) (a shared prompt) and
 // keys at positions >= np from Vs[key - np]; np = 0 for a plain sequence.
+// Every lane reads a valid row (key clamped to n - 1, n >= 1) and store_vt
+// zeroes keys >= n, so the loads need no branches.
 template <int DP>
-__device__ __forceinline__ void stage_vt(uint16_t *__restrict__ sV, const uint16_t *__restrict__ Vp,
-                                         const uint16_t *__restrict__ Vs, int np, int ldq, int k0,
-                                         int n, int lane) {
-  constexpr int OCT = DP / 8;
+__device__ __forceinline__ void load_vt(VtTile<DP> &t, const uint16_t *__restrict__ Vp,
+                                        const uint16_t *__restrict__ Vs, int np, int ldq, int k0,
+                                        int n, int lane) {
+  using T = VtTile<DP>;
 #pragma unroll
-  for (int u = lane; u < 8 * OCT; u += 64) {
-    const int quad = u / OCT, oct = u % OCT;
-    uint4 r[4];
+  for (int i = 0; i < T::NU; ++i) {
+    const int u = (lane + 64 * i) % T::UNITS, quad = u / T::OCT, oct = u % T::OCT;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int key = k0 + 4 * quad + j;
-      const uint16_t *row = key < np ? Vp + (int64_t)key * ldq : Vs + (int64_t)(key - np) * ldq;
-      r[j] = key < n ? *reinterpret_cast<const uint4 *>(row + oct * 8) : make_uint4(0, 0, 0, 0);
+      const int key = k0 + 4 * quad + j, kc = min(key, n - 1);
+      const uint16_t *row = kc < np ? Vp + (int64_t)kc * ldq : Vs + (int64_t)(kc - np) * ldq;
+      t.r[i][j] = *reinterpret_cast<const uint4 *>(row + oct * 8);
     }
+  }
+}
+
+template <int DP>
+__device__ __forceinline__ void store_vt(uint16_t *__restrict__ sV, VtTile<DP> &t, int k0, int n,
+                                         int lane) {
+  using T = VtTile<DP>;
 #pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      const int c = d >> 1, sh = (d & 1) * 16;
-      auto pick = [&](const uint4 &x) {
-        const uint32_t w = c == 0 ? x.x : c == 1 ? x.y : c == 2 ? x.z : x.w;
-        return (w >> sh) & 0xffffu;
-      };
-      const uint2 w = make_uint2(pick(r[0]) | (pick(r[1]) << 16), pick(r[2]) | (pick(r[3]) << 16));
-      *reinterpret_cast<uint2 *>(sV + (oct * 8 + d) * kVP + 4 * quad) = w;
+  for (int i = 0; i < T::NU; ++i) {
+    const int u = lane + 64 * i, quad = (u % T::UNITS) / T::OCT, oct = u % T::OCT;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (k0 + 4 * quad + j >= n) t.r[i][j] = make_uint4(0, 0, 0, 0);
+    if (T::UNITS % 64 == 0 || u < T::UNITS) {
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        const int c = d >> 1, sh = (d & 1) * 16;
+        auto pick = [&](const uint4 &x) {
+          const uint32_t w = c == 0 ? x.x : c == 1 ? x.y : c == 2 ? x.z : x.w;
+          return (w >> sh) & 0xffffu;
+        };
+        const uint2 w = make_uint2(pick(t.r[i][0]) | (pick(t.r[i][1]) << 16),
+                                   pick(t.r[i][2]) | (pick(t.r[i][3]) << 16));
+        *reinterpret_cast<uint2 *>(sV + (oct * 8 + d) * kVP + 4 * quad) = w;
+      }
     }
   }
 }
@@ -247,8 +277,10 @@ __global__ __launch_bounds__(64) void pv_mfma_kernel(const uint16_t *__restrict_
     for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
   const int kend = causal ? min(n, q0 + kQTile) : n;
   for (int k0 = 0; k0 < kend; k0 += 32) {
+    VtTile<DP> vt;
+    load_vt<DP>(vt, V, V, 0, ldq, k0, n, lane);
     __syncthreads();
-    stage_vt<DP>(sV, V, V, 0, ldq, k0, n, lane);
+    store_vt<DP>(sV, vt, k0, n, lane);
     __syncthreads();
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
@@ -320,10 +352,15 @@ __global__ __launch_bounds__(64) void attn_fused_kernel(const uint16_t *__restri
   const int ntot = np + n;
   const int fr = lane & 31, fh = lane >> 5;
   const int q = q0 + fr;
+  // rows are clamped to the sequence and the out-of-range fragments zeroed
+  // after the load, so no load sits behind a branch: Q, and each tile's K and
+  // V, are in flight together
   bf16x8 qf[KS];
-  const uint16_t *Qr = qkv + (t0 + q) * ldq + h * DP + fh * 8;
+  const uint16_t *Qr = qkv + (t0 + min(q, n - 1)) * ldq + h * DP + fh * 8;
 #pragma unroll
-  for (int kk = 0; kk < KS; ++kk) qf[kk] = q < n ? ld_frag(Qr + kk * 16) : zero_frag();
+  for (int kk = 0; kk < KS; ++kk) qf[kk] = ld_frag(Qr + kk * 16);
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) qf[kk] = q < n ? qf[kk] : zero_frag();
   const uint16_t *Kb = qkv + t0 * ldq + (n_heads + h) * DP + fh * 8;
   const uint16_t *Kp = qkv + p0 * ldq + (n_heads + h) * DP + fh * 8;
   const uint16_t *V = qkv + t0 * ldq + (2 * n_heads + h) * DP;
@@ -340,18 +377,21 @@ __global__ __launch_bounds__(64) void attn_fused_kernel(const uint16_t *__restri
   const int qpos = np + q;
   const int kend = causal ? min(ntot, np + q0 + kQTile) : ntot;
   for (int k0 = 0; k0 < kend; k0 += 32) {
-    __syncthreads();
-    stage_vt<DP>(sV, Vp, V, np, ldq, k0, ntot, lane);
-    const int k = k0 + fr;
-    const uint16_t *Kr = PFX && k < np ? Kp + (int64_t)k * ldq : Kb + (int64_t)(k - np) * ldq;
+    const int k = k0 + fr, kc = min(k, ntot - 1);
+    const uint16_t *Kr = PFX && kc < np ? Kp + (int64_t)kc * ldq : Kb + (int64_t)(kc - np) * ldq;
+    bf16x8 kf[KS];
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) kf[kk] = ld_frag(Kr + kk * 16);
+    VtTile<DP> vt;
+    load_vt<DP>(vt, Vp, V, np, ldq, k0, ntot, lane);
     f32x16 s;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      const bf16x8 kf = k < ntot ? ld_frag(Kr + kk * 16) : zero_frag();
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s, 0, 0, 0);
-    }
+    for (int kk = 0; kk < KS; ++kk)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k < ntot ? kf[kk] : zero_frag(), qf[kk], s, 0, 0, 0);
+    __syncthreads();  // the previous tile's P.V reads of sV are done
+    store_vt<DP>(sV, vt, k0, ntot, lane);
     // the first tile shows every query key 0, so m_run is finite after it; a
     // later tile whose keys are all masked for a query leaves that query's
     // running max, sum and accumulator exactly unchanged (alpha = 1, p = 0)
