@@ -125,6 +125,8 @@ def main():
     ap.add_argument("--group", type=int, default=4,
                     help="planned batches packed into one pass through the layers "
                          "(es_set_batch_grouping)")
+    ap.add_argument("--memory", default="length_aware", choices=["length_aware", "fixed", "exact"],
+                    help="workspace memory mode (es_set_memory_mode)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the scoring path is "
@@ -158,6 +160,7 @@ def main():
     roff = np.concatenate([[0], np.cumsum(rlen)]).astype(np.int32)
     if not args.single_step:
         sc.reward_offset = sc.calibrate_offset(d_ref, roff)   # reference set averages zero
+    sc.set_memory_mode(args.memory)
     sc.set_grouping(args.group)
     sc.set_concurrency(args.in_flight)
     if cfg.bf16:
@@ -191,11 +194,13 @@ def main():
     for _ in range(max(1, args.warmup)):
         step()
     torch.cuda.synchronize()
+    sc.memory_stats(reset=True)
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    mem = sc.memory_stats()
     ms = (t1 - t0) * 1e3 / args.steps
     value = n / (ms / 1e3)
     assert torch.isfinite(out).all().item(), "non-finite rewards"
@@ -276,6 +281,12 @@ def main():
                                           "kernels": class_table(pc_other)}
         sc.set_attention(args.attention)
 
+    # the workspace the fixed mode would hold for the same settings
+    sc.set_memory_mode("fixed")
+    fixed_bytes = sc.memory_stats()["work_bytes"]
+    line_mem = {"mode": args.memory, "work_bytes": mem["work_bytes"],
+                "peak_work_bytes": mem["peak_work_bytes"], "fixed_mode_work_bytes": fixed_bytes,
+                "allocs_in_timed_steps": mem["allocs"], "alloc_ms_in_timed_steps": round(mem["alloc_ms"], 3)}
     line = {
         "metric": "sequences scored/sec on var-len batches",
         "value": round(value, 2),
@@ -304,6 +315,7 @@ def main():
                      "launches_per_step": launches,
                      "measured": f"HIP events around every launch over {prof_steps} steps with one "
                                  f"pass in flight ({ms_isolated:.2f} ms/step)"},
+        "memory": line_mem,
         "kernels": kernels,
         "variants": variants,
         "device": torch.cuda.get_device_name(0),

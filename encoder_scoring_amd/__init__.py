@@ -8,11 +8,13 @@ provides device memory and the current stream):
     Scorer.score_requests(d_ids, lengths)    plan + pack + score + scatter a stream
     plan_batches(lengths, max_tokens, c)     host DP batch planner
     pack_offsets(lengths, order, b, e)       packed offsets of one planned batch
+    plan_arena(bytes, first, last, align)    offsets of tensors with lifetimes (workspace planner)
 """
 from .api import (  # noqa: F401
     Scorer,
     plan_batches,
     pack_offsets,
+    plan_arena,
     layernorm,
     RaggedScores,
     softmax_ragged,

@@ -52,6 +52,23 @@ def plan_batches(lengths, max_tokens, batch_overhead, lib=None):
     return order, starts[: nb.value + 1].copy(), cost.value
 
 
+def plan_arena(nbytes, first_step, last_step, align=1, lib=None):
+    """Offsets of tensors with step lifetimes in one arena (es_plan_arena)
+    -> (offsets int64[n], total bytes)."""
+    lib = lib or _lib.load()
+    nbytes = np.ascontiguousarray(nbytes, dtype=np.int64)
+    first, last = as_i32(first_step), as_i32(last_step)
+    n = nbytes.size
+    if first.size != n or last.size != n:
+        raise ValueError("nbytes, first_step and last_step differ in length")
+    off = np.zeros(n, dtype=np.int64)
+    total = ctypes.c_int64()
+    p64 = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    check(lib, lib.es_plan_arena(p64(nbytes), i32p(first), i32p(last), n, int(align), p64(off),
+                                 ctypes.byref(total)))
+    return off, total.value
+
+
 def pack_offsets(lengths, order, begin, end, lib=None):
     lib = lib or _lib.load()
     lengths, order = as_i32(lengths), as_i32(order)
@@ -61,6 +78,12 @@ def pack_offsets(lengths, order, begin, end, lib=None):
 
 
 # ------------------------------------------------------------------ model
+
+class _MemoryStats(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("device_bytes", ctypes.c_int64),
+                ("work_bytes", ctypes.c_int64), ("peak_work_bytes", ctypes.c_int64),
+                ("allocs", ctypes.c_int64), ("alloc_ms", ctypes.c_double)]
+
 
 class Scorer:
     """A loaded scoring model on the current device.
@@ -184,6 +207,21 @@ class Scorer:
     def set_pruning(self, enabled):
         """Last layer on the last tokens only (default on; es_set_pruning)."""
         check(self.lib, self.lib.es_set_pruning(self.handle, 1 if enabled else 0))
+
+    MEMORY_MODES = {"fixed": 0, "length_aware": 1, "exact": 2}
+
+    def set_memory_mode(self, mode):
+        """"length_aware" (default), "fixed" or "exact" (es_set_memory_mode)."""
+        check(self.lib, self.lib.es_set_memory_mode(self.handle, self.MEMORY_MODES[mode]))
+
+    def memory_stats(self, reset=False):
+        """es_memory_stats as a dict (bytes, allocation count, ms)."""
+        st = _MemoryStats()
+        check(self.lib, self.lib.es_memory_stats(self.handle, ctypes.byref(st), 1 if reset else 0))
+        names = {v: k for k, v in self.MEMORY_MODES.items()}
+        return {"mode": names.get(st.mode, st.mode), "device_bytes": st.device_bytes,
+                "work_bytes": st.work_bytes, "peak_work_bytes": st.peak_work_bytes,
+                "allocs": st.allocs, "alloc_ms": st.alloc_ms}
 
     def set_attention(self, mode):
         """"unfused" (scores, softmax row reduction, P.V) or "fused" (one kernel)."""

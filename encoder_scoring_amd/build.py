@@ -18,8 +18,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libencscore.so")
 HOST_LIB = os.path.join(HERE, "libencscore_host.so")
 
-SOURCES = ["planner.cpp", "blob.cpp", "model.hip", "ops.hip", "rowops.hip", "gemm.hip", "attn.hip"]
-HOST_SOURCES = ["planner.cpp", "blob.cpp"]
+SOURCES = ["planner.cpp", "blob.cpp", "memplan.cpp", "model.hip", "ops.hip", "rowops.hip", "gemm.hip", "attn.hip"]
+HOST_SOURCES = ["planner.cpp", "blob.cpp", "memplan.cpp"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",

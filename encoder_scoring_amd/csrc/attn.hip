@@ -228,9 +228,11 @@ __device__ __forceinline__ void store_vt(uint16_t *__restrict__ sV, VtTile<DP> &
 #pragma unroll
   for (int i = 0; i < T::NU; ++i) {
     const int u = lane + 64 * i, quad = (u % T::UNITS) / T::OCT, oct = u % T::OCT;
+    if (k0 + 32 > n) {  // only the last tile of a sequence has keys to clear
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (k0 + 4 * quad + j >= n) t.r[i][j] = make_uint4(0, 0, 0, 0);
+      for (int j = 0; j < 4; ++j)
+        if (k0 + 4 * quad + j >= n) t.r[i][j] = make_uint4(0, 0, 0, 0);
+    }
     if (T::UNITS % 64 == 0 || u < T::UNITS) {
 #pragma unroll
       for (int d = 0; d < 8; ++d) {
@@ -376,40 +378,53 @@ __global__ __launch_bounds__(64) void attn_fused_kernel(const uint16_t *__restri
   float m_run = -INFINITY, l_run = 0.f;
   const int qpos = np + q;
   const int kend = causal ? min(ntot, np + q0 + kQTile) : ntot;
-  for (int k0 = 0; k0 < kend; k0 += 32) {
-    const int k = k0 + fr, kc = min(k, ntot - 1);
+  // K fragments and V rows of key tile k0 (branch-free, see above)
+  auto load_tile = [&](int k0, bf16x8 (&kf)[KS], VtTile<DP> &vt) {
+    const int kc = min(k0 + fr, ntot - 1);
     const uint16_t *Kr = PFX && kc < np ? Kp + (int64_t)kc * ldq : Kb + (int64_t)(kc - np) * ldq;
-    bf16x8 kf[KS];
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) kf[kk] = ld_frag(Kr + kk * 16);
-    VtTile<DP> vt;
     load_vt<DP>(vt, Vp, V, np, ldq, k0, ntot, lane);
+    // every load of the tile is issued before the first MFMA waits for K
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // One key tile: scores, online softmax, P.V.
+  auto process = [&](int k0, bf16x8 (&kf)[KS], VtTile<DP> &vt) {
+    // keys past the sequence hold the clamped row's (finite) K; their scores
+    // are replaced by -inf below, so the fragments need no clearing
     f32x16 s;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk)
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k < ntot ? kf[kk] : zero_frag(), qf[kk], s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], s, 0, 0, 0);
     __syncthreads();  // the previous tile's P.V reads of sV are done
     store_vt<DP>(sV, vt, k0, ntot, lane);
-    // the first tile shows every query key 0, so m_run is finite after it; a
-    // later tile whose keys are all masked for a query leaves that query's
-    // running max, sum and accumulator exactly unchanged (alpha = 1, p = 0)
-    float mx = -INFINITY;
+    // Masking only where a key of the tile can be invisible to a query of the
+    // tile: the sequence's last key tile and, causal, tiles reaching past the
+    // first query's position.  The first tile shows every query key 0, so
+    // m_run is finite after it; a later tile whose keys are all masked for a
+    // query leaves that query's running max, sum and accumulator exactly
+    // unchanged (alpha = 1, p = 0).
+    if (k0 + 32 > ntot || (causal && k0 + 31 > np + q0)) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = k0 + 8 * (r >> 2) + 4 * fh + (r & 3);
-      const bool ok = key < ntot && (!causal || key <= qpos);
-      s[r] = ok ? s[r] * sl2 : -INFINITY;
-      mx = fmaxf(mx, s[r]);
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + 8 * (r >> 2) + 4 * fh + (r & 3);
+        if (key >= ntot || (causal && key > qpos)) s[r] = -INFINITY;
+      }
     }
+    // the running max is kept in scaled units; scaling by sl2 > 0 commutes
+    // with the max, and each exponent is one fma: 2^(s sl2 - m)
+    float mx = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));  // the other 16 keys of this query
-    const float m_new = fmaxf(m_run, mx);
+    const float m_new = fmaxf(m_run, mx * sl2);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     float psum = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      s[r] = __builtin_amdgcn_exp2f(s[r] - m_new);
+      s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -m_new));
       psum += s[r];
     }
     l_run = l_run * alpha + psum;
@@ -434,6 +449,15 @@ __global__ __launch_bounds__(64) void attn_fused_kernel(const uint16_t *__restri
         acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, acc[t], 0, 0, 0);
       }
     }
+  };
+  // Each tile's K and V loads are in flight together; issuing the next
+  // tile's loads ahead as well (a second register set) was measured slower:
+  // the occupancy it costs outweighs the latency it hides.
+  for (int k0 = 0; k0 < kend; k0 += 32) {
+    bf16x8 kf[KS];
+    VtTile<DP> vt;
+    load_tile(k0, kf, vt);
+    process(k0, kf, vt);
   }
   if (q >= n) return;
   const float inv = 1.0f / (l_run + __shfl_xor(l_run, 32, kWave));

@@ -50,10 +50,15 @@ hipError_t launch_embed(bool w_bf16, bool act_bf16, bool ln, const int32_t *ids,
                         const float *b, float eps, float *x, void *xb, int ldb, int *flag,
                         hipStream_t st);
 // Row LayerNorm of x (of x + sub when sub is non-NULL, both [rows, cols]):
-// y fp32 [rows, cols] (nullable, may alias x or sub), yb [rows, ldb] (nullable).
+// y fp32 [rows, cols] (nullable, may alias x or sub), yb [rows, ldb] (nullable;
+// its columns [cols, pad_cols) are written with zeros, pad_cols <= ldb).
 hipError_t launch_layernorm(bool act_bf16, const float *x, const float *sub, const float *g,
                             const float *b, int64_t rows, int cols, float eps, float *y, void *yb,
-                            int ldb, hipStream_t st);
+                            int ldb, int pad_cols, hipStream_t st);
+// Zero bytes [c0_bytes, c1_bytes) of each of `rows` rows of ld_bytes (all
+// multiples of 4): the padding band of a K-padded GEMM operand.
+hipError_t launch_zero_cols(void *base, int64_t ld_bytes, int rows, int64_t c0_bytes,
+                            int64_t c1_bytes, hipStream_t st);
 // Ragged softmax over score blocks: S fp32 -> P (bf16 bits or fp32).
 hipError_t launch_softmax(bool p_bf16, const float *S, void *P, const Ragged &r, int n_heads,
                           bool causal, hipStream_t st);

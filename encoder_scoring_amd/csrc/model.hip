@@ -15,6 +15,7 @@
 // to a power of two >= 32 by inserting zero rows into W_qkv and zero columns
 // into W_o, which leaves every result unchanged.
 #include <algorithm>
+#include <chrono>
 #include <cinttypes>
 #include <cmath>
 #include <cstring>
@@ -24,6 +25,7 @@
 #include "blob.h"
 #include "common.h"
 #include "kernels.h"
+#include "memplan.h"
 
 namespace {
 
@@ -69,12 +71,20 @@ struct es_model {
   std::vector<DevLayer> layers;
   // workspaces: one per batch in flight (es_set_concurrency)
   struct Workspace {
-    int scale = 0;  // capacity in planned batches (tokens, sequences, score elements)
+    int scale = 0;  // fixed buffers: capacity in planned batches (tokens, sequences, score elements)
     float *x = nullptr, *y = nullptr, *S = nullptr;
     void *xb = nullptr, *qkv = nullptr, *ctx = nullptr, *hmid = nullptr, *Pb = nullptr;
     hipStream_t stream = nullptr;  // internal stream used when several batches are in flight
     hipEvent_t done = nullptr;
+    // length-aware memory: one arena; the tensors above point into it per pass
+    char *arena = nullptr;
+    int64_t arena_cap = 0;
+    int64_t call_need = 0, prev_call_need = 0;  // largest pass need of this / the last call
+    bool first_in_call = false;
   };
+  int mem_mode = 1;  // ES_MEM_FIXED / ES_MEM_LENGTH_AWARE / ES_MEM_EXACT (es_set_memory_mode)
+  int64_t work_allocs = 0, peak_work = 0;  // workspace / arena allocations, largest total held
+  double work_alloc_ms = 0.0;                // host time spent allocating them
   std::vector<Workspace> ws;  // allocated workspaces; the first `lanes` are used
   int lanes = 1;
   int group = 1;  // planned batches scored by one pass through the layers
@@ -115,6 +125,10 @@ es_status dalloc(es_model *m, void **p, size_t bytes) {
   m->device_bytes += (int64_t)bytes;
   e = hipMemset(*p, 0, bytes);
   if (e != hipSuccess) return fail(ES_ERR_HIP, "hipMemset failed: %s", hipGetErrorString(e));
+  // the fill may still be running on the null stream, which the internal
+  // (non-blocking) streams do not wait for
+  e = hipDeviceSynchronize();
+  if (e != hipSuccess) return fail(ES_ERR_HIP, "hipDeviceSynchronize failed: %s", hipGetErrorString(e));
   return ES_OK;
 }
 
@@ -199,15 +213,48 @@ int64_t qkv_row(int64_t r, const es_model *m) {
 }
 int64_t ctx_col(int64_t c, const es_model *m) { return (c / m->d) * m->dp + c % m->d; }
 
-// Activations and score buffers for one batch in flight (zero-filled once:
-// padding columns stay zero forever).
-// Activation and score buffers for `scale` planned batches of up to
-// max_tokens tokens each; a workspace that already holds buffers is resized.
-es_status alloc_workspace(es_model *m, es_model::Workspace &w, int scale) {
+double ms_since(const std::chrono::steady_clock::time_point &t0) {
+  return std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+}
+
+// Device bytes of all workspaces (fixed buffers or arenas).
+int64_t work_bytes(const es_model *m) {
+  int64_t b = 0;
+  for (const auto &w : m->ws) {
+    b += w.arena_cap;
+    if (w.scale > 0) {
+      const int act = m->bf16 ? 2 : 4;
+      const int64_t T = round_up(w.scale * m->max_tokens, 256), S = w.scale * m->score_cap;
+      b += T * (m->H * 8 + (int64_t)(m->Hp + m->Nqkv + m->Kc + m->Fp) * act) + S * (4 + act);
+    }
+  }
+  return b;
+}
+
+void free_fixed(es_model *m, es_model::Workspace &w) {
+  if (w.arena) return;  // the tensor pointers are views into the arena
   for (void *p : {(void *)w.x, (void *)w.y, (void *)w.S, w.xb, w.qkv, w.ctx, w.hmid, w.Pb}) dfree(m, p);
   w.x = w.y = w.S = nullptr;
   w.xb = w.qkv = w.ctx = w.hmid = w.Pb = nullptr;
   w.scale = 0;
+}
+
+void free_arena(es_model *m, es_model::Workspace &w) {
+  if (!w.arena) return;
+  dfree(m, w.arena);
+  w.arena = nullptr;
+  w.arena_cap = 0;
+  w.x = w.y = w.S = nullptr;
+  w.xb = w.qkv = w.ctx = w.hmid = w.Pb = nullptr;
+}
+
+// Activation and score buffers for `scale` planned batches of up to
+// max_tokens tokens each (fixed memory mode), zero-filled once so padding
+// columns stay zero; a workspace that already holds buffers is resized.
+es_status alloc_workspace(es_model *m, es_model::Workspace &w, int scale) {
+  const auto t0 = std::chrono::steady_clock::now();
+  free_arena(m, w);
+  free_fixed(m, w);
   const int act = m->bf16 ? 2 : 4;
   const int64_t T = round_up(scale * m->max_tokens, 256);
   const int64_t S = scale * m->score_cap;
@@ -221,7 +268,99 @@ es_status alloc_workspace(es_model *m, es_model::Workspace &w, int scale) {
   if ((s = dalloc(m, (void **)&w.S, S * 4)) != ES_OK) return s;
   if ((s = dalloc(m, &w.Pb, S * act)) != ES_OK) return s;
   w.scale = scale;
+  m->work_allocs += 8;
+  m->work_alloc_ms += ms_since(t0);
+  m->peak_work = std::max(m->peak_work, work_bytes(m));
   return ES_OK;
+}
+
+// ---- length-aware workspace (TurboTransformers review, Proposed method: a
+// sequence-length-aware allocator for variable-length inputs).  A pass's
+// intermediates are sized from its own token count and score blocks, and
+// placed in one arena per pass in flight by es_plan_arena's rule: tensors
+// whose steps do not meet share addresses.  Steps (one layer repeats 2..9;
+// x and xb carry across layers): 0 embedding, 1 pre-LN LayerNorm, 2 QKV GEMM,
+// 3 attention (scores, softmax, P.V or fused), 4 last-row gather, 5
+// attention-out GEMM, 6 its LayerNorm, 7 FFN1, 8 FFN2, 9 FFN LayerNorm,
+// 10 head.  Bytes shared over time hold any bit pattern, so the padding
+// columns of the K-padded GEMM inputs are written with zeros by their
+// producers every time (LayerNorm / embedding: xb past H; FFN1 computes its
+// zero padding columns past F; attention clears ctx past A dp).
+enum { kTX, kTXb, kTQkv, kTCtx, kTY, kTHmid, kTS, kTP, kTensors };
+constexpr int64_t kArenaAlign = 4096;
+constexpr int64_t kArenaChunk = (int64_t)16 << 20;
+
+std::vector<es::Usage> pass_usage(const es_model *m, int64_t rows, int64_t score_elems) {
+  const int64_t act = m->bf16 ? 2 : 4;
+  std::vector<es::Usage> u(kTensors);
+  u[kTX] = {rows * m->H * 4, 0, 10};
+  u[kTXb] = {rows * m->Hp * act, 0, 10};
+  u[kTQkv] = {rows * m->Nqkv * act, 2, 5};
+  u[kTCtx] = {rows * m->Kc * act, 3, 5};
+  u[kTY] = {rows * m->H * 4, 4, 9};
+  u[kTHmid] = {rows * m->Fp * act, 7, 8};
+  u[kTS] = {score_elems * 4, 3, 3};
+  u[kTP] = {score_elems * act, 3, 3};
+  return u;
+}
+
+// Point w's tensors at a pass of n_tokens tokens (and score_elems score
+// elements when the unfused attention runs).  Fixed mode: nothing to do.
+// Length-aware: the arena grows (once queued work is done, with 1/8
+// headroom, in 16 MiB steps) when this pass needs more, and at a call's first
+// pass it shrinks to the previous call's largest need (plus 1/8, in 16 MiB
+// steps) when it holds at least twice that.  Exact: a fresh arena of exactly
+// this pass's need.
+es_status bind_workspace(es_model *m, es_model::Workspace &w, int64_t n_tokens, int64_t score_elems,
+                         hipStream_t st) {
+  if (m->mem_mode == ES_MEM_FIXED) return ES_OK;
+  const int64_t rows = std::max<int64_t>(round_up(n_tokens, 256), 256);
+  std::vector<int64_t> off;
+  const int64_t need = es::plan_arena(pass_usage(m, rows, score_elems), kArenaAlign, off);
+  w.call_need = std::max(w.call_need, need);
+  int64_t want = 0;
+  if (m->mem_mode == ES_MEM_EXACT)
+    want = need;
+  else if (need > w.arena_cap)
+    want = round_up(need + need / 8, kArenaChunk);
+  else if (w.first_in_call && w.prev_call_need > 0) {
+    const int64_t target = round_up(std::max(w.prev_call_need, need) * 9 / 8, kArenaChunk);
+    if (2 * target <= w.arena_cap) want = target;
+  }
+  w.first_in_call = false;
+  if (want > 0) {
+    const auto t0 = std::chrono::steady_clock::now();
+    // earlier passes (this lane's, or a previous call's on another stream)
+    // may still use the old arena
+    HIP_TRY(hipDeviceSynchronize());
+    free_fixed(m, w);
+    free_arena(m, w);
+    es_status s = dalloc(m, (void **)&w.arena, (size_t)want);
+    if (s != ES_OK) return s;
+    w.arena_cap = want;
+    m->work_allocs += 1;
+    m->work_alloc_ms += ms_since(t0);
+    m->peak_work = std::max(m->peak_work, work_bytes(m));
+  }
+  char *a = w.arena;
+  w.x = reinterpret_cast<float *>(a + off[kTX]);
+  w.xb = a + off[kTXb];
+  w.qkv = a + off[kTQkv];
+  w.ctx = a + off[kTCtx];
+  w.y = reinterpret_cast<float *>(a + off[kTY]);
+  w.hmid = a + off[kTHmid];
+  w.S = reinterpret_cast<float *>(a + off[kTS]);
+  w.Pb = a + off[kTP];
+  return ES_OK;
+}
+
+// Start of a scoring call: each lane's shrink check looks at the last call.
+void begin_call(es_model *m) {
+  for (auto &w : m->ws) {
+    if (w.call_need > 0) w.prev_call_need = w.call_need;
+    w.call_need = 0;
+    w.first_in_call = true;
+  }
 }
 
 es_status build(const es::ParsedBlob &pb, int64_t max_tokens, int32_t max_seqs, es_model *m) {
@@ -273,14 +412,14 @@ es_status build(const es::ParsedBlob &pb, int64_t max_tokens, int32_t max_seqs, 
     if ((s = upload_vec(m, &D.ln1_g, L.ln1_g, m->H)) != ES_OK) return s;
     if ((s = upload_vec(m, &D.ln1_b, L.ln1_b, m->H)) != ES_OK) return s;
     if ((s = upload_matrix(m, &D.w_1, L.w_1, round_up(m->F, 256), m->Hp, id, id)) != ES_OK) return s;
-    if ((s = upload_vec(m, &D.b_1, L.b_1, m->F)) != ES_OK) return s;
+    if ((s = upload_vec(m, &D.b_1, L.b_1, m->Fp)) != ES_OK) return s;  // zero past F
     if ((s = upload_matrix(m, &D.w_2, L.w_2, round_up(m->H, 256), m->Fp, id, id)) != ES_OK) return s;
     if ((s = upload_vec(m, &D.b_2, L.b_2, m->H)) != ES_OK) return s;
     if ((s = upload_vec(m, &D.ln2_g, L.ln2_g, m->H)) != ES_OK) return s;
     if ((s = upload_vec(m, &D.ln2_b, L.ln2_b, m->H)) != ES_OK) return s;
   }
   m->ws.resize(1);
-  if ((s = alloc_workspace(m, m->ws[0], 1)) != ES_OK) return s;
+  if (m->mem_mode == ES_MEM_FIXED && (s = alloc_workspace(m, m->ws[0], 1)) != ES_OK) return s;
   if ((s = dalloc(m, (void **)&m->flag, 4)) != ES_OK) return s;
   HIP_TRY(hipEventCreateWithFlags(&m->meta_ev, hipEventDisableTiming));
   HIP_TRY(hipDeviceSynchronize());
@@ -297,6 +436,7 @@ struct BatchLayout {
   bool has_src = false, has_dest = false, has_prefix = false;
   int n = 0, n_items = 0, n_sm_items = 0, max_len = 0, n_tokens = 0;
   int64_t pairs = 0;  // visible (query, key) pairs summed over heads
+  int64_t score_elems = 0;  // ragged score-block elements (unfused attention)
 };
 
 size_t push_bytes(std::vector<uint8_t> &buf, const void *p, size_t bytes) {
@@ -336,6 +476,7 @@ es_status add_batch(es_model *m, const int32_t *h_off, int32_t n, const int32_t 
     sbase[i] = score;
     score += (int64_t)m->A * len * es::score_ld((int)len);
   }
+  L->score_elems = score;
   if (!plen && score > scale * m->score_cap)
     return fail(ES_ERR_CAPACITY, "batch needs %" PRId64 " score elements (capacity %" PRId64 ")",
                 score, m->score_cap);
@@ -511,9 +652,11 @@ struct Prof {
   }
 };
 
+// Nreal (if >= 0): output columns the method computes when N includes
+// padding columns (the FFN1 GEMM writes zeros there, for the next GEMM's K).
 es_status gemm(es_model *m, int cls, const void *A, int lda, const void *W, const float *bias,
                const float *res, void *out, int ldc, int M, int N, int K, int Kreal, int epi,
-               hipStream_t st) {
+               hipStream_t st, int Nreal = -1) {
   Prof p(m, st, cls);
   if (m->bf16)
     HIP_TRY(es::launch_gemm_bf16((const uint16_t *)A, lda, (const uint16_t *)W, bias, res, out, ldc,
@@ -524,15 +667,30 @@ es_status gemm(es_model *m, int cls, const void *A, int lda, const void *W, cons
     HIP_TRY(es::launch_gemm_f32((const float *)A, lda, (const float *)W, bias, res, (float *)out, ldc,
                                 M, N, K, epi, st));
   const double a = m->bf16 ? 2.0 : 4.0, out_b = (epi == es::kEpiBias || epi == es::kEpiGelu) ? a : 4.0;
-  p.done(2.0 * M * N * Kreal,
-         (double)M * Kreal * a + (double)N * Kreal * a + (double)M * N * out_b +
-             (epi == es::kEpiResidual ? 4.0 * M * N : 0.0) + 4.0 * N);
+  const double Nr = Nreal >= 0 ? Nreal : N;
+  p.done(2.0 * M * Nr * Kreal,
+         (double)M * Kreal * a + Nr * Kreal * a + (double)M * Nr * out_b +
+             (epi == es::kEpiResidual ? 4.0 * M * Nr : 0.0) + 4.0 * Nr);
   return ES_OK;
 }
 
 using Workspace = es_model::Workspace;
 
+es_status attention_heads(es_model *m, Workspace &w, const es::Ragged &r, int64_t pairs, hipStream_t st);
+
+// The heads write context columns [0, A dp); when Kc is larger the band
+// [A dp, Kc) is cleared (the output GEMM reads K = Kc, and with
+// length-aware memory those bytes may hold another tensor's bits).
 es_status attention(es_model *m, Workspace &w, const es::Ragged &r, int64_t pairs, hipStream_t st) {
+  es_status s = attention_heads(m, w, r, pairs, st);
+  if (s != ES_OK || m->Kc == m->A * m->dp) return s;
+  const int act = m->bf16 ? 2 : 4;
+  HIP_TRY(es::launch_zero_cols(w.ctx, (int64_t)m->Kc * act, r.n_tokens, (int64_t)m->A * m->dp * act,
+                               (int64_t)m->Kc * act, st));
+  return ES_OK;
+}
+
+es_status attention_heads(es_model *m, Workspace &w, const es::Ragged &r, int64_t pairs, hipStream_t st) {
   const float scale = 1.0f / std::sqrt((float)m->d);
   const double a = m->bf16 ? 2.0 : 4.0, T = r.n_tokens, Hd = (double)m->H;
   if (m->bf16 && (m->attn_mode == 1 || r.plen)) {  // shared prompts: fused only
@@ -565,7 +723,7 @@ es_status attention(es_model *m, Workspace &w, const es::Ragged &r, int64_t pair
 es_status layernorm(es_model *m, Workspace &w, const float *x, const float *g, const float *b, int T,
                     float *y, hipStream_t st, const float *sub = nullptr) {
   Prof p(m, st, ES_KC_LAYERNORM);
-  HIP_TRY(es::launch_layernorm(m->bf16, x, sub, g, b, T, m->H, m->eps, y, w.xb, m->Hp, st));
+  HIP_TRY(es::launch_layernorm(m->bf16, x, sub, g, b, T, m->H, m->eps, y, w.xb, m->Hp, m->Hp, st));
   const double a = m->bf16 ? 2.0 : 4.0;
   p.done((sub ? 9.0 : 8.0) * T * m->H, (double)T * m->H * (4.0 + a + (y ? 4.0 : 0.0) + (sub ? 4.0 : 0.0)));
   return ES_OK;
@@ -613,8 +771,8 @@ es_status forward(es_model *m, Workspace &w, const int32_t *d_ids, const es::Rag
         if ((s = gemm(m, ES_KC_OPROJ, w.ctx, m->Kc, D.w_o, D.b_o, w.x, w.y, H, T, H, m->Kc, Hd,
                       es::kEpiResidual, st)) != ES_OK) return s;
         if ((s = layernorm(m, w, w.y, D.ln1_g, D.ln1_b, T, w.x, st)) != ES_OK) return s;
-        if ((s = gemm(m, ES_KC_FFN1, w.xb, m->Hp, D.w_1, D.b_1, nullptr, w.hmid, m->Fp, T, F, m->Hp,
-                      H, es::kEpiGelu, st)) != ES_OK) return s;
+        if ((s = gemm(m, ES_KC_FFN1, w.xb, m->Hp, D.w_1, D.b_1, nullptr, w.hmid, m->Fp, T, m->Fp, m->Hp,
+                      H, es::kEpiGelu, st, F)) != ES_OK) return s;
         // the residual joins in the LayerNorm: the GEMM's output tiles then
         // end without a read (its grid is often a single wave of tiles, whose
         // epilogues all hit HBM at once), and LayerNorm streams it instead
@@ -628,8 +786,8 @@ es_status forward(es_model *m, Workspace &w, const int32_t *d_ids, const es::Rag
         if ((s = gemm(m, ES_KC_OPROJ, w.qkv, m->Nqkv, D.w_o, D.b_o, w.y, w.x, H, n, H, m->Kc, Hd,
                       es::kEpiResidual, st)) != ES_OK) return s;
         if ((s = layernorm(m, w, w.x, D.ln1_g, D.ln1_b, n, w.y, st)) != ES_OK) return s;
-        if ((s = gemm(m, ES_KC_FFN1, w.xb, m->Hp, D.w_1, D.b_1, nullptr, w.hmid, m->Fp, n, F, m->Hp,
-                      H, es::kEpiGelu, st)) != ES_OK) return s;
+        if ((s = gemm(m, ES_KC_FFN1, w.xb, m->Hp, D.w_1, D.b_1, nullptr, w.hmid, m->Fp, n, m->Fp, m->Hp,
+                      H, es::kEpiGelu, st, F)) != ES_OK) return s;
         if ((s = gemm(m, ES_KC_FFN2, w.hmid, m->Fp, D.w_2, D.b_2, w.y, w.x, H, n, H, m->Fp, F,
                       es::kEpiResidual, st)) != ES_OK) return s;
         if ((s = layernorm(m, w, w.x, D.ln2_g, D.ln2_b, n, w.x, st)) != ES_OK) return s;
@@ -643,8 +801,8 @@ es_status forward(es_model *m, Workspace &w, const int32_t *d_ids, const es::Rag
         if ((s = gemm(m, ES_KC_OPROJ, w.ctx, m->Kc, D.w_o, D.b_o, w.x, w.x, H, T, H, m->Kc, Hd,
                       es::kEpiResidual, st)) != ES_OK) return s;
         if ((s = layernorm(m, w, w.x, D.ln2_g, D.ln2_b, T, nullptr, st)) != ES_OK) return s;
-        if ((s = gemm(m, ES_KC_FFN1, w.xb, m->Hp, D.w_1, D.b_1, nullptr, w.hmid, m->Fp, T, F, m->Hp,
-                      H, es::kEpiGelu, st)) != ES_OK) return s;
+        if ((s = gemm(m, ES_KC_FFN1, w.xb, m->Hp, D.w_1, D.b_1, nullptr, w.hmid, m->Fp, T, m->Fp, m->Hp,
+                      H, es::kEpiGelu, st, F)) != ES_OK) return s;
         if ((s = gemm(m, ES_KC_FFN2, w.hmid, m->Fp, D.w_2, D.b_2, w.x, w.x, H, T, H, m->Fp, F,
                       es::kEpiResidual, st)) != ES_OK) return s;
       } else {
@@ -654,8 +812,8 @@ es_status forward(es_model *m, Workspace &w, const int32_t *d_ids, const es::Rag
         if ((s = gemm(m, ES_KC_OPROJ, w.qkv, m->Nqkv, D.w_o, D.b_o, w.y, w.y, H, n, H, m->Kc, Hd,
                       es::kEpiResidual, st)) != ES_OK) return s;
         if ((s = layernorm(m, w, w.y, D.ln2_g, D.ln2_b, n, nullptr, st)) != ES_OK) return s;
-        if ((s = gemm(m, ES_KC_FFN1, w.xb, m->Hp, D.w_1, D.b_1, nullptr, w.hmid, m->Fp, n, F, m->Hp,
-                      H, es::kEpiGelu, st)) != ES_OK) return s;
+        if ((s = gemm(m, ES_KC_FFN1, w.xb, m->Hp, D.w_1, D.b_1, nullptr, w.hmid, m->Fp, n, m->Fp, m->Hp,
+                      H, es::kEpiGelu, st, F)) != ES_OK) return s;
         if ((s = gemm(m, ES_KC_FFN2, w.hmid, m->Fp, D.w_2, D.b_2, w.y, w.x, H, n, H, m->Fp, F,
                       es::kEpiResidual, st)) != ES_OK) return s;
       }
@@ -742,7 +900,9 @@ extern "C" es_status es_model_info(const es_model *m, es_model_info_t *info) {
 es_status score_pass(es_model *m, Workspace &w, const int32_t *d_ids, const BatchLayout &L,
                      float *d_rewards, hipStream_t st) {
   const es::Ragged r = ragged_of(m, L);
+  const bool fused = m->bf16 && (m->attn_mode == 1 || L.has_prefix);
   es_status s;
+  if ((s = bind_workspace(m, w, L.n_tokens, fused ? 0 : L.score_elems, st)) != ES_OK) return s;
   if (m->prune && m->L > 0) {
     const LastView lv = last_view_of(m, L);
     if ((s = forward(m, w, d_ids, r, L.pairs, m->L, st, &lv)) != ES_OK) return s;
@@ -761,6 +921,7 @@ extern "C" es_status es_score_batch(es_model *m, const int32_t *d_token_ids, con
   es::Ragged r;
   int64_t pairs = 0;
   BatchLayout L;
+  begin_call(m);
   if ((s = prepare(m, h_offsets, n_seqs, st, &r, &pairs, &L)) != ES_OK) return s;
   if ((s = score_pass(m, m->ws[0], d_token_ids, L, d_rewards, st)) != ES_OK) return s;
   es::clear_error();
@@ -830,6 +991,7 @@ extern "C" es_status es_score_requests(es_model *m, const int32_t *d_token_ids,
   // order.  With k workspaces, group g runs on internal stream g % k, forked
   // from and joined back to the caller's stream.
   const int k = m->lanes;
+  begin_call(m);
   if (k > 1) {
     HIP_TRY(hipEventRecord(m->fork_ev, st));
     for (int i = 0; i < k; ++i) HIP_TRY(hipStreamWaitEvent(m->ws[i].stream, m->fork_ev, 0));
@@ -953,6 +1115,7 @@ extern "C" es_status es_score_best_of_n(es_model *m, const int32_t *d_token_ids,
   if ((s = upload_meta(m, st)) != ES_OK) return s;
   // a3..a13 per pass, passes in flight as in es_score_requests
   const int k = m->lanes;
+  begin_call(m);
   if (k > 1) {
     HIP_TRY(hipEventRecord(m->fork_ev, st));
     for (int i = 0; i < k; ++i) HIP_TRY(hipStreamWaitEvent(m->ws[i].stream, m->fork_ev, 0));
@@ -991,7 +1154,11 @@ extern "C" es_status es_forward_hidden(es_model *m, const int32_t *d_token_ids,
   hipStream_t st = static_cast<hipStream_t>(stream);
   es::Ragged r;
   int64_t pairs = 0;
-  if ((s = prepare(m, h_offsets, n_seqs, st, &r, &pairs)) != ES_OK) return s;
+  BatchLayout L;
+  begin_call(m);
+  if ((s = prepare(m, h_offsets, n_seqs, st, &r, &pairs, &L)) != ES_OK) return s;
+  const bool fused = m->bf16 && m->attn_mode == 1;
+  if ((s = bind_workspace(m, m->ws[0], L.n_tokens, fused ? 0 : L.score_elems, st)) != ES_OK) return s;
   if ((s = forward(m, m->ws[0], d_token_ids, r, pairs, n_layers, st)) != ES_OK) return s;
   HIP_TRY(hipMemcpyAsync(d_hidden, m->ws[0].x, (size_t)r.n_tokens * m->H * 4, hipMemcpyDeviceToDevice, st));
   return ES_OK;
@@ -1006,7 +1173,7 @@ extern "C" es_status es_set_concurrency(es_model *m, int32_t batches_in_flight) 
   while ((int)m->ws.size() < batches_in_flight) m->ws.emplace_back();
   for (int i = 0; i < batches_in_flight; ++i) {
     es_model::Workspace &w = m->ws[i];
-    if (w.scale < m->group) {
+    if (m->mem_mode == ES_MEM_FIXED && w.scale < m->group) {
       es_status s = alloc_workspace(m, w, m->group);
       if (s != ES_OK) return s;
     }
@@ -1025,10 +1192,45 @@ extern "C" es_status es_set_batch_grouping(es_model *m, int32_t batches_per_pass
   m->group = batches_per_pass;
   for (int i = 0; i < m->lanes; ++i) {
     es_model::Workspace &w = m->ws[i];
-    if (w.scale < m->group) {
+    if (m->mem_mode == ES_MEM_FIXED && w.scale < m->group) {
       es_status s = alloc_workspace(m, w, m->group);
       if (s != ES_OK) return s;
     }
+  }
+  return ES_OK;
+}
+
+extern "C" es_status es_set_memory_mode(es_model *m, int32_t mode) {
+  if (!m) return fail(ES_ERR_ARG, "model handle is NULL");
+  if (mode != ES_MEM_FIXED && mode != ES_MEM_LENGTH_AWARE && mode != ES_MEM_EXACT)
+    return fail(ES_ERR_ARG, "memory mode %d is not ES_MEM_FIXED, ES_MEM_LENGTH_AWARE or ES_MEM_EXACT", mode);
+  HIP_TRY(hipDeviceSynchronize());
+  m->mem_mode = mode;
+  for (int i = 0; i < (int)m->ws.size(); ++i) {
+    es_model::Workspace &w = m->ws[i];
+    free_arena(m, w);
+    free_fixed(m, w);
+    w.call_need = w.prev_call_need = 0;
+    if (mode == ES_MEM_FIXED && i < m->lanes) {
+      es_status s = alloc_workspace(m, w, m->group);
+      if (s != ES_OK) return s;
+    }
+  }
+  return ES_OK;
+}
+
+extern "C" es_status es_memory_stats(es_model *m, es_memory_stats_t *out, int32_t reset) {
+  if (!m || !out) return fail(ES_ERR_ARG, "NULL argument");
+  out->mode = m->mem_mode;
+  out->device_bytes = m->device_bytes;
+  out->work_bytes = work_bytes(m);
+  out->peak_work_bytes = std::max(m->peak_work, out->work_bytes);
+  out->allocs = m->work_allocs;
+  out->alloc_ms = m->work_alloc_ms;
+  if (reset) {
+    m->work_allocs = 0;
+    m->work_alloc_ms = 0.0;
+    m->peak_work = out->work_bytes;
   }
   return ES_OK;
 }

@@ -29,7 +29,7 @@ extern "C" es_status es_op_layernorm(const float *d_x, const float *d_gamma, con
   if (rows < 0 || cols < 4 || cols % 4 || cols > 8192 || (d_ybf16 && (ld_bf16 < cols || ld_bf16 % 4)))
     return fail(ES_ERR_ARG, "es_op_layernorm: rows=%" PRId64 " cols=%d ld_bf16=%d", rows, cols, ld_bf16);
   HIP_TRY(es::launch_layernorm(true, d_x, nullptr, d_gamma, d_beta, rows, cols, eps, d_y, d_ybf16,
-                               ld_bf16, static_cast<hipStream_t>(stream)));
+                               ld_bf16, cols, static_cast<hipStream_t>(stream)));
   return ES_OK;
 }
 
@@ -43,7 +43,7 @@ extern "C" es_status es_op_add_layernorm(const float *d_x, const float *d_sub, c
     return fail(ES_ERR_ARG, "es_op_add_layernorm: rows=%" PRId64 " cols=%d ld_bf16=%d", rows, cols,
                 ld_bf16);
   HIP_TRY(es::launch_layernorm(true, d_x, d_sub, d_gamma, d_beta, rows, cols, eps, d_y, d_ybf16,
-                               ld_bf16, static_cast<hipStream_t>(stream)));
+                               ld_bf16, cols, static_cast<hipStream_t>(stream)));
   return ES_OK;
 }
 

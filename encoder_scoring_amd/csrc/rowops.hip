@@ -79,7 +79,7 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float *x, const fl
                                                         const float *__restrict__ g,
                                                         const float *__restrict__ b, int64_t rows,
                                                         int cols, float eps, float *y, OutB *yb,
-                                                        int ldb) {
+                                                        int ldb, int padc4) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
   if (row >= rows) return;
@@ -102,8 +102,20 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float *x, const fl
     if (c4 < c4n) {
       if (y) store4(y + row * cols + 4 * c4, v[j]);
       if (yb) store4(yb + row * ldb + 4 * c4, v[j]);
+    } else if (yb && c4 < padc4) {  // zero padding columns of the GEMM input
+      store4(yb + row * ldb + 4 * c4, make_float4(0.f, 0.f, 0.f, 0.f));
     }
   }
+}
+
+// Zero `words` 4-byte words at the start of each of `rows` rows (stride ld
+// words): the padding band of a K-padded GEMM operand.  One wavefront per row.
+__global__ __launch_bounds__(256) void zero_cols_kernel(char *base, int64_t ld, int rows, int words) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  uint32_t *p = reinterpret_cast<uint32_t *>(base) + (int64_t)row * ld;
+  for (int i = lane; i < words; i += kWave) p[i] = 0u;
 }
 
 // Token t of the packed batch belongs to sequence s; its id is read at
@@ -119,7 +131,7 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t *__restrict__ 
                                                     const float *__restrict__ g,
                                                     const float *__restrict__ b, float eps,
                                                     float *__restrict__ x, OutB *__restrict__ xb,
-                                                    int ldb, int *flag) {
+                                                    int ldb, int padc4, int *flag) {
   const int lane = threadIdx.x & (kWave - 1);
   const int t = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -152,6 +164,8 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t *__restrict__ 
     if (c4 < c4n) {
       store4(x + (int64_t)t * H + 4 * c4, v[j]);
       if (LN) store4(xb + (int64_t)t * ldb + 4 * c4, v[j]);
+    } else if (LN && c4 < padc4) {  // zero padding columns of the GEMM input
+      store4(xb + (int64_t)t * ldb + 4 * c4, make_float4(0.f, 0.f, 0.f, 0.f));
     }
   }
 }
@@ -308,20 +322,34 @@ hipError_t dispatch_nc(int cols, F &&f) {
 
 hipError_t launch_layernorm(bool act_bf16, const float *x, const float *sub, const float *g,
                             const float *b, int64_t rows, int cols, float eps, float *y, void *yb,
-                            int ldb, hipStream_t st) {
+                            int ldb, int pad_cols, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
+  if (pad_cols < cols || pad_cols % 4 || (yb && pad_cols > ldb) ||
+      pad_cols > 4 * kWave * ((cols / 4 + kWave - 1) / kWave))
+    return hipErrorInvalidValue;
+  const int padc4 = pad_cols / 4;
   const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)), block(256);
   return dispatch_nc(cols, [&](auto nc) {
     constexpr int NC = decltype(nc)::value;
     if (act_bf16) {
       auto k = sub ? layernorm_kernel<NC, uint16_t, true> : layernorm_kernel<NC, uint16_t, false>;
-      k<<<grid, block, 0, st>>>(x, sub, g, b, rows, cols, eps, y, (uint16_t *)yb, ldb);
+      k<<<grid, block, 0, st>>>(x, sub, g, b, rows, cols, eps, y, (uint16_t *)yb, ldb, padc4);
     } else {
       auto k = sub ? layernorm_kernel<NC, float, true> : layernorm_kernel<NC, float, false>;
-      k<<<grid, block, 0, st>>>(x, sub, g, b, rows, cols, eps, y, (float *)yb, ldb);
+      k<<<grid, block, 0, st>>>(x, sub, g, b, rows, cols, eps, y, (float *)yb, ldb, padc4);
     }
     return hipGetLastError();
   });
+}
+
+hipError_t launch_zero_cols(void *base, int64_t ld_bytes, int rows, int64_t c0_bytes,
+                            int64_t c1_bytes, hipStream_t st) {
+  if (rows <= 0 || c1_bytes <= c0_bytes) return hipSuccess;
+  if (c0_bytes % 4 || c1_bytes % 4 || ld_bytes % 4 || c1_bytes > ld_bytes) return hipErrorInvalidValue;
+  const int words = (int)((c1_bytes - c0_bytes) / 4);
+  const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)), block(256);
+  zero_cols_kernel<<<grid, block, 0, st>>>(static_cast<char *>(base) + c0_bytes, ld_bytes / 4, rows, words);
+  return hipGetLastError();
 }
 
 hipError_t launch_embed(bool w_bf16, bool act_bf16, bool ln, const int32_t *ids, const Ragged &r,
@@ -337,11 +365,12 @@ hipError_t launch_embed(bool w_bf16, bool act_bf16, bool ln, const int32_t *ids,
       auto k = ln ? embed_kernel<NC, uint16_t, true, uint16_t> : embed_kernel<NC, uint16_t, false, uint16_t>;
       k<<<grid, block, 0, st>>>(ids, r.off, r.src, r.plen, r.n_seqs, r.n_tokens, (const uint16_t *)tok,
                                 (const uint16_t *)pos, vocab, H, g, b, eps, x, (uint16_t *)xb, ldb,
-                                flag);
+                                ldb / 4, flag);
     } else {
       auto k = ln ? embed_kernel<NC, float, true, float> : embed_kernel<NC, float, false, float>;
       k<<<grid, block, 0, st>>>(ids, r.off, r.src, r.plen, r.n_seqs, r.n_tokens, (const float *)tok,
-                                (const float *)pos, vocab, H, g, b, eps, x, (float *)xb, ldb, flag);
+                                (const float *)pos, vocab, H, g, b, eps, x, (float *)xb, ldb,
+                                ldb / 4, flag);
     }
     return hipGetLastError();
   });

@@ -220,6 +220,48 @@ es_status es_forward_hidden(es_model *m, const int32_t *d_token_ids, const int32
 es_status es_set_concurrency(es_model *m, int32_t batches_in_flight);
 
 /*
+ * es_set_memory_mode -- where the intermediates of a pass (residual stream,
+ * GEMM inputs, Q|K|V, context, FFN middle, score blocks) live
+ * (TurboTransformers review, Proposed method: a sequence-length-aware
+ * allocator for variable-length inputs, balancing footprint against
+ * allocation cost):
+ *   ES_MEM_LENGTH_AWARE (default): per pass, sizes from the pass's own token
+ *     count and score blocks, placed by es_plan_arena (tensors whose steps do
+ *     not overlap share bytes) in one arena per pass in flight.  An arena
+ *     grows when a pass needs more (the host waits for queued work first;
+ *     1/8 headroom, 16 MiB steps) and, at a call's first pass, shrinks to the
+ *     previous call's largest need (same rounding) if it holds at least
+ *     twice that.
+ *   ES_MEM_FIXED: one workspace per pass in flight, allocated up front for
+ *     max_tokens x batches_per_pass tokens and worst-case score blocks; no
+ *     allocation while scoring.
+ *   ES_MEM_EXACT: per pass, an arena of exactly that pass's need, replacing
+ *     the previous one after the host waits for the device -- the smallest
+ *     footprint at the largest allocation cost (for comparison).
+ * Rewards are bitwise the same in every mode.  Synchronises the device.
+ * Errors: ES_ERR_ARG (unknown mode), ES_ERR_HIP.
+ */
+enum { ES_MEM_FIXED = 0, ES_MEM_LENGTH_AWARE = 1, ES_MEM_EXACT = 2 };
+es_status es_set_memory_mode(es_model *m, int32_t mode);
+
+/* Workspace memory of a handle (es_memory_stats). */
+typedef struct {
+  int32_t mode;            /* ES_MEM_*                                            */
+  int64_t device_bytes;    /* device memory held now: weights, workspaces, arenas */
+  int64_t work_bytes;      /* of which workspaces / arenas                        */
+  int64_t peak_work_bytes; /* largest work_bytes since load or the last reset     */
+  int64_t allocs;          /* workspace / arena allocations since then            */
+  double alloc_ms;         /* host time spent in them (incl. waiting for a lane)  */
+} es_memory_stats_t;
+
+/*
+ * es_memory_stats -- fill *out; reset != 0 then zeroes the allocation count
+ * and time and restarts the peak from the current size.  Host only (no
+ * synchronisation).  Errors: ES_ERR_ARG.
+ */
+es_status es_memory_stats(es_model *m, es_memory_stats_t *out, int32_t reset);
+
+/*
  * es_set_pruning -- last-layer pruning for the scoring entry points (default
  * on).  The reward reads only the final state of each sequence's last token
  * ("Learning to summarize from human feedback", Method adaptation: the
@@ -308,6 +350,20 @@ es_status es_plan_batches(const int32_t *lengths, int32_t n, int64_t max_tokens,
  */
 es_status es_pack_offsets(const int32_t *lengths, const int32_t *order, int32_t begin,
                           int32_t end, int32_t *offsets);
+
+/*
+ * es_plan_arena -- host-only offset planning for tensors with lifetimes, the
+ * placement rule of ES_MEM_LENGTH_AWARE: record i holds bytes[i] (>= 0) and
+ * is used from step first_step[i] to last_step[i] (inclusive).  Records are
+ * placed largest first (equal sizes: lower index first), each at the lowest
+ * offset, a multiple of align (a power of two), where its bytes (rounded up
+ * to align) overlap no placed record whose step interval meets its own.
+ * offsets[i] receives the offset (0 for empty records), *total the arena size
+ * max(offset + rounded bytes).  Errors: ES_ERR_ARG (NULL, n < 0, bad align,
+ * negative bytes, first_step > last_step).
+ */
+es_status es_plan_arena(const int64_t *bytes, const int32_t *first_step, const int32_t *last_step,
+                        int32_t n, int64_t align, int64_t *offsets, int64_t *total);
 
 /* ------------------------------------------------------- single-kernel ops */
 /*

@@ -11,7 +11,8 @@ import numpy as np
 import pytest
 
 import oracle
-from encoder_scoring_amd import _lib, blob, pack_offsets, plan_batches
+from oracle import memplan
+from encoder_scoring_amd import _lib, blob, pack_offsets, plan_arena, plan_batches
 from encoder_scoring_amd._lib import EncScoreError
 from synth import CONFIGS, get_config, make_requests, make_weights
 from synth.configs import ORDERED
@@ -104,6 +105,60 @@ def test_planner_empty_and_null():
 def test_pack_offsets_errors():
     with pytest.raises(EncScoreError):
         pack_offsets([1, 2], [0, 1], 2, 1)
+
+
+# ------------------------------------------------------------------ arena planner
+
+def test_plan_arena_matches_oracle_random():
+    """es_plan_arena places exactly as the oracle's largest-first lowest-fit
+    rule, validly, and never below the brute-force optimum (n <= 6)."""
+    rng = np.random.default_rng(17)
+    for trial in range(400):
+        n = int(rng.integers(0, 12))
+        nb = [int(x) for x in rng.integers(0, 50, size=n) * int(rng.choice([1, 3, 1000]))]
+        f = [int(x) for x in rng.integers(0, 10, size=n)]
+        l = [a + int(rng.integers(0, 5)) for a in f]
+        align = int(rng.choice([1, 64, 4096]))
+        off, total = plan_arena(nb, f, l, align)
+        o_off, o_total = memplan.greedy_by_size(nb, f, l, align)
+        assert list(off) == o_off and total == o_total, (nb, f, l, align)
+        assert memplan.valid(nb, f, l, list(off), align)
+        assert total >= memplan.lower_bound(nb, f, l, align)
+        if n <= 6:
+            assert total >= memplan.optimum(nb, f, l, align)
+
+
+def test_plan_arena_on_a_pass_of_the_encoder():
+    """The workspace records of a BERT-base pass (16384 rows, fused attention):
+    x, xb, qkv, ctx, y, hmid; the plan reaches the bytes alive at the
+    attention-out GEMM (x + xb + qkv + ctx + y), the lower bound."""
+    rows, H, act = 16384, 768, 2
+    nb = [rows * H * 4, rows * H * act, rows * 3 * H * act, rows * H * act, rows * H * 4,
+          rows * 4 * H * act, 0, 0]
+    f = [0, 0, 2, 3, 4, 7, 3, 3]
+    l = [10, 10, 5, 5, 9, 8, 3, 3]
+    off, total = plan_arena(nb, f, l, 4096)
+    assert memplan.valid(nb, f, l, list(off), 4096)
+    assert total == memplan.lower_bound(nb, f, l, 4096) == rows * H * (4 + 2 + 6 + 2 + 4)
+    assert total < sum(nb)
+
+
+def test_plan_arena_errors():
+    with pytest.raises(EncScoreError):
+        plan_arena([10], [3], [2])            # first step after last
+    with pytest.raises(EncScoreError):
+        plan_arena([-1], [0], [0])            # negative size
+    with pytest.raises(EncScoreError):
+        plan_arena([10], [0], [0], align=48)  # not a power of two
+    off, total = plan_arena([], [], [])
+    assert off.size == 0 and total == 0
+
+
+def test_host_only_build_exports_the_arena_planner(tmp_path):
+    from encoder_scoring_amd import build
+    lib = _lib.load_host(build.build_host())
+    off, total = plan_arena([5, 7], [0, 1], [1, 2], 4, lib=lib)
+    assert total == 16 and memplan.valid([5, 7], [0, 1], [1, 2], list(off), 4)
 
 
 # ------------------------------------------------------------------ blob
