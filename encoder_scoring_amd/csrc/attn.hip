@@ -330,82 +330,51 @@ __global__ __launch_bounds__(64) void pv_mfma_kernel(const uint16_t *__restrict_
 // and reading the transposed V tile in the same order (two 8-byte LDS reads).
 // The contraction is order-free, so the result equals softmax(S) V up to
 // rounding.
-template <int DP, bool PFX>
-__global__ __launch_bounds__(64) void attn_fused_kernel(const uint16_t *__restrict__ qkv, int ldq,
-                                                        int n_heads, float scale, int causal,
-                                                        const int32_t *__restrict__ off,
-                                                        const int32_t *__restrict__ items,
-                                                        const int32_t *__restrict__ pref,
-                                                        const int32_t *__restrict__ plen,
-                                                        uint16_t *__restrict__ ctx, int ldc) {
-  constexpr int KS = DP / 16, NT = DP / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t sV[DP * kVP];
-  const int item = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
-  const int seq = items[2 * item], q0 = items[2 * item + 1];
-  const int64_t t0 = off[seq];
-  const int n = off[seq + 1] - (int)t0;
-  // With a shared prompt of np tokens at rows p0.., key position j < np is
-  // row p0 + j and position j >= np is the sequence's own row t0 + j - np;
-  // query q (own token q) sits at position np + q.  Key tiles stay aligned to
-  // position 0, so every query sees the same tiles, in the same order, as in
-  // the prompt + continuation laid out as one sequence.
-  const int np = PFX ? plen[seq] : 0;
-  const int64_t p0 = PFX ? pref[seq] : 0;
-  const int ntot = np + n;
-  const int fr = lane & 31, fh = lane >> 5;
-  const int q = q0 + fr;
-  // rows are clamped to the sequence and the out-of-range fragments zeroed
-  // after the load, so no load sits behind a branch: Q, and each tile's K and
-  // V, are in flight together
-  bf16x8 qf[KS];
-  const uint16_t *Qr = qkv + (t0 + min(q, n - 1)) * ldq + h * DP + fh * 8;
-#pragma unroll
-  for (int kk = 0; kk < KS; ++kk) qf[kk] = ld_frag(Qr + kk * 16);
-#pragma unroll
-  for (int kk = 0; kk < KS; ++kk) qf[kk] = q < n ? qf[kk] : zero_frag();
-  const uint16_t *Kb = qkv + t0 * ldq + (n_heads + h) * DP + fh * 8;
-  const uint16_t *Kp = qkv + p0 * ldq + (n_heads + h) * DP + fh * 8;
-  const uint16_t *V = qkv + t0 * ldq + (2 * n_heads + h) * DP;
-  const uint16_t *Vp = qkv + p0 * ldq + (2 * n_heads + h) * DP;
+//
+// The per-tile arithmetic of one wavefront's 32 queries lives in QueryTile,
+// shared by the one-wavefront kernel (short sequences) and the four-wavefront
+// kernel (long sequences, K and V staged once per block): a query's result
+// does not depend on which kernel ran it.
+template <int DP>
+struct QueryTile {
+  static constexpr int KS = DP / 16, NT = DP / 32;
   f32x16 acc[NT];
+  float m_run, l_run;
+  int q0, fr, fh;
+
+  __device__ __forceinline__ void init(int q0_, int lane) {
+    q0 = q0_;
+    fr = lane & 31;
+    fh = lane >> 5;
+    m_run = -INFINITY;
+    l_run = 0.f;
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
-  // scores are kept in base 2: s log2(e) / sqrt(d), so every probability is
-  // one v_exp_f32 (2^x) -- exp(x) = 2^(x log2 e), the same softmax
-  const float sl2 = scale * 1.44269504088896340736f;
-  float m_run = -INFINITY, l_run = 0.f;
-  const int qpos = np + q;
-  const int kend = causal ? min(ntot, np + q0 + kQTile) : ntot;
-  // K fragments and V rows of key tile k0 (branch-free, see above)
-  auto load_tile = [&](int k0, bf16x8 (&kf)[KS], VtTile<DP> &vt) {
-    const int kc = min(k0 + fr, ntot - 1);
-    const uint16_t *Kr = PFX && kc < np ? Kp + (int64_t)kc * ldq : Kb + (int64_t)(kc - np) * ldq;
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) kf[kk] = ld_frag(Kr + kk * 16);
-    load_vt<DP>(vt, Vp, V, np, ldq, k0, ntot, lane);
-    // every load of the tile is issued before the first MFMA waits for K
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  // One key tile: scores, online softmax, P.V.
-  auto process = [&](int k0, bf16x8 (&kf)[KS], VtTile<DP> &vt) {
-    // keys past the sequence hold the clamped row's (finite) K; their scores
-    // are replaced by -inf below, so the fragments need no clearing
+      for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
+  }
+  // S^T tile of this wavefront's queries against 32 keys.
+  __device__ __forceinline__ f32x16 scores(const bf16x8 (&kf)[KS], const bf16x8 (&qf)[KS]) const {
     f32x16 s;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk)
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], s, 0, 0, 0);
-    __syncthreads();  // the previous tile's P.V reads of sV are done
-    store_vt<DP>(sV, vt, k0, ntot, lane);
-    // Masking only where a key of the tile can be invisible to a query of the
-    // tile: the sequence's last key tile and, causal, tiles reaching past the
-    // first query's position.  The first tile shows every query key 0, so
-    // m_run is finite after it; a later tile whose keys are all masked for a
-    // query leaves that query's running max, sum and accumulator exactly
-    // unchanged (alpha = 1, p = 0).
+    for (int kk = 0; kk < KS; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], s, 0, 0, 0);
+    return s;
+  }
+  // Online-softmax update with key tile k0: s becomes the tile's
+  // probabilities (unnormalised), the accumulator is rescaled.
+  // Masking only where a key of the tile can be invisible to a query of the
+  // tile: the sequence's last key tile and, causal, tiles reaching past the
+  // first query's position.  The first tile shows every query key 0, so
+  // m_run is finite after it; a later tile whose keys are all masked for a
+  // query leaves that query's running max, sum and accumulator exactly
+  // unchanged (alpha = 1, p = 0).  Scores are kept in base 2, s log2(e) /
+  // sqrt(d) (sl2), so every probability is one v_exp_f32; the running max is
+  // kept in scaled units (scaling by sl2 > 0 commutes with the max) and each
+  // exponent is one fma: 2^(s sl2 - m).
+  __device__ __forceinline__ void update(f32x16 &s, int k0, int ntot, int np, bool causal, float sl2) {
+    const int qpos = np + q0 + fr;
     if (k0 + 32 > ntot || (causal && k0 + 31 > np + q0)) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -413,8 +382,6 @@ __global__ __launch_bounds__(64) void attn_fused_kernel(const uint16_t *__restri
         if (key >= ntot || (causal && key > qpos)) s[r] = -INFINITY;
       }
     }
-    // the running max is kept in scaled units; scaling by sl2 > 0 commutes
-    // with the max, and each exponent is one fma: 2^(s sl2 - m)
     float mx = s[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
@@ -433,12 +400,14 @@ __global__ __launch_bounds__(64) void attn_fused_kernel(const uint16_t *__restri
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[t][r] *= alpha;
-    __syncthreads();
+  }
+  // ctx^T += V^T P^T with the tile's V transposed in LDS (sV).
+  __device__ __forceinline__ void pv(const f32x16 &p, const uint16_t *sV) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       bf16x8 pf;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) pf[j] = (__bf16)s[8 * kk + j];
+      for (int j = 0; j < 8; ++j) pf[j] = (__bf16)p[8 * kk + j];
       const int c0 = 16 * kk + 4 * fh;  // tile keys of slots 0..3; slots 4..7 are c0 + 8
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
@@ -449,28 +418,177 @@ __global__ __launch_bounds__(64) void attn_fused_kernel(const uint16_t *__restri
         acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, acc[t], 0, 0, 0);
       }
     }
-  };
+  }
+  // Normalised context of the wavefront's valid queries (query < n).
+  __device__ __forceinline__ void store(uint16_t *ctx, int ldc, int64_t t0, int n, int h) {
+    const int q = q0 + fr;
+    const float inv = 1.0f / (l_run + __shfl_xor(l_run, 32, kWave));
+    if (q >= n) return;
+    uint16_t *Cr = ctx + (t0 + q) * ldc + h * DP;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        uint2 u;
+        u.x = f2bf2(acc[t][4 * g] * inv, acc[t][4 * g + 1] * inv);
+        u.y = f2bf2(acc[t][4 * g + 2] * inv, acc[t][4 * g + 3] * inv);
+        *reinterpret_cast<uint2 *>(Cr + t * 32 + 8 * g + 4 * fh) = u;
+      }
+  }
+};
+
+// Key and query rows of a (sequence, head): with a shared prompt of np tokens
+// at rows p0.., key position j < np is row p0 + j and position j >= np is the
+// sequence's own row t0 + j - np; query q (own token q) sits at position
+// np + q.  Key tiles stay aligned to position 0, so every query sees the same
+// tiles, in the same order, as in the prompt + continuation laid out as one
+// sequence.  Rows are clamped to the sequence, so no load sits behind a
+// branch; values past the sequence are masked (K), zeroed (V) or never stored
+// (queries).
+struct HeadRows {
+  const uint16_t *Qs, *Ks, *Kp, *Vs, *Vp;  // own rows (t0) and prompt rows (p0), this head
+  int n, np, ntot;
+  int64_t t0;
+  int ldq;
+  __device__ __forceinline__ const uint16_t *key_row(int k) const {  // k < ntot
+    return k < np ? Kp + (int64_t)k * ldq : Ks + (int64_t)(k - np) * ldq;
+  }
+};
+
+template <int DP, bool PFX>
+__device__ __forceinline__ HeadRows head_rows(const uint16_t *qkv, int ldq, int n_heads, int h, int seq,
+                                              const int32_t *off, const int32_t *pref,
+                                              const int32_t *plen) {
+  HeadRows r;
+  r.t0 = off[seq];
+  r.n = off[seq + 1] - (int)r.t0;
+  r.np = PFX ? plen[seq] : 0;
+  const int64_t p0 = PFX ? pref[seq] : 0;
+  r.ntot = r.np + r.n;
+  r.ldq = ldq;
+  r.Qs = qkv + r.t0 * ldq + h * DP;
+  r.Ks = qkv + r.t0 * ldq + (n_heads + h) * DP;
+  r.Kp = qkv + p0 * ldq + (n_heads + h) * DP;
+  r.Vs = qkv + r.t0 * ldq + (2 * n_heads + h) * DP;
+  r.Vp = qkv + p0 * ldq + (2 * n_heads + h) * DP;
+  return r;
+}
+
+template <int DP>
+__device__ __forceinline__ void load_q(bf16x8 (&qf)[DP / 16], const HeadRows &hr, int q, int fh) {
+  const uint16_t *Qr = hr.Qs + (int64_t)min(q, hr.n - 1) * hr.ldq + fh * 8;
+#pragma unroll
+  for (int kk = 0; kk < DP / 16; ++kk) qf[kk] = ld_frag(Qr + kk * 16);
+#pragma unroll
+  for (int kk = 0; kk < DP / 16; ++kk) qf[kk] = q < hr.n ? qf[kk] : zero_frag();
+}
+
+// One wavefront per (32-query tile, head): K fragments straight from the
+// packed rows into registers, V transposed through LDS.
+template <int DP, bool PFX>
+__global__ __launch_bounds__(64) void attn_fused_kernel(const uint16_t *__restrict__ qkv, int ldq,
+                                                        int n_heads, float scale, int causal,
+                                                        const int32_t *__restrict__ off,
+                                                        const int32_t *__restrict__ items,
+                                                        const int32_t *__restrict__ pref,
+                                                        const int32_t *__restrict__ plen,
+                                                        uint16_t *__restrict__ ctx, int ldc) {
+  constexpr int KS = DP / 16;
+  __shared__ __attribute__((aligned(16))) uint16_t sV[DP * kVP];
+  const int item = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+  const int seq = items[2 * item], q0 = items[2 * item + 1];
+  const HeadRows hr = head_rows<DP, PFX>(qkv, ldq, n_heads, h, seq, off, pref, plen);
+  QueryTile<DP> qt;
+  qt.init(q0, lane);
+  bf16x8 qf[KS];
+  load_q<DP>(qf, hr, q0 + qt.fr, qt.fh);
+  const float sl2 = scale * 1.44269504088896340736f;
+  const int kend = causal ? min(hr.ntot, hr.np + q0 + kQTile) : hr.ntot;
   // Each tile's K and V loads are in flight together; issuing the next
   // tile's loads ahead as well (a second register set) was measured slower:
   // the occupancy it costs outweighs the latency it hides.
   for (int k0 = 0; k0 < kend; k0 += 32) {
     bf16x8 kf[KS];
+    const uint16_t *Kr = hr.key_row(min(k0 + qt.fr, hr.ntot - 1)) + qt.fh * 8;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) kf[kk] = ld_frag(Kr + kk * 16);
     VtTile<DP> vt;
-    load_tile(k0, kf, vt);
-    process(k0, kf, vt);
+    load_vt<DP>(vt, hr.Vp, hr.Vs, hr.np, ldq, k0, hr.ntot, lane);
+    __builtin_amdgcn_sched_barrier(0);  // every load of the tile issued before the first wait
+    f32x16 s = qt.scores(kf, qf);
+    __syncthreads();  // the previous tile's P.V reads of sV are done
+    store_vt<DP>(sV, vt, k0, hr.ntot, lane);
+    qt.update(s, k0, hr.ntot, hr.np, causal != 0, sl2);
+    __syncthreads();
+    qt.pv(s, sV);
   }
-  if (q >= n) return;
-  const float inv = 1.0f / (l_run + __shfl_xor(l_run, 32, kWave));
-  uint16_t *Cr = ctx + (t0 + q) * ldc + h * DP;
+  qt.store(ctx, ldc, hr.t0, hr.n, h);
+}
+
+// Four wavefronts per (128-query block, head) for long sequences: each key
+// tile's K (swizzled rows) and V (transposed) go to LDS once and serve the
+// four 32-query tiles, which otherwise each fetch them from L2.  Wavefront w
+// owns queries [qb + 32 w, qb + 32 w + 32) and runs the same per-tile
+// arithmetic (QueryTile) over the same key tiles as the one-wavefront
+// kernel; wavefronts past the sequence or, causal, past their last visible
+// key tile only help stage.
+template <int DP, bool PFX>
+__global__ __launch_bounds__(256) void attn_fused_mw_kernel(const uint16_t *__restrict__ qkv, int ldq,
+                                                            int n_heads, float scale, int causal,
+                                                            const int32_t *__restrict__ off,
+                                                            const int32_t *__restrict__ items,
+                                                            const int32_t *__restrict__ pref,
+                                                            const int32_t *__restrict__ plen,
+                                                            uint16_t *__restrict__ ctx, int ldc) {
+  constexpr int KS = DP / 16, CPR = DP / 8, RPL = DP * 2 >= 256 ? 1 : 256 / (DP * 2);
+  constexpr int KCH = 32 * CPR;                 // 16-byte chunks of a K tile
+  constexpr int KPT = (KCH + 255) / 256;        // chunks per thread
+  __shared__ __attribute__((aligned(16))) uint16_t sK[32 * DP];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[DP * kVP];
+  const int item = blockIdx.x, h = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int seq = items[2 * item], qb = items[2 * item + 1];
+  const HeadRows hr = head_rows<DP, PFX>(qkv, ldq, n_heads, h, seq, off, pref, plen);
+  QueryTile<DP> qt;
+  qt.init(qb + 32 * wave, lane);
+  const bool active = qt.q0 < hr.n;
+  bf16x8 qf[KS];
+  load_q<DP>(qf, hr, qt.q0 + qt.fr, qt.fh);
+  const float sl2 = scale * 1.44269504088896340736f;
+  const int kend_blk = causal ? min(hr.ntot, hr.np + qb + 4 * kQTile) : hr.ntot;
+  const int kend = causal ? min(hr.ntot, hr.np + qt.q0 + kQTile) : hr.ntot;
+  // K chunk c of a tile: key c / CPR, 16-byte chunk c % CPR, stored at the
+  // XOR-swizzled slot of its row (conflict-free fragment reads)
+  auto swz = [](int row, int chunk) { return chunk ^ ((row / RPL) % CPR); };
+  for (int k0 = 0; k0 < kend_blk; k0 += 32) {
+    uint4 kr[KPT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      uint2 u;
-      u.x = f2bf2(acc[t][4 * g] * inv, acc[t][4 * g + 1] * inv);
-      u.y = f2bf2(acc[t][4 * g + 2] * inv, acc[t][4 * g + 3] * inv);
-      *reinterpret_cast<uint2 *>(Cr + t * 32 + 8 * g + 4 * fh) = u;
+    for (int i = 0; i < KPT; ++i) {
+      const int c = (tid + 256 * i) % KCH, key = c / CPR, ch = c % CPR;
+      kr[i] = *reinterpret_cast<const uint4 *>(hr.key_row(min(k0 + key, hr.ntot - 1)) + ch * 8);
     }
+    VtTile<DP> vt;
+    if (wave == 0) load_vt<DP>(vt, hr.Vp, hr.Vs, hr.np, ldq, k0, hr.ntot, lane);
+    __syncthreads();  // the previous tile's reads of sK and sV are done
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int c = tid + 256 * i, key = (c % KCH) / CPR, ch = c % CPR;
+      if (KCH % 256 == 0 || c < KCH)
+        *reinterpret_cast<uint4 *>(sK + key * DP + (swz(key, ch) << 3)) = kr[i];
+    }
+    if (wave == 0) store_vt<DP>(sV, vt, k0, hr.ntot, lane);
+    __syncthreads();
+    if (active && k0 < kend) {
+      bf16x8 kf[KS];
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk)
+        kf[kk] = *reinterpret_cast<const bf16x8 *>(sK + qt.fr * DP + (swz(qt.fr, kk * 2 + qt.fh) << 3));
+      f32x16 s = qt.scores(kf, qf);
+      qt.update(s, k0, hr.ntot, hr.np, causal != 0, sl2);
+      qt.pv(s, sV);
+    }
+  }
+  if (active) qt.store(ctx, ldc, hr.t0, hr.n, h);
 }
 
 template <typename F>
@@ -523,17 +641,32 @@ hipError_t launch_pv(bool act_bf16, const void *P, const void *qkv, int ldq, int
 
 hipError_t launch_attn_fused(const uint16_t *qkv, int ldq, int n_heads, int dp, float scale,
                              bool causal, const Ragged &r, uint16_t *ctx, int ldc, hipStream_t st) {
-  if (r.n_items <= 0) return hipSuccess;
   if ((r.plen != nullptr) != (r.pref != nullptr)) return hipErrorInvalidValue;
-  const dim3 grid(r.n_items, n_heads);
+  // long sequences on the four-wavefront kernel, the rest one wavefront per tile
+  const int32_t *sw = r.fused_items ? r.fused_items : r.items;
+  const int n_sw = r.fused_items ? r.n_fused_items : r.n_items;
+  const int n_mw = r.fused_items ? r.n_mw_items : 0;
   return dispatch_dp(dp, [&](auto dpc) {
     constexpr int DP = decltype(dpc)::value;
-    if (r.plen)
-      attn_fused_kernel<DP, true><<<grid, dim3(64), 0, st>>>(qkv, ldq, n_heads, scale, causal ? 1 : 0,
-                                                             r.off, r.items, r.pref, r.plen, ctx, ldc);
-    else
-      attn_fused_kernel<DP, false><<<grid, dim3(64), 0, st>>>(qkv, ldq, n_heads, scale, causal ? 1 : 0,
-                                                              r.off, r.items, nullptr, nullptr, ctx, ldc);
+    const int c = causal ? 1 : 0;
+    if (n_sw > 0) {
+      const dim3 grid(n_sw, n_heads);
+      if (r.plen)
+        attn_fused_kernel<DP, true><<<grid, dim3(64), 0, st>>>(qkv, ldq, n_heads, scale, c, r.off, sw,
+                                                               r.pref, r.plen, ctx, ldc);
+      else
+        attn_fused_kernel<DP, false><<<grid, dim3(64), 0, st>>>(qkv, ldq, n_heads, scale, c, r.off, sw,
+                                                                nullptr, nullptr, ctx, ldc);
+    }
+    if (n_mw > 0) {
+      const dim3 grid(n_mw, n_heads);
+      if (r.plen)
+        attn_fused_mw_kernel<DP, true><<<grid, dim3(256), 0, st>>>(qkv, ldq, n_heads, scale, c, r.off,
+                                                                   r.mw_items, r.pref, r.plen, ctx, ldc);
+      else
+        attn_fused_mw_kernel<DP, false><<<grid, dim3(256), 0, st>>>(qkv, ldq, n_heads, scale, c, r.off,
+                                                                    r.mw_items, nullptr, nullptr, ctx, ldc);
+    }
     return hipGetLastError();
   });
 }

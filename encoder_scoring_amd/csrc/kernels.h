@@ -21,8 +21,18 @@ struct Ragged {
   // the plen[i] tokens at packed rows pref[i].. -- its positions start at
   // plen[i] and its queries also see those rows' keys and values.  NULL: none.
   const int32_t *pref = nullptr, *plen = nullptr;
+  // Fused attention work, when split by length (NULL fused_items: every
+  // entry of items runs on the one-wavefront kernel): fused_items [2 *
+  // n_fused_items] (sequence, first query) 32-query tiles of short sequences,
+  // mw_items [2 * n_mw_items] (sequence, first query) 128-query blocks of
+  // sequences longer than kMwMinLen.
+  const int32_t *fused_items = nullptr, *mw_items = nullptr;
+  int32_t n_fused_items = 0, n_mw_items = 0;
   int32_t n_seqs = 0, n_items = 0, max_len = 0, n_tokens = 0, n_sm_items = 0;
 };
+
+// Sequences longer than this run fused attention four query tiles per block.
+constexpr int kMwMinLen = 64;
 
 // Softmax work geometry (shared by the host item builder and the kernel): the
 // A * n rows of a sequence's score block ([head][query] major, stride ld) are

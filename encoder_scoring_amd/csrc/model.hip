@@ -431,6 +431,8 @@ es_status build(const es::ParsedBlob &pb, int64_t max_tokens, int32_t max_seqs, 
 // assembled on the host, staged in pinned memory and uploaded in ONE copy.
 struct BatchLayout {
   size_t off = 0, sbase = 0, items = 0, sm_items = 0, src = 0, dest = 0, pref = 0, plen = 0;
+  size_t fitems = 0, mitems = 0;  // fused attention split by length (es::Ragged)
+  int n_fitems = 0, n_mitems = 0;
   size_t last_items = 0, last_rows = 0, iota = 0;  // last-token work of the pruned last layer
   int64_t last_pairs = 0;  // visible (query, key) pairs of the last queries, over heads
   bool has_src = false, has_dest = false, has_prefix = false;
@@ -486,12 +488,18 @@ es_status add_batch(es_model *m, const int32_t *h_off, int32_t n, const int32_t 
   for (int32_t i = 0; i < n; ++i) ord[i] = i;
   auto keys_of = [&](int32_t i) { return h_off[i + 1] - h_off[i] + (plen ? plen[i] : 0); };
   std::stable_sort(ord.begin(), ord.end(), [&](int32_t a, int32_t b) { return keys_of(a) > keys_of(b); });
-  std::vector<int32_t> items, sm_items;
+  std::vector<int32_t> items, sm_items, fitems, mitems;
   for (int32_t sq : ord) {
     const int len = h_off[sq + 1] - h_off[sq];
     for (int q0 = 0; q0 < len; q0 += es::kQTile) {
       items.push_back(sq);
       items.push_back(q0);
+    }
+    // fused attention: long sequences in 128-query blocks (K, V staged once)
+    auto &fl = len > es::kMwMinLen ? mitems : fitems;
+    for (int q0 = 0; q0 < len; q0 += len > es::kMwMinLen ? 4 * es::kQTile : es::kQTile) {
+      fl.push_back(sq);
+      fl.push_back(q0);
     }
     const int rpi = es::softmax_rows_per_item(len);
     for (int r0 = 0; r0 < m->A * len; r0 += rpi) {
@@ -503,6 +511,10 @@ es_status add_batch(es_model *m, const int32_t *h_off, int32_t n, const int32_t 
   L->off = push_bytes(buf, h_off, sizeof(int32_t) * (n + 1));
   L->sbase = push_bytes(buf, sbase.data(), sizeof(int64_t) * n);
   L->items = push_bytes(buf, items.data(), sizeof(int32_t) * items.size());
+  L->fitems = push_bytes(buf, fitems.data(), sizeof(int32_t) * fitems.size());
+  L->mitems = push_bytes(buf, mitems.data(), sizeof(int32_t) * mitems.size());
+  L->n_fitems = (int)(fitems.size() / 2);
+  L->n_mitems = (int)(mitems.size() / 2);
   L->sm_items = push_bytes(buf, sm_items.data(), sizeof(int32_t) * sm_items.size());
   L->n_sm_items = (int)(sm_items.size() / 2);
   L->has_src = src != nullptr;
@@ -584,6 +596,8 @@ LastView last_view_of(const es_model *m, const BatchLayout &L) {
   v.attn = ragged_of(m, L);
   v.attn.items = reinterpret_cast<const int32_t *>(m->meta_dev + L.last_items);
   v.attn.n_items = L.n;
+  v.attn.fused_items = v.attn.mw_items = nullptr;  // last queries: one tile each
+  v.attn.n_fused_items = v.attn.n_mw_items = 0;
   v.rows = reinterpret_cast<const int32_t *>(m->meta_dev + L.last_rows);
   v.tail = v.attn;
   v.tail.off = reinterpret_cast<const int32_t *>(m->meta_dev + L.iota);
@@ -598,6 +612,10 @@ es::Ragged ragged_of(const es_model *m, const BatchLayout &L) {
   r.off = reinterpret_cast<const int32_t *>(m->meta_dev + L.off);
   r.sbase = reinterpret_cast<const int64_t *>(m->meta_dev + L.sbase);
   r.items = reinterpret_cast<const int32_t *>(m->meta_dev + L.items);
+  r.fused_items = reinterpret_cast<const int32_t *>(m->meta_dev + L.fitems);
+  r.mw_items = reinterpret_cast<const int32_t *>(m->meta_dev + L.mitems);
+  r.n_fused_items = L.n_fitems;
+  r.n_mw_items = L.n_mitems;
   r.sm_items = reinterpret_cast<const int32_t *>(m->meta_dev + L.sm_items);
   r.n_sm_items = L.n_sm_items;
   r.src = L.has_src ? reinterpret_cast<const int32_t *>(m->meta_dev + L.src) : nullptr;
