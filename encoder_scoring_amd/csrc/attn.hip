@@ -591,6 +591,97 @@ __global__ __launch_bounds__(256) void attn_fused_mw_kernel(const uint16_t *__re
   if (active) qt.store(ctx, ldc, hr.t0, hr.n, h);
 }
 
+// Shared-prompt candidates, four 32-query tiles of candidates of the same
+// prompt per block (wavefront w: items[8 b + 2 w], sequence < 0 = empty).
+// Key tiles that lie wholly inside the prompt (k0 + 32 <= np) are the same for
+// all four and are staged in LDS once, as in the four-wavefront kernel; the
+// remaining tiles (the one holding the prompt's end and the candidate's own
+// keys) differ per wavefront, which then works alone as the one-wavefront
+// kernel does, with its own V region and no block barrier.  Per query, the
+// same key tiles in the same order and the same per-tile arithmetic
+// (QueryTile) as the other two kernels.
+template <int DP>
+__global__ __launch_bounds__(256) void attn_fused_pfx_kernel(const uint16_t *__restrict__ qkv, int ldq,
+                                                             int n_heads, float scale, int causal,
+                                                             const int32_t *__restrict__ off,
+                                                             const int32_t *__restrict__ items,
+                                                             const int32_t *__restrict__ pref,
+                                                             const int32_t *__restrict__ plen,
+                                                             uint16_t *__restrict__ ctx, int ldc) {
+  constexpr int KS = DP / 16, CPR = DP / 8, RPL = DP * 2 >= 256 ? 1 : 256 / (DP * 2);
+  constexpr int KCH = 32 * CPR, KPT = (KCH + 255) / 256;
+  __shared__ __attribute__((aligned(16))) uint16_t sK[32 * DP];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[DP * kVP];
+  __shared__ __attribute__((aligned(16))) uint16_t sVw[4][DP * kVP];
+  const int item = blockIdx.x, h = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int seq = items[8 * item + 2 * wave], q0 = items[8 * item + 2 * wave + 1];
+  const bool active = seq >= 0;
+  // the block's prompt (every non-empty slot shares it; slot 0 is never empty)
+  const int seq0 = items[8 * item];
+  const int np = plen[seq0];
+  const HeadRows hr = head_rows<DP, true>(qkv, ldq, n_heads, h, active ? seq : seq0, off, pref, plen);
+  QueryTile<DP> qt;
+  qt.init(q0, lane);
+  bf16x8 qf[KS];
+  load_q<DP>(qf, hr, q0 + qt.fr, qt.fh);
+  const float sl2 = scale * 1.44269504088896340736f;
+  auto swz = [](int row, int chunk) { return chunk ^ ((row / RPL) % CPR); };
+  // prompt tiles, shared: keys [0, kp)
+  const int kp = np / 32 * 32;
+  for (int k0 = 0; k0 < kp; k0 += 32) {
+    uint4 kr[KPT];
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int c = (tid + 256 * i) % KCH, key = c / CPR, ch = c % CPR;
+      kr[i] = *reinterpret_cast<const uint4 *>(hr.key_row(k0 + key) + ch * 8);
+    }
+    VtTile<DP> vt;
+    if (wave == 0) load_vt<DP>(vt, hr.Vp, hr.Vs, hr.np, ldq, k0, hr.ntot, lane);
+    __syncthreads();  // the previous tile's reads of sK and sV are done
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int c = tid + 256 * i, key = (c % KCH) / CPR, ch = c % CPR;
+      if (KCH % 256 == 0 || c < KCH)
+        *reinterpret_cast<uint4 *>(sK + key * DP + (swz(key, ch) << 3)) = kr[i];
+    }
+    if (wave == 0) store_vt<DP>(sV, vt, k0, hr.ntot, lane);
+    __syncthreads();
+    if (active) {
+      bf16x8 kf[KS];
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk)
+        kf[kk] = *reinterpret_cast<const bf16x8 *>(sK + qt.fr * DP + (swz(qt.fr, kk * 2 + qt.fh) << 3));
+      f32x16 s = qt.scores(kf, qf);
+      qt.update(s, k0, hr.ntot, hr.np, causal != 0, sl2);
+      qt.pv(s, sV);
+    }
+  }
+  if (!active) return;  // no block barrier follows
+  // the wavefront's own tiles: keys [kp, kend)
+  const int kend = causal ? min(hr.ntot, hr.np + q0 + kQTile) : hr.ntot;
+  uint16_t *myV = sVw[wave];
+  for (int k0 = kp; k0 < kend; k0 += 32) {
+    bf16x8 kf[KS];
+    const uint16_t *Kr = hr.key_row(min(k0 + qt.fr, hr.ntot - 1)) + qt.fh * 8;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) kf[kk] = ld_frag(Kr + kk * 16);
+    VtTile<DP> vt;
+    load_vt<DP>(vt, hr.Vp, hr.Vs, hr.np, ldq, k0, hr.ntot, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 s = qt.scores(kf, qf);
+    // myV belongs to this wavefront alone, so fences (no barrier) order the
+    // previous tile's reads of it before these writes and these writes
+    // before this tile's reads (lanes exchange keys through it)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    store_vt<DP>(myV, vt, k0, hr.ntot, lane);
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+    qt.update(s, k0, hr.ntot, hr.np, causal != 0, sl2);
+    qt.pv(s, myV);
+  }
+  qt.store(ctx, ldc, hr.t0, hr.n, h);
+}
+
 template <typename F>
 hipError_t dispatch_dp(int dp, F &&f) {
   switch (dp) {
@@ -657,6 +748,11 @@ hipError_t launch_attn_fused(const uint16_t *qkv, int ldq, int n_heads, int dp, 
       else
         attn_fused_kernel<DP, false><<<grid, dim3(64), 0, st>>>(qkv, ldq, n_heads, scale, c, r.off, sw,
                                                                 nullptr, nullptr, ctx, ldc);
+    }
+    if (r.plen && r.n_pfx_items > 0) {
+      const dim3 grid(r.n_pfx_items, n_heads);
+      attn_fused_pfx_kernel<DP><<<grid, dim3(256), 0, st>>>(qkv, ldq, n_heads, scale, c, r.off,
+                                                             r.pfx_items, r.pref, r.plen, ctx, ldc);
     }
     if (n_mw > 0) {
       const dim3 grid(n_mw, n_heads);

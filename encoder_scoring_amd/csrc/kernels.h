@@ -28,11 +28,21 @@ struct Ragged {
   // sequences longer than kMwMinLen.
   const int32_t *fused_items = nullptr, *mw_items = nullptr;
   int32_t n_fused_items = 0, n_mw_items = 0;
+  // Shared-prompt candidates (with plen): pfx_items [8 * n_pfx_items], four
+  // (sequence, first query) 32-query tiles of candidates of one prompt per
+  // entry (sequence < 0: empty slot; slot 0 never empty); those tiles are not
+  // in fused_items / mw_items.
+  const int32_t *pfx_items = nullptr;
+  int32_t n_pfx_items = 0;
   int32_t n_seqs = 0, n_items = 0, max_len = 0, n_tokens = 0, n_sm_items = 0;
 };
 
 // Sequences longer than this run fused attention four query tiles per block.
 constexpr int kMwMinLen = 64;
+// Shared-prompt candidates of at most kMwMinLen tokens run four query tiles
+// (of candidates of one prompt) per block when the prompt has at least this
+// many tokens (two key tiles staged once for the block).
+constexpr int kPfxMinPrompt = 64;
 
 // Softmax work geometry (shared by the host item builder and the kernel): the
 // A * n rows of a sequence's score block ([head][query] major, stride ld) are

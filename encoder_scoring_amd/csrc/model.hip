@@ -431,8 +431,8 @@ es_status build(const es::ParsedBlob &pb, int64_t max_tokens, int32_t max_seqs, 
 // assembled on the host, staged in pinned memory and uploaded in ONE copy.
 struct BatchLayout {
   size_t off = 0, sbase = 0, items = 0, sm_items = 0, src = 0, dest = 0, pref = 0, plen = 0;
-  size_t fitems = 0, mitems = 0;  // fused attention split by length (es::Ragged)
-  int n_fitems = 0, n_mitems = 0;
+  size_t fitems = 0, mitems = 0, pitems = 0;  // fused attention split by length (es::Ragged)
+  int n_fitems = 0, n_mitems = 0, n_pitems = 0;
   size_t last_items = 0, last_rows = 0, iota = 0;  // last-token work of the pruned last layer
   int64_t last_pairs = 0;  // visible (query, key) pairs of the last queries, over heads
   bool has_src = false, has_dest = false, has_prefix = false;
@@ -488,18 +488,50 @@ es_status add_batch(es_model *m, const int32_t *h_off, int32_t n, const int32_t 
   for (int32_t i = 0; i < n; ++i) ord[i] = i;
   auto keys_of = [&](int32_t i) { return h_off[i + 1] - h_off[i] + (plen ? plen[i] : 0); };
   std::stable_sort(ord.begin(), ord.end(), [&](int32_t a, int32_t b) { return keys_of(a) > keys_of(b); });
-  std::vector<int32_t> items, sm_items, fitems, mitems;
+  std::vector<int32_t> items, sm_items, fitems, mitems, pitems;
+  // shared-prompt candidates of up to kMwMinLen tokens whose prompt spans at
+  // least kPfxMinPrompt positions: their 32-query tiles go four to a block,
+  // grouped by prompt (all candidates of a prompt sort together: equal
+  // prompt keys, then longest first), so the prompt's key tiles are staged
+  // once per block
+  auto pfx_tile = [&](int32_t i) {
+    return plen && plen[i] >= es::kPfxMinPrompt && h_off[i + 1] - h_off[i] <= es::kMwMinLen;
+  };
+  if (plen)
+    std::stable_sort(ord.begin(), ord.end(), [&](int32_t a, int32_t b) {
+      const bool pa = pfx_tile(a), pb = pfx_tile(b);
+      if (pa != pb) return pa < pb;
+      if (pa && (plen[a] != plen[b] || pref[a] != pref[b]))
+        return plen[a] != plen[b] ? plen[a] > plen[b] : pref[a] < pref[b];
+      return keys_of(a) > keys_of(b);
+    });
+  int32_t pfx_slot = 0, pfx_np = -1, pfx_row = -1;
   for (int32_t sq : ord) {
     const int len = h_off[sq + 1] - h_off[sq];
     for (int q0 = 0; q0 < len; q0 += es::kQTile) {
       items.push_back(sq);
       items.push_back(q0);
     }
-    // fused attention: long sequences in 128-query blocks (K, V staged once)
-    auto &fl = len > es::kMwMinLen ? mitems : fitems;
-    for (int q0 = 0; q0 < len; q0 += len > es::kMwMinLen ? 4 * es::kQTile : es::kQTile) {
-      fl.push_back(sq);
-      fl.push_back(q0);
+    if (pfx_tile(sq)) {
+      if (plen[sq] != pfx_np || pref[sq] != pfx_row) {  // a new prompt starts a new block
+        for (; pfx_slot % 4; ++pfx_slot) {
+          pitems.push_back(-1);
+          pitems.push_back(0);
+        }
+        pfx_np = plen[sq];
+        pfx_row = pref[sq];
+      }
+      for (int q0 = 0; q0 < len; q0 += es::kQTile, ++pfx_slot) {
+        pitems.push_back(sq);
+        pitems.push_back(q0);
+      }
+    } else {
+      // fused attention: long sequences in 128-query blocks (K, V staged once)
+      auto &fl = len > es::kMwMinLen ? mitems : fitems;
+      for (int q0 = 0; q0 < len; q0 += len > es::kMwMinLen ? 4 * es::kQTile : es::kQTile) {
+        fl.push_back(sq);
+        fl.push_back(q0);
+      }
     }
     const int rpi = es::softmax_rows_per_item(len);
     for (int r0 = 0; r0 < m->A * len; r0 += rpi) {
@@ -513,8 +545,14 @@ es_status add_batch(es_model *m, const int32_t *h_off, int32_t n, const int32_t 
   L->items = push_bytes(buf, items.data(), sizeof(int32_t) * items.size());
   L->fitems = push_bytes(buf, fitems.data(), sizeof(int32_t) * fitems.size());
   L->mitems = push_bytes(buf, mitems.data(), sizeof(int32_t) * mitems.size());
+  for (; pfx_slot % 4; ++pfx_slot) {
+    pitems.push_back(-1);
+    pitems.push_back(0);
+  }
+  L->pitems = push_bytes(buf, pitems.data(), sizeof(int32_t) * pitems.size());
   L->n_fitems = (int)(fitems.size() / 2);
   L->n_mitems = (int)(mitems.size() / 2);
+  L->n_pitems = (int)(pitems.size() / 8);
   L->sm_items = push_bytes(buf, sm_items.data(), sizeof(int32_t) * sm_items.size());
   L->n_sm_items = (int)(sm_items.size() / 2);
   L->has_src = src != nullptr;
@@ -598,6 +636,8 @@ LastView last_view_of(const es_model *m, const BatchLayout &L) {
   v.attn.n_items = L.n;
   v.attn.fused_items = v.attn.mw_items = nullptr;  // last queries: one tile each
   v.attn.n_fused_items = v.attn.n_mw_items = 0;
+  v.attn.pfx_items = nullptr;
+  v.attn.n_pfx_items = 0;
   v.rows = reinterpret_cast<const int32_t *>(m->meta_dev + L.last_rows);
   v.tail = v.attn;
   v.tail.off = reinterpret_cast<const int32_t *>(m->meta_dev + L.iota);
@@ -616,6 +656,8 @@ es::Ragged ragged_of(const es_model *m, const BatchLayout &L) {
   r.mw_items = reinterpret_cast<const int32_t *>(m->meta_dev + L.mitems);
   r.n_fused_items = L.n_fitems;
   r.n_mw_items = L.n_mitems;
+  r.pfx_items = reinterpret_cast<const int32_t *>(m->meta_dev + L.pitems);
+  r.n_pfx_items = L.n_pitems;
   r.sm_items = reinterpret_cast<const int32_t *>(m->meta_dev + L.sm_items);
   r.n_sm_items = L.n_sm_items;
   r.src = L.has_src ? reinterpret_cast<const int32_t *>(m->meta_dev + L.src) : nullptr;
