@@ -194,9 +194,9 @@ __global__ __launch_bounds__(64) void scores_mfma_kernel(const uint16_t *__restr
 // of a tile in flight together with its other loads before it waits.
 constexpr int kVP = 40;  // LDS pitch of a transposed row (32 keys + 8, keeps 16-byte reads aligned)
 
-template <int DP>
+template <int DP, int NTH = 64>
 struct VtTile {
-  static constexpr int OCT = DP / 8, UNITS = 8 * OCT, NU = (UNITS + 63) / 64;
+  static constexpr int OCT = DP / 8, UNITS = 8 * OCT, NU = (UNITS + NTH - 1) / NTH;
   uint4 r[NU][4];
 };
 
@@ -204,14 +204,14 @@ struct VtTile {
 // keys at positions >= np from Vs[key - np]; np = 0 for a plain sequence.
 // Every lane reads a valid row (key clamped to n - 1, n >= 1) and store_vt
 // zeroes keys >= n, so the loads need no branches.
-template <int DP>
-__device__ __forceinline__ void load_vt(VtTile<DP> &t, const uint16_t *__restrict__ Vp,
+template <int DP, int NTH = 64>
+__device__ __forceinline__ void load_vt(VtTile<DP, NTH> &t, const uint16_t *__restrict__ Vp,
                                         const uint16_t *__restrict__ Vs, int np, int ldq, int k0,
                                         int n, int lane) {
-  using T = VtTile<DP>;
+  using T = VtTile<DP, NTH>;
 #pragma unroll
   for (int i = 0; i < T::NU; ++i) {
-    const int u = (lane + 64 * i) % T::UNITS, quad = u / T::OCT, oct = u % T::OCT;
+    const int u = (lane + NTH * i) % T::UNITS, quad = u / T::OCT, oct = u % T::OCT;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int key = k0 + 4 * quad + j, kc = min(key, n - 1);
@@ -221,19 +221,19 @@ __device__ __forceinline__ void load_vt(VtTile<DP> &t, const uint16_t *__restric
   }
 }
 
-template <int DP>
-__device__ __forceinline__ void store_vt(uint16_t *__restrict__ sV, VtTile<DP> &t, int k0, int n,
+template <int DP, int NTH = 64>
+__device__ __forceinline__ void store_vt(uint16_t *__restrict__ sV, VtTile<DP, NTH> &t, int k0, int n,
                                          int lane) {
-  using T = VtTile<DP>;
+  using T = VtTile<DP, NTH>;
 #pragma unroll
   for (int i = 0; i < T::NU; ++i) {
-    const int u = lane + 64 * i, quad = (u % T::UNITS) / T::OCT, oct = u % T::OCT;
+    const int u = lane + NTH * i, quad = (u % T::UNITS) / T::OCT, oct = u % T::OCT;
     if (k0 + 32 > n) {  // only the last tile of a sequence has keys to clear
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         if (k0 + 4 * quad + j >= n) t.r[i][j] = make_uint4(0, 0, 0, 0);
     }
-    if (T::UNITS % 64 == 0 || u < T::UNITS) {
+    if (T::UNITS % NTH == 0 || u < T::UNITS) {
 #pragma unroll
       for (int d = 0; d < 8; ++d) {
         const int c = d >> 1, sh = (d & 1) * 16;
@@ -560,15 +560,24 @@ __global__ __launch_bounds__(256) void attn_fused_mw_kernel(const uint16_t *__re
   // K chunk c of a tile: key c / CPR, 16-byte chunk c % CPR, stored at the
   // XOR-swizzled slot of its row (conflict-free fragment reads)
   auto swz = [](int row, int chunk) { return chunk ^ ((row / RPL) % CPR); };
-  for (int k0 = 0; k0 < kend_blk; k0 += 32) {
-    uint4 kr[KPT];
+  // Every thread stages part of each key tile: KPT 16-byte K chunks and, for
+  // the first VT threads, one 4-key x 8-dim unit of V.  The next tile's
+  // loads are issued right after the current tile is written to LDS, so they
+  // are in flight while the current tile is computed.
+  using VT = VtTile<DP, 256>;
+  constexpr int VTH = (VT::UNITS + 63) / 64 * 64;  // whole wavefronts that load V
+  uint4 kr[KPT];
+  VT vt;
+  auto load_tile = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int c = (tid + 256 * i) % KCH, key = c / CPR, ch = c % CPR;
       kr[i] = *reinterpret_cast<const uint4 *>(hr.key_row(min(k0 + key, hr.ntot - 1)) + ch * 8);
     }
-    VtTile<DP> vt;
-    if (wave == 0) load_vt<DP>(vt, hr.Vp, hr.Vs, hr.np, ldq, k0, hr.ntot, lane);
+    if (tid < VTH) load_vt<DP, 256>(vt, hr.Vp, hr.Vs, hr.np, ldq, k0, hr.ntot, tid);
+  };
+  load_tile(0);
+  for (int k0 = 0; k0 < kend_blk; k0 += 32) {
     __syncthreads();  // the previous tile's reads of sK and sV are done
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
@@ -576,7 +585,8 @@ __global__ __launch_bounds__(256) void attn_fused_mw_kernel(const uint16_t *__re
       if (KCH % 256 == 0 || c < KCH)
         *reinterpret_cast<uint4 *>(sK + key * DP + (swz(key, ch) << 3)) = kr[i];
     }
-    if (wave == 0) store_vt<DP>(sV, vt, k0, hr.ntot, lane);
+    if (tid < VTH) store_vt<DP, 256>(sV, vt, k0, hr.ntot, tid);
+    if (k0 + 32 < kend_blk) load_tile(k0 + 32);
     __syncthreads();
     if (active && k0 < kend) {
       bf16x8 kf[KS];
