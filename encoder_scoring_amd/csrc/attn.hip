@@ -637,17 +637,23 @@ __global__ __launch_bounds__(256) void attn_fused_pfx_kernel(const uint16_t *__r
   load_q<DP>(qf, hr, q0 + qt.fr, qt.fh);
   const float sl2 = scale * 1.44269504088896340736f;
   auto swz = [](int row, int chunk) { return chunk ^ ((row / RPL) % CPR); };
-  // prompt tiles, shared: keys [0, kp)
+  // prompt tiles, shared: keys [0, kp), staged by every thread with the next
+  // tile's loads in flight, as in the four-wavefront kernel
   const int kp = np / 32 * 32;
-  for (int k0 = 0; k0 < kp; k0 += 32) {
-    uint4 kr[KPT];
+  using VT = VtTile<DP, 256>;
+  constexpr int VTH = (VT::UNITS + 63) / 64 * 64;
+  uint4 kr[KPT];
+  VT vt;
+  auto load_tile = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int c = (tid + 256 * i) % KCH, key = c / CPR, ch = c % CPR;
       kr[i] = *reinterpret_cast<const uint4 *>(hr.key_row(k0 + key) + ch * 8);
     }
-    VtTile<DP> vt;
-    if (wave == 0) load_vt<DP>(vt, hr.Vp, hr.Vs, hr.np, ldq, k0, hr.ntot, lane);
+    if (tid < VTH) load_vt<DP, 256>(vt, hr.Vp, hr.Vs, hr.np, ldq, k0, hr.ntot, tid);
+  };
+  if (kp > 0) load_tile(0);
+  for (int k0 = 0; k0 < kp; k0 += 32) {
     __syncthreads();  // the previous tile's reads of sK and sV are done
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
@@ -655,7 +661,8 @@ __global__ __launch_bounds__(256) void attn_fused_pfx_kernel(const uint16_t *__r
       if (KCH % 256 == 0 || c < KCH)
         *reinterpret_cast<uint4 *>(sK + key * DP + (swz(key, ch) << 3)) = kr[i];
     }
-    if (wave == 0) store_vt<DP>(sV, vt, k0, hr.ntot, lane);
+    if (tid < VTH) store_vt<DP, 256>(sV, vt, k0, hr.ntot, tid);
+    if (k0 + 32 < kp) load_tile(k0 + 32);
     __syncthreads();
     if (active) {
       bf16x8 kf[KS];
