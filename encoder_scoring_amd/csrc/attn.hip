@@ -363,16 +363,24 @@ struct QueryTile {
     return s;
   }
   // Online-softmax update with key tile k0: s becomes the tile's
-  // probabilities (unnormalised), the accumulator is rescaled.
+  // probabilities (unnormalised, relative to the reference m_run).
   // Masking only where a key of the tile can be invisible to a query of the
   // tile: the sequence's last key tile and, causal, tiles reaching past the
   // first query's position.  The first tile shows every query key 0, so
   // m_run is finite after it; a later tile whose keys are all masked for a
-  // query leaves that query's running max, sum and accumulator exactly
-  // unchanged (alpha = 1, p = 0).  Scores are kept in base 2, s log2(e) /
-  // sqrt(d) (sl2), so every probability is one v_exp_f32; the running max is
-  // kept in scaled units (scaling by sl2 > 0 commutes with the max) and each
+  // query leaves that query's reference, sum and accumulator exactly
+  // unchanged (p = 0).  Scores are kept in base 2, s log2(e) / sqrt(d)
+  // (sl2), so every probability is one v_exp_f32; the reference is kept in
+  // scaled units (scaling by sl2 > 0 commutes with the max) and each
   // exponent is one fma: 2^(s sl2 - m).
+  // The reference need not be the running max: the sum and the accumulator
+  // are both relative to it, so the normalised result is the same for any
+  // m_run.  It moves up to the tile's max only when that exceeds it by more
+  // than kSlack (base-2 units, so every p stays <= 2^kSlack), and the
+  // wavefront skips rescaling its accumulator (NT x 16 multiplies) when none
+  // of its queries' references moved -- after the first key tiles, the
+  // usual case.
+  static constexpr float kSlack = 8.0f;
   __device__ __forceinline__ void update(f32x16 &s, int k0, int ntot, int np, bool causal, float sl2) {
     const int qpos = np + q0 + fr;
     if (k0 + 32 > ntot || (causal && k0 + 31 > np + q0)) {
@@ -386,20 +394,25 @@ struct QueryTile {
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));  // the other 16 keys of this query
-    const float m_new = fmaxf(m_run, mx * sl2);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    const float m_tile = mx * sl2;
+    const bool move = m_tile > m_run + kSlack;  // always at the first tile (m_run = -inf)
+    if (__any(move)) {
+      const float m_new = move ? m_tile : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 1 where the reference stays
+      l_run *= alpha;
+      m_run = m_new;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[t][r] *= alpha;
+    }
     float psum = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -m_new));
+      s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -m_run));
       psum += s[r];
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[t][r] *= alpha;
+    l_run += psum;
   }
   // ctx^T += V^T P^T with the tile's V transposed in LDS (sV).
   __device__ __forceinline__ void pv(const f32x16 &p, const uint16_t *sV) {
