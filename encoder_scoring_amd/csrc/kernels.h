@@ -37,11 +37,13 @@ struct Ragged {
   int32_t n_seqs = 0, n_items = 0, max_len = 0, n_tokens = 0, n_sm_items = 0;
 };
 
-// Sequences longer than this run fused attention four query tiles per block.
-constexpr int kMwMinLen = 64;
-// Shared-prompt candidates of at most kMwMinLen tokens run four query tiles
-// (of candidates of one prompt) per block when the prompt has at least this
-// many tokens (two key tiles staged once for the block).
+// Sequences longer than this (more than one query tile) run fused attention
+// four query tiles per block.
+constexpr int kMwMinLen = 32;
+// Shared-prompt candidates of at most kPfxMaxLen tokens run four query tiles
+// (of candidates of one prompt) per block when the prompt has at least
+// kPfxMinPrompt tokens (two key tiles staged once for the block).
+constexpr int kPfxMaxLen = 64;
 constexpr int kPfxMinPrompt = 64;
 
 // Softmax work geometry (shared by the host item builder and the kernel): the

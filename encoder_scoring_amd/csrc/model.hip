@@ -489,13 +489,13 @@ es_status add_batch(es_model *m, const int32_t *h_off, int32_t n, const int32_t 
   auto keys_of = [&](int32_t i) { return h_off[i + 1] - h_off[i] + (plen ? plen[i] : 0); };
   std::stable_sort(ord.begin(), ord.end(), [&](int32_t a, int32_t b) { return keys_of(a) > keys_of(b); });
   std::vector<int32_t> items, sm_items, fitems, mitems, pitems;
-  // shared-prompt candidates of up to kMwMinLen tokens whose prompt spans at
+  // shared-prompt candidates of up to kPfxMaxLen tokens whose prompt spans at
   // least kPfxMinPrompt positions: their 32-query tiles go four to a block,
   // grouped by prompt (all candidates of a prompt sort together: equal
   // prompt keys, then longest first), so the prompt's key tiles are staged
   // once per block
   auto pfx_tile = [&](int32_t i) {
-    return plen && plen[i] >= es::kPfxMinPrompt && h_off[i + 1] - h_off[i] <= es::kMwMinLen;
+    return plen && plen[i] >= es::kPfxMinPrompt && h_off[i + 1] - h_off[i] <= es::kPfxMaxLen;
   };
   if (plen)
     std::stable_sort(ord.begin(), ord.end(), [&](int32_t a, int32_t b) {
