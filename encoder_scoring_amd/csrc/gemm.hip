@@ -726,36 +726,62 @@ constexpr int kCUs = 256;
 
 }  // namespace
 
-// Configuration for an M x N x K problem, from a sweep of the model's GEMM
-// shapes on MI355X (TFLOP/s; tile 0 / 1 / 2 / 3):
-//   M      N     K    epilogue     0     1     2     3
-//   2048   768   768  residual    203   194    90   105
-//   4096   2304  768  bias        471   555   515   561
-//   4096   3072  768  GELU        481   577   478   497
-//   8192   768   3072 residual    577   794   469   522
-//   16384  2304  768  bias        566   791   712   772
-//   16384  3072  768  GELU        509   655   634   554
-//   16384  768   3072 residual    608   795   833   915
-//   16384  6144  2048 bias        645   973  1163  1052
-//   16384  2048  8192 residual    644   973  1091   975
-// Wide blocks (2, 3) pay off only with a long K, and only while their count
-// fills the chip: 128 x 384 for narrow outputs (N <= 1024) once its blocks
-// cover 90 % of the CUs, 256 x 256 once they cover half; 128 x 128 while its
-// blocks cover half the CUs; else 128 x 64 (more blocks).  Every
-// configuration issues the same MFMA over K in the same order and K is never
-// split, so each output's accumulation order does not depend on the
-// configuration chosen or on the other sequences in the batch.
-int gemm_tile_index(int M, int N, int K) {
+// Configuration for an M x N x K problem.  Blocks run in rounds of as many
+// as are resident at once (128 x 128: two per CU; 256 x 256 and 128 x 384:
+// one), and a round costs about as long as one block's work whatever the
+// number of blocks in it, so the choice is mostly about how the last round
+// is filled.  Cost of configuration c = rounds x (a_c + b_c K) microseconds,
+// a partial last round counting (0.71 + 0.29 fill) of a full one, the GELU
+// epilogue making a wide block's round 10 % longer; a_c, b_c fitted to a
+// sweep of the model's shapes on MI355X (M = 2048 .. 16640 in steps of 256
+// for K = 768 / 3072, 8192 .. 16384 in steps of 512 for K = 2048 / 8192;
+// same-stream launches, time per launch):
+//   shape (N x K, epilogue)     heuristic before -> this model, summed over M
+//   2304 x 768 bias              2609 -> 2556 us
+//   768 x 768 fp32               1185 -> 1157
+//   3072 x 768 GELU              3937 -> 3982 (same tiles; run-to-run noise)
+//   768 x 3072 fp32              3222 -> 3138
+//   2048 x 2048 fp32             1877 -> 1825
+//   2048 x 8192 fp32             6915 -> 6558
+//   8192 x 2048 GELU             7307 -> 7274
+//   6144 x 2048 bias             4707 -> 4801 (same tiles; noise)
+// The 128 x 384 block is only considered for K >= 2048, and the wide blocks
+// not at all when both N and K are below 2048.  Problems too small to give
+// the 128 x 128 block half the CUs take the
+// 128 x 64 block (more, smaller blocks).  Every configuration issues the
+// same MFMA over K in the same order and K is never split, so each output's
+// accumulation order does not depend on the configuration chosen or on the
+// other sequences in the batch.
+int gemm_tile_index(int M, int N, int K, int epi) {
   const int64_t b128 = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
-  const int64_t b256 = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
-  const int64_t b384 = (int64_t)((M + 127) / 128) * ((N + 383) / 384);
+  if (b128 < kCUs / 2) return 0;
+  // small N and K (the attention-out GEMM): the wide blocks time faster
+  // alone but slower inside the layer sequence (15.9 k rows: 2.97 -> 3.1-3.25
+  // ms per step), so the 128 x 128 block stays
+  if (N < 2048 && K < 2048) return 1;
+  struct Option { int tile, bm, bn, resident; double a, b; };
+  static constexpr Option opts[] = {
+      {1, 128, 128, 2 * kCUs, 4.5, 0.013},
+      {2, 256, 256, kCUs, 11.69, 0.0205},
+      {3, 128, 384, kCUs, 10.7, 0.0186},
+  };
   const bool p3_fits = (N + 383) / 384 * 384 <= (N + 255) / 256 * 256;
-  if (K >= 2048) {
-    if (N <= 1024 && p3_fits && 10 * b384 >= 9 * kCUs) return 3;
-    if (b256 >= kCUs / 2) return 2;
+  int best = 1;
+  double best_cost = 0;
+  for (const Option &o : opts) {
+    if (o.tile == 3 && (!p3_fits || K < 2048)) continue;  // 128 x 384: long K only
+    const int64_t blocks = (int64_t)((M + o.bm - 1) / o.bm) * ((N + o.bn - 1) / o.bn);
+    const int64_t full = blocks / o.resident;
+    const double fill = (double)(blocks - full * o.resident) / o.resident;
+    const double rounds = (double)full + (fill > 0 ? 0.71 + 0.29 * fill : 0.0);
+    double cost = rounds * (o.a + o.b * K);
+    if (epi == kEpiGelu && o.tile != 1) cost *= 1.1;
+    if (o.tile == 1 || cost < best_cost) {
+      best = o.tile;
+      best_cost = cost;
+    }
   }
-  if (b128 >= kCUs / 2) return 1;
-  return 0;
+  return best;
 }
 
 hipError_t launch_gemm_bf16_tile(int tile, const uint16_t *A, int lda, const uint16_t *W,
@@ -785,7 +811,7 @@ hipError_t launch_gemm_bf16(const uint16_t *A, int lda, const uint16_t *W, const
     const char *e = std::getenv("ES_GEMM_TILE");
     return e ? std::atoi(e) : -1;
   }();
-  const int tile = forced >= 0 && forced < kGemmTiles ? forced : gemm_tile_index(M, N, K);
+  const int tile = forced >= 0 && forced < kGemmTiles ? forced : gemm_tile_index(M, N, K, epi);
   return launch_gemm_bf16_tile(tile, A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
 }
 
