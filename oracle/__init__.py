@@ -37,6 +37,7 @@ from .model import (  # noqa: F401
     gelu,
     linear,
     attention,
+    masked_attention,
 )
 from .selection import best_of_n  # noqa: F401
 from .scheduler import (  # noqa: F401

@@ -63,15 +63,22 @@ def attention(x, w_qkv, b_qkv, n_heads, causal, key_mask=None):
     of each block.  ``key_mask`` [n, n] (True = visible) replaces the default
     mask (all keys, or keys j <= i when causal); used by the packed form.
     """
-    n, H = x.shape
-    d = H // n_heads
+    H = x.shape[1]
     qkv = linear(x, w_qkv, b_qkv)
-    q, k, v = qkv[:, :H], qkv[:, H:2 * H], qkv[:, 2 * H:]
+    return masked_attention(qkv[:, :H], qkv[:, H:2 * H], qkv[:, 2 * H:], n_heads, causal, key_mask)
+
+
+def masked_attention(q, k, v, n_heads, causal, key_mask=None):
+    """Per head h: softmax(Q_h K_h^T / sqrt(d)) V_h over the visible keys,
+    heads concatenated; q, k, v are [n, H] with head h at columns
+    h*d..h*d+d-1.  Mask as in ``attention``."""
+    n, H = q.shape
+    d = H // n_heads
     if key_mask is None:
         key_mask = np.ones((n, n), dtype=bool)
         if causal:
             key_mask = np.tril(key_mask)
-    scale = x.dtype.type(1.0 / math.sqrt(d))
+    scale = q.dtype.type(1.0 / math.sqrt(d))
     ctx = np.empty_like(q)
     for h in range(n_heads):
         sl = slice(h * d, (h + 1) * d)

@@ -11,7 +11,7 @@ import os
 import numpy as np
 import pytest
 
-from oracle import attention, gelu, layer_norm, softmax_rows
+from oracle import attention, gelu, layer_norm, masked_attention, softmax_rows
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -151,6 +151,36 @@ def test_attention_zero_query_gives_means():
     np.testing.assert_allclose(attention(x, w, b, A, False), np.broadcast_to(v.mean(0), v.shape), atol=1e-13)
     prefix = np.cumsum(v, axis=0) / np.arange(1, n + 1)[:, None]
     np.testing.assert_allclose(attention(x, w, b, A, True), prefix, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_masked_attention_matches_torch_sdpa(causal):
+    """Independent implementation on given Q, K, V: torch's
+    scaled_dot_product_attention on the CPU (float64), heads split from the
+    concatenated columns."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(6)
+    n, A, d = 37, 3, 8
+    q, k, v = (rng.standard_normal((n, A * d)) for _ in range(3))
+    heads = lambda a: torch.from_numpy(a.reshape(n, A, d).transpose(1, 0, 2).copy())
+    ref = torch.nn.functional.scaled_dot_product_attention(heads(q), heads(k), heads(v), is_causal=causal)
+    ref = ref.numpy().transpose(1, 0, 2).reshape(n, A * d)
+    np.testing.assert_allclose(masked_attention(q, k, v, A, causal), ref, atol=1e-12)
+
+
+def test_masked_attention_dominant_key():
+    """A key whose score exceeds every other by 60 takes all the weight: each
+    query's context is that key's value row (to exp(-60))."""
+    n, H = 6, 4
+    rng = np.random.default_rng(7)
+    v = rng.standard_normal((n, H))
+    q = np.zeros((n, H)); q[:, 0] = 1.0
+    k = np.zeros((n, H)); k[2, 0] = 120.0          # score 120 / sqrt(4) = 60
+    ctx = masked_attention(q, k, v, 1, False)
+    np.testing.assert_allclose(ctx, np.broadcast_to(v[2], (n, H)), atol=1e-20 + 1e-24)
+    causal = masked_attention(q, k, v, 1, True)   # rows 0, 1 cannot see key 2
+    np.testing.assert_allclose(causal[2:], np.broadcast_to(v[2], (n - 2, H)), atol=1e-20)
+    np.testing.assert_allclose(causal[1], v[:2].mean(0), atol=1e-14)
 
 
 @pytest.mark.parametrize("causal", [False, True])
