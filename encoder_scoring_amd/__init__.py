@@ -18,6 +18,7 @@ from .api import (  # noqa: F401
     layernorm,
     RaggedScores,
     softmax_ragged,
+    attention_fused,
     gemm_bf16,
     version,
 )

@@ -24,7 +24,7 @@ EXPORTS = [
     "es_score_requests",
     "es_forward_hidden", "es_set_reward_offset", "es_get_reward_offset", "es_calibrate_offset",
     "es_check_device_errors", "es_plan_batches", "es_pack_offsets", "es_op_layernorm", "es_op_add_layernorm",
-    "es_ragged_create", "es_ragged_free", "es_op_softmax", "es_op_gemm_bf16", "es_op_gemm_bf16_tile", "es_last_error",
+    "es_ragged_create", "es_ragged_free", "es_op_softmax", "es_op_attention", "es_op_gemm_bf16", "es_op_gemm_bf16_tile", "es_last_error",
     "es_version", "es_set_concurrency", "es_set_batch_grouping", "es_score_best_of_n", "es_set_pruning", "es_set_memory_mode", "es_memory_stats", "es_plan_arena", "es_set_attention", "es_profile_enable", "es_profile_collect", "es_kernel_class_name",
 ]
 
@@ -89,6 +89,7 @@ _SIGS = {
     "es_ragged_create": (ctypes.c_int32, [_I32P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(_P), _I64P]),
     "es_ragged_free": (None, [_P]),
     "es_op_softmax": (ctypes.c_int32, [_P, _P, _P, ctypes.c_int32, _P]),
+    "es_op_attention": (ctypes.c_int32, [_P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, _P, ctypes.c_int32, _P]),
     "es_op_gemm_bf16": (ctypes.c_int32, [_P, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P]),
     "es_op_gemm_bf16_tile": (ctypes.c_int32, [_P, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P]),
     "es_profile_enable": (ctypes.c_int32, [_P, ctypes.c_uint32]),

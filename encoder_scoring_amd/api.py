@@ -303,6 +303,20 @@ def softmax_ragged(rag, scores, probs):
                                  _dptr(probs, probs.dtype, "probs"), int(p_bf16), _stream()))
 
 
+def attention_fused(rag, qkv, ctx, head_dim, scale=None):
+    """Fused masked attention over the ragged layout (es_op_attention): qkv and
+    ctx int16 tensors of bf16 bits, [T, ld] row-major."""
+    torch = _torch()
+    lib = _lib.load()
+    if qkv.dim() != 2 or ctx.dim() != 2 or qkv.shape[0] != ctx.shape[0]:
+        raise ValueError("qkv and ctx must be [T, ld] with the same T")
+    if scale is None:
+        scale = 1.0 / float(head_dim) ** 0.5
+    check(lib, lib.es_op_attention(rag.handle, _dptr(qkv, torch.int16, "qkv"), int(qkv.stride(0)),
+                                   int(head_dim), float(scale), _dptr(ctx, torch.int16, "ctx"),
+                                   int(ctx.stride(0)), _stream()))
+
+
 def gemm_bf16(a, w, bias, out, M, N, K, epilogue, res=None, tile=None):
     """out = epilogue(A W^T + bias) on the bf16 MFMA kernel (a, w as int16 bits);
     tile forces a block-tile configuration (0..3), None chooses from the shape."""

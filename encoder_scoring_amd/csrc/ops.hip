@@ -54,7 +54,7 @@ extern "C" es_status es_ragged_create(const int32_t *h_lengths, int32_t n_seqs, 
   *out = nullptr;
   std::vector<int32_t> off(n_seqs + 1, 0);
   std::vector<int64_t> sbase(n_seqs);
-  std::vector<int32_t> items, sm_items;
+  std::vector<int32_t> items, sm_items, fitems, mitems;
   int64_t acc = 0;
   int max_len = 0;
   for (int32_t i = 0; i < n_seqs; ++i) {
@@ -69,6 +69,12 @@ extern "C" es_status es_ragged_create(const int32_t *h_lengths, int32_t n_seqs, 
       items.push_back(i);
       items.push_back(q0);
     }
+    // fused attention work, split by length as in a scoring pass
+    auto &fl = n > es::kMwMinLen ? mitems : fitems;
+    for (int q0 = 0; q0 < n; q0 += n > es::kMwMinLen ? 4 * es::kQTile : es::kQTile) {
+      fl.push_back(i);
+      fl.push_back(q0);
+    }
     for (int r0 = 0; r0 < n_heads * n; r0 += es::softmax_rows_per_item(n)) {
       sm_items.push_back(i);
       sm_items.push_back(r0);
@@ -77,7 +83,9 @@ extern "C" es_status es_ragged_create(const int32_t *h_lengths, int32_t n_seqs, 
   const size_t b_off = es::round_up((int64_t)off.size() * 4, 16);
   const size_t b_sb = es::round_up((int64_t)sbase.size() * 8, 16);
   const size_t b_it = es::round_up((int64_t)items.size() * 4, 16);
-  const size_t bytes = b_off + b_sb + b_it + sm_items.size() * 4;
+  const size_t b_sm = es::round_up((int64_t)sm_items.size() * 4, 16);
+  const size_t b_fi = es::round_up((int64_t)fitems.size() * 4, 16);
+  const size_t bytes = b_off + b_sb + b_it + b_sm + b_fi + mitems.size() * 4 + 16;
   es_ragged *g = new es_ragged();
   hipError_t e = hipMalloc(&g->dev, bytes);
   if (e == hipSuccess) e = hipMemcpy(g->dev, off.data(), off.size() * 4, hipMemcpyHostToDevice);
@@ -88,6 +96,12 @@ extern "C" es_status es_ragged_create(const int32_t *h_lengths, int32_t n_seqs, 
   if (e == hipSuccess)
     e = hipMemcpy((char *)g->dev + b_off + b_sb + b_it, sm_items.data(), sm_items.size() * 4,
                   hipMemcpyHostToDevice);
+  if (e == hipSuccess && !fitems.empty())
+    e = hipMemcpy((char *)g->dev + b_off + b_sb + b_it + b_sm, fitems.data(), fitems.size() * 4,
+                  hipMemcpyHostToDevice);
+  if (e == hipSuccess && !mitems.empty())
+    e = hipMemcpy((char *)g->dev + b_off + b_sb + b_it + b_sm + b_fi, mitems.data(),
+                  mitems.size() * 4, hipMemcpyHostToDevice);
   if (e != hipSuccess) {
     if (g->dev) (void)hipFree(g->dev);
     delete g;
@@ -100,6 +114,10 @@ extern "C" es_status es_ragged_create(const int32_t *h_lengths, int32_t n_seqs, 
   g->r.n_items = (int32_t)(items.size() / 2);
   g->r.sm_items = (const int32_t *)((char *)g->dev + b_off + b_sb + b_it);
   g->r.n_sm_items = (int32_t)(sm_items.size() / 2);
+  g->r.fused_items = (const int32_t *)((char *)g->dev + b_off + b_sb + b_it + b_sm);
+  g->r.n_fused_items = (int32_t)(fitems.size() / 2);
+  g->r.mw_items = (const int32_t *)((char *)g->dev + b_off + b_sb + b_it + b_sm + b_fi);
+  g->r.n_mw_items = (int32_t)(mitems.size() / 2);
   g->r.max_len = max_len;
   g->r.n_tokens = off[n_seqs];
   g->n_heads = n_heads;
@@ -121,6 +139,20 @@ extern "C" es_status es_op_softmax(const es_ragged *r, const float *d_scores, vo
   if (!r || !d_scores || !d_p) return fail(ES_ERR_ARG, "es_op_softmax: NULL pointer");
   HIP_TRY(es::launch_softmax(p_bf16 != 0, d_scores, d_p, r->r, r->n_heads, r->causal != 0,
                              static_cast<hipStream_t>(stream)));
+  return ES_OK;
+}
+
+extern "C" es_status es_op_attention(const es_ragged *r, const uint16_t *d_qkv, int32_t ld_qkv,
+                                     int32_t head_dim, float scale, uint16_t *d_ctx, int32_t ld_ctx,
+                                     void *stream) {
+  if (!r || !d_qkv || !d_ctx) return fail(ES_ERR_ARG, "es_op_attention: NULL pointer");
+  const int64_t width = (int64_t)r->n_heads * head_dim;
+  if ((head_dim != 32 && head_dim != 64 && head_dim != 128) || ld_qkv < 3 * width || ld_qkv % 8 ||
+      ld_ctx < width || ld_ctx % 4 || !(scale > 0.f))
+    return fail(ES_ERR_ARG, "es_op_attention: head_dim=%d ld_qkv=%d ld_ctx=%d scale=%g (n_heads=%d)",
+                head_dim, ld_qkv, ld_ctx, (double)scale, r->n_heads);
+  HIP_TRY(es::launch_attn_fused(d_qkv, ld_qkv, r->n_heads, head_dim, scale, r->causal != 0, r->r,
+                                d_ctx, ld_ctx, static_cast<hipStream_t>(stream)));
   return ES_OK;
 }
 

@@ -431,6 +431,28 @@ es_status es_op_softmax(const es_ragged *r, const float *d_scores, void *d_p, in
                         void *stream);
 
 /*
+ * es_op_attention -- masked multi-head attention over the ragged layout of
+ * `r` in one fused pass per query tile (TurboTransformers review, Proposed
+ * method: the attention scores, their Softmax row reduction and the
+ * context product; here the scores never leave registers): for sequence i,
+ * head h, query q
+ *     ctx[t0_i + q, h d + e] = sum_k softmax_k(scale * Q_q . K_k) V_k[e]
+ * over keys k < n_i (causal = 1 in `r`: k <= q).  d_qkv: bf16 bits
+ * [T, ld_qkv] row-major, T = sum of the lengths, packed in sequence order;
+ * row t holds Q | K | V, each n_heads * head_dim wide, head h at columns
+ * h * head_dim .. of each.  d_ctx: bf16 bits [T, ld_ctx], columns
+ * [0, n_heads * head_dim) written, the rest untouched.  head_dim 32, 64 or
+ * 128; ld_qkv >= 3 n_heads head_dim and a multiple of 8; ld_ctx >=
+ * n_heads head_dim and a multiple of 4; scale > 0 (normally 1 / sqrt(d)).
+ * Probabilities are rounded to bf16 before the context product, as in a
+ * scoring pass.  Asynchronous; allocates nothing; the caller owns all
+ * buffers.  Errors: ES_ERR_ARG, ES_ERR_HIP.
+ */
+es_status es_op_attention(const es_ragged *r, const uint16_t *d_qkv, int32_t ld_qkv,
+                          int32_t head_dim, float scale, uint16_t *d_ctx, int32_t ld_ctx,
+                          void *stream);
+
+/*
  * es_op_gemm_bf16 -- C = epilogue(A W^T + bias) on bf16 MFMA, fp32 accumulate.
  *   d_a  bf16[rows >= round_up(M,256), lda]  (K columns used)
  *   d_w  bf16[rows >= round_up(N,256), K]    (row n = output feature n)
