@@ -564,7 +564,9 @@ __global__ __launch_bounds__(512, 2) void gemm_pp_kernel(
   // chunk, bias (and residual) loads and output stores cover whole row
   // segments.  Rows are padded by 4 floats so both the staging writes and
   // the row reads spread over the LDS banks.  Every access is by the wave
-  // that wrote it, in program order, so no barrier is needed.
+  // that wrote it and a wave's LDS operations execute in program order, so
+  // no barrier is needed; wavefront-scope fences (no instructions) keep the
+  // compiler from moving a lane's reads of other lanes' writes across them.
   constexpr int PITCH = C::WN + 4;              // floats per staged row
   constexpr int CH = C::WN / 4;                 // 4-column chunks per row
   constexpr int RPI = 64 / CH;                  // rows per read instruction (lanes beyond
@@ -583,6 +585,7 @@ __global__ __launch_bounds__(512, 2) void gemm_pp_kernel(
       for (int g = 0; g < 4; ++g)
         *reinterpret_cast<float4 *>(stage + fr * PITCH + j * 32 + 8 * g + 4 * fh) =
             make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 #pragma unroll
     for (int r0 = 0; r0 < 32; r0 += RPI) {
       const int row = r0 + rr;
@@ -592,6 +595,7 @@ __global__ __launch_bounds__(512, 2) void gemm_pp_kernel(
         if (m < M && n < N) epi_store4_bias<EPI>(out, res, ldc, m, n, N, v, bv, bias);
       }
     }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   }
 }
 
