@@ -78,6 +78,38 @@ def test_shared_prompts_bitwise_equal_concatenated(cfg, group, lanes):
     assert torch.equal(full, rew)
 
 
+@pytest.mark.parametrize("cfg", [DEC64, DEC128], ids=["d64", "d128"])
+def test_shared_prompt_blocks_edge_cases(cfg):
+    """Prompts just below, at and above the length from which candidates of
+    a prompt share its key tiles four query tiles to a block (64), candidate
+    lengths at the tile and block limits (1, 32, 33, 64, 65), and candidate
+    counts that leave 1, 2 and 3 of a block's four slots filled: every
+    reward bitwise equal to the prompt + candidate scored as one sequence."""
+    torch = need_gpu()
+    w = make_weights(cfg)
+    rng = np.random.default_rng(31)
+    plens = [63, 64, 65, 96, 130]
+    clen_sets = [[1, 32], [33], [64, 65, 1], [32, 33, 64, 1, 2], [65, 64]]
+    prompts = [rng.integers(0, cfg.vocab, size=n).astype(np.int32) for n in plens]
+    cands, clens, counts, full = [], [], [], []
+    for p, cl in zip(prompts, clen_sets):
+        counts.append(len(cl))
+        for n in cl:
+            c = rng.integers(0, cfg.vocab, size=n).astype(np.int32)
+            cands.append(c)
+            clens.append(n)
+            full.append(np.concatenate([p, c]))
+    ids = np.concatenate(prompts + cands).astype(np.int32)
+    sc = Scorer(blob.to_bytes(cfg, w, 0.0), 1200, 512)
+    sc.set_attention("fused")
+    want = concatenated_rewards(torch, sc, full)
+    rew, best, _ = sc.score_best_of_n(torch.from_numpy(ids).cuda(), np.array(plens, np.int32),
+                                      np.array(clens, np.int32), np.array(counts, np.int32),
+                                      batch_overhead=64)
+    torch.cuda.synchronize()
+    assert torch.equal(rew, want), float((rew - want).abs().max())
+
+
 def test_shared_prompts_match_oracle():
     torch = need_gpu()
     cfg = DEC64
