@@ -122,7 +122,7 @@ def main():
     ap.add_argument("--best-of-n", action="store_true",
                     help="decoder_rm only: score through es_score_best_of_n (each prompt run once "
                          "for its candidates) instead of prompt + candidate sequences")
-    ap.add_argument("--group", type=int, default=4,
+    ap.add_argument("--group", type=int, default=5,
                     help="planned batches packed into one pass through the layers "
                          "(es_set_batch_grouping)")
     ap.add_argument("--memory", default="length_aware", choices=["length_aware", "fixed", "exact"],

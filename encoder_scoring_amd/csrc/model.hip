@@ -1025,7 +1025,8 @@ extern "C" es_status es_score_requests(es_model *m, const int32_t *d_token_ids,
   std::vector<int32_t> off, goff, src, dest;
   int64_t padded = 0;
   for (int32_t g = 0; g < ng; ++g) {
-    const int32_t b0 = g * G, b1 = std::min<int32_t>(nb, b0 + G);
+    // ng passes of as equal a batch count as possible (each at most G)
+    const int32_t b0 = (int32_t)((int64_t)g * nb / ng), b1 = (int32_t)((int64_t)(g + 1) * nb / ng);
     goff.assign(1, 0);
     src.clear();
     dest.clear();
@@ -1139,7 +1140,7 @@ extern "C" es_status es_score_best_of_n(es_model *m, const int32_t *d_token_ids,
   std::vector<int32_t> off, src, dest, pref, plen;
   int64_t padded = 0;
   for (int32_t gi = 0; gi < ng; ++gi) {
-    const int32_t b0 = gi * G, b1 = std::min<int32_t>(nb, b0 + G);
+    const int32_t b0 = (int32_t)((int64_t)gi * nb / ng), b1 = (int32_t)((int64_t)(gi + 1) * nb / ng);
     off.assign(1, 0);
     src.clear();
     dest.clear();
