@@ -719,12 +719,17 @@ hipError_t go_pp(const uint16_t *A, int lda, const uint16_t *W, const float *bia
 //          a layer sequence at 15880 x 768 x 3072: 125 -> 117 us.  For the
 //          K = 768 products, whose A panels are shared by many column tiles
 //          and already hit in L2, the same prefetch costs 5-10 %)
+//   4  T0  32 x 64, register-staged, 2 waves (32 x 32 each): the pruned last
+//          layer's GEMMs on one row per sequence (a few hundred rows), where
+//          128 x 64 blocks would leave most CUs idle (380 x 768 x 3072:
+//          27.2 -> 20.4 us)
 //                  BM  BN  BK WGM WGN PF MINW
 using T1 = Cfg<128, 64, 64, 2, 2, 2, 3>;
+using T0 = Cfg<32, 64, 64, 1, 2, 2, 3>;
 using P1 = PPCfg<128, 128>;
 using P2 = PPCfg<256, 256>;
 using P3 = PPCfg<128, 384>;
-static_assert(kGemmTiles == 4, "tile menu and launcher disagree");
+static_assert(kGemmTiles == 5, "tile menu and launcher disagree");
 
 constexpr int kCUs = 256;
 
@@ -751,14 +756,18 @@ constexpr int kCUs = 256;
 //   6144 x 2048 bias             4707 -> 4801 (same tiles; noise)
 // The 128 x 384 block is only considered for K >= 2048, and the wide blocks
 // not at all when both N and K are below 2048.  Problems too small to give
-// the 128 x 128 block half the CUs take the
-// 128 x 64 block (more, smaller blocks).  Every configuration issues the
+// the 128 x 128 block half the CUs take the 128 x 64 block (more, smaller
+// blocks), or the 32 x 64 block when even the 128 x 64 blocks would not
+// cover the CUs.  Every configuration issues the
 // same MFMA over K in the same order and K is never split, so each output's
 // accumulation order does not depend on the configuration chosen or on the
 // other sequences in the batch.
 int gemm_tile_index(int M, int N, int K, int epi) {
   const int64_t b128 = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
-  if (b128 < kCUs / 2) return 0;
+  if (b128 < kCUs / 2) {
+    const int64_t b128x64 = (int64_t)((M + 127) / 128) * ((N + 63) / 64);
+    return b128x64 < kCUs ? 4 : 0;  // fewer 128 x 64 blocks than CUs: 32 x 64
+  }
   // small N and K (the attention-out GEMM): the wide blocks time faster
   // alone but slower inside the layer sequence (15.9 k rows: 2.97 -> 3.1-3.25
   // ms per step), so the 128 x 128 block stays
@@ -803,6 +812,7 @@ hipError_t launch_gemm_bf16_tile(int tile, const uint16_t *A, int lda, const uin
       if ((N + 383) / 384 * 384 > (N + 255) / 256 * 256)
         return go_pp<P1, 0>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
       return go_pp<P3, 1>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
+    case 4: return go_bf16<T0>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
     default: return hipErrorInvalidValue;
   }
 }

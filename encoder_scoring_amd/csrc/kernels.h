@@ -109,7 +109,7 @@ hipError_t launch_gemm_bf16(const uint16_t *A, int lda, const uint16_t *W, const
                             hipStream_t st);
 // The same with one tile configuration forced: 0 = 128 x 64 register-staged,
 // 1 = 128 x 128 ping-pong, 2 = 256 x 256 ping-pong, 3 = 128 x 384 ping-pong.
-constexpr int kGemmTiles = 4;
+constexpr int kGemmTiles = 5;
 hipError_t launch_gemm_bf16_tile(int tile, const uint16_t *A, int lda, const uint16_t *W,
                                  const float *bias, const float *res, void *out, int ldc, int M,
                                  int N, int K, int epi, hipStream_t st);
