@@ -46,4 +46,8 @@ from .scheduler import (  # noqa: F401
     plan_cost,
     exhaustive_set_partition_cost,
     best_contiguous_plan,
+    plan_batches_table,
+    plan_cost_table,
+    exhaustive_set_partition_cost_table,
+    best_contiguous_plan_table,
 )

@@ -5,6 +5,11 @@
 * closed forms: c = 0 gives zero padding; equal lengths give the fewest
   batches; a huge overhead gives one batch when it fits;
 * hand-worked examples in tests/golden/hand_examples.json.
+
+The measured-cost planner (cost of a batch = a table entry C[|B|, max_len])
+has the same three kinds of pins: brute force over all set partitions and
+all contiguous plans for random length-monotone tables, a constant table
+(cost = number of batches, closed form), and hand-worked examples.
 """
 import json
 import os
@@ -12,6 +17,7 @@ import os
 import numpy as np
 import pytest
 
+import oracle
 from oracle import (best_contiguous_plan, exhaustive_set_partition_cost, pack_offsets,
                     plan_batches, plan_cost)
 
@@ -108,3 +114,64 @@ def test_pack_offsets_prefix_sums():
     assert pack_offsets(lengths, order, 0, 3).tolist() == [0, 1, 4, 7]
     assert pack_offsets(lengths, order, 3, 5).tolist() == [0, 5, 13]
     assert pack_offsets(lengths, order, 2, 2).tolist() == [0]
+
+
+# ------------------------------------------------------ measured cost table
+
+def random_monotone_table(rng, max_batch, max_len):
+    """Random integer table, non-decreasing along the length (a row per batch
+    size), with steps of 0 often enough to create ties."""
+    steps = rng.integers(0, 4, size=(max_batch, max_len)) * (rng.random((max_batch, max_len)) < 0.7)
+    return np.cumsum(steps, axis=1) + rng.integers(0, 5, size=(max_batch, 1))
+
+
+def test_table_dp_equals_exhaustive_search():
+    """Brute force over ALL set partitions (optimal cost) and over all
+    contiguous plans of the sorted order (plan and tie-break)."""
+    rng = np.random.default_rng(77)
+    for _ in range(300):
+        n = int(rng.integers(1, 8))
+        max_len = int(rng.choice([3, 6, 10]))
+        max_batch = int(rng.integers(1, 6))
+        T = int(rng.choice([max_len, 2 * max_len, 40]))
+        table = random_monotone_table(rng, max_batch, max_len)
+        lengths = rng.integers(1, max_len + 1, size=n)
+        order, starts, cost = oracle.plan_batches_table(lengths, T, table)
+        assert cost == oracle.exhaustive_set_partition_cost_table(lengths, T, table)
+        best_starts, best_cost = oracle.best_contiguous_plan_table(lengths, T, table)
+        assert (list(starts), cost) == (best_starts, best_cost)
+        assert oracle.plan_cost_table(lengths, order, list(starts), table) == cost
+        sizes = np.diff(starts)
+        assert np.all(sizes <= max_batch)
+        assert np.all(sizes * lengths[order][starts[1:] - 1] <= T)
+
+
+def test_table_hand_examples():
+    with open(os.path.join(GOLD, "hand_examples.json")) as f:
+        cases = json.load(f)["scheduler_table"]
+    for c in cases:
+        order, starts, cost = oracle.plan_batches_table(c["lengths"], c["max_tokens"], c["table"])
+        assert order.tolist() == c["order"]
+        assert starts.tolist() == c["batch_starts"]
+        assert cost == c["total_cost"]
+
+
+def test_table_constant_cost_counts_batches():
+    """C = 1 everywhere: the cost is the number of batches, so equal lengths
+    give ceil(n / min(max_batch, T // len)) batches."""
+    for n, ell, T, mb in [(10, 3, 9, 5), (10, 3, 100, 4), (1, 7, 7, 1), (33, 2, 64, 8)]:
+        table = np.ones((mb, ell), dtype=np.int64)
+        _, starts, cost = oracle.plan_batches_table([ell] * n, T, table)
+        k = min(mb, T // ell)
+        assert cost == len(starts) - 1 == -(-n // k)
+
+
+def test_table_rejects_bad_tables():
+    with pytest.raises(ValueError):
+        oracle.plan_batches_table([1, 2], 10, [[1, 0, 2]])        # falls along the length
+    with pytest.raises(ValueError):
+        oracle.plan_batches_table([1, 2], 10, [[-1, 0]])          # negative
+    with pytest.raises(ValueError):
+        oracle.plan_batches_table([3], 10, [[1, 2]])              # length beyond the table
+    order, starts, cost = oracle.plan_batches_table([], 10, [[1]])
+    assert order.size == 0 and starts.tolist() == [0] and cost == 0
