@@ -125,6 +125,9 @@ def main():
     ap.add_argument("--group", type=int, default=5,
                     help="planned batches packed into one pass through the layers "
                          "(es_set_batch_grouping)")
+    ap.add_argument("--cost-model", default="linear", choices=["linear", "measured"],
+                    help="planner cost of a batch: overhead + |B| * max_len, or a table measured "
+                         "on this GPU before the run (es_set_cost_table)")
     ap.add_argument("--memory", default="length_aware", choices=["length_aware", "fixed", "exact"],
                     help="workspace memory mode (es_set_memory_mode)")
     args = ap.parse_args()
@@ -165,6 +168,21 @@ def main():
     sc.set_concurrency(args.in_flight)
     if cfg.bf16:
         sc.set_attention(args.attention)
+    cost_note = None
+    if args.cost_model == "measured":
+        if args.best_of_n:
+            sys.exit("--cost-model measured applies to es_score_requests, not --best-of-n")
+        from encoder_scoring_amd.costmodel import dense_cost_table, measure_cost_grid
+        t = time.perf_counter()
+        cap = min(cfg.max_tokens, 65536)
+        bg = [b for b in (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048) if b * 8 <= cap]
+        lg = sorted({l for l in (8, 16, 32, 64, 128, 256, 512, 1024) if l < cfg.max_pos} | {cfg.max_pos})
+        meas = measure_cost_grid(sc, bg, lg, cfg.max_tokens, cfg.vocab)
+        sc.set_cost_table(dense_cost_table(bg, lg, meas, cfg.max_pos))
+        cost_note = (f"{int(np.sum(~np.isnan(meas)))} points, batch sizes {bg[0]}..{bg[-1]} x "
+                     f"lengths {lg[0]}..{lg[-1]}, measured in {time.perf_counter() - t:.1f} s "
+                     "before the run")
+        log("cost table: " + cost_note)
     d_ids = torch.from_numpy(ids).cuda()
     out = torch.empty(n, dtype=torch.float32, device="cuda")
     stats = None
@@ -303,7 +321,10 @@ def main():
         "config": {"workload": cfg.name, "description": WORKLOAD_DESC[cfg.name],
                    "requests": n, "tokens": n_tokens, "batches": stats["n_batches"],
                    "padded_tokens": stats["padded_tokens"], "max_tokens": cfg.max_tokens,
-                   "batch_overhead": c, "batches_per_pass": args.group,
+                   "batch_overhead": c if cost_note is None else None,
+                   "cost_model": args.cost_model if cost_note is None else
+                   {"kind": "measured", "grid": cost_note},
+                   "batches_per_pass": args.group,
                    "passes_in_flight": args.in_flight,
                    "attention": ("fused" if args.best_of_n else args.attention) if cfg.bf16 else "unfused",
                    "shared_prompts": bool(args.best_of_n),

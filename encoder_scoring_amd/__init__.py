@@ -7,12 +7,14 @@ provides device memory and the current stream):
     Scorer.score(d_ids, offsets)             one packed batch -> rewards (device)
     Scorer.score_requests(d_ids, lengths)    plan + pack + score + scatter a stream
     plan_batches(lengths, max_tokens, c)     host DP batch planner
+    plan_batches_measured(lengths, T, C)     the same DP under a measured cost table C[b-1, l-1]
     pack_offsets(lengths, order, b, e)       packed offsets of one planned batch
     plan_arena(bytes, first, last, align)    offsets of tensors with lifetimes (workspace planner)
 """
 from .api import (  # noqa: F401
     Scorer,
     plan_batches,
+    plan_batches_measured,
     pack_offsets,
     plan_arena,
     layernorm,

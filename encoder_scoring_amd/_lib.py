@@ -23,7 +23,7 @@ EXPORTS = [
     "es_load_weights", "es_load_weights_mem", "es_free", "es_model_info", "es_score_batch",
     "es_score_requests",
     "es_forward_hidden", "es_set_reward_offset", "es_get_reward_offset", "es_calibrate_offset",
-    "es_check_device_errors", "es_plan_batches", "es_pack_offsets", "es_op_layernorm", "es_op_add_layernorm",
+    "es_check_device_errors", "es_plan_batches", "es_plan_batches_measured", "es_set_cost_table", "es_pack_offsets", "es_op_layernorm", "es_op_add_layernorm",
     "es_ragged_create", "es_ragged_free", "es_op_softmax", "es_op_attention", "es_op_gemm_bf16", "es_op_gemm_bf16_tile", "es_last_error",
     "es_version", "es_set_concurrency", "es_set_batch_grouping", "es_score_best_of_n", "es_set_pruning", "es_set_memory_mode", "es_memory_stats", "es_plan_arena", "es_set_attention", "es_profile_enable", "es_profile_collect", "es_kernel_class_name",
 ]
@@ -83,6 +83,8 @@ _SIGS = {
     "es_set_memory_mode": (ctypes.c_int32, [_P, ctypes.c_int32]),
     "es_memory_stats": (ctypes.c_int32, [_P, _P, ctypes.c_int32]),
     "es_plan_batches": (ctypes.c_int32, [_I32P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, _I32P, _I32P, _I32P, _I64P]),
+    "es_plan_batches_measured": (ctypes.c_int32, [_I32P, ctypes.c_int32, ctypes.c_int64, _I64P, ctypes.c_int32, ctypes.c_int32, _I32P, _I32P, _I32P, _I64P]),
+    "es_set_cost_table": (ctypes.c_int32, [_P, _I64P, ctypes.c_int32, ctypes.c_int32]),
     "es_pack_offsets": (ctypes.c_int32, [_I32P, _I32P, ctypes.c_int32, ctypes.c_int32, _I32P]),
     "es_op_layernorm": (ctypes.c_int32, [_P, _P, _P, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, _P, _P, ctypes.c_int32, _P]),
     "es_op_add_layernorm": (ctypes.c_int32, [_P, _P, _P, _P, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, _P, _P, ctypes.c_int32, _P]),
@@ -124,7 +126,7 @@ def load(path=None):
 def load_host(path):
     """Load a host-only build (planner + blob parser) with the planner signatures."""
     lib = ctypes.CDLL(path)
-    for name in ("es_plan_batches", "es_pack_offsets", "es_plan_arena", "es_last_error", "es_version"):
+    for name in ("es_plan_batches", "es_plan_batches_measured", "es_pack_offsets", "es_plan_arena", "es_last_error", "es_version"):
         res, args = _SIGS[name]
         fn = getattr(lib, name)
         fn.restype, fn.argtypes = res, args

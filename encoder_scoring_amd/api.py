@@ -52,6 +52,26 @@ def plan_batches(lengths, max_tokens, batch_overhead, lib=None):
     return order, starts[: nb.value + 1].copy(), cost.value
 
 
+def plan_batches_measured(lengths, max_tokens, cost_table, lib=None):
+    """Host DP planner under a measured cost table (es_plan_batches_measured):
+    cost_table[b-1, l-1] is the cost of b sequences whose longest has l
+    tokens -> (order int32[n], batch_starts int32[B+1], total_cost)."""
+    lib = lib or _lib.load()
+    lengths = as_i32(lengths)
+    table = np.ascontiguousarray(cost_table, dtype=np.int64)
+    if table.ndim != 2:
+        raise ValueError("cost_table must be 2-D [max_batch, max_len]")
+    n = lengths.size
+    order = np.zeros(n, dtype=np.int32)
+    starts = np.zeros(n + 1, dtype=np.int32)
+    nb = ctypes.c_int32()
+    cost = ctypes.c_int64()
+    check(lib, lib.es_plan_batches_measured(
+        i32p(lengths), n, int(max_tokens), table.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+        table.shape[0], table.shape[1], i32p(order), i32p(starts), ctypes.byref(nb), ctypes.byref(cost)))
+    return order, starts[: nb.value + 1].copy(), cost.value
+
+
 def plan_arena(nbytes, first_step, last_step, align=1, lib=None):
     """Offsets of tensors with step lifetimes in one arena (es_plan_arena)
     -> (offsets int64[n], total bytes)."""
@@ -203,6 +223,20 @@ class Scorer:
     def set_grouping(self, batches_per_pass):
         """Planned batches score_requests packs into one pass (es_set_batch_grouping)."""
         check(self.lib, self.lib.es_set_batch_grouping(self.handle, int(batches_per_pass)))
+
+    def set_cost_table(self, cost_table):
+        """Plan score_requests with measured batch costs (es_set_cost_table):
+        cost_table[b-1, l-1] = cost of b sequences whose longest has l tokens;
+        None goes back to the linear cost."""
+        if cost_table is None:
+            check(self.lib, self.lib.es_set_cost_table(self.handle, None, 0, 0))
+            return
+        table = np.ascontiguousarray(cost_table, dtype=np.int64)
+        if table.ndim != 2:
+            raise ValueError("cost_table must be 2-D [max_batch, max_len]")
+        check(self.lib, self.lib.es_set_cost_table(
+            self.handle, table.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+            table.shape[0], table.shape[1]))
 
     def set_pruning(self, enabled):
         """Last layer on the last tokens only (default on; es_set_pruning)."""

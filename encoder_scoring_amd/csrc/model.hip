@@ -88,6 +88,10 @@ struct es_model {
   std::vector<Workspace> ws;  // allocated workspaces; the first `lanes` are used
   int lanes = 1;
   int group = 1;  // planned batches scored by one pass through the layers
+  // measured batch costs for es_score_requests' planner (es_set_cost_table);
+  // empty: the linear cost overhead + |B| * max_len
+  std::vector<int64_t> cost_table;
+  int32_t cost_max_batch = 0, cost_max_len = 0;
   bool prune = true;  // last layer on the last token of each sequence only (es_set_pruning)
   hipEvent_t fork_ev = nullptr;
   float *rew = nullptr;  // raw rewards of a reference set (es_calibrate_offset)
@@ -1002,9 +1006,14 @@ extern "C" es_status es_score_requests(es_model *m, const int32_t *d_token_ids,
   std::vector<int32_t> order((size_t)n), starts((size_t)n + 1);
   int32_t nb = 0;
   int64_t cost = 0;
-  if ((s = es_plan_batches(h_lengths, n, m->max_tokens, batch_overhead, order.data(),
-                           starts.data(), &nb, &cost)) != ES_OK)
-    return s;
+  if (m->cost_table.empty())
+    s = es_plan_batches(h_lengths, n, m->max_tokens, batch_overhead, order.data(), starts.data(),
+                        &nb, &cost);
+  else  // the table's first max_seqs rows: no planned batch outgrows a workspace
+    s = es_plan_batches_measured(h_lengths, n, m->max_tokens, m->cost_table.data(),
+                                 std::min(m->cost_max_batch, m->max_seqs), m->cost_max_len,
+                                 order.data(), starts.data(), &nb, &cost);
+  if (s != ES_OK) return s;
   // request-order start of every sequence's ids in d_token_ids
   std::vector<int32_t> first((size_t)n);
   int64_t acc = 0;
@@ -1258,6 +1267,27 @@ extern "C" es_status es_set_batch_grouping(es_model *m, int32_t batches_per_pass
       if (s != ES_OK) return s;
     }
   }
+  return ES_OK;
+}
+
+extern "C" es_status es_set_cost_table(es_model *m, const int64_t *cost_table, int32_t max_batch,
+                                       int32_t max_len) {
+  if (!m) return fail(ES_ERR_ARG, "model handle is NULL");
+  if (!cost_table) {
+    m->cost_table.clear();
+    m->cost_max_batch = m->cost_max_len = 0;
+    return ES_OK;
+  }
+  if (max_len < m->P) return fail(ES_ERR_ARG, "cost table max_len=%d below max_pos=%d", max_len, m->P);
+  // the planner's own checks of the table (entries, monotone rows, size)
+  int32_t start0 = 0, nb = 0;
+  int64_t cost = 0;
+  es_status s = es_plan_batches_measured(nullptr, 0, m->max_tokens, cost_table, max_batch, max_len,
+                                         nullptr, &start0, &nb, &cost);
+  if (s != ES_OK) return s;
+  m->cost_table.assign(cost_table, cost_table + (size_t)max_batch * max_len);
+  m->cost_max_batch = max_batch;
+  m->cost_max_len = max_len;
   return ES_OK;
 }
 

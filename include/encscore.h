@@ -131,7 +131,8 @@ es_status es_score_batch(es_model *m, const int32_t *d_token_ids, const int32_t 
 /* Plan / work summary of one es_score_requests call. */
 typedef struct {
   int32_t n_batches;     /* batches the planner formed                           */
-  int64_t total_cost;    /* planner objective: sum of overhead + |B| * max_len   */
+  int64_t total_cost;    /* planner objective: sum of overhead + |B| * max_len,  */
+                         /* or of the cost table's entries (es_set_cost_table) */
   int64_t padded_tokens; /* sum over batches of |B| * max_len(B)                 */
   int64_t packed_tokens; /* tokens actually computed (no padding)                */
 } es_stream_stats_t;
@@ -288,6 +289,20 @@ es_status es_set_pruning(es_model *m, int32_t enabled);
 es_status es_set_batch_grouping(es_model *m, int32_t batches_per_pass);
 
 /*
+ * es_set_cost_table -- make es_score_requests plan with measured batch costs
+ * (es_plan_batches_measured; TurboTransformers review, Proposed method: the
+ * DP batch scheduler) instead of batch_overhead + |B| * max_len.  The table
+ * has the layout es_plan_batches_measured documents and is copied; only its
+ * first max_seqs rows are used, so no planned batch has more sequences than a
+ * workspace holds, and batch_overhead is then ignored.  cost_table = NULL
+ * goes back to the linear cost.  es_score_best_of_n keeps the linear cost
+ * (its items are prompt groups, not sequences).  Errors: ES_ERR_ARG (a table
+ * es_plan_batches_measured rejects, or max_len below the model's max_pos).
+ */
+es_status es_set_cost_table(es_model *m, const int64_t *cost_table, int32_t max_batch,
+                            int32_t max_len);
+
+/*
  * es_set_attention -- how the masked attention of each layer runs (bf16
  * models): 0 (default) = three kernels, scores to HBM, the Softmax row
  * reduction (TurboTransformers review, Proposed method), then P.V; 1 = one
@@ -341,6 +356,32 @@ es_status es_check_device_errors(es_model *m, void *stream);
 es_status es_plan_batches(const int32_t *lengths, int32_t n, int64_t max_tokens,
                           int64_t batch_overhead, int32_t *order, int32_t *batch_starts,
                           int32_t *n_batches, int64_t *total_cost);
+
+/*
+ * es_plan_batches_measured -- host-only batch planner under a measured cost
+ * table (never touches HIP).
+ *
+ * TurboTransformers review (Abstract; Proposed method): the DP batch
+ * scheduler aims at throughput on variable-length requests; here the cost of
+ * a batch is what it was measured to take instead of a linear formula.
+ * Reading used: minimise  sum_B C[|B|-1][max_len(B)-1]  subject to
+ * |B| <= max_batch and |B| * max_len(B) <= max_tokens.
+ *   cost_table  int64[max_batch * max_len], row-major: entry
+ *               [(b-1) * max_len + (l-1)] is the cost of b sequences whose
+ *               longest has l tokens, in any unit (e.g. ns).  Every entry
+ *               >= 0 and every row non-decreasing in l (then contiguous
+ *               batches of the length-sorted order are optimal over all
+ *               partitions).  Read only during the call.
+ *   order, batch_starts, n_batches, total_cost: as es_plan_batches, with the
+ *               same tie rule (first minimising split point).
+ * Errors: ES_ERR_ARG (NULL pointers, n < 0, max_tokens < 1, a table of
+ * fewer than 1 or more than 2^28 entries, a negative, too large or falling
+ * entry), ES_ERR_RANGE (a length < 1 or above max_tokens or max_len).
+ */
+es_status es_plan_batches_measured(const int32_t *lengths, int32_t n, int64_t max_tokens,
+                                   const int64_t *cost_table, int32_t max_batch, int32_t max_len,
+                                   int32_t *order, int32_t *batch_starts, int32_t *n_batches,
+                                   int64_t *total_cost);
 
 /*
  * es_pack_offsets -- host-only: offsets[0] = 0, offsets[k+1] = offsets[k] +

@@ -12,7 +12,8 @@ import pytest
 
 import oracle
 from oracle import memplan
-from encoder_scoring_amd import _lib, blob, pack_offsets, plan_arena, plan_batches
+from encoder_scoring_amd import _lib, blob, pack_offsets, plan_arena, plan_batches, plan_batches_measured
+from encoder_scoring_amd.costmodel import dense_cost_table
 from encoder_scoring_amd._lib import EncScoreError
 from synth import CONFIGS, get_config, make_requests, make_weights
 from synth.configs import ORDERED
@@ -105,6 +106,107 @@ def test_planner_empty_and_null():
 def test_pack_offsets_errors():
     with pytest.raises(EncScoreError):
         pack_offsets([1, 2], [0, 1], 2, 1)
+
+
+# ------------------------------------------------------------------ measured-cost planner
+
+def _monotone_table(rng, max_batch, max_len, step=4):
+    steps = rng.integers(0, step, size=(max_batch, max_len)) * (rng.random((max_batch, max_len)) < 0.7)
+    return np.cumsum(steps, axis=1) + rng.integers(0, 5, size=(max_batch, 1))
+
+
+def test_measured_planner_matches_oracle_random():
+    rng = np.random.default_rng(31)
+    for _ in range(300):
+        n = int(rng.integers(0, 60))
+        max_len = int(rng.choice([4, 20, 64]))
+        max_batch = int(rng.integers(1, 40))
+        T = int(rng.choice([max_len, 3 * max_len, 300]))
+        table = _monotone_table(rng, max_batch, max_len)
+        lengths = rng.integers(1, max_len + 1, size=n)
+        got = plan_batches_measured(lengths, T, table)
+        want = oracle.plan_batches_table(lengths, T, table)
+        assert np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1])
+        assert got[2] == want[2]
+
+
+def test_measured_planner_matches_exhaustive_small():
+    rng = np.random.default_rng(6)
+    for _ in range(150):
+        n = int(rng.integers(1, 8))
+        max_len, max_batch = 6, int(rng.integers(1, 5))
+        T = int(rng.choice([6, 12, 20]))
+        table = _monotone_table(rng, max_batch, max_len)
+        lengths = rng.integers(1, 7, size=n)
+        _, starts, cost = plan_batches_measured(lengths, T, table)
+        assert cost == oracle.exhaustive_set_partition_cost_table(lengths, T, table)
+        assert list(starts) == oracle.best_contiguous_plan_table(lengths, T, table)[0]
+
+
+@pytest.mark.parametrize("name", ["bert_base_short", "bert_base_longtail"])
+def test_linear_table_reproduces_the_linear_planner(name):
+    """C[b, l] = c + b * l is the linear cost: the same plan, bit for bit."""
+    cfg = get_config(name)
+    _, lengths, _ = make_requests(cfg)
+    T, c = cfg.max_tokens, cfg.batch_overhead
+    P = int(lengths.max())
+    b = np.arange(1, T + 1, dtype=np.int64)[:, None]
+    table = c + b * np.arange(1, P + 1, dtype=np.int64)[None, :]
+    got = plan_batches_measured(lengths, T, table)
+    want = plan_batches(lengths, T, c)
+    for g, w in zip(got, want):
+        assert np.array_equal(g, w)
+
+
+@pytest.mark.parametrize("table,lengths,T,code", [
+    ([[1, 0, 2]], [1], 10, _lib.ES_ERR_ARG),           # falls along the length
+    ([[-1, 0]], [1], 10, _lib.ES_ERR_ARG),             # negative entry
+    ([[2 ** 62, 2 ** 62]], [1], 10, _lib.ES_ERR_ARG),  # too large for int64 sums
+    ([[1, 2]], [3], 10, _lib.ES_ERR_RANGE),            # longer than the table
+    ([[1, 2, 3]], [3], 2, _lib.ES_ERR_RANGE),          # longer than the budget
+    ([[1, 2]], [1], 0, _lib.ES_ERR_ARG),               # max_tokens < 1
+])
+def test_measured_planner_errors(table, lengths, T, code):
+    with pytest.raises(EncScoreError) as e:
+        plan_batches_measured(lengths, T, np.array(table, dtype=np.int64))
+    assert e.value.status == code
+
+
+def test_measured_planner_empty_and_null():
+    order, starts, cost = plan_batches_measured([], 10, np.ones((2, 3), dtype=np.int64))
+    assert order.size == 0 and starts.tolist() == [0] and cost == 0
+    lib = _lib.load()
+    nb, cost = ctypes.c_int32(), ctypes.c_int64()
+    st = lib.es_plan_batches_measured(None, 0, 10, None, 1, 1, None, None, ctypes.byref(nb),
+                                      ctypes.byref(cost))
+    assert st == _lib.ES_ERR_ARG
+
+
+def test_dense_cost_table_is_exact_on_bilinear_costs():
+    """Piecewise-linear in the batch size, then in the length, reproduces a
+    function linear in each (also past the last measured size, and where
+    corners beyond the token budget were not measured)."""
+    f = lambda b, l: 0.02 + 0.001 * b + 0.0004 * l + 0.00003 * b * l   # ms
+    bg, lg = [1, 2, 4, 8, 16], [1, 16, 64, 128]
+    meas = np.array([[f(b, l) if b * l <= 512 else np.nan for l in lg] for b in bg])
+    table = dense_cost_table(bg, lg, meas, 160)
+    assert table.shape == (16, 160)
+    b = np.arange(1, 17)[:, None]
+    l = np.arange(1, 161)[None, :]
+    assert np.abs(table - f(b, l) * 1e6).max() <= 1.0                    # ns rounding (+ fp)
+    assert np.all(np.diff(table, axis=1) >= 0)
+
+
+def test_dense_cost_table_clamps_and_is_monotone():
+    bg, lg = [1, 4], [8, 32]
+    meas = np.array([[1.0, 0.5], [2.0, 3.0]])                     # falls along the length at b = 1
+    table = dense_cost_table(bg, lg, meas, 40)
+    assert np.all(np.diff(table, axis=1) >= 0) and np.all(table >= 0)
+    assert np.all(table[0, :8] == 1_000_000)                       # below the grid: the first point
+    assert np.all(table[0, 8:] == 1_000_000)                       # running maximum keeps 1 ms
+    assert table[3, 7] == 2_000_000 and table[3, 31] == 3_000_000
+    with pytest.raises(ValueError):
+        dense_cost_table([2, 1], lg, meas, 40)
 
 
 # ------------------------------------------------------------------ arena planner
