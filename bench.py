@@ -177,7 +177,7 @@ def main():
         cap = min(cfg.max_tokens, 65536)
         bg = [b for b in (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048) if b * 8 <= cap]
         lg = sorted({l for l in (8, 16, 32, 64, 128, 256, 512, 1024) if l < cfg.max_pos} | {cfg.max_pos})
-        meas = measure_cost_grid(sc, bg, lg, cfg.max_tokens, cfg.vocab)
+        meas = measure_cost_grid(sc, bg, lg)
         sc.set_cost_table(dense_cost_table(bg, lg, meas, cfg.max_pos))
         cost_note = (f"{int(np.sum(~np.isnan(meas)))} points, batch sizes {bg[0]}..{bg[-1]} x "
                      f"lengths {lg[0]}..{lg[-1]}, measured in {time.perf_counter() - t:.1f} s "

@@ -73,19 +73,23 @@ def dense_cost_table(batch_grid, len_grid, measured_ms, max_len):
     return np.maximum.accumulate(ns, axis=1)
 
 
-def measure_cost_grid(scorer, batch_grid, len_grid, max_tokens, vocab, reps=5, warmup=2, seed=0):
-    """Median time (ms) of one forward pass of b sequences of l tokens for
-    every (b, l) of the grids with b * l <= max_tokens (NaN elsewhere), timed
-    with events on the current stream."""
+def measure_cost_grid(scorer, batch_grid, len_grid, reps=5, warmup=2, seed=0):
+    """Median time (ms) of one forward pass of b sequences of l tokens (ids
+    drawn uniformly from the vocabulary) for every (b, l) of the grids that
+    the handle can score in one batch -- b <= max_seqs, l <= max_pos,
+    b * l <= max_tokens -- and NaN elsewhere; timed with events on the
+    current stream."""
     import torch
+    info = scorer.info
     rng = np.random.default_rng(seed)
     out = np.full((len(batch_grid), len(len_grid)), np.nan)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     for i, b in enumerate(batch_grid):
         for j, l in enumerate(len_grid):
-            if b * l > max_tokens:
+            if b > info.max_seqs or l > info.max_pos or b * l > info.max_tokens:
                 continue
-            d_ids = torch.from_numpy(rng.integers(0, vocab, size=b * l).astype(np.int32)).cuda()
+            ids = rng.integers(0, info.vocab, size=b * l).astype(np.int32)
+            d_ids = torch.from_numpy(ids).cuda()
             offsets = (np.arange(b + 1) * l).astype(np.int32)
             rew = torch.empty(b, dtype=torch.float32, device="cuda")
             times = []

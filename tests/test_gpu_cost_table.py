@@ -64,22 +64,22 @@ def test_cost_table_plans_and_keeps_rewards():
 def test_measured_table_end_to_end():
     torch = need_gpu()
     sc = Scorer(blob.to_bytes(CFG, make_weights(CFG), 0.0), T, MAX_SEQS)
-    bg, lg = [1, 4, 16, 48], [8, 32, 100, 200]
-    meas = measure_cost_grid(sc, bg, lg, T, CFG.vocab, reps=3, warmup=1)
+    bg, lg = [1, 4, 16, 48, 64], [8, 32, 100, 200, 256]      # 64 > max_seqs, 256 > max_pos
+    meas = measure_cost_grid(sc, bg, lg, reps=3, warmup=1)
     say("measured grid (ms):", np.round(meas, 3).tolist())
     for i, bb in enumerate(bg):
         for j, ll in enumerate(lg):
-            assert np.isnan(meas[i, j]) == (bb * ll > T)
+            assert np.isnan(meas[i, j]) == (bb * ll > T or bb > MAX_SEQS or ll > CFG.max_pos)
     assert np.all(meas[~np.isnan(meas)] > 0)
     table = dense_cost_table(bg, lg, meas, CFG.max_pos)
-    assert table.shape == (48, CFG.max_pos)
+    assert table.shape == (64, CFG.max_pos)
     ids, lengths = random_stream(42, 150, 1, 200, CFG.vocab)
     d = torch.from_numpy(ids).cuda()
     base, _ = run(torch, sc, d, lengths)
     sc.set_cost_table(table)
     got, st = run(torch, sc, d, lengths)
     assert torch.equal(got, base)
-    _, starts, cost = oracle.plan_batches_table(lengths, T, table)
+    _, starts, cost = oracle.plan_batches_table(lengths, T, table[:MAX_SEQS])
     assert st["n_batches"] == len(starts) - 1 and st["total_cost"] == cost
 
 
