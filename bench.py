@@ -299,6 +299,30 @@ def main():
                                           "kernels": class_table(pc_other)}
         sc.set_attention(args.attention)
 
+    # fixed-length batches at batch 1 (latency) and batch 64 (throughput):
+    # one es_score_batch call each, host-synchronised, wall clock per call
+    latency = None
+    if cfg.name == "tinybert":
+        latency = {}
+        for seq_len in (64, 128, 256):
+            for batch in (1, 64):
+                fid, flen = make_fixed_batch(cfg, seq_len, batch)
+                d_f = torch.from_numpy(fid).cuda()
+                f_off = np.concatenate([[0], np.cumsum(flen)]).astype(np.int32)
+                r_f = torch.empty(batch, dtype=torch.float32, device="cuda")
+                walls = []
+                for it in range(10 + 200):
+                    torch.cuda.synchronize()
+                    ta = time.perf_counter()
+                    sc.score(d_f, f_off, out=r_f)
+                    torch.cuda.synchronize()
+                    if it >= 10:
+                        walls.append((time.perf_counter() - ta) * 1e3)
+                med = float(np.median(walls))
+                latency[f"len{seq_len}_batch{batch}"] = {
+                    "ms_median": round(med, 4), "ms_p99": round(float(np.percentile(walls, 99)), 4),
+                    "sequences_per_s": round(batch / (med / 1e3), 1)}
+
     # the workspace the fixed mode would hold for the same settings
     sc.set_memory_mode("fixed")
     fixed_bytes = sc.memory_stats()["work_bytes"]
@@ -339,6 +363,7 @@ def main():
         "memory": line_mem,
         "kernels": kernels,
         "variants": variants,
+        "fixed_length_calls": latency,
         "device": torch.cuda.get_device_name(0),
     }
     if not args.no_cpu_baseline:
