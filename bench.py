@@ -104,6 +104,36 @@ def cpu_baseline(cfg, weights, ids, lengths, budget_s):
             "tokens_per_s": round(tokens / dt, 1)}
 
 
+def fixed_length_calls(sc, cfg):
+    """Fixed-length batches at batch 1 (latency) and batch 64 (throughput):
+    one es_score_batch call each, host-synchronised, wall clock per call,
+    median and 99th percentile of 200 after 10 warm-up calls."""
+    import numpy as np
+    import torch
+    from synth import make_fixed_batch
+    latency = {}
+    for seq_len in (64, 128, 256):
+        for batch in (1, 64):
+            fid, flen = make_fixed_batch(cfg, seq_len, batch)
+            d_f = torch.from_numpy(fid).cuda()
+            f_off = np.concatenate([[0], np.cumsum(flen)]).astype(np.int32)
+            r_f = torch.empty(batch, dtype=torch.float32, device="cuda")
+            walls = []
+            for it in range(10 + 200):
+                torch.cuda.synchronize()
+                ta = time.perf_counter()
+                sc.score(d_f, f_off, out=r_f)
+                torch.cuda.synchronize()
+                if it >= 10:
+                    walls.append((time.perf_counter() - ta) * 1e3)
+            assert torch.isfinite(r_f).all().item(), "non-finite rewards"
+            med = float(np.median(walls))
+            latency[f"len{seq_len}_batch{batch}"] = {
+                "ms_median": round(med, 4), "ms_p99": round(float(np.percentile(walls, 99)), 4),
+                "sequences_per_s": round(batch / (med / 1e3), 1)}
+    return latency
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -128,6 +158,9 @@ def main():
     ap.add_argument("--cost-model", default="linear", choices=["linear", "measured"],
                     help="planner cost of a batch: overhead + |B| * max_len, or a table measured "
                          "on this GPU before the run (es_set_cost_table)")
+    ap.add_argument("--fixed-length-only", action="store_true",
+                    help="tinybert only: time the fixed-length calls (lengths 64/128/256 at batch "
+                         "1 and 64) and print them alone, without the stream")
     ap.add_argument("--memory", default="length_aware", choices=["length_aware", "fixed", "exact"],
                     help="workspace memory mode (es_set_memory_mode)")
     args = ap.parse_args()
@@ -183,6 +216,12 @@ def main():
                      f"lengths {lg[0]}..{lg[-1]}, measured in {time.perf_counter() - t:.1f} s "
                      "before the run")
         log("cost table: " + cost_note)
+    if args.fixed_length_only:
+        if cfg.name != "tinybert":
+            sys.exit("--fixed-length-only applies to the tinybert workload")
+        print(json.dumps({"workload": cfg.name, "fixed_length_calls": fixed_length_calls(sc, cfg)}),
+              flush=True)
+        return
     d_ids = torch.from_numpy(ids).cuda()
     out = torch.empty(n, dtype=torch.float32, device="cuda")
     stats = None
@@ -299,29 +338,7 @@ def main():
                                           "kernels": class_table(pc_other)}
         sc.set_attention(args.attention)
 
-    # fixed-length batches at batch 1 (latency) and batch 64 (throughput):
-    # one es_score_batch call each, host-synchronised, wall clock per call
-    latency = None
-    if cfg.name == "tinybert":
-        latency = {}
-        for seq_len in (64, 128, 256):
-            for batch in (1, 64):
-                fid, flen = make_fixed_batch(cfg, seq_len, batch)
-                d_f = torch.from_numpy(fid).cuda()
-                f_off = np.concatenate([[0], np.cumsum(flen)]).astype(np.int32)
-                r_f = torch.empty(batch, dtype=torch.float32, device="cuda")
-                walls = []
-                for it in range(10 + 200):
-                    torch.cuda.synchronize()
-                    ta = time.perf_counter()
-                    sc.score(d_f, f_off, out=r_f)
-                    torch.cuda.synchronize()
-                    if it >= 10:
-                        walls.append((time.perf_counter() - ta) * 1e3)
-                med = float(np.median(walls))
-                latency[f"len{seq_len}_batch{batch}"] = {
-                    "ms_median": round(med, 4), "ms_p99": round(float(np.percentile(walls, 99)), 4),
-                    "sequences_per_s": round(batch / (med / 1e3), 1)}
+    latency = fixed_length_calls(sc, cfg) if cfg.name == "tinybert" else None
 
     # the workspace the fixed mode would hold for the same settings
     sc.set_memory_mode("fixed")
