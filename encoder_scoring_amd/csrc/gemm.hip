@@ -259,9 +259,9 @@ __global__ __launch_bounds__(C::NT, C::MINW) void gemm_bf16_kernel(
   Stage<C, BN> rb0, rb1;
   load_stage<C, BM>(ra0, Ag, lda, 0, tid);
   load_stage<C, BN>(rb0, Wg, K, 0, tid);
-  if (C::PF == 2 && nk > 1) {
-    load_stage<C, BM>(ra1, Ag, lda, BK, tid);
-    load_stage<C, BN>(rb1, Wg, K, BK, tid);
+  if (C::PF == 2) {  // tile 1 (tile 0 again when K has one step: see below)
+    load_stage<C, BM>(ra1, Ag, lda, min(1, nk - 1) * BK, tid);
+    load_stage<C, BN>(rb1, Wg, K, min(1, nk - 1) * BK, tid);
   }
   store_stage<C, BM>(ra0, sA[0], tid);
   store_stage<C, BN>(rb0, sB[0], tid);
@@ -270,12 +270,13 @@ __global__ __launch_bounds__(C::NT, C::MINW) void gemm_bf16_kernel(
   if (C::PF == 2) {
     // LDS buffer kt & 1 holds tile kt, register set (kt + 1) & 1 holds tile
     // kt + 1, loads of tile kt + 2 go into the free set.  Unrolled by two so
-    // both register sets are fixed names.
+    // both register sets are fixed names.  The loads are issued on every
+    // step, past the end at tile nk - 1 again (in bounds, never stored): a
+    // load under a branch makes the compiler's wait before the next LDS
+    // store drain every load in flight, which left one step of prefetch.
     for (int kt = 0; kt < nk; kt += 2) {
-      if (kt + 2 < nk) {
-        load_stage<C, BM>(ra0, Ag, lda, (kt + 2) * BK, tid);
-        load_stage<C, BN>(rb0, Wg, K, (kt + 2) * BK, tid);
-      }
+      load_stage<C, BM>(ra0, Ag, lda, min(kt + 2, nk - 1) * BK, tid);
+      load_stage<C, BN>(rb0, Wg, K, min(kt + 2, nk - 1) * BK, tid);
       mma_tile(0);
       if (kt + 1 < nk) {
         store_stage<C, BM>(ra1, sA[1], tid);
@@ -283,10 +284,8 @@ __global__ __launch_bounds__(C::NT, C::MINW) void gemm_bf16_kernel(
       }
       __syncthreads();
       if (kt + 1 >= nk) break;
-      if (kt + 3 < nk) {
-        load_stage<C, BM>(ra1, Ag, lda, (kt + 3) * BK, tid);
-        load_stage<C, BN>(rb1, Wg, K, (kt + 3) * BK, tid);
-      }
+      load_stage<C, BM>(ra1, Ag, lda, min(kt + 3, nk - 1) * BK, tid);
+      load_stage<C, BN>(rb1, Wg, K, min(kt + 3, nk - 1) * BK, tid);
       mma_tile(1);
       if (kt + 2 < nk) {
         store_stage<C, BM>(ra0, sA[0], tid);
