@@ -31,19 +31,24 @@ __device__ __forceinline__ void store4(uint16_t *p, float4 v) {
 // LayerNorm of one row held as NC float4 chunks per lane (chunk c4 = lane + 64 j).
 // Two passes over registers: mean, then the biased variance of (x - mean).
 // Gains and shifts are loaded before the reductions so their latency overlaps.
+// The affine parameters of the columns a lane owns (unconditional loads at
+// in-bounds chunks, so they can be issued together with the row's own).
 template <int NC>
-__device__ __forceinline__ void ln_row(float4 (&v)[NC], int lane, int c4n, int cols,
-                                       const float *__restrict__ g, const float *__restrict__ b,
-                                       float eps) {
-  float4 gg[NC], bb[NC];
+__device__ __forceinline__ void ln_load_affine(float4 (&gg)[NC], float4 (&bb)[NC], int lane, int c4n,
+                                               const float *__restrict__ g,
+                                               const float *__restrict__ b) {
 #pragma unroll
   for (int j = 0; j < NC; ++j) {
-    const int c4 = lane + kWave * j;
-    if (c4 < c4n) {
-      gg[j] = load4(g + 4 * c4);
-      bb[j] = load4(b + 4 * c4);
-    }
+    const int c4 = min(lane + kWave * j, c4n - 1);
+    gg[j] = load4(g + 4 * c4);
+    bb[j] = load4(b + 4 * c4);
   }
+}
+
+template <int NC>
+__device__ __forceinline__ void ln_apply(float4 (&v)[NC], const float4 (&gg)[NC],
+                                         const float4 (&bb)[NC], int lane, int c4n, int cols,
+                                         float eps) {
   float s = 0.f;
 #pragma unroll
   for (int j = 0; j < NC; ++j)
@@ -71,6 +76,15 @@ __device__ __forceinline__ void ln_row(float4 (&v)[NC], int lane, int c4n, int c
   }
 }
 
+template <int NC>
+__device__ __forceinline__ void ln_row(float4 (&v)[NC], int lane, int c4n, int cols,
+                                       const float *__restrict__ g, const float *__restrict__ b,
+                                       float eps) {
+  float4 gg[NC], bb[NC];
+  ln_load_affine<NC>(gg, bb, lane, c4n, g, b);
+  ln_apply<NC>(v, gg, bb, lane, c4n, cols, eps);
+}
+
 // With ADD, the row is x + sub (a residual connection followed by its
 // LayerNorm); y may alias x or sub: a wavefront reads its whole row before
 // it writes any of it.
@@ -85,17 +99,30 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float *x, const fl
   if (row >= rows) return;
   const int c4n = cols >> 2;
   const float *xr = x + row * cols;
-  float4 v[NC];
+  // every load is issued before any is used, at an in-bounds chunk (lanes
+  // past the row end re-read its last chunk and are zeroed below): loads
+  // under a per-chunk branch made the compiler wait for each chunk's pair
+  // before issuing the next, one memory round trip per chunk
+  float4 v[NC], u[NC], gg[NC], bb[NC];
 #pragma unroll
   for (int j = 0; j < NC; ++j) {
-    const int c4 = lane + kWave * j;
-    v[j] = c4 < c4n ? load4(xr + 4 * c4) : make_float4(0.f, 0.f, 0.f, 0.f);
-    if (ADD && c4 < c4n) {
-      const float4 u = load4(sub + row * cols + 4 * c4);
-      v[j].x += u.x; v[j].y += u.y; v[j].z += u.z; v[j].w += u.w;
-    }
+    const int c4 = min(lane + kWave * j, c4n - 1);
+    v[j] = load4(xr + 4 * c4);
+    if (ADD) u[j] = load4(sub + row * cols + 4 * c4);
   }
-  ln_row<NC>(v, lane, c4n, cols, g, b, eps);
+  ln_load_affine<NC>(gg, bb, lane, c4n, g, b);
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {  // selects, no branches
+    const bool in = lane + kWave * j < c4n;
+    if (ADD) {
+      v[j].x += u[j].x; v[j].y += u[j].y; v[j].z += u[j].z; v[j].w += u[j].w;
+    }
+    v[j].x = in ? v[j].x : 0.f;
+    v[j].y = in ? v[j].y : 0.f;
+    v[j].z = in ? v[j].z : 0.f;
+    v[j].w = in ? v[j].w : 0.f;
+  }
+  ln_apply<NC>(v, gg, bb, lane, c4n, cols, eps);
 #pragma unroll
   for (int j = 0; j < NC; ++j) {
     const int c4 = lane + kWave * j;
