@@ -173,18 +173,25 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t *__restrict__ 
   const int c4n = H >> 2;
   const W *tr = tok + (int64_t)id * H;
   const W *pr = pos + (int64_t)p * H;
-  float4 v[NC];
+  // all loads issued before any is used, at in-bounds chunks (as in the
+  // LayerNorm kernel): lanes past the row end are zeroed by a select
+  float4 v[NC], c[NC], gg[NC], bb[NC];
 #pragma unroll
   for (int j = 0; j < NC; ++j) {
-    const int c4 = lane + kWave * j;
-    if (c4 < c4n) {
-      const float4 a = load4(tr + 4 * c4), c = load4(pr + 4 * c4);
-      v[j] = make_float4(a.x + c.x, a.y + c.y, a.z + c.z, a.w + c.w);
-    } else {
-      v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
+    const int c4 = min(lane + kWave * j, c4n - 1);
+    v[j] = load4(tr + 4 * c4);
+    c[j] = load4(pr + 4 * c4);
   }
-  if (LN) ln_row<NC>(v, lane, c4n, H, g, b, eps);
+  if (LN) ln_load_affine<NC>(gg, bb, lane, c4n, g, b);
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    const bool in = lane + kWave * j < c4n;
+    v[j].x = in ? v[j].x + c[j].x : 0.f;
+    v[j].y = in ? v[j].y + c[j].y : 0.f;
+    v[j].z = in ? v[j].z + c[j].z : 0.f;
+    v[j].w = in ? v[j].w + c[j].w : 0.f;
+  }
+  if (LN) ln_apply<NC>(v, gg, bb, lane, c4n, H, eps);
 #pragma unroll
   for (int j = 0; j < NC; ++j) {
     const int c4 = lane + kWave * j;
