@@ -87,9 +87,10 @@ __device__ __forceinline__ void store_stage(const Stage<C, ROWS> &r, uint16_t *s
 
 // Four consecutive outputs (m, n..n+3) of one lane, with bias[n..n+3]
 // already loaded in bv when n + 3 < N.
+// With a residual, rv holds res[m][n..n+3], loaded ahead by the caller.
 template <int EPI>
 __device__ __forceinline__ void epi_store4_bias(void *out, const float *res, int ldc, int64_t m,
-                                                int n, int N, float4 v, float4 bv,
+                                                int n, int N, float4 v, float4 bv, float4 rv,
                                                 const float *__restrict__ bias) {
   const int64_t o = m * ldc + n;
   constexpr bool RES = EPI == kEpiResidual || EPI == kEpiResidualFfn;
@@ -103,8 +104,7 @@ __device__ __forceinline__ void epi_store4_bias(void *out, const float *res, int
       *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(out) + o) = make_uint2(f2bf2(v.x, v.y), f2bf2(v.z, v.w));
     } else {
       if (RES) {
-        const float4 r = *reinterpret_cast<const float4 *>(res + o);
-        v.x += r.x; v.y += r.y; v.z += r.z; v.w += r.w;
+        v.x += rv.x; v.y += rv.y; v.z += rv.z; v.w += rv.w;
       }
       *reinterpret_cast<float4 *>(static_cast<float *>(out) + o) = v;
     }
@@ -576,8 +576,24 @@ __global__ __launch_bounds__(512, 2) void gemm_pp_kernel(
   const int n = n0 + C::WN * q + 4 * cc;
   float4 bv = make_float4(0.f, 0.f, 0.f, 0.f);
   if (n + 3 < N) bv = *reinterpret_cast<const float4 *>(bias + n);
+  constexpr bool RES = EPI == kEpiResidual || EPI == kEpiResidualFfn;
+  constexpr int NR = (32 + RPI - 1) / RPI;      // row reads per 32-row slab
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
+    // the slab's residual chunks, all issued before the first is used (one
+    // memory round trip per slab, not one per row read); indices clamped
+    // into the output's rows and columns, rows or chunks outside it are
+    // never stored (N < 4 takes the per-element path, which reads res itself)
+    float4 rv[NR];
+#pragma unroll
+    for (int k = 0; k < NR; ++k) rv[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (RES && N >= 4) {
+#pragma unroll
+      for (int k = 0; k < NR; ++k) {
+        const int64_t m = min(m0 + C::WM * grp + i * 32 + k * RPI + rr, (int64_t)M - 1);
+        rv[k] = *reinterpret_cast<const float4 *>(res + m * ldc + min(n, N - 4));
+      }
+    }
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -586,12 +602,12 @@ __global__ __launch_bounds__(512, 2) void gemm_pp_kernel(
             make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 #pragma unroll
-    for (int r0 = 0; r0 < 32; r0 += RPI) {
-      const int row = r0 + rr;
+    for (int k = 0; k < NR; ++k) {
+      const int row = k * RPI + rr;
       if (rr < RPI && row < 32) {
         const int64_t m = m0 + C::WM * grp + i * 32 + row;
         const float4 v = *reinterpret_cast<const float4 *>(stage + row * PITCH + 4 * cc);
-        if (m < M && n < N) epi_store4_bias<EPI>(out, res, ldc, m, n, N, v, bv, bias);
+        if (m < M && n < N) epi_store4_bias<EPI>(out, res, ldc, m, n, N, v, bv, rv[k], bias);
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
