@@ -12,7 +12,6 @@
 // Epilogues fuse what follows each GEMM: bias (QKV), bias + exact GELU (FFN1),
 // bias + fp32 residual (attention output, FFN2).
 #include <cmath>
-#include <cstdlib>
 
 #include "device.h"
 #include "kernels.h"
@@ -832,16 +831,13 @@ hipError_t launch_gemm_bf16_tile(int tile, const uint16_t *A, int lda, const uin
   }
 }
 
-// ES_GEMM_TILE=<0..3> forces one configuration (for tuning sweeps); unset = model.
+// The configuration from the cost model above (es_op_gemm_bf16_tile forces
+// one, for tests and tuning sweeps).
 hipError_t launch_gemm_bf16(const uint16_t *A, int lda, const uint16_t *W, const float *bias,
                             const float *res, void *out, int ldc, int M, int N, int K, int epi,
                             hipStream_t st) {
-  static const int forced = [] {
-    const char *e = std::getenv("ES_GEMM_TILE");
-    return e ? std::atoi(e) : -1;
-  }();
-  const int tile = forced >= 0 && forced < kGemmTiles ? forced : gemm_tile_index(M, N, K, epi);
-  return launch_gemm_bf16_tile(tile, A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
+  return launch_gemm_bf16_tile(gemm_tile_index(M, N, K, epi), A, lda, W, bias, res, out, ldc, M, N,
+                               K, epi, st);
 }
 
 hipError_t launch_gemm_f32(const float *A, int lda, const float *W, const float *bias,

@@ -62,7 +62,7 @@ struct es_model {
   int Hp = 0, Nqkv = 0, Kc = 0, Fp = 0;
   // capacity
   int64_t max_tokens = 0, Tcap = 0, score_cap = 0;
-  int attn_mode = 0;  // 0: scores -> softmax -> P.V, 1: fused
+  int attn_mode = 0;  // 0: scores -> softmax -> P.V, 1: fused (the bf16 default, set in build)
   int max_seqs = 0;
   int device = 0;
   // weights
@@ -380,6 +380,7 @@ es_status build(const es::ParsedBlob &pb, int64_t max_tokens, int32_t max_seqs, 
   m->pre_ln = h.pre_ln != 0;
   m->causal = h.causal != 0;
   m->bf16 = h.wdtype == 1;
+  m->attn_mode = m->bf16 ? 1 : 0;
   m->eps = h.eps;
   m->offset = h.reward_offset;
   m->Hp = (int)round_up(m->H, 64);

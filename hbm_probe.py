@@ -1,6 +1,6 @@
 """Plain device-to-device copy of a known size, for calibrating HBM byte counters.
 
-    python -m encoder_scoring_amd.hbm_probe [MiB] [repeats]
+    python hbm_probe.py [MiB] [repeats]
 
 Copies a MiB-sized buffer `repeats` times with torch's copy kernel; a
 rocprofv3 --pmc run over it gives FETCH_SIZE / WRITE_SIZE per dispatch for

@@ -303,12 +303,13 @@ es_status es_set_cost_table(es_model *m, const int64_t *cost_table, int32_t max_
                             int32_t max_len);
 
 /*
- * es_set_attention -- how the masked attention of each layer runs (bf16
- * models): 0 (default) = three kernels, scores to HBM, the Softmax row
- * reduction (TurboTransformers review, Proposed method), then P.V; 1 = one
- * fused kernel per (query tile, head) that keeps each score row in registers
- * with an online softmax (same result up to rounding, no score traffic).
- * fp32 models support 0 only.  Errors: ES_ERR_ARG.
+ * es_set_attention -- how the masked attention of each layer runs: 0 =
+ * three kernels, scores to HBM, the Softmax row reduction (TurboTransformers
+ * review, Proposed method), then P.V; 1 = one fused kernel per (query tile,
+ * head) that keeps each score row in registers with an online softmax (same
+ * result up to rounding, no score traffic).  Default: 1 for bf16 models, 0
+ * for fp32 models, which support 0 only.  Shared-prompt scoring
+ * (es_score_best_of_n) always runs the fused form.  Errors: ES_ERR_ARG.
  */
 es_status es_set_attention(es_model *m, int32_t mode);
 

@@ -39,13 +39,18 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("name,cfg,tol", CASES, ids=[c[0] for c in CASES])
-def test_rewards_match_oracle(name, cfg, tol):
+ATTENTION_CASES = [(n, c, t, a) for n, c, t in CASES for a in (["unfused", "fused"] if c.bf16 else ["unfused"])]
+
+
+@pytest.mark.parametrize("name,cfg,tol,attention", ATTENTION_CASES,
+                         ids=[f"{c[0]}-{c[3]}" for c in ATTENTION_CASES])
+def test_rewards_match_oracle(name, cfg, tol, attention):
     torch = need_gpu()
-    say("rewards", name)
+    say("rewards", name, attention)
     w = make_weights(cfg)
     ids, lengths = random_stream(5, 11, 1, min(cfg.max_pos, 150), cfg.vocab)
     sc = scorer_for(cfg, w, offset=0.125)
+    sc.set_attention(attention)
     got = gpu_score(torch, sc, ids, lengths)
     want = oracle.OracleModel(cfg, w).score_many(split(ids, lengths), 0.125)
     say(name, "max |d reward| =", float(np.max(np.abs(got - want))))
@@ -114,12 +119,15 @@ def test_bert_base_short_sample():
     assert np.max(np.abs(got - want)) <= BF16_TOL
 
 
-@pytest.mark.parametrize("cfg", [CASES[0][1], CASES[3][1]], ids=["fp32", "bf16_causal"])
-def test_batch_invariance_and_determinism(cfg):
+@pytest.mark.parametrize("cfg,attention", [(CASES[0][1], "unfused"), (CASES[3][1], "unfused"),
+                                           (CASES[3][1], "fused"), (CASES[4][1], "fused")],
+                         ids=["fp32", "bf16_causal-unfused", "bf16_causal-fused", "bf16_enc-fused"])
+def test_batch_invariance_and_determinism(cfg, attention):
     torch = need_gpu()
     w = make_weights(cfg)
     ids, lengths = random_stream(8, 9, 1, min(cfg.max_pos, 120), cfg.vocab)
     sc = scorer_for(cfg, w)
+    sc.set_attention(attention)
     packed = gpu_score(torch, sc, ids, lengths)
     again = gpu_score(torch, sc, ids, lengths)
     assert np.array_equal(packed, again)                       # run to run, bitwise
@@ -292,10 +300,13 @@ def test_fused_attention_matches_oracle_and_unfused(name, cfg):
     w = make_weights(cfg)
     ids, lengths = random_stream(15, 13, 1, min(cfg.max_pos, 200), cfg.vocab)
     sc = scorer_for(cfg, w, offset=0.125)
+    fused_default = gpu_score(torch, sc, ids, lengths)     # bf16 models default to fused
+    sc.set_attention("unfused")
     unfused = gpu_score(torch, sc, ids, lengths)
     sc.set_attention("fused")
     fused = gpu_score(torch, sc, ids, lengths)
     assert np.array_equal(fused, gpu_score(torch, sc, ids, lengths))
+    assert np.array_equal(fused, fused_default)
     want = oracle.OracleModel(cfg, w).score_many(split(ids, lengths), 0.125)
     say(name, "fused max |d| =", float(np.max(np.abs(fused - want))),
         "vs unfused", float(np.max(np.abs(fused - unfused))))
