@@ -14,6 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libencscore.so")
 
 ES_OK, ES_ERR_ARG, ES_ERR_RANGE, ES_ERR_CAPACITY = 0, -1, -2, -3
+STATIC_SCRATCH_BYTES = 64 * 1024 * 1024  # ES_STATIC_SCRATCH_BYTES (es_score_batch_static)
 ES_ERR_FORMAT, ES_ERR_IO, ES_ERR_HIP, ES_ERR_DEVICE_FLAG = -4, -5, -6, -7
 STATUS_NAMES = {0: "ES_OK", -1: "ES_ERR_ARG", -2: "ES_ERR_RANGE", -3: "ES_ERR_CAPACITY",
                 -4: "ES_ERR_FORMAT", -5: "ES_ERR_IO", -6: "ES_ERR_HIP", -7: "ES_ERR_DEVICE_FLAG"}
@@ -21,6 +22,7 @@ STATUS_NAMES = {0: "ES_OK", -1: "ES_ERR_ARG", -2: "ES_ERR_RANGE", -3: "ES_ERR_CA
 # every symbol declared in include/encscore.h
 EXPORTS = [
     "es_load_weights", "es_load_weights_mem", "es_free", "es_model_info", "es_score_batch",
+    "es_score_batch_static",
     "es_score_requests",
     "es_forward_hidden", "es_set_reward_offset", "es_get_reward_offset", "es_calibrate_offset",
     "es_check_device_errors", "es_plan_batches", "es_plan_batches_measured", "es_set_cost_table", "es_pack_offsets", "es_op_layernorm", "es_op_add_layernorm",
@@ -68,6 +70,7 @@ _SIGS = {
     "es_free": (None, [_P]),
     "es_model_info": (ctypes.c_int32, [_P, ctypes.POINTER(ModelInfo)]),
     "es_score_batch": (ctypes.c_int32, [_P, _P, _I32P, ctypes.c_int32, _P, _P]),
+    "es_score_batch_static": (ctypes.c_int32, [_P, _P, _I32P, ctypes.c_int32, _P, _P]),
     "es_score_requests": (ctypes.c_int32, [_P, _P, _I32P, ctypes.c_int32, ctypes.c_int64, _P, _P, ctypes.POINTER(StreamStats)]),
     "es_forward_hidden": (ctypes.c_int32, [_P, _P, _I32P, ctypes.c_int32, ctypes.c_int32, _P, _P]),
     "es_score_best_of_n": (ctypes.c_int32, [_P, _P, _I32P, ctypes.c_int32, _I32P, _I32P, ctypes.c_int64, _P, _P, _P, ctypes.POINTER(StreamStats)]),

@@ -160,6 +160,17 @@ class Scorer:
                                                 _dptr(out, torch.float32, "out"), _stream()))
         return out
 
+    def score_static(self, d_ids, offsets, out):
+        """es_score_batch_static: like score(), with every intermediate in the
+        library's fixed per-GPU scratch array (no device allocation; the
+        caller provides ``out``)."""
+        torch = _torch()
+        offsets = as_i32(offsets)
+        check(self.lib, self.lib.es_score_batch_static(
+            self.handle, _dptr(d_ids, torch.int32, "ids"), i32p(offsets), offsets.size - 1,
+            _dptr(out, torch.float32, "out"), _stream()))
+        return out
+
     def score_requests(self, d_ids, lengths, batch_overhead=1024, out=None):
         """Plan, pack, score and scatter a request stream; returns (rewards, stats)."""
         torch = _torch()

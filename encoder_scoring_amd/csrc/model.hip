@@ -20,12 +20,20 @@
 #include <cmath>
 #include <cstring>
 #include <fstream>
+#include <mutex>
 #include <vector>
 
 #include "blob.h"
 #include "common.h"
 #include "kernels.h"
 #include "memplan.h"
+
+// Scratch of es_score_batch_static, the entry point that allocates nothing:
+// every intermediate of its pass (uploaded batch metadata, activations, score
+// blocks) lives here.  Each GPU the library's code is loaded on holds its own
+// copy until the process ends; host code reaches a device's copy only through
+// the address hipGetSymbolAddress returns for it (static_scratch_of below).
+static __device__ __align__(256) char scratch[ES_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -94,6 +102,7 @@ struct es_model {
   int32_t cost_max_batch = 0, cost_max_len = 0;
   bool prune = true;  // last layer on the last token of each sequence only (es_set_pruning)
   hipEvent_t fork_ev = nullptr;
+  char *static_scratch = nullptr;  // this device's copy of `scratch` (es_score_batch_static)
   float *rew = nullptr;  // raw rewards of a reference set (es_calibrate_offset)
   size_t rew_cap = 0;
   int *flag = nullptr;
@@ -367,6 +376,30 @@ void begin_call(es_model *m) {
   }
 }
 
+// Device address of `scratch` on `device`, looked up once per device (with
+// that device current) and kept for the life of the process.
+es_status static_scratch_of(int device, char **out) {
+  static std::mutex mu;
+  static std::vector<char *> addr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (device < 0) return fail(ES_ERR_ARG, "device %d", device);
+  if ((size_t)device >= addr.size()) addr.resize((size_t)device + 1, nullptr);
+  if (!addr[device]) {
+    int cur = 0;
+    HIP_TRY(hipGetDevice(&cur));
+    if (cur != device) HIP_TRY(hipSetDevice(device));
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != device) HIP_TRY(hipSetDevice(cur));
+    if (e != hipSuccess || !p)
+      return fail(ES_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d failed: %s", device,
+                  hipGetErrorString(e));
+    addr[device] = static_cast<char *>(p);
+  }
+  *out = addr[device];
+  return ES_OK;
+}
+
 es_status build(const es::ParsedBlob &pb, int64_t max_tokens, int32_t max_seqs, es_model *m) {
   const es::BlobHeader &h = pb.h;
   m->L = (int)h.n_layers;
@@ -427,6 +460,7 @@ es_status build(const es::ParsedBlob &pb, int64_t max_tokens, int32_t max_seqs, 
   if (m->mem_mode == ES_MEM_FIXED && (s = alloc_workspace(m, m->ws[0], 1)) != ES_OK) return s;
   if ((s = dalloc(m, (void **)&m->flag, 4)) != ES_OK) return s;
   HIP_TRY(hipEventCreateWithFlags(&m->meta_ev, hipEventDisableTiming));
+  if ((s = static_scratch_of(m->device, &m->static_scratch)) != ES_OK) return s;
   HIP_TRY(hipDeviceSynchronize());
   return ES_OK;
 }
@@ -632,43 +666,43 @@ struct LastView {
   int64_t pairs = 0;
 };
 
-es::Ragged ragged_of(const es_model *m, const BatchLayout &L);
+es::Ragged ragged_of(const char *meta, const BatchLayout &L);
 
-LastView last_view_of(const es_model *m, const BatchLayout &L) {
+LastView last_view_of(const char *meta, const BatchLayout &L) {
   LastView v;
-  v.attn = ragged_of(m, L);
-  v.attn.items = reinterpret_cast<const int32_t *>(m->meta_dev + L.last_items);
+  v.attn = ragged_of(meta, L);
+  v.attn.items = reinterpret_cast<const int32_t *>(meta + L.last_items);
   v.attn.n_items = L.n;
   v.attn.fused_items = v.attn.mw_items = nullptr;  // last queries: one tile each
   v.attn.n_fused_items = v.attn.n_mw_items = 0;
   v.attn.pfx_items = nullptr;
   v.attn.n_pfx_items = 0;
-  v.rows = reinterpret_cast<const int32_t *>(m->meta_dev + L.last_rows);
+  v.rows = reinterpret_cast<const int32_t *>(meta + L.last_rows);
   v.tail = v.attn;
-  v.tail.off = reinterpret_cast<const int32_t *>(m->meta_dev + L.iota);
+  v.tail.off = reinterpret_cast<const int32_t *>(meta + L.iota);
   v.tail.n_tokens = L.n;
   v.tail.pref = v.tail.plen = nullptr;
   v.pairs = L.last_pairs;
   return v;
 }
 
-es::Ragged ragged_of(const es_model *m, const BatchLayout &L) {
+es::Ragged ragged_of(const char *meta, const BatchLayout &L) {
   es::Ragged r;
-  r.off = reinterpret_cast<const int32_t *>(m->meta_dev + L.off);
-  r.sbase = reinterpret_cast<const int64_t *>(m->meta_dev + L.sbase);
-  r.items = reinterpret_cast<const int32_t *>(m->meta_dev + L.items);
-  r.fused_items = reinterpret_cast<const int32_t *>(m->meta_dev + L.fitems);
-  r.mw_items = reinterpret_cast<const int32_t *>(m->meta_dev + L.mitems);
+  r.off = reinterpret_cast<const int32_t *>(meta + L.off);
+  r.sbase = reinterpret_cast<const int64_t *>(meta + L.sbase);
+  r.items = reinterpret_cast<const int32_t *>(meta + L.items);
+  r.fused_items = reinterpret_cast<const int32_t *>(meta + L.fitems);
+  r.mw_items = reinterpret_cast<const int32_t *>(meta + L.mitems);
   r.n_fused_items = L.n_fitems;
   r.n_mw_items = L.n_mitems;
-  r.pfx_items = reinterpret_cast<const int32_t *>(m->meta_dev + L.pitems);
+  r.pfx_items = reinterpret_cast<const int32_t *>(meta + L.pitems);
   r.n_pfx_items = L.n_pitems;
-  r.sm_items = reinterpret_cast<const int32_t *>(m->meta_dev + L.sm_items);
+  r.sm_items = reinterpret_cast<const int32_t *>(meta + L.sm_items);
   r.n_sm_items = L.n_sm_items;
-  r.src = L.has_src ? reinterpret_cast<const int32_t *>(m->meta_dev + L.src) : nullptr;
-  r.dest = L.has_dest ? reinterpret_cast<const int32_t *>(m->meta_dev + L.dest) : nullptr;
-  r.pref = L.has_prefix ? reinterpret_cast<const int32_t *>(m->meta_dev + L.pref) : nullptr;
-  r.plen = L.has_prefix ? reinterpret_cast<const int32_t *>(m->meta_dev + L.plen) : nullptr;
+  r.src = L.has_src ? reinterpret_cast<const int32_t *>(meta + L.src) : nullptr;
+  r.dest = L.has_dest ? reinterpret_cast<const int32_t *>(meta + L.dest) : nullptr;
+  r.pref = L.has_prefix ? reinterpret_cast<const int32_t *>(meta + L.pref) : nullptr;
+  r.plen = L.has_prefix ? reinterpret_cast<const int32_t *>(meta + L.plen) : nullptr;
   r.n_seqs = L.n;
   r.n_items = L.n_items;
   r.max_len = L.max_len;
@@ -684,7 +718,7 @@ es_status prepare(es_model *m, const int32_t *h_off, int32_t n, hipStream_t st, 
   es_status s = add_batch(m, h_off, n, nullptr, nullptr, &L);
   if (s != ES_OK) return s;
   if ((s = upload_meta(m, st)) != ES_OK) return s;
-  *r = ragged_of(m, L);
+  *r = ragged_of(m->meta_dev, L);
   *pairs = L.pairs;
   if (layout) *layout = L;
   return ES_OK;
@@ -963,13 +997,16 @@ extern "C" es_status es_model_info(const es_model *m, es_model_info_t *info) {
 
 // One pass of a laid-out batch: every layer, then the head.
 es_status score_pass(es_model *m, Workspace &w, const int32_t *d_ids, const BatchLayout &L,
-                     float *d_rewards, hipStream_t st) {
-  const es::Ragged r = ragged_of(m, L);
+                     float *d_rewards, hipStream_t st, const char *meta = nullptr,
+                     bool bound = false) {
+  if (!meta) meta = m->meta_dev;
+  const es::Ragged r = ragged_of(meta, L);
   const bool fused = m->bf16 && (m->attn_mode == 1 || L.has_prefix);
   es_status s;
-  if ((s = bind_workspace(m, w, L.n_tokens, fused ? 0 : L.score_elems, st)) != ES_OK) return s;
+  if (!bound && (s = bind_workspace(m, w, L.n_tokens, fused ? 0 : L.score_elems, st)) != ES_OK)
+    return s;
   if (m->prune && m->L > 0) {
-    const LastView lv = last_view_of(m, L);
+    const LastView lv = last_view_of(meta, L);
     if ((s = forward(m, w, d_ids, r, L.pairs, m->L, st, &lv)) != ES_OK) return s;
     return head(m, w, lv.tail, m->offset, d_rewards, st);
   }
@@ -989,6 +1026,53 @@ extern "C" es_status es_score_batch(es_model *m, const int32_t *d_token_ids, con
   begin_call(m);
   if ((s = prepare(m, h_offsets, n_seqs, st, &r, &pairs, &L)) != ES_OK) return s;
   if ((s = score_pass(m, m->ws[0], d_token_ids, L, d_rewards, st)) != ES_OK) return s;
+  es::clear_error();
+  return ES_OK;
+}
+
+// es_score_batch with every intermediate in this device's `scratch`: the
+// batch metadata first (aligned to kArenaAlign), then the pass's tensors at
+// the offsets es_plan_arena gives their lifetimes (the length-aware layout).
+// No device or pinned allocation: the metadata goes up by a copy from the
+// host assembly buffer, and a batch whose need exceeds the array is refused.
+extern "C" es_status es_score_batch_static(es_model *m, const int32_t *d_token_ids,
+                                           const int32_t *h_offsets, int32_t n_seqs,
+                                           float *d_rewards, void *stream) {
+  es_status s = check_model(m);
+  if (s != ES_OK) return s;
+  if (!d_token_ids || !d_rewards) return fail(ES_ERR_ARG, "NULL device pointer");
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  if (dev != m->device)
+    return fail(ES_ERR_ARG, "current device %d is not the model's device %d", dev, m->device);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  begin_call(m);
+  m->meta_asm.clear();
+  BatchLayout L;
+  if ((s = add_batch(m, h_offsets, n_seqs, nullptr, nullptr, &L)) != ES_OK) return s;
+  const bool fused = m->bf16 && m->attn_mode == 1;
+  const int64_t rows = std::max<int64_t>(round_up(L.n_tokens, 256), 256);
+  std::vector<int64_t> off;
+  const int64_t need = es::plan_arena(pass_usage(m, rows, fused ? 0 : L.score_elems), kArenaAlign, off);
+  const int64_t meta_bytes = round_up(std::max<int64_t>((int64_t)m->meta_asm.size(), 16), kArenaAlign);
+  if (meta_bytes + need > ES_STATIC_SCRATCH_BYTES)
+    return fail(ES_ERR_CAPACITY,
+                "batch needs %" PRId64 " bytes of scratch (%" PRId64 " metadata + %" PRId64
+                " tensors), above ES_STATIC_SCRATCH_BYTES=%lld",
+                meta_bytes + need, meta_bytes, need, (long long)ES_STATIC_SCRATCH_BYTES);
+  char *base = m->static_scratch;
+  HIP_TRY(hipMemcpyAsync(base, m->meta_asm.data(), m->meta_asm.size(), hipMemcpyHostToDevice, st));
+  Workspace w;
+  char *a = base + meta_bytes;
+  w.x = reinterpret_cast<float *>(a + off[kTX]);
+  w.xb = a + off[kTXb];
+  w.qkv = a + off[kTQkv];
+  w.ctx = a + off[kTCtx];
+  w.y = reinterpret_cast<float *>(a + off[kTY]);
+  w.hmid = a + off[kTHmid];
+  w.S = reinterpret_cast<float *>(a + off[kTS]);
+  w.Pb = a + off[kTP];
+  if ((s = score_pass(m, w, d_token_ids, L, d_rewards, st, base, true)) != ES_OK) return s;
   es::clear_error();
   return ES_OK;
 }

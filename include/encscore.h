@@ -128,6 +128,29 @@ es_status es_model_info(const es_model *m, es_model_info_t *info);
 es_status es_score_batch(es_model *m, const int32_t *d_token_ids, const int32_t *h_offsets,
                          int32_t n_seqs, float *d_rewards, void *stream);
 
+/*
+ * es_score_batch_static -- es_score_batch for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid hipMalloc.  Same arguments, validation, kernels and
+ * results (bitwise equal to es_score_batch on the same model settings); it
+ * calls no hipMalloc, hipHostMalloc or hipFree.  Every intermediate -- the
+ * batch metadata, activations, and (unfused attention) the score blocks --
+ * lives in one fixed device array of ES_STATIC_SCRATCH_BYTES (64 MiB) that
+ * the library holds on every GPU it is loaded on until the process ends.
+ * A batch needing more (metadata + tensors at their lifetime-shared
+ * offsets; e.g. BERT-base shapes hold about 4096 tokens with fused attention)
+ * is refused with ES_ERR_CAPACITY before any device work.  The metadata is
+ * copied from pageable host memory on `stream`.  All calls on one GPU share
+ * that array, which keeps the previous call's contents (no kernel relies on
+ * it being zero): calls that overlap in time on one GPU -- on different
+ * streams, threads or handles -- race and must be serialised by the caller.
+ * The current device must be the model's (else ES_ERR_ARG).
+ */
+#define ES_STATIC_SCRATCH_BYTES (64ll * 1024 * 1024)
+es_status es_score_batch_static(es_model *m, const int32_t *d_token_ids,
+                                const int32_t *h_offsets, int32_t n_seqs, float *d_rewards,
+                                void *stream);
+
 /* Plan / work summary of one es_score_requests call. */
 typedef struct {
   int32_t n_batches;     /* batches the planner formed                           */
