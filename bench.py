@@ -332,6 +332,26 @@ class Workload:
         self.sc.close()
 
 
+def row_reductions(workload, tables):
+    """The Softmax and LayerNorm row reductions' bandwidth: algorithmic bytes
+    over HIP-event time, and HBM bytes from the committed rocprofv3 counter
+    summary (when it describes the current source) over the same time."""
+    out = {}
+    for cls in ("softmax", "layernorm"):
+        t = next((tb[cls] for tb in tables if cls in tb), None)
+        if t is None:
+            continue
+        e = {"avg_launch_us": t["avg_launch_us"], "algorithmic_GBps": t["achieved"],
+             "frac_algorithmic": t["frac"]}
+        b = traffic_from_profiles(workload, cls)
+        if b is not None:
+            gbps = b / (t["avg_launch_us"] * 1e-6) / 1e9
+            e.update({"counter_bytes_per_launch": b, "counter_GBps": round(gbps, 1),
+                      "frac_counter": round(gbps / PEAKS["hbm"][0], 4)})
+        out[cls] = e
+    return out
+
+
 def run_entry(w, args, steps, warmup, prof_steps, variants=True):
     """Timed steps, kernel table, roofline and (optionally) the other attention
     form for one workload."""
@@ -347,6 +367,8 @@ def run_entry(w, args, steps, warmup, prof_steps, variants=True):
         k, v = w.other_attention(steps, warmup, prof_steps)
         res["variants"][k] = v
         log(f"  {k}: {v['value']} seq/s")
+    res["row_reductions"] = row_reductions(
+        w.cfg.name, [res["kernels"]] + [v["kernels"] for v in res["variants"].values()])
     res["config"] = w.config(args)
     return res
 
@@ -463,6 +485,7 @@ def main():
                    "allocs_in_timed_steps": mem["allocs"],
                    "alloc_ms_in_timed_steps": round(mem["alloc_ms"], 3)},
         "kernels": head["kernels"],
+        "row_reductions": head["row_reductions"],
         "variants": head["variants"],
         "fixed_length_calls": latency,
         "device": torch.cuda.get_device_name(0),

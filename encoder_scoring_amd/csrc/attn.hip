@@ -7,8 +7,9 @@
 //   context: ctx[q, h*dp + e] = sum_k P_ih[q, k] v_k[h*dp + e].
 // Work is a list of (sequence, 32-query-row tile) items built on the host,
 // longest sequences first, times the heads on the second grid axis, so no
-// block is spent on padding.  Score blocks of sequence i are n_i x ld_i
-// (ld_i = n_i rounded up to 8) per head, packed back to back.
+// block is spent on padding.  Score blocks follow score_row_off /
+// score_block (kernels.h): n_i x ld_i per head, or the packed lower triangle
+// when causal.
 #include "device.h"
 #include "kernels.h"
 
@@ -29,8 +30,7 @@ __global__ __launch_bounds__(256) void scores_kernel(const Act *__restrict__ qkv
   const int seq = items[2 * item], q0 = items[2 * item + 1];
   const int64_t t0 = off[seq];
   const int n = off[seq + 1] - (int)t0;
-  const int ld = score_ld(n);
-  const int64_t base = sbase[seq] + (int64_t)h * n * ld;
+  const int64_t base = sbase[seq] + (int64_t)h * score_block(n, causal);
   const Act *Q = qkv + t0 * ldq + h * DP;
   const Act *Kp = qkv + t0 * ldq + (n_heads + h) * DP;
   for (int e = tid; e < kQTile * DP; e += 256) {
@@ -57,7 +57,7 @@ __global__ __launch_bounds__(256) void scores_kernel(const Act *__restrict__ qkv
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int q = q0 + rg + i;
-      if (q < n && k < n && (!causal || k <= q)) S[base + (int64_t)q * ld + k] = acc[i] * scale;
+      if (q < n && k < n && (!causal || k <= q)) S[base + score_row_off(q, n, causal) + k] = acc[i] * scale;
     }
   }
 }
@@ -76,8 +76,7 @@ __global__ __launch_bounds__(256) void pv_kernel(const PT *__restrict__ P, const
   const int seq = items[2 * item], q0 = items[2 * item + 1];
   const int64_t t0 = off[seq];
   const int n = off[seq + 1] - (int)t0;
-  const int ld = score_ld(n);
-  const int64_t base = sbase[seq] + (int64_t)h * n * ld;
+  const int64_t base = sbase[seq] + (int64_t)h * score_block(n, causal);
   const Act *V = qkv + t0 * ldq + (2 * n_heads + h) * DP;
   const int e = tid % DP, r0 = tid / DP;
   float acc[NR] = {};
@@ -87,7 +86,7 @@ __global__ __launch_bounds__(256) void pv_kernel(const PT *__restrict__ P, const
     for (int x = tid; x < kQTile * 64; x += 256) {
       const int r = x >> 6, c = x & 63, q = q0 + r, k = k0 + c;
       const bool ok = q < n && k < n && (!causal || k <= q);
-      sP[r][c] = ok ? to_f(P[base + (int64_t)q * ld + k]) : 0.f;
+      sP[r][c] = ok ? to_f(P[base + score_row_off(q, n, causal) + k]) : 0.f;
     }
     for (int x = tid; x < 64 * DP; x += 256) {
       const int r = x / DP, c = x % DP, k = k0 + r;
@@ -141,8 +140,7 @@ __global__ __launch_bounds__(64) void scores_mfma_kernel(const uint16_t *__restr
   const int seq = items[2 * item], q0 = items[2 * item + 1];
   const int64_t t0 = off[seq];
   const int n = off[seq + 1] - (int)t0;
-  const int ld = score_ld(n);
-  const int64_t base = sbase[seq] + (int64_t)h * n * ld;
+  const int64_t base = sbase[seq] + (int64_t)h * score_block(n, causal);
   const int fr = lane & 31, fh = lane >> 5;
   const int q = q0 + fr;
   // rows are clamped to the sequence and the out-of-range fragments zeroed
@@ -154,7 +152,7 @@ __global__ __launch_bounds__(64) void scores_mfma_kernel(const uint16_t *__restr
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk) qf[kk] = q < n ? qf[kk] : zero_frag();
   const int kend = causal ? min(n, q0 + kQTile) : n;
-  float *Sr = S + base + (int64_t)q * ld;
+  float *Sr = S + base + score_row_off(q, n, causal);
   const int qlim = causal ? min(q + 1, n) : n;  // keys visible to this query row
   for (int k0 = 0; k0 < kend; k0 += 32) {
     const int k = k0 + fr;
@@ -265,12 +263,11 @@ __global__ __launch_bounds__(64) void pv_mfma_kernel(const uint16_t *__restrict_
   const int seq = items[2 * item], q0 = items[2 * item + 1];
   const int64_t t0 = off[seq];
   const int n = off[seq + 1] - (int)t0;
-  const int ld = score_ld(n);
-  const int64_t base = sbase[seq] + (int64_t)h * n * ld;
+  const int64_t base = sbase[seq] + (int64_t)h * score_block(n, causal);
   const int fr = lane & 31, fh = lane >> 5;
   const int q = q0 + fr;
   const int qlim = q < n ? (causal ? q + 1 : n) : 0;  // valid P entries of this row
-  const uint16_t *Pr = P + base + (int64_t)q * ld;
+  const uint16_t *Pr = P + base + score_row_off(q, n, causal);
   const uint16_t *V = qkv + t0 * ldq + (2 * n_heads + h) * DP;
   f32x16 acc[NT];
 #pragma unroll

@@ -421,6 +421,75 @@ struct PPCfg {
   static_assert(DR % RPL == 0 && (DR / RPL) % CPR == 0, "swizzle must repeat between loads");
 };
 
+// Staged epilogue of the eight-wavefront blocks (wave (grp, q) owns rows
+// [grp WM, (grp+1) WM) and columns [q WN, (q+1) WN) of the block).
+// acc[i][j] = D[n][m] of the W x A product: lane holds row m = lane & 31 and
+// register r column 8 (r / 4) + 4 (lane / 32) + (r % 4), so stored straight
+// from registers one instruction writes 16-32 bytes in each of 32 rows.
+// Instead each wave stages 32 rows of its accumulators at a time in its own
+// LDS region of `buf` (a stage buffer, free once the K loop is done) and
+// reads them back along rows: a lane then owns one 4-column chunk, bias (and
+// residual) loads and output stores cover whole row segments.  Rows are
+// padded by 4 floats so both the staging writes and the row reads spread
+// over the LDS banks.  Every access is by the wave that wrote it and a
+// wave's LDS operations execute in program order, so no barrier is needed;
+// wavefront-scope fences (no instructions) keep the compiler from moving a
+// lane's reads of other lanes' writes across them.
+template <class C, int EPI>
+__device__ __forceinline__ void staged_epilogue(const f32x16 (&acc)[C::TM][C::TN], float *buf, int grp,
+                                                int q, int lane, int64_t m0, int n0,
+                                                const float *__restrict__ bias, const float *res,
+                                                void *out, int ldc, int M, int N) {
+  constexpr int TM = C::TM, TN = C::TN;
+  const int fr = lane & 31, fh = lane >> 5;
+  constexpr int PITCH = C::WN + 4;              // floats per staged row
+  constexpr int CH = C::WN / 4;                 // 4-column chunks per row
+  constexpr int RPI = 64 / CH;                  // rows per read instruction (lanes beyond
+                                                // RPI * CH idle when CH does not divide 64)
+  static_assert(4 * 32 * PITCH * 4 <= C::SZ * 2, "epilogue staging exceeds a stage buffer");
+  float *stage = buf + q * 32 * PITCH;  // group g in buffer g
+  const int cc = lane % CH, rr = lane / CH;
+  const int n = n0 + C::WN * q + 4 * cc;
+  float4 bv = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (n + 3 < N) bv = *reinterpret_cast<const float4 *>(bias + n);
+  constexpr bool RES = EPI == kEpiResidual || EPI == kEpiResidualFfn;
+  constexpr int NR = (32 + RPI - 1) / RPI;      // row reads per 32-row slab
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    // the slab's residual chunks, all issued before the first is used (one
+    // memory round trip per slab, not one per row read); indices clamped
+    // into the output's rows and columns, rows or chunks outside it are
+    // never stored (N < 4 takes the per-element path, which reads res itself)
+    float4 rv[NR];
+#pragma unroll
+    for (int k = 0; k < NR; ++k) rv[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (RES && N >= 4) {
+#pragma unroll
+      for (int k = 0; k < NR; ++k) {
+        const int64_t m = min(m0 + C::WM * grp + i * 32 + k * RPI + rr, (int64_t)M - 1);
+        rv[k] = *reinterpret_cast<const float4 *>(res + m * ldc + min(n, N - 4));
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<float4 *>(stage + fr * PITCH + j * 32 + 8 * g + 4 * fh) =
+            make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+      const int row = k * RPI + rr;
+      if (rr < RPI && row < 32) {
+        const int64_t m = m0 + C::WM * grp + i * 32 + row;
+        const float4 v = *reinterpret_cast<const float4 *>(stage + row * PITCH + 4 * cc);
+        if (m < M && n < N) epi_store4_bias<EPI>(out, res, ldc, m, n, N, v, bv, rv[k], bias);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  }
+}
+
 template <class C, int EPI, int PFD>
 __global__ __launch_bounds__(512, 2) void gemm_pp_kernel(
     const uint16_t *__restrict__ A, int lda, const uint16_t *__restrict__ W,
@@ -553,64 +622,167 @@ __global__ __launch_bounds__(512, 2) void gemm_pp_kernel(
   }
   if (grp == 0) __builtin_amdgcn_s_barrier();
 
-  // Epilogue.  acc[i][j] = D[n][m] of the W x A product: lane holds row
-  // m = lane & 31 and register r column 8 (r / 4) + 4 (lane / 32) + (r % 4),
-  // so stored straight from registers one instruction writes 16-32 bytes in
-  // each of 32 rows.  Instead each wave stages 32 rows of its accumulators at
-  // a time in its own LDS region (the stage buffers are free after the last
-  // barrier) and reads them back along rows: a lane then owns one 4-column
-  // chunk, bias (and residual) loads and output stores cover whole row
-  // segments.  Rows are padded by 4 floats so both the staging writes and
-  // the row reads spread over the LDS banks.  Every access is by the wave
-  // that wrote it and a wave's LDS operations execute in program order, so
-  // no barrier is needed; wavefront-scope fences (no instructions) keep the
-  // compiler from moving a lane's reads of other lanes' writes across them.
-  constexpr int PITCH = C::WN + 4;              // floats per staged row
-  constexpr int CH = C::WN / 4;                 // 4-column chunks per row
-  constexpr int RPI = 64 / CH;                  // rows per read instruction (lanes beyond
-                                                // RPI * CH idle when CH does not divide 64)
-  static_assert(4 * 32 * PITCH * 4 <= C::SZ * 2, "epilogue staging exceeds a stage buffer");
-  float *stage = reinterpret_cast<float *>(grp == 0 ? L0 : L1) + q * 32 * PITCH;  // group g in buffer g
-  const int cc = lane % CH, rr = lane / CH;
-  const int n = n0 + C::WN * q + 4 * cc;
-  float4 bv = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (n + 3 < N) bv = *reinterpret_cast<const float4 *>(bias + n);
-  constexpr bool RES = EPI == kEpiResidual || EPI == kEpiResidualFfn;
-  constexpr int NR = (32 + RPI - 1) / RPI;      // row reads per 32-row slab
+  staged_epilogue<C, EPI>(acc, reinterpret_cast<float *>(grp == 0 ? L0 : L1), grp, q, lane, m0, n0,
+                          bias, res, out, ldc, M, N);
+}
+
+// ---------------------------------------------------------------- bf16 MFMA, software pipeline
+//
+// Block BM x BN x 64 with the eight-wavefront layout of the ping-pong blocks
+// (wave (grp, q) owns a WM x WN sub-tile), but every wavefront runs the same
+// schedule, pipelined one MFMA k-step (16 deep) ahead: while the matrix core
+// works through a k-step's TM x TN MFMAs, the LDS reads of the next k-step's
+// fragments are in flight.  Scheduling fences pin that order (left alone,
+// the compiler issues the reads after the MFMAs that free their registers
+// and waits for them at once).  All eight wavefronts share the direct loads;
+// one barrier per stage, after the last k-step's reads, with this
+// wavefront's loads of the next stage landed first.  Two waves per SIMD
+// interleave their MFMA streams, so neither the barrier nor the LDS latency
+// leaves the matrix core idle for long.
+//
+// A (the activations, streamed from HBM when the pass is large) has NA stage
+// buffers and W (the weights, mostly L2 hits) two: stage k + NA - 1's A
+// loads go out during stage k, so they have NA - 1 stages to arrive; stage
+// k + 1's W loads go out at the start of stage k.  With NA = 3 and a 256 x
+// 256 block that is the whole 160 KiB of LDS.
+template <int BM_, int BN_, int NA_>
+struct SPCfg {
+  static constexpr int BM = BM_, BN = BN_, BK = 64, NA = NA_;
+  static constexpr int WM = BM / 2, WN = BN / 4, TM = WM / 32, TN = WN / 32;
+  static constexpr int CPR = BK / 8, RPL = 256 / (BK * 2), KS = BK / 16;
+  static constexpr int NL = 8;  // wavefronts issuing the direct loads (all)
+  static constexpr int NIA = BM * CPR / (64 * NL), NIB = BN * CPR / (64 * NL);
+  static constexpr int ABYTES = BM * BK * 2, BBYTES = BN * BK * 2;  // one stage of A / of W
+  static constexpr int LDS = NA * ABYTES + 2 * BBYTES;
+  static constexpr int SZ = (BM + BN) * BK;  // bf16 elements of an A + W stage (epilogue regions)
+  static constexpr int DR = NL * 64 / CPR;
+  static_assert(TM >= 1 && TN >= 1 && NA >= 2, "bad tile");
+  static_assert(NIA * 64 * NL == BM * CPR && NIB * 64 * NL == BN * CPR, "stage not divisible");
+  static_assert(DR % RPL == 0 && (DR / RPL) % CPR == 0, "swizzle must repeat between loads");
+  static_assert(LDS <= 160 * 1024 && 2 * SZ * 2 <= LDS, "LDS budget");
+};
+
+template <class C, int EPI>
+__global__ __launch_bounds__(512, 1) void gemm_sp_kernel(
+    const uint16_t *__restrict__ A, int lda, const uint16_t *__restrict__ W,
+    const float *__restrict__ bias, const float *res, void *out, int ldc, int M, int N, int K,
+    int tiles_m, int tiles_n) {
+  constexpr int BM = C::BM, BK = C::BK, TM = C::TM, TN = C::TN, KS = C::KS, DR = C::DR, NA = C::NA;
+  // A stage buffers at [0, NA ABYTES), W stage buffers after them
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS];
+
+  int tm, tn;
+  tile_of_block(tiles_m, tiles_n, (int64_t)8 * C::BN * K * 2, tm, tn);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, q = wave & 3;
+  const int64_t m0 = (int64_t)tm * BM;
+  const int n0 = tn * C::BN;
+  const uint16_t *Ag = A + m0 * lda;
+  const uint16_t *Wg = W + (int64_t)n0 * K;
+
+  const i32x4 ra = make_rsrc(Ag), rb = make_rsrc(Wg);
+  int voA, voB;  // byte offsets of this lane's chunk in the wave's first load
+  {
+    const int e = wave * 64 + lane, row = e / C::CPR, slot = e % C::CPR;
+    voA = (row * lda + swz_slot<C>(row, slot) * 8) * 2;
+    voB = (row * K + swz_slot<C>(row, slot) * 8) * 2;
+  }
+  const uint32_t lds0 = lds_addr(lds);
+  // this wavefront's direct loads of one stage of A / of W, each chunk
+  // landing at its swizzled LDS position
+  auto issue_a = [&](int stage) {
+    const uint32_t l0 = lds0 + (stage % NA) * C::ABYTES + wave * 1024;
+    const int k0 = stage * BK;
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    // the slab's residual chunks, all issued before the first is used (one
-    // memory round trip per slab, not one per row read); indices clamped
-    // into the output's rows and columns, rows or chunks outside it are
-    // never stored (N < 4 takes the per-element path, which reads res itself)
-    float4 rv[NR];
+    for (int t = 0; t < C::NIA; ++t) dma16(ra, voA, (k0 + t * DR * lda) * 2, l0 + t * C::NL * 1024);
+  };
+  auto issue_b = [&](int stage) {
+    const uint32_t l0 = lds0 + NA * C::ABYTES + (stage & 1) * C::BBYTES + wave * 1024;
+    const int k0 = stage * BK;
 #pragma unroll
-    for (int k = 0; k < NR; ++k) rv[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (RES && N >= 4) {
+    for (int t = 0; t < C::NIB; ++t) dma16(rb, voB, (k0 + t * DR * K) * 2, l0 + t * C::NL * 1024);
+  };
+
+  f32x16 acc[TM][TN];
 #pragma unroll
-      for (int k = 0; k < NR; ++k) {
-        const int64_t m = min(m0 + C::WM * grp + i * 32 + k * RPI + rr, (int64_t)M - 1);
-        rv[k] = *reinterpret_cast<const float4 *>(res + m * ldc + min(n, N - 4));
-      }
-    }
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *reinterpret_cast<float4 *>(stage + fr * PITCH + j * 32 + 8 * g + 4 * fh) =
-            make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int fr = lane & 31, fh = lane >> 5;
+  const uint16_t *a_lane = reinterpret_cast<const uint16_t *>(lds) + (C::WM * grp + fr) * BK;
+  const uint16_t *b_lane =
+      reinterpret_cast<const uint16_t *>(lds + NA * C::ABYTES) + (C::WN * q + fr) * BK;
+  bf16x8 fa[2][TM], fb[2][TN];
+  auto read_kstep = [&](int set, int stage, int kk) {
+    const uint16_t *a_s = a_lane + (stage % NA) * (C::ABYTES / 2);
+    const uint16_t *b_s = b_lane + (stage & 1) * (C::BBYTES / 2);
+    const int slot = swz_slot<C>(fr, kk * 2 + fh) << 3;
 #pragma unroll
-    for (int k = 0; k < NR; ++k) {
-      const int row = k * RPI + rr;
-      if (rr < RPI && row < 32) {
-        const int64_t m = m0 + C::WM * grp + i * 32 + row;
-        const float4 v = *reinterpret_cast<const float4 *>(stage + row * PITCH + 4 * cc);
-        if (m < M && n < N) epi_store4_bias<EPI>(out, res, ldc, m, n, N, v, bv, rv[k], bias);
-      }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    for (int i = 0; i < TM; ++i) fa[set][i] = *reinterpret_cast<const bf16x8 *>(a_s + i * 32 * BK + slot);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) fb[set][j] = *reinterpret_cast<const bf16x8 *>(b_s + j * 32 * BK + slot);
+  };
+  auto mma_kstep = [&](int set) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[set][j], fa[set][i], acc[i][j], 0, 0, 0);
+  };
+
+  const int nk = K / BK;
+  // prologue: A stages 0 .. NA - 2 and W stage 0; wait for stage 0 only
+  // (loads complete in order)
+  issue_a(0);
+  issue_b(0);
+  for (int p = 1; p < NA - 1; ++p)
+    if (p < nk) issue_a(p);
+  {
+    const int ahead = min(NA - 2, nk - 1);  // A stages issued after W stage 0
+    if (ahead >= 2) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(2 * C::NIA));
+    else if (ahead == 1) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(C::NIA));
+    else __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
   }
+  __builtin_amdgcn_s_barrier();
+  read_kstep(0, 0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // Stage k: k-step kk computes on fragment set kk & 1 (read one k-step
+  // earlier) while the next k-step's reads fly.  W stage k + 1 goes out in
+  // k-step 0 and A stage k + NA - 1 in k-step 1, into buffers whose last
+  // reads (stage k - 1) every wavefront finished before the previous
+  // barrier.  The last k-step waits for A and W stage k + 1 (leaving A stage
+  // k + NA - 1 in flight) and for its LDS reads, passes the barrier, then
+  // reads stage k + 1's first fragments.
+  for (int k = 0; k < nk; ++k) {
+    const bool more = k + 1 < nk;
+    const bool far = k + NA - 1 < nk;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const int set = kk & 1;
+      if (kk + 1 < KS) {
+        read_kstep(set ^ 1, k, kk + 1);
+        if (kk == 0 && more) issue_b(k + 1);
+        if (kk == 1 && far) issue_a(k + NA - 1);
+      } else {
+        if (NA > 2 && far) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(C::NIA));
+        else __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
+        __builtin_amdgcn_s_barrier();
+        if (more) read_kstep(set ^ 1, k + 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      mma_kstep(set);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // every wavefront's last fragment reads completed before the final
+  // barrier, so the whole LDS is free for the staging
+  staged_epilogue<C, EPI>(acc, reinterpret_cast<float *>(lds + grp * C::SZ * 2), grp, q, lane, m0,
+                          n0, bias, res, out, ldc, M, N);
 }
 
 // ---------------------------------------------------------------- fp32 SIMT
@@ -723,6 +895,35 @@ hipError_t go_pp(const uint16_t *A, int lda, const uint16_t *W, const float *bia
   return hipGetLastError();
 }
 
+template <class C>
+hipError_t go_sp(const uint16_t *A, int lda, const uint16_t *W, const float *bias,
+                 const float *res, void *out, int ldc, int M, int N, int K, int epi,
+                 hipStream_t st) {
+  if (K % C::BK) return hipErrorInvalidValue;
+  const int tm = (M + C::BM - 1) / C::BM, tn = (N + C::BN - 1) / C::BN;
+  const dim3 grid(tm * tn), block(512);
+  switch (epi) {
+    case kEpiBias:
+      gemm_sp_kernel<C, kEpiBias><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K, tm, tn);
+      break;
+    case kEpiGelu:
+      gemm_sp_kernel<C, kEpiGelu><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K, tm, tn);
+      break;
+    case kEpiResidual:
+      gemm_sp_kernel<C, kEpiResidual><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K, tm, tn);
+      break;
+    case kEpiF32:
+      gemm_sp_kernel<C, kEpiF32><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K, tm, tn);
+      break;
+    case kEpiResidualFfn:
+      gemm_sp_kernel<C, kEpiResidualFfn><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K, tm, tn);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 // Tile configurations:
 //   0  T1  128 x 64, register-staged, 4 waves (64 x 32 each), three blocks per CU
 //   1  P1  128 x 128 ping-pong, 8 waves (64 x 32 each), two blocks per CU
@@ -737,13 +938,17 @@ hipError_t go_pp(const uint16_t *A, int lda, const uint16_t *W, const float *bia
 //          layer's GEMMs on one row per sequence (a few hundred rows), where
 //          128 x 64 blocks would leave most CUs idle (380 x 768 x 3072:
 //          27.2 -> 20.4 us)
+//   5  S2  256 x 256 software-pipelined, 8 waves (128 x 64 each), one block
+//          per CU, A triple-buffered (all 160 KiB of LDS); it runs wherever
+//          the cost model below picks a wide block (2 or 3)
 //                  BM  BN  BK WGM WGN PF MINW
 using T1 = Cfg<128, 64, 64, 2, 2, 2, 3>;
 using T0 = Cfg<32, 64, 64, 1, 2, 2, 3>;
 using P1 = PPCfg<128, 128>;
 using P2 = PPCfg<256, 256>;
 using P3 = PPCfg<128, 384>;
-static_assert(kGemmTiles == 5, "tile menu and launcher disagree");
+using S2 = SPCfg<256, 256, 3>;
+static_assert(kGemmTiles == 6, "tile menu and launcher disagree");
 
 constexpr int kCUs = 256;
 
@@ -808,7 +1013,13 @@ int gemm_tile_index(int M, int N, int K, int epi) {
       best_cost = cost;
     }
   }
-  return best;
+  // where a wide block wins, the software-pipelined 256 x 256 block does the
+  // work: inside the layer sequence it matched or beat both wide ping-pong
+  // blocks on every such shape (decoder at ~79 k rows per pass: attention-out
+  // 115.0 -> 105.6 and FFN2 362.3 -> 339.4 ms per step, QKV and FFN1 equal;
+  // BERT-base FFN2 6.34 -> 5.86 / 29.2 -> 26.3 ms per step on the short /
+  // long-tail streams; same box)
+  return best == 1 ? 1 : 5;
 }
 
 hipError_t launch_gemm_bf16_tile(int tile, const uint16_t *A, int lda, const uint16_t *W,
@@ -827,6 +1038,7 @@ hipError_t launch_gemm_bf16_tile(int tile, const uint16_t *A, int lda, const uin
         return go_pp<P1, 0>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
       return go_pp<P3, 1>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
     case 4: return go_bf16<T0>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
+    case 5: return go_sp<S2>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -8,7 +8,8 @@
 //   qkv   act  [T, 3*A*dp]   Q | K | V, head h at columns h*dp of each part
 //   ctx   act  [T, Kc]       attention context, head h at columns h*dp
 //   hmid  act  [T, Fp]       GELU(FFN1)
-//   S     fp32 ragged        per (sequence, head) n x ld score blocks
+//   S     fp32 ragged        per (sequence, head) score blocks: n x ld, or the packed
+//                            lower triangle when causal (score_row_off)
 //   P     act  ragged        softmax output, same indexing as S
 // act = bf16 for bf16 models (fp32 accumulation everywhere), fp32 otherwise.
 // Hp, Kc, Fp round widths up to 64 (zero columns); dp rounds the head dim up
@@ -475,7 +476,7 @@ struct BatchLayout {
   size_t last_items = 0, last_rows = 0, iota = 0;  // last-token work of the pruned last layer
   int64_t last_pairs = 0;  // visible (query, key) pairs of the last queries, over heads
   bool has_src = false, has_dest = false, has_prefix = false;
-  int n = 0, n_items = 0, n_sm_items = 0, max_len = 0, n_tokens = 0;
+  int n = 0, n_items = 0, n_sm_items = 0, n_sm_narrow = 0, max_len = 0, n_tokens = 0;
   int64_t pairs = 0;  // visible (query, key) pairs summed over heads
   int64_t score_elems = 0;  // ragged score-block elements (unfused attention)
 };
@@ -515,7 +516,7 @@ es_status add_batch(es_model *m, const int32_t *h_off, int32_t n, const int32_t 
     // visible (query, key) pairs over the sequence's own queries
     L->pairs += (int64_t)m->A * (m->causal ? len * np + len * (len + 1) / 2 : len * len);
     sbase[i] = score;
-    score += (int64_t)m->A * len * es::score_ld((int)len);
+    score += (int64_t)m->A * es::score_block((int)len, m->causal);
   }
   L->score_elems = score;
   if (!plen && score > scale * m->score_cap)
@@ -527,7 +528,7 @@ es_status add_batch(es_model *m, const int32_t *h_off, int32_t n, const int32_t 
   for (int32_t i = 0; i < n; ++i) ord[i] = i;
   auto keys_of = [&](int32_t i) { return h_off[i + 1] - h_off[i] + (plen ? plen[i] : 0); };
   std::stable_sort(ord.begin(), ord.end(), [&](int32_t a, int32_t b) { return keys_of(a) > keys_of(b); });
-  std::vector<int32_t> items, sm_items, fitems, mitems, pitems;
+  std::vector<int32_t> items, sm_items, sm_wide, fitems, mitems, pitems;
   // shared-prompt candidates of up to kPfxMaxLen tokens whose prompt spans at
   // least kPfxMinPrompt positions: their 32-query tiles go four to a block,
   // grouped by prompt (all candidates of a prompt sort together: equal
@@ -572,11 +573,11 @@ es_status add_batch(es_model *m, const int32_t *h_off, int32_t n, const int32_t 
         fl.push_back(q0);
       }
     }
-    const int rpi = es::softmax_rows_per_item(len);
-    for (int r0 = 0; r0 < m->A * len; r0 += rpi) {
-      sm_items.push_back(sq);
-      sm_items.push_back(r0);
-    }
+    es::softmax_items(len, m->A, m->causal, [&](int r0, bool wide) {
+      auto &dst = wide ? sm_wide : sm_items;
+      dst.push_back(sq);
+      dst.push_back(r0);
+    });
   }
   auto &buf = m->meta_asm;
   L->off = push_bytes(buf, h_off, sizeof(int32_t) * (n + 1));
@@ -592,6 +593,8 @@ es_status add_batch(es_model *m, const int32_t *h_off, int32_t n, const int32_t 
   L->n_fitems = (int)(fitems.size() / 2);
   L->n_mitems = (int)(mitems.size() / 2);
   L->n_pitems = (int)(pitems.size() / 8);
+  L->n_sm_narrow = (int)(sm_items.size() / 2);
+  sm_items.insert(sm_items.end(), sm_wide.begin(), sm_wide.end());
   L->sm_items = push_bytes(buf, sm_items.data(), sizeof(int32_t) * sm_items.size());
   L->n_sm_items = (int)(sm_items.size() / 2);
   L->has_src = src != nullptr;
@@ -699,6 +702,7 @@ es::Ragged ragged_of(const char *meta, const BatchLayout &L) {
   r.n_pfx_items = L.n_pitems;
   r.sm_items = reinterpret_cast<const int32_t *>(meta + L.sm_items);
   r.n_sm_items = L.n_sm_items;
+  r.n_sm_narrow = L.n_sm_narrow;
   r.src = L.has_src ? reinterpret_cast<const int32_t *>(meta + L.src) : nullptr;
   r.dest = L.has_dest ? reinterpret_cast<const int32_t *>(meta + L.dest) : nullptr;
   r.pref = L.has_prefix ? reinterpret_cast<const int32_t *>(meta + L.pref) : nullptr;

@@ -54,7 +54,7 @@ extern "C" es_status es_ragged_create(const int32_t *h_lengths, int32_t n_seqs, 
   *out = nullptr;
   std::vector<int32_t> off(n_seqs + 1, 0);
   std::vector<int64_t> sbase(n_seqs);
-  std::vector<int32_t> items, sm_items, fitems, mitems;
+  std::vector<int32_t> items, sm_items, sm_wide, fitems, mitems;
   int64_t acc = 0;
   int max_len = 0;
   for (int32_t i = 0; i < n_seqs; ++i) {
@@ -63,7 +63,7 @@ extern "C" es_status es_ragged_create(const int32_t *h_lengths, int32_t n_seqs, 
     if ((int64_t)off[i] + n > INT32_MAX) return fail(ES_ERR_RANGE, "es_ragged_create: too many tokens");
     off[i + 1] = off[i] + n;
     sbase[i] = acc;
-    acc += (int64_t)n_heads * n * es::score_ld(n);
+    acc += (int64_t)n_heads * es::score_block(n, causal != 0);
     max_len = max_len > n ? max_len : n;
     for (int q0 = 0; q0 < n; q0 += es::kQTile) {
       items.push_back(i);
@@ -75,11 +75,14 @@ extern "C" es_status es_ragged_create(const int32_t *h_lengths, int32_t n_seqs, 
       fl.push_back(i);
       fl.push_back(q0);
     }
-    for (int r0 = 0; r0 < n_heads * n; r0 += es::softmax_rows_per_item(n)) {
-      sm_items.push_back(i);
-      sm_items.push_back(r0);
-    }
+    es::softmax_items(n, n_heads, causal != 0, [&](int r0, bool wide) {
+      auto &dst = wide ? sm_wide : sm_items;
+      dst.push_back(i);
+      dst.push_back(r0);
+    });
   }
+  const int32_t n_sm_narrow = (int32_t)(sm_items.size() / 2);
+  sm_items.insert(sm_items.end(), sm_wide.begin(), sm_wide.end());
   const size_t b_off = es::round_up((int64_t)off.size() * 4, 16);
   const size_t b_sb = es::round_up((int64_t)sbase.size() * 8, 16);
   const size_t b_it = es::round_up((int64_t)items.size() * 4, 16);
@@ -114,6 +117,7 @@ extern "C" es_status es_ragged_create(const int32_t *h_lengths, int32_t n_seqs, 
   g->r.n_items = (int32_t)(items.size() / 2);
   g->r.sm_items = (const int32_t *)((char *)g->dev + b_off + b_sb + b_it);
   g->r.n_sm_items = (int32_t)(sm_items.size() / 2);
+  g->r.n_sm_narrow = n_sm_narrow;
   g->r.fused_items = (const int32_t *)((char *)g->dev + b_off + b_sb + b_it + b_sm);
   g->r.n_fused_items = (int32_t)(fitems.size() / 2);
   g->r.mw_items = (const int32_t *)((char *)g->dev + b_off + b_sb + b_it + b_sm + b_fi);

@@ -206,12 +206,58 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t *__restrict__ 
 
 constexpr float kLog2e = 1.44269504088896340736f;
 
-// Softmax over the ragged score rows.  One item covers a run of rows of one
-// sequence's [A * n, ld] score block (all heads; rows of equal length n, or
-// q + 1 when causal).  Each row is owned by G lanes (G from its length) that
-// read it as float4 chunks straight into registers; both passes of rows are
-// loaded before any reduction so two rows per lane group are in flight.
-// Max and sum reduce by butterfly shuffles within the G-lane group.
+// Eight probabilities (chunk of a row) to P: one 16-byte store of bf16
+// (round to nearest even), or two float4 for an fp32 P.
+__device__ __forceinline__ void store8(uint16_t *p, const float (&o)[8]) {
+  *reinterpret_cast<uint4 *>(p) =
+      make_uint4(f2bf2(o[0], o[1]), f2bf2(o[2], o[3]), f2bf2(o[4], o[5]), f2bf2(o[6], o[7]));
+}
+__device__ __forceinline__ void store8(float *p, const float (&o)[8]) {
+  *reinterpret_cast<float4 *>(p) = make_float4(o[0], o[1], o[2], o[3]);
+  *reinterpret_cast<float4 *>(p + 4) = make_float4(o[4], o[5], o[6], o[7]);
+}
+
+// Softmax over the ragged score rows (TurboTransformers review, Proposed
+// method: Softmax as a parallel batch reduction over rows).  One item covers
+// a run of rows of one sequence's [A * n, ld] score block whose rows need the
+// same lane count G (softmax_item): G lanes own a row, each lane eight
+// consecutive scores per chunk, read as two float4 straight into registers
+// (branch-free: addresses clamped into the row, values past its end masked
+// to -inf); only the chunks the item's longest row needs are touched.  The
+// block walks its rows in passes of 4 wavefronts x (64 / G) rows with the
+// next pass's loads in flight while the current pass reduces, so a block
+// keeps memory busy through its whole run instead of one round trip per
+// pass.  Max and sum reduce by butterfly shuffles within the G-lane group;
+// each chunk goes out as one 16-byte store, with zeros past the row's last
+// score up to the next multiple of 8 (inside the row's allocated length; no
+// reader looks there).  Rows are addressed through score_row_off, so causal
+// blocks are read and written as their packed lower triangles.
+template <int NJ>
+__device__ __forceinline__ void softmax_load(const float *__restrict__ S, int64_t ro, int m, int c0,
+                                             int G, int nj, int cap, float (&v)[NJ][8]) {
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    if (j >= nj) break;  // uniform over the item
+    const int c = (c0 + G * j) * 8;
+    float4 lo, hi;
+    if (j == 0) {  // every lane: address clamped into the row, no branch
+      const int ca = min(c, cap - 8);
+      lo = *reinterpret_cast<const float4 *>(S + ro + ca);
+      hi = *reinterpret_cast<const float4 *>(S + ro + ca + 4);
+    } else if (c < m) {  // later chunks of long rows: only lanes inside the row
+      lo = *reinterpret_cast<const float4 *>(S + ro + c);
+      hi = *reinterpret_cast<const float4 *>(S + ro + c + 4);
+    } else {
+      lo = hi = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    const float t[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[j][e] = c + e < m ? t[e] : -INFINITY;
+  }
+}
+
+constexpr int kSmRing = 2;  // register sets of the softmax pipeline
+
 template <int NJ, typename PT>
 __global__ __launch_bounds__(256) void softmax_kernel(const float *__restrict__ S, PT *__restrict__ P,
                                                       const int32_t *__restrict__ off,
@@ -220,63 +266,83 @@ __global__ __launch_bounds__(256) void softmax_kernel(const float *__restrict__ 
                                                       int causal) {
   const int seq = items[2 * blockIdx.x], row0 = items[2 * blockIdx.x + 1];
   const int n = off[seq + 1] - off[seq];
-  const int ld = score_ld(n);
-  const int64_t base = sbase[seq];
-  const int G = softmax_lanes(n), rpw = kWave / G;
-  const int row_end = min(row0 + softmax_rows_per_item(n), n_heads * n);
+  const int64_t base = sbase[seq], block = score_block(n, causal != 0);
+  const SoftmaxItem it = softmax_item(row0, n, n_heads, causal != 0);
+  const int G = it.g;
+  const int nj = (it.longest + 8 * G - 1) / (8 * G);  // chunks per lane its longest row needs
+  const int rpw = kWave / G, rpp = 4 * rpw;  // rows per wavefront / per pass
+  const int passes = (it.rows + rpp - 1) / rpp;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
   const int sub = lane / G, c0 = lane % G;
-  float4 v[kSoftmaxPasses][NJ];
-  int m[kSoftmaxPasses];
-  int64_t ro[kSoftmaxPasses];
-#pragma unroll
-  for (int p = 0; p < kSoftmaxPasses; ++p) {
-    const int r = row0 + (p * 4 + wave) * rpw + sub;
-    m[p] = r < row_end ? (causal ? r % n + 1 : n) : 0;  // valid scores of row r
-    ro[p] = base + (int64_t)r * ld;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int c = (c0 + G * j) * 4;
-      v[p][j] = c < m[p] ? *reinterpret_cast<const float4 *>(S + ro[p] + c)
-                         : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+  // row i of the item (clamped to its last row for the lanes past it): its
+  // valid scores m (0 past the item), start ro and allocated length cap
+  auto row_of = [&](int p, int &m, int64_t &ro, int &cap) {
+    const int i = p * rpp + wave * rpw + sub, ic = min(i, it.rows - 1);
+    int h, q;
+    if (causal) {
+      const int qn = it.qe - it.qs;
+      h = it.h0 + ic / qn;
+      q = it.qs + ic % qn;
+    } else {
+      h = (row0 + ic) / n;
+      q = (row0 + ic) % n;
     }
+    m = i < it.rows ? (causal ? q + 1 : n) : 0;
+    ro = base + (int64_t)h * block + score_row_off(q, n, causal != 0);
+    cap = causal ? score_ld(q + 1) : score_ld(n);
+  };
+  // a ring of kSmRing register sets: pass p computes in set p % kSmRing
+  // while the loads of the next kSmRing - 1 passes are in flight
+  float v[kSmRing][NJ][8];
+  int m[kSmRing], cap[kSmRing];
+  int64_t ro[kSmRing];
+#pragma unroll
+  for (int d = 0; d < kSmRing - 1; ++d) {
+    if (d >= passes) break;
+    row_of(d, m[d], ro[d], cap[d]);
+    softmax_load<NJ>(S, ro[d], m[d], c0, G, nj, cap[d], v[d]);
   }
+  for (int p0 = 0; p0 < passes; p0 += kSmRing) {
 #pragma unroll
-  for (int p = 0; p < kSoftmaxPasses; ++p) {
-    float mx = -INFINITY;
+    for (int h = 0; h < kSmRing; ++h) {
+      const int p = p0 + h;
+      if (p >= passes) break;
+      constexpr int kAhead = kSmRing - 1;
+      const int nx = (h + kAhead) % kSmRing;
+      if (p + kAhead < passes) {
+        row_of(p + kAhead, m[nx], ro[nx], cap[nx]);
+        softmax_load<NJ>(S, ro[nx], m[nx], c0, G, nj, cap[nx], v[nx]);
+      }
+      float mx = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int c = (c0 + G * j) * 4;
-      if (c < m[p]) mx = fmaxf(mx, v[p][j].x);
-      if (c + 1 < m[p]) mx = fmaxf(mx, v[p][j].y);
-      if (c + 2 < m[p]) mx = fmaxf(mx, v[p][j].z);
-      if (c + 3 < m[p]) mx = fmaxf(mx, v[p][j].w);
-    }
-    mx = group_max(mx, G);
-    float sum = 0.f;
+      for (int j = 0; j < NJ; ++j) {
+        if (j >= nj) break;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int c = (c0 + G * j) * 4;
-      // exp(v - max) as 2^((v - max) log2 e): one v_exp_f32 each
-      v[p][j].x = c < m[p] ? __builtin_amdgcn_exp2f((v[p][j].x - mx) * kLog2e) : 0.f;
-      v[p][j].y = c + 1 < m[p] ? __builtin_amdgcn_exp2f((v[p][j].y - mx) * kLog2e) : 0.f;
-      v[p][j].z = c + 2 < m[p] ? __builtin_amdgcn_exp2f((v[p][j].z - mx) * kLog2e) : 0.f;
-      v[p][j].w = c + 3 < m[p] ? __builtin_amdgcn_exp2f((v[p][j].w - mx) * kLog2e) : 0.f;
-      sum += (v[p][j].x + v[p][j].y) + (v[p][j].z + v[p][j].w);
-    }
-    sum = group_sum(sum, G);
-    PT *pr = P + ro[p];
+        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, v[h][j][e]);
+      }
+      mx = group_max(mx, G);
+      float sum = 0.f;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int c = (c0 + G * j) * 4;
-      if (c >= m[p]) continue;
-      const float4 o = make_float4(v[p][j].x / sum, v[p][j].y / sum, v[p][j].z / sum, v[p][j].w / sum);
-      if (c + 3 < m[p]) {
-        store4(pr + c, o);
-      } else {
-        pr[c] = from_f<PT>(o.x);
-        if (c + 1 < m[p]) pr[c + 1] = from_f<PT>(o.y);
-        if (c + 2 < m[p]) pr[c + 2] = from_f<PT>(o.z);
+      for (int j = 0; j < NJ; ++j) {
+        if (j >= nj) break;
+        // exp(v - max) as 2^((v - max) log2 e): one v_exp_f32 each (masked
+        // entries give exp2(-inf) = 0)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[h][j][e] = __builtin_amdgcn_exp2f((v[h][j][e] - mx) * kLog2e);
+        sum += ((v[h][j][0] + v[h][j][1]) + (v[h][j][2] + v[h][j][3])) +
+               ((v[h][j][4] + v[h][j][5]) + (v[h][j][6] + v[h][j][7]));
+      }
+      sum = group_sum(sum, G);
+      const float inv = 1.0f / sum;  // one correctly rounded reciprocal per row
+      PT *pr = P + ro[h];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int c = (c0 + G * j) * 8;
+        if (j >= nj || c >= m[h]) continue;
+        float o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = v[h][j][e] * inv;
+        store8(pr + c, o);
       }
     }
   }
@@ -413,24 +479,30 @@ hipError_t launch_embed(bool w_bf16, bool act_bf16, bool ln, const int32_t *ids,
 hipError_t launch_softmax(bool p_bf16, const float *S, void *P, const Ragged &r, int n_heads,
                           bool causal, hipStream_t st) {
   if (r.n_sm_items <= 0) return hipSuccess;
-  const dim3 grid(r.n_sm_items), block(256);
-  const int nc = (r.max_len + 3) / 4;
-  const int nj = nc <= 64 ? 1 : (nc + 63) / 64;
-  auto go = [&](auto njc) {
+  const dim3 block(256);
+  // items [0, n_sm_narrow): rows of at most 512 scores, one chunk per lane;
+  // the rest: as many chunks as the longest row needs
+  auto go = [&](auto njc, int first, int count) {
     constexpr int NJ = decltype(njc)::value;
+    if (count <= 0) return hipSuccess;
+    const int32_t *it = r.sm_items + 2 * first;
     if (p_bf16)
-      softmax_kernel<NJ, uint16_t><<<grid, block, 0, st>>>(S, (uint16_t *)P, r.off, r.sbase,
-                                                            r.sm_items, n_heads, causal ? 1 : 0);
+      softmax_kernel<NJ, uint16_t><<<count, block, 0, st>>>(S, (uint16_t *)P, r.off, r.sbase, it,
+                                                             n_heads, causal ? 1 : 0);
     else
-      softmax_kernel<NJ, float><<<grid, block, 0, st>>>(S, (float *)P, r.off, r.sbase, r.sm_items,
-                                                         n_heads, causal ? 1 : 0);
+      softmax_kernel<NJ, float><<<count, block, 0, st>>>(S, (float *)P, r.off, r.sbase, it, n_heads,
+                                                          causal ? 1 : 0);
     return hipGetLastError();
   };
-  if (nj <= 1) return go(std::integral_constant<int, 1>{});
-  if (nj <= 2) return go(std::integral_constant<int, 2>{});
-  if (nj <= 4) return go(std::integral_constant<int, 4>{});
-  if (nj <= 8) return go(std::integral_constant<int, 8>{});
-  if (nj <= 16) return go(std::integral_constant<int, 16>{});
+  hipError_t e = go(std::integral_constant<int, 1>{}, 0, r.n_sm_narrow);
+  if (e != hipSuccess) return e;
+  const int first = r.n_sm_narrow, count = r.n_sm_items - r.n_sm_narrow;
+  const int nc = (r.max_len + 7) / 8;  // eight-score chunks of the longest row
+  const int nj = (nc + 63) / 64;
+  if (count <= 0) return hipSuccess;
+  if (nj <= 2) return go(std::integral_constant<int, 2>{}, first, count);
+  if (nj <= 4) return go(std::integral_constant<int, 4>{}, first, count);
+  if (nj <= 8) return go(std::integral_constant<int, 8>{}, first, count);
   return hipErrorInvalidValue;
 }
 

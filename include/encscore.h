@@ -471,11 +471,14 @@ es_status es_op_add_layernorm(const float *d_x, const float *d_sub, const float 
  * so that es_op_softmax can be launched repeatedly without host work.
  *
  * For sequence i of length n_i (h_lengths[i], 1..4096) and head h < n_heads,
- * rows q < n_i of the score block start at element
- *     base_i + (h * n_i + q) * ld_i,  ld_i = round_up(n_i, 8),
- *     base_0 = 0, base_{i+1} = base_i + n_heads * n_i * ld_i,
- * and hold n_i scores (causal = 1: q + 1 scores).  *n_elems (may be NULL)
- * receives base_{n_seqs}, the element count the score buffers need.
+ * row q < n_i of the score block starts at element
+ *     base_i + h * B_i + R_i(q),  base_0 = 0, base_{i+1} = base_i + n_heads * B_i,
+ * with B_i = R_i(n_i).  Bidirectional (causal = 0): R_i(q) = q * ld_i,
+ * ld_i = round_up(n_i, 8), and every row holds n_i scores.  Causal: the
+ * lower triangle packed, row q holding q + 1 scores in round_up(q + 1, 8)
+ * elements: R(q) = sum_{r<q} round_up(r + 1, 8) = 8 (t + 1)(4 t + s) for
+ * q = 8 t + s.  *n_elems (may be NULL) receives base_{n_seqs}, the element
+ * count the score buffers need.
  * Errors: ES_ERR_ARG (NULL, n_seqs < 1, n_heads < 1), ES_ERR_RANGE (a length
  * outside [1, 4096]), ES_ERR_HIP.
  */
@@ -489,7 +492,9 @@ void es_ragged_free(es_ragged *r);
  * (TurboTransformers review, Proposed method: Softmax as a row "batch
  * reduction"):  p = exp(s - max) / sum exp(s - max)  over the valid scores
  * of every row, written to the same positions of d_p (bf16 bits if
- * p_bf16 = 1, else float32); other positions are not written.  Asynchronous;
+ * p_bf16 = 1, else float32).  A row of m valid scores is written in chunks
+ * of 8: positions m .. round_up(m, 8) - 1 of the row (still inside its
+ * stride ld_i) receive 0; no other position is written.  Asynchronous;
  * allocates nothing.  Errors: ES_ERR_ARG.
  */
 es_status es_op_softmax(const es_ragged *r, const float *d_scores, void *d_p, int32_t p_bf16,
@@ -541,10 +546,11 @@ es_status es_op_gemm_bf16(const uint16_t *d_a, int32_t lda, const uint16_t *d_w,
  * es_op_gemm_bf16_tile -- es_op_gemm_bf16 with the block-tile configuration
  * forced instead of chosen from the shape (for tests and tuning): tile -1 =
  * automatic, 0 = 128x64 register-staged, 1 = 128x128 ping-pong, 2 = 256x256
- * ping-pong, 3 = 128x384 ping-pong, 4 = 32x64 register-staged.  Every
+ * ping-pong, 3 = 128x384 ping-pong, 4 = 32x64 register-staged, 5 = 256x256
+ * software-pipelined.  Every
  * configuration accumulates each
  * output over K in the same order, so all give bitwise the same result.
- * Errors: as es_op_gemm_bf16, and ES_ERR_ARG for a tile outside [-1, 4].
+ * Errors: as es_op_gemm_bf16, and ES_ERR_ARG for a tile outside [-1, 5].
  */
 es_status es_op_gemm_bf16_tile(const uint16_t *d_a, int32_t lda, const uint16_t *d_w,
                                const float *d_bias, const float *d_res, void *d_out, int32_t ldc,

@@ -78,24 +78,35 @@ def test_add_layernorm_op(rows, cols):
 
 
 def _ragged_rows(lengths, n_heads, causal):
-    """(element index of row start, n valid) for every (seq, head, row)."""
+    """(element index of row start, n valid) for every (seq, head, row): rows
+    of stride round_up(n, 8), or the causal lower triangle packed with row q
+    in round_up(q + 1, 8) elements (summed here row by row)."""
     out = []
     base = 0
     for n in lengths:
         ld = (n + 7) // 8 * 8
         for h in range(n_heads):
             for q in range(n):
-                out.append((base + (h * n + q) * ld, q + 1 if causal else n))
-        base += n_heads * n * ld
+                out.append((base, q + 1 if causal else n))
+                base += (q + 8) // 8 * 8 if causal else ld
     return out, base
 
 
+SOFTMAX_LENGTHS = {
+    "to560": [1, 2, 7, 8, 9, 16, 17, 31, 32, 33, 63, 64, 65, 100, 127, 128, 129, 255, 256, 257,
+              500, 511, 512, 513, 560],
+    "to1100": [3, 600, 1024, 1025, 1100],
+    "to4096": [5, 4096],
+}
+
+
+@pytest.mark.parametrize("lengths", list(SOFTMAX_LENGTHS), ids=list(SOFTMAX_LENGTHS))
 @pytest.mark.parametrize("causal", [0, 1])
-def test_softmax_op(causal):
+def test_softmax_op(causal, lengths):
     torch = need_gpu()
-    lengths = [1, 2, 7, 8, 9, 16, 17, 31, 32, 33, 63, 64, 65, 100, 127, 128, 129, 500, 560]
+    lengths = SOFTMAX_LENGTHS[lengths]
     A = 3
-    say("softmax causal", causal)
+    say("softmax causal", causal, "lengths up to", max(lengths))
     rag = RaggedScores(lengths, A, causal)
     rows, total = _ragged_rows(lengths, A, causal)
     assert rag.n_elems == total
@@ -110,16 +121,20 @@ def test_softmax_op(causal):
     g32 = p32.cpu().numpy()
     g16 = bf16_bits_to_f32(p16)
     written = np.zeros(total, dtype=bool)
+    zeroed = np.zeros(total, dtype=bool)
     worst32 = worst16 = 0.0
     for start, m in rows:
         want = oracle.softmax_rows(s[start:start + m].astype(np.float64)[None])[0]
         worst32 = max(worst32, float(np.max(np.abs(g32[start:start + m] - want))))
         worst16 = max(worst16, float(np.max(np.abs(g16[start:start + m] - want) / (want + 1e-30))))
         written[start:start + m] = True
+        zeroed[start + m:start + (m + 7) // 8 * 8] = True     # rest of the row's last 8-chunk
     assert worst32 < 2e-6
     assert worst16 <= 2.0 ** -8 + 1e-5
-    assert np.all(np.isnan(g32[~written]))                 # nothing outside valid scores
-    assert np.all(p16.cpu().numpy()[~written] == 0x7FC1)
+    assert np.all(g32[zeroed] == 0.0) and np.all(p16.cpu().numpy()[zeroed] == 0)
+    untouched = ~(written | zeroed)
+    assert np.all(np.isnan(g32[untouched]))                # nothing else written
+    assert np.all(p16.cpu().numpy()[untouched] == 0x7FC1)
     # rows sum to one
     assert max(abs(g32[st:st + m].sum() - 1.0) for st, m in rows) < 5e-6
     rag.close()
@@ -131,7 +146,7 @@ GEMM_SHAPES = [(1, 64, 64), (37, 936, 320), (300, 768, 768), (1000, 3072, 768),
 
 @pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
 @pytest.mark.parametrize("epi", [0, 1, 2, 3])
-@pytest.mark.parametrize("tile", [None, 0, 1, 2, 3, 4])
+@pytest.mark.parametrize("tile", [None, 0, 1, 2, 3, 4, 5])
 def test_gemm_bf16_op(M, N, K, epi, tile):
     torch = need_gpu()
     say("gemm", M, N, K, "epilogue", epi, "tile", tile)
@@ -169,7 +184,8 @@ def test_gemm_bf16_op(M, N, K, epi, tile):
         assert np.all(np.isnan(out.cpu().numpy()[:, N:]))
 
 
-@pytest.mark.parametrize("M,N,K", [(300, 768, 768), (4100, 2304, 768), (2100, 3072, 2048)])
+@pytest.mark.parametrize("M,N,K", [(300, 768, 768), (4100, 2304, 768), (2100, 3072, 2048),
+                                   (700, 2048, 8192)])
 def test_gemm_tiles_bitwise_identical(M, N, K):
     """Every tile configuration accumulates each output over K in the same
     order, so all of them give bitwise the same fp32 result (this is what
@@ -182,7 +198,7 @@ def test_gemm_tiles_bitwise_identical(M, N, K):
     dw = torch.from_numpy(f32_to_bf16_bits((rng.standard_normal((Nr, K)) / np.sqrt(K)).astype(np.float32)).view(np.int16)).cuda()
     db = torch.from_numpy((0.1 * rng.standard_normal(N)).astype(np.float32)).cuda()
     outs = []
-    for tile in (0, 1, 2, 3, 4):
+    for tile in (0, 1, 2, 3, 4, 5):
         out = torch.empty((M, N), dtype=torch.float32, device="cuda")
         gemm_bf16(da, dw, db, out, M, N, K, 3, tile=tile)
         outs.append(out)
@@ -202,7 +218,7 @@ def test_gemm_rejects_bad_shapes():
     a64 = torch.zeros((256, 64), dtype=torch.int16, device="cuda")
     w64 = torch.zeros((256, 64), dtype=torch.int16, device="cuda")
     with pytest.raises(EncScoreError):
-        gemm_bf16(a64, w64, bias, out, 4, 64, 64, 0, tile=5)  # no such tile
+        gemm_bf16(a64, w64, bias, out, 4, 64, 64, 0, tile=6)  # no such tile
 
 
 def test_bf16_conversion_ties_and_specials():
