@@ -10,6 +10,7 @@ provides device memory and the current stream):
     plan_batches_measured(lengths, T, C)     the same DP under a measured cost table C[b-1, l-1]
     pack_offsets(lengths, order, b, e)       packed offsets of one planned batch
     plan_arena(bytes, first, last, align)    offsets of tensors with lifetimes (workspace planner)
+    check_plan(lengths, heads, causal, ...)  build a call's per-pass metadata and check every index
 """
 from .api import (  # noqa: F401
     Scorer,
@@ -17,6 +18,7 @@ from .api import (  # noqa: F401
     plan_batches_measured,
     pack_offsets,
     plan_arena,
+    check_plan,
     layernorm,
     RaggedScores,
     softmax_ragged,

@@ -22,7 +22,7 @@ STATUS_NAMES = {0: "ES_OK", -1: "ES_ERR_ARG", -2: "ES_ERR_RANGE", -3: "ES_ERR_CA
 # every symbol declared in include/encscore.h
 EXPORTS = [
     "es_load_weights", "es_load_weights_mem", "es_free", "es_model_info", "es_score_batch",
-    "es_score_batch_static",
+    "es_score_batch_static", "es_check_plan", "es_blob_info",
     "es_score_requests",
     "es_forward_hidden", "es_set_reward_offset", "es_get_reward_offset", "es_calibrate_offset",
     "es_check_device_errors", "es_plan_batches", "es_plan_batches_measured", "es_set_cost_table", "es_pack_offsets", "es_op_layernorm", "es_op_add_layernorm",
@@ -71,6 +71,12 @@ _SIGS = {
     "es_model_info": (ctypes.c_int32, [_P, ctypes.POINTER(ModelInfo)]),
     "es_score_batch": (ctypes.c_int32, [_P, _P, _I32P, ctypes.c_int32, _P, _P]),
     "es_score_batch_static": (ctypes.c_int32, [_P, _P, _I32P, ctypes.c_int32, _P, _P]),
+    "es_blob_info": (ctypes.c_int32, [_P, ctypes.c_int64, ctypes.POINTER(ModelInfo)]),
+    "es_check_plan": (ctypes.c_int32, [_I32P, ctypes.c_int32, _I32P, _I32P, ctypes.c_int32,
+                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                       ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+                                       ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64),
+                                       ctypes.POINTER(ctypes.c_int64)]),
     "es_score_requests": (ctypes.c_int32, [_P, _P, _I32P, ctypes.c_int32, ctypes.c_int64, _P, _P, ctypes.POINTER(StreamStats)]),
     "es_forward_hidden": (ctypes.c_int32, [_P, _P, _I32P, ctypes.c_int32, ctypes.c_int32, _P, _P]),
     "es_score_best_of_n": (ctypes.c_int32, [_P, _P, _I32P, ctypes.c_int32, _I32P, _I32P, ctypes.c_int64, _P, _P, _P, ctypes.POINTER(StreamStats)]),
@@ -129,7 +135,8 @@ def load(path=None):
 def load_host(path):
     """Load a host-only build (planner + blob parser) with the planner signatures."""
     lib = ctypes.CDLL(path)
-    for name in ("es_plan_batches", "es_plan_batches_measured", "es_pack_offsets", "es_plan_arena", "es_last_error", "es_version"):
+    for name in ("es_plan_batches", "es_plan_batches_measured", "es_pack_offsets", "es_plan_arena",
+                 "es_check_plan", "es_blob_info", "es_last_error", "es_version"):
         res, args = _SIGS[name]
         fn = getattr(lib, name)
         fn.restype, fn.argtypes = res, args

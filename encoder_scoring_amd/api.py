@@ -89,6 +89,26 @@ def plan_arena(nbytes, first_step, last_step, align=1, lib=None):
     return off, total.value
 
 
+def check_plan(lengths, n_heads, causal, max_pos, max_tokens, max_seqs, batch_overhead,
+               batches_per_pass, prompt_lengths=None, cand_counts=None, lib=None):
+    """es_check_plan: build a call's per-pass metadata on the host and check
+    every index in it -> (passes, checks, violations); raises on a failure."""
+    lib = lib or _lib.load()
+    lengths = as_i32(lengths)
+    n_prompts = 0
+    pl = cc = None
+    if prompt_lengths is not None:
+        pl, cc = as_i32(prompt_lengths), as_i32(cand_counts)
+        n_prompts = pl.size
+    passes, checked, bad = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    check(lib, lib.es_check_plan(i32p(lengths), lengths.size, i32p(pl) if pl is not None else None,
+                                 i32p(cc) if cc is not None else None, n_prompts, int(n_heads),
+                                 int(bool(causal)), int(max_pos), int(max_tokens), int(max_seqs),
+                                 int(batch_overhead), int(batches_per_pass), ctypes.byref(passes),
+                                 ctypes.byref(checked), ctypes.byref(bad)))
+    return passes.value, checked.value, bad.value
+
+
 def pack_offsets(lengths, order, begin, end, lib=None):
     lib = lib or _lib.load()
     lengths, order = as_i32(lengths), as_i32(order)

@@ -18,8 +18,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libencscore.so")
 HOST_LIB = os.path.join(HERE, "libencscore_host.so")
 
-SOURCES = ["planner.cpp", "blob.cpp", "memplan.cpp", "model.hip", "ops.hip", "rowops.hip", "gemm.hip", "attn.hip"]
-HOST_SOURCES = ["planner.cpp", "blob.cpp", "memplan.cpp"]
+SOURCES = ["planner.cpp", "blob.cpp", "memplan.cpp", "layout.cpp", "model.hip", "ops.hip", "rowops.hip", "gemm.hip", "attn.hip"]
+HOST_SOURCES = ["planner.cpp", "blob.cpp", "memplan.cpp", "layout.cpp"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
@@ -69,14 +69,17 @@ def build(verbose=False, jobs=None):
     return LIB
 
 
-def build_host(extra_flags=()):
-    """Host-only planner + blob parser with g++ (no HIP); used by CPU tests."""
+def build_host(extra_flags=(), out=None):
+    """Host-only part (planner, arena planner, blob parser, pass metadata and
+    its checker) with g++, no HIP; used by the CPU tests.  `extra_flags`
+    (e.g. sanitizers) and `out` (another output path) for special builds."""
+    out = out or HOST_LIB
     cmd = ["g++", "-O2", "-g", "-fPIC", "-shared", "-std=c++17", "-Wall", *extra_flags,
-           *[os.path.join(CSRC, s) for s in HOST_SOURCES], "-o", HOST_LIB]
+           *[os.path.join(CSRC, s) for s in HOST_SOURCES], "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"host build failed: {' '.join(cmd)}\n{r.stderr}")
-    return HOST_LIB
+    return out
 
 
 def main(argv=None):

@@ -73,3 +73,26 @@ es_status parse_blob(const void *p, int64_t nbytes, ParsedBlob *out) {
 }
 
 }  // namespace es
+
+// Host only: validate a blob and report the model it holds.
+extern "C" es_status es_blob_info(const void *h_blob, int64_t nbytes, es_model_info_t *info) {
+  if (!h_blob || !info) return es::fail(ES_ERR_ARG, "es_blob_info: NULL argument");
+  es::ParsedBlob pb;
+  const es_status s = es::parse_blob(h_blob, nbytes, &pb);
+  if (s != ES_OK) return s;
+  std::memset(info, 0, sizeof(*info));
+  info->n_layers = (int32_t)pb.h.n_layers;
+  info->hidden = (int32_t)pb.h.hidden;
+  info->n_heads = (int32_t)pb.h.n_heads;
+  info->head_dim = (int32_t)(pb.h.hidden / pb.h.n_heads);
+  info->ffn = (int32_t)pb.h.ffn;
+  info->vocab = (int32_t)pb.h.vocab;
+  info->max_pos = (int32_t)pb.h.max_pos;
+  info->pre_ln = (int32_t)pb.h.pre_ln;
+  info->causal = (int32_t)pb.h.causal;
+  info->bf16 = pb.h.wdtype == 1;
+  info->eps = pb.h.eps;
+  info->reward_offset = pb.h.reward_offset;
+  es::clear_error();
+  return ES_OK;
+}

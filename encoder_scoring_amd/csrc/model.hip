@@ -27,6 +27,7 @@
 #include "blob.h"
 #include "common.h"
 #include "kernels.h"
+#include "layout.h"
 #include "memplan.h"
 
 // Scratch of es_score_batch_static, the entry point that allocates nothing:
@@ -40,6 +41,8 @@ namespace {
 
 using es::fail;
 using es::round_up;
+using es::BatchLayout;
+using es::push_bytes;
 
 #define HIP_TRY(expr)                                                                     \
   do {                                                                                    \
@@ -469,163 +472,23 @@ es_status build(const es::ParsedBlob &pb, int64_t max_tokens, int32_t max_seqs, 
 // ---- per-call metadata.  Every batch of a call gets offsets, score-block
 // bases, attention work items and (optionally) id-source / reward-slot maps,
 // assembled on the host, staged in pinned memory and uploaded in ONE copy.
-struct BatchLayout {
-  size_t off = 0, sbase = 0, items = 0, sm_items = 0, src = 0, dest = 0, pref = 0, plen = 0;
-  size_t fitems = 0, mitems = 0, pitems = 0;  // fused attention split by length (es::Ragged)
-  int n_fitems = 0, n_mitems = 0, n_pitems = 0;
-  size_t last_items = 0, last_rows = 0, iota = 0;  // last-token work of the pruned last layer
-  int64_t last_pairs = 0;  // visible (query, key) pairs of the last queries, over heads
-  bool has_src = false, has_dest = false, has_prefix = false;
-  int n = 0, n_items = 0, n_sm_items = 0, n_sm_narrow = 0, max_len = 0, n_tokens = 0;
-  int64_t pairs = 0;  // visible (query, key) pairs summed over heads
-  int64_t score_elems = 0;  // ragged score-block elements (unfused attention)
-};
 
-size_t push_bytes(std::vector<uint8_t> &buf, const void *p, size_t bytes) {
-  const size_t at = (size_t)round_up((int64_t)buf.size(), 16);
-  buf.resize(at + bytes);
-  if (bytes) std::memcpy(buf.data() + at, p, bytes);
-  return at;
+
+// The layout parameters of a loaded model (layout.cpp builds the metadata).
+es::LayoutParams layout_params(const es_model *m) {
+  es::LayoutParams p;
+  p.A = m->A;
+  p.causal = m->causal;
+  p.P = m->P;
+  p.max_tokens = m->max_tokens;
+  p.max_seqs = m->max_seqs;
+  p.score_cap = m->score_cap;
+  return p;
 }
 
-// Validate one batch's host offsets and append its metadata to m->meta_asm.
-// pref/plen (optional, both or neither): sequence i continues the plen[i]
-// tokens at packed rows pref[i].. (a shared prompt); then score capacity is
-// not checked (only the fused attention, which keeps no score buffer, takes
-// such layouts) and lengths are checked with the prompt included.
 es_status add_batch(es_model *m, const int32_t *h_off, int32_t n, const int32_t *src,
-                    const int32_t *dest, BatchLayout *L, int scale = 1,
-                    const int32_t *pref = nullptr, const int32_t *plen = nullptr) {
-  if (!h_off) return fail(ES_ERR_ARG, "offsets pointer is NULL");
-  if (n < 1) return fail(ES_ERR_ARG, "n_seqs=%d < 1", n);
-  if (n > (int64_t)scale * m->max_seqs)
-    return fail(ES_ERR_CAPACITY, "n_seqs=%d above max_seqs=%d", n, m->max_seqs);
-  if (h_off[0] != 0) return fail(ES_ERR_ARG, "offsets[0]=%d, must be 0", h_off[0]);
-  int max_len = 0;
-  int64_t score = 0;
-  std::vector<int64_t> sbase((size_t)n);
-  for (int32_t i = 0; i < n; ++i) {
-    const int64_t len = (int64_t)h_off[i + 1] - h_off[i];
-    const int64_t np = plen ? plen[i] : 0;
-    if (len < 1) return fail(ES_ERR_ARG, "offsets not strictly increasing at %d", i);
-    if (np + len > m->P)
-      return fail(ES_ERR_RANGE, "sequence %d has length %" PRId64 " > max_pos=%d", i, np + len, m->P);
-    if (h_off[i + 1] > scale * m->max_tokens)
-      return fail(ES_ERR_CAPACITY, "batch has more than max_tokens=%" PRId64 " tokens", m->max_tokens);
-    max_len = std::max<int>(max_len, (int)len);
-    // visible (query, key) pairs over the sequence's own queries
-    L->pairs += (int64_t)m->A * (m->causal ? len * np + len * (len + 1) / 2 : len * len);
-    sbase[i] = score;
-    score += (int64_t)m->A * es::score_block((int)len, m->causal);
-  }
-  L->score_elems = score;
-  if (!plen && score > scale * m->score_cap)
-    return fail(ES_ERR_CAPACITY, "batch needs %" PRId64 " score elements (capacity %" PRId64 ")",
-                score, m->score_cap);
-  // attention work items, longest sequences first
-  auto &ord = m->order_scratch;
-  ord.resize(n);
-  for (int32_t i = 0; i < n; ++i) ord[i] = i;
-  auto keys_of = [&](int32_t i) { return h_off[i + 1] - h_off[i] + (plen ? plen[i] : 0); };
-  std::stable_sort(ord.begin(), ord.end(), [&](int32_t a, int32_t b) { return keys_of(a) > keys_of(b); });
-  std::vector<int32_t> items, sm_items, sm_wide, fitems, mitems, pitems;
-  // shared-prompt candidates of up to kPfxMaxLen tokens whose prompt spans at
-  // least kPfxMinPrompt positions: their 32-query tiles go four to a block,
-  // grouped by prompt (all candidates of a prompt sort together: equal
-  // prompt keys, then longest first), so the prompt's key tiles are staged
-  // once per block
-  auto pfx_tile = [&](int32_t i) {
-    return plen && plen[i] >= es::kPfxMinPrompt && h_off[i + 1] - h_off[i] <= es::kPfxMaxLen;
-  };
-  if (plen)
-    std::stable_sort(ord.begin(), ord.end(), [&](int32_t a, int32_t b) {
-      const bool pa = pfx_tile(a), pb = pfx_tile(b);
-      if (pa != pb) return pa < pb;
-      if (pa && (plen[a] != plen[b] || pref[a] != pref[b]))
-        return plen[a] != plen[b] ? plen[a] > plen[b] : pref[a] < pref[b];
-      return keys_of(a) > keys_of(b);
-    });
-  int32_t pfx_slot = 0, pfx_np = -1, pfx_row = -1;
-  for (int32_t sq : ord) {
-    const int len = h_off[sq + 1] - h_off[sq];
-    for (int q0 = 0; q0 < len; q0 += es::kQTile) {
-      items.push_back(sq);
-      items.push_back(q0);
-    }
-    if (pfx_tile(sq)) {
-      if (plen[sq] != pfx_np || pref[sq] != pfx_row) {  // a new prompt starts a new block
-        for (; pfx_slot % 4; ++pfx_slot) {
-          pitems.push_back(-1);
-          pitems.push_back(0);
-        }
-        pfx_np = plen[sq];
-        pfx_row = pref[sq];
-      }
-      for (int q0 = 0; q0 < len; q0 += es::kQTile, ++pfx_slot) {
-        pitems.push_back(sq);
-        pitems.push_back(q0);
-      }
-    } else {
-      // fused attention: long sequences in 128-query blocks (K, V staged once)
-      auto &fl = len > es::kMwMinLen ? mitems : fitems;
-      for (int q0 = 0; q0 < len; q0 += len > es::kMwMinLen ? 4 * es::kQTile : es::kQTile) {
-        fl.push_back(sq);
-        fl.push_back(q0);
-      }
-    }
-    es::softmax_items(len, m->A, m->causal, [&](int r0, bool wide) {
-      auto &dst = wide ? sm_wide : sm_items;
-      dst.push_back(sq);
-      dst.push_back(r0);
-    });
-  }
-  auto &buf = m->meta_asm;
-  L->off = push_bytes(buf, h_off, sizeof(int32_t) * (n + 1));
-  L->sbase = push_bytes(buf, sbase.data(), sizeof(int64_t) * n);
-  L->items = push_bytes(buf, items.data(), sizeof(int32_t) * items.size());
-  L->fitems = push_bytes(buf, fitems.data(), sizeof(int32_t) * fitems.size());
-  L->mitems = push_bytes(buf, mitems.data(), sizeof(int32_t) * mitems.size());
-  for (; pfx_slot % 4; ++pfx_slot) {
-    pitems.push_back(-1);
-    pitems.push_back(0);
-  }
-  L->pitems = push_bytes(buf, pitems.data(), sizeof(int32_t) * pitems.size());
-  L->n_fitems = (int)(fitems.size() / 2);
-  L->n_mitems = (int)(mitems.size() / 2);
-  L->n_pitems = (int)(pitems.size() / 8);
-  L->n_sm_narrow = (int)(sm_items.size() / 2);
-  sm_items.insert(sm_items.end(), sm_wide.begin(), sm_wide.end());
-  L->sm_items = push_bytes(buf, sm_items.data(), sizeof(int32_t) * sm_items.size());
-  L->n_sm_items = (int)(sm_items.size() / 2);
-  L->has_src = src != nullptr;
-  L->has_dest = dest != nullptr;
-  if (src) L->src = push_bytes(buf, src, sizeof(int32_t) * n);
-  if (dest) L->dest = push_bytes(buf, dest, sizeof(int32_t) * n);
-  {
-    std::vector<int32_t> li((size_t)2 * n), lr((size_t)n), io((size_t)n + 1);
-    for (int32_t i = 0; i < n; ++i) {
-      const int32_t len = h_off[i + 1] - h_off[i];
-      li[2 * i] = i;
-      li[2 * i + 1] = len - 1;
-      lr[i] = h_off[i + 1] - 1;
-      io[i] = i;
-      L->last_pairs += (int64_t)m->A * (m->causal ? len + (plen ? plen[i] : 0) : len);
-    }
-    io[n] = n;
-    L->last_items = push_bytes(buf, li.data(), sizeof(int32_t) * li.size());
-    L->last_rows = push_bytes(buf, lr.data(), sizeof(int32_t) * lr.size());
-    L->iota = push_bytes(buf, io.data(), sizeof(int32_t) * io.size());
-  }
-  L->has_prefix = plen != nullptr;
-  if (plen) {
-    L->pref = push_bytes(buf, pref, sizeof(int32_t) * n);
-    L->plen = push_bytes(buf, plen, sizeof(int32_t) * n);
-  }
-  L->n = n;
-  L->n_items = (int)(items.size() / 2);
-  L->max_len = max_len;
-  L->n_tokens = h_off[n];
-  return ES_OK;
+                    const int32_t *dest, BatchLayout *L) {
+  return es::add_batch(layout_params(m), m->meta_asm, m->order_scratch, h_off, n, src, dest, L);
 }
 
 // Stage m->meta_asm in pinned memory and enqueue its upload on `st`.
@@ -1088,62 +951,15 @@ extern "C" es_status es_score_requests(es_model *m, const int32_t *d_token_ids,
   if (s != ES_OK) return s;
   if (!d_token_ids || !d_rewards || !h_lengths) return fail(ES_ERR_ARG, "NULL argument");
   if (n < 1) return fail(ES_ERR_ARG, "n=%d < 1", n);
-  for (int32_t i = 0; i < n; ++i)
-    if (h_lengths[i] < 1 || h_lengths[i] > m->P)
-      return fail(ES_ERR_RANGE, "lengths[%d]=%d outside [1, max_pos=%d]", i, h_lengths[i], m->P);
-  // a1: plan over the whole stream (host DP), budget = the workspace size
-  std::vector<int32_t> order((size_t)n), starts((size_t)n + 1);
-  int32_t nb = 0;
-  int64_t cost = 0;
-  if (m->cost_table.empty())
-    s = es_plan_batches(h_lengths, n, m->max_tokens, batch_overhead, order.data(), starts.data(),
-                        &nb, &cost);
-  else  // the table's first max_seqs rows: no planned batch outgrows a workspace
-    s = es_plan_batches_measured(h_lengths, n, m->max_tokens, m->cost_table.data(),
-                                 std::min(m->cost_max_batch, m->max_seqs), m->cost_max_len,
-                                 order.data(), starts.data(), &nb, &cost);
-  if (s != ES_OK) return s;
-  // request-order start of every sequence's ids in d_token_ids
-  std::vector<int32_t> first((size_t)n);
-  int64_t acc = 0;
-  for (int32_t i = 0; i < n; ++i) {
-    first[i] = (int32_t)acc;
-    acc += h_lengths[i];
-    if (acc > INT32_MAX) return fail(ES_ERR_RANGE, "more than INT32_MAX tokens in one call");
-  }
-  // a2: pack -- per batch, offsets over the plan order plus id-source and
-  // reward-slot maps.  G consecutive planned batches (similar lengths, the
-  // plan is sorted) are packed back to back into one layout and scored by one
-  // pass through the layers: every kernel works per token or per sequence, so
-  // a sequence's reward does not depend on which batches share the pass.
-  const int G = m->group;
-  const int32_t ng = (nb + G - 1) / G;
-  m->meta_asm.clear();
-  std::vector<BatchLayout> layouts((size_t)ng);
-  std::vector<int32_t> off, goff, src, dest;
-  int64_t padded = 0;
-  for (int32_t g = 0; g < ng; ++g) {
-    // ng passes of as equal a batch count as possible (each at most G)
-    const int32_t b0 = (int32_t)((int64_t)g * nb / ng), b1 = (int32_t)((int64_t)(g + 1) * nb / ng);
-    goff.assign(1, 0);
-    src.clear();
-    dest.clear();
-    for (int32_t b = b0; b < b1; ++b) {
-      const int32_t lo = starts[b], hi = starts[b + 1], k = hi - lo;
-      off.assign((size_t)k + 1, 0);
-      if ((s = es_pack_offsets(h_lengths, order.data(), lo, hi, off.data())) != ES_OK) return s;
-      const int32_t base = goff.back();
-      for (int32_t j = 0; j < k; ++j) {
-        goff.push_back(base + off[j + 1]);
-        src.push_back(first[order[lo + j]]);
-        dest.push_back(order[lo + j]);
-      }
-      padded += (int64_t)k * h_lengths[order[hi - 1]];
-    }
-    if ((s = add_batch(m, goff.data(), (int32_t)dest.size(), src.data(), dest.data(), &layouts[g],
-                       b1 - b0)) != ES_OK)
-      return s;
-  }
+  // a1 + a2 on the host (layout.cpp): plan the stream, pack groups of
+  // planned batches into passes with id-source and reward-slot maps
+  es::CallPlan plan;
+  if ((s = es::build_stream(layout_params(m), h_lengths, n, batch_overhead, m->group, m->cost_table,
+                            std::min(m->cost_max_batch, m->max_seqs), m->cost_max_len, m->meta_asm,
+                            m->order_scratch, &plan)) != ES_OK)
+    return s;
+  const std::vector<BatchLayout> &layouts = plan.passes;
+  const int32_t ng = (int32_t)layouts.size();
   hipStream_t st = static_cast<hipStream_t>(stream);
   if ((s = upload_meta(m, st)) != ES_OK) return s;
   // a3..a13: every group through the layers; the head scatters to request
@@ -1167,10 +983,10 @@ extern "C" es_status es_score_requests(es_model *m, const int32_t *d_token_ids,
     }
   }
   if (stats) {
-    stats->n_batches = nb;
-    stats->total_cost = cost;
-    stats->padded_tokens = padded;
-    stats->packed_tokens = acc;
+    stats->n_batches = plan.n_batches;
+    stats->total_cost = plan.total_cost;
+    stats->padded_tokens = plan.padded_tokens;
+    stats->packed_tokens = plan.packed_tokens;
   }
   es::clear_error();
   return ES_OK;
@@ -1189,87 +1005,16 @@ extern "C" es_status es_score_best_of_n(es_model *m, const int32_t *d_token_ids,
     return fail(ES_ERR_ARG, "shared-prompt scoring needs a causal bf16 model (a bidirectional "
                             "prompt's states depend on its continuation)");
   if (n_prompts < 1) return fail(ES_ERR_ARG, "n_prompts=%d < 1", n_prompts);
-  // per prompt: first candidate, token totals, group size (prompt + its candidates)
-  std::vector<int32_t> cstart((size_t)n_prompts + 1, 0), group((size_t)n_prompts);
-  std::vector<int64_t> pfirst((size_t)n_prompts), cfirst;
-  int64_t ptok = 0;
-  for (int32_t p = 0; p < n_prompts; ++p) {
-    if (h_cand_counts[p] < 1) return fail(ES_ERR_ARG, "prompt %d has %d candidates", p, h_cand_counts[p]);
-    if (h_prompt_lengths[p] < 1) return fail(ES_ERR_RANGE, "prompt %d has length %d", p, h_prompt_lengths[p]);
-    cstart[p + 1] = cstart[p] + h_cand_counts[p];
-    pfirst[p] = ptok;
-    ptok += h_prompt_lengths[p];
-  }
-  const int32_t n_cand = cstart[n_prompts];
-  cfirst.resize((size_t)n_cand);
-  int64_t ctok = 0;
-  for (int32_t p = 0; p < n_prompts; ++p) {
-    int64_t g = h_prompt_lengths[p];
-    for (int32_t c = cstart[p]; c < cstart[p + 1]; ++c) {
-      const int32_t len = h_cand_lengths[c];
-      if (len < 1 || (int64_t)h_prompt_lengths[p] + len > m->P)
-        return fail(ES_ERR_RANGE, "candidate %d: prompt %d + %d tokens outside [2, max_pos=%d]", c,
-                    h_prompt_lengths[p], len, m->P);
-      cfirst[c] = ptok + ctok;
-      ctok += len;
-      g += len;
-    }
-    if (g > m->max_tokens)
-      return fail(ES_ERR_CAPACITY, "prompt %d with its candidates has %" PRId64 " tokens > max_tokens=%" PRId64,
-                  p, g, m->max_tokens);
-    if (1 + h_cand_counts[p] > m->max_seqs)
-      return fail(ES_ERR_CAPACITY, "prompt %d has %d candidates (max_seqs=%d)", p, h_cand_counts[p], m->max_seqs);
-    group[p] = (int32_t)g;
-  }
-  if (ptok + ctok > INT32_MAX) return fail(ES_ERR_RANGE, "more than INT32_MAX tokens in one call");
-  // a1: the planner over prompt groups, each an item as long as its tokens
-  std::vector<int32_t> order((size_t)n_prompts), starts((size_t)n_prompts + 1);
-  int32_t nb = 0;
-  int64_t cost = 0;
-  if ((s = es_plan_batches(group.data(), n_prompts, m->max_tokens, batch_overhead, order.data(),
-                           starts.data(), &nb, &cost)) != ES_OK)
+  // a1 + a2 on the host (layout.cpp): plan prompt groups, lay out each pass
+  // as prompts followed by their candidates
+  es::CallPlan plan;
+  if ((s = es::build_best_of_n(layout_params(m), h_prompt_lengths, n_prompts, h_cand_lengths,
+                               h_cand_counts, batch_overhead, m->group, m->meta_asm,
+                               m->order_scratch, &plan)) != ES_OK)
     return s;
-  // a2: per pass (G planned batches), every group as its prompt followed by
-  // its candidates; a candidate continues its prompt's rows
-  const int G = m->group;
-  const int32_t ng = (nb + G - 1) / G;
-  m->meta_asm.clear();
-  std::vector<BatchLayout> layouts((size_t)ng);
-  std::vector<int32_t> off, src, dest, pref, plen;
-  int64_t padded = 0;
-  for (int32_t gi = 0; gi < ng; ++gi) {
-    const int32_t b0 = (int32_t)((int64_t)gi * nb / ng), b1 = (int32_t)((int64_t)(gi + 1) * nb / ng);
-    off.assign(1, 0);
-    src.clear();
-    dest.clear();
-    pref.clear();
-    plen.clear();
-    for (int32_t b = b0; b < b1; ++b) {
-      int32_t gmax = 0;
-      for (int32_t k = starts[b]; k < starts[b + 1]; ++k) {
-        const int32_t p = order[k];
-        gmax = std::max(gmax, group[p]);
-        const int32_t prow = off.back();
-        off.push_back(prow + h_prompt_lengths[p]);
-        src.push_back((int32_t)pfirst[p]);
-        dest.push_back(-1);
-        pref.push_back(0);
-        plen.push_back(0);
-        for (int32_t c = cstart[p]; c < cstart[p + 1]; ++c) {
-          off.push_back(off.back() + h_cand_lengths[c]);
-          src.push_back((int32_t)cfirst[c]);
-          dest.push_back(c);
-          pref.push_back(prow);
-          plen.push_back(h_prompt_lengths[p]);
-        }
-      }
-      padded += (int64_t)(starts[b + 1] - starts[b]) * gmax;
-    }
-    if ((s = add_batch(m, off.data(), (int32_t)dest.size(), src.data(), dest.data(), &layouts[gi],
-                       b1 - b0, pref.data(), plen.data())) != ES_OK)
-      return s;
-  }
-  const size_t cs_at = push_bytes(m->meta_asm, cstart.data(), sizeof(int32_t) * cstart.size());
+  const std::vector<BatchLayout> &layouts = plan.passes;
+  const int32_t ng = (int32_t)layouts.size();
+  const size_t cs_at = plan.cand_starts;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if ((s = upload_meta(m, st)) != ES_OK) return s;
   // a3..a13 per pass, passes in flight as in es_score_requests
@@ -1294,10 +1039,10 @@ extern "C" es_status es_score_best_of_n(es_model *m, const int32_t *d_token_ids,
   HIP_TRY(es::launch_best_of_n(d_rewards, reinterpret_cast<const int32_t *>(m->meta_dev + cs_at),
                                n_prompts, d_best, st));
   if (stats) {
-    stats->n_batches = nb;
-    stats->total_cost = cost;
-    stats->padded_tokens = padded;
-    stats->packed_tokens = ptok + ctok;
+    stats->n_batches = plan.n_batches;
+    stats->total_cost = plan.total_cost;
+    stats->padded_tokens = plan.padded_tokens;
+    stats->packed_tokens = plan.packed_tokens;
   }
   es::clear_error();
   return ES_OK;

@@ -99,6 +99,15 @@ void es_free(es_model *m);
 
 es_status es_model_info(const es_model *m, es_model_info_t *info);
 
+/*
+ * es_blob_info -- host only (never touches HIP): validate `nbytes` bytes of a
+ * weight blob exactly as es_load_weights_mem does (header fields, tensor
+ * sizes, no trailing bytes) and report the model's shape in *info (the
+ * capacity and device_bytes fields are 0).  Errors: ES_ERR_ARG (NULL),
+ * ES_ERR_FORMAT.
+ */
+es_status es_blob_info(const void *h_blob, int64_t nbytes, es_model_info_t *info);
+
 /* ----------------------------------------------------------------- scoring */
 
 /*
@@ -429,6 +438,29 @@ es_status es_pack_offsets(const int32_t *lengths, const int32_t *order, int32_t 
  */
 es_status es_plan_arena(const int64_t *bytes, const int32_t *first_step, const int32_t *last_step,
                         int32_t n, int64_t align, int64_t *offsets, int64_t *total);
+
+/*
+ * es_check_plan -- host only (never touches HIP): build every pass's
+ * metadata exactly as es_score_requests (n_prompts = 0: `lengths` are the n
+ * request lengths) or es_score_best_of_n (n_prompts > 0: `lengths` are the n
+ * candidate lengths, prompt_lengths[n_prompts] and cand_counts[n_prompts] as
+ * there) would for a model with n_heads heads, the given mask and max_pos,
+ * on a handle of max_tokens / max_seqs with batches_per_pass planned batches
+ * per pass, and check every index in it against the buffer it addresses:
+ * packed token offsets within the pass's rows, id sources within the id
+ * buffer, reward slots in range and written once, score-block bases and
+ * every softmax row's score elements within the pass's score buffer, and
+ * attention, softmax and last-token work items covering every query tile and
+ * score row exactly once.  *n_passes, *n_checked and *n_violations receive
+ * the counts.  Errors: those of es_score_requests / es_score_best_of_n's
+ * host validation, ES_ERR_ARG for a bad shape, ES_ERR_FORMAT when a check
+ * fails (es_last_error names the first).
+ */
+es_status es_check_plan(const int32_t *lengths, int32_t n, const int32_t *prompt_lengths,
+                        const int32_t *cand_counts, int32_t n_prompts, int32_t n_heads,
+                        int32_t causal, int32_t max_pos, int64_t max_tokens, int32_t max_seqs,
+                        int64_t batch_overhead, int32_t batches_per_pass, int64_t *n_passes,
+                        int64_t *n_checked, int64_t *n_violations);
 
 /* ------------------------------------------------------- single-kernel ops */
 /*
