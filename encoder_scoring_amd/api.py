@@ -384,7 +384,7 @@ def attention_fused(rag, qkv, ctx, head_dim, scale=None):
 
 def gemm_bf16(a, w, bias, out, M, N, K, epilogue, res=None, tile=None):
     """out = epilogue(A W^T + bias) on the bf16 MFMA kernel (a, w as int16 bits);
-    tile forces a block-tile configuration (0..4), None chooses from the shape."""
+    tile forces a block-tile configuration (0..6), None chooses from the shape."""
     torch = _torch()
     lib = _lib.load()
     args = (_dptr(a, torch.int16, "a"), a.shape[1], _dptr(w, torch.int16, "w"),

@@ -785,6 +785,75 @@ __global__ __launch_bounds__(512, 1) void gemm_sp_kernel(
                           n0, bias, res, out, ldc, M, N);
 }
 
+// ------------------------------------------------------------ latency tile
+// One wavefront per 32 x 32 output tile, operands loaded from global memory
+// straight into the MFMA's registers, D k-steps of 16 ahead: no LDS and no
+// barrier.  Lane (r, h) loads, for k-step kk, the 16-byte chunk of row r at
+// columns 16 kk + 8 h .. + 8 of A and of W -- the fragment the LDS-staged
+// blocks hand to the same MFMA -- so each output accumulates bitwise as in
+// every other tile.  For the small passes (one short sequence, a last layer
+// pruned to one row per sequence) a block's time is the chain of K / 16
+// dependent MFMAs plus memory latency; the LDS-staged blocks add an LDS
+// write, a barrier and an LDS read round trip to every k-step of that chain.
+template <int EPI, int D>
+__global__ __launch_bounds__(64) void gemm_lat_kernel(const uint16_t *__restrict__ A, int lda,
+                                                      const uint16_t *__restrict__ W,
+                                                      const float *__restrict__ bias,
+                                                      const float *res, void *out, int ldc, int M,
+                                                      int N, int K, int tiles_n) {
+  const int lane = threadIdx.x, fr = lane & 31, fh = lane >> 5;
+  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+  const int64_t m0 = (int64_t)tm * 32;
+  const int n0 = tn * 32;
+  const uint16_t *ap = A + (m0 + fr) * lda + 8 * fh;
+  const uint16_t *wp = W + (int64_t)(n0 + fr) * K + 8 * fh;
+  const int nk = K / 16;
+  static_assert(D % 4 == 0, "the tail runs in groups of 4 k-steps");
+  bf16x8 fa[D], fb[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    const int k = min(d, nk - 1);
+    fa[d] = *reinterpret_cast<const bf16x8 *>(ap + 16 * k);
+    fb[d] = *reinterpret_cast<const bf16x8 *>(wp + 16 * k);
+  }
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  // fragment set d holds k-step k + d; once used it is refilled with k-step
+  // k + d + D (past the end: the last k-step again, in bounds, never used).
+  // No branch inside the loop, so the compiler's waits stay per fragment.
+  int k = 0;
+  for (; k + D <= nk; k += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[d], fa[d], acc, 0, 0, 0);
+      const int kn = min(k + d + D, nk - 1);
+      fa[d] = *reinterpret_cast<const bf16x8 *>(ap + 16 * kn);
+      fb[d] = *reinterpret_cast<const bf16x8 *>(wp + 16 * kn);
+      __builtin_amdgcn_sched_barrier(0);  // keep each refill right after its MFMA
+    }
+  }
+  // the last nk - k < D k-steps (a multiple of 4: K is a multiple of 64)
+#pragma unroll
+  for (int d = 0; d < D; d += 4) {
+    if (k + d < nk) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[d + e], fa[d + e], acc, 0, 0, 0);
+    }
+  }
+  // lane holds row m0 + (lane & 31), register r column 8 (r / 4) + 4 (lane / 32) + r % 4
+  const int64_t m = m0 + fr;
+  if (m >= M) return;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int n = n0 + 8 * g + 4 * fh;
+    if (n < N)
+      epi_store4<EPI>(out, res, ldc, m, n, N, make_float4(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]),
+                      bias);
+  }
+}
+
 // ---------------------------------------------------------------- fp32 SIMT
 // 64 x 64 tile, K step 16, 4 x 4 outputs per thread; for the fp32 model.
 template <int EPI>
@@ -924,6 +993,36 @@ hipError_t go_sp(const uint16_t *A, int lda, const uint16_t *W, const float *bia
   return hipGetLastError();
 }
 
+constexpr int kLatDepth = 16;  // k-steps of 16 in flight per wavefront (128 VGPRs of fragments)
+
+hipError_t go_lat(const uint16_t *A, int lda, const uint16_t *W, const float *bias,
+                  const float *res, void *out, int ldc, int M, int N, int K, int epi,
+                  hipStream_t st) {
+  if (K % 16) return hipErrorInvalidValue;
+  const int tm = (M + 31) / 32, tn = (N + 31) / 32;
+  const dim3 grid((unsigned)tm * tn), block(64);
+  switch (epi) {
+    case kEpiBias:
+      gemm_lat_kernel<kEpiBias, kLatDepth><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K, tn);
+      break;
+    case kEpiGelu:
+      gemm_lat_kernel<kEpiGelu, kLatDepth><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K, tn);
+      break;
+    case kEpiResidual:
+      gemm_lat_kernel<kEpiResidual, kLatDepth><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K, tn);
+      break;
+    case kEpiF32:
+      gemm_lat_kernel<kEpiF32, kLatDepth><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K, tn);
+      break;
+    case kEpiResidualFfn:
+      gemm_lat_kernel<kEpiResidualFfn, kLatDepth><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K, tn);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 // Tile configurations:
 //   0  T1  128 x 64, register-staged, 4 waves (64 x 32 each), three blocks per CU
 //   1  P1  128 x 128 ping-pong, 8 waves (64 x 32 each), two blocks per CU
@@ -939,8 +1038,11 @@ hipError_t go_sp(const uint16_t *A, int lda, const uint16_t *W, const float *bia
 //          128 x 64 blocks would leave most CUs idle (380 x 768 x 3072:
 //          27.2 -> 20.4 us)
 //   5  S2  256 x 256 software-pipelined, 8 waves (128 x 64 each), one block
-//          per CU, A triple-buffered (all 160 KiB of LDS); it runs wherever
-//          the cost model below picks a wide block (2 or 3)
+//          per CU, A triple-buffered (all 160 KiB of LDS) for N < 2048, double
+//          buffered for wider products; it runs wherever the cost model below
+//          picks a wide block (2 or 3)
+//   6  L   32 x 32 per wavefront, one wavefront per block, operands straight
+//          from memory into registers (latency tile for the smallest passes)
 //                  BM  BN  BK WGM WGN PF MINW
 using T1 = Cfg<128, 64, 64, 2, 2, 2, 3>;
 using T0 = Cfg<32, 64, 64, 1, 2, 2, 3>;
@@ -948,7 +1050,8 @@ using P1 = PPCfg<128, 128>;
 using P2 = PPCfg<256, 256>;
 using P3 = PPCfg<128, 384>;
 using S2 = SPCfg<256, 256, 3>;
-static_assert(kGemmTiles == 6, "tile menu and launcher disagree");
+using S2w = SPCfg<256, 256, 2>;
+static_assert(kGemmTiles == 7, "tile menu and launcher disagree");
 
 constexpr int kCUs = 256;
 
@@ -983,6 +1086,13 @@ constexpr int kCUs = 256;
 // other sequences in the batch.
 int gemm_tile_index(int M, int N, int K, int epi) {
   const int64_t b128 = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
+  // at most one 32 x 32 wavefront per CU: the latency tile (kernel time on
+  // MI355X, TinyBERT at 64 rows: 4.7 -> 4.4 us QKV, 8.4 -> 6.9 us FFN2;
+  // BERT-base FFN2 at 64 rows 16.6 -> 13.8 us; decoder FFN2 at one row 38.7
+  // -> 30.6 us).  With more wavefronts than CUs its operand loads, 32 rows
+  // of 32 bytes per instruction, queue in the CUs' address units and the
+  // 32 x 64 block wins (decoder QKV at 256 rows: 18.7 vs 53.0 us).
+  if (b128 < kCUs / 2 && (int64_t)((M + 31) / 32) * ((N + 31) / 32) <= kCUs) return 6;
   if (b128 < kCUs / 2) {
     const int64_t b128x64 = (int64_t)((M + 127) / 128) * ((N + 63) / 64);
     return b128x64 < kCUs ? 4 : 0;  // fewer 128 x 64 blocks than CUs: 32 x 64
@@ -1038,7 +1148,14 @@ hipError_t launch_gemm_bf16_tile(int tile, const uint16_t *A, int lda, const uin
         return go_pp<P1, 0>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
       return go_pp<P3, 1>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
     case 4: return go_bf16<T0>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
-    case 5: return go_sp<S2>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
+    case 5:
+      // A triple-buffered only for narrow N, whose few column tiles share each
+      // A panel little, so A streams from HBM (BERT-base FFN2 at ~80 k rows:
+      // 857 -> 946 TFLOP/s); the wide decoder products run 2-9 % faster with
+      // two A buffers (QKV at 80 k rows: 2.49e7 -> 2.28e7 busy cycles)
+      if (N >= 2048) return go_sp<S2w>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
+      return go_sp<S2>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
+    case 6: return go_lat(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -84,8 +84,9 @@ hipError_t launch_gemm_bf16(const uint16_t *A, int lda, const uint16_t *W, const
                             hipStream_t st);
 // The same with one tile configuration forced: 0 = 128 x 64 register-staged,
 // 1 = 128 x 128 ping-pong, 2 = 256 x 256 ping-pong, 3 = 128 x 384 ping-pong,
-// 4 = 32 x 64 register-staged, 5 = 256 x 256 software-pipelined.
-constexpr int kGemmTiles = 6;
+// 4 = 32 x 64 register-staged, 5 = 256 x 256 software-pipelined, 6 = 32 x 32
+// per wavefront fed straight from memory (latency tile).
+constexpr int kGemmTiles = 7;
 hipError_t launch_gemm_bf16_tile(int tile, const uint16_t *A, int lda, const uint16_t *W,
                                  const float *bias, const float *res, void *out, int ldc, int M,
                                  int N, int K, int epi, hipStream_t st);

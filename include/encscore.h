@@ -579,10 +579,10 @@ es_status es_op_gemm_bf16(const uint16_t *d_a, int32_t lda, const uint16_t *d_w,
  * forced instead of chosen from the shape (for tests and tuning): tile -1 =
  * automatic, 0 = 128x64 register-staged, 1 = 128x128 ping-pong, 2 = 256x256
  * ping-pong, 3 = 128x384 ping-pong, 4 = 32x64 register-staged, 5 = 256x256
- * software-pipelined.  Every
- * configuration accumulates each
- * output over K in the same order, so all give bitwise the same result.
- * Errors: as es_op_gemm_bf16, and ES_ERR_ARG for a tile outside [-1, 5].
+ * software-pipelined, 6 = 32x32 per wavefront with operands loaded straight
+ * into registers.  Every configuration accumulates each output over K in the
+ * same order, so all give bitwise the same result.
+ * Errors: as es_op_gemm_bf16, and ES_ERR_ARG for a tile outside [-1, 6].
  */
 es_status es_op_gemm_bf16_tile(const uint16_t *d_a, int32_t lda, const uint16_t *d_w,
                                const float *d_bias, const float *d_res, void *d_out, int32_t ldc,

@@ -146,7 +146,7 @@ GEMM_SHAPES = [(1, 64, 64), (37, 936, 320), (300, 768, 768), (1000, 3072, 768),
 
 @pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
 @pytest.mark.parametrize("epi", [0, 1, 2, 3])
-@pytest.mark.parametrize("tile", [None, 0, 1, 2, 3, 4, 5])
+@pytest.mark.parametrize("tile", [None, 0, 1, 2, 3, 4, 5, 6])
 def test_gemm_bf16_op(M, N, K, epi, tile):
     torch = need_gpu()
     say("gemm", M, N, K, "epilogue", epi, "tile", tile)
@@ -198,7 +198,7 @@ def test_gemm_tiles_bitwise_identical(M, N, K):
     dw = torch.from_numpy(f32_to_bf16_bits((rng.standard_normal((Nr, K)) / np.sqrt(K)).astype(np.float32)).view(np.int16)).cuda()
     db = torch.from_numpy((0.1 * rng.standard_normal(N)).astype(np.float32)).cuda()
     outs = []
-    for tile in (0, 1, 2, 3, 4, 5):
+    for tile in (0, 1, 2, 3, 4, 5, 6):
         out = torch.empty((M, N), dtype=torch.float32, device="cuda")
         gemm_bf16(da, dw, db, out, M, N, K, 3, tile=tile)
         outs.append(out)
@@ -218,7 +218,7 @@ def test_gemm_rejects_bad_shapes():
     a64 = torch.zeros((256, 64), dtype=torch.int16, device="cuda")
     w64 = torch.zeros((256, 64), dtype=torch.int16, device="cuda")
     with pytest.raises(EncScoreError):
-        gemm_bf16(a64, w64, bias, out, 4, 64, 64, 0, tile=6)  # no such tile
+        gemm_bf16(a64, w64, bias, out, 4, 64, 64, 0, tile=7)  # no such tile
 
 
 def test_bf16_conversion_ties_and_specials():
