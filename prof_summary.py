@@ -5,11 +5,18 @@ kept under profiles/.
     python prof_summary.py kernels STATS_CSV --command CMD [--title T] [--top N]
     python prof_summary.py traffic --fetch CSV --write CSV --probe-fetch CSV --probe-write CSV
                                    --probe-mib MIB --kernel-class CLASS --command CMD...
+    python prof_summary.py calls TRACE_CSV --bench-json JSON --command CMD [--title T]
 
 `kernels` reads `<prefix>_kernel_stats.csv` (rocprofv3 --kernel-trace --stats)
 and prints the per-kernel table plus, for every GEMM class, the calls-weighted
 average launch duration over the kernels of that class (the tile is chosen per
 pass size, so a class can span several kernels).
+
+`calls` reads `<prefix>_kernel_trace.csv` of bench.py --fixed-length-only
+(tinybert) and splits the library's dispatches into es_score_batch calls at
+each embedding kernel: per shape (200 timed calls after 10 warm-up calls,
+shapes in bench.py's order) the kernels per call, the median summed kernel
+time and the median per-kernel time, next to the plain run's wall clock.
 
 `traffic` reads the `counter_collection.csv` files of two --pmc runs of the
 same command (FETCH_SIZE, then WRITE_SIZE) and of two runs over hbm_probe.py
@@ -99,6 +106,50 @@ def kernels(a):
               f"({d['config']['passes_in_flight']} pass(es) in flight)")
 
 
+def calls(a):
+    import json
+    import statistics
+    rows = sorted(csv.DictReader(open(a.trace)), key=lambda r: int(r["Dispatch_Id"]))
+    per_call, cur = [], None
+    for r in rows:
+        if "embed_kernel" in r["Kernel_Name"]:
+            cur = []
+            per_call.append(cur)
+        if cur is not None and "es::" in r["Kernel_Name"]:
+            cur.append(r)
+    walls = json.loads([l for l in open(a.bench_json) if l.startswith("{")][-1])["fixed_length_calls"]
+    shapes = list(walls)
+    warm, timed = 10, 200
+    want = len(shapes) * (warm + timed)
+    if len(per_call) < want:
+        sys.exit(f"{len(per_call)} calls in the trace, expected at least {want}")
+    per_call = per_call[len(per_call) - want:]  # calls made before the timed shapes (warm-up) dropped
+    dur = lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    print(f"# rocprofv3 kernel trace: {a.title}")
+    print("# command (after `cd /tmp && export TMPDIR=/tmp`, from the repository root):")
+    print(f"#   {a.command}")
+    print("# per shape: 200 timed calls (after 10 warm-up calls) split at each embedding kernel; medians over")
+    print("# the calls; the library's kernels only.  'wall clock' = bench.py's fixed_length_calls figure of the")
+    print("# same command run plainly (host-synchronised call, median and 99th percentile).")
+    for i, shape in enumerate(shapes):
+        cs = per_call[i * (warm + timed) + warm:(i + 1) * (warm + timed)]
+        ksum = statistics.median(sum(dur(r) for r in c) for c in cs)
+        w = walls[shape]
+        print()
+        print(f"{shape}: {statistics.median(len(c) for c in cs):.0f} kernels per call, kernel sum {ksum:.1f} us; "
+              f"wall clock {w['ms_median'] * 1e3:.1f} us (p99 {w['ms_p99'] * 1e3:.1f} us) per call")
+        agg = defaultdict(list)
+        for c in cs:
+            d = defaultdict(float)
+            for r in c:
+                d[short(r["Kernel_Name"])] += dur(r)
+            for k, v in d.items():
+                agg[k].append(v)
+        for k, v in sorted(agg.items(), key=lambda kv: -statistics.median(kv[1])):
+            n = statistics.median(sum(1 for r in c if short(r["Kernel_Name"]) == k) for c in cs[:5])
+            print(f"  {k[:64]:64s} {n:3.0f} per call  {statistics.median(v):8.2f} us per call")
+
+
 def counter_kib(path, pattern):
     """(dispatches, summed counter value) of the kernels whose name matches."""
     disp = set()
@@ -158,6 +209,11 @@ def main():
     k.add_argument("--title", default="")
     k.add_argument("--top", type=int, default=24)
     k.add_argument("--bench-log", default=None, help="stdout of the profiled bench.py run")
+    c = sub.add_parser("calls")
+    c.add_argument("trace")
+    c.add_argument("--bench-json", required=True, help="stdout of the plain bench.py run")
+    c.add_argument("--command", required=True)
+    c.add_argument("--title", default="")
     t = sub.add_parser("traffic")
     for f in ("fetch", "write", "probe_fetch", "probe_write"):
         t.add_argument("--" + f.replace("_", "-"), dest=f, required=True)
@@ -169,7 +225,7 @@ def main():
                    help="kernel dispatches that make one launch of the class (the softmax "
                         "runs rows of up to 512 scores and longer rows as two dispatches)")
     a = ap.parse_args()
-    (kernels if a.mode == "kernels" else traffic)(a)
+    {"kernels": kernels, "traffic": traffic, "calls": calls}[a.mode](a)
 
 
 if __name__ == "__main__":
