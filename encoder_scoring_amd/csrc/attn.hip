@@ -185,12 +185,23 @@ __global__ __launch_bounds__(64) void scores_mfma_kernel(const uint16_t *__restr
 }
 
 // V tile of keys [k0, k0 + 32) of one head, staged into LDS transposed:
-// sV[e * kVP + key].  A lane loads 4 keys x 8 dims (four coalesced 16-byte
-// reads along the key rows) and writes them as eight 8-byte rows of 4 keys,
-// so the MFMA fragments below read keys contiguously.  Keys >= n become 0.
-// Loading and storing are separate steps so that a kernel can put the loads
-// of a tile in flight together with its other loads before it waits.
-constexpr int kVP = 40;  // LDS pitch of a transposed row (32 keys + 8, keeps 16-byte reads aligned)
+// sV[e * VP + key].  A lane loads 4 keys x 8 dims (four 16-byte reads along
+// the key rows) and writes them as eight 8-byte rows of 4 keys, so the MFMA
+// fragments below read keys contiguously.  Keys >= n become 0.  Loading and
+// storing are separate steps so that a kernel can put the loads of a tile in
+// flight together with its other loads before it waits.
+// Lane u takes keys 4 (u % 8) .. + 3 and dims 8 (u / 8) .. + 7, so the 32
+// lanes of one 8-byte LDS store cycle write 4 dim octets x 8 key quads.  The
+// fused kernels use pitch kVPF = 36 (72 bytes): those stores then land on
+// 16 oct + 18 d + 2 quad (mod 64) -- every bank once -- and the fragment
+// reads of lanes r = 0..31 (8 bytes at row r) on 18 r (mod 64), also
+// distinct.  With the earlier pitch of 40 and dim-octet-fastest lanes, a
+// store hit each bank pair eight times (rocprofv3 on the decoder's
+// attention: SQ_LDS_BANK_CONFLICT 1.56e8 cycles per launch, 37 % of the
+// CUs' time).  The unfused P.V kernel reads 16-byte fragments and keeps the
+// 16-byte aligned pitch kVP = 40.
+constexpr int kVP = 40;   // pitch for 16-byte fragment reads (unfused P.V)
+constexpr int kVPF = 36;  // pitch for the fused kernels' 8-byte reads (conflict-free)
 
 template <int DP, int NTH = 64>
 struct VtTile {
@@ -209,7 +220,7 @@ __device__ __forceinline__ void load_vt(VtTile<DP, NTH> &t, const uint16_t *__re
   using T = VtTile<DP, NTH>;
 #pragma unroll
   for (int i = 0; i < T::NU; ++i) {
-    const int u = (lane + NTH * i) % T::UNITS, quad = u / T::OCT, oct = u % T::OCT;
+    const int u = (lane + NTH * i) % T::UNITS, quad = u % 8, oct = u / 8;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int key = k0 + 4 * quad + j, kc = min(key, n - 1);
@@ -219,13 +230,13 @@ __device__ __forceinline__ void load_vt(VtTile<DP, NTH> &t, const uint16_t *__re
   }
 }
 
-template <int DP, int NTH = 64>
+template <int DP, int VP, int NTH = 64>
 __device__ __forceinline__ void store_vt(uint16_t *__restrict__ sV, VtTile<DP, NTH> &t, int k0, int n,
                                          int lane) {
   using T = VtTile<DP, NTH>;
 #pragma unroll
   for (int i = 0; i < T::NU; ++i) {
-    const int u = lane + NTH * i, quad = (u % T::UNITS) / T::OCT, oct = u % T::OCT;
+    const int u = lane + NTH * i, quad = u % 8, oct = (u % T::UNITS) / 8;
     if (k0 + 32 > n) {  // only the last tile of a sequence has keys to clear
 #pragma unroll
       for (int j = 0; j < 4; ++j)
@@ -241,7 +252,7 @@ __device__ __forceinline__ void store_vt(uint16_t *__restrict__ sV, VtTile<DP, N
         };
         const uint2 w = make_uint2(pick(t.r[i][0]) | (pick(t.r[i][1]) << 16),
                                    pick(t.r[i][2]) | (pick(t.r[i][3]) << 16));
-        *reinterpret_cast<uint2 *>(sV + (oct * 8 + d) * kVP + 4 * quad) = w;
+        *reinterpret_cast<uint2 *>(sV + (oct * 8 + d) * VP + 4 * quad) = w;
       }
     }
   }
@@ -279,7 +290,7 @@ __global__ __launch_bounds__(64) void pv_mfma_kernel(const uint16_t *__restrict_
     VtTile<DP> vt;
     load_vt<DP>(vt, V, V, 0, ldq, k0, n, lane);
     __syncthreads();
-    store_vt<DP>(sV, vt, k0, n, lane);
+    store_vt<DP, kVP>(sV, vt, k0, n, lane);
     __syncthreads();
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
@@ -421,7 +432,7 @@ struct QueryTile {
       const int c0 = 16 * kk + 4 * fh;  // tile keys of slots 0..3; slots 4..7 are c0 + 8
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const uint16_t *vr = sV + (t * 32 + fr) * kVP + c0;
+        const uint16_t *vr = sV + (t * 32 + fr) * kVPF + c0;
         const uint2 lo = *reinterpret_cast<const uint2 *>(vr);
         const uint2 hi = *reinterpret_cast<const uint2 *>(vr + 8);
         const bf16x8 vf = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
@@ -504,7 +515,7 @@ __global__ __launch_bounds__(64) void attn_fused_kernel(const uint16_t *__restri
                                                         const int32_t *__restrict__ plen,
                                                         uint16_t *__restrict__ ctx, int ldc) {
   constexpr int KS = DP / 16;
-  __shared__ __attribute__((aligned(16))) uint16_t sV[DP * kVP];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[DP * kVPF];
   const int item = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
   const int seq = items[2 * item], q0 = items[2 * item + 1];
   const HeadRows hr = head_rows<DP, PFX>(qkv, ldq, n_heads, h, seq, off, pref, plen);
@@ -527,7 +538,7 @@ __global__ __launch_bounds__(64) void attn_fused_kernel(const uint16_t *__restri
     __builtin_amdgcn_sched_barrier(0);  // every load of the tile issued before the first wait
     f32x16 s = qt.scores(kf, qf);
     __syncthreads();  // the previous tile's P.V reads of sV are done
-    store_vt<DP>(sV, vt, k0, hr.ntot, lane);
+    store_vt<DP, kVPF>(sV, vt, k0, hr.ntot, lane);
     qt.update(s, k0, hr.ntot, hr.np, causal != 0, sl2);
     __syncthreads();
     qt.pv(s, sV);
@@ -554,7 +565,7 @@ __global__ __launch_bounds__(256) void attn_fused_mw_kernel(const uint16_t *__re
   constexpr int KCH = 32 * CPR;                 // 16-byte chunks of a K tile
   constexpr int KPT = (KCH + 255) / 256;        // chunks per thread
   __shared__ __attribute__((aligned(16))) uint16_t sK[32 * DP];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[DP * kVP];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[DP * kVPF];
   const int item = blockIdx.x, h = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int seq = items[2 * item], qb = items[2 * item + 1];
@@ -595,7 +606,7 @@ __global__ __launch_bounds__(256) void attn_fused_mw_kernel(const uint16_t *__re
       if (KCH % 256 == 0 || c < KCH)
         *reinterpret_cast<uint4 *>(sK + key * DP + (swz(key, ch) << 3)) = kr[i];
     }
-    if (tid < VTH) store_vt<DP, 256>(sV, vt, k0, hr.ntot, tid);
+    if (tid < VTH) store_vt<DP, kVPF, 256>(sV, vt, k0, hr.ntot, tid);
     if (k0 + 32 < kend_blk) load_tile(k0 + 32);
     __syncthreads();
     if (active && k0 < kend) {
@@ -631,8 +642,8 @@ __global__ __launch_bounds__(256) void attn_fused_pfx_kernel(const uint16_t *__r
   constexpr int KS = DP / 16, CPR = DP / 8, RPL = DP * 2 >= 256 ? 1 : 256 / (DP * 2);
   constexpr int KCH = 32 * CPR, KPT = (KCH + 255) / 256;
   __shared__ __attribute__((aligned(16))) uint16_t sK[32 * DP];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[DP * kVP];
-  __shared__ __attribute__((aligned(16))) uint16_t sVw[4][DP * kVP];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[DP * kVPF];
+  __shared__ __attribute__((aligned(16))) uint16_t sVw[4][DP * kVPF];
   const int item = blockIdx.x, h = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int seq = items[8 * item + 2 * wave], q0 = items[8 * item + 2 * wave + 1];
@@ -671,7 +682,7 @@ __global__ __launch_bounds__(256) void attn_fused_pfx_kernel(const uint16_t *__r
       if (KCH % 256 == 0 || c < KCH)
         *reinterpret_cast<uint4 *>(sK + key * DP + (swz(key, ch) << 3)) = kr[i];
     }
-    if (tid < VTH) store_vt<DP, 256>(sV, vt, k0, hr.ntot, tid);
+    if (tid < VTH) store_vt<DP, kVPF, 256>(sV, vt, k0, hr.ntot, tid);
     if (k0 + 32 < kp) load_tile(k0 + 32);
     __syncthreads();
     if (active) {
@@ -701,7 +712,7 @@ __global__ __launch_bounds__(256) void attn_fused_pfx_kernel(const uint16_t *__r
     // previous tile's reads of it before these writes and these writes
     // before this tile's reads (lanes exchange keys through it)
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    store_vt<DP>(myV, vt, k0, hr.ntot, lane);
+    store_vt<DP, kVPF>(myV, vt, k0, hr.ntot, lane);
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
     qt.update(s, k0, hr.ntot, hr.np, causal != 0, sl2);
     qt.pv(s, myV);
