@@ -34,11 +34,14 @@ constexpr int kPfxMinPrompt = 64;
 // probabilities with one 16-byte bf16 store.  Bidirectional rows all have the
 // sequence's length n, so one G serves all A * n rows of a sequence's block
 // ([head][query] major) and items run across heads.  Causal row q has q + 1
-// scores: rows are grouped by lane count -- q < 64 on 8 lanes, then 16, 32,
-// and 64 lanes from q = 256 on -- so a lane group is at least half used,
-// and an item never crosses a head or a lane-count boundary.  An item is up
-// to kSoftmaxPasses (causal: kSoftmaxPassesCausal) passes of 4 wavefronts x
-// (64 / G) rows.
+// scores: rows are grouped by lane count -- q < 64 on 8 lanes, then 16, 32
+// and 64 lanes up to 512 scores -- so a lane group is at least half used, and
+// an item never crosses a head or a lane-count boundary.  Causal rows of 513
+// to 1024 scores take 32 lanes and three or four chunks each (70 % of the
+// lanes' slots used at 540 scores, against 53 % for 64 lanes and two
+// chunks, and two rows per wavefront instead of one); longer causal rows
+// 64 lanes again.  An item is up to kSoftmaxPasses (causal:
+// kSoftmaxPassesCausal) passes of 4 wavefronts x (64 / G) rows.
 constexpr int kSoftmaxPasses = 2;
 constexpr int kSoftmaxPassesCausal = 8;
 ES_HD inline int softmax_lanes(int m) {
@@ -48,8 +51,21 @@ ES_HD inline int softmax_lanes(int m) {
   return g;
 }
 ES_HD inline int softmax_row_lanes(int m, bool causal) {
+  if (causal && m > 512 && m <= 1024) return 32;
   const int g = softmax_lanes(m);
   return causal && g < 8 ? 8 : g;
+}
+// The causal lane-count class of row q of a sequence of n: rows [cs, ce)
+// all take softmax_row_lanes(q + 1) lanes.
+ES_HD inline void softmax_causal_class(int q, int n, int &cs, int &ce) {
+  const int m = q + 1;
+  if (m <= 64) cs = 0, ce = 64;
+  else if (m <= 128) cs = 64, ce = 128;
+  else if (m <= 256) cs = 128, ce = 256;
+  else if (m <= 512) cs = 256, ce = 512;
+  else if (m <= 1024) cs = 512, ce = 1024;
+  else cs = 1024, ce = n;
+  if (ce > n) ce = n;
 }
 ES_HD inline int softmax_rows_per_item(int g, bool causal) {
   return 4 * (64 / g) * (causal ? kSoftmaxPassesCausal : kSoftmaxPasses);
@@ -79,9 +95,8 @@ ES_HD inline SoftmaxItem softmax_item(int r0, int n, int n_heads, bool causal) {
   const int h0 = r0 / n, q0 = r0 % n;
   const int g = softmax_row_lanes(q0 + 1, true);
   const int rpi = softmax_rows_per_item(g, true);
-  const int cs = g <= 8 ? 0 : 4 * g;                  // class of rows needing g lanes
-  int ce = g >= 64 ? n : 8 * g;
-  if (ce > n) ce = n;
+  int cs, ce;                                         // class of rows needing g lanes
+  softmax_causal_class(q0, n, cs, ce);
   it.g = g;
   it.h0 = h0;
   if (q0 == cs && ce - cs < rpi) {                    // whole class, several heads
@@ -113,8 +128,8 @@ inline void softmax_items(int n, int n_heads, bool causal, F emit) {
     return;
   }
   for (int cs = 0; cs < n;) {  // lane-count classes in order, heads inside
-    const int g = softmax_row_lanes(cs + 1, true);
-    const int ce = g >= 64 || 8 * g > n ? n : 8 * g;
+    int c0, ce;
+    softmax_causal_class(cs, n, c0, ce);  // c0 == cs
     for (int h0 = 0; h0 < n_heads;) {
       int q = cs, hc = 1;
       while (q < ce) {

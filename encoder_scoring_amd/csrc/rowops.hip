@@ -6,6 +6,8 @@
 // 64-lane wavefront: coalesced 16-byte loads straight into registers, one
 // pass over HBM in and out, reductions by butterfly shuffles inside the
 // wavefront, no barriers.
+#include <algorithm>
+
 #include "device.h"
 #include "kernels.h"
 
@@ -498,9 +500,12 @@ hipError_t launch_softmax(bool p_bf16, const float *S, void *P, const Ragged &r,
   if (e != hipSuccess) return e;
   const int first = r.n_sm_narrow, count = r.n_sm_items - r.n_sm_narrow;
   const int nc = (r.max_len + 7) / 8;  // eight-score chunks of the longest row
-  const int nj = (nc + 63) / 64;
+  // chunks per lane: rows of 64 lanes; causal rows of up to 1024 scores 32
+  int nj = (nc + 63) / 64;
+  if (causal) nj = std::max(nj, (std::min(nc, 128) + 31) / 32);
   if (count <= 0) return hipSuccess;
   if (nj <= 2) return go(std::integral_constant<int, 2>{}, first, count);
+  if (nj <= 3) return go(std::integral_constant<int, 3>{}, first, count);
   if (nj <= 4) return go(std::integral_constant<int, 4>{}, first, count);
   if (nj <= 8) return go(std::integral_constant<int, 8>{}, first, count);
   return hipErrorInvalidValue;
