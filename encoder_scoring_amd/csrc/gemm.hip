@@ -1038,7 +1038,7 @@ hipError_t go_lat(const uint16_t *A, int lda, const uint16_t *W, const float *bi
 //          128 x 64 blocks would leave most CUs idle (380 x 768 x 3072:
 //          27.2 -> 20.4 us)
 //   5  S2  256 x 256 software-pipelined, 8 waves (128 x 64 each), one block
-//          per CU, A triple-buffered (all 160 KiB of LDS) for N < 2048, double
+//          per CU, A triple-buffered (all 160 KiB of LDS) for N < 4096, double
 //          buffered for wider products; it runs wherever the cost model below
 //          picks a wide block (2 or 3)
 //   6  L   32 x 32 per wavefront, one wavefront per block, operands straight
@@ -1149,11 +1149,14 @@ hipError_t launch_gemm_bf16_tile(int tile, const uint16_t *A, int lda, const uin
       return go_pp<P3, 1>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
     case 4: return go_bf16<T0>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
     case 5:
-      // A triple-buffered only for narrow N, whose few column tiles share each
-      // A panel little, so A streams from HBM (BERT-base FFN2 at ~80 k rows:
-      // 857 -> 946 TFLOP/s); the wide decoder products run 2-9 % faster with
-      // two A buffers (QKV at 80 k rows: 2.49e7 -> 2.28e7 busy cycles)
-      if (N >= 2048) return go_sp<S2w>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
+      // two A buffers for the wide decoder products (N = 6144, 8192: QKV and
+      // FFN1 inside the layer sequence 286 -> 277 and 415 -> 409 ms per step
+      // on the decoder stream; QKV alone at 80 k rows 2.49e7 -> 2.28e7 busy
+      // cycles); three for N <= 3072 (with two, the decoder's attention-out
+      // and FFN2 took 104 -> 112 and 328 -> 348 ms per step and BERT-base's
+      // QKV on the long-tail stream 24.5 -> 25.4 ms; BERT-base FFN2 at ~80 k
+      // rows 857 -> 946 TFLOP/s with three)
+      if (N >= 4096) return go_sp<S2w>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
       return go_sp<S2>(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
     case 6: return go_lat(A, lda, W, bias, res, out, ldc, M, N, K, epi, st);
     default: return hipErrorInvalidValue;

@@ -6,6 +6,7 @@ kept under profiles/.
     python prof_summary.py traffic --fetch CSV --write CSV --probe-fetch CSV --probe-write CSV
                                    --probe-mib MIB --kernel-class CLASS --command CMD...
     python prof_summary.py calls TRACE_CSV --bench-json JSON --command CMD [--title T]
+    python prof_summary.py rowbench --json JSON --dir DIR --workload W --launches N --probe-mib MIB
 
 `kernels` reads `<prefix>_kernel_stats.csv` (rocprofv3 --kernel-trace --stats)
 and prints the per-kernel table plus, for every GEMM class, the calls-weighted
@@ -17,6 +18,12 @@ pass size, so a class can span several kernels).
 each embedding kernel: per shape (200 timed calls after 10 warm-up calls,
 shapes in bench.py's order) the kernels per call, the median summed kernel
 time and the median per-kernel time, next to the plain run's wall clock.
+
+`rowbench` combines rowbench.py's JSON line (event-timed launches, warm and
+cold) with four --pmc runs of rowbench.py (FETCH_SIZE / WRITE_SIZE, --mode
+warm / cold, directories DIR/pmc_rb_<workload>_<mode>_<counter>) and the
+copy calibration (DIR/pmc_probe_<counter>): counter bytes per launch and the
+bandwidth they give over the event-timed launch.
 
 `traffic` reads the `counter_collection.csv` files of two --pmc runs of the
 same command (FETCH_SIZE, then WRITE_SIZE) and of two runs over hbm_probe.py
@@ -150,6 +157,39 @@ def calls(a):
             print(f"  {k[:64]:64s} {n:3.0f} per call  {statistics.median(v):8.2f} us per call")
 
 
+def rowbench(a):
+    import json
+    rb = json.loads([l for l in open(a.json) if l.startswith("{")][-1])
+    cal = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        n, kib = counter_kib(os.path.join(a.dir, f"pmc_probe_{c}", "p_counter_collection.csv"), r"copyBuffer")
+        cal[c] = a.probe_mib * 1024.0 / (kib / n)
+    ps = rb["pass"]
+    print(f"# Softmax and LayerNorm on one pass of {a.workload} ({ps['sequences']} sequences, {ps['tokens']} tokens, "
+          f"{ps['heads']} heads, {'causal' if ps['causal'] else 'bidirectional'}), warm and cold cache")
+    print("# commands (after `cd /tmp && export TMPDIR=/tmp`, from the repository root):")
+    print(f"#   python3 rowbench.py --workload {a.workload}")
+    print(f"#   rocprofv3 --pmc {{FETCH_SIZE|WRITE_SIZE}} --output-format csv -d <dir> -o p -- python3 rowbench.py "
+          f"--workload {a.workload} --mode {{warm|cold}} --reps 10")
+    print("#   rocprofv3 --pmc {FETCH_SIZE|WRITE_SIZE} --output-format csv -d <dir> -o p -- python3 hbm_probe.py 256 5")
+    print(f"# cold: {rb['flush_mib_between_cold_launches']} MiB device copy between launches (the MALL holds 256 MB);"
+          f" counter scale from the copy: FETCH_SIZE x {cal['FETCH_SIZE']:.4f}, WRITE_SIZE x {cal['WRITE_SIZE']:.4f}")
+    print("# columns: kernel, mode, event-timed launch (us), algorithmic GB/s, counter bytes per launch (MB), counter GB/s")
+    pats = {"softmax": CLASS_PATTERNS["softmax"], "layernorm": CLASS_PATTERNS["layernorm"]}
+    for k in ("softmax", "layernorm"):
+        alg = rb[k]["algorithmic_bytes_per_launch"]
+        print(f"{k}: {rb[k]['form']}; algorithmic {alg / 1e6:.1f} MB per launch")
+        for mode in ("warm", "cold"):
+            tot = 0.0
+            for c in ("FETCH_SIZE", "WRITE_SIZE"):
+                _, kib = counter_kib(os.path.join(a.dir, f"pmc_rb_{a.workload}_{mode}_{c}", "p_counter_collection.csv"),
+                                     pats[k])
+                tot += kib * 1024.0 * cal[c] / a.launches
+            ms = rb[k][mode]["ms_median"]
+            print(f"  {k:9s} {mode}: {ms * 1e3:8.1f} us  {alg / ms / 1e6:7.1f} GB/s algorithmic  "
+                  f"{tot / 1e6:8.1f} MB  {tot / ms / 1e6:7.1f} GB/s by counters")
+
+
 def counter_kib(path, pattern):
     """(dispatches, summed counter value) of the kernels whose name matches."""
     disp = set()
@@ -214,6 +254,12 @@ def main():
     c.add_argument("--bench-json", required=True, help="stdout of the plain bench.py run")
     c.add_argument("--command", required=True)
     c.add_argument("--title", default="")
+    r = sub.add_parser("rowbench")
+    r.add_argument("--json", required=True)
+    r.add_argument("--dir", required=True)
+    r.add_argument("--workload", required=True)
+    r.add_argument("--launches", type=int, required=True, help="launches per kernel in each --pmc run")
+    r.add_argument("--probe-mib", type=float, required=True)
     t = sub.add_parser("traffic")
     for f in ("fetch", "write", "probe_fetch", "probe_write"):
         t.add_argument("--" + f.replace("_", "-"), dest=f, required=True)
@@ -225,7 +271,7 @@ def main():
                    help="kernel dispatches that make one launch of the class (the softmax "
                         "runs rows of up to 512 scores and longer rows as two dispatches)")
     a = ap.parse_args()
-    {"kernels": kernels, "traffic": traffic, "calls": calls}[a.mode](a)
+    {"kernels": kernels, "traffic": traffic, "calls": calls, "rowbench": rowbench}[a.mode](a)
 
 
 if __name__ == "__main__":
