@@ -31,7 +31,7 @@ EXPORTS = [
 ]
 
 KERNEL_CLASSES = ["embed", "qkv_gemm", "scores", "softmax", "pv", "oproj_gemm", "layernorm",
-                  "ffn1_gemm", "ffn2_gemm", "head", "attn_fused", "gather"]
+                  "ffn1_gemm", "ffn2_gemm", "head", "attn_fused", "gather", "refine"]
 
 
 class EncScoreError(RuntimeError):

@@ -720,6 +720,122 @@ __global__ __launch_bounds__(256) void attn_fused_pfx_kernel(const uint16_t *__r
   qt.store(ctx, ldc, hr.t0, hr.n, h);
 }
 
+// Last-token attention in fp32, for the refinement of the reward rows: the
+// query, and the key and value of the last token itself, come from the fp32
+// row of that token (ql: row i = sequence i, Q | K | V at the bulk layout's
+// columns, pitch ldl); every other key / value is the bulk layer's bf16 row
+// (shared prompt rows first, as in the fused kernels).  The last query sees
+// every key of its sequence under either mask.  One block of four wavefronts
+// per (sequence, head).  A key's DP dims are split over DP / 8 neighbouring
+// lanes, 16 bytes each, so a wavefront instruction reads whole rows (one
+// 256-byte row per 16 lanes at DP = 128) and the block takes 256 / (DP / 8)
+// keys at once; a key's dot product is 8 fmas per lane and a butterfly over
+// its lanes.  Max and sum reduce over the block; P . V runs on the same
+// lane split, each key slot accumulating its keys in ascending order, and
+// the slots are summed in fixed order through LDS, so the result is
+// reproducible.  Writes ctx[i, h dp .. h dp + dp) (fp32, pitch ldc); the
+// head of index 0 also zeroes columns [n_heads dp, kc), the band a wider
+// GEMM K reads.
+constexpr int kLastMaxKeys = kLastMaxKeysHost;
+constexpr int kLastThreads = 256;
+
+template <int DP>
+__global__ __launch_bounds__(kLastThreads) void attn_last_kernel(
+    const uint16_t *__restrict__ qkv, int ldq, const float *__restrict__ ql, int ldl, int n_heads,
+    float scale, const int32_t *__restrict__ off, const int32_t *__restrict__ pref,
+    const int32_t *__restrict__ plen, float *__restrict__ ctx, int ldc, int kc) {
+  constexpr int CH = DP / 8, G = kLastThreads / CH, NW = kLastThreads / kWave;
+  static_assert(CH <= kWave && kWave % CH == 0, "a key's lanes lie in one wavefront");
+  __shared__ float sp[kLastMaxKeys];
+  __shared__ __align__(16) float red[G * DP];
+  __shared__ float wred[2 * NW];
+  const int seq = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+  const int c = t % CH, g = t / CH, lane = t % kWave, wv = t / kWave;
+  const int t0 = off[seq], n = off[seq + 1] - off[seq];
+  const int np = plen ? plen[seq] : 0, p0 = pref ? pref[seq] : 0;
+  const int L = np + n;  // keys of the last query, its own last
+  const int kq = h * DP + 8 * c, kk = n_heads * DP + h * DP + 8 * c, kv = 2 * n_heads * DP + h * DP + 8 * c;
+  const float *qrow = ql + (int64_t)seq * ldl;
+  float q[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) q[e] = qrow[kq + e];
+  auto row = [&](int j) { return qkv + (int64_t)(j < np ? p0 + j : t0 + j - np) * ldq; };
+  auto unpack = [](const uint4 &u, float (&v)[8]) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] = bf2f(w[e] & 0xffffu);
+      v[2 * e + 1] = bf2f(w[e] >> 16);
+    }
+  };
+  float mx = -INFINITY;
+#pragma unroll 4
+  for (int j = g; j < L; j += G) {
+    float k[8];
+    if (j == L - 1) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) k[e] = qrow[kk + e];
+    } else {
+      unpack(*reinterpret_cast<const uint4 *>(row(j) + kk), k);
+    }
+    float dot = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dot = fmaf(q[e], k[e], dot);
+#pragma unroll
+    for (int o = CH / 2; o > 0; o >>= 1) dot += __shfl_xor(dot, o, kWave);
+    const float sc = dot * scale;
+    if (c == 0) sp[j] = sc;
+    mx = fmaxf(mx, sc);
+  }
+  mx = wave_max(mx);
+  if (lane == 0) wred[wv] = mx;
+  __syncthreads();  // scores and per-wavefront maxima in LDS
+  mx = wred[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) mx = fmaxf(mx, wred[w]);
+  float sum = 0.f;
+  for (int j = t; j < L; j += kLastThreads) {
+    const float pj = expf(sp[j] - mx);
+    sp[j] = pj;
+    sum += pj;
+  }
+  sum = wave_sum(sum);
+  if (lane == 0) wred[NW + wv] = sum;
+  __syncthreads();  // probabilities and per-wavefront sums in LDS
+  sum = wred[NW];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) sum += wred[NW + w];
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll 4
+  for (int j = g; j < L; j += G) {
+    float v[8];
+    if (j == L - 1) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = qrow[kv + e];
+    } else {
+      unpack(*reinterpret_cast<const uint4 *>(row(j) + kv), v);
+    }
+    const float pj = sp[j];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = fmaf(pj, v[e], acc[e]);
+  }
+  // red[g][8 c + e]: thread t's 8 values at 8 t
+  *reinterpret_cast<float4 *>(red + 8 * t) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  *reinterpret_cast<float4 *>(red + 8 * t + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  __syncthreads();
+  float *crow = ctx + (int64_t)seq * ldc;
+  const float inv = 1.0f / sum;
+  for (int e = t; e < DP; e += kLastThreads) {
+    float a = red[e];
+    for (int s2 = 1; s2 < G; ++s2) a += red[s2 * DP + e];
+    crow[h * DP + e] = a * inv;
+  }
+  if (h == 0)
+    for (int col = n_heads * DP + t; col < kc; col += kLastThreads) crow[col] = 0.f;
+}
+
 template <typename F>
 hipError_t dispatch_dp(int dp, F &&f) {
   switch (dp) {
@@ -801,6 +917,22 @@ hipError_t launch_attn_fused(const uint16_t *qkv, int ldq, int n_heads, int dp, 
         attn_fused_mw_kernel<DP, false><<<grid, dim3(256), 0, st>>>(qkv, ldq, n_heads, scale, c, r.off,
                                                                     r.mw_items, nullptr, nullptr, ctx, ldc);
     }
+    return hipGetLastError();
+  });
+}
+
+hipError_t launch_attn_last(const uint16_t *qkv, int ldq, const float *ql, int ldl, int n_heads,
+                            int dp, float scale, const Ragged &r, float *ctx, int ldc, int kc,
+                            hipStream_t st) {
+  if (r.n_seqs <= 0) return hipSuccess;
+  if ((r.plen != nullptr) != (r.pref != nullptr) || r.max_len <= 0 || kc < n_heads * dp || ldc < kc ||
+      ldl < 3 * n_heads * dp)
+    return hipErrorInvalidValue;
+  return dispatch_dp(dp, [&](auto dpc) {
+    constexpr int DP = decltype(dpc)::value;
+    attn_last_kernel<DP><<<dim3(r.n_seqs, n_heads), dim3(kLastThreads), 0, st>>>(qkv, ldq, ql, ldl, n_heads, scale,
+                                                                      r.off, r.pref, r.plen, ctx, ldc,
+                                                                      kc);
     return hipGetLastError();
   });
 }

@@ -785,6 +785,121 @@ __global__ __launch_bounds__(512, 1) void gemm_sp_kernel(
                           n0, bias, res, out, ldc, M, N);
 }
 
+// ------------------------------------------------------ split-precision tile
+// out = epi(A W^T + bias) for fp32 activations A against the bf16 weights, on
+// bf16 MFMA with fp32 accumulation: each A element enters as the pair hi =
+// bf16(a), lo = bf16(a - hi), two MFMAs per k-step into one accumulator, so
+// the operand keeps 16 significant bits (|a - hi - lo| <= 2^-18 |a|) instead
+// of bf16's 8.  It serves the last-token refinement of the reward rows: one
+// row per sequence, fp32 throughout, so those rows carry none of the bulk
+// path's bf16 activation rounding.  Few rows, so the weights dominate the
+// bytes: one block of KW wavefronts per 32 output columns and MT 32-row
+// tiles, each W fragment loaded once and used for all MT row tiles;
+// wavefront w takes the w-th of KW equal k-ranges, operands loaded straight
+// into registers D k-steps ahead (the latency tile's fragment layout), and
+// the KW partial tiles are summed in wavefront order through LDS.  Rows past
+// M (A) or N (W) are read at the last row and never stored.  Epilogues (fp32
+// out): kEpiF32 acc + bias, kEpiResidual acc + bias + res[m, n] (res may be
+// out), kEpiGelu GELU(acc + bias) with the device erff.
+template <int EPI, int MT, int D>
+__global__ __launch_bounds__(256) void gemm_split_kernel(const float *__restrict__ A, int lda,
+                                                         const uint16_t *__restrict__ W,
+                                                         const float *__restrict__ bias,
+                                                         const float *res, float *out, int ldc, int M,
+                                                         int N, int K, int tiles_n) {
+  __shared__ __align__(16) float part[3][MT][16][64];
+  const int lane = threadIdx.x % 64, wv = threadIdx.x / 64, kw = blockDim.x / 64;
+  const int fr = lane & 31, fh = lane >> 5;
+  const int ch = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+  const int64_t m0 = (int64_t)ch * MT * 32;
+  const int n0 = tn * 32;
+  const int nk = K / 16 / kw, kb = wv * nk;  // this wavefront's k-steps [kb, kb + nk)
+  const float *ap[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) ap[t] = A + min(m0 + 32 * t + fr, (int64_t)M - 1) * lda + 8 * fh + 16 * kb;
+  const uint16_t *wp = W + (int64_t)min(n0 + fr, N - 1) * K + 8 * fh + 16 * kb;
+  static_assert(D % 4 == 0, "the tail runs in groups of 4 k-steps");
+  float4 fa[D][MT][2];
+  bf16x8 fb[D];
+  auto load = [&](int d, int k) {
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      fa[d][t][0] = *reinterpret_cast<const float4 *>(ap[t] + 16 * k);
+      fa[d][t][1] = *reinterpret_cast<const float4 *>(ap[t] + 16 * k + 4);
+    }
+    fb[d] = *reinterpret_cast<const bf16x8 *>(wp + 16 * k);
+  };
+#pragma unroll
+  for (int d = 0; d < D; ++d) load(d, min(d, nk - 1));
+  f32x16 acc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
+  auto mma = [&](int d) {
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const float4 *a = fa[d][t];
+      const float v[8] = {a[0].x, a[0].y, a[0].z, a[0].w, a[1].x, a[1].y, a[1].z, a[1].w};
+      bf16x8 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        hi[e] = (__bf16)v[e];
+        lo[e] = (__bf16)(v[e] - (float)hi[e]);
+      }
+      acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[d], hi, acc[t], 0, 0, 0);
+      acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[d], lo, acc[t], 0, 0, 0);
+    }
+  };
+  int k = 0;
+  for (; k + D <= nk; k += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      mma(d);
+      load(d, min(k + d + D, nk - 1));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < D; d += 4) {
+    if (k + d < nk) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mma(d + e);
+    }
+  }
+  if (wv > 0) {
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) part[wv - 1][t][r][lane] = acc[t][r];
+  }
+  __syncthreads();
+  if (wv > 0) return;
+  for (int w = 1; w < kw; ++w) {
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[t][r] += part[w - 1][t][r][lane];
+  }
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int64_t m = m0 + 32 * t + fr;
+    if (m >= M) break;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int n = n0 + 8 * g + 4 * fh;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (n + e >= N) break;
+        float x = acc[t][4 * g + e] + bias[n + e];
+        if (EPI == kEpiResidual) x += res[m * ldc + n + e];
+        if (EPI == kEpiGelu) x = gelu_erf(x);
+        out[m * ldc + n + e] = x;
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------ latency tile
 // One wavefront per 32 x 32 output tile, operands loaded from global memory
 // straight into the MFMA's registers, D k-steps of 16 ahead: no LDS and no
@@ -1170,6 +1285,36 @@ hipError_t launch_gemm_bf16(const uint16_t *A, int lda, const uint16_t *W, const
                             hipStream_t st) {
   return launch_gemm_bf16_tile(gemm_tile_index(M, N, K, epi), A, lda, W, bias, res, out, ldc, M, N,
                                K, epi, st);
+}
+
+hipError_t launch_gemm_split(const float *A, int lda, const uint16_t *W, const float *bias,
+                             const float *res, float *out, int ldc, int M, int N, int K, int epi,
+                             hipStream_t st) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (K <= 0 || K % 64 || lda < K || lda % 4) return hipErrorInvalidValue;
+  if (epi != kEpiF32 && epi != kEpiResidual && epi != kEpiGelu) return hipErrorInvalidValue;
+  // up to 4 row tiles per block, as even as the row count allows
+  const int mtiles = (M + 31) / 32, chunks = (mtiles + 3) / 4, mt = (mtiles + chunks - 1) / chunks;
+  const int tn = (N + 31) / 32;
+  // k-ranges of a multiple of 4 k-steps each
+  const int kw = K % 256 == 0 ? 4 : K % 128 == 0 ? 2 : 1;
+  const dim3 grid((unsigned)chunks * tn), block(64 * kw);
+  auto go = [&](auto mtc) {
+    constexpr int MT = decltype(mtc)::value, D = MT <= 2 ? 8 : 4;
+    if (epi == kEpiF32)
+      gemm_split_kernel<kEpiF32, MT, D><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K, tn);
+    else if (epi == kEpiResidual)
+      gemm_split_kernel<kEpiResidual, MT, D><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K, tn);
+    else
+      gemm_split_kernel<kEpiGelu, MT, D><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K, tn);
+    return hipGetLastError();
+  };
+  switch (mt) {
+    case 1: return go(std::integral_constant<int, 1>{});
+    case 2: return go(std::integral_constant<int, 2>{});
+    case 3: return go(std::integral_constant<int, 3>{});
+    default: return go(std::integral_constant<int, 4>{});
+  }
 }
 
 hipError_t launch_gemm_f32(const float *A, int lda, const float *W, const float *bias,

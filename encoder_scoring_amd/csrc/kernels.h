@@ -90,6 +90,14 @@ constexpr int kGemmTiles = 7;
 hipError_t launch_gemm_bf16_tile(int tile, const uint16_t *A, int lda, const uint16_t *W,
                                  const float *bias, const float *res, void *out, int ldc, int M,
                                  int N, int K, int epi, hipStream_t st);
+// out (fp32) = epi(A W^T + bias) with fp32 activations A [M, lda >= K] and the
+// bf16 weights, each A element entering bf16 MFMA as a hi + lo bf16 pair
+// (16 significant bits), fp32 accumulation; epi kEpiF32, kEpiResidual (res
+// fp32 [M, ldc], may be out) or kEpiGelu (fp32 output).  Rows of A past M are
+// not read.  For the last-token refinement of the reward rows.
+hipError_t launch_gemm_split(const float *A, int lda, const uint16_t *W, const float *bias,
+                             const float *res, float *out, int ldc, int M, int N, int K, int epi,
+                             hipStream_t st);
 hipError_t launch_gemm_f32(const float *A, int lda, const float *W, const float *bias,
                            const float *res, float *out, int ldc, int M, int N, int K, int epi,
                            hipStream_t st);
@@ -104,5 +112,15 @@ hipError_t launch_pv(bool act_bf16, const void *P, const void *qkv, int ldq, int
 // score rows never leave registers.
 hipError_t launch_attn_fused(const uint16_t *qkv, int ldq, int n_heads, int dp, float scale,
                              bool causal, const Ragged &r, uint16_t *ctx, int ldc, hipStream_t st);
+// Last-token refinement: for each sequence i of r, the attention of its last
+// query in fp32 -- query and last key / value from row i of ql (fp32, pitch
+// ldl, the bulk layout's Q | K | V columns), the other keys and values from
+// the bulk bf16 qkv rows (shared-prompt rows first) -- into ctx row i (fp32,
+// pitch ldc); columns [n_heads dp, kc) zeroed.  Every sequence (prompt
+// included) at most kLastMaxKeys positions.
+constexpr int kLastMaxKeysHost = 4096;
+hipError_t launch_attn_last(const uint16_t *qkv, int ldq, const float *ql, int ldl, int n_heads,
+                            int dp, float scale, const Ragged &r, float *ctx, int ldc, int kc,
+                            hipStream_t st);
 
 }  // namespace es

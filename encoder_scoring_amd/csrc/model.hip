@@ -75,6 +75,8 @@ struct es_model {
   // capacity
   int64_t max_tokens = 0, Tcap = 0, score_cap = 0;
   int attn_mode = 0;  // 0: scores -> softmax -> P.V, 1: fused (the bf16 default, set in build)
+  // last-token refinement of the reward rows (pre-LN bf16 models, set in build)
+  bool refine = false;
   int max_seqs = 0;
   int device = 0;
   // weights
@@ -86,6 +88,7 @@ struct es_model {
     int scale = 0;  // fixed buffers: capacity in planned batches (tokens, sequences, score elements)
     float *x = nullptr, *y = nullptr, *S = nullptr;
     void *xb = nullptr, *qkv = nullptr, *ctx = nullptr, *hmid = nullptr, *Pb = nullptr;
+    float *ref = nullptr;  // last-token refinement rows (refine_floats per sequence)
     hipStream_t stream = nullptr;  // internal stream used when several batches are in flight
     hipEvent_t done = nullptr;
     // length-aware memory: one arena; the tensors above point into it per pass
@@ -234,6 +237,12 @@ double ms_since(const std::chrono::steady_clock::time_point &t0) {
   return std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
 }
 
+// fp32 values per sequence of the last-token refinement: its residual row,
+// LayerNorm output, Q | K | V row, context row and FFN middle row.
+int64_t refine_floats(const es_model *m) {
+  return m->refine ? (int64_t)2 * m->H + m->Nqkv + m->Kc + m->Fp : 0;
+}
+
 // Device bytes of all workspaces (fixed buffers or arenas).
 int64_t work_bytes(const es_model *m) {
   int64_t b = 0;
@@ -242,7 +251,8 @@ int64_t work_bytes(const es_model *m) {
     if (w.scale > 0) {
       const int act = m->bf16 ? 2 : 4;
       const int64_t T = round_up(w.scale * m->max_tokens, 256), S = w.scale * m->score_cap;
-      b += T * (m->H * 8 + (int64_t)(m->Hp + m->Nqkv + m->Kc + m->Fp) * act) + S * (4 + act);
+      b += T * (m->H * 8 + (int64_t)(m->Hp + m->Nqkv + m->Kc + m->Fp) * act) + S * (4 + act) +
+           (int64_t)w.scale * m->max_seqs * refine_floats(m) * 4;
     }
   }
   return b;
@@ -250,8 +260,9 @@ int64_t work_bytes(const es_model *m) {
 
 void free_fixed(es_model *m, es_model::Workspace &w) {
   if (w.arena) return;  // the tensor pointers are views into the arena
-  for (void *p : {(void *)w.x, (void *)w.y, (void *)w.S, w.xb, w.qkv, w.ctx, w.hmid, w.Pb}) dfree(m, p);
-  w.x = w.y = w.S = nullptr;
+  for (void *p : {(void *)w.x, (void *)w.y, (void *)w.S, w.xb, w.qkv, w.ctx, w.hmid, w.Pb, (void *)w.ref})
+    dfree(m, p);
+  w.x = w.y = w.S = w.ref = nullptr;
   w.xb = w.qkv = w.ctx = w.hmid = w.Pb = nullptr;
   w.scale = 0;
 }
@@ -261,7 +272,7 @@ void free_arena(es_model *m, es_model::Workspace &w) {
   dfree(m, w.arena);
   w.arena = nullptr;
   w.arena_cap = 0;
-  w.x = w.y = w.S = nullptr;
+  w.x = w.y = w.S = w.ref = nullptr;
   w.xb = w.qkv = w.ctx = w.hmid = w.Pb = nullptr;
 }
 
@@ -284,8 +295,11 @@ es_status alloc_workspace(es_model *m, es_model::Workspace &w, int scale) {
   if ((s = dalloc(m, &w.hmid, T * m->Fp * act)) != ES_OK) return s;
   if ((s = dalloc(m, (void **)&w.S, S * 4)) != ES_OK) return s;
   if ((s = dalloc(m, &w.Pb, S * act)) != ES_OK) return s;
+  if (m->refine &&
+      (s = dalloc(m, (void **)&w.ref, (int64_t)scale * m->max_seqs * refine_floats(m) * 4)) != ES_OK)
+    return s;
   w.scale = scale;
-  m->work_allocs += 8;
+  m->work_allocs += m->refine ? 9 : 8;
   m->work_alloc_ms += ms_since(t0);
   m->peak_work = std::max(m->peak_work, work_bytes(m));
   return ES_OK;
@@ -303,11 +317,12 @@ es_status alloc_workspace(es_model *m, es_model::Workspace &w, int scale) {
 // columns of the K-padded GEMM inputs are written with zeros by their
 // producers every time (LayerNorm / embedding: xb past H; FFN1 computes its
 // zero padding columns past F; attention clears ctx past A dp).
-enum { kTX, kTXb, kTQkv, kTCtx, kTY, kTHmid, kTS, kTP, kTensors };
+enum { kTX, kTXb, kTQkv, kTCtx, kTY, kTHmid, kTS, kTP, kTRef, kTensors };
 constexpr int64_t kArenaAlign = 4096;
 constexpr int64_t kArenaChunk = (int64_t)16 << 20;
 
-std::vector<es::Usage> pass_usage(const es_model *m, int64_t rows, int64_t score_elems) {
+std::vector<es::Usage> pass_usage(const es_model *m, int64_t rows, int64_t score_elems,
+                                  int64_t n_seqs) {
   const int64_t act = m->bf16 ? 2 : 4;
   std::vector<es::Usage> u(kTensors);
   u[kTX] = {rows * m->H * 4, 0, 10};
@@ -318,6 +333,7 @@ std::vector<es::Usage> pass_usage(const es_model *m, int64_t rows, int64_t score
   u[kTHmid] = {rows * m->Fp * act, 7, 8};
   u[kTS] = {score_elems * 4, 3, 3};
   u[kTP] = {score_elems * act, 3, 3};
+  u[kTRef] = {n_seqs * refine_floats(m) * 4, 0, 10};  // the pass's refinement rows
   return u;
 }
 
@@ -329,11 +345,11 @@ std::vector<es::Usage> pass_usage(const es_model *m, int64_t rows, int64_t score
 // steps) when it holds at least twice that.  Exact: a fresh arena of exactly
 // this pass's need.
 es_status bind_workspace(es_model *m, es_model::Workspace &w, int64_t n_tokens, int64_t score_elems,
-                         hipStream_t st) {
+                         int64_t n_seqs, hipStream_t st) {
   if (m->mem_mode == ES_MEM_FIXED) return ES_OK;
   const int64_t rows = std::max<int64_t>(round_up(n_tokens, 256), 256);
   std::vector<int64_t> off;
-  const int64_t need = es::plan_arena(pass_usage(m, rows, score_elems), kArenaAlign, off);
+  const int64_t need = es::plan_arena(pass_usage(m, rows, score_elems, n_seqs), kArenaAlign, off);
   w.call_need = std::max(w.call_need, need);
   int64_t want = 0;
   if (m->mem_mode == ES_MEM_EXACT)
@@ -368,6 +384,7 @@ es_status bind_workspace(es_model *m, es_model::Workspace &w, int64_t n_tokens, 
   w.hmid = a + off[kTHmid];
   w.S = reinterpret_cast<float *>(a + off[kTS]);
   w.Pb = a + off[kTP];
+  w.ref = reinterpret_cast<float *>(a + off[kTRef]);
   return ES_OK;
 }
 
@@ -418,6 +435,8 @@ es_status build(const es::ParsedBlob &pb, int64_t max_tokens, int32_t max_seqs, 
   m->causal = h.causal != 0;
   m->bf16 = h.wdtype == 1;
   m->attn_mode = m->bf16 ? 1 : 0;
+  m->refine = m->bf16 && m->pre_ln && h.hidden % 64 == 0 && h.ffn % 64 == 0 &&
+              h.max_pos <= es::kLastMaxKeysHost;
   m->eps = h.eps;
   m->offset = h.reward_offset;
   m->Hp = (int)round_up(m->H, 64);
@@ -707,6 +726,63 @@ es_status gather_last(es_model *m, Workspace &w, const LastView &lv, hipStream_t
   return ES_OK;
 }
 
+// ---- last-token refinement (pre-LN bf16 models).  The reward reads one
+// row per sequence, and in bf16 most of its error is that row's own rounding
+// (its LayerNorm outputs, context and FFN middle rounded to bf16 at every
+// layer).  So beside the bulk pass the last row of each sequence is carried
+// in fp32: its GEMMs take the fp32 activations as hi + lo bf16 pairs against
+// the same bf16 weights, and its attention runs in fp32 over the bulk's K / V
+// of the other positions and its own fp32 K / V.  Only the last rows change:
+// every other row (and so every key and value) is the bulk pass's.
+struct RefineRows {
+  float *x, *u, *q, *c, *h;  // residual, LayerNorm out, Q | K | V, context, FFN middle
+};
+
+RefineRows refine_rows(const es_model *m, const Workspace &w, int n) {
+  RefineRows R;
+  R.x = w.ref;
+  R.u = R.x + (int64_t)n * m->H;
+  R.q = R.u + (int64_t)n * m->H;
+  R.c = R.q + (int64_t)n * m->Nqkv;
+  R.h = R.c + (int64_t)n * m->Kc;
+  return R;
+}
+
+// The last-token rows of the residual stream after the embedding.
+es_status refine_start(es_model *m, Workspace &w, const LastView &lv, hipStream_t st) {
+  Prof p(m, st, ES_KC_REFINE);
+  const int n = lv.tail.n_seqs;
+  const RefineRows R = refine_rows(m, w, n);
+  HIP_TRY(es::launch_gather_rows(w.x, m->H * 4, R.x, m->H * 4, m->H * 4, nullptr, 0, nullptr, 0, 0,
+                                 lv.rows, n, st));
+  p.done(0.0, 2.0 * n * m->H * 4.0);
+  return ES_OK;
+}
+
+// One layer on the refined rows; w.qkv holds this layer's bulk Q | K | V.
+es_status refine_layer(es_model *m, Workspace &w, const DevLayer &D, const LastView &lv,
+                       hipStream_t st) {
+  Prof p(m, st, ES_KC_REFINE);
+  const int n = lv.tail.n_seqs, H = m->H;
+  const RefineRows R = refine_rows(m, w, n);
+  const uint16_t *Wq = (const uint16_t *)D.w_qkv, *Wo = (const uint16_t *)D.w_o;
+  const uint16_t *W1 = (const uint16_t *)D.w_1, *W2 = (const uint16_t *)D.w_2;
+  HIP_TRY(es::launch_layernorm(false, R.x, nullptr, D.ln1_g, D.ln1_b, n, H, m->eps, R.u, nullptr, 0, H, st));
+  HIP_TRY(es::launch_gemm_split(R.u, H, Wq, D.b_qkv, nullptr, R.q, m->Nqkv, n, m->Nqkv, H, es::kEpiF32, st));
+  HIP_TRY(es::launch_attn_last((const uint16_t *)w.qkv, m->Nqkv, R.q, m->Nqkv, m->A, m->dp,
+                               1.0f / std::sqrt((float)m->d), lv.attn, R.c, m->Kc, m->Kc, st));
+  HIP_TRY(es::launch_gemm_split(R.c, m->Kc, Wo, D.b_o, R.x, R.x, H, n, H, m->Kc, es::kEpiResidual, st));
+  HIP_TRY(es::launch_layernorm(false, R.x, nullptr, D.ln2_g, D.ln2_b, n, H, m->eps, R.u, nullptr, 0, H, st));
+  HIP_TRY(es::launch_gemm_split(R.u, H, W1, D.b_1, nullptr, R.h, m->Fp, n, m->Fp, H, es::kEpiGelu, st));
+  HIP_TRY(es::launch_gemm_split(R.h, m->Fp, W2, D.b_2, R.x, R.x, H, n, H, m->Fp, es::kEpiResidual, st));
+  // bytes: the layer's bf16 weights once, the bf16 K and V of every
+  // (last query, key, head) once, and the fp32 rows each step reads and writes
+  const double Hd = (double)m->A * m->d, F = m->F, pr = (double)lv.pairs;
+  p.done(2.0 * n * (4.0 * H * Hd + 2.0 * H * F) + 4.0 * m->d * pr,
+         2.0 * (4.0 * H * Hd + 2.0 * H * F) + 4.0 * m->d * pr + 4.0 * n * (10.0 * H + 8.0 * Hd + 2.0 * F));
+  return ES_OK;
+}
+
 // Embedding and n_layers layers.  With `last` (scoring), the last layer runs
 // its QKV GEMM on every token (all keys and values are needed) and everything
 // after it on the last token of each sequence only -- the reward reads nothing
@@ -715,7 +791,8 @@ es_status gather_last(es_model *m, Workspace &w, const LastView &lv, hipStream_t
 // query sees the same key tiles in the same order), so rewards are bitwise
 // those of the full last layer.
 es_status forward(es_model *m, Workspace &w, const int32_t *d_ids, const es::Ragged &r,
-                  int64_t pairs, int n_layers, hipStream_t st, const LastView *last = nullptr) {
+                  int64_t pairs, int n_layers, hipStream_t st, const LastView *last = nullptr,
+                  bool prune = true) {
   const int T = r.n_tokens, H = m->H, F = m->F, Hd = m->A * m->d;
   const double a = m->bf16 ? 2.0 : 4.0;
   const bool fused = m->bf16 && (m->attn_mode == 1 || r.plen);
@@ -726,9 +803,11 @@ es_status forward(es_model *m, Workspace &w, const int32_t *d_ids, const es::Rag
                              m->norm_g, m->norm_b, m->eps, w.x, w.xb, m->Hp, m->flag, st));
     p.done(10.0 * T * H, (double)T * H * (2.0 * a + 4.0 + (m->pre_ln ? 0.0 : a)) + 4.0 * T);
   }
+  const bool refine = last && m->refine;
+  if (refine && (s = refine_start(m, w, *last, st)) != ES_OK) return s;
   for (int l = 0; l < n_layers; ++l) {
     const DevLayer &D = m->layers[l];
-    const bool tail = last && l == n_layers - 1;
+    const bool tail = last && prune && l == n_layers - 1;
     if (!m->pre_ln) {
       if ((s = gemm(m, ES_KC_QKV, w.xb, m->Hp, D.w_qkv, D.b_qkv, nullptr, w.qkv, m->Nqkv, T,
                     m->Nqkv, m->Hp, H, es::kEpiBias, st)) != ES_OK) return s;
@@ -762,6 +841,8 @@ es_status forward(es_model *m, Workspace &w, const int32_t *d_ids, const es::Rag
       if ((s = layernorm(m, w, w.x, D.ln1_g, D.ln1_b, T, nullptr, st)) != ES_OK) return s;
       if ((s = gemm(m, ES_KC_QKV, w.xb, m->Hp, D.w_qkv, D.b_qkv, nullptr, w.qkv, m->Nqkv, T,
                     m->Nqkv, m->Hp, H, es::kEpiBias, st)) != ES_OK) return s;
+      // before anything of the bulk layer may reuse the Q | K | V memory
+      if (refine && (s = refine_layer(m, w, D, *last, st)) != ES_OK) return s;
       if (!tail) {
         if ((s = attention(m, w, r, pairs, st)) != ES_OK) return s;
         if ((s = gemm(m, ES_KC_OPROJ, w.ctx, m->Kc, D.w_o, D.b_o, w.x, w.x, H, T, H, m->Kc, Hd,
@@ -771,7 +852,7 @@ es_status forward(es_model *m, Workspace &w, const int32_t *d_ids, const es::Rag
                       H, es::kEpiGelu, st, F)) != ES_OK) return s;
         if ((s = gemm(m, ES_KC_FFN2, w.hmid, m->Fp, D.w_2, D.b_2, w.x, w.x, H, T, H, m->Fp, F,
                       es::kEpiResidual, st)) != ES_OK) return s;
-      } else {
+      } else if (!refine) {  // refined: the last rows are already done
         const int n = last->tail.n_seqs;
         if ((s = attention(m, w, fused ? last->attn : r, fused ? last->pairs : pairs, st)) != ES_OK) return s;
         if ((s = gather_last(m, w, *last, st)) != ES_OK) return s;  // x -> y, ctx -> qkv
@@ -789,10 +870,10 @@ es_status forward(es_model *m, Workspace &w, const int32_t *d_ids, const es::Rag
   return ES_OK;
 }
 
-es_status head(es_model *m, Workspace &w, const es::Ragged &r, float offset, float *rewards,
+es_status head(es_model *m, const float *x, const es::Ragged &r, float offset, float *rewards,
                hipStream_t st) {
   Prof p(m, st, ES_KC_HEAD);
-  HIP_TRY(es::launch_head(m->pre_ln, w.x, m->H, r, m->norm_g, m->norm_b, m->eps, m->head_w,
+  HIP_TRY(es::launch_head(m->pre_ln, x, m->H, r, m->norm_g, m->norm_b, m->eps, m->head_w,
                           m->head_b, offset, rewards, st));
   p.done(2.0 * r.n_seqs * m->H, 8.0 * r.n_seqs * m->H);
   return ES_OK;
@@ -870,15 +951,15 @@ es_status score_pass(es_model *m, Workspace &w, const int32_t *d_ids, const Batc
   const es::Ragged r = ragged_of(meta, L);
   const bool fused = m->bf16 && (m->attn_mode == 1 || L.has_prefix);
   es_status s;
-  if (!bound && (s = bind_workspace(m, w, L.n_tokens, fused ? 0 : L.score_elems, st)) != ES_OK)
+  if (!bound && (s = bind_workspace(m, w, L.n_tokens, fused ? 0 : L.score_elems, L.n, st)) != ES_OK)
     return s;
-  if (m->prune && m->L > 0) {
+  if ((m->prune || m->refine) && m->L > 0) {
     const LastView lv = last_view_of(meta, L);
-    if ((s = forward(m, w, d_ids, r, L.pairs, m->L, st, &lv)) != ES_OK) return s;
-    return head(m, w, lv.tail, m->offset, d_rewards, st);
+    if ((s = forward(m, w, d_ids, r, L.pairs, m->L, st, &lv, m->prune)) != ES_OK) return s;
+    return head(m, m->refine ? w.ref : w.x, lv.tail, m->offset, d_rewards, st);
   }
   if ((s = forward(m, w, d_ids, r, L.pairs, m->L, st)) != ES_OK) return s;
-  return head(m, w, r, m->offset, d_rewards, st);
+  return head(m, w.x, r, m->offset, d_rewards, st);
 }
 
 extern "C" es_status es_score_batch(es_model *m, const int32_t *d_token_ids, const int32_t *h_offsets,
@@ -920,7 +1001,8 @@ extern "C" es_status es_score_batch_static(es_model *m, const int32_t *d_token_i
   const bool fused = m->bf16 && m->attn_mode == 1;
   const int64_t rows = std::max<int64_t>(round_up(L.n_tokens, 256), 256);
   std::vector<int64_t> off;
-  const int64_t need = es::plan_arena(pass_usage(m, rows, fused ? 0 : L.score_elems), kArenaAlign, off);
+  const int64_t need =
+      es::plan_arena(pass_usage(m, rows, fused ? 0 : L.score_elems, L.n), kArenaAlign, off);
   const int64_t meta_bytes = round_up(std::max<int64_t>((int64_t)m->meta_asm.size(), 16), kArenaAlign);
   if (meta_bytes + need > ES_STATIC_SCRATCH_BYTES)
     return fail(ES_ERR_CAPACITY,
@@ -939,6 +1021,7 @@ extern "C" es_status es_score_batch_static(es_model *m, const int32_t *d_token_i
   w.hmid = a + off[kTHmid];
   w.S = reinterpret_cast<float *>(a + off[kTS]);
   w.Pb = a + off[kTP];
+  w.ref = reinterpret_cast<float *>(a + off[kTRef]);
   if ((s = score_pass(m, w, d_token_ids, L, d_rewards, st, base, true)) != ES_OK) return s;
   es::clear_error();
   return ES_OK;
@@ -1062,7 +1145,7 @@ extern "C" es_status es_forward_hidden(es_model *m, const int32_t *d_token_ids,
   begin_call(m);
   if ((s = prepare(m, h_offsets, n_seqs, st, &r, &pairs, &L)) != ES_OK) return s;
   const bool fused = m->bf16 && m->attn_mode == 1;
-  if ((s = bind_workspace(m, m->ws[0], L.n_tokens, fused ? 0 : L.score_elems, st)) != ES_OK) return s;
+  if ((s = bind_workspace(m, m->ws[0], L.n_tokens, fused ? 0 : L.score_elems, 0, st)) != ES_OK) return s;
   if ((s = forward(m, m->ws[0], d_token_ids, r, pairs, n_layers, st)) != ES_OK) return s;
   HIP_TRY(hipMemcpyAsync(d_hidden, m->ws[0].x, (size_t)r.n_tokens * m->H * 4, hipMemcpyDeviceToDevice, st));
   return ES_OK;
@@ -1272,6 +1355,6 @@ extern "C" es_status es_profile_collect(es_model *m, es_kernel_stat_t *out) {
 extern "C" const char *es_kernel_class_name(int32_t cls) {
   static const char *names[ES_KC_COUNT] = {"embed", "qkv_gemm", "scores", "softmax", "pv",
                                            "oproj_gemm", "layernorm", "ffn1_gemm", "ffn2_gemm",
-                                           "head", "attn_fused", "gather"};
+                                           "head", "attn_fused", "gather", "refine"};
   return (cls >= 0 && cls < ES_KC_COUNT) ? names[cls] : "";
 }

@@ -595,7 +595,7 @@ es_status es_op_gemm_bf16_tile(const uint16_t *d_a, int32_t lda, const uint16_t 
 enum {
   ES_KC_EMBED = 0, ES_KC_QKV = 1, ES_KC_SCORES = 2, ES_KC_SOFTMAX = 3, ES_KC_PV = 4,
   ES_KC_OPROJ = 5, ES_KC_LAYERNORM = 6, ES_KC_FFN1 = 7, ES_KC_FFN2 = 8, ES_KC_HEAD = 9,
-  ES_KC_ATTN_FUSED = 10, ES_KC_GATHER = 11, ES_KC_COUNT = 12
+  ES_KC_ATTN_FUSED = 10, ES_KC_GATHER = 11, ES_KC_REFINE = 12, ES_KC_COUNT = 13
 };
 
 typedef struct {
