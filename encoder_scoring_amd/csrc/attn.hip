@@ -726,16 +726,18 @@ __global__ __launch_bounds__(256) void attn_fused_pfx_kernel(const uint16_t *__r
 // columns, pitch ldl); every other key / value is the bulk layer's bf16 row
 // (shared prompt rows first, as in the fused kernels).  The last query sees
 // every key of its sequence under either mask.  One block of four wavefronts
-// per (sequence, head).  A key's DP dims are split over DP / 8 neighbouring
-// lanes, 16 bytes each, so a wavefront instruction reads whole rows (one
-// 256-byte row per 16 lanes at DP = 128) and the block takes 256 / (DP / 8)
-// keys at once; a key's dot product is 8 fmas per lane and a butterfly over
-// its lanes.  Max and sum reduce over the block; P . V runs on the same
+// per (sequence, head), a head's sequences in order on one XCD (the
+// candidates of a shared prompt then read its keys and values from one L2).
+// A key's DP dims are split over DP / 8 neighbouring lanes, 16 bytes each,
+// so a wavefront instruction reads whole rows (one 256-byte row per 16 lanes
+// at DP = 128) and the block takes 256 / (DP / 8) keys at once; a key's dot
+// product is 8 fmas per lane and a butterfly over its lanes.  Max and sum reduce over the block; P . V runs on the same
 // lane split, each key slot accumulating its keys in ascending order, and
 // the slots are summed in fixed order through LDS, so the result is
-// reproducible.  Writes ctx[i, h dp .. h dp + dp) (fp32, pitch ldc); the
-// head of index 0 also zeroes columns [n_heads dp, kc), the band a wider
-// GEMM K reads.
+// reproducible.  Writes columns [h dp, h dp + dp) of row i of ctx in the
+// split-operand layout (split_off, K = kc), the input of the output
+// projection's split GEMM; the head of index 0 also zeroes columns
+// [n_heads dp, kc), the band a wider GEMM K reads.
 constexpr int kLastMaxKeys = kLastMaxKeysHost;
 constexpr int kLastThreads = 256;
 
@@ -743,13 +745,16 @@ template <int DP>
 __global__ __launch_bounds__(kLastThreads) void attn_last_kernel(
     const uint16_t *__restrict__ qkv, int ldq, const float *__restrict__ ql, int ldl, int n_heads,
     float scale, const int32_t *__restrict__ off, const int32_t *__restrict__ pref,
-    const int32_t *__restrict__ plen, float *__restrict__ ctx, int ldc, int kc) {
+    const int32_t *__restrict__ plen, uint16_t *__restrict__ ctx, int kc) {
   constexpr int CH = DP / 8, G = kLastThreads / CH, NW = kLastThreads / kWave;
   static_assert(CH <= kWave && kWave % CH == 0, "a key's lanes lie in one wavefront");
   __shared__ float sp[kLastMaxKeys];
   __shared__ __align__(16) float red[G * DP];
   __shared__ float wred[2 * NW];
-  const int seq = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+  // sequences of one head run together on one XCD: a shared prompt's keys
+  // and values then come from that XCD's L2 for all its candidates
+  const int item = xcd_contiguous(blockIdx.x, gridDim.x);
+  const int n_seqs = gridDim.x / n_heads, seq = item % n_seqs, h = item / n_seqs, t = threadIdx.x;
   const int c = t % CH, g = t / CH, lane = t % kWave, wv = t / kWave;
   const int t0 = off[seq], n = off[seq + 1] - off[seq];
   const int np = plen ? plen[seq] : 0, p0 = pref ? pref[seq] : 0;
@@ -768,24 +773,35 @@ __global__ __launch_bounds__(kLastThreads) void attn_last_kernel(
       v[2 * e + 1] = bf2f(w[e] >> 16);
     }
   };
+  // Keys in batches of U per key slot, all U loads issued before any use:
+  // the rows are read at min(j, L - 1) (always a row of the sequence) and
+  // position L - 1 takes the fp32 key instead.
+  constexpr int U = 8;
   float mx = -INFINITY;
-#pragma unroll 4
-  for (int j = g; j < L; j += G) {
-    float k[8];
-    if (j == L - 1) {
+  for (int j0 = g; j0 < L; j0 += U * G) {
+    uint4 kb[U];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) k[e] = qrow[kk + e];
-    } else {
-      unpack(*reinterpret_cast<const uint4 *>(row(j) + kk), k);
+    for (int u = 0; u < U; ++u) kb[u] = *reinterpret_cast<const uint4 *>(row(min(j0 + u * G, L - 1)) + kk);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + u * G;
+      if (j >= L) break;  // the same for a key's CH lanes
+      float k[8];
+      if (j == L - 1) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) k[e] = qrow[kk + e];
+      } else {
+        unpack(kb[u], k);
+      }
+      float dot = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dot = fmaf(q[e], k[e], dot);
+#pragma unroll
+      for (int o = CH / 2; o > 0; o >>= 1) dot += __shfl_xor(dot, o, kWave);
+      const float sc = dot * scale;
+      if (c == 0) sp[j] = sc;
+      mx = fmaxf(mx, sc);
     }
-    float dot = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) dot = fmaf(q[e], k[e], dot);
-#pragma unroll
-    for (int o = CH / 2; o > 0; o >>= 1) dot += __shfl_xor(dot, o, kWave);
-    const float sc = dot * scale;
-    if (c == 0) sp[j] = sc;
-    mx = fmaxf(mx, sc);
   }
   mx = wave_max(mx);
   if (lane == 0) wred[wv] = mx;
@@ -808,32 +824,49 @@ __global__ __launch_bounds__(kLastThreads) void attn_last_kernel(
   float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-#pragma unroll 4
-  for (int j = g; j < L; j += G) {
-    float v[8];
-    if (j == L - 1) {
+  for (int j0 = g; j0 < L; j0 += U * G) {
+    uint4 vb[U];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = qrow[kv + e];
-    } else {
-      unpack(*reinterpret_cast<const uint4 *>(row(j) + kv), v);
+    for (int u = 0; u < U; ++u) vb[u] = *reinterpret_cast<const uint4 *>(row(min(j0 + u * G, L - 1)) + kv);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + u * G;
+      if (j >= L) break;
+      float v[8];
+      if (j == L - 1) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = qrow[kv + e];
+      } else {
+        unpack(vb[u], v);
+      }
+      const float pj = sp[j];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(pj, v[e], acc[e]);
     }
-    const float pj = sp[j];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = fmaf(pj, v[e], acc[e]);
   }
   // red[g][8 c + e]: thread t's 8 values at 8 t
   *reinterpret_cast<float4 *>(red + 8 * t) = make_float4(acc[0], acc[1], acc[2], acc[3]);
   *reinterpret_cast<float4 *>(red + 8 * t + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
   __syncthreads();
-  float *crow = ctx + (int64_t)seq * ldc;
   const float inv = 1.0f / sum;
-  for (int e = t; e < DP; e += kLastThreads) {
-    float a = red[e];
-    for (int s2 = 1; s2 < G; ++s2) a += red[s2 * DP + e];
-    crow[h * DP + e] = a * inv;
+  for (int o = t; o < DP / 4; o += kLastThreads) {  // 4 dims per thread, slots in order
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float a = red[4 * o + e];
+      for (int s2 = 1; s2 < G; ++s2) a += red[s2 * DP + 4 * o + e];
+      v[e] = a * inv;
+    }
+    uint2 hi, lo;
+    split4(v, hi, lo);
+    *reinterpret_cast<uint2 *>(ctx + split_off(seq, h * DP + 4 * o, kc, 0)) = hi;
+    *reinterpret_cast<uint2 *>(ctx + split_off(seq, h * DP + 4 * o, kc, 1)) = lo;
   }
   if (h == 0)
-    for (int col = n_heads * DP + t; col < kc; col += kLastThreads) crow[col] = 0.f;
+    for (int c4 = n_heads * DP / 4 + t; c4 < kc / 4; c4 += kLastThreads) {
+      *reinterpret_cast<uint2 *>(ctx + split_off(seq, 4 * c4, kc, 0)) = make_uint2(0, 0);
+      *reinterpret_cast<uint2 *>(ctx + split_off(seq, 4 * c4, kc, 1)) = make_uint2(0, 0);
+    }
 }
 
 template <typename F>
@@ -922,17 +955,17 @@ hipError_t launch_attn_fused(const uint16_t *qkv, int ldq, int n_heads, int dp, 
 }
 
 hipError_t launch_attn_last(const uint16_t *qkv, int ldq, const float *ql, int ldl, int n_heads,
-                            int dp, float scale, const Ragged &r, float *ctx, int ldc, int kc,
+                            int dp, float scale, const Ragged &r, uint16_t *ctx, int kc,
                             hipStream_t st) {
   if (r.n_seqs <= 0) return hipSuccess;
-  if ((r.plen != nullptr) != (r.pref != nullptr) || r.max_len <= 0 || kc < n_heads * dp || ldc < kc ||
+  if ((int64_t)r.n_seqs * n_heads > INT32_MAX) return hipErrorInvalidValue;
+  if ((r.plen != nullptr) != (r.pref != nullptr) || r.max_len <= 0 || kc < n_heads * dp || kc % 16 ||
       ldl < 3 * n_heads * dp)
     return hipErrorInvalidValue;
   return dispatch_dp(dp, [&](auto dpc) {
     constexpr int DP = decltype(dpc)::value;
-    attn_last_kernel<DP><<<dim3(r.n_seqs, n_heads), dim3(kLastThreads), 0, st>>>(qkv, ldq, ql, ldl, n_heads, scale,
-                                                                      r.off, r.pref, r.plen, ctx, ldc,
-                                                                      kc);
+    attn_last_kernel<DP><<<dim3(r.n_seqs * n_heads), dim3(kLastThreads), 0, st>>>(qkv, ldq, ql, ldl, n_heads, scale,
+                                                                      r.off, r.pref, r.plen, ctx, kc);
     return hipGetLastError();
   });
 }

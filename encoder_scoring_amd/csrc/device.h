@@ -22,6 +22,36 @@ __device__ __forceinline__ uint32_t f2bf2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Block ids are dealt round-robin to the 8 XCDs (each with its own L2):
+// the block of id bid on a grid of nblk takes logical index
+// xcd_contiguous(bid, nblk), so each XCD runs one contiguous run of logical
+// indices and neighbouring work items share that XCD's L2.
+__device__ __forceinline__ int xcd_contiguous(int bid, int nblk) {
+  const int per = (nblk + 7) / 8, xcd = bid & 7, loc = bid >> 3;
+  const int full = nblk - (per - 1) * 8;  // XCDs that receive `per` blocks
+  return xcd < full ? xcd * per + loc : full * per + (xcd - full) * (per - 1) + loc;
+}
+
+// Split-operand layout of an fp32 matrix [rows, K] (K a multiple of 16) for
+// the refinement GEMMs: each element a as the bf16 pair hi = bf16(a), lo =
+// bf16(a - hi), stored in the order the 32 x 32 x 16 MFMA takes its operand.
+// For row tile t (rows 32 t ..), k-step s (columns 16 s ..) and half h (0 hi,
+// 1 lo) a block of 64 lanes x 8 bf16; lane 32 f + r holds row 32 t + r,
+// columns 16 s + 8 f .. + 8.  So one wavefront load of 16 bytes per lane
+// reads 1 KB of contiguous memory.  Offset (bf16 units) of element (m, k):
+__device__ __forceinline__ int64_t split_off(int64_t m, int k, int K, int h) {
+  return ((((m >> 5) * (K >> 4) + (k >> 4)) * 2 + h) * 64 + ((k >> 3) & 1) * 32 + (m & 31)) * 8 + (k & 7);
+}
+
+// hi / lo bf16 bits of 4 consecutive floats (8 bytes each).
+__device__ __forceinline__ void split4(const float (&v)[4], uint2 &hi, uint2 &lo) {
+  float r[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) r[e] = v[e] - bf2f(f2bf(v[e]));
+  hi = make_uint2(f2bf2(v[0], v[1]), f2bf2(v[2], v[3]));
+  lo = make_uint2(f2bf2(r[0], r[1]), f2bf2(r[2], r[3]));
+}
+
 __device__ __forceinline__ float to_f(float v) { return v; }
 __device__ __forceinline__ float to_f(uint16_t v) { return bf2f(v); }
 

@@ -173,13 +173,7 @@ __device__ __forceinline__ void epi_store4(void *out, const float *res, int ldc,
 // per group instead of re-reading the much larger A rows.
 __device__ __forceinline__ void tile_of_block(int tiles_m, int tiles_n, int64_t w_group_bytes,
                                               int &tm, int &tn) {
-  const int nblk = tiles_m * tiles_n;
-  int bid = blockIdx.x;
-  {
-    const int per = (nblk + 7) / 8, xcd = bid & 7, loc = bid >> 3;
-    const int full = nblk - (per - 1) * 8;  // XCDs that receive `per` blocks
-    bid = xcd < full ? xcd * per + loc : full * per + (xcd - full) * (per - 1) + loc;
-  }
+  const int bid = xcd_contiguous(blockIdx.x, tiles_m * tiles_n);
   constexpr int G = 8;
   if (tiles_n <= G || w_group_bytes <= ((int64_t)2 << 20)) {
     const int group = bid / (G * tiles_m), first_n = group * G;
@@ -792,40 +786,45 @@ __global__ __launch_bounds__(512, 1) void gemm_sp_kernel(
 // the operand keeps 16 significant bits (|a - hi - lo| <= 2^-18 |a|) instead
 // of bf16's 8.  It serves the last-token refinement of the reward rows: one
 // row per sequence, fp32 throughout, so those rows carry none of the bulk
-// path's bf16 activation rounding.  Few rows, so the weights dominate the
-// bytes: one block of KW wavefronts per 32 output columns and MT 32-row
-// tiles, each W fragment loaded once and used for all MT row tiles;
+// path's bf16 activation rounding.  A arrives already split, in fragment
+// order (split_off): each of its loads is 1 KB of contiguous memory per
+// wavefront, where fp32 rows read straight into the fragments touched 32
+// cache lines per load and ran at half the speed.  Few rows, so the weights
+// dominate the bytes: one block of KW wavefronts per 32 output columns and
+// MT 32-row tiles, each W fragment loaded once for all MT row tiles;
 // wavefront w takes the w-th of KW equal k-ranges, operands loaded straight
 // into registers D k-steps ahead (the latency tile's fragment layout), and
-// the KW partial tiles are summed in wavefront order through LDS.  Rows past
-// M (A) or N (W) are read at the last row and never stored.  Epilogues (fp32
-// out): kEpiF32 acc + bias, kEpiResidual acc + bias + res[m, n] (res may be
-// out), kEpiGelu GELU(acc + bias) with the device erff.
+// the KW partial tiles are summed in wavefront order through LDS.  W rows
+// past N are read at the last row and never stored.  Epilogues: kEpiF32
+// acc + bias and kEpiResidual acc + bias + res[m, n] (res may be out) into
+// fp32 rows; kEpiGelu GELU(acc + bias) (device erff) into outp, split again
+// (split_off with K' = N) for the next split GEMM.
 template <int EPI, int MT, int D>
-__global__ __launch_bounds__(256) void gemm_split_kernel(const float *__restrict__ A, int lda,
+__global__ __launch_bounds__(256) void gemm_split_kernel(const uint16_t *__restrict__ A,
                                                          const uint16_t *__restrict__ W,
                                                          const float *__restrict__ bias,
-                                                         const float *res, float *out, int ldc, int M,
+                                                         const float *res, float *out,
+                                                         uint16_t *__restrict__ outp, int ldc, int M,
                                                          int N, int K, int tiles_n) {
   __shared__ __align__(16) float part[3][MT][16][64];
   const int lane = threadIdx.x % 64, wv = threadIdx.x / 64, kw = blockDim.x / 64;
   const int fr = lane & 31, fh = lane >> 5;
   const int ch = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
-  const int64_t m0 = (int64_t)ch * MT * 32;
+  const int mtiles = (M + 31) / 32;
+  const int nkt = K / 16, nk = nkt / kw, kb = wv * nk;  // this wavefront's k-steps [kb, kb + nk)
   const int n0 = tn * 32;
-  const int nk = K / 16 / kw, kb = wv * nk;  // this wavefront's k-steps [kb, kb + nk)
-  const float *ap[MT];
+  const uint16_t *ap[MT];  // k-step k of row tile t: hi at ap[t] + 1024 k, lo 512 further
 #pragma unroll
-  for (int t = 0; t < MT; ++t) ap[t] = A + min(m0 + 32 * t + fr, (int64_t)M - 1) * lda + 8 * fh + 16 * kb;
+  for (int t = 0; t < MT; ++t)
+    ap[t] = A + (((int64_t)min(ch * MT + t, mtiles - 1) * nkt + kb) * 128 + lane) * 8;
   const uint16_t *wp = W + (int64_t)min(n0 + fr, N - 1) * K + 8 * fh + 16 * kb;
   static_assert(D % 4 == 0, "the tail runs in groups of 4 k-steps");
-  float4 fa[D][MT][2];
-  bf16x8 fb[D];
+  bf16x8 fa[D][MT][2], fb[D];
   auto load = [&](int d, int k) {
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
-      fa[d][t][0] = *reinterpret_cast<const float4 *>(ap[t] + 16 * k);
-      fa[d][t][1] = *reinterpret_cast<const float4 *>(ap[t] + 16 * k + 4);
+      fa[d][t][0] = *reinterpret_cast<const bf16x8 *>(ap[t] + 1024 * k);
+      fa[d][t][1] = *reinterpret_cast<const bf16x8 *>(ap[t] + 1024 * k + 512);
     }
     fb[d] = *reinterpret_cast<const bf16x8 *>(wp + 16 * k);
   };
@@ -839,16 +838,8 @@ __global__ __launch_bounds__(256) void gemm_split_kernel(const float *__restrict
   auto mma = [&](int d) {
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
-      const float4 *a = fa[d][t];
-      const float v[8] = {a[0].x, a[0].y, a[0].z, a[0].w, a[1].x, a[1].y, a[1].z, a[1].w};
-      bf16x8 hi, lo;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        hi[e] = (__bf16)v[e];
-        lo[e] = (__bf16)(v[e] - (float)hi[e]);
-      }
-      acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[d], hi, acc[t], 0, 0, 0);
-      acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[d], lo, acc[t], 0, 0, 0);
+      acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[d], fa[d][t][0], acc[t], 0, 0, 0);
+      acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[d], fa[d][t][1], acc[t], 0, 0, 0);
     }
   };
   int k = 0;
@@ -883,18 +874,28 @@ __global__ __launch_bounds__(256) void gemm_split_kernel(const float *__restrict
   }
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
-    const int64_t m = m0 + 32 * t + fr;
+    const int64_t m = (int64_t)(ch * MT + t) * 32 + fr;
     if (m >= M) break;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int n = n0 + 8 * g + 4 * fh;
+      if (EPI == kEpiGelu) {  // N a multiple of 16: all four or none
+        if (n >= N) break;
+        float v[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (n + e >= N) break;
-        float x = acc[t][4 * g + e] + bias[n + e];
-        if (EPI == kEpiResidual) x += res[m * ldc + n + e];
-        if (EPI == kEpiGelu) x = gelu_erf(x);
-        out[m * ldc + n + e] = x;
+        for (int e = 0; e < 4; ++e) v[e] = gelu_erf(acc[t][4 * g + e] + bias[n + e]);
+        uint2 hi, lo;
+        split4(v, hi, lo);
+        *reinterpret_cast<uint2 *>(outp + split_off(m, n, N, 0)) = hi;
+        *reinterpret_cast<uint2 *>(outp + split_off(m, n, N, 1)) = lo;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (n + e >= N) break;
+          float x = acc[t][4 * g + e] + bias[n + e];
+          if (EPI == kEpiResidual) x += res[m * ldc + n + e];
+          out[m * ldc + n + e] = x;
+        }
       }
     }
   }
@@ -1287,33 +1288,41 @@ hipError_t launch_gemm_bf16(const uint16_t *A, int lda, const uint16_t *W, const
                                K, epi, st);
 }
 
-hipError_t launch_gemm_split(const float *A, int lda, const uint16_t *W, const float *bias,
-                             const float *res, float *out, int ldc, int M, int N, int K, int epi,
-                             hipStream_t st) {
+hipError_t launch_gemm_split(const uint16_t *A, const uint16_t *W, const float *bias,
+                             const float *res, float *out, uint16_t *outp, int ldc, int M, int N,
+                             int K, int epi, hipStream_t st) {
   if (M <= 0 || N <= 0) return hipSuccess;
-  if (K <= 0 || K % 64 || lda < K || lda % 4) return hipErrorInvalidValue;
-  if (epi != kEpiF32 && epi != kEpiResidual && epi != kEpiGelu) return hipErrorInvalidValue;
-  // up to 4 row tiles per block, as even as the row count allows
-  const int mtiles = (M + 31) / 32, chunks = (mtiles + 3) / 4, mt = (mtiles + chunks - 1) / chunks;
-  const int tn = (N + 31) / 32;
+  if (K <= 0 || K % 64) return hipErrorInvalidValue;
+  if (epi == kEpiGelu ? (N % 16 || !outp) : ((epi != kEpiF32 && epi != kEpiResidual) || !out || ldc < N))
+    return hipErrorInvalidValue;
+  // Up to 3 row tiles per block, as even as the row count allows, but at
+  // least 192 blocks where fewer tiles per block give them (measured at 155
+  // and 1024 rows of the decoder's shapes: 3 tiles best where the grid stays
+  // large, 2 on the N = 2048 GEMMs at 155 rows, 4 never clearly better).
+  const int mtiles = (M + 31) / 32, tn = (N + 31) / 32;
+  int chunks = 1, mt = 1;
+  for (int mx = 3; mx >= 1; --mx) {
+    chunks = (mtiles + mx - 1) / mx;
+    mt = (mtiles + chunks - 1) / chunks;
+    if ((int64_t)chunks * tn >= 192) break;
+  }
   // k-ranges of a multiple of 4 k-steps each
   const int kw = K % 256 == 0 ? 4 : K % 128 == 0 ? 2 : 1;
   const dim3 grid((unsigned)chunks * tn), block(64 * kw);
   auto go = [&](auto mtc) {
     constexpr int MT = decltype(mtc)::value, D = MT <= 2 ? 8 : 4;
     if (epi == kEpiF32)
-      gemm_split_kernel<kEpiF32, MT, D><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K, tn);
+      gemm_split_kernel<kEpiF32, MT, D><<<grid, block, 0, st>>>(A, W, bias, res, out, outp, ldc, M, N, K, tn);
     else if (epi == kEpiResidual)
-      gemm_split_kernel<kEpiResidual, MT, D><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K, tn);
+      gemm_split_kernel<kEpiResidual, MT, D><<<grid, block, 0, st>>>(A, W, bias, res, out, outp, ldc, M, N, K, tn);
     else
-      gemm_split_kernel<kEpiGelu, MT, D><<<grid, block, 0, st>>>(A, lda, W, bias, res, out, ldc, M, N, K, tn);
+      gemm_split_kernel<kEpiGelu, MT, D><<<grid, block, 0, st>>>(A, W, bias, res, out, outp, ldc, M, N, K, tn);
     return hipGetLastError();
   };
   switch (mt) {
     case 1: return go(std::integral_constant<int, 1>{});
     case 2: return go(std::integral_constant<int, 2>{});
-    case 3: return go(std::integral_constant<int, 3>{});
-    default: return go(std::integral_constant<int, 4>{});
+    default: return go(std::integral_constant<int, 3>{});
   }
 }
 

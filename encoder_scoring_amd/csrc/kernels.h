@@ -52,6 +52,10 @@ hipError_t launch_embed(bool w_bf16, bool act_bf16, bool ln, const int32_t *ids,
 hipError_t launch_layernorm(bool act_bf16, const float *x, const float *sub, const float *g,
                             const float *b, int64_t rows, int cols, float eps, float *y, void *yb,
                             int ldb, int pad_cols, hipStream_t st);
+// LayerNorm of fp32 rows [rows, cols] (cols a multiple of 16) into the
+// split-operand layout (device.h split_off): the input of a split GEMM.
+hipError_t launch_layernorm_split(const float *x, const float *g, const float *b, int rows, int cols,
+                                  float eps, uint16_t *out, hipStream_t st);
 // Zero bytes [c0_bytes, c1_bytes) of each of `rows` rows of ld_bytes (all
 // multiples of 4): the padding band of a K-padded GEMM operand.
 hipError_t launch_zero_cols(void *base, int64_t ld_bytes, int rows, int64_t c0_bytes,
@@ -90,14 +94,17 @@ constexpr int kGemmTiles = 7;
 hipError_t launch_gemm_bf16_tile(int tile, const uint16_t *A, int lda, const uint16_t *W,
                                  const float *bias, const float *res, void *out, int ldc, int M,
                                  int N, int K, int epi, hipStream_t st);
-// out (fp32) = epi(A W^T + bias) with fp32 activations A [M, lda >= K] and the
-// bf16 weights, each A element entering bf16 MFMA as a hi + lo bf16 pair
-// (16 significant bits), fp32 accumulation; epi kEpiF32, kEpiResidual (res
-// fp32 [M, ldc], may be out) or kEpiGelu (fp32 output).  Rows of A past M are
-// not read.  For the last-token refinement of the reward rows.
-hipError_t launch_gemm_split(const float *A, int lda, const uint16_t *W, const float *bias,
-                             const float *res, float *out, int ldc, int M, int N, int K, int epi,
-                             hipStream_t st);
+// out = epi(A W^T + bias) with A [M, K] in the split-operand layout (each
+// element a hi + lo bf16 pair, 16 significant bits; device.h split_off) and
+// the bf16 weights, fp32 accumulation; K a multiple of 64.  epi kEpiF32 or
+// kEpiResidual (res fp32 [M, ldc], may be out): fp32 rows in out; kEpiGelu:
+// GELU(acc + bias) into outp in the split-operand layout with K' = N (N a
+// multiple of 16), the next split GEMM's input.  A's row tiles are read
+// whole (rows up to 32 ceil(M / 32)); outputs past M are not written.  For
+// the last-token refinement of the reward rows.
+hipError_t launch_gemm_split(const uint16_t *A, const uint16_t *W, const float *bias,
+                             const float *res, float *out, uint16_t *outp, int ldc, int M, int N,
+                             int K, int epi, hipStream_t st);
 hipError_t launch_gemm_f32(const float *A, int lda, const float *W, const float *bias,
                            const float *res, float *out, int ldc, int M, int N, int K, int epi,
                            hipStream_t st);
@@ -115,12 +122,13 @@ hipError_t launch_attn_fused(const uint16_t *qkv, int ldq, int n_heads, int dp, 
 // Last-token refinement: for each sequence i of r, the attention of its last
 // query in fp32 -- query and last key / value from row i of ql (fp32, pitch
 // ldl, the bulk layout's Q | K | V columns), the other keys and values from
-// the bulk bf16 qkv rows (shared-prompt rows first) -- into ctx row i (fp32,
-// pitch ldc); columns [n_heads dp, kc) zeroed.  Every sequence (prompt
-// included) at most kLastMaxKeys positions.
+// the bulk bf16 qkv rows (shared-prompt rows first) -- into row i of ctx in
+// the split-operand layout with K = kc (a multiple of 16); columns
+// [n_heads dp, kc) zeroed.  Every sequence (prompt included) at most
+// kLastMaxKeys positions.
 constexpr int kLastMaxKeysHost = 4096;
 hipError_t launch_attn_last(const uint16_t *qkv, int ldq, const float *ql, int ldl, int n_heads,
-                            int dp, float scale, const Ragged &r, float *ctx, int ldc, int kc,
+                            int dp, float scale, const Ragged &r, uint16_t *ctx, int kc,
                             hipStream_t st);
 
 }  // namespace es

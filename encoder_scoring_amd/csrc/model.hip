@@ -237,10 +237,16 @@ double ms_since(const std::chrono::steady_clock::time_point &t0) {
   return std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
 }
 
-// fp32 values per sequence of the last-token refinement: its residual row,
-// LayerNorm output, Q | K | V row, context row and FFN middle row.
+// 4-byte words per sequence of the last-token refinement: its residual row
+// and Q | K | V row (fp32), and its LayerNorm output, context and FFN middle
+// rows (hi + lo bf16 pairs); sequences are counted in whole tiles of 32
+// (refine_rows) since the split GEMMs read their operands tile by tile.
 int64_t refine_floats(const es_model *m) {
   return m->refine ? (int64_t)2 * m->H + m->Nqkv + m->Kc + m->Fp : 0;
+}
+
+int64_t refine_bytes(const es_model *m, int64_t n_seqs) {
+  return ((n_seqs + 31) / 32 * 32) * refine_floats(m) * 4;
 }
 
 // Device bytes of all workspaces (fixed buffers or arenas).
@@ -252,7 +258,7 @@ int64_t work_bytes(const es_model *m) {
       const int act = m->bf16 ? 2 : 4;
       const int64_t T = round_up(w.scale * m->max_tokens, 256), S = w.scale * m->score_cap;
       b += T * (m->H * 8 + (int64_t)(m->Hp + m->Nqkv + m->Kc + m->Fp) * act) + S * (4 + act) +
-           (int64_t)w.scale * m->max_seqs * refine_floats(m) * 4;
+           refine_bytes(m, (int64_t)w.scale * m->max_seqs);
     }
   }
   return b;
@@ -296,7 +302,7 @@ es_status alloc_workspace(es_model *m, es_model::Workspace &w, int scale) {
   if ((s = dalloc(m, (void **)&w.S, S * 4)) != ES_OK) return s;
   if ((s = dalloc(m, &w.Pb, S * act)) != ES_OK) return s;
   if (m->refine &&
-      (s = dalloc(m, (void **)&w.ref, (int64_t)scale * m->max_seqs * refine_floats(m) * 4)) != ES_OK)
+      (s = dalloc(m, (void **)&w.ref, refine_bytes(m, (int64_t)scale * m->max_seqs))) != ES_OK)
     return s;
   w.scale = scale;
   m->work_allocs += m->refine ? 9 : 8;
@@ -333,7 +339,7 @@ std::vector<es::Usage> pass_usage(const es_model *m, int64_t rows, int64_t score
   u[kTHmid] = {rows * m->Fp * act, 7, 8};
   u[kTS] = {score_elems * 4, 3, 3};
   u[kTP] = {score_elems * act, 3, 3};
-  u[kTRef] = {n_seqs * refine_floats(m) * 4, 0, 10};  // the pass's refinement rows
+  u[kTRef] = {refine_bytes(m, n_seqs), 0, 10};  // the pass's refinement rows
   return u;
 }
 
@@ -735,16 +741,18 @@ es_status gather_last(es_model *m, Workspace &w, const LastView &lv, hipStream_t
 // of the other positions and its own fp32 K / V.  Only the last rows change:
 // every other row (and so every key and value) is the bulk pass's.
 struct RefineRows {
-  float *x, *u, *q, *c, *h;  // residual, LayerNorm out, Q | K | V, context, FFN middle
+  float *x, *q;           // residual, Q | K | V (fp32 rows)
+  uint16_t *u, *c, *h;    // LayerNorm out, context, FFN middle (split-operand layout)
 };
 
 RefineRows refine_rows(const es_model *m, const Workspace &w, int n) {
+  const int64_t n32 = (n + 31) / 32 * 32;
   RefineRows R;
   R.x = w.ref;
-  R.u = R.x + (int64_t)n * m->H;
-  R.q = R.u + (int64_t)n * m->H;
-  R.c = R.q + (int64_t)n * m->Nqkv;
-  R.h = R.c + (int64_t)n * m->Kc;
+  R.q = R.x + n32 * m->H;
+  R.u = reinterpret_cast<uint16_t *>(R.q + n32 * m->Nqkv);
+  R.c = R.u + n32 * m->H * 2;
+  R.h = R.c + n32 * m->Kc * 2;
   return R;
 }
 
@@ -767,14 +775,15 @@ es_status refine_layer(es_model *m, Workspace &w, const DevLayer &D, const LastV
   const RefineRows R = refine_rows(m, w, n);
   const uint16_t *Wq = (const uint16_t *)D.w_qkv, *Wo = (const uint16_t *)D.w_o;
   const uint16_t *W1 = (const uint16_t *)D.w_1, *W2 = (const uint16_t *)D.w_2;
-  HIP_TRY(es::launch_layernorm(false, R.x, nullptr, D.ln1_g, D.ln1_b, n, H, m->eps, R.u, nullptr, 0, H, st));
-  HIP_TRY(es::launch_gemm_split(R.u, H, Wq, D.b_qkv, nullptr, R.q, m->Nqkv, n, m->Nqkv, H, es::kEpiF32, st));
+  HIP_TRY(es::launch_layernorm_split(R.x, D.ln1_g, D.ln1_b, n, H, m->eps, R.u, st));
+  HIP_TRY(es::launch_gemm_split(R.u, Wq, D.b_qkv, nullptr, R.q, nullptr, m->Nqkv, n, m->Nqkv, H,
+                                es::kEpiF32, st));
   HIP_TRY(es::launch_attn_last((const uint16_t *)w.qkv, m->Nqkv, R.q, m->Nqkv, m->A, m->dp,
-                               1.0f / std::sqrt((float)m->d), lv.attn, R.c, m->Kc, m->Kc, st));
-  HIP_TRY(es::launch_gemm_split(R.c, m->Kc, Wo, D.b_o, R.x, R.x, H, n, H, m->Kc, es::kEpiResidual, st));
-  HIP_TRY(es::launch_layernorm(false, R.x, nullptr, D.ln2_g, D.ln2_b, n, H, m->eps, R.u, nullptr, 0, H, st));
-  HIP_TRY(es::launch_gemm_split(R.u, H, W1, D.b_1, nullptr, R.h, m->Fp, n, m->Fp, H, es::kEpiGelu, st));
-  HIP_TRY(es::launch_gemm_split(R.h, m->Fp, W2, D.b_2, R.x, R.x, H, n, H, m->Fp, es::kEpiResidual, st));
+                               1.0f / std::sqrt((float)m->d), lv.attn, R.c, m->Kc, st));
+  HIP_TRY(es::launch_gemm_split(R.c, Wo, D.b_o, R.x, R.x, nullptr, H, n, H, m->Kc, es::kEpiResidual, st));
+  HIP_TRY(es::launch_layernorm_split(R.x, D.ln2_g, D.ln2_b, n, H, m->eps, R.u, st));
+  HIP_TRY(es::launch_gemm_split(R.u, W1, D.b_1, nullptr, nullptr, R.h, 0, n, m->Fp, H, es::kEpiGelu, st));
+  HIP_TRY(es::launch_gemm_split(R.h, W2, D.b_2, R.x, R.x, nullptr, H, n, H, m->Fp, es::kEpiResidual, st));
   // bytes: the layer's bf16 weights once, the bf16 K and V of every
   // (last query, key, head) once, and the fp32 rows each step reads and writes
   const double Hd = (double)m->A * m->d, F = m->F, pr = (double)lv.pairs;

@@ -548,6 +548,58 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint32_t *__rest
 }
 }  // namespace
 
+namespace {
+// LayerNorm of fp32 rows into the split-operand layout (split_off): one block
+// per row, mean and variance over the row in two passes, fixed reduction
+// order.  For the refinement rows, which feed the split GEMMs.
+__global__ __launch_bounds__(256) void layernorm_split_kernel(const float *__restrict__ x,
+                                                              const float *__restrict__ g,
+                                                              const float *__restrict__ b, int cols,
+                                                              float eps, uint16_t *__restrict__ out) {
+  __shared__ float red[2][4];
+  const int64_t row = blockIdx.x;
+  const int t = threadIdx.x, lane = t % kWave, wv = t / kWave, c4 = cols / 4;
+  const float4 *xr = reinterpret_cast<const float4 *>(x + row * cols);
+  float s = 0.f;
+  for (int c = t; c < c4; c += 256) {
+    const float4 v = xr[c];
+    s += (v.x + v.y) + (v.z + v.w);
+  }
+  s = wave_sum(s);
+  if (lane == 0) red[0][wv] = s;
+  __syncthreads();
+  const float mean = ((red[0][0] + red[0][1]) + (red[0][2] + red[0][3])) / cols;
+  float q = 0.f;
+  for (int c = t; c < c4; c += 256) {
+    const float4 v = xr[c];
+    const float d0 = v.x - mean, d1 = v.y - mean, d2 = v.z - mean, d3 = v.w - mean;
+    q += (d0 * d0 + d1 * d1) + (d2 * d2 + d3 * d3);
+  }
+  q = wave_sum(q);
+  if (lane == 0) red[1][wv] = q;
+  __syncthreads();
+  const float rstd = rsqrtf(((red[1][0] + red[1][1]) + (red[1][2] + red[1][3])) / cols + eps);
+  for (int c = t; c < c4; c += 256) {
+    const float4 v = xr[c], gg = reinterpret_cast<const float4 *>(g)[c],
+                 bb = reinterpret_cast<const float4 *>(b)[c];
+    const float y[4] = {(v.x - mean) * rstd * gg.x + bb.x, (v.y - mean) * rstd * gg.y + bb.y,
+                        (v.z - mean) * rstd * gg.z + bb.z, (v.w - mean) * rstd * gg.w + bb.w};
+    uint2 hi, lo;
+    split4(y, hi, lo);
+    *reinterpret_cast<uint2 *>(out + split_off(row, 4 * c, cols, 0)) = hi;
+    *reinterpret_cast<uint2 *>(out + split_off(row, 4 * c, cols, 1)) = lo;
+  }
+}
+}  // namespace
+
+hipError_t launch_layernorm_split(const float *x, const float *g, const float *b, int rows, int cols,
+                                  float eps, uint16_t *out, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  if (cols <= 0 || cols % 16) return hipErrorInvalidValue;
+  layernorm_split_kernel<<<rows, 256, 0, st>>>(x, g, b, cols, eps, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_gather_rows(const void *a_src, int a_pitch, void *a_dst, int a_dpitch, int a_bytes,
                               const void *c_src, int c_pitch, void *c_dst, int c_dpitch, int c_bytes,
                               const int32_t *rows, int n, hipStream_t st) {
