@@ -11,6 +11,10 @@ provides device memory and the current stream):
     pack_offsets(lengths, order, b, e)       packed offsets of one planned batch
     plan_arena(bytes, first, last, align)    offsets of tensors with lifetimes (workspace planner)
     check_plan(lengths, heads, causal, ...)  build a call's per-pass metadata and check every index
+    layernorm, softmax_ragged, attention_fused, gemm_bf16
+                                             single kernels of the bf16 pass on caller buffers
+    split_rows, layernorm_split, gemm_split, attention_last
+                                             the last-token refinement's kernels (split-operand layout)
 """
 from .api import (  # noqa: F401
     Scorer,
@@ -24,6 +28,10 @@ from .api import (  # noqa: F401
     softmax_ragged,
     attention_fused,
     gemm_bf16,
+    split_rows,
+    layernorm_split,
+    gemm_split,
+    attention_last,
     version,
 )
 from ._lib import EncScoreError, EXPORTS  # noqa: F401

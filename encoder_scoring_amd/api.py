@@ -395,3 +395,51 @@ def gemm_bf16(a, w, bias, out, M, N, K, epilogue, res=None, tile=None):
         check(lib, lib.es_op_gemm_bf16(*args, _stream()))
     else:
         check(lib, lib.es_op_gemm_bf16_tile(*args, int(tile), _stream()))
+
+
+# ------------------------------------------- last-token refinement kernels
+
+def split_rows(a, out):
+    """fp32 rows a [M, K] into the split-operand layout (es_op_split); out an
+    int16 tensor of at least 2 * 32 ceil(M / 32) * K elements."""
+    torch = _torch()
+    lib = _lib.load()
+    M, K = a.shape
+    check(lib, lib.es_op_split(_dptr(a, torch.float32, "a"), int(a.stride(0)), int(M), int(K),
+                               _dptr(out, torch.int16, "out"), _stream()))
+
+
+def layernorm_split(x, gamma, beta, eps, out):
+    """Row LayerNorm of fp32 x [rows, cols] into the split-operand layout."""
+    torch = _torch()
+    lib = _lib.load()
+    rows, cols = x.shape
+    check(lib, lib.es_op_layernorm_split(_dptr(x, torch.float32, "x"), _dptr(gamma, torch.float32, "gamma"),
+                                         _dptr(beta, torch.float32, "beta"), int(rows), int(cols),
+                                         float(eps), _dptr(out, torch.int16, "out"), _stream()))
+
+
+def gemm_split(a_split, w, bias, M, N, K, epilogue, out=None, out_split=None, res=None):
+    """epilogue(A W^T + bias) with A in the split-operand layout (es_op_gemm_split):
+    epilogue 3 / 2 into fp32 out [M, ldc] (2 adds res), 1 (GELU) into out_split."""
+    torch = _torch()
+    lib = _lib.load()
+    check(lib, lib.es_op_gemm_split(_dptr(a_split, torch.int16, "a_split"), _dptr(w, torch.int16, "w"),
+                                    _dptr(bias, torch.float32, "bias"),
+                                    _dptr(res, torch.float32, "res") if res is not None else None,
+                                    _dptr(out, torch.float32, "out") if out is not None else None,
+                                    _dptr(out_split, torch.int16, "out_split") if out_split is not None else None,
+                                    int(out.stride(0)) if out is not None else 0, int(M), int(N), int(K),
+                                    int(epilogue), _stream()))
+
+
+def attention_last(rag, qkv, ql, ctx_split, head_dim, kc, scale=None):
+    """fp32 attention of each sequence's last query (es_op_attention_last)."""
+    torch = _torch()
+    lib = _lib.load()
+    if scale is None:
+        scale = 1.0 / float(head_dim) ** 0.5
+    check(lib, lib.es_op_attention_last(rag.handle, _dptr(qkv, torch.int16, "qkv"), int(qkv.stride(0)),
+                                        _dptr(ql, torch.float32, "ql"), int(ql.stride(0)), int(head_dim),
+                                        float(scale), _dptr(ctx_split, torch.int16, "ctx_split"), int(kc),
+                                        _stream()))

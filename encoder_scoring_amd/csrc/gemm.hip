@@ -783,7 +783,7 @@ __global__ __launch_bounds__(512, 1) void gemm_sp_kernel(
 // out = epi(A W^T + bias) for fp32 activations A against the bf16 weights, on
 // bf16 MFMA with fp32 accumulation: each A element enters as the pair hi =
 // bf16(a), lo = bf16(a - hi), two MFMAs per k-step into one accumulator, so
-// the operand keeps 16 significant bits (|a - hi - lo| <= 2^-18 |a|) instead
+// the operand keeps 16 significant bits (|a - hi - lo| <= 2^-16 |a|) instead
 // of bf16's 8.  It serves the last-token refinement of the reward rows: one
 // row per sequence, fp32 throughout, so those rows carry none of the bulk
 // path's bf16 activation rounding.  A arrives already split, in fragment

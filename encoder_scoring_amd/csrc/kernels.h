@@ -52,6 +52,9 @@ hipError_t launch_embed(bool w_bf16, bool act_bf16, bool ln, const int32_t *ids,
 hipError_t launch_layernorm(bool act_bf16, const float *x, const float *sub, const float *g,
                             const float *b, int64_t rows, int cols, float eps, float *y, void *yb,
                             int ldb, int pad_cols, hipStream_t st);
+// fp32 rows a [M, lda] (K columns, K a multiple of 16) into the
+// split-operand layout; rows [M, 32 ceil(M / 32)) written as zeros.
+hipError_t launch_split_rows(const float *a, int lda, int M, int K, uint16_t *out, hipStream_t st);
 // LayerNorm of fp32 rows [rows, cols] (cols a multiple of 16) into the
 // split-operand layout (device.h split_off): the input of a split GEMM.
 hipError_t launch_layernorm_split(const float *x, const float *g, const float *b, int rows, int cols,

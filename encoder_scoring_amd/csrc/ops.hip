@@ -196,3 +196,55 @@ extern "C" es_status es_op_gemm_bf16_tile(const uint16_t *d_a, int32_t lda, cons
   return gemm_bf16_checked("es_op_gemm_bf16_tile", d_a, lda, d_w, d_bias, d_res, d_out, ldc, M, N,
                            K, epilogue, tile, stream);
 }
+
+// ---- the refinement's split-operand kernels (last-token rows in fp32)
+
+extern "C" es_status es_op_split(const float *d_a, int32_t lda, int32_t M, int32_t K,
+                                 uint16_t *d_out, void *stream) {
+  if (!d_a || !d_out) return fail(ES_ERR_ARG, "es_op_split: NULL pointer");
+  if (M < 0 || K <= 0 || K % 16 || lda < K || lda % 4)
+    return fail(ES_ERR_ARG, "es_op_split: M=%d K=%d lda=%d", M, K, lda);
+  HIP_TRY(es::launch_split_rows(d_a, lda, M, K, d_out, static_cast<hipStream_t>(stream)));
+  return ES_OK;
+}
+
+extern "C" es_status es_op_layernorm_split(const float *d_x, const float *d_gamma,
+                                           const float *d_beta, int32_t rows, int32_t cols,
+                                           float eps, uint16_t *d_out, void *stream) {
+  if (!d_x || !d_gamma || !d_beta || !d_out) return fail(ES_ERR_ARG, "es_op_layernorm_split: NULL pointer");
+  if (rows < 0 || cols <= 0 || cols % 16) return fail(ES_ERR_ARG, "es_op_layernorm_split: rows=%d cols=%d", rows, cols);
+  HIP_TRY(es::launch_layernorm_split(d_x, d_gamma, d_beta, rows, cols, eps, d_out,
+                                     static_cast<hipStream_t>(stream)));
+  return ES_OK;
+}
+
+extern "C" es_status es_op_gemm_split(const uint16_t *d_a, const uint16_t *d_w, const float *d_bias,
+                                      const float *d_res, float *d_out, uint16_t *d_out_split,
+                                      int32_t ldc, int32_t M, int32_t N, int32_t K, int32_t epilogue,
+                                      void *stream) {
+  if (!d_a || !d_w || !d_bias) return fail(ES_ERR_ARG, "es_op_gemm_split: NULL pointer");
+  if (epilogue != es::kEpiGelu && epilogue != es::kEpiResidual && epilogue != es::kEpiF32)
+    return fail(ES_ERR_ARG, "es_op_gemm_split: epilogue %d", epilogue);
+  if (epilogue == es::kEpiGelu ? !d_out_split : (!d_out || (epilogue == es::kEpiResidual && !d_res)))
+    return fail(ES_ERR_ARG, "es_op_gemm_split: NULL output or residual");
+  if (M < 0 || N <= 0 || K <= 0 || K % 64 || (epilogue == es::kEpiGelu ? N % 16 != 0 : ldc < N))
+    return fail(ES_ERR_ARG, "es_op_gemm_split: M=%d N=%d K=%d ldc=%d", M, N, K, ldc);
+  HIP_TRY(es::launch_gemm_split(d_a, d_w, d_bias, d_res, d_out, d_out_split, ldc, M, N, K, epilogue,
+                                static_cast<hipStream_t>(stream)));
+  return ES_OK;
+}
+
+extern "C" es_status es_op_attention_last(const es_ragged *r, const uint16_t *d_qkv, int32_t ld_qkv,
+                                          const float *d_ql, int32_t ld_ql, int32_t head_dim,
+                                          float scale, uint16_t *d_ctx_split, int32_t kc,
+                                          void *stream) {
+  if (!r || !d_qkv || !d_ql || !d_ctx_split) return fail(ES_ERR_ARG, "es_op_attention_last: NULL pointer");
+  const int64_t width = (int64_t)r->n_heads * head_dim;
+  if ((head_dim != 32 && head_dim != 64 && head_dim != 128) || ld_qkv < 3 * width || ld_qkv % 8 ||
+      ld_ql < 3 * width || kc < width || kc % 16 || !(scale > 0.f))
+    return fail(ES_ERR_ARG, "es_op_attention_last: head_dim=%d ld_qkv=%d ld_ql=%d kc=%d scale=%g (n_heads=%d)",
+                head_dim, ld_qkv, ld_ql, kc, (double)scale, r->n_heads);
+  HIP_TRY(es::launch_attn_last(d_qkv, ld_qkv, d_ql, ld_ql, r->n_heads, head_dim, scale, r->r,
+                               d_ctx_split, kc, static_cast<hipStream_t>(stream)));
+  return ES_OK;
+}

@@ -590,7 +590,34 @@ __global__ __launch_bounds__(256) void layernorm_split_kernel(const float *__res
     *reinterpret_cast<uint2 *>(out + split_off(row, 4 * c, cols, 1)) = lo;
   }
 }
+// fp32 rows into the split-operand layout, 4 elements per thread; rows in
+// [M, 32 ceil(M / 32)) become zeros.
+__global__ __launch_bounds__(256) void split_rows_kernel(const float *__restrict__ a, int lda, int M,
+                                                         int K, int64_t n4, uint16_t *__restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  const int k4 = K / 4;
+  const int64_t m = i / k4;
+  const int c = (int)(i % k4);
+  float v[4] = {0.f, 0.f, 0.f, 0.f};
+  if (m < M) {
+    const float4 x = *reinterpret_cast<const float4 *>(a + m * lda + 4 * c);
+    v[0] = x.x, v[1] = x.y, v[2] = x.z, v[3] = x.w;
+  }
+  uint2 hi, lo;
+  split4(v, hi, lo);
+  *reinterpret_cast<uint2 *>(out + split_off(m, 4 * c, K, 0)) = hi;
+  *reinterpret_cast<uint2 *>(out + split_off(m, 4 * c, K, 1)) = lo;
+}
 }  // namespace
+
+hipError_t launch_split_rows(const float *a, int lda, int M, int K, uint16_t *out, hipStream_t st) {
+  if (M <= 0) return hipSuccess;
+  if (K <= 0 || K % 16 || lda < K || lda % 4) return hipErrorInvalidValue;
+  const int64_t n4 = (int64_t)(M + 31) / 32 * 32 * (K / 4);
+  split_rows_kernel<<<(unsigned)((n4 + 255) / 256), 256, 0, st>>>(a, lda, M, K, n4, out);
+  return hipGetLastError();
+}
 
 hipError_t launch_layernorm_split(const float *x, const float *g, const float *b, int rows, int cols,
                                   float eps, uint16_t *out, hipStream_t st) {

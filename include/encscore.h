@@ -589,6 +589,64 @@ es_status es_op_gemm_bf16_tile(const uint16_t *d_a, int32_t lda, const uint16_t 
                                int32_t M, int32_t N, int32_t K, int32_t epilogue, int32_t tile,
                                void *stream);
 
+/* ------------------------------------------- last-token refinement kernels
+ *
+ * For pre-LN bf16 models the scoring entry points carry the last row of every
+ * sequence (the one the reward reads: "Learning to summarize from human
+ * feedback", Method adaptation) through the layers in fp32 beside the bf16
+ * pass of all rows.  Its GEMMs take each fp32 activation a as the bf16 pair
+ * hi = bf16(a), lo = bf16(a - hi) (round to nearest even both times; a - hi
+ * is exact in fp32), two bf16 MFMAs into one fp32 accumulator: 16
+ * significant bits, |a - hi - lo| <= 2^-16 |a|.  Those operands live in the
+ * split-operand layout: for an fp32 matrix [M, K] (K a multiple of 16), rows
+ * in tiles of 32 and columns in k-steps of 16, element (m, k) half h (0 hi,
+ * 1 lo) at bf16 index
+ *   ((((m / 32) (K / 16) + k / 16) 2 + h) 64 + ((k / 8) % 2) 32 + m % 32) 8 + k % 8,
+ * 4 * 32 ceil(M / 32) * K bytes in all.  The four entry points below run the
+ * refinement's kernels on caller buffers, for per-kernel parity tests;
+ * asynchronous, they allocate nothing.
+ */
+
+/* es_op_split -- fp32 rows d_a [M, lda] (K columns; lda >= K, lda % 4 == 0,
+ * 16-byte aligned) into the split-operand layout d_out; rows
+ * [M, 32 ceil(M/32)) are written as zeros.  Errors: ES_ERR_ARG, ES_ERR_HIP. */
+es_status es_op_split(const float *d_a, int32_t lda, int32_t M, int32_t K, uint16_t *d_out,
+                      void *stream);
+
+/* es_op_layernorm_split -- per-row LayerNorm (as es_op_layernorm, fp32
+ * arithmetic) of d_x float32[rows, cols] (cols a multiple of 16) into the
+ * split-operand layout d_out (rows past `rows` in the last tile untouched).
+ * Errors: ES_ERR_ARG, ES_ERR_HIP. */
+es_status es_op_layernorm_split(const float *d_x, const float *d_gamma, const float *d_beta,
+                                int32_t rows, int32_t cols, float eps, uint16_t *d_out,
+                                void *stream);
+
+/* es_op_gemm_split -- epilogue(A W^T + bias), A [M, K] in the split-operand
+ * layout (d_a, 32 ceil(M/32) rows read), W bf16 bits [N, K] row-major, K a
+ * positive multiple of 64, fp32 accumulation.  epilogue 3: d_out fp32
+ * [M, ldc] = acc + bias; 2: d_out = acc + bias + d_res[m, n] (d_res fp32
+ * [M, ldc], may be d_out); 1: GELU(acc + bias) (erf form) into d_out_split
+ * in the split-operand layout with K' = N (N a multiple of 16; rows past M
+ * untouched).  Only m < M, n < N written.  Errors: ES_ERR_ARG, ES_ERR_HIP. */
+es_status es_op_gemm_split(const uint16_t *d_a, const uint16_t *d_w, const float *d_bias,
+                           const float *d_res, float *d_out, uint16_t *d_out_split, int32_t ldc,
+                           int32_t M, int32_t N, int32_t K, int32_t epilogue, void *stream);
+
+/* es_op_attention_last -- the attention of each sequence's last query in
+ * fp32 over the ragged layout of `r` (Attention Is All You Need, Scaled
+ * Dot-Product Attention; the last query sees every key of its sequence,
+ * causal or not): for sequence i (rows t0_i .. t0_i + n_i - 1 of d_qkv) and
+ * head h,  ctx_i[h d + e] = sum_k softmax_k(scale q . K_k) V_k[e]  with q,
+ * and the last key and value, from row i of d_ql (fp32 [n_seqs, ld_ql],
+ * Q | K | V as in d_qkv), the other keys and values from d_qkv (bf16 bits
+ * [T, ld_qkv], ld_qkv a multiple of 8).  Row i of d_ctx_split, in the
+ * split-operand layout with K = kc (>= n_heads d, a multiple of 16), gets
+ * columns [0, n_heads d) and zeros in [n_heads d, kc).  head_dim 32, 64 or
+ * 128.  Errors: ES_ERR_ARG, ES_ERR_HIP. */
+es_status es_op_attention_last(const es_ragged *r, const uint16_t *d_qkv, int32_t ld_qkv,
+                               const float *d_ql, int32_t ld_ql, int32_t head_dim, float scale,
+                               uint16_t *d_ctx_split, int32_t kc, void *stream);
+
 /* ------------------------------------------------------------- profiling */
 
 /* Kernel classes of the hot path, in launch order within a layer. */

@@ -39,3 +39,20 @@ def f32_to_bf16_bits(x):
 
 def offsets_of(lengths):
     return np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+
+
+def split_decode(bits, M, K):
+    """Split-operand layout (es_op_split) -> (hi, lo) uint16 bf16 patterns,
+    each [32 ceil(M / 32), K]: element (m, k) half h sits at
+    ((((m // 32) (K // 16) + k // 16) 2 + h) 64 + ((k // 8) % 2) 32 + m % 32) 8 + k % 8."""
+    M32 = -(-M // 32) * 32
+    a = np.asarray(bits).view(np.uint16)[: M32 * K * 2].reshape(M32 // 32, K // 16, 2, 2, 32, 8)
+    # [tile][kstep][half][k-octet][row][e] -> [tile][row][kstep][k-octet][e]
+    hi = a[:, :, 0].transpose(0, 3, 1, 2, 4).reshape(M32, K)
+    lo = a[:, :, 1].transpose(0, 3, 1, 2, 4).reshape(M32, K)
+    return hi, lo
+
+
+def bits_to_f64(bits):
+    """uint16 bf16 patterns (numpy) -> float64."""
+    return (np.asarray(bits).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
