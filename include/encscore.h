@@ -125,6 +125,15 @@ es_status es_blob_info(const void *h_blob, int64_t nbytes, es_model_info_t *info
  *                ("Learning to summarize from human feedback", Method adaptation: scalar
  *                head, reward at the end of the complete sequence).
  *
+ * Precision: bf16 models run every row with bf16 GEMM operands and fp32
+ * accumulation.  For pre-LN bf16 models (hidden and FFN widths multiples of
+ * 64, max_pos <= 4096) the last row of each sequence -- the only one the
+ * reward reads -- is also carried through every layer in fp32 beside that
+ * pass, its GEMM operands split into hi + lo bf16 pairs and its attention
+ * in fp32 over the pass's keys and values (the last-token refinement
+ * kernels below); the reward is read from that row.  Its bf16 operand
+ * rounding otherwise dominates the decoder's reward error.
+ *
  * Host-side validation (synchronous, before any device work): n_seqs in
  * [1, max_seqs] (ES_ERR_ARG / ES_ERR_CAPACITY), offsets malformed (ES_ERR_ARG),
  * a length above max_pos (ES_ERR_RANGE), total tokens above max_tokens
@@ -236,6 +245,7 @@ es_status es_score_best_of_n(es_model *m, const int32_t *d_token_ids,
  * and the first `n_layers` layers (0 <= n_layers <= model layers) and copies
  * the fp32 residual stream into d_hidden float32[offsets[n_seqs], hidden]
  * (row t = token t of the packed batch).  Same validation as es_score_batch.
+ * These are the bf16 pass's rows (no last-token refinement).
  */
 es_status es_forward_hidden(es_model *m, const int32_t *d_token_ids, const int32_t *h_offsets,
                             int32_t n_seqs, int32_t n_layers, float *d_hidden, void *stream);
@@ -301,7 +311,9 @@ es_status es_memory_stats(es_model *m, es_memory_stats_t *out, int32_t reset);
  * reward is read at the end of the complete sequence), so the last layer runs
  * its QKV GEMM on every token (all keys and values) and the rest -- the last
  * query's attention, the output projection, the LayerNorms and the FFN -- on
- * the last token of each sequence only.  Rewards are bitwise the same either
+ * the last token of each sequence only (with the last-token refinement of
+ * es_score_batch those rows already run in the refinement, so the pruned last
+ * layer stops after its QKV GEMM).  Rewards are bitwise the same either
  * way; es_forward_hidden never prunes.  enabled: 0 or 1.  Errors: ES_ERR_ARG.
  */
 es_status es_set_pruning(es_model *m, int32_t enabled);

@@ -53,6 +53,7 @@ CLASS_PATTERNS = {  # kernel classes that are not GEMMs, by kernel name
     "scores": r"scores_(mfma_)?kernel",
     "pv": r"pv_(mfma_)?kernel",
     "embed": r"embed_kernel",
+    "refine": r"gemm_split_kernel|layernorm_split_kernel|attn_last_kernel",
 }
 CLASS_SOURCE = {"softmax": "rowops.hip", "layernorm": "rowops.hip", "attn_fused": "attn.hip",
                 "embed": "rowops.hip"}
