@@ -14,7 +14,8 @@ The headline is the decoder reward model's best-of-16 stream scored as
 1024 plain prompt + summary sequences (the largest workload).  Each step is
 bracketed by HIP events on the stream, so the line carries the median and a
 95 % t-interval of the step time next to the mean over the timed region.
-The other attention form is timed on the same stream ("variants"), and with
+The other attention form is timed on the same stream ("variants"; for the
+decoder also the stream without the last-token refinement), and with
 the default workload the shared-prompt form of the same stream and the two
 BERT-base streams follow as "extra_workloads", each with its own step
 statistics and dominant-kernel roofline.
@@ -319,6 +320,15 @@ class Workload:
         self.sc.set_attention(self.attention)
         return "attention_" + other, res
 
+    def without_refinement(self, steps, warmup):
+        """The same stream with the last-token refinement off (es_set_refinement):
+        timed steps only, to show what the reward rows' fp32 pass costs."""
+        self.sc.set_refinement(False)
+        try:
+            return self.measure(steps, warmup)
+        finally:
+            self.sc.set_refinement(True)
+
     def config(self, args):
         cfg, st = self.cfg, self.stats
         return {"workload": cfg.name, "description": WORKLOAD_DESC[cfg.name],
@@ -352,9 +362,9 @@ def row_reductions(workload, tables):
     return out
 
 
-def run_entry(w, args, steps, warmup, prof_steps, variants=True):
+def run_entry(w, args, steps, warmup, prof_steps, variants=True, refinement_variant=False):
     """Timed steps, kernel table, roofline and (optionally) the other attention
-    form for one workload."""
+    form, and the stream without the last-token refinement, for one workload."""
     res = w.measure(steps, warmup)
     log(f"{w.cfg.name}{' shared prompts' if w.best_of_n else ''}: {res['value']} seq/s, "
         f"step ms {res['step_ms']}")
@@ -367,8 +377,12 @@ def run_entry(w, args, steps, warmup, prof_steps, variants=True):
         k, v = w.other_attention(steps, warmup, prof_steps)
         res["variants"][k] = v
         log(f"  {k}: {v['value']} seq/s")
+    if refinement_variant and w.sc.refinement():
+        v = w.without_refinement(steps, warmup)
+        res["variants"]["no_refinement"] = v
+        log(f"  no_refinement: {v['value']} seq/s")
     res["row_reductions"] = row_reductions(
-        w.cfg.name, [res["kernels"]] + [v["kernels"] for v in res["variants"].values()])
+        w.cfg.name, [res["kernels"]] + [v["kernels"] for v in res["variants"].values() if "kernels" in v])
     res["config"] = w.config(args)
     return res
 
@@ -451,7 +465,8 @@ def main():
         return
 
     prof_steps = max(2, min(args.steps, 3 if cfg.name == "decoder_rm" else 5))
-    head = run_entry(w, args, args.steps, args.warmup, prof_steps, variants=not args.no_variants)
+    head = run_entry(w, args, args.steps, args.warmup, prof_steps, variants=not args.no_variants,
+                     refinement_variant=not (args.no_variants or args.no_extras))
     mem = w.sc.memory_stats()
     w.sc.set_memory_mode("fixed")   # the workspace the fixed mode would hold for the same settings
     fixed_bytes = w.sc.memory_stats()["work_bytes"]

@@ -27,7 +27,7 @@ EXPORTS = [
     "es_forward_hidden", "es_set_reward_offset", "es_get_reward_offset", "es_calibrate_offset",
     "es_check_device_errors", "es_plan_batches", "es_plan_batches_measured", "es_set_cost_table", "es_pack_offsets", "es_op_layernorm", "es_op_add_layernorm",
     "es_ragged_create", "es_ragged_free", "es_op_softmax", "es_op_attention", "es_op_gemm_bf16", "es_op_gemm_bf16_tile", "es_op_split", "es_op_layernorm_split", "es_op_gemm_split", "es_op_attention_last", "es_last_error",
-    "es_version", "es_set_concurrency", "es_set_batch_grouping", "es_score_best_of_n", "es_set_pruning", "es_set_memory_mode", "es_memory_stats", "es_plan_arena", "es_set_attention", "es_profile_enable", "es_profile_collect", "es_kernel_class_name",
+    "es_version", "es_set_concurrency", "es_set_batch_grouping", "es_score_best_of_n", "es_set_pruning", "es_set_refinement", "es_get_refinement", "es_set_memory_mode", "es_memory_stats", "es_plan_arena", "es_set_attention", "es_profile_enable", "es_profile_collect", "es_kernel_class_name",
 ]
 
 KERNEL_CLASSES = ["embed", "qkv_gemm", "scores", "softmax", "pv", "oproj_gemm", "layernorm",
@@ -84,6 +84,8 @@ _SIGS = {
     "es_set_concurrency": (ctypes.c_int32, [_P, ctypes.c_int32]),
     "es_set_batch_grouping": (ctypes.c_int32, [_P, ctypes.c_int32]),
     "es_set_pruning": (ctypes.c_int32, [_P, ctypes.c_int32]),
+    "es_set_refinement": (ctypes.c_int32, [_P, ctypes.c_int32]),
+    "es_get_refinement": (ctypes.c_int32, [_P, ctypes.POINTER(ctypes.c_int32)]),
     "es_set_attention": (ctypes.c_int32, [_P, ctypes.c_int32]),
     "es_get_reward_offset": (ctypes.c_int32, [_P, ctypes.POINTER(ctypes.c_float)]),
     "es_calibrate_offset": (ctypes.c_int32, [_P, _P, _I32P, ctypes.c_int32, _P, ctypes.POINTER(ctypes.c_float)]),

@@ -273,6 +273,17 @@ class Scorer:
         """Last layer on the last tokens only (default on; es_set_pruning)."""
         check(self.lib, self.lib.es_set_pruning(self.handle, 1 if enabled else 0))
 
+    def set_refinement(self, enabled):
+        """Last-token refinement of the reward rows (es_set_refinement; default on
+        where the model supports it)."""
+        check(self.lib, self.lib.es_set_refinement(self.handle, 1 if enabled else 0))
+
+    def refinement(self):
+        """Whether the last-token refinement runs (es_get_refinement)."""
+        v = ctypes.c_int32()
+        check(self.lib, self.lib.es_get_refinement(self.handle, ctypes.byref(v)))
+        return bool(v.value)
+
     MEMORY_MODES = {"fixed": 0, "length_aware": 1, "exact": 2}
 
     def set_memory_mode(self, mode):

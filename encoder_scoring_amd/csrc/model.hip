@@ -75,8 +75,10 @@ struct es_model {
   // capacity
   int64_t max_tokens = 0, Tcap = 0, score_cap = 0;
   int attn_mode = 0;  // 0: scores -> softmax -> P.V, 1: fused (the bf16 default, set in build)
-  // last-token refinement of the reward rows (pre-LN bf16 models, set in build)
-  bool refine = false;
+  // last-token refinement of the reward rows: refine_ok where the model
+  // supports it (pre-LN bf16, set in build), refine whether it runs
+  // (es_set_refinement, default refine_ok)
+  bool refine_ok = false, refine = false;
   int max_seqs = 0;
   int device = 0;
   // weights
@@ -242,7 +244,7 @@ double ms_since(const std::chrono::steady_clock::time_point &t0) {
 // rows (hi + lo bf16 pairs); sequences are counted in whole tiles of 32
 // (refine_rows) since the split GEMMs read their operands tile by tile.
 int64_t refine_floats(const es_model *m) {
-  return m->refine ? (int64_t)2 * m->H + m->Nqkv + m->Kc + m->Fp : 0;
+  return m->refine_ok ? (int64_t)2 * m->H + m->Nqkv + m->Kc + m->Fp : 0;
 }
 
 int64_t refine_bytes(const es_model *m, int64_t n_seqs) {
@@ -301,11 +303,11 @@ es_status alloc_workspace(es_model *m, es_model::Workspace &w, int scale) {
   if ((s = dalloc(m, &w.hmid, T * m->Fp * act)) != ES_OK) return s;
   if ((s = dalloc(m, (void **)&w.S, S * 4)) != ES_OK) return s;
   if ((s = dalloc(m, &w.Pb, S * act)) != ES_OK) return s;
-  if (m->refine &&
+  if (m->refine_ok &&
       (s = dalloc(m, (void **)&w.ref, refine_bytes(m, (int64_t)scale * m->max_seqs))) != ES_OK)
     return s;
   w.scale = scale;
-  m->work_allocs += m->refine ? 9 : 8;
+  m->work_allocs += m->refine_ok ? 9 : 8;
   m->work_alloc_ms += ms_since(t0);
   m->peak_work = std::max(m->peak_work, work_bytes(m));
   return ES_OK;
@@ -339,7 +341,7 @@ std::vector<es::Usage> pass_usage(const es_model *m, int64_t rows, int64_t score
   u[kTHmid] = {rows * m->Fp * act, 7, 8};
   u[kTS] = {score_elems * 4, 3, 3};
   u[kTP] = {score_elems * act, 3, 3};
-  u[kTRef] = {refine_bytes(m, n_seqs), 0, 10};  // the pass's refinement rows
+  u[kTRef] = {m->refine ? refine_bytes(m, n_seqs) : 0, 0, 10};  // the pass's refinement rows
   return u;
 }
 
@@ -441,8 +443,9 @@ es_status build(const es::ParsedBlob &pb, int64_t max_tokens, int32_t max_seqs, 
   m->causal = h.causal != 0;
   m->bf16 = h.wdtype == 1;
   m->attn_mode = m->bf16 ? 1 : 0;
-  m->refine = m->bf16 && m->pre_ln && h.hidden % 64 == 0 && h.ffn % 64 == 0 &&
-              h.max_pos <= es::kLastMaxKeysHost;
+  m->refine_ok = m->bf16 && m->pre_ln && h.hidden % 64 == 0 && h.ffn % 64 == 0 &&
+                 h.max_pos <= es::kLastMaxKeysHost;
+  m->refine = m->refine_ok;
   m->eps = h.eps;
   m->offset = h.reward_offset;
   m->Hp = (int)round_up(m->H, 64);
@@ -1256,6 +1259,22 @@ extern "C" es_status es_set_pruning(es_model *m, int32_t enabled) {
   if (!m) return fail(ES_ERR_ARG, "model handle is NULL");
   if (enabled != 0 && enabled != 1) return fail(ES_ERR_ARG, "enabled=%d (0 or 1)", enabled);
   m->prune = enabled != 0;
+  return ES_OK;
+}
+
+extern "C" es_status es_set_refinement(es_model *m, int32_t enabled) {
+  if (!m) return fail(ES_ERR_ARG, "model handle is NULL");
+  if (enabled != 0 && enabled != 1) return fail(ES_ERR_ARG, "enabled=%d (0 or 1)", enabled);
+  if (enabled && !m->refine_ok)
+    return fail(ES_ERR_ARG, "the last-token refinement needs a pre-LN bf16 model with hidden and FFN "
+                            "widths multiples of 64 and max_pos <= %d", es::kLastMaxKeysHost);
+  m->refine = enabled != 0;
+  return ES_OK;
+}
+
+extern "C" es_status es_get_refinement(const es_model *m, int32_t *enabled) {
+  if (!m || !enabled) return fail(ES_ERR_ARG, "NULL argument");
+  *enabled = m->refine ? 1 : 0;
   return ES_OK;
 }
 

@@ -319,6 +319,21 @@ es_status es_memory_stats(es_model *m, es_memory_stats_t *out, int32_t reset);
 es_status es_set_pruning(es_model *m, int32_t enabled);
 
 /*
+ * es_set_refinement / es_get_refinement -- the last-token refinement of the
+ * scoring entry points (es_score_batch: the reward row of each sequence
+ * carried in fp32 with hi + lo bf16 GEMM operands).  On by default wherever
+ * the model supports it: pre-LN bf16 models with hidden and FFN widths
+ * multiples of 64 and max_pos <= 4096.  0 turns it off: rewards then carry
+ * the bf16 pass's operand rounding (on the 24-layer decoder up to 1.5e-2
+ * from the float64 reference, against 7.3e-3 with it), and the scoring pass
+ * is about 4 % faster there.  Takes effect from the next call.
+ * Errors: ES_ERR_ARG (enabled not 0 / 1, or 1 on a model that does not
+ * support it).
+ */
+es_status es_set_refinement(es_model *m, int32_t enabled);
+es_status es_get_refinement(const es_model *m, int32_t *enabled);
+
+/*
  * es_set_batch_grouping -- number of consecutive planned batches (1..8,
  * default 1) that es_score_requests packs back to back and scores in one
  * pass through the layers.  The planner's batches stay as planned

@@ -327,3 +327,36 @@ def test_fused_attention_hidden_states():
     got = sc.hidden(torch.from_numpy(ids).cuda(), offsets_of(lengths), 1).cpu().numpy()
     want = np.concatenate([m.hidden(s, 1) for s in split(ids, lengths)])
     assert np.max(np.abs(got - want)) < 0.05 * max(1.0, float(np.max(np.abs(want))))
+
+
+def test_refinement_switch_and_effect():
+    """The last-token refinement: on by default for a pre-LN bf16 model and
+    refused for a post-LN one; with it the rewards sit closer to the float64
+    oracle (the reward rows carry no bf16 operand rounding) than the bf16
+    pass's own (es_set_refinement(0)), both within the bf16 bar, and pruning
+    gives the same bits either way."""
+    torch = need_gpu()
+    cfg = mini("dec_bf16_deep", True, True, True, H=256, A=2, F=1024, L=8, V=1000, P=300)
+    w = make_weights(cfg)
+    ids, lengths = random_stream(21, 24, 20, 250, cfg.vocab)
+    sc = scorer_for(cfg, w)
+    assert sc.refinement()
+    want = oracle.OracleModel(cfg, w).score_many(split(ids, lengths), 0.0)
+    errs = {}
+    for on in (True, False):
+        sc.set_refinement(on)
+        assert sc.refinement() == on
+        got = gpu_score(torch, sc, ids, lengths)
+        sc.set_pruning(False)
+        assert np.array_equal(gpu_score(torch, sc, ids, lengths), got)
+        sc.set_pruning(True)
+        errs[on] = np.abs(got - want)
+        say("refinement", on, "max", float(errs[on].max()), "mean", float(errs[on].mean()))
+        assert errs[on].max() <= BF16_TOL
+    assert errs[True].max() < errs[False].max() and errs[True].mean() < errs[False].mean()
+    enc = CASES[4][1]
+    sc2 = scorer_for(enc, make_weights(enc))
+    assert not sc2.refinement()
+    sc2.set_refinement(False)
+    with pytest.raises(EncScoreError):
+        sc2.set_refinement(True)
