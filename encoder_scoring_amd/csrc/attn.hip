@@ -958,7 +958,7 @@ hipError_t launch_attn_last(const uint16_t *qkv, int ldq, const float *ql, int l
                             int dp, float scale, const Ragged &r, uint16_t *ctx, int kc,
                             hipStream_t st) {
   if (r.n_seqs <= 0) return hipSuccess;
-  if ((int64_t)r.n_seqs * n_heads > INT32_MAX) return hipErrorInvalidValue;
+  if ((int64_t)r.n_seqs * n_heads > INT32_MAX || r.max_len > kLastMaxKeys) return hipErrorInvalidValue;
   if ((r.plen != nullptr) != (r.pref != nullptr) || r.max_len <= 0 || kc < n_heads * dp || kc % 16 ||
       ldl < 3 * n_heads * dp)
     return hipErrorInvalidValue;

@@ -128,8 +128,9 @@ hipError_t launch_attn_fused(const uint16_t *qkv, int ldq, int n_heads, int dp, 
 // the bulk bf16 qkv rows (shared-prompt rows first) -- into row i of ctx in
 // the split-operand layout with K = kc (a multiple of 16); columns
 // [n_heads dp, kc) zeroed.  Every sequence (prompt included) at most
-// kLastMaxKeys positions.
-constexpr int kLastMaxKeysHost = 4096;
+// kLastMaxKeysHost positions (the weight blob's max_pos limit); a layout
+// whose longest own sequence is longer is refused.
+constexpr int kLastMaxKeysHost = 1024;
 hipError_t launch_attn_last(const uint16_t *qkv, int ldq, const float *ql, int ldl, int n_heads,
                             int dp, float scale, const Ragged &r, uint16_t *ctx, int kc,
                             hipStream_t st);

@@ -443,8 +443,8 @@ es_status build(const es::ParsedBlob &pb, int64_t max_tokens, int32_t max_seqs, 
   m->causal = h.causal != 0;
   m->bf16 = h.wdtype == 1;
   m->attn_mode = m->bf16 ? 1 : 0;
-  m->refine_ok = m->bf16 && m->pre_ln && h.hidden % 64 == 0 && h.ffn % 64 == 0 &&
-                 h.max_pos <= es::kLastMaxKeysHost;
+  static_assert(es::kLastMaxKeysHost >= es::kMaxPos, "the last-token attention holds every position");
+  m->refine_ok = m->bf16 && m->pre_ln && h.hidden % 64 == 0 && h.ffn % 64 == 0;
   m->refine = m->refine_ok;
   m->eps = h.eps;
   m->offset = h.reward_offset;
@@ -1267,7 +1267,7 @@ extern "C" es_status es_set_refinement(es_model *m, int32_t enabled) {
   if (enabled != 0 && enabled != 1) return fail(ES_ERR_ARG, "enabled=%d (0 or 1)", enabled);
   if (enabled && !m->refine_ok)
     return fail(ES_ERR_ARG, "the last-token refinement needs a pre-LN bf16 model with hidden and FFN "
-                            "widths multiples of 64 and max_pos <= %d", es::kLastMaxKeysHost);
+                            "widths multiples of 64");
   m->refine = enabled != 0;
   return ES_OK;
 }

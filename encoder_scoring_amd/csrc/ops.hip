@@ -244,6 +244,9 @@ extern "C" es_status es_op_attention_last(const es_ragged *r, const uint16_t *d_
       ld_ql < 3 * width || kc < width || kc % 16 || !(scale > 0.f))
     return fail(ES_ERR_ARG, "es_op_attention_last: head_dim=%d ld_qkv=%d ld_ql=%d kc=%d scale=%g (n_heads=%d)",
                 head_dim, ld_qkv, ld_ql, kc, (double)scale, r->n_heads);
+  if (r->r.max_len > es::kLastMaxKeysHost)
+    return fail(ES_ERR_RANGE, "es_op_attention_last: a sequence of %d tokens (at most %d)", r->r.max_len,
+                es::kLastMaxKeysHost);
   HIP_TRY(es::launch_attn_last(d_qkv, ld_qkv, d_ql, ld_ql, r->n_heads, head_dim, scale, r->r,
                                d_ctx_split, kc, static_cast<hipStream_t>(stream)));
   return ES_OK;

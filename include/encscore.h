@@ -127,7 +127,7 @@ es_status es_blob_info(const void *h_blob, int64_t nbytes, es_model_info_t *info
  *
  * Precision: bf16 models run every row with bf16 GEMM operands and fp32
  * accumulation.  For pre-LN bf16 models (hidden and FFN widths multiples of
- * 64, max_pos <= 4096) the last row of each sequence -- the only one the
+ * 64) the last row of each sequence -- the only one the
  * reward reads -- is also carried through every layer in fp32 beside that
  * pass, its GEMM operands split into hi + lo bf16 pairs and its attention
  * in fp32 over the pass's keys and values (the last-token refinement
@@ -323,7 +323,7 @@ es_status es_set_pruning(es_model *m, int32_t enabled);
  * scoring entry points (es_score_batch: the reward row of each sequence
  * carried in fp32 with hi + lo bf16 GEMM operands).  On by default wherever
  * the model supports it: pre-LN bf16 models with hidden and FFN widths
- * multiples of 64 and max_pos <= 4096.  0 turns it off: rewards then carry
+ * multiples of 64.  0 turns it off: rewards then carry
  * the bf16 pass's operand rounding (on the 24-layer decoder up to 1.5e-2
  * from the float64 reference, against 7.3e-3 with it), and the scoring pass
  * is about 4 % faster there.  Takes effect from the next call.
@@ -669,7 +669,8 @@ es_status es_op_gemm_split(const uint16_t *d_a, const uint16_t *d_w, const float
  * [T, ld_qkv], ld_qkv a multiple of 8).  Row i of d_ctx_split, in the
  * split-operand layout with K = kc (>= n_heads d, a multiple of 16), gets
  * columns [0, n_heads d) and zeros in [n_heads d, kc).  head_dim 32, 64 or
- * 128.  Errors: ES_ERR_ARG, ES_ERR_HIP. */
+ * 128; sequences of at most 1024 tokens.
+ * Errors: ES_ERR_ARG, ES_ERR_RANGE (a longer sequence), ES_ERR_HIP. */
 es_status es_op_attention_last(const es_ragged *r, const uint16_t *d_qkv, int32_t ld_qkv,
                                const float *d_ql, int32_t ld_ql, int32_t head_dim, float scale,
                                uint16_t *d_ctx_split, int32_t kc, void *stream);

@@ -360,3 +360,26 @@ def test_refinement_switch_and_effect():
     sc2.set_refinement(False)
     with pytest.raises(EncScoreError):
         sc2.set_refinement(True)
+
+
+@pytest.mark.parametrize("attention", ["unfused", "fused"])
+def test_refinement_at_the_longest_sequences(attention):
+    """A pre-LN bf16 model at max_pos = 1024 (the weight format's limit, which
+    the last-token attention holds): a 1024-token sequence next to 1-token and mid-length
+    ones, rewards against the oracle within the bf16 bar, and bitwise the same
+    when each sequence is scored alone."""
+    torch = need_gpu()
+    cfg = mini("dec_long", True, True, True, H=128, A=2, F=256, V=500, P=1024)
+    w = make_weights(cfg)
+    lengths = np.array([1024, 1, 333, 700, 2], dtype=np.int32)
+    rng = np.random.default_rng(44)
+    ids = rng.integers(0, cfg.vocab, size=int(lengths.sum())).astype(np.int32)
+    sc = scorer_for(cfg, w, max_tokens=4096, max_seqs=16)
+    assert sc.refinement()
+    sc.set_attention(attention)
+    got = gpu_score(torch, sc, ids, lengths)
+    want = oracle.OracleModel(cfg, w).score_many(split(ids, lengths), 0.0)
+    say("dec_long", attention, "max |d reward| =", float(np.max(np.abs(got - want))))
+    assert np.max(np.abs(got - want)) <= BF16_TOL
+    for i, s in enumerate(split(ids, lengths)):
+        assert gpu_score(torch, sc, s, np.array([s.size], dtype=np.int32))[0] == got[i]

@@ -21,7 +21,7 @@ import numpy as np
 import pytest
 
 import oracle
-from encoder_scoring_amd import RaggedScores, attention_last, gemm_split, layernorm_split, split_rows
+from encoder_scoring_amd import EncScoreError, RaggedScores, attention_last, gemm_split, layernorm_split, split_rows
 from helpers import bits_to_f64, f32_to_bf16_bits, need_gpu, say, split_decode
 
 pytestmark = pytest.mark.gpu
@@ -145,7 +145,7 @@ def test_layernorm_split(rows, cols):
 
 
 @pytest.mark.parametrize("head_dim", [32, 64, 128])
-@pytest.mark.parametrize("lengths", [[1, 5, 40], [300, 77, 1, 1030]])
+@pytest.mark.parametrize("lengths", [[1, 5, 40], [300, 77, 1, 1024]])
 def test_attention_last(head_dim, lengths):
     torch = need_gpu()
     A = 3
@@ -180,3 +180,14 @@ def test_attention_last(head_dim, lengths):
             assert np.all(err <= 2.0 ** -16 * np.abs(want) + 1e-5 * np.abs(V).max()), (i, h, err.max())
         t0 += L
     assert np.all(got[:, width:] == 0.0)
+
+
+def test_attention_last_refuses_longer_sequences():
+    torch = need_gpu()
+    rag = RaggedScores(np.array([3, 1025], dtype=np.int32), 2, 1)
+    qkv = torch.zeros((1028, 3 * 64), dtype=torch.int16, device="cuda")
+    ql = torch.zeros((2, 3 * 64), dtype=torch.float32, device="cuda")
+    out = torch.zeros(2 * 32 * 64, dtype=torch.int16, device="cuda")
+    with pytest.raises(EncScoreError, match="ES_ERR_RANGE"):
+        attention_last(rag, qkv, ql, out, 32, 64)
+    rag.close()
