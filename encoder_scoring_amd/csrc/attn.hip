@@ -754,9 +754,10 @@ __global__ __launch_bounds__(kLastThreads) void attn_last_kernel(
   // sequences of one head run together on one XCD: a shared prompt's keys
   // and values then come from that XCD's L2 for all its candidates
   const int item = xcd_contiguous(blockIdx.x, gridDim.x);
-  // sequences from the last packed row back: the layer's QKV GEMM wrote those
-  // rows last, so their keys and values are the likeliest still in the MALL
-  const int n_seqs = gridDim.x / n_heads, seq = n_seqs - 1 - item % n_seqs, h = item / n_seqs;
+  // sequences in packed order: the bulk attention, which runs just before
+  // and walks the longest first, read the first (shortest, the plan being
+  // sorted) last, so their keys and values are the likeliest still in the MALL
+  const int n_seqs = gridDim.x / n_heads, seq = item % n_seqs, h = item / n_seqs;
   const int t = threadIdx.x;
   const int c = t % CH, g = t / CH, lane = t % kWave, wv = t / kWave;
   const int t0 = off[seq], n = off[seq + 1] - off[seq];

@@ -771,16 +771,25 @@ es_status refine_start(es_model *m, Workspace &w, const LastView &lv, hipStream_
 }
 
 // One layer on the refined rows; w.qkv holds this layer's bulk Q | K | V.
+// part 0: the refined rows' LayerNorm and Q | K | V; part 1: their
+// attention over this layer's Q | K | V (w.qkv, still live) and the rest of
+// the layer.  Part 1 runs right after the bulk attention, whose last key
+// reads are then the likeliest still in the MALL.
 es_status refine_layer(es_model *m, Workspace &w, const DevLayer &D, const LastView &lv,
-                       hipStream_t st) {
+                       hipStream_t st, int part) {
   Prof p(m, st, ES_KC_REFINE);
   const int n = lv.tail.n_seqs, H = m->H;
   const RefineRows R = refine_rows(m, w, n);
   const uint16_t *Wq = (const uint16_t *)D.w_qkv, *Wo = (const uint16_t *)D.w_o;
   const uint16_t *W1 = (const uint16_t *)D.w_1, *W2 = (const uint16_t *)D.w_2;
-  HIP_TRY(es::launch_layernorm_split(R.x, D.ln1_g, D.ln1_b, n, H, m->eps, R.u, st));
-  HIP_TRY(es::launch_gemm_split(R.u, Wq, D.b_qkv, nullptr, R.q, nullptr, m->Nqkv, n, m->Nqkv, H,
-                                es::kEpiF32, st));
+  const double Hd = (double)m->A * m->d, F = m->F, pr = (double)lv.pairs;
+  if (part == 0) {
+    HIP_TRY(es::launch_layernorm_split(R.x, D.ln1_g, D.ln1_b, n, H, m->eps, R.u, st));
+    HIP_TRY(es::launch_gemm_split(R.u, Wq, D.b_qkv, nullptr, R.q, nullptr, m->Nqkv, n, m->Nqkv, H,
+                                  es::kEpiF32, st));
+    p.done(2.0 * n * 3.0 * H * Hd * 2.0, 2.0 * 3.0 * H * Hd + 4.0 * n * (3.0 * H + 3.0 * Hd));
+    return ES_OK;
+  }
   HIP_TRY(es::launch_attn_last((const uint16_t *)w.qkv, m->Nqkv, R.q, m->Nqkv, m->A, m->dp,
                                1.0f / std::sqrt((float)m->d), lv.attn, R.c, m->Kc, st));
   HIP_TRY(es::launch_gemm_split(R.c, Wo, D.b_o, R.x, R.x, nullptr, H, n, H, m->Kc, es::kEpiResidual, st));
@@ -789,9 +798,8 @@ es_status refine_layer(es_model *m, Workspace &w, const DevLayer &D, const LastV
   HIP_TRY(es::launch_gemm_split(R.h, W2, D.b_2, R.x, R.x, nullptr, H, n, H, m->Fp, es::kEpiResidual, st));
   // bytes: the layer's bf16 weights once, the bf16 K and V of every
   // (last query, key, head) once, and the fp32 rows each step reads and writes
-  const double Hd = (double)m->A * m->d, F = m->F, pr = (double)lv.pairs;
-  p.done(2.0 * n * (4.0 * H * Hd + 2.0 * H * F) + 4.0 * m->d * pr,
-         2.0 * (4.0 * H * Hd + 2.0 * H * F) + 4.0 * m->d * pr + 4.0 * n * (10.0 * H + 8.0 * Hd + 2.0 * F));
+  p.done(2.0 * n * (H * Hd + 2.0 * H * F) * 2.0 + 4.0 * m->d * pr,
+         2.0 * (H * Hd + 2.0 * H * F) + 4.0 * m->d * pr + 4.0 * n * (7.0 * H + 5.0 * Hd + 2.0 * F));
   return ES_OK;
 }
 
@@ -853,10 +861,11 @@ es_status forward(es_model *m, Workspace &w, const int32_t *d_ids, const es::Rag
       if ((s = layernorm(m, w, w.x, D.ln1_g, D.ln1_b, T, nullptr, st)) != ES_OK) return s;
       if ((s = gemm(m, ES_KC_QKV, w.xb, m->Hp, D.w_qkv, D.b_qkv, nullptr, w.qkv, m->Nqkv, T,
                     m->Nqkv, m->Hp, H, es::kEpiBias, st)) != ES_OK) return s;
-      // before anything of the bulk layer may reuse the Q | K | V memory
-      if (refine && (s = refine_layer(m, w, D, *last, st)) != ES_OK) return s;
+      if (refine && (s = refine_layer(m, w, D, *last, st, 0)) != ES_OK) return s;
       if (!tail) {
         if ((s = attention(m, w, r, pairs, st)) != ES_OK) return s;
+        // before anything of the bulk layer may reuse the Q | K | V memory
+        if (refine && (s = refine_layer(m, w, D, *last, st, 1)) != ES_OK) return s;
         if ((s = gemm(m, ES_KC_OPROJ, w.ctx, m->Kc, D.w_o, D.b_o, w.x, w.x, H, T, H, m->Kc, Hd,
                       es::kEpiResidual, st)) != ES_OK) return s;
         if ((s = layernorm(m, w, w.x, D.ln2_g, D.ln2_b, T, nullptr, st)) != ES_OK) return s;
@@ -864,7 +873,9 @@ es_status forward(es_model *m, Workspace &w, const int32_t *d_ids, const es::Rag
                       H, es::kEpiGelu, st, F)) != ES_OK) return s;
         if ((s = gemm(m, ES_KC_FFN2, w.hmid, m->Fp, D.w_2, D.b_2, w.x, w.x, H, T, H, m->Fp, F,
                       es::kEpiResidual, st)) != ES_OK) return s;
-      } else if (!refine) {  // refined: the last rows are already done
+      } else if (refine) {  // the refined rows carry the pruned last layer
+        if ((s = refine_layer(m, w, D, *last, st, 1)) != ES_OK) return s;
+      } else {
         const int n = last->tail.n_seqs;
         if ((s = attention(m, w, fused ? last->attn : r, fused ? last->pairs : pairs, st)) != ES_OK) return s;
         if ((s = gather_last(m, w, *last, st)) != ES_OK) return s;  // x -> y, ctx -> qkv
