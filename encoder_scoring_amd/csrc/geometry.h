@@ -37,11 +37,13 @@ constexpr int kPfxMinPrompt = 64;
 // scores: rows are grouped by lane count -- q < 64 on 8 lanes, then 16, 32
 // and 64 lanes up to 512 scores -- so a lane group is at least half used, and
 // an item never crosses a head or a lane-count boundary.  Causal rows of 513
-// to 1024 scores take 32 lanes and three or four chunks each (70 % of the
-// lanes' slots used at 540 scores, against 53 % for 64 lanes and two
-// chunks, and two rows per wavefront instead of one); longer causal rows
-// 64 lanes again.  An item is up to kSoftmaxPasses (causal:
-// kSoftmaxPassesCausal) passes of 4 wavefronts x (64 / G) rows.
+// to 1024 scores take G = 128 lanes, two wavefronts of one chunk each,
+// which combine their max and sum through LDS: they stay on the lean
+// one-chunk kernel (as a launch of their own, with three chunks on 32 lanes,
+// those rows were a single round of latency-bound blocks).  Longer causal
+// rows take 64 lanes and several chunks each.  An item is up to
+// kSoftmaxPasses (causal: kSoftmaxPassesCausal) passes of the block's 4
+// wavefronts, 256 / G rows per pass.
 constexpr int kSoftmaxPasses = 2;
 constexpr int kSoftmaxPassesCausal = 8;
 ES_HD inline int softmax_lanes(int m) {
@@ -51,7 +53,7 @@ ES_HD inline int softmax_lanes(int m) {
   return g;
 }
 ES_HD inline int softmax_row_lanes(int m, bool causal) {
-  if (causal && m > 512 && m <= 1024) return 32;
+  if (causal && m > 512 && m <= 1024) return 128;
   const int g = softmax_lanes(m);
   return causal && g < 8 ? 8 : g;
 }
@@ -68,7 +70,12 @@ ES_HD inline void softmax_causal_class(int q, int n, int &cs, int &ce) {
   if (ce > n) ce = n;
 }
 ES_HD inline int softmax_rows_per_item(int g, bool causal) {
-  return 4 * (64 / g) * (causal ? kSoftmaxPassesCausal : kSoftmaxPasses);
+  return (256 / g) * (causal ? kSoftmaxPassesCausal : kSoftmaxPasses);
+}
+// Items whose rows take one eight-score chunk per lane (at most 512 scores,
+// or a causal row of at most 1024 on two wavefronts) run on the lean kernel.
+ES_HD inline bool softmax_one_chunk(int longest, bool causal) {
+  return longest <= (causal ? 1024 : 512);
 }
 // The rows of one softmax item.  Bidirectional: rows r0 .. r0 + rows - 1
 // of the sequence's A * n rows ([head][query] major).  Causal: rows qs ..
@@ -114,15 +121,14 @@ ES_HD inline SoftmaxItem softmax_item(int r0, int n, int n_heads, bool causal) {
   return it;
 }
 // First rows of the softmax items of one sequence, in order, with whether
-// the item's longest row has more than 512 scores (needs more than one
-// 8-score chunk per lane: such items run on a kernel with more registers,
-// the rest on the lean one).
+// the item's rows need more than one 8-score chunk per lane (such items run
+// on a kernel with more registers, the rest on the lean one).
 template <class F>
 inline void softmax_items(int n, int n_heads, bool causal, F emit) {
   if (!causal) {
     for (int r0 = 0; r0 < n_heads * n;) {
       const SoftmaxItem it = softmax_item(r0, n, n_heads, false);
-      emit(r0, it.longest > 512);
+      emit(r0, !softmax_one_chunk(it.longest, false));
       r0 += it.rows;
     }
     return;
@@ -134,7 +140,7 @@ inline void softmax_items(int n, int n_heads, bool causal, F emit) {
       int q = cs, hc = 1;
       while (q < ce) {
         const SoftmaxItem it = softmax_item(h0 * n + q, n, n_heads, true);
-        emit(h0 * n + q, it.longest > 512);
+        emit(h0 * n + q, !softmax_one_chunk(it.longest, true));
         hc = it.hc;
         q = it.qe;
       }

@@ -483,7 +483,8 @@ int64_t check_pass(const LayoutParams &p, const std::vector<uint8_t> &meta, cons
       }
       const int m = len[seq];
       const SoftmaxItem it = softmax_item(r0, m, A, p.causal);
-      c.expect((k < L.n_sm_narrow) == (it.longest <= 512), "softmax item %d on the wrong kernel", k);
+      c.expect((k < L.n_sm_narrow) == softmax_one_chunk(it.longest, p.causal),
+               "softmax item %d on the wrong kernel", k);
       for (int i = 0; i < it.rows; ++i) {
         int h, q;
         if (p.causal) {

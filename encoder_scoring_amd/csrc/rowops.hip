@@ -226,10 +226,12 @@ __device__ __forceinline__ void store8(float *p, const float (&o)[8]) {
 // consecutive scores per chunk, read as two float4 straight into registers
 // (branch-free: addresses clamped into the row, values past its end masked
 // to -inf); only the chunks the item's longest row needs are touched.  The
-// block walks its rows in passes of 4 wavefronts x (64 / G) rows with the
+// block walks its rows in passes of 256 / G rows (4 wavefronts) with the
 // next pass's loads in flight while the current pass reduces, so a block
 // keeps memory busy through its whole run instead of one round trip per
-// pass.  Max and sum reduce by butterfly shuffles within the G-lane group;
+// pass.  Max and sum reduce by butterfly shuffles within the G-lane group
+// (G = 128: within each of the row's two wavefronts, then across the pair
+// through LDS);
 // each chunk goes out as one 16-byte store, with zeros past the row's last
 // score up to the next multiple of 8 (inside the row's allocated length; no
 // reader looks there).  Rows are addressed through score_row_off, so causal
@@ -272,14 +274,20 @@ __global__ __launch_bounds__(256) void softmax_kernel(const float *__restrict__ 
   const SoftmaxItem it = softmax_item(row0, n, n_heads, causal != 0);
   const int G = it.g;
   const int nj = (it.longest + 8 * G - 1) / (8 * G);  // chunks per lane its longest row needs
-  const int rpw = kWave / G, rpp = 4 * rpw;  // rows per wavefront / per pass
+  // G = 128: a row on two wavefronts (uniform over the block)
+  const bool pair = G > kWave;
+  const int Gw = pair ? kWave : G;            // lanes of a row inside one wavefront
+  const int rpw = kWave / Gw, rpp = 256 / G;  // rows per wavefront / per pass
   const int passes = (it.rows + rpp - 1) / rpp;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
-  const int sub = lane / G, c0 = lane % G;
+  const int sub = lane / Gw, c0 = (pair ? (wave & 1) * kWave : 0) + lane % Gw;
+  const int wrow = pair ? wave >> 1 : wave * rpw + sub;  // the lane's row within a pass
+  // pair exchange: [pass parity][max, sum][wavefront]
+  __shared__ float xch[2][2][4];
   // row i of the item (clamped to its last row for the lanes past it): its
   // valid scores m (0 past the item), start ro and allocated length cap
   auto row_of = [&](int p, int &m, int64_t &ro, int &cap) {
-    const int i = p * rpp + wave * rpw + sub, ic = min(i, it.rows - 1);
+    const int i = p * rpp + wrow, ic = min(i, it.rows - 1);
     int h, q;
     if (causal) {
       const int qn = it.qe - it.qs;
@@ -322,7 +330,12 @@ __global__ __launch_bounds__(256) void softmax_kernel(const float *__restrict__ 
 #pragma unroll
         for (int e = 0; e < 8; ++e) mx = fmaxf(mx, v[h][j][e]);
       }
-      mx = group_max(mx, G);
+      mx = group_max(mx, Gw);
+      if (pair) {  // block-uniform
+        if (lane == 0) xch[p & 1][0][wave] = mx;
+        __syncthreads();
+        mx = fmaxf(mx, xch[p & 1][0][wave ^ 1]);
+      }
       float sum = 0.f;
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
@@ -334,7 +347,13 @@ __global__ __launch_bounds__(256) void softmax_kernel(const float *__restrict__ 
         sum += ((v[h][j][0] + v[h][j][1]) + (v[h][j][2] + v[h][j][3])) +
                ((v[h][j][4] + v[h][j][5]) + (v[h][j][6] + v[h][j][7]));
       }
-      sum = group_sum(sum, G);
+      sum = group_sum(sum, Gw);
+      if (pair) {  // both wavefronts add the same two partial sums
+        if (lane == 0) xch[p & 1][1][wave] = sum;
+        __syncthreads();
+        const float o = xch[p & 1][1][wave ^ 1];
+        sum = (wave & 1) ? o + sum : sum + o;
+      }
       const float inv = 1.0f / sum;  // one correctly rounded reciprocal per row
       PT *pr = P + ro[h];
 #pragma unroll
@@ -482,8 +501,9 @@ hipError_t launch_softmax(bool p_bf16, const float *S, void *P, const Ragged &r,
                           bool causal, hipStream_t st) {
   if (r.n_sm_items <= 0) return hipSuccess;
   const dim3 block(256);
-  // items [0, n_sm_narrow): rows of at most 512 scores, one chunk per lane;
-  // the rest: as many chunks as the longest row needs
+  // items [0, n_sm_narrow): one chunk per lane (rows of at most 512 scores,
+  // causal rows of at most 1024 on two wavefronts); the rest: 64 lanes per
+  // row and as many chunks as the longest row needs
   auto go = [&](auto njc, int first, int count) {
     constexpr int NJ = decltype(njc)::value;
     if (count <= 0) return hipSuccess;
@@ -500,9 +520,7 @@ hipError_t launch_softmax(bool p_bf16, const float *S, void *P, const Ragged &r,
   if (e != hipSuccess) return e;
   const int first = r.n_sm_narrow, count = r.n_sm_items - r.n_sm_narrow;
   const int nc = (r.max_len + 7) / 8;  // eight-score chunks of the longest row
-  // chunks per lane: rows of 64 lanes; causal rows of up to 1024 scores 32
-  int nj = (nc + 63) / 64;
-  if (causal) nj = std::max(nj, (std::min(nc, 128) + 31) / 32);
+  const int nj = (nc + 63) / 64;       // chunks per lane of 64-lane rows
   if (count <= 0) return hipSuccess;
   if (nj <= 2) return go(std::integral_constant<int, 2>{}, first, count);
   if (nj <= 3) return go(std::integral_constant<int, 3>{}, first, count);
