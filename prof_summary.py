@@ -270,7 +270,8 @@ def main():
     t.add_argument("--command", action="append", required=True)
     t.add_argument("--dispatches-per-launch", type=int, default=1,
                    help="kernel dispatches that make one launch of the class (the softmax "
-                        "runs rows of up to 512 scores and longer rows as two dispatches)")
+                        "runs rows of more than one chunk per lane -- bidirectional rows over "
+                        "512 scores, causal rows over 1024 -- as a second dispatch)")
     a = ap.parse_args()
     {"kernels": kernels, "traffic": traffic, "calls": calls, "rowbench": rowbench}[a.mode](a)
 
