@@ -38,11 +38,24 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-# launch settings of the timed configuration (the full-size parity tests
-# run the same ones)
-DEFAULT_GROUP = 5        # planned batches packed into one pass (es_set_batch_grouping)
-DEFAULT_IN_FLIGHT = 2    # passes overlapped on internal streams (es_set_concurrency)
+# launch settings of the timed configuration, per workload (the full-size
+# parity tests run the same ones): planned batches packed into one pass
+# (es_set_batch_grouping) and passes overlapped on internal streams
+# (es_set_concurrency).  The encoders gain from two passes in flight
+# (bert_base_short 71.7 k -> 77.9 k sequences/s); the decoder's passes each
+# fill the GPU with long GEMMs, and one pass at a time of seven planned
+# batches runs fastest (same box: 741 sequences/s at 5 / 2, 755 at 5 / 1,
+# 762 at 7 / 1).
+DEFAULT_GROUP = 5
+DEFAULT_IN_FLIGHT = 2
+LAUNCH = {"decoder_rm": (7, 1)}
 HEADLINE = "decoder_rm"
+
+
+def launch_config(workload):
+    """(planned batches per pass, passes in flight) timed for a workload."""
+    return LAUNCH.get(workload, (DEFAULT_GROUP, DEFAULT_IN_FLIGHT))
+
 
 PEAKS = {  # MI355X published peaks
     "hbm": (8000.0, "GB/s"),
@@ -232,9 +245,11 @@ class Workload:
             roff = np.concatenate([[0], np.cumsum(rlen)]).astype(np.int32)
             sc.reward_offset = sc.calibrate_offset(d_ref, roff)   # reference set averages zero
         sc.set_memory_mode(args.memory)
-        sc.set_grouping(args.group)
-        sc.set_concurrency(args.in_flight)
-        self.in_flight = args.in_flight
+        per_pass, in_flight = launch_config(name)
+        self.group = args.group if args.group is not None else per_pass
+        self.in_flight = args.in_flight if args.in_flight is not None else in_flight
+        sc.set_grouping(self.group)
+        sc.set_concurrency(self.in_flight)
         self.attention = ("fused" if best_of_n else args.attention) if cfg.bf16 else "unfused"
         if cfg.bf16:
             sc.set_attention(self.attention)
@@ -275,6 +290,12 @@ class Workload:
                 "tokens_per_s": round(self.n_tokens / (ms / 1e3), 1),
                 "step_ms": step_stats(per_step)}
 
+    def profile_name(self):
+        """Name of the committed counter profiles of this stream: the shared-
+        prompt form runs other passes than the plain stream, so it has its own
+        (traffic_<class>_decoder_rm_best_of_n.txt)."""
+        return self.cfg.name + ("_best_of_n" if self.best_of_n else "")
+
     def profile(self, steps):
         """Per-class kernel times: one pass in flight so each kernel runs alone,
         every launch bracketed by HIP events on the stream it runs on."""
@@ -304,7 +325,7 @@ class Workload:
         peak, unit = PEAKS[key]
         return {"bound": bound, "kernel": dominant, "achieved": round(achieved, 2),
                 "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
-                "traffic": traffic_from_profiles(self.cfg.name, dominant),
+                "traffic": traffic_from_profiles(self.profile_name(), dominant),
                 "avg_launch_ms": round(avg_ms, 5), "launches_per_step": launches,
                 "measured": f"HIP events around every launch over {prof_steps} steps with one "
                             f"pass in flight ({ms_isolated:.2f} ms/step)"}
@@ -334,8 +355,8 @@ class Workload:
         return {"workload": cfg.name, "description": WORKLOAD_DESC[cfg.name],
                 "requests": self.n, "tokens": self.n_tokens, "batches": st["n_batches"],
                 "padded_tokens": st["padded_tokens"], "max_tokens": cfg.max_tokens,
-                "batch_overhead": self.c, "batches_per_pass": args.group,
-                "passes_in_flight": args.in_flight, "attention": self.attention,
+                "batch_overhead": self.c, "batches_per_pass": self.group,
+                "passes_in_flight": self.in_flight, "attention": self.attention,
                 "shared_prompts": self.best_of_n, "computed_tokens": st["packed_tokens"]}
 
     def close(self):
@@ -382,7 +403,7 @@ def run_entry(w, args, steps, warmup, prof_steps, variants=True, refinement_vari
         res["variants"]["no_refinement"] = v
         log(f"  no_refinement: {v['value']} seq/s")
     res["row_reductions"] = row_reductions(
-        w.cfg.name, [res["kernels"]] + [v["kernels"] for v in res["variants"].values() if "kernels" in v])
+        w.profile_name(), [res["kernels"]] + [v["kernels"] for v in res["variants"].values() if "kernels" in v])
     res["config"] = w.config(args)
     return res
 
@@ -404,14 +425,15 @@ def main():
                     help="one warm-up call and one step, then exit (for counter collection)")
     ap.add_argument("--attention", default="fused", choices=["unfused", "fused"],
                     help="attention as scores + softmax row reduction + P.V, or one fused kernel")
-    ap.add_argument("--in-flight", type=int, default=DEFAULT_IN_FLIGHT,
-                    help="passes overlapped on internal streams (es_set_concurrency)")
+    ap.add_argument("--in-flight", type=int, default=None,
+                    help="passes overlapped on internal streams (es_set_concurrency); "
+                         "default: the workload's timed configuration (launch_config)")
     ap.add_argument("--best-of-n", action="store_true",
                     help="decoder_rm only: score through es_score_best_of_n (each prompt run once "
                          "for its candidates) instead of prompt + candidate sequences")
-    ap.add_argument("--group", type=int, default=DEFAULT_GROUP,
+    ap.add_argument("--group", type=int, default=None,
                     help="planned batches packed into one pass through the layers "
-                         "(es_set_batch_grouping)")
+                         "(es_set_batch_grouping); default: the workload's timed configuration")
     ap.add_argument("--cost-model", default="linear", choices=["linear", "measured"],
                     help="planner cost of a batch: overhead + |B| * max_len, or a table measured "
                          "on this GPU before the run (es_set_cost_table)")

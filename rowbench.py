@@ -5,8 +5,9 @@ on one pass of a workload's planned stream.
     python rowbench.py [--workload decoder_rm] [--reps 20] [--mode both|warm|cold]
 
 The pass: the DP plan of the workload's request stream split, as the
-library splits it, into ceil(nb / 5) passes of as equal a planned-batch count
-as possible (bench.py's grouping), and of those the one with the most
+library splits it, into ceil(nb / G) passes of as equal a planned-batch count
+as possible (G from bench.py's timed configuration of the workload), and of
+those the one with the most
 visible score pairs (the plan is sorted by length, so that is the pass of
 the longest sequences: the one that dominates the Softmax's time).
 Softmax runs es_op_softmax over that pass's ragged score layout (causal or
@@ -32,7 +33,6 @@ import sys
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-GROUP = 5          # planned batches per pass (bench.py's DEFAULT_GROUP)
 FLUSH_MIB = 1024   # bytes copied between cold launches (4x the 256 MB MALL)
 
 
@@ -43,7 +43,9 @@ def pass_lengths(cfg):
     _, lengths, _ = make_requests(cfg)
     order, starts, _ = plan_batches(lengths, cfg.max_tokens, cfg.batch_overhead)
     nb = len(starts) - 1
-    groups = np.array_split(np.arange(nb), -(-nb // GROUP))
+    from bench import launch_config
+    group = launch_config(cfg.name)[0]
+    groups = np.array_split(np.arange(nb), -(-nb // group))
     srt = np.asarray(lengths)[order]
 
     def pairs(ls):

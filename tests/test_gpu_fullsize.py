@@ -25,7 +25,7 @@ import numpy as np
 import pytest
 
 import oracle
-from bench import DEFAULT_GROUP, DEFAULT_IN_FLIGHT
+from bench import launch_config
 from encoder_scoring_amd import Scorer, blob
 from helpers import need_gpu, offsets_of, say
 from synth import get_config, make_fixed_batch, make_requests, make_weights
@@ -52,8 +52,9 @@ def weights_of(name):
 
 def _stream(torch, cfg, w, ids, lengths, attention):
     sc = Scorer(blob.to_bytes(cfg, w, 0.0), cfg.max_tokens, min(cfg.max_tokens, 65536))
-    sc.set_grouping(DEFAULT_GROUP)
-    sc.set_concurrency(DEFAULT_IN_FLIGHT)
+    group, in_flight = launch_config(cfg.name)
+    sc.set_grouping(group)
+    sc.set_concurrency(in_flight)
     if cfg.bf16:
         sc.set_attention(attention)
     d = torch.from_numpy(ids).cuda()

@@ -9,7 +9,10 @@ import ctypes
 import numpy as np
 import pytest
 
-from bench import DEFAULT_GROUP
+from bench import DEFAULT_GROUP, LAUNCH
+
+# every grouping a timed configuration uses, and the edges
+GROUPS = sorted({1, 2, DEFAULT_GROUP, 8} | {g for g, _ in LAUNCH.values()})
 from encoder_scoring_amd import _lib, blob, check_plan
 from encoder_scoring_amd._lib import ES_ERR_CAPACITY, ES_ERR_FORMAT, ES_ERR_RANGE, EncScoreError
 from synth import get_config, make_fixed_batch, make_requests, make_weights
@@ -22,7 +25,7 @@ def _shape(cfg):
                 max_tokens=cfg.max_tokens, max_seqs=min(cfg.max_tokens, 65536))
 
 
-@pytest.mark.parametrize("group", [1, 2, DEFAULT_GROUP, 8])
+@pytest.mark.parametrize("group", GROUPS)
 @pytest.mark.parametrize("name", ORDERED)
 def test_every_workload_plan_indexes_inside_its_buffers(name, group):
     cfg = get_config(name)
@@ -35,7 +38,7 @@ def test_every_workload_plan_indexes_inside_its_buffers(name, group):
     assert bad == 0 and passes >= 1 and checked > 100 * lengths.size
 
 
-@pytest.mark.parametrize("group", [1, DEFAULT_GROUP, 8])
+@pytest.mark.parametrize("group", sorted(set(GROUPS) - {2}))
 def test_shared_prompt_plan_indexes_inside_its_buffers(group):
     cfg = get_config("decoder_rm")
     ids, lengths, grp = make_requests(cfg)
