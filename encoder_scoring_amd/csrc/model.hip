@@ -111,6 +111,10 @@ struct es_model {
   int32_t cost_max_batch = 0, cost_max_len = 0;
   bool prune = true;  // last layer on the last token of each sequence only (es_set_pruning)
   hipEvent_t fork_ev = nullptr;
+  // the last-token refinement's own stream (used with one pass in flight)
+  // and the events that order it against the pass's stream
+  hipStream_t ref_stream = nullptr;
+  hipEvent_t ref_fork = nullptr, ref_qkv = nullptr, ref_attn = nullptr, ref_join = nullptr;
   char *static_scratch = nullptr;  // this device's copy of `scratch` (es_score_batch_static)
   float *rew = nullptr;  // raw rewards of a reference set (es_calibrate_offset)
   size_t rew_cap = 0;
@@ -177,6 +181,9 @@ void release(es_model *m) {
   if (m->rew) (void)hipFree(m->rew);
   if (m->meta_ev) (void)hipEventDestroy(m->meta_ev);
   if (m->fork_ev) (void)hipEventDestroy(m->fork_ev);
+  for (hipEvent_t e : {m->ref_fork, m->ref_qkv, m->ref_attn, m->ref_join})
+    if (e) (void)hipEventDestroy(e);
+  if (m->ref_stream) (void)hipStreamDestroy(m->ref_stream);
   for (auto &w : m->ws) {
     if (w.stream) (void)hipStreamDestroy(w.stream);
     if (w.done) (void)hipEventDestroy(w.done);
@@ -492,6 +499,11 @@ es_status build(const es::ParsedBlob &pb, int64_t max_tokens, int32_t max_seqs, 
   if (m->mem_mode == ES_MEM_FIXED && (s = alloc_workspace(m, m->ws[0], 1)) != ES_OK) return s;
   if ((s = dalloc(m, (void **)&m->flag, 4)) != ES_OK) return s;
   HIP_TRY(hipEventCreateWithFlags(&m->meta_ev, hipEventDisableTiming));
+  if (m->refine_ok) {  // default priority (every stream of the library)
+    HIP_TRY(hipStreamCreateWithFlags(&m->ref_stream, hipStreamNonBlocking));
+    for (hipEvent_t *e : {&m->ref_fork, &m->ref_qkv, &m->ref_attn, &m->ref_join})
+      HIP_TRY(hipEventCreateWithFlags(e, hipEventDisableTiming));
+  }
   if ((s = static_scratch_of(m->device, &m->static_scratch)) != ES_OK) return s;
   HIP_TRY(hipDeviceSynchronize());
   return ES_OK;
@@ -776,7 +788,7 @@ es_status refine_start(es_model *m, Workspace &w, const LastView &lv, hipStream_
 // the layer.  Part 1 runs right after the bulk attention, whose last key
 // reads are then the likeliest still in the MALL.
 es_status refine_layer(es_model *m, Workspace &w, const DevLayer &D, const LastView &lv,
-                       hipStream_t st, int part) {
+                       hipStream_t st, int part, hipEvent_t attn_done = nullptr) {
   Prof p(m, st, ES_KC_REFINE);
   const int n = lv.tail.n_seqs, H = m->H;
   const RefineRows R = refine_rows(m, w, n);
@@ -792,6 +804,7 @@ es_status refine_layer(es_model *m, Workspace &w, const DevLayer &D, const LastV
   }
   HIP_TRY(es::launch_attn_last((const uint16_t *)w.qkv, m->Nqkv, R.q, m->Nqkv, m->A, m->dp,
                                1.0f / std::sqrt((float)m->d), lv.attn, R.c, m->Kc, st));
+  if (attn_done) HIP_TRY(hipEventRecord(attn_done, st));  // the last read of w.qkv
   HIP_TRY(es::launch_gemm_split(R.c, Wo, D.b_o, R.x, R.x, nullptr, H, n, H, m->Kc, es::kEpiResidual, st));
   HIP_TRY(es::launch_layernorm_split(R.x, D.ln2_g, D.ln2_b, n, H, m->eps, R.u, st));
   HIP_TRY(es::launch_gemm_split(R.u, W1, D.b_1, nullptr, nullptr, R.h, 0, n, m->Fp, H, es::kEpiGelu, st));
@@ -825,6 +838,23 @@ es_status forward(es_model *m, Workspace &w, const int32_t *d_ids, const es::Rag
   }
   const bool refine = last && m->refine;
   if (refine && (s = refine_start(m, w, *last, st)) != ES_OK) return s;
+  // With one pass in flight the refinement runs on a stream of its own
+  // (rs), beside the pass's compute-bound GEMMs: it touches only its own
+  // rows (the arena region kTRef, live all pass) and reads the bulk Q | K | V
+  // of the layer (w.qkv).  Its attention waits for the layer's QKV GEMM; the
+  // bulk FFN1 GEMM -- the first step that may reuse the Q | K | V memory
+  // (arena steps 7-8 against 2-5), and before the next layer's QKV GEMM --
+  // waits for that attention; the pass's stream waits for the whole side
+  // stream before the head reads the refined rows.  With more passes in
+  // flight they fill each other's gaps, and more streams than the GPU's
+  // hardware queues would serialise, so the refinement stays on the pass's
+  // stream.
+  const bool side = refine && m->lanes == 1 && m->ref_stream;
+  hipStream_t rs = side ? m->ref_stream : st;
+  if (side) {
+    HIP_TRY(hipEventRecord(m->ref_fork, st));  // the gathered rows
+    HIP_TRY(hipStreamWaitEvent(rs, m->ref_fork, 0));
+  }
   for (int l = 0; l < n_layers; ++l) {
     const DevLayer &D = m->layers[l];
     const bool tail = last && prune && l == n_layers - 1;
@@ -861,20 +891,27 @@ es_status forward(es_model *m, Workspace &w, const int32_t *d_ids, const es::Rag
       if ((s = layernorm(m, w, w.x, D.ln1_g, D.ln1_b, T, nullptr, st)) != ES_OK) return s;
       if ((s = gemm(m, ES_KC_QKV, w.xb, m->Hp, D.w_qkv, D.b_qkv, nullptr, w.qkv, m->Nqkv, T,
                     m->Nqkv, m->Hp, H, es::kEpiBias, st)) != ES_OK) return s;
-      if (refine && (s = refine_layer(m, w, D, *last, st, 0)) != ES_OK) return s;
+      if (refine && (s = refine_layer(m, w, D, *last, rs, 0)) != ES_OK) return s;
+      if (side) {  // the layer's bulk Q | K | V
+        HIP_TRY(hipEventRecord(m->ref_qkv, st));
+        HIP_TRY(hipStreamWaitEvent(rs, m->ref_qkv, 0));
+      }
+      if (side && !tail &&
+          (s = refine_layer(m, w, D, *last, rs, 1, m->ref_attn)) != ES_OK) return s;
       if (!tail) {
         if ((s = attention(m, w, r, pairs, st)) != ES_OK) return s;
         // before anything of the bulk layer may reuse the Q | K | V memory
-        if (refine && (s = refine_layer(m, w, D, *last, st, 1)) != ES_OK) return s;
+        if (refine && !side && (s = refine_layer(m, w, D, *last, st, 1)) != ES_OK) return s;
         if ((s = gemm(m, ES_KC_OPROJ, w.ctx, m->Kc, D.w_o, D.b_o, w.x, w.x, H, T, H, m->Kc, Hd,
                       es::kEpiResidual, st)) != ES_OK) return s;
         if ((s = layernorm(m, w, w.x, D.ln2_g, D.ln2_b, T, nullptr, st)) != ES_OK) return s;
+        if (side) HIP_TRY(hipStreamWaitEvent(st, m->ref_attn, 0));  // w.qkv read by rs
         if ((s = gemm(m, ES_KC_FFN1, w.xb, m->Hp, D.w_1, D.b_1, nullptr, w.hmid, m->Fp, T, m->Fp, m->Hp,
                       H, es::kEpiGelu, st, F)) != ES_OK) return s;
         if ((s = gemm(m, ES_KC_FFN2, w.hmid, m->Fp, D.w_2, D.b_2, w.x, w.x, H, T, H, m->Fp, F,
                       es::kEpiResidual, st)) != ES_OK) return s;
       } else if (refine) {  // the refined rows carry the pruned last layer
-        if ((s = refine_layer(m, w, D, *last, st, 1)) != ES_OK) return s;
+        if ((s = refine_layer(m, w, D, *last, rs, 1)) != ES_OK) return s;
       } else {
         const int n = last->tail.n_seqs;
         if ((s = attention(m, w, fused ? last->attn : r, fused ? last->pairs : pairs, st)) != ES_OK) return s;
@@ -888,6 +925,10 @@ es_status forward(es_model *m, Workspace &w, const int32_t *d_ids, const es::Rag
                       es::kEpiResidual, st)) != ES_OK) return s;
       }
     }
+  }
+  if (side) {  // the refined rows, before the head reads them
+    HIP_TRY(hipEventRecord(m->ref_join, rs));
+    HIP_TRY(hipStreamWaitEvent(st, m->ref_join, 0));
   }
   (void)a;
   return ES_OK;
