@@ -848,8 +848,9 @@ es_status forward(es_model *m, Workspace &w, const int32_t *d_ids, const es::Rag
   // stream before the head reads the refined rows.  With more passes in
   // flight they fill each other's gaps, and more streams than the GPU's
   // hardware queues would serialise, so the refinement stays on the pass's
-  // stream.
-  const bool side = refine && m->lanes == 1 && m->ref_stream;
+  // stream; so it does under the profiling hook, whose per-class times are
+  // those of kernels running alone.
+  const bool side = refine && m->lanes == 1 && m->ref_stream && m->prof_mask == 0;
   hipStream_t rs = side ? m->ref_stream : st;
   if (side) {
     HIP_TRY(hipEventRecord(m->ref_fork, st));  // the gathered rows

@@ -257,8 +257,11 @@ es_status es_forward_hidden(es_model *m, const int32_t *d_token_ids, const int32
  * an internal stream forked from and joined back to the caller's stream, so
  * the call stays ordered on that stream.  Batches are still formed by the
  * planner; this only overlaps their kernels to fill the GPU.  Other entry
- * points use one workspace on the caller's stream.  Errors: ES_ERR_ARG,
- * ES_ERR_HIP.
+ * points use one workspace on the caller's stream.  With one batch in
+ * flight, the last-token refinement (es_set_refinement) of a pass runs on an
+ * internal stream of the model's, forked from and joined back to the pass's
+ * stream (the call stays ordered on the caller's stream).  Errors:
+ * ES_ERR_ARG, ES_ERR_HIP.
  */
 es_status es_set_concurrency(es_model *m, int32_t batches_in_flight);
 
@@ -696,7 +699,8 @@ typedef struct {
  * es_profile_enable -- from the next call on, record a HIP event pair on the
  * call's stream around every launch of the classes in `class_mask`
  * (bit ES_KC_x), together with that launch's algorithmic flops and bytes.
- * 0 disables.  Clears earlier records.
+ * While enabled, the last-token refinement runs on the pass's stream, so
+ * each recorded launch runs alone.  0 disables.  Clears earlier records.
  */
 es_status es_profile_enable(es_model *m, uint32_t class_mask);
 
