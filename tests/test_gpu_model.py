@@ -199,7 +199,10 @@ def test_out_of_range_token_sets_device_flag():
 
 @pytest.mark.parametrize("lanes", [2, 3])
 def test_batches_in_flight_match_serial(lanes):
-    """Overlapping planned batches on internal streams changes nothing (bitwise)."""
+    """Overlapping planned batches on internal streams changes nothing (bitwise).
+    The model is a pre-LN bf16 decoder, so this also pins the last-token
+    refinement on its own stream (one pass in flight) against the refinement
+    on the pass's stream (several in flight)."""
     torch = need_gpu()
     cfg = CASES[3][1]
     w = make_weights(cfg)
