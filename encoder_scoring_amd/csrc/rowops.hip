@@ -89,50 +89,66 @@ __device__ __forceinline__ void ln_row(float4 (&v)[NC], int lane, int c4n, int c
 
 // With ADD, the row is x + sub (a residual connection followed by its
 // LayerNorm); y may alias x or sub: a wavefront reads its whole row before
-// it writes any of it.
-template <int NC, typename OutB, bool ADD>
+// it writes any of it, and no other wavefront touches that row.  A
+// wavefront takes R consecutive rows: the affine parameters are loaded once
+// for all of them (per row, at 2048 columns, they were 16 KB of L2 reads
+// beside the row's 8 KB from HBM), and the next row's loads are in flight
+// while the current row is reduced and stored.
+template <int NC, typename OutB, bool ADD, int R>
 __global__ __launch_bounds__(256) void layernorm_kernel(const float *x, const float *sub,
                                                         const float *__restrict__ g,
                                                         const float *__restrict__ b, int64_t rows,
                                                         int cols, float eps, float *y, OutB *yb,
                                                         int ldb, int padc4) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-  if (row >= rows) return;
+  const int64_t r0 = ((int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6)) * R;
+  if (r0 >= rows) return;
   const int c4n = cols >> 2;
-  const float *xr = x + row * cols;
   // every load is issued before any is used, at an in-bounds chunk (lanes
-  // past the row end re-read its last chunk and are zeroed below): loads
-  // under a per-chunk branch made the compiler wait for each chunk's pair
-  // before issuing the next, one memory round trip per chunk
-  float4 v[NC], u[NC], gg[NC], bb[NC];
+  // past the row end re-read its last chunk and are zeroed below) and an
+  // in-bounds row (the row after the last is the last again, never stored):
+  // loads under a per-chunk branch made the compiler wait for each chunk's
+  // pair before issuing the next, one memory round trip per chunk
+  constexpr int NS = R > 1 ? 2 : 1;  // register sets: the current row and the next
+  float4 v[NS][NC], u[NS][NC], gg[NC], bb[NC];
+  auto load_row = [&](int set, int64_t row) {
 #pragma unroll
-  for (int j = 0; j < NC; ++j) {
-    const int c4 = min(lane + kWave * j, c4n - 1);
-    v[j] = load4(xr + 4 * c4);
-    if (ADD) u[j] = load4(sub + row * cols + 4 * c4);
-  }
+    for (int j = 0; j < NC; ++j) {
+      const int c4 = min(lane + kWave * j, c4n - 1);
+      v[set][j] = load4(x + row * cols + 4 * c4);
+      if (ADD) u[set][j] = load4(sub + row * cols + 4 * c4);
+    }
+  };
+  load_row(0, r0);
   ln_load_affine<NC>(gg, bb, lane, c4n, g, b);
 #pragma unroll
-  for (int j = 0; j < NC; ++j) {  // selects, no branches
-    const bool in = lane + kWave * j < c4n;
-    if (ADD) {
-      v[j].x += u[j].x; v[j].y += u[j].y; v[j].z += u[j].z; v[j].w += u[j].w;
-    }
-    v[j].x = in ? v[j].x : 0.f;
-    v[j].y = in ? v[j].y : 0.f;
-    v[j].z = in ? v[j].z : 0.f;
-    v[j].w = in ? v[j].w : 0.f;
-  }
-  ln_apply<NC>(v, gg, bb, lane, c4n, cols, eps);
+  for (int i = 0; i < R; ++i) {
+    const int cur = i % NS;
+    const int64_t row = r0 + i;
+    if (i + 1 < R) load_row((i + 1) % NS, min(row + 1, rows - 1));
+    if (row >= rows) break;  // uniform over the wavefront
+    float4(&w)[NC] = v[cur];
 #pragma unroll
-  for (int j = 0; j < NC; ++j) {
-    const int c4 = lane + kWave * j;
-    if (c4 < c4n) {
-      if (y) store4(y + row * cols + 4 * c4, v[j]);
-      if (yb) store4(yb + row * ldb + 4 * c4, v[j]);
-    } else if (yb && c4 < padc4) {  // zero padding columns of the GEMM input
-      store4(yb + row * ldb + 4 * c4, make_float4(0.f, 0.f, 0.f, 0.f));
+    for (int j = 0; j < NC; ++j) {  // selects, no branches
+      const bool in = lane + kWave * j < c4n;
+      if (ADD) {
+        w[j].x += u[cur][j].x; w[j].y += u[cur][j].y; w[j].z += u[cur][j].z; w[j].w += u[cur][j].w;
+      }
+      w[j].x = in ? w[j].x : 0.f;
+      w[j].y = in ? w[j].y : 0.f;
+      w[j].z = in ? w[j].z : 0.f;
+      w[j].w = in ? w[j].w : 0.f;
+    }
+    ln_apply<NC>(w, gg, bb, lane, c4n, cols, eps);
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      const int c4 = lane + kWave * j;
+      if (c4 < c4n) {
+        if (y) store4(y + row * cols + 4 * c4, w[j]);
+        if (yb) store4(yb + row * ldb + 4 * c4, w[j]);
+      } else if (yb && c4 < padc4) {  // zero padding columns of the GEMM input
+        store4(yb + row * ldb + 4 * c4, make_float4(0.f, 0.f, 0.f, 0.f));
+      }
     }
   }
 }
@@ -449,17 +465,31 @@ hipError_t launch_layernorm(bool act_bf16, const float *x, const float *sub, con
       pad_cols > 4 * kWave * ((cols / 4 + kWave - 1) / kWave))
     return hipErrorInvalidValue;
   const int padc4 = pad_cols / 4;
-  const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)), block(256);
-  return dispatch_nc(cols, [&](auto nc) {
-    constexpr int NC = decltype(nc)::value;
+  // Four rows per wavefront for rows of 1025-2048 columns with nothing to
+  // add, once there are enough rows for 16 such wavefronts per CU, one
+  // otherwise.  Measured on one pass of each
+  // largest stream: the decoder's pre-LN LayerNorm (2048 columns, affine
+  // parameters twice the row's bytes) 282.5 -> 255.6-258.4 us; BERT-base's
+  // residual-adding one (768 columns, parameters half the row's bytes) went
+  // 160.6 -> 170.5 us with four rows (fewer wavefronts per SIMD), so it and
+  // the narrower rows keep one row per wavefront.
+  const bool many = rows >= (int64_t)4 * 256 * 16;  // 16 four-row wavefronts per CU
+  auto go = [&](auto nc, auto rc) {
+    constexpr int NC = decltype(nc)::value, R = decltype(rc)::value;
+    const dim3 grid((unsigned)((rows + R * kRowsPerBlock - 1) / (R * kRowsPerBlock))), block(256);
     if (act_bf16) {
-      auto k = sub ? layernorm_kernel<NC, uint16_t, true> : layernorm_kernel<NC, uint16_t, false>;
+      auto k = sub ? layernorm_kernel<NC, uint16_t, true, R> : layernorm_kernel<NC, uint16_t, false, R>;
       k<<<grid, block, 0, st>>>(x, sub, g, b, rows, cols, eps, y, (uint16_t *)yb, ldb, padc4);
     } else {
-      auto k = sub ? layernorm_kernel<NC, float, true> : layernorm_kernel<NC, float, false>;
+      auto k = sub ? layernorm_kernel<NC, float, true, R> : layernorm_kernel<NC, float, false, R>;
       k<<<grid, block, 0, st>>>(x, sub, g, b, rows, cols, eps, y, (float *)yb, ldb, padc4);
     }
     return hipGetLastError();
+  };
+  return dispatch_nc(cols, [&](auto nc) {
+    constexpr int NC = decltype(nc)::value;
+    if (NC == 8 && many && sub == nullptr) return go(nc, std::integral_constant<int, 4>{});
+    return go(nc, std::integral_constant<int, 1>{});
   });
 }
 
